@@ -1,0 +1,384 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-decoding verify step on one MI355X.
+
+One step = one verify pass of a synthetic 9B-class decoder weight stack
+(32 layers, hidden 4096, FFN 12288; q/k/v/o 4096x4096, gate/up 4096x12288,
+down 12288x4096; W4 asymmetric, group 64) at k = 16 bf16 draft rows --
+grouped per layer as qkv, o, gate|up, down (4 dependent launches per layer)
+-- followed by the accept/correct call for those k drafts over a 152000-entry
+vocabulary.  The step is captured in a HIP graph and replayed; inputs are
+resident in HBM before timing starts.
+
+Printed: one JSON line.  `value` is drafted tokens per second (k / step
+time).  Extra fields report the weight stream (GB/s of the W4 pass), the
+roofline of the W4 GEMM kernel, the accept latency, the k sweep (W4 and W8),
+the int8 path, accept statistics over 4096 trials per noise level, the
+measured HBM read peak, and the CPU oracle baseline.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--quick]
+       python bench.py --profile-pass   (short run for rocprofv3 counters)
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("verify-pass weight GB/s and drafted tokens/s at k=16, 9B-shape W4; accept µs")
+HBM_PEAK_GBPS = 8000.0
+LAYERS, HIDDEN, FFN, GROUP = 32, 4096, 12288, 64
+VOCAB = 152000
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- workloads --
+def make_w4_stack(torch, synth, dev, layers=LAYERS):
+    """Per layer: fused qkv [3H, H], o [H, H], fused gate|up [2F, H], down [H, F]."""
+    shapes = [("qkv", 3 * HIDDEN, HIDDEN), ("o", HIDDEN, HIDDEN),
+              ("gateup", 2 * FFN, HIDDEN), ("down", HIDDEN, FFN)]
+    stack = []
+    for l in range(layers):
+        layer = []
+        for i, (name, N, K) in enumerate(shapes):
+            c, s, z = synth.w4_matrix(N, K, seed=1000 * l + i, device=dev)
+            layer.append((name, N, K, c, s, z))
+        stack.append(layer)
+    return stack
+
+
+def make_w8_stack(torch, synth, dev, layers=LAYERS):
+    shapes = [("qkv", 3 * HIDDEN, HIDDEN), ("o", HIDDEN, HIDDEN),
+              ("gateup", 2 * FFN, HIDDEN), ("down", HIDDEN, FFN)]
+    stack = []
+    for l in range(layers):
+        layer = []
+        for i, (name, N, K) in enumerate(shapes):
+            c, s = synth.w8_matrix(N, K, seed=5000 + 1000 * l + i, device=dev)
+            layer.append((name, N, K, c, s))
+        stack.append(layer)
+    return stack
+
+
+def w4_bytes(stack):
+    return sum(N * K // 2 + 4 * N * (K // GROUP) for layer in stack
+               for (_, N, K, *_r) in layer)
+
+
+def w8_bytes(stack):
+    return sum(N * K + 2 * N for layer in stack for (_, N, K, *_r) in layer)
+
+
+# ------------------------------------------------------------------- timing --
+def time_graph(torch, fn, steps, warmup):
+    """Capture fn() in a HIP graph, replay warmup + steps times; ms per replay."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # first eager call outside capture (one-time attribute setup)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, g
+
+
+def per_launch_durations(torch, launches, reps):
+    """Event-bracketed duration of each launch (stream order), averaged over reps."""
+    import collections
+    acc = collections.defaultdict(list)
+    for _ in range(reps):
+        evs = []
+        for key, fn in launches:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs.append((key, a, b))
+        torch.cuda.synchronize()
+        for key, a, b in evs:
+            acc[key].append(a.elapsed_time(b))
+    return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) // reps for k, v in acc.items()}
+
+
+# --------------------------------------------------------------- cpu oracle --
+def cpu_baseline(k=16):
+    """The binary64 oracle on the host: one full layer of the W4 stack at k rows
+    (7 matrices, dequantize + matmul, rows in chunks) plus one accept trial at
+    V = 152000; per-step time extrapolated to 32 layers + accept."""
+    import numpy as np
+    import torch
+    import oracle
+    from verify_pass_sv_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    shapes = [(N, K) for _, N, K in oracle.decoder_stack_shapes(HIDDEN, FFN)]
+    xs = {K: synth.activations(k, K, seed=7).view(torch.int16).numpy().view(np.uint16)
+          for K in (HIDDEN, FFN)}
+    t0 = time.perf_counter()
+    for i, (N, K) in enumerate(shapes):
+        c, s, z = synth.w4_matrix(N, K, seed=900 + i)
+        c, s, z = c.numpy(), s.numpy(), z.numpy()
+        for r0 in range(0, N, 2048):
+            oracle.qgemm_w4(xs[K], c[r0:r0 + 2048], s[r0:r0 + 2048], z[r0:r0 + 2048])
+    t_layer = time.perf_counter() - t0
+    tgt, dft, tok = synth.accept_inputs(1, k, VOCAB, seed=3, sigma=1.0)
+    t1 = time.perf_counter()
+    oracle.verify_accept(tgt.numpy(), dft.numpy(), tok.numpy(), seed=0)
+    t_acc = time.perf_counter() - t1
+    t_step = LAYERS * t_layer + t_acc
+    return {"value": k / t_step, "unit": "drafted tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"1 of 32 layers (7 W4 matrices, k={k}, binary64 dequantize+matmul) "
+                       f"timed {t_layer:.2f} s and extrapolated x32, plus 1 accept trial "
+                       f"(V={VOCAB}, k={k}) {t_acc:.2f} s; {t_step:.1f} s per step")}
+
+
+# --------------------------------------------------------------------- main --
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--k", type=int, default=16)
+    ap.add_argument("--quick", action="store_true", help="skip sweeps, stats and cpu baseline")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="copy kernel + read probe + 2 eager W4 passes, then exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import verify_pass_sv_amd as sv
+    from verify_pass_sv_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    k = args.k
+    log(f"device {torch.cuda.get_device_name(0)}; building W4 stack")
+    w4 = make_w4_stack(torch, synth, dev)
+    x_h = synth.activations(32, HIDDEN, seed=11, device=dev)
+    x_f = synth.activations(32, FFN, seed=12, device=dev)
+    ys = {N: torch.empty((32, N), dtype=torch.float32, device=dev)
+          for N in (3 * HIDDEN, HIDDEN, 2 * FFN)}
+
+    def w4_launches(kk):
+        xh, xf = x_h[:kk].contiguous(), x_f[:kk].contiguous()
+        out = {N: y[:kk] for N, y in ys.items()}
+        L = []
+        for li, layer in enumerate(w4):
+            for (name, N, K, c, s, z) in layer:
+                xx = xh if K == HIDDEN else xf
+                yy = out[N]
+                L.append(((name, N, K), (lambda xx=xx, c=c, s=s, z=z, yy=yy:
+                                         sv.sv_qgemm_w4(xx, c, s, z, yy))))
+        return L
+
+    pass_bytes = w4_bytes(w4)
+    torch.cuda.synchronize()
+
+    if args.profile_pass:
+        src = torch.empty(1 << 28, dtype=torch.uint8, device=dev).random_(0, 255)
+        dst = torch.empty_like(src)
+        dst.copy_(src)  # plain copy kernel of 256 MiB (counter scale reference)
+        sink = torch.empty(sv.sv_read_probe_sink_words(), dtype=torch.int32, device=dev)
+        sv.sv_read_bandwidth_probe(src, sink)
+        for _ in range(2):
+            for _, fn in w4_launches(k):
+                fn()
+        torch.cuda.synchronize()
+        log("profile pass done")
+        return
+
+    # ---- the step: W4 pass at k rows + accept over V = 152000 ----
+    tgt, dft, tok = synth.accept_inputs(1, k, VOCAB, seed=21, sigma=1.0, device=dev)
+    acc_out = {"tokens": torch.empty((1, k + 1), dtype=torch.int32, device=dev),
+               "n_acc": torch.empty((1,), dtype=torch.int32, device=dev),
+               "status": torch.empty((1,), dtype=torch.int32, device=dev)}
+    acc_ws = torch.empty(sv.sv_verify_accept_workspace_bytes(1, k, VOCAB), dtype=torch.uint8,
+                         device=dev)
+    launches = w4_launches(k)
+
+    def step():
+        for _, fn in launches:
+            fn()
+        sv.sv_verify_accept(tgt, dft, tok, seed=0, out=acc_out, workspace=acc_ws)
+
+    log("timing the step (graph replay)")
+    ms_step, _ = time_graph(torch, step, args.steps, args.warmup)
+
+    def pass_only():
+        for _, fn in launches:
+            fn()
+
+    ms_pass, _ = time_graph(torch, pass_only, args.steps, args.warmup)
+    weight_gbps = pass_bytes / (ms_pass * 1e-3) / 1e9
+
+    # ---- roofline of the W4 GEMM kernel: event-timed launches of one pass ----
+    dur, cnt = per_launch_durations(torch, launches, reps=3)
+    tot_bytes = tot_ms = 0.0
+    per_shape = {}
+    for (name, N, K), d in dur.items():
+        nb = N * K // 2 + 4 * N * (K // GROUP)
+        n = cnt[(name, N, K)]
+        tot_bytes += nb * n
+        tot_ms += d * n
+        per_shape[f"{name}_{N}x{K}"] = {"us": round(d * 1e3, 2),
+                                        "GBps": round(nb / (d * 1e-3) / 1e9, 1)}
+    achieved = tot_bytes / (tot_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "kernel": "qgemm_w4_kernel<1,8,true>",
+                "bytes_per_launch_avg": int(tot_bytes / sum(cnt.values())),
+                "launch_us_avg": round(tot_ms * 1e3 / sum(cnt.values()), 2),
+                "per_shape": per_shape}
+
+    # ---- accept latency at k = 32 (B = 1) and throughput at B = 64 ----
+    def accept_bench(B, kk):
+        t, d, tk = synth.accept_inputs(B, kk, VOCAB, seed=31 + B, sigma=1.0, device=dev)
+        out = {"tokens": torch.empty((B, kk + 1), dtype=torch.int32, device=dev),
+               "n_acc": torch.empty((B,), dtype=torch.int32, device=dev),
+               "status": torch.empty((B,), dtype=torch.int32, device=dev)}
+        ws = torch.empty(sv.sv_verify_accept_workspace_bytes(B, kk, VOCAB), dtype=torch.uint8,
+                         device=dev)
+        ms, _ = time_graph(torch, lambda: sv.sv_verify_accept(t, d, tk, seed=0, out=out,
+                                                              workspace=ws), 50, 5)
+        del t, d, tk
+        return ms * 1e3
+
+    accept_us_b1 = accept_bench(1, 32)
+    accept_us_b64 = accept_bench(64, 32)
+    accept_bytes = ((2 * 32 + 1) * VOCAB * 4 + 2 * VOCAB * 4)
+    extra = {"weight_GBps": round(weight_gbps, 1),
+             "weight_frac_of_8TBps": round(weight_gbps / HBM_PEAK_GBPS, 4),
+             "pass_ms": round(ms_pass, 4), "pass_weight_bytes": pass_bytes,
+             "accept_us_k32_B1": round(accept_us_b1, 2),
+             "accept_us_per_trial_k32_B64": round(accept_us_b64 / 64, 3),
+             "accept_GBps_B64": round(64 * accept_bytes / (accept_us_b64 * 1e-6) / 1e9, 1)}
+
+    if not args.quick:
+        # measured read peak
+        big = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+        sink = torch.empty(sv.sv_read_probe_sink_words(), dtype=torch.int32, device=dev)
+        ms_rd, _ = time_graph(torch, lambda: sv.sv_read_bandwidth_probe(big, sink), 10, 2)
+        extra["read_probe_GBps"] = round(big.numel() / (ms_rd * 1e-3) / 1e9, 1)
+        extra["weight_frac_of_read_probe"] = round(weight_gbps / extra["read_probe_GBps"], 4)
+        del big
+        # W4 k sweep: memory-bound to MFMA crossover, latency ratio
+        sweep = {}
+        for kk in (1, 4, 8, 16, 32):
+            L = w4_launches(kk)
+            ms, _ = time_graph(torch, lambda L=L: [fn() for _, fn in L], 10, 2)
+            sweep[kk] = {"pass_ms": round(ms, 4), "GBps": round(pass_bytes / (ms * 1e-3) / 1e9, 1),
+                         "drafted_tok_s": round(kk / (ms * 1e-3), 1)}
+        extra["w4_k_sweep"] = sweep
+        extra["w4_latency_ratio_k32_over_k1"] = round(sweep[32]["pass_ms"] / sweep[1]["pass_ms"], 3)
+        # int8 path: Hadamard (block 4096) + int8 W4 GEMM per input, 32 layers
+        signs_h = synth.hadamard_signs(HIDDEN, seed=3, device=dev)
+        signs_f = synth.hadamard_signs(FFN, seed=4, device=dev)
+        xo_h, _ = synth.outlier_activations(k, HIDDEN, seed=5, device=dev)
+        xo_f, _ = synth.outlier_activations(k, FFN, seed=6, device=dev)
+        xq_h = torch.empty((k, HIDDEN), dtype=torch.int8, device=dev)
+        xq_f = torch.empty((k, FFN), dtype=torch.int8, device=dev)
+        sc_h = torch.empty((k,), dtype=torch.float32, device=dev)
+        sc_f = torch.empty((k,), dtype=torch.float32, device=dev)
+
+        def int8_pass():
+            for layer in w4:
+                for (name, N, K, c, s, z) in layer:
+                    if K == HIDDEN:
+                        sv.sv_hadamard_i8(xo_h, signs_h, 4096, xq_h, sc_h)
+                        sv.sv_qgemm_w4_i8(xq_h, sc_h, c, s, z, ys[N][:k])
+                    else:
+                        sv.sv_hadamard_i8(xo_f, signs_f, 4096, xq_f, sc_f)
+                        sv.sv_qgemm_w4_i8(xq_f, sc_f, c, s, z, ys[N][:k])
+
+        ms_i8, _ = time_graph(torch, int8_pass, 10, 2)
+        had = [(("had", K, 0), (lambda xx=xx, sg=sg, q=q, sc=sc: sv.sv_hadamard_i8(xx, sg, 4096, q, sc)))
+               for xx, sg, q, sc, K in ((xo_h, signs_h, xq_h, sc_h, HIDDEN),
+                                         (xo_f, signs_f, xq_f, sc_f, FFN))]
+        hd, _ = per_launch_durations(torch, had * 8, reps=2)
+        extra["int8_path"] = {"pass_ms": round(ms_i8, 4),
+                              "GBps": round(pass_bytes / (ms_i8 * 1e-3) / 1e9, 1),
+                              "hadamard_us": {f"K{key[1]}": round(v * 1e3, 2)
+                                              for key, v in hd.items()}}
+        # W8 k sweep
+        del launches
+        w8 = make_w8_stack(torch, synth, dev)
+        b8 = w8_bytes(w8)
+        sweep8 = {}
+        for kk in (1, 4, 8, 16, 32):
+            xh, xf = x_h[:kk].contiguous(), x_f[:kk].contiguous()
+            L = []
+            for layer in w8:
+                for (name, N, K, c, s) in layer:
+                    L.append((xh if K == HIDDEN else xf, c, s, ys[N][:kk]))
+            ms, _ = time_graph(torch, lambda L=L: [sv.sv_qgemm_w8(a, c, s, y) for a, c, s, y in L],
+                               10, 2)
+            sweep8[kk] = {"pass_ms": round(ms, 4), "GBps": round(b8 / (ms * 1e-3) / 1e9, 1)}
+        extra["w8_k_sweep"] = sweep8
+        del w8
+        # accept statistics: 4096 trials per noise level, k = 32
+        stats = {}
+        B = 64
+        out = {"tokens": torch.empty((B, 33), dtype=torch.int32, device=dev),
+               "n_acc": torch.empty((B,), dtype=torch.int32, device=dev),
+               "status": torch.empty((B,), dtype=torch.int32, device=dev)}
+        ws = torch.empty(sv.sv_verify_accept_workspace_bytes(B, 32, VOCAB), dtype=torch.uint8,
+                         device=dev)
+        for sigma in (0.1, 1.0, 3.0):
+            tot = 0
+            for rep in range(4096 // B):
+                t, d, tk = synth.accept_inputs(B, 32, VOCAB, seed=100000 * int(sigma * 10) + rep,
+                                               sigma=sigma, device=dev)
+                sv.sv_verify_accept(t, d, tk, seed=0, offset=rep, out=out, workspace=ws)
+                tot += int(out["n_acc"].sum().item())
+            mean_acc = tot / 4096
+            stats[str(sigma)] = {"mean_accepted": round(mean_acc, 3),
+                                 "tokens_per_pass": round(mean_acc + 1, 3)}
+        extra["accept_stats_k32"] = stats
+
+    cpu = None
+    if not (args.quick or args.no_cpu):
+        log("timing the CPU oracle baseline")
+        cpu = cpu_baseline(k)
+
+    line = {
+        "metric": METRIC, "value": round(k / (ms_step * 1e-3), 1), "unit": "drafted tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "9B-class decoder weight stack, W4 asymmetric group 64, "
+                               "32 layers (hidden 4096, ffn 12288), k=16 bf16 draft rows, "
+                               "then accept/correct over V=152000",
+                   "k": k, "layers": LAYERS, "hidden": HIDDEN, "ffn": FFN, "group": GROUP,
+                   "vocab": VOCAB, "launches_per_pass": 4 * LAYERS + 3,
+                   "graph": "hipGraph replay"},
+        "roofline": roofline, "cpu_baseline": cpu, **extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

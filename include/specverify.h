@@ -1,0 +1,230 @@
+/*
+ * libspecverify -- the data-parallel hot path of speculative-decoding
+ * verification on AMD Instinct MI355X (gfx950).
+ *
+ * The target model scores a block of k draft tokens in one pass, streaming
+ * its quantized weights from HBM once for all k rows; a left-to-right
+ * accept/correct step then keeps a prefix of the drafts and samples one more
+ * token.  Sources (cited by page title and section):
+ *   - "Speculative Decoding Clearly Explained": "Check the guesses together",
+ *     "Accept from left to right", "Correct and continue".
+ *   - "Karpathy's Trick for Faster Local LLMs Finally Has Proper Tooling":
+ *     "Why batch-one decoding is memory-bound", "How Uzu optimizes bytes and
+ *     tokens per pass", "Producing several tokens from one model pass".
+ *   - "Local LLM 4x Faster -- Not Through Hardware, but Through Speculative
+ *     Decoding" (int8 matrix path, random Hadamard transform).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; the
+ *     library never allocates or frees memory.  Tensors are contiguous and
+ *     row-major; every pointer must be 16-byte aligned.
+ *   - Arguments are validated synchronously, before any launch; a bad
+ *     argument returns SV_ERR_* and nothing is enqueued.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the default
+ *     stream).  A failed launch returns SV_ERR_HIP.
+ *   - No global mutable state; calls are thread-safe.  Calls that share an
+ *     output or workspace buffer on one device must be ordered by the caller.
+ *   - bf16 = bfloat16 (upper half of an IEEE binary32), f16 = IEEE binary16,
+ *     passed as `const void*`.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_NULL = 1,          /* a required pointer is NULL                      */
+  SV_ERR_INVALID_ARG = 2,   /* a size or parameter is out of range             */
+  SV_ERR_ALIGN = 3,         /* a pointer is not 16-byte aligned                */
+  SV_ERR_UNSUPPORTED = 4,   /* valid in principle, not implemented (e.g. group)*/
+  SV_ERR_WORKSPACE = 5,     /* workspace missing or too small                  */
+  SV_ERR_HIP = 6            /* the HIP runtime reported an error at launch     */
+} sv_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* sv_status_str(sv_status status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int sv_version(void);
+
+/* Maximum number of draft rows / draft tokens per call (the pages' 16-32
+ * token budgets: @trymirai timeline; Karpathy's Trick ..., "Producing several
+ * tokens from one model pass"). */
+#define SV_MAX_ROWS 32
+
+/*
+ * sv_qgemm_w4 -- verify GEMM over 4-bit asymmetric group-quantized weights.
+ *
+ * Defines (Karpathy's Trick ..., "How Uzu optimizes bytes and tokens per
+ * pass": the Medium checkpoint uses 4-bit asymmetric integer quantization
+ * where every value of a group shares one scale; Speculative Decoding Clearly
+ * Explained, "Check the guesses together": all draft positions are scored in
+ * one pass):
+ *
+ *   Y[r, n] = sum_k X[r, k] * (C[n, k] - Z[n, k/group]) * S[n, k/group],
+ *   r < m, n < N, k < K.
+ *
+ *   x       bf16 [m, K]        activations, one row per draft position
+ *   m       1 .. SV_MAX_ROWS
+ *   K       input features; K % 64 == 0
+ *   codes   uint8 [N, K/2]     byte j of row n: code of k = 2j in the low
+ *                              nibble, k = 2j + 1 in the high nibble
+ *   scales  f16 [N, K/group]   per-group scale S
+ *   zeros   f16 [N, K/group]   per-group zero point Z (any f16 value; the
+ *                              dequantized weight is exact in binary32 when
+ *                              Z is integer-valued)
+ *   N       output features; N % 16 == 0
+ *   group   must be 64 (SV_ERR_UNSUPPORTED otherwise)
+ *   y       f32 [m, N]         output, fully overwritten
+ *
+ * Every weight byte is read from HBM once for all m rows.  Accumulation is
+ * binary32; the result is deterministic (bitwise identical across runs).
+ */
+sv_status sv_qgemm_w4(const void* x, int m, int K,
+                      const uint8_t* codes, const void* scales, const void* zeros,
+                      int N, int group, float* y, hipStream_t stream);
+
+/*
+ * sv_qgemm_w8 -- verify GEMM over 8-bit symmetric per-output-channel weights.
+ *
+ * Defines (Karpathy's Trick ..., "How Uzu optimizes bytes and tokens per
+ * pass": the Large checkpoint uses 8-bit symmetric quantization):
+ *
+ *   Y[r, n] = S[n] * sum_k X[r, k] * C[n, k]
+ *
+ *   x       bf16 [m, K], m in 1 .. SV_MAX_ROWS, K % 64 == 0
+ *   codes   int8 [N, K], values in [-127, 127] (-128 is rejected by nothing
+ *           but is outside the format; it dequantizes as -128 * S)
+ *   scales  f16 [N]
+ *   N % 16 == 0;  y f32 [m, N], fully overwritten.
+ */
+sv_status sv_qgemm_w8(const void* x, int m, int K, const int8_t* codes,
+                      const void* scales, int N, float* y, hipStream_t stream);
+
+/*
+ * sv_hadamard_i8 -- randomized block-diagonal Hadamard rotation of the
+ * activations followed by per-token symmetric int8 quantization.
+ *
+ * Defines (Karpathy's Trick ..., "How Uzu optimizes bytes and tokens per
+ * pass": random sign flips, then mixing by a +-1 Hadamard matrix with one
+ * overall scale, each block mixed on its own, exactly reversible; activations
+ * quantized to 8 bits on the fly so both GEMM operands are integers):
+ *
+ *   xt[r, b*B + i] = B^-1/2 * sum_j H_B[i, j] * signs[b*B + j] * x[r, b*B + j]
+ *   xscale[r] = max_k |xt[r, k]| / 127   (1 if the row is all zero)
+ *   xq[r, k]  = clamp(round_half_even(xt[r, k] / xscale[r]), -127, 127)
+ *
+ * with H_B the Sylvester Hadamard matrix, H[i, j] = (-1)^popcount(i & j).
+ * The rotation is summed in binary64 and rounded once to binary32; the scale
+ * and the rounding decision are binary32.
+ *
+ *   x       bf16 [m, K], m in 1 .. SV_MAX_ROWS
+ *   signs   int8 [K], each +1 or -1 (other values are used as given)
+ *   block   power of two, 2 <= block <= 4096, block divides K
+ *   K       K % 64 == 0, K <= 16384
+ *   xq      int8 [m, K]  output
+ *   xscale  f32 [m]      output
+ */
+sv_status sv_hadamard_i8(const void* x, int m, int K, const int8_t* signs, int block,
+                         int8_t* xq, float* xscale, hipStream_t stream);
+
+/*
+ * sv_qgemm_w4_i8 -- the int8 matrix path: int8 activations times 4-bit
+ * weights with exact int32 per-group partials.
+ *
+ * Defines (Local LLM 4x Faster: the 4-bit checkpoint runs on the GPU's int8
+ * matrix path; Karpathy's Trick ..., "How Uzu optimizes bytes and tokens per
+ * pass"):
+ *
+ *   I[r, n, g]  = sum_{k in g} C[n, k] * xq[r, k]          (exact int32)
+ *   Xg[r, g]    = sum_{k in g} xq[r, k]                    (exact int32)
+ *   Y[r, n]     = xscale[r] * sum_g S[n, g] * (I[r, n, g] - Z[n, g] * Xg[r, g])
+ *
+ *   xq      int8 [m, K], xscale f32 [m] (typically from sv_hadamard_i8)
+ *   codes, scales, zeros, N, group: as sv_qgemm_w4
+ *   y       f32 [m, N], fully overwritten.
+ */
+sv_status sv_qgemm_w4_i8(const int8_t* xq, const float* xscale, int m, int K,
+                         const uint8_t* codes, const void* scales, const void* zeros,
+                         int N, int group, float* y, hipStream_t stream);
+
+/*
+ * sv_verify_accept -- fused vocabulary softmax for target and draft, the
+ * left-to-right accept scan, and the residual / bonus resample.
+ *
+ * Defines (Speculative Decoding Clearly Explained, "Accept from left to
+ * right" and "Correct and continue"; Karpathy's Trick ..., "Producing several
+ * tokens from one model pass"), per independent trial b:
+ *
+ *   p_i = softmax(target[b, i, :]),  q_i = softmax(draft[b, i, :])
+ *   (temperature 1; a logit of -inf is probability 0)
+ *   For i = 0, 1, ..: accept draft d_i iff u_i * q_i(d_i) < p_i(d_i); stop at
+ *   the first rejection.  n_acc = number accepted (0..k).
+ *   r = n_acc.  If r < k: w_v = max(0, p_r(v) - q_r(v)); else w_v = p_k(v)
+ *   (the bonus token after all drafts).  S = sum_v w_v (if S == 0, w = p_r).
+ *   The new token is the smallest v whose running sum, in ascending vocab
+ *   order, exceeds u'_r * S.
+ *   out_tokens[b, 0..n_acc-1] = d_0..d_{n_acc-1}; out_tokens[b, n_acc] = new
+ *   token; entries after it are -1.  Tokens emitted = n_acc + 1.
+ *
+ * Random numbers: Philox4x32-10 (Salmon et al., SC'11) with key =
+ * (seed & 0xffffffff, seed >> 32) and counter = (i, b, offset, 0); output
+ * word 0 gives u_i, word 1 gives u'_i, each as (word >> 8) * 2^-24.
+ *
+ *   target_logits  f32 [B, k+1, V]  (row k scores the bonus position)
+ *   draft_logits   f32 [B, k, V]
+ *   draft_tokens   int32 [B, k]
+ *   B >= 1, 1 <= k <= SV_MAX_ROWS, V >= 1, (k+1)*V < 2^31
+ *   out_tokens     int32 [B, k+1]
+ *   out_n_acc      int32 [B]    (-1 when out_status[b] != 0)
+ *   out_status     int32 [B]    0 ok; 1 a draft token outside [0, V);
+ *                               2 a row holds NaN or +inf or no finite logit
+ *   p_at, q_at     f32 [B, k]   optional (NULL to skip): p_i(d_i), q_i(d_i)
+ *   lse            f32 [B, 2k+1] optional: log-sum-exp of target rows 0..k,
+ *                               then draft rows 0..k-1
+ *   workspace      device scratch of at least
+ *                  sv_verify_accept_workspace_bytes(B, k, V) bytes; contents
+ *                  need no initialization and are clobbered.
+ *
+ * Device-data problems are reported through out_status, never raised.
+ */
+size_t sv_verify_accept_workspace_bytes(int B, int k, int V);
+sv_status sv_verify_accept(const float* target_logits, const float* draft_logits,
+                           const int32_t* draft_tokens, int B, int k, int V,
+                           uint64_t seed, uint32_t offset,
+                           int32_t* out_tokens, int32_t* out_n_acc, int32_t* out_status,
+                           float* p_at, float* q_at, float* lse,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sv_philox4x32_10 -- the device Philox4x32-10 bijection used by
+ * sv_verify_accept, exposed so callers can check it against the published
+ * known-answer vectors.  ctr uint32 [n, 4], key uint32 [n, 2], out uint32
+ * [n, 4]; n >= 1.
+ */
+sv_status sv_philox4x32_10(const uint32_t* ctr, const uint32_t* key, uint32_t* out,
+                           int n, hipStream_t stream);
+
+/*
+ * sv_read_bandwidth_probe -- streams `bytes` bytes from `src` with 16-byte
+ * loads and writes one 32-bit checksum per workgroup to `sink`
+ * (sink must hold sv_read_probe_sink_words() words).  A plain read kernel
+ * used to state the measured HBM read peak next to roofline fractions.
+ * bytes % 16 == 0.
+ */
+int sv_read_probe_sink_words(void);
+sv_status sv_read_bandwidth_probe(const void* src, size_t bytes, uint32_t* sink,
+                                  hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

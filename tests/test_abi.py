@@ -1,0 +1,78 @@
+"""The C-ABI library loads and exports every entry point the header declares.
+
+CPU-only: nothing here launches a kernel; the argument checks below return
+before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declarations_found():
+    names = _declared()
+    assert "sv_qgemm_w4" in names and "sv_verify_accept" in names
+    assert len(names) >= 11
+
+
+def test_library_exports_every_declared_symbol():
+    import verify_pass_sv_amd as sv
+    lib = ctypes.CDLL(sv.lib_path)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, f"missing exports: {missing}"
+    assert set(_declared()) == set(sv.EXPORTED_SYMBOLS)
+
+
+def test_version_and_status_strings():
+    import verify_pass_sv_amd as sv
+    assert sv.sv_version() == 100
+    assert sv.sv_status_str(0) == "SV_OK"
+    assert sv.sv_status_str(5) == "SV_ERR_WORKSPACE"
+    assert sv.sv_status_str(99) == "SV_ERR_UNKNOWN"
+
+
+def test_argument_validation_before_launch():
+    import verify_pass_sv_amd as sv
+    L = sv.lib
+    fake = ctypes.c_void_p(0x100000)     # aligned, never dereferenced
+    odd = ctypes.c_void_p(0x100002)
+    # null pointer
+    assert L.sv_qgemm_w4(None, 4, 512, fake, fake, fake, 64, 64, fake, None) == 1
+    # unsupported group size
+    assert L.sv_qgemm_w4(fake, 4, 512, fake, fake, fake, 64, 32, fake, None) == 4
+    # m out of range, N not a multiple of 16, K not a multiple of 64
+    assert L.sv_qgemm_w4(fake, 33, 512, fake, fake, fake, 64, 64, fake, None) == 2
+    assert L.sv_qgemm_w4(fake, 4, 512, fake, fake, fake, 40, 64, fake, None) == 2
+    assert L.sv_qgemm_w8(fake, 4, 100, fake, fake, 64, fake, None) == 2
+    # misaligned pointer
+    assert L.sv_qgemm_w4(odd, 4, 512, fake, fake, fake, 64, 64, fake, None) == 3
+    # Hadamard block must be a power of two dividing K, at most 4096
+    assert L.sv_hadamard_i8(fake, 4, 4096, fake, 48, fake, fake, None) == 2
+    assert L.sv_hadamard_i8(fake, 4, 4096, fake, 8192, fake, fake, None) == 2
+    assert L.sv_hadamard_i8(fake, 4, 32768, fake, 4096, fake, fake, None) == 2
+    # accept: k range, workspace size
+    ws = sv.sv_verify_accept_workspace_bytes(4, 8, 1000)
+    assert ws > 0 and sv.sv_verify_accept_workspace_bytes(4, 33, 1000) == 0
+    args = [fake, fake, fake, 4, 8, 1000, 0, 0, fake, fake, fake, None, None, None]
+    assert L.sv_verify_accept(*args, fake, ws - 1, None) == 5
+    assert L.sv_verify_accept(*args, None, ws, None) == 5
+    bad_k = [fake, fake, fake, 4, 0, 1000, 0, 0, fake, fake, fake, None, None, None]
+    assert L.sv_verify_accept(*bad_k, fake, ws, None) == 2
+
+
+def test_workspace_grows_with_batch():
+    import verify_pass_sv_amd as sv
+    a = sv.sv_verify_accept_workspace_bytes(1, 32, 152000)
+    b = sv.sv_verify_accept_workspace_bytes(64, 32, 152000)
+    assert 0 < a < b

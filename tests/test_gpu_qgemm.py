@@ -1,0 +1,158 @@
+"""GPU parity of sv_qgemm_w4 / sv_qgemm_w8 against the binary64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from verify_pass_sv_amd import synth
+from gpu_util import DEV, to_dev, bf16_bits, assert_rows_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _sv():
+    import verify_pass_sv_amd as sv
+    return sv
+
+
+def _w4_case(m, K, N, seed):
+    codes, scales, zeros = synth.w4_matrix(N, K, seed=seed)
+    x = synth.activations(m, K, seed=seed + 1)
+    return x, codes, scales, zeros
+
+
+def _w4_oracle(x, codes, scales, zeros, rows=None):
+    c, s, z = codes.numpy(), scales.numpy(), zeros.numpy()
+    if rows is not None:
+        c, s, z = c[rows], s[rows], z[rows]
+    return oracle.qgemm_w4(bf16_bits(x), c, s, z)
+
+
+@pytest.mark.parametrize("m,K,N", [(4, 512, 1024),     # the tiny configuration
+                                   (1, 1024, 256), (7, 1024, 256), (16, 2048, 128),
+                                   (17, 1024, 256), (32, 4096, 64), (5, 192, 48),
+                                   (3, 320, 16)])
+def test_w4_matches_oracle(m, K, N):
+    sv = _sv()
+    x, codes, scales, zeros = _w4_case(m, K, N, seed=10 + m)
+    y = sv.sv_qgemm_w4(*to_dev(x, codes, scales, zeros))
+    torch.cuda.synchronize()
+    assert_rows_close(y.cpu().numpy(), _w4_oracle(x, codes, scales, zeros),
+                      what=f"w4 m={m} K={K} N={N}")
+
+
+@pytest.mark.parametrize("K", [512, 4096, 320])
+def test_w4_one_hot_rows_expose_exact_dequant(K):
+    # an activation row e_j makes Y[r, n] the single dequantized weight
+    # (c - z) * s, which is exact in binary32 for integer zero points
+    sv = _sv()
+    N, m = 64, 32
+    codes, scales, zeros = synth.w4_matrix(N, K, seed=3)
+    rng = np.random.default_rng(4)
+    cols = rng.choice(K, size=m, replace=False)
+    x = torch.zeros((m, K), dtype=torch.bfloat16)
+    x[torch.arange(m), torch.as_tensor(cols)] = 1.0
+    y = sv.sv_qgemm_w4(*to_dev(x, codes, scales, zeros))
+    torch.cuda.synchronize()
+    W = oracle.dequant_w4(codes.numpy(), scales.numpy(), zeros.numpy())
+    expect = W[:, cols].T.astype(np.float32)
+    got = y.cpu().numpy()
+    bad = np.argwhere(got != expect)
+    assert bad.size == 0, f"{len(bad)} mismatches, first (row, col) {bad[:5].tolist()}: " \
+        f"got {got[tuple(bad[0])]} expect {expect[tuple(bad[0])]}"
+
+
+def test_w4_fractional_zero_points_within_tolerance():
+    sv = _sv()
+    m, K, N = 8, 1024, 128
+    x, codes, scales, _ = _w4_case(m, K, N, seed=21)
+    zeros = (torch.rand((N, K // 64), generator=torch.Generator().manual_seed(5)) * 15).half()
+    y = sv.sv_qgemm_w4(*to_dev(x, codes, scales, zeros))
+    torch.cuda.synchronize()
+    assert_rows_close(y.cpu().numpy(), _w4_oracle(x, codes, scales, zeros), what="w4 frac z")
+
+
+@pytest.mark.parametrize("N,K", [(4096, 4096), (12288, 4096), (24576, 4096), (4096, 12288)])
+def test_w4_full_size_shapes_sampled_channels(N, K):
+    # the 9B-class layer shapes at k = 16 in the launch configuration the
+    # bench uses; the oracle checks a sample of output channels
+    sv = _sv()
+    m = 16
+    codes, scales, zeros = synth.w4_matrix(N, K, seed=N + K, device=DEV)
+    x = synth.activations(m, K, seed=7, device=DEV)
+    y = sv.sv_qgemm_w4(x, codes, scales, zeros)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(N).choice(N, size=96, replace=False))
+    idx = torch.as_tensor(rows, device=DEV)
+    ref = oracle.qgemm_w4(bf16_bits(x), codes[idx].cpu().numpy(), scales[idx].cpu().numpy(),
+                          zeros[idx].cpu().numpy())
+    assert_rows_close(y[:, idx].cpu().numpy(), ref, what=f"w4 full {N}x{K}")
+
+
+def test_w4_deterministic():
+    sv = _sv()
+    x, codes, scales, zeros = to_dev(*_w4_case(16, 4096, 1024, seed=30))
+    y1 = sv.sv_qgemm_w4(x, codes, scales, zeros)
+    y2 = sv.sv_qgemm_w4(x, codes, scales, zeros)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_w4_argument_errors():
+    sv = _sv()
+    x, codes, scales, zeros = to_dev(*_w4_case(4, 512, 64, seed=31))
+    y = torch.empty((4, 64), dtype=torch.float32, device=DEV)
+    L, vp = sv.lib, __import__("ctypes").c_void_p
+    P = lambda t, off=0: vp(t.data_ptr() + off)
+    st = vp(torch.cuda.current_stream().cuda_stream)
+    assert L.sv_qgemm_w4(P(x), 4, 512, P(codes), P(scales), P(zeros), 64, 32, P(y), st) == 4
+    assert L.sv_qgemm_w4(P(x), 4, 512, P(codes), P(scales), P(zeros), 56, 64, P(y), st) == 2
+    assert L.sv_qgemm_w4(P(x), 0, 512, P(codes), P(scales), P(zeros), 64, 64, P(y), st) == 2
+    assert L.sv_qgemm_w4(P(x), 33, 512, P(codes), P(scales), P(zeros), 64, 64, P(y), st) == 2
+    assert L.sv_qgemm_w4(P(x), 4, 500, P(codes), P(scales), P(zeros), 64, 64, P(y), st) == 2
+    assert L.sv_qgemm_w4(P(x, 2), 4, 512, P(codes), P(scales), P(zeros), 64, 64, P(y), st) == 3
+    assert L.sv_qgemm_w4(None, 4, 512, P(codes), P(scales), P(zeros), 64, 64, P(y), st) == 1
+
+
+# ---- W8 ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("m,K,N", [(1, 1024, 256), (4, 512, 1024), (16, 4096, 128),
+                                   (17, 1024, 64), (32, 2048, 64), (8, 192, 32)])
+def test_w8_matches_oracle(m, K, N):
+    sv = _sv()
+    codes, scales = synth.w8_matrix(N, K, seed=40 + m)
+    x = synth.activations(m, K, seed=41 + m)
+    y = sv.sv_qgemm_w8(*to_dev(x, codes, scales))
+    torch.cuda.synchronize()
+    ref = oracle.qgemm_w8(bf16_bits(x), codes.numpy(), scales.numpy())
+    assert_rows_close(y.cpu().numpy(), ref, what=f"w8 m={m} K={K} N={N}")
+
+
+def test_w8_one_hot_rows_exact():
+    sv = _sv()
+    N, K, m = 64, 1024, 32
+    codes, scales = synth.w8_matrix(N, K, seed=50)
+    codes[0, :8] = torch.tensor([-127, 127, -1, 0, 1, -64, 64, 3], dtype=torch.int8)
+    cols = np.concatenate([np.arange(8), np.random.default_rng(5).choice(np.arange(8, K), m - 8,
+                                                                         replace=False)])
+    x = torch.zeros((m, K), dtype=torch.bfloat16)
+    x[torch.arange(m), torch.as_tensor(cols)] = 1.0
+    y = sv.sv_qgemm_w8(*to_dev(x, codes, scales))
+    torch.cuda.synchronize()
+    W = oracle.dequant_w8(codes.numpy(), scales.numpy())
+    expect = W[:, cols].T.astype(np.float32)
+    assert np.array_equal(y.cpu().numpy(), expect)
+
+
+@pytest.mark.parametrize("N,K", [(4096, 4096), (4096, 12288)])
+def test_w8_full_size_sampled(N, K):
+    sv = _sv()
+    for m in (1, 16, 32):
+        codes, scales = synth.w8_matrix(N, K, seed=N + K, device=DEV)
+        x = synth.activations(m, K, seed=8, device=DEV)
+        y = sv.sv_qgemm_w8(x, codes, scales)
+        torch.cuda.synchronize()
+        rows = np.sort(np.random.default_rng(K).choice(N, size=64, replace=False))
+        idx = torch.as_tensor(rows, device=DEV)
+        ref = oracle.qgemm_w8(bf16_bits(x), codes[idx].cpu().numpy(), scales[idx].cpu().numpy())
+        assert_rows_close(y[:, idx].cpu().numpy(), ref, what=f"w8 full m={m}")

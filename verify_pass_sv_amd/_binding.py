@@ -1,0 +1,221 @@
+"""ctypes binding of libspecverify with the same entry-point names.
+
+Each wrapper takes torch tensors, checks dtype/shape/device, passes raw
+device pointers plus the current HIP stream to the C ABI, and raises SvError
+on a non-zero status.  No arithmetic of the method happens here.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libspecverify.so")
+
+SV_MAX_ROWS = 32
+
+EXPORTED_SYMBOLS = (
+    "sv_status_str", "sv_version", "sv_qgemm_w4", "sv_qgemm_w8", "sv_hadamard_i8",
+    "sv_qgemm_w4_i8", "sv_verify_accept_workspace_bytes", "sv_verify_accept",
+    "sv_philox4x32_10", "sv_read_probe_sink_words", "sv_read_bandwidth_probe",
+)
+
+_STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_INVALID_ARG", 3: "SV_ERR_ALIGN",
+           4: "SV_ERR_UNSUPPORTED", 5: "SV_ERR_WORKSPACE", 6: "SV_ERR_HIP"}
+
+
+class SvError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)}")
+
+
+def _load():
+    if not os.path.exists(lib_path):
+        raise ImportError(
+            f"{lib_path} is missing: build it with `python -c 'import __graft_entry__ as g; "
+            f"g.build()'` (hipcc, gfx950).  There is no CPU fallback.")
+    L = ctypes.CDLL(lib_path)
+    vp, i32, u32, u64, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32,
+                             ctypes.c_uint64, ctypes.c_size_t)
+    sig = {
+        "sv_status_str": (ctypes.c_char_p, [i32]),
+        "sv_version": (i32, []),
+        "sv_qgemm_w4": (i32, [vp, i32, i32, vp, vp, vp, i32, i32, vp, vp]),
+        "sv_qgemm_w8": (i32, [vp, i32, i32, vp, vp, i32, vp, vp]),
+        "sv_hadamard_i8": (i32, [vp, i32, i32, vp, i32, vp, vp, vp]),
+        "sv_qgemm_w4_i8": (i32, [vp, vp, i32, i32, vp, vp, vp, i32, i32, vp, vp]),
+        "sv_verify_accept_workspace_bytes": (sz, [i32, i32, i32]),
+        "sv_verify_accept": (i32, [vp, vp, vp, i32, i32, i32, u64, u32, vp, vp, vp, vp, vp,
+                                   vp, vp, sz, vp]),
+        "sv_philox4x32_10": (i32, [vp, vp, vp, i32, vp]),
+        "sv_read_probe_sink_words": (i32, []),
+        "sv_read_bandwidth_probe": (i32, [vp, sz, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+lib = _load()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, status):
+    if status != 0:
+        raise SvError(fn, status)
+
+
+def _need(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def sv_status_str(status):
+    return lib.sv_status_str(int(status)).decode()
+
+
+def sv_version():
+    return lib.sv_version()
+
+
+def sv_qgemm_w4(x, codes, scales, zeros, y=None, group=64, stream=None):
+    """Y = X @ dequant_w4(codes, scales, zeros).T  (x bf16 [m, K] -> y f32 [m, N])."""
+    m, K = x.shape
+    N = codes.shape[0]
+    _need(x, "x", torch.bfloat16)
+    _need(codes, "codes", torch.uint8, (N, K // 2))
+    _need(scales, "scales", torch.float16, (N, K // group))
+    _need(zeros, "zeros", torch.float16, (N, K // group))
+    if y is None:
+        y = torch.empty((m, N), dtype=torch.float32, device=x.device)
+    _need(y, "y", torch.float32, (m, N))
+    _check("sv_qgemm_w4", lib.sv_qgemm_w4(_ptr(x), m, K, _ptr(codes), _ptr(scales), _ptr(zeros),
+                                          N, group, _ptr(y), _stream(stream)))
+    return y
+
+
+def sv_qgemm_w8(x, codes, scales, y=None, stream=None):
+    m, K = x.shape
+    N = codes.shape[0]
+    _need(x, "x", torch.bfloat16)
+    _need(codes, "codes", torch.int8, (N, K))
+    _need(scales, "scales", torch.float16, (N,))
+    if y is None:
+        y = torch.empty((m, N), dtype=torch.float32, device=x.device)
+    _need(y, "y", torch.float32, (m, N))
+    _check("sv_qgemm_w8", lib.sv_qgemm_w8(_ptr(x), m, K, _ptr(codes), _ptr(scales), N, _ptr(y),
+                                          _stream(stream)))
+    return y
+
+
+def sv_hadamard_i8(x, signs, block, xq=None, xscale=None, stream=None):
+    m, K = x.shape
+    _need(x, "x", torch.bfloat16)
+    _need(signs, "signs", torch.int8, (K,))
+    if xq is None:
+        xq = torch.empty((m, K), dtype=torch.int8, device=x.device)
+    if xscale is None:
+        xscale = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _need(xq, "xq", torch.int8, (m, K))
+    _need(xscale, "xscale", torch.float32, (m,))
+    _check("sv_hadamard_i8", lib.sv_hadamard_i8(_ptr(x), m, K, _ptr(signs), int(block), _ptr(xq),
+                                                _ptr(xscale), _stream(stream)))
+    return xq, xscale
+
+
+def sv_qgemm_w4_i8(xq, xscale, codes, scales, zeros, y=None, group=64, stream=None):
+    m, K = xq.shape
+    N = codes.shape[0]
+    _need(xq, "xq", torch.int8)
+    _need(xscale, "xscale", torch.float32, (m,))
+    _need(codes, "codes", torch.uint8, (N, K // 2))
+    _need(scales, "scales", torch.float16, (N, K // group))
+    _need(zeros, "zeros", torch.float16, (N, K // group))
+    if y is None:
+        y = torch.empty((m, N), dtype=torch.float32, device=xq.device)
+    _need(y, "y", torch.float32, (m, N))
+    _check("sv_qgemm_w4_i8", lib.sv_qgemm_w4_i8(_ptr(xq), _ptr(xscale), m, K, _ptr(codes),
+                                                _ptr(scales), _ptr(zeros), N, group, _ptr(y),
+                                                _stream(stream)))
+    return y
+
+
+def sv_verify_accept_workspace_bytes(B, k, V):
+    return int(lib.sv_verify_accept_workspace_bytes(int(B), int(k), int(V)))
+
+
+def sv_verify_accept(target_logits, draft_logits, draft_tokens, seed, offset=0, out=None,
+                     diagnostics=False, workspace=None, stream=None):
+    """Accept/correct for B independent trials.
+
+    Returns dict(tokens [B, k+1] int32, n_acc [B], status [B]) plus p_at, q_at
+    [B, k] and lse [B, 2k+1] when diagnostics=True.
+    """
+    B, k1, V = target_logits.shape
+    k = k1 - 1
+    dev = target_logits.device
+    _need(target_logits, "target_logits", torch.float32, (B, k + 1, V))
+    _need(draft_logits, "draft_logits", torch.float32, (B, k, V))
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, k))
+    if out is None:
+        out = {
+            "tokens": torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+            "n_acc": torch.empty((B,), dtype=torch.int32, device=dev),
+            "status": torch.empty((B,), dtype=torch.int32, device=dev),
+        }
+        if diagnostics:
+            out["p_at"] = torch.empty((B, k), dtype=torch.float32, device=dev)
+            out["q_at"] = torch.empty((B, k), dtype=torch.float32, device=dev)
+            out["lse"] = torch.empty((B, 2 * k + 1), dtype=torch.float32, device=dev)
+    need = sv_verify_accept_workspace_bytes(B, k, V)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    _check("sv_verify_accept", lib.sv_verify_accept(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), B, k, V,
+        ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), ctypes.c_uint32(int(offset) & 0xFFFFFFFF),
+        _ptr(out["tokens"]), _ptr(out["n_acc"]), _ptr(out["status"]), _ptr(out.get("p_at")),
+        _ptr(out.get("q_at")), _ptr(out.get("lse")), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel()), _stream(stream)))
+    return out
+
+
+def sv_philox4x32_10(ctr, key, out=None, stream=None):
+    n = ctr.shape[0]
+    _need(ctr, "ctr", torch.int32, (n, 4))
+    _need(key, "key", torch.int32, (n, 2))
+    if out is None:
+        out = torch.empty((n, 4), dtype=torch.int32, device=ctr.device)
+    _check("sv_philox4x32_10", lib.sv_philox4x32_10(_ptr(ctr), _ptr(key), _ptr(out), n,
+                                                    _stream(stream)))
+    return out
+
+
+def sv_read_probe_sink_words():
+    return int(lib.sv_read_probe_sink_words())
+
+
+def sv_read_bandwidth_probe(src, sink, nbytes=None, stream=None):
+    nbytes = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    _check("sv_read_bandwidth_probe", lib.sv_read_bandwidth_probe(
+        _ptr(src), ctypes.c_size_t(nbytes), _ptr(sink), _stream(stream)))
