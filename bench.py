@@ -39,8 +39,9 @@ def log(msg):
 
 
 # ---------------------------------------------------------------- workloads --
-def make_w4_stack(torch, synth, dev, layers=LAYERS):
-    """Per layer: fused qkv [3H, H], o [H, H], fused gate|up [2F, H], down [H, F]."""
+def make_w4_stack(torch, synth, sv, dev, layers=LAYERS):
+    """Per layer: fused qkv [3H, H], o [H, H], fused gate|up [2F, H], down [H, F];
+    each matrix kept row-major and in the packed streaming layout."""
     shapes = [("qkv", 3 * HIDDEN, HIDDEN), ("o", HIDDEN, HIDDEN),
               ("gateup", 2 * FFN, HIDDEN), ("down", HIDDEN, FFN)]
     stack = []
@@ -48,7 +49,8 @@ def make_w4_stack(torch, synth, dev, layers=LAYERS):
         layer = []
         for i, (name, N, K) in enumerate(shapes):
             c, s, z = synth.w4_matrix(N, K, seed=1000 * l + i, device=dev)
-            layer.append((name, N, K, c, s, z))
+            pc, ps = sv.sv_w4_pack(c, s, z)
+            layer.append((name, N, K, c, s, z, pc, ps))
         stack.append(layer)
     return stack
 
@@ -177,22 +179,26 @@ def main():
     dev = torch.device("cuda:0")
     k = args.k
     log(f"device {torch.cuda.get_device_name(0)}; building W4 stack")
-    w4 = make_w4_stack(torch, synth, dev)
+    w4 = make_w4_stack(torch, synth, sv, dev)
     x_h = synth.activations(32, HIDDEN, seed=11, device=dev)
     x_f = synth.activations(32, FFN, seed=12, device=dev)
     ys = {N: torch.empty((32, N), dtype=torch.float32, device=dev)
           for N in (3 * HIDDEN, HIDDEN, 2 * FFN)}
 
-    def w4_launches(kk):
+    def w4_launches(kk, packed=True):
         xh, xf = x_h[:kk].contiguous(), x_f[:kk].contiguous()
         out = {N: y[:kk] for N, y in ys.items()}
         L = []
         for li, layer in enumerate(w4):
-            for (name, N, K, c, s, z) in layer:
+            for (name, N, K, c, s, z, pc, ps) in layer:
                 xx = xh if K == HIDDEN else xf
                 yy = out[N]
-                L.append(((name, N, K), (lambda xx=xx, c=c, s=s, z=z, yy=yy:
-                                         sv.sv_qgemm_w4(xx, c, s, z, yy))))
+                if packed:
+                    fn = (lambda xx=xx, pc=pc, ps=ps, N=N, yy=yy:
+                          sv.sv_qgemm_w4_packed(xx, pc, ps, N, yy))
+                else:
+                    fn = (lambda xx=xx, c=c, s=s, z=z, yy=yy: sv.sv_qgemm_w4(xx, c, s, z, yy))
+                L.append(((name, N, K), fn))
         return L
 
     pass_bytes = w4_bytes(w4)
@@ -249,7 +255,7 @@ def main():
     achieved = tot_bytes / (tot_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                "kernel": "qgemm_w4_kernel<1,8,true>",
+                "kernel": "qgemm_w4p_kernel (packed layout)",
                 "bytes_per_launch_avg": int(tot_bytes / sum(cnt.values())),
                 "launch_us_avg": round(tot_ms * 1e3 / sum(cnt.values()), 2),
                 "per_shape": per_shape}
@@ -267,6 +273,7 @@ def main():
         del t, d, tk
         return ms * 1e3
 
+    log(f"step {ms_step:.3f} ms, pass {ms_pass:.3f} ms ({weight_gbps:.0f} GB/s); timing accept")
     accept_us_b1 = accept_bench(1, 32)
     accept_us_b64 = accept_bench(64, 32)
     accept_bytes = ((2 * 32 + 1) * VOCAB * 4 + 2 * VOCAB * 4)
@@ -285,6 +292,11 @@ def main():
         extra["read_probe_GBps"] = round(big.numel() / (ms_rd * 1e-3) / 1e9, 1)
         extra["weight_frac_of_read_probe"] = round(weight_gbps / extra["read_probe_GBps"], 4)
         del big
+        log(f"read probe {extra['read_probe_GBps']} GB/s; W4 k sweep")
+        Lrm = w4_launches(k, packed=False)
+        ms_rm, _ = time_graph(torch, lambda: [fn() for _, fn in Lrm], 10, 2)
+        extra["w4_row_major_pass_ms"] = round(ms_rm, 4)
+        extra["w4_row_major_GBps"] = round(pass_bytes / (ms_rm * 1e-3) / 1e9, 1)
         # W4 k sweep: memory-bound to MFMA crossover, latency ratio
         sweep = {}
         for kk in (1, 4, 8, 16, 32):
@@ -294,6 +306,7 @@ def main():
                          "drafted_tok_s": round(kk / (ms * 1e-3), 1)}
         extra["w4_k_sweep"] = sweep
         extra["w4_latency_ratio_k32_over_k1"] = round(sweep[32]["pass_ms"] / sweep[1]["pass_ms"], 3)
+        log("int8 path")
         # int8 path: Hadamard (block 4096) + int8 W4 GEMM per input, 32 layers
         signs_h = synth.hadamard_signs(HIDDEN, seed=3, device=dev)
         signs_f = synth.hadamard_signs(FFN, seed=4, device=dev)
@@ -306,7 +319,7 @@ def main():
 
         def int8_pass():
             for layer in w4:
-                for (name, N, K, c, s, z) in layer:
+                for (name, N, K, c, s, z, _pc, _ps) in layer:
                     if K == HIDDEN:
                         sv.sv_hadamard_i8(xo_h, signs_h, 4096, xq_h, sc_h)
                         sv.sv_qgemm_w4_i8(xq_h, sc_h, c, s, z, ys[N][:k])
@@ -323,6 +336,7 @@ def main():
                               "GBps": round(pass_bytes / (ms_i8 * 1e-3) / 1e9, 1),
                               "hadamard_us": {f"K{key[1]}": round(v * 1e3, 2)
                                               for key, v in hd.items()}}
+        log("W8 k sweep")
         # W8 k sweep
         del launches
         w8 = make_w8_stack(torch, synth, dev)
@@ -339,6 +353,7 @@ def main():
             sweep8[kk] = {"pass_ms": round(ms, 4), "GBps": round(b8 / (ms * 1e-3) / 1e9, 1)}
         extra["w8_k_sweep"] = sweep8
         del w8
+        log("accept statistics")
         # accept statistics: 4096 trials per noise level, k = 32
         stats = {}
         B = 64

@@ -92,6 +92,47 @@ sv_status sv_qgemm_w4(const void* x, int m, int K,
                       int N, int group, float* y, hipStream_t stream);
 
 /*
+ * Packed W4 layout -- the checkpoint layout the fast verify GEMM streams.
+ *
+ * The pages describe a checkpoint format designed together with the kernels
+ * (Karpathy's Trick ..., "How Uzu optimizes bytes and tokens per pass";
+ * @trymirai timeline).  sv_w4_pack rewrites row-major W4 weights (the
+ * sv_qgemm_w4 format) once into a tile-major layout whose every 1 KiB block
+ * is one wave load in MFMA operand order:
+ *   packed_codes uint8, N*K/2 bytes: for 16-row tile t and 128-wide k block j,
+ *     the block at byte (t*K/128 + j)*1024 holds, at bytes [16l, 16l+16),
+ *     row 16t + (l & 15) with q = l >> 4: its codes for k = 128j + 16q + [0,16)
+ *     (bytes 0-7) and k = 128j + 64 + 16q + [0,16) (bytes 8-15); inside each
+ *     4-byte word covering k0..k0+7, byte b holds code k0+b in its low nibble
+ *     and code k0+b+4 in its high nibble.
+ *   packed_sz f16, N*(K/group)*4 bytes: for (t, j) a 128-byte block at
+ *     (t*K/128 + j)*128; row n of the tile owns 8 bytes
+ *     [S(2j), Z(2j), S(2j+1), Z(2j+1)].
+ * Requirements: group == 64, N % 16 == 0, K % 128 == 0, N*K/2 < 2^31.  The
+ * pack enqueues
+ * two kernels on `stream`; the caller owns both output buffers (sizes from
+ * sv_w4_packed_codes_bytes / sv_w4_packed_sz_bytes).
+ */
+size_t sv_w4_packed_codes_bytes(int N, int K);
+size_t sv_w4_packed_sz_bytes(int N, int K, int group);
+sv_status sv_w4_pack(const uint8_t* codes, const void* scales, const void* zeros,
+                     int N, int K, int group, uint8_t* packed_codes, void* packed_sz,
+                     hipStream_t stream);
+
+/*
+ * sv_qgemm_w4_packed -- the same product as sv_qgemm_w4,
+ *   Y[r, n] = sum_k X[r, k] * (C[n, k] - Z[n, k/64]) * S[n, k/64],
+ * over weights in the packed layout above: x bf16 [m, K] (m in
+ * 1..SV_MAX_ROWS), y f32 [m, N] fully overwritten; N % 16 == 0,
+ * K % 128 == 0, group == 64.  Every weight byte is read from HBM once for
+ * all m rows; results are deterministic and, for integer zero points and a
+ * one-hot activation row, exactly (C - Z) * S in binary32.
+ */
+sv_status sv_qgemm_w4_packed(const void* x, int m, int K, const uint8_t* packed_codes,
+                             const void* packed_sz, int N, int group, float* y,
+                             hipStream_t stream);
+
+/*
  * sv_qgemm_w8 -- verify GEMM over 8-bit symmetric per-output-channel weights.
  *
  * Defines (Karpathy's Trick ..., "How Uzu optimizes bytes and tokens per

@@ -156,3 +156,98 @@ def test_w8_full_size_sampled(N, K):
         idx = torch.as_tensor(rows, device=DEV)
         ref = oracle.qgemm_w8(bf16_bits(x), codes[idx].cpu().numpy(), scales[idx].cpu().numpy())
         assert_rows_close(y[:, idx].cpu().numpy(), ref, what=f"w8 full m={m}")
+
+
+# ---- packed W4 layout (the streaming layout of the verify pass) --------------
+
+def _packed(codes, scales, zeros):
+    sv = _sv()
+    return sv.sv_w4_pack(*to_dev(codes, scales, zeros))
+
+
+def test_w4_pack_layout_matches_contract():
+    # the documented tile-major layout, rebuilt independently from the contract
+    N, K = 32, 256
+    codes, scales, zeros = synth.w4_matrix(N, K, seed=77)
+    pc, ps = _packed(codes, scales, zeros)
+    torch.cuda.synchronize()
+    cu = oracle.unpack_w4(codes.numpy())            # [N, K] codes in natural k order
+    pcn = pc.cpu().numpy().reshape(N // 16, K // 128, 64, 4, 4)
+    for t in range(N // 16):
+        for j in range(K // 128):
+            for l in range(64):
+                n, q = 16 * t + (l & 15), l >> 4
+                for wd in range(4):
+                    k0 = 128 * j + 64 * (wd // 2) + 16 * q + 8 * (wd % 2)
+                    exp = [cu[n, k0 + b] | (cu[n, k0 + b + 4] << 4) for b in range(4)]
+                    assert pcn[t, j, l, wd].tolist() == exp, (t, j, l, wd)
+    s, z = scales.numpy(), zeros.numpy()
+    psn = ps.cpu().numpy().reshape(N // 16, K // 128, 16, 4)
+    for t in range(N // 16):
+        for j in range(K // 128):
+            for n in range(16):
+                row = 16 * t + n
+                exp = np.array([s[row, 2 * j], z[row, 2 * j], s[row, 2 * j + 1], z[row, 2 * j + 1]])
+                assert np.array_equal(psn[t, j, n], exp)
+
+
+@pytest.mark.parametrize("m,K,N", [(4, 512, 1024),     # the tiny configuration
+                                   (1, 4096, 4096), (16, 4096, 8192), (7, 4096, 12288),
+                                   (16, 1024, 16384), (32, 4096, 24576), (17, 12288, 4096),
+                                   (3, 2176, 48), (32, 128, 16), (12, 8192, 4160)])
+def test_w4_packed_matches_oracle(m, K, N):
+    sv = _sv()
+    x, codes, scales, zeros = _w4_case(m, K, N, seed=90 + m)
+    pc, ps = _packed(codes, scales, zeros)
+    y = sv.sv_qgemm_w4_packed(x.to(DEV), pc, ps, N)
+    torch.cuda.synchronize()
+    rows = np.arange(N) if N <= 2048 else np.sort(
+        np.random.default_rng(N).choice(N, size=256, replace=False))
+    ref = _w4_oracle(x, codes, scales, zeros, rows=rows)
+    assert_rows_close(y.cpu().numpy()[:, rows], ref, what=f"w4 packed m={m} K={K} N={N}")
+
+
+@pytest.mark.parametrize("m", [1, 16, 32])
+def test_w4_packed_one_hot_rows_exact(m):
+    sv = _sv()
+    N, K = 8192, 4096
+    codes, scales, zeros = synth.w4_matrix(N, K, seed=5)
+    cols = np.random.default_rng(m).choice(K, size=m, replace=False)
+    x = torch.zeros((m, K), dtype=torch.bfloat16)
+    x[torch.arange(m), torch.as_tensor(cols)] = 1.0
+    pc, ps = _packed(codes, scales, zeros)
+    y = sv.sv_qgemm_w4_packed(x.to(DEV), pc, ps, N)
+    torch.cuda.synchronize()
+    W = oracle.dequant_w4(codes.numpy(), scales.numpy(), zeros.numpy())
+    expect = W[:, cols].T.astype(np.float32)
+    got = y.cpu().numpy()
+    bad = np.argwhere(got != expect)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+
+
+def test_w4_packed_agrees_with_row_major_entry_point():
+    sv = _sv()
+    m, K, N = 16, 4096, 12288
+    x, codes, scales, zeros = to_dev(*_w4_case(m, K, N, seed=123))
+    pc, ps = sv.sv_w4_pack(codes, scales, zeros)
+    y1 = sv.sv_qgemm_w4_packed(x, pc, ps, N)
+    y2 = sv.sv_qgemm_w4(x, codes, scales, zeros)
+    y3 = sv.sv_qgemm_w4_packed(x, pc, ps, N)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y3)                     # deterministic
+    rel = (y1 - y2).norm(dim=1) / y2.norm(dim=1)    # same product, other summation order
+    assert float(rel.max()) < 1e-5
+
+
+def test_w4_packed_argument_errors():
+    sv = _sv()
+    x, codes, scales, zeros = to_dev(*_w4_case(4, 512, 64, seed=31))
+    pc, ps = sv.sv_w4_pack(codes, scales, zeros)
+    L, vp = sv.lib, __import__("ctypes").c_void_p
+    P = lambda t, off=0: vp(t.data_ptr() + off)
+    y = torch.empty((4, 64), dtype=torch.float32, device=DEV)
+    st = vp(torch.cuda.current_stream().cuda_stream)
+    assert L.sv_qgemm_w4_packed(P(x), 4, 448, P(pc), P(ps), 64, 64, P(y), st) == 2   # K % 128
+    assert L.sv_qgemm_w4_packed(P(x), 4, 512, P(pc), P(ps), 64, 128, P(y), st) == 4  # group
+    assert L.sv_qgemm_w4_packed(P(x), 4, 512, P(pc, 8), P(ps), 64, 64, P(y), st) == 3
+    assert L.sv_w4_pack(P(codes), P(scales), P(zeros), 64, 192, 64, P(pc), P(ps), st) == 2

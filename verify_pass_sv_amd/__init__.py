@@ -11,7 +11,7 @@ _BINDING_NAMES = (
     "SvError", "lib", "lib_path", "sv_status_str", "sv_version", "sv_qgemm_w4", "sv_qgemm_w8",
     "sv_hadamard_i8", "sv_qgemm_w4_i8", "sv_verify_accept", "sv_verify_accept_workspace_bytes",
     "sv_philox4x32_10", "sv_read_bandwidth_probe", "sv_read_probe_sink_words",
-    "EXPORTED_SYMBOLS", "SV_MAX_ROWS",
+    "EXPORTED_SYMBOLS", "SV_MAX_ROWS", "sv_w4_pack", "sv_qgemm_w4_packed",
 )
 
 __all__ = list(_BINDING_NAMES)

@@ -19,6 +19,7 @@ EXPORTED_SYMBOLS = (
     "sv_status_str", "sv_version", "sv_qgemm_w4", "sv_qgemm_w8", "sv_hadamard_i8",
     "sv_qgemm_w4_i8", "sv_verify_accept_workspace_bytes", "sv_verify_accept",
     "sv_philox4x32_10", "sv_read_probe_sink_words", "sv_read_bandwidth_probe",
+    "sv_w4_packed_codes_bytes", "sv_w4_packed_sz_bytes", "sv_w4_pack", "sv_qgemm_w4_packed",
 )
 
 _STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_INVALID_ARG", 3: "SV_ERR_ALIGN",
@@ -52,6 +53,10 @@ def _load():
         "sv_philox4x32_10": (i32, [vp, vp, vp, i32, vp]),
         "sv_read_probe_sink_words": (i32, []),
         "sv_read_bandwidth_probe": (i32, [vp, sz, vp, vp]),
+        "sv_w4_packed_codes_bytes": (sz, [i32, i32]),
+        "sv_w4_packed_sz_bytes": (sz, [i32, i32, i32]),
+        "sv_w4_pack": (i32, [vp, vp, vp, i32, i32, i32, vp, vp, vp]),
+        "sv_qgemm_w4_packed": (i32, [vp, i32, i32, vp, vp, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -112,6 +117,39 @@ def sv_qgemm_w4(x, codes, scales, zeros, y=None, group=64, stream=None):
     _need(y, "y", torch.float32, (m, N))
     _check("sv_qgemm_w4", lib.sv_qgemm_w4(_ptr(x), m, K, _ptr(codes), _ptr(scales), _ptr(zeros),
                                           N, group, _ptr(y), _stream(stream)))
+    return y
+
+
+def sv_w4_pack(codes, scales, zeros, group=64, stream=None):
+    """Row-major W4 (codes [N, K/2], scales/zeros [N, K/group]) -> packed layout.
+
+    Returns (packed_codes uint8 [N*K/2], packed_sz fp16 [N*(K/group)*2]).
+    """
+    N, half = codes.shape
+    K = 2 * half
+    _need(codes, "codes", torch.uint8, (N, K // 2))
+    _need(scales, "scales", torch.float16, (N, K // group))
+    _need(zeros, "zeros", torch.float16, (N, K // group))
+    pc = torch.empty((int(lib.sv_w4_packed_codes_bytes(N, K)),), dtype=torch.uint8,
+                     device=codes.device)
+    ps = torch.empty((int(lib.sv_w4_packed_sz_bytes(N, K, group)) // 2,), dtype=torch.float16,
+                     device=codes.device)
+    _check("sv_w4_pack", lib.sv_w4_pack(_ptr(codes), _ptr(scales), _ptr(zeros), N, K, group,
+                                        _ptr(pc), _ptr(ps), _stream(stream)))
+    return pc, ps
+
+
+def sv_qgemm_w4_packed(x, packed_codes, packed_sz, N, y=None, group=64, stream=None):
+    """Y = X @ W.T over packed W4 weights (x bf16 [m, K] -> y f32 [m, N])."""
+    m, K = x.shape
+    _need(x, "x", torch.bfloat16)
+    _need(packed_codes, "packed_codes", torch.uint8, (N * K // 2,))
+    _need(packed_sz, "packed_sz", torch.float16, (N * (K // group) * 2,))
+    if y is None:
+        y = torch.empty((m, N), dtype=torch.float32, device=x.device)
+    _need(y, "y", torch.float32, (m, N))
+    _check("sv_qgemm_w4_packed", lib.sv_qgemm_w4_packed(
+        _ptr(x), m, K, _ptr(packed_codes), _ptr(packed_sz), N, group, _ptr(y), _stream(stream)))
     return y
 
 

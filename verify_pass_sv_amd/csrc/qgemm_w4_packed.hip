@@ -1,0 +1,408 @@
+// sv_w4_pack + sv_qgemm_w4_packed: the verify GEMM over 4-bit asymmetric
+// group-quantized weights stored in a tile-major layout made for gfx950.
+//
+// Source: Karpathy's Trick for Faster Local LLMs, "How Uzu optimizes bytes and
+// tokens per pass" (4-bit asymmetric integer quantization, one scale per
+// group; checkpoint format and kernels designed together) and "Why batch-one
+// decoding is memory-bound" (every weight streamed once per pass);
+// Speculative Decoding Clearly Explained, "Check the guesses together".
+//
+// Packed layout (made once from the row-major codes by sv_w4_pack):
+//   codes: for each 16-row tile t and each 128-wide k block j, one 1 KiB block
+//          at byte (t * K/128 + j) * 1024.  Bytes [16l, 16l+16) of the block
+//          belong to lane l of a wave: row 16t + (l & 15), slice q = l >> 4;
+//          bytes 0-7 hold the row's codes for k = 128j + 16q + [0, 16), bytes
+//          8-15 for k = 128j + 64 + 16q + [0, 16).  Inside each 4-byte word
+//          covering k0..k0+7, byte b holds code k0+b in its low nibble and
+//          code k0+b+4 in its high nibble, so masking the low and the high
+//          nibbles yields codes in natural k order.
+//   sz:    for each (t, j) a 128-byte block at (t * K/128 + j) * 128; row n
+//          of the tile owns 8 bytes [s(2j), z(2j), s(2j+1), z(2j+1)] (fp16).
+// A wave reads every code byte once with fully contiguous 1 KiB loads,
+// already in the lane order of the MFMA B operand.
+//
+// Kernel design (one workgroup of 8 waves per T consecutive row tiles):
+//  * Activations of each K chunk are copied once per workgroup into LDS by
+//    asynchronous global->LDS loads (global_load_lds_dwordx4) into a double
+//    buffer; all T tiles reuse them, so activation traffic per weight byte
+//    is 4m / (16 T).  The row pitch is padded by 16 bytes so the MFMA
+//    A-operand reads are bank-conflict free.
+//  * Weights are read with buffer loads at scalar offsets, one chunk ahead
+//    into a register double buffer, so HBM streams while a chunk computes.
+//  * A nibble pair becomes two bf16 values 128 + c with a mask and one byte
+//    permute against a 0x43 exponent byte (7 VALU per 8 weights).  The MFMA
+//    v_mfma_f32_16x16x32_bf16 (A = 16 draft rows, B = 16 channels) forms
+//    sum x (128 + c) per group for every tile before any of them is folded;
+//    an MFMA against all-ones gives sum x once per group for all T tiles; the
+//    fold  y += s * (acc - (128 + z) * xsum)  removes the bias and applies
+//    zero point and scale in binary32 (exact (c - z) * s for a one-hot row
+//    and integer z).
+//  * Split-K partials of the 8 waves are summed through LDS in a fixed order.
+#include "sv_common.h"
+
+namespace {
+
+constexpr int kGroup = 64;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kLdsBytes = 160 * 1024;  // gfx950 LDS per workgroup
+
+// ---- packing ----------------------------------------------------------------
+// Row-major word (byte i = codes 2i | 2i+1 << 4) -> packed word
+// (byte b = codes b | b+4 << 4).
+__device__ __forceinline__ unsigned int regroup8(unsigned int w) {
+  unsigned int out = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const unsigned int c_lo = (w >> (4 * b)) & 0xFu;        // code b
+    const unsigned int c_hi = (w >> (4 * (b + 4))) & 0xFu;  // code b + 4
+    out |= (c_lo | (c_hi << 4)) << (8 * b);
+  }
+  return out;
+}
+__global__ void pack_codes_kernel(const uint8_t* __restrict__ codes, int N, int K,
+                                  uint8_t* __restrict__ out) {
+  const size_t piece = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int KB = K / 128;
+  const size_t total = static_cast<size_t>(N / 16) * KB * 64;
+  if (piece >= total) return;
+  const int l = static_cast<int>(piece & 63);
+  const size_t blk = piece >> 6;
+  const int j = static_cast<int>(blk % KB);
+  const int t = static_cast<int>(blk / KB);
+  const int n = 16 * t + (l & 15), q = l >> 4;
+  const uint8_t* row = codes + static_cast<size_t>(n) * (K / 2);
+  const sv_u32x2 lo = sv_ld8(row + 64 * j + 8 * q);
+  const sv_u32x2 hi = sv_ld8(row + 64 * j + 32 + 8 * q);
+  sv_u32x4 v = {regroup8(lo.x), regroup8(lo.y), regroup8(hi.x), regroup8(hi.y)};
+  *reinterpret_cast<sv_u32x4*>(out + piece * 16) = v;
+}
+
+__global__ void pack_sz_kernel(const uint16_t* __restrict__ scales,
+                               const uint16_t* __restrict__ zeros, int N, int K,
+                               uint16_t* __restrict__ out) {
+  const size_t item = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int KB = K / 128, G = K / kGroup;
+  const size_t total = static_cast<size_t>(N / 16) * KB * 16;
+  if (item >= total) return;
+  const int n16 = static_cast<int>(item & 15);
+  const size_t blk = item >> 4;
+  const int j = static_cast<int>(blk % KB);
+  const int t = static_cast<int>(blk / KB);
+  const size_t src = static_cast<size_t>(16 * t + n16) * G + 2 * j;
+  uint16_t* o = out + item * 4;
+  o[0] = scales[src];
+  o[1] = zeros[src];
+  o[2] = scales[src + 1];
+  o[3] = zeros[src + 1];
+}
+
+// ---- GEMM ---------------------------------------------------------------------
+__device__ __forceinline__ unsigned int opaque_u32(unsigned int v) {
+  unsigned int r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+  return r;
+}
+
+// Packed word (byte b = codes b | b+4 << 4) -> bf16 pairs (128 + c), natural k order.
+__device__ __forceinline__ sv_u32x4 dequant8(unsigned int w, unsigned int magic) {
+  const unsigned int lo = w & 0x0F0F0F0Fu;          // codes 0..3
+  const unsigned int hi = (w >> 4) & 0x0F0F0F0Fu;   // codes 4..7
+  sv_u32x4 o;
+  o.x = __builtin_amdgcn_perm(magic, lo, 0x04010400u);
+  o.y = __builtin_amdgcn_perm(magic, lo, 0x04030402u);
+  o.z = __builtin_amdgcn_perm(magic, hi, 0x04010400u);
+  o.w = __builtin_amdgcn_perm(magic, hi, 0x04030402u);
+  return o;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding global load); the "memory" clobber keeps the
+// compiler from moving LDS accesses across it.  LDS data written by the
+// global->LDS loads is covered by the explicit vmcnt wait before it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n only.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14));
+}
+
+// MT: 16-row activation tiles (m <= 16 * MT); T: row tiles per workgroup;
+// PPW: 128-wide k blocks per wave per chunk (chunk = 8 * PPW * 128 k);
+// P: pipeline slots (P - 1 chunks in flight while one computes).
+template <int MT, int T, int PPW, int P>
+__global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
+    const uint16_t* __restrict__ x, int m, int K, const uint8_t* __restrict__ pcodes,
+    const uint16_t* __restrict__ psz, int N, float* __restrict__ y) {
+  constexpr int KC = PPW * 128 * kWaves;          // k per chunk
+  constexpr int PITCH = KC + 8;                   // bf16 per LDS row (16-byte pad)
+  constexpr int BUF = 16 * MT * PITCH;            // bf16 per LDS slot
+  constexpr int SEGS = KC / 512;                  // 1 KiB DMA pieces per row
+  constexpr int D = 16 * MT * SEGS / kWaves;      // activation DMA pieces per wave per chunk
+  constexpr int DS = (T + kWaves - 1) / kWaves;   // scale/zero DMA pieces per wave per chunk
+  constexpr int L = T * PPW + D + DS;             // loads per wave per chunk
+  constexpr int SZB = (T + 1) * 512;              // u16 per LDS slot of scales/zeros: 1 KiB per
+                                                  // tile plus 1 KiB that absorbs dummy loads
+  static_assert(PPW == 1, "one 128-wide k block per wave per chunk");
+  static_assert((16 * MT * SEGS) % kWaves == 0, "uneven DMA split");
+  static_assert(P * (BUF + SZB) * 2 <= kLdsBytes, "pipeline slots do not fit LDS");
+  static_assert(T * MT * 256 * kWaves * 4 <= kLdsBytes, "reduction does not fit LDS");
+  static_assert(L * (P - 1) < 64, "too many loads in flight for vmcnt");
+  extern __shared__ __align__(16) uint16_t lds[];
+
+  const int lane = threadIdx.x & 63;
+  // wave-uniform by construction; readfirstlane lets the compiler keep the
+  // buffer offsets derived from it in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15;
+  const int q = lane >> 4;
+  const int ntile = N / 16;
+  const int t0 = blockIdx.x * T;
+  const int KB = K / 128;
+  const int nchunk = (K + KC - 1) / KC;
+  const unsigned int magic = opaque_u32(0x43434343u);
+  const sv_u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const sv_f32x4 fz = {0.f, 0.f, 0.f, 0.f};
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(pcodes), 0, static_cast<int>(ntile * KB * 1024u), 0x00020000);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(psz), 0, static_cast<int>(ntile * KB * 128u), 0x00020000);
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x), 0, m * K * 2, 0x00020000);
+
+  sv_f32x4 yacc[T][MT];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int a = 0; a < MT; ++a) yacc[t][a] = fz;
+
+  sv_u32x4 wb[P][T][PPW];
+  uint16_t* const szl = lds + P * BUF;            // P slots of T KiB: scales/zeros
+
+  // Issue all L loads of chunk c into slot `slot`: this wave's weight blocks
+  // (registers), D pieces of the activation chunk and DS of the chunk's
+  // scale/zero blocks (1 KiB per tile: 8 k blocks x 16 rows x 8 bytes, already
+  // contiguous in the packed layout), both buffer -> LDS.  Every
+  // load is a bounds-checked buffer load, so the count is the same for every
+  // wave and step, including the steps past the last chunk, whose loads fall
+  // outside the buffers and only zero-fill registers and an idle LDS slot.
+  // That keeps the vmcnt waits below exact.
+  auto issue = [&](const int slot, int c) {
+    const bool live = c < nchunk;
+    const int jb = c * (KC / 128) + wave * PPW;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int p = 0; p < PPW; ++p) {
+        const bool ok = live && (t0 + t < ntile) && (jb + p < KB);
+        const int blk = ok ? (t0 + t) * KB + jb + p : 0x3FFFFF;   // past the end -> zeros
+        wb[slot][t][p] = __builtin_amdgcn_raw_buffer_load_b128(wrs, lane * 16, blk * 1024, 0);
+      }
+#pragma unroll
+    for (int i = 0; i < DS; ++i) {
+      const int t = wave + kWaves * i;            // this piece's tile (>= T: dummy)
+      const bool ok = live && t < T && (t0 + t < ntile);
+      const int sblk = ok ? ((t0 + t) * KB + c * (KC / 128)) * 128 : 0x7FFFFFF0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          srs, (lds_void*)(szl + slot * SZB + (t < T ? t : T) * 512), 16, lane * 16, sblk, 0, 0);
+    }
+    const int k0 = c * KC;
+    uint16_t* dst = lds + slot * BUF;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int piece = wave + kWaves * i;
+      const int r = piece / SEGS, seg = piece - r * SEGS;
+      const int rr = min(r, m - 1);                 // rows >= m re-read row m-1
+      // lanes past K land past the row (ignored) or past the buffer (zeros)
+      const int soff = live ? (rr * K + k0) * 2 : 0x7FFFFFF0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void*)(dst + r * PITCH + seg * 512), 16,
+                                               seg * 1024 + lane * 16, soff, 0, 0);
+    }
+  };
+
+  auto compute = [&](const int slot, int c) {
+    const int jb = c * (KC / 128) + wave * PPW;
+    const uint16_t* buf = lds + slot * BUF;
+    // this wave's k block inside the chunk is block `wave` of each tile's KiB
+    const uint16_t* szp = szl + slot * SZB + (wave * 16 + col) * 4;
+#pragma unroll
+    for (int p = 0; p < PPW; ++p) {
+      if (jb + p >= KB) break;
+      const int kl = (wave * PPW + p) * 128;       // k offset inside the chunk
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {                // the two groups of the block
+        sv_u32x4 a0[MT], a1[MT];
+        sv_f32x4 xs[MT];
+#pragma unroll
+        for (int a = 0; a < MT; ++a) {
+          const uint16_t* ap = buf + (col + 16 * a) * PITCH + kl + 64 * h + 16 * q;
+          a0[a] = *reinterpret_cast<const sv_u32x4*>(ap);
+          a1[a] = *reinterpret_cast<const sv_u32x4*>(ap + 8);
+          xs[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a0[a]),
+                                                          sv_as_bf16x8(ones), fz, 0, 0, 0);
+          xs[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a1[a]),
+                                                          sv_as_bf16x8(ones), xs[a], 0, 0, 0);
+        }
+        sv_f32x4 acc[T][MT];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const sv_u32x4 w = wb[slot][t][p];
+          const sv_u32x4 b0 = dequant8(h ? w.z : w.x, magic);
+          const sv_u32x4 b1 = dequant8(h ? w.w : w.y, magic);
+#pragma unroll
+          for (int a = 0; a < MT; ++a) {
+            acc[t][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                sv_as_bf16x8(a0[a]), sv_as_bf16x8(b0), fz, 0, 0, 0);
+            acc[t][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                sv_as_bf16x8(a1[a]), sv_as_bf16x8(b1), acc[t][a], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const sv_u32x2 sbt = *reinterpret_cast<const sv_u32x2*>(szp + t * 512);
+          const unsigned int sz = h ? sbt.y : sbt.x;
+          const float s = sv_half_lo(sz);
+          const float zb = 128.0f + sv_half_hi(sz);
+#pragma unroll
+          for (int a = 0; a < MT; ++a)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              yacc[t][a][i] = fmaf(s, fmaf(-zb, xs[a][i], acc[t][a][i]), yacc[t][a][i]);
+        }
+      }
+    }
+  };
+
+  // Ring of P slots: at step c the loads of chunks c+1 .. c+P-2 stay in
+  // flight while this wave waits for chunk c; the barrier then publishes
+  // chunk c's LDS data and guarantees every wave has finished chunk c-1, whose
+  // slot the issue of chunk c+P-1 reuses.  Steps run in whole rounds of P so
+  // every step issues and waits alike; only the compute is skipped past the
+  // last chunk.
+#pragma unroll
+  for (int i = 0; i < P - 1; ++i) issue(i, i);
+  for (int c0 = 0; c0 < nchunk; c0 += P) {
+#pragma unroll
+    for (int s = 0; s < P; ++s) {
+      const int c = c0 + s;
+      wait_vmcnt<L * (P - 2)>();
+      barrier_no_fence();
+      issue((s + P - 1) % P, c + P - 1);
+      if (c < nchunk) compute(s, c);
+    }
+  }
+  __syncthreads();
+
+  // Fixed-order reduction of the 8 waves' partials through LDS.
+  float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int a = 0; a < MT; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        red[(((wave * T + t) * MT + a) * 4 + i) * 64 + lane] = yacc[t][a][i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < T * MT * 256; e += kThreads) {
+    const int l = e & 63, i = (e >> 6) & 3, ta = e >> 8;
+    const int t = ta / MT, a = ta - t * MT;
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) acc += red[(((w * T + t) * MT + a) * 4 + i) * 64 + l];
+    const int r = 16 * a + 4 * (l >> 4) + i;
+    const int n = 16 * (t0 + t) + (l & 15);
+    if (r < m && t0 + t < ntile) y[static_cast<size_t>(r) * N + n] = acc;
+  }
+}
+
+template <int MT, int T>
+sv_status launch_packed(const uint16_t* x, int m, int K, const uint8_t* pc, const uint16_t* ps,
+                        int N, float* y, hipStream_t st) {
+  // Chunks of 1024 k; three LDS slots for m <= 16 (two chunks in flight),
+  // two for m <= 32 (32 activation rows per slot).
+  constexpr int PPW = 1;
+  constexpr int P = MT == 1 ? 3 : 2;
+  auto kern = qgemm_w4p_kernel<MT, T, PPW, P>;
+  // LDS: P slots of activations + scales/zeros, reused for the final reduction.
+  constexpr int kBuf = 16 * MT * (PPW * 128 * kWaves + 8) + (T + 1) * 512;
+  constexpr int kLds = (P * kBuf * 2 > T * MT * 256 * kWaves * 4) ? P * kBuf * 2
+                                                                  : T * MT * 256 * kWaves * 4;
+  const dim3 grid((N / 16 + T - 1) / T);
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess)
+    return SV_ERR_HIP;
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), kLds, st, x, m, K, pc, ps, N, y);
+  SV_LAUNCH_CHECK();
+  return SV_OK;
+}
+
+template <int MT>
+sv_status dispatch_T(int T, const uint16_t* x, int m, int K, const uint8_t* pc,
+                     const uint16_t* ps, int N, float* y, hipStream_t st) {
+  switch (T) {
+    case 1: return launch_packed<MT, 1>(x, m, K, pc, ps, N, y, st);
+    case 2: return launch_packed<MT, 2>(x, m, K, pc, ps, N, y, st);
+    case 3: return launch_packed<MT, 3>(x, m, K, pc, ps, N, y, st);
+    case 4: return launch_packed<MT, 4>(x, m, K, pc, ps, N, y, st);
+    default: return launch_packed<MT, 6>(x, m, K, pc, ps, N, y, st);
+  }
+}
+
+}  // namespace
+
+extern "C" size_t sv_w4_packed_codes_bytes(int N, int K) {
+  return static_cast<size_t>(N) * static_cast<size_t>(K) / 2;
+}
+extern "C" size_t sv_w4_packed_sz_bytes(int N, int K, int group) {
+  return group > 0 ? static_cast<size_t>(N) * static_cast<size_t>(K / group) * 4 : 0;
+}
+
+extern "C" sv_status sv_w4_pack(const uint8_t* codes, const void* scales, const void* zeros,
+                                int N, int K, int group, uint8_t* packed_codes,
+                                void* packed_sz, hipStream_t stream) {
+  if (!codes || !scales || !zeros || !packed_codes || !packed_sz) return SV_ERR_NULL;
+  if (group != kGroup) return SV_ERR_UNSUPPORTED;
+  if (N < 16 || N % 16 != 0 || K < 128 || K % 128 != 0) return SV_ERR_INVALID_ARG;
+  if (!sv_aligned16(codes) || !sv_aligned16(scales) || !sv_aligned16(zeros) ||
+      !sv_aligned16(packed_codes) || !sv_aligned16(packed_sz))
+    return SV_ERR_ALIGN;
+  const size_t pieces = static_cast<size_t>(N / 16) * (K / 128) * 64;
+  const size_t items = static_cast<size_t>(N / 16) * (K / 128) * 16;
+  hipLaunchKernelGGL(pack_codes_kernel, dim3(static_cast<unsigned>((pieces + 255) / 256)),
+                     dim3(256), 0, stream, codes, N, K, packed_codes);
+  SV_LAUNCH_CHECK();
+  hipLaunchKernelGGL(pack_sz_kernel, dim3(static_cast<unsigned>((items + 255) / 256)), dim3(256),
+                     0, stream, static_cast<const uint16_t*>(scales),
+                     static_cast<const uint16_t*>(zeros), N, K,
+                     static_cast<uint16_t*>(packed_sz));
+  SV_LAUNCH_CHECK();
+  return SV_OK;
+}
+
+extern "C" sv_status sv_qgemm_w4_packed(const void* x, int m, int K, const uint8_t* packed_codes,
+                                        const void* packed_sz, int N, int group, float* y,
+                                        hipStream_t stream) {
+  if (!x || !packed_codes || !packed_sz || !y) return SV_ERR_NULL;
+  if (m < 1 || m > SV_MAX_ROWS) return SV_ERR_INVALID_ARG;
+  if (group != kGroup) return SV_ERR_UNSUPPORTED;
+  if (N < 16 || N % 16 != 0 || K < 128 || K % 128 != 0) return SV_ERR_INVALID_ARG;
+  // Buffer-resource offsets are 32-bit: one matrix holds less than 2 GiB of codes.
+  if (static_cast<long long>(N) * K / 2 >= (1LL << 31)) return SV_ERR_UNSUPPORTED;
+  if (!sv_aligned16(x) || !sv_aligned16(packed_codes) || !sv_aligned16(packed_sz) ||
+      !sv_aligned16(y))
+    return SV_ERR_ALIGN;
+  // Row tiles per workgroup: spread the N/16 tiles over at most 256
+  // workgroups (one per compute unit) so each reuses its staged activations
+  // across as many tiles as possible.
+  const int tiles = N / 16;
+  int T = (tiles + 255) / 256;
+  T = T <= 1 ? 1 : T <= 2 ? 2 : T <= 3 ? 3 : T <= 4 ? 4 : 6;
+  const uint16_t* xs = static_cast<const uint16_t*>(x);
+  const uint16_t* ps = static_cast<const uint16_t*>(packed_sz);
+  if (m <= 16) return dispatch_T<1>(T, xs, m, K, packed_codes, ps, N, y, stream);
+  return dispatch_T<2>(T, xs, m, K, packed_codes, ps, N, y, stream);
+}
