@@ -3,17 +3,17 @@
 
 One step = one verify pass of a synthetic 9B-class decoder weight stack
 (32 layers, hidden 4096, FFN 12288; q/k/v/o 4096x4096, gate/up 4096x12288,
-down 12288x4096; W4 asymmetric, group 64) at k = 16 bf16 draft rows --
-grouped per layer as qkv, o, gate|up, down (4 dependent launches per layer)
--- followed by the accept/correct call for those k drafts over a 152000-entry
-vocabulary.  The step is captured in a HIP graph and replayed; inputs are
-resident in HBM before timing starts.
+down 12288x4096; W4 asymmetric, group 64) at k = 16 bf16 draft rows -- the
+128 GEMMs (per layer: fused qkv, o, fused gate|up, down) planned once and run
+by the pass executor in one launch -- followed by the accept/correct call for
+those k drafts over a 152000-entry vocabulary.  The step is captured in a HIP
+graph and replayed; inputs are resident in HBM before timing starts.
 
 Printed: one JSON line.  `value` is drafted tokens per second (k / step
 time).  Extra fields report the weight stream (GB/s of the W4 pass), the
-roofline of the W4 GEMM kernel, the accept latency, the k sweep (W4 and W8),
-the int8 path, accept statistics over 4096 trials per noise level, the
-measured HBM read peak, and the CPU oracle baseline.
+roofline of the pass kernel, the accept latency, the k sweep (W4 and W8), the
+per-GEMM-launch variant, the int8 path, accept statistics over 4096 trials
+per noise level, the measured HBM read peak, and the CPU oracle baseline.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--quick]
        python bench.py --profile-pass   (short run for rocprofv3 counters)
@@ -184,6 +184,16 @@ def main():
     x_f = synth.activations(32, FFN, seed=12, device=dev)
     ys = {N: torch.empty((32, N), dtype=torch.float32, device=dev)
           for N in (3 * HIDDEN, HIDDEN, 2 * FFN)}
+    # one output per GEMM of the pass (the executor runs them concurrently)
+    y_own = [[torch.empty((32, N), dtype=torch.float32, device=dev)
+              for (_, N, *_r) in layer] for layer in w4]
+
+    def w4_pass(kk):
+        xh, xf = x_h[:kk].contiguous(), x_f[:kk].contiguous()
+        gemms = [(xh if K == HIDDEN else xf, pc, ps, N, y_own[li][gi][:kk])
+                 for li, layer in enumerate(w4)
+                 for gi, (name, N, K, c, s, z, pc, ps) in enumerate(layer)]
+        return sv.sv_w4_pass_plan(gemms)
 
     def w4_launches(kk, packed=True):
         xh, xf = x_h[:kk].contiguous(), x_f[:kk].contiguous()
@@ -210,9 +220,9 @@ def main():
         dst.copy_(src)  # plain copy kernel of 256 MiB (counter scale reference)
         sink = torch.empty(sv.sv_read_probe_sink_words(), dtype=torch.int32, device=dev)
         sv.sv_read_bandwidth_probe(src, sink)
+        p = w4_pass(k)
         for _ in range(2):
-            for _, fn in w4_launches(k):
-                fn()
+            sv.sv_qgemm_w4_pass(p)
         torch.cuda.synchronize()
         log("profile pass done")
         return
@@ -224,41 +234,24 @@ def main():
                "status": torch.empty((1,), dtype=torch.int32, device=dev)}
     acc_ws = torch.empty(sv.sv_verify_accept_workspace_bytes(1, k, VOCAB), dtype=torch.uint8,
                          device=dev)
-    launches = w4_launches(k)
+    plan = w4_pass(k)
 
     def step():
-        for _, fn in launches:
-            fn()
+        sv.sv_qgemm_w4_pass(plan)
         sv.sv_verify_accept(tgt, dft, tok, seed=0, out=acc_out, workspace=acc_ws)
 
-    log("timing the step (graph replay)")
+    log(f"timing the step (graph replay); pass plan: {plan.items} items on {plan.grid} "
+        f"workgroups")
     ms_step, _ = time_graph(torch, step, args.steps, args.warmup)
 
-    def pass_only():
-        for _, fn in launches:
-            fn()
-
-    ms_pass, _ = time_graph(torch, pass_only, args.steps, args.warmup)
+    # ---- roofline of the pass kernel: one launch per pass, event-timed on
+    # the stream it runs on (graph replays of that single launch) ----
+    ms_pass, _ = time_graph(torch, lambda: sv.sv_qgemm_w4_pass(plan), args.steps, args.warmup)
     weight_gbps = pass_bytes / (ms_pass * 1e-3) / 1e9
-
-    # ---- roofline of the W4 GEMM kernel: event-timed launches of one pass ----
-    dur, cnt = per_launch_durations(torch, launches, reps=3)
-    tot_bytes = tot_ms = 0.0
-    per_shape = {}
-    for (name, N, K), d in dur.items():
-        nb = N * K // 2 + 4 * N * (K // GROUP)
-        n = cnt[(name, N, K)]
-        tot_bytes += nb * n
-        tot_ms += d * n
-        per_shape[f"{name}_{N}x{K}"] = {"us": round(d * 1e3, 2),
-                                        "GBps": round(nb / (d * 1e-3) / 1e9, 1)}
-    achieved = tot_bytes / (tot_ms * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                "kernel": "qgemm_w4p_kernel (packed layout)",
-                "bytes_per_launch_avg": int(tot_bytes / sum(cnt.values())),
-                "launch_us_avg": round(tot_ms * 1e3 / sum(cnt.values()), 2),
-                "per_shape": per_shape}
+    roofline = {"bound": "hbm", "achieved": round(weight_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(weight_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "kernel": "w4_pass_kernel (all 128 GEMMs of the pass in one launch)",
+                "bytes_per_launch": pass_bytes, "launch_us": round(ms_pass * 1e3, 2)}
 
     # ---- accept latency at k = 32 (B = 1) and throughput at B = 64 ----
     def accept_bench(B, kk):
@@ -293,15 +286,17 @@ def main():
         extra["weight_frac_of_read_probe"] = round(weight_gbps / extra["read_probe_GBps"], 4)
         del big
         log(f"read probe {extra['read_probe_GBps']} GB/s; W4 k sweep")
-        Lrm = w4_launches(k, packed=False)
-        ms_rm, _ = time_graph(torch, lambda: [fn() for _, fn in Lrm], 10, 2)
-        extra["w4_row_major_pass_ms"] = round(ms_rm, 4)
-        extra["w4_row_major_GBps"] = round(pass_bytes / (ms_rm * 1e-3) / 1e9, 1)
+        # the same pass as 128 separate launches (packed and row-major layouts)
+        for key, packed in (("w4_per_gemm_launches", True), ("w4_row_major_launches", False)):
+            Ls = w4_launches(k, packed=packed)
+            ms_l, _ = time_graph(torch, lambda Ls=Ls: [fn() for _, fn in Ls], 10, 2)
+            extra[key] = {"pass_ms": round(ms_l, 4),
+                          "GBps": round(pass_bytes / (ms_l * 1e-3) / 1e9, 1)}
         # W4 k sweep: memory-bound to MFMA crossover, latency ratio
         sweep = {}
         for kk in (1, 4, 8, 16, 32):
-            L = w4_launches(kk)
-            ms, _ = time_graph(torch, lambda L=L: [fn() for _, fn in L], 10, 2)
+            pk = w4_pass(kk)
+            ms, _ = time_graph(torch, lambda pk=pk: sv.sv_qgemm_w4_pass(pk), 10, 2)
             sweep[kk] = {"pass_ms": round(ms, 4), "GBps": round(pass_bytes / (ms * 1e-3) / 1e9, 1),
                          "drafted_tok_s": round(kk / (ms * 1e-3), 1)}
         extra["w4_k_sweep"] = sweep
@@ -338,7 +333,6 @@ def main():
                                               for key, v in hd.items()}}
         log("W8 k sweep")
         # W8 k sweep
-        del launches
         w8 = make_w8_stack(torch, synth, dev)
         b8 = w8_bytes(w8)
         sweep8 = {}
@@ -388,7 +382,7 @@ def main():
                                "32 layers (hidden 4096, ffn 12288), k=16 bf16 draft rows, "
                                "then accept/correct over V=152000",
                    "k": k, "layers": LAYERS, "hidden": HIDDEN, "ffn": FFN, "group": GROUP,
-                   "vocab": VOCAB, "launches_per_pass": 4 * LAYERS + 3,
+                   "vocab": VOCAB, "launches_per_step": 1 + 3,
                    "graph": "hipGraph replay"},
         "roofline": roofline, "cpu_baseline": cpu, **extra,
     }

@@ -133,6 +133,69 @@ sv_status sv_qgemm_w4_packed(const void* x, int m, int K, const uint8_t* packed_
                              hipStream_t stream);
 
 /*
+ * Verify-pass executor: every W4 GEMM of one verify pass in ONE launch.
+ *
+ * A pass reads every weight of the stack once for all m draft rows (Karpathy's
+ * Trick ..., "Why batch-one decoding is memory-bound": the pass time is the
+ * weight bytes divided by bandwidth; Speculative Decoding Clearly Explained,
+ * "Check the guesses together").  Launching each GEMM separately stops the
+ * HBM stream at every GEMM boundary; the executor streams all of them
+ * back to back from one persistent kernel.
+ *
+ * sv_w4_gemm describes one product Y = X * W^T with W in the packed layout of
+ * sv_w4_pack (group 64):
+ *   x             bf16 [m, K]  activations (device)
+ *   packed_codes  sv_w4_pack codes of W [N, K] (device)
+ *   packed_sz     sv_w4_pack scales/zeros of W (device)
+ *   y             f32 [m, N]   output, fully overwritten (device)
+ *   K, N          K % 128 == 0, N % 16 == 0; N*K/2, m*K*2 and m*N*4 < 2^31
+ * The GEMMs of one pass are independent: no y may overlap another GEMM's x
+ * or y (their order of execution inside the launch is unspecified).
+ *
+ * sv_w4_pass_plan_bytes(gemms, count, m): bytes of the device plan buffer,
+ *   0 if an argument is invalid.
+ * sv_w4_pass_plan(gemms, count, m, group, plan, plan_bytes, pass, stream):
+ *   validates every descriptor (SV_ERR_NULL / _INVALID_ARG / _ALIGN /
+ *   _UNSUPPORTED as for sv_qgemm_w4_packed; SV_ERR_WORKSPACE if plan_bytes is
+ *   too small), splits the GEMMs into work items of 256 output channels,
+ *   assigns them to one workgroup per compute unit of the current device,
+ *   writes the plan into `plan` (caller-owned device memory, 16-byte aligned)
+ *   and fills the host struct *pass.  This is a setup call: it copies the
+ *   plan with `stream` and synchronizes that stream before returning.
+ *   The plan stores the descriptors' pointers; it stays valid while those
+ *   buffers and `plan` live, for any number of launches.
+ * sv_qgemm_w4_pass(pass, stream): enqueues the whole pass as one kernel
+ *   launch on `stream` (capturable in a HIP graph).  A plan buffer that no
+ *   longer holds the plan described by *pass makes the kernel return without
+ *   writing anything.
+ * Results equal sv_qgemm_w4_packed's up to the order of the binary32
+ * accumulation over K (deterministic from run to run).
+ */
+typedef struct sv_w4_gemm {
+  const void* x;
+  const uint8_t* packed_codes;
+  const void* packed_sz;
+  float* y;
+  int K;
+  int N;
+} sv_w4_gemm;
+
+typedef struct sv_w4_pass {
+  void* plan;       /* device plan buffer given to sv_w4_pass_plan */
+  int m;            /* draft rows of every GEMM in the pass        */
+  int count;        /* number of GEMMs                             */
+  int grid;         /* workgroups of the launch                    */
+  int items;        /* work items over all GEMMs                   */
+  int max_steps;    /* longest per-workgroup chunk count           */
+  int reserved;
+} sv_w4_pass;
+
+size_t sv_w4_pass_plan_bytes(const sv_w4_gemm* gemms, int count, int m);
+sv_status sv_w4_pass_plan(const sv_w4_gemm* gemms, int count, int m, int group, void* plan,
+                          size_t plan_bytes, sv_w4_pass* pass, hipStream_t stream);
+sv_status sv_qgemm_w4_pass(const sv_w4_pass* pass, hipStream_t stream);
+
+/*
  * sv_qgemm_w8 -- verify GEMM over 8-bit symmetric per-output-channel weights.
  *
  * Defines (Karpathy's Trick ..., "How Uzu optimizes bytes and tokens per

@@ -76,3 +76,45 @@ def test_workspace_grows_with_batch():
     a = sv.sv_verify_accept_workspace_bytes(1, 32, 152000)
     b = sv.sv_verify_accept_workspace_bytes(64, 32, 152000)
     assert 0 < a < b
+
+
+def test_pass_plan_validation_before_any_hip_call():
+    import verify_pass_sv_amd as sv
+    L = sv.lib
+    a = 0x100000                                   # aligned, never dereferenced
+
+    def gemms(*shapes, x=a):
+        arr = (sv.SvW4Gemm * len(shapes))()
+        for i, (K, N) in enumerate(shapes):
+            arr[i] = sv.SvW4Gemm(x, a, a, a, K, N)
+        return arr
+
+    good = gemms((4096, 12288), (4096, 4096), (12288, 4096), (128, 16))
+    nb = L.sv_w4_pass_plan_bytes(good, 4, 16)
+    # header + per-workgroup tables + 48 bytes per 256-channel item
+    items = 48 + 16 + 16 + 1
+    assert nb >= items * 48 and nb < items * 48 + 64 * 1024
+    assert L.sv_w4_pass_plan_bytes(good, 4, 0) == 0
+    assert L.sv_w4_pass_plan_bytes(good, 4, 33) == 0
+    assert L.sv_w4_pass_plan_bytes(good, 0, 16) == 0
+    assert L.sv_w4_pass_plan_bytes(gemms((4096, 40)), 1, 16) == 0     # N % 16
+    assert L.sv_w4_pass_plan_bytes(gemms((4000, 64)), 1, 16) == 0     # K % 128
+    info = sv.SvW4Pass()
+    plan = ctypes.c_void_p(a)
+    assert L.sv_w4_pass_plan(good, 4, 16, 64, None, nb, ctypes.byref(info), None) == 1
+    assert L.sv_w4_pass_plan(good, 4, 16, 64, plan, nb, None, None) == 1
+    assert L.sv_w4_pass_plan(good, 4, 16, 32, plan, nb, ctypes.byref(info), None) == 4
+    assert L.sv_w4_pass_plan(good, 4, 16, 64, plan, nb - 1, ctypes.byref(info), None) == 5
+    assert L.sv_w4_pass_plan(good, 4, 16, 64, ctypes.c_void_p(a + 8), nb,
+                             ctypes.byref(info), None) == 3
+    assert L.sv_w4_pass_plan(gemms((4096, 64), x=a + 2), 1, 16, 64, plan, nb,
+                             ctypes.byref(info), None) == 3
+    assert L.sv_w4_pass_plan(gemms((4096, 64), x=0), 1, 16, 64, plan, nb,
+                             ctypes.byref(info), None) == 1
+    # a single matrix with 2 GiB of codes does not fit 32-bit buffer offsets
+    assert L.sv_w4_pass_plan_bytes(gemms((65536, 65536)), 1, 1) == 0
+    assert L.sv_qgemm_w4_pass(None, None) == 1
+    bad = sv.SvW4Pass(plan=a, m=0, count=1, grid=256, items=1, max_steps=1, reserved=0)
+    assert L.sv_qgemm_w4_pass(ctypes.byref(bad), None) == 2
+    bad = sv.SvW4Pass(plan=a, m=16, count=1, grid=0, items=1, max_steps=1, reserved=0)
+    assert L.sv_qgemm_w4_pass(ctypes.byref(bad), None) == 2

@@ -1,0 +1,185 @@
+"""GPU parity of the verify-pass executor (sv_w4_pass_plan + sv_qgemm_w4_pass).
+
+Every GEMM of a planned pass runs in one launch; each output is compared
+with the binary64 oracle (dequantize + matmul) on the same seeded inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from verify_pass_sv_amd import synth
+from gpu_util import DEV, to_dev, bf16_bits, assert_rows_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _sv():
+    import verify_pass_sv_amd as sv
+    return sv
+
+
+def _gemm(m, K, N, seed):
+    """One seeded GEMM: host copies for the oracle, device tensors for the pass."""
+    sv = _sv()
+    codes, scales, zeros = synth.w4_matrix(N, K, seed=seed)
+    x = synth.activations(m, K, seed=seed + 1)
+    pc, ps = sv.sv_w4_pack(*to_dev(codes, scales, zeros))
+    y = torch.full((m, N), float("nan"), dtype=torch.float32, device=DEV)
+    return dict(host=(x, codes, scales, zeros), dev=(x.to(DEV), pc, ps, N, y))
+
+
+def _oracle(host, rows=None):
+    x, codes, scales, zeros = host
+    c, s, z = codes.numpy(), scales.numpy(), zeros.numpy()
+    if rows is not None:
+        c, s, z = c[rows], s[rows], z[rows]
+    return oracle.qgemm_w4(bf16_bits(x), c, s, z)
+
+
+# Shapes: several chunks and item boundaries, a K that is not a multiple of the
+# 512-wide chunk, N that is not a multiple of the 256-channel item, the
+# smallest legal matrix, and more items than compute units in total.
+MIXED = [(512, 1024), (2176, 48), (640, 4160), (128, 16), (4096, 272), (1152, 8192)]
+
+
+@pytest.mark.parametrize("m", [1, 4, 16, 17, 32])
+def test_pass_matches_oracle_mixed_shapes(m):
+    sv = _sv()
+    gs = [_gemm(m, K, N, seed=300 + 10 * i + m) for i, (K, N) in enumerate(MIXED)]
+    p = sv.sv_w4_pass_plan([g["dev"] for g in gs])
+    assert p.items == sum((N // 16 + 15) // 16 for _, N in MIXED)
+    sv.sv_qgemm_w4_pass(p)
+    torch.cuda.synchronize()
+    for (K, N), g in zip(MIXED, gs):
+        y = g["dev"][4].cpu().numpy()
+        assert np.isfinite(y).all(), f"unwritten outputs K={K} N={N}"
+        rows = np.arange(N) if N <= 1024 else np.sort(
+            np.random.default_rng(N + K).choice(N, size=512, replace=False))
+        assert_rows_close(y[:, rows], _oracle(g["host"], rows),
+                          what=f"pass m={m} K={K} N={N}")
+
+
+def test_pass_tiny_configuration():
+    # one linear layer K=512, N=1024 at m=4: fewer items than compute units
+    sv = _sv()
+    g = _gemm(4, 512, 1024, seed=0)
+    p = sv.sv_w4_pass_plan([g["dev"]])
+    assert p.grid == 4 and p.items == 4
+    sv.sv_qgemm_w4_pass(p)
+    torch.cuda.synchronize()
+    assert_rows_close(g["dev"][4].cpu().numpy(), _oracle(g["host"]), what="tiny")
+
+
+@pytest.mark.parametrize("m", [1, 16, 32])
+def test_pass_one_hot_rows_exact(m):
+    # a one-hot activation row exposes single dequantized weights: exactly
+    # (c - z) * s in binary32 for integer zero points
+    sv = _sv()
+    shapes = [(4096, 4096), (1024, 2064), (12288, 512)]
+    gs, cols = [], []
+    for i, (K, N) in enumerate(shapes):
+        codes, scales, zeros = synth.w4_matrix(N, K, seed=40 + i)
+        c = np.random.default_rng(m + 7 * i).choice(K, size=m, replace=False)
+        x = torch.zeros((m, K), dtype=torch.bfloat16)
+        x[torch.arange(m), torch.as_tensor(c)] = 1.0
+        pc, ps = sv.sv_w4_pack(*to_dev(codes, scales, zeros))
+        y = torch.empty((m, N), dtype=torch.float32, device=DEV)
+        gs.append(((codes, scales, zeros), (x.to(DEV), pc, ps, N, y)))
+        cols.append(c)
+    p = sv.sv_w4_pass_plan([d for _, d in gs])
+    sv.sv_qgemm_w4_pass(p)
+    torch.cuda.synchronize()
+    for ((codes, scales, zeros), d), c in zip(gs, cols):
+        W = oracle.dequant_w4(codes.numpy(), scales.numpy(), zeros.numpy())
+        expect = W[:, c].T.astype(np.float32)
+        got = d[4].cpu().numpy()
+        bad = np.argwhere(got != expect)
+        assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+
+
+def test_pass_agrees_with_per_gemm_entry_point_and_is_deterministic():
+    sv = _sv()
+    m = 16
+    shapes = [(4096, 12288), (4096, 4096), (4096, 24576), (12288, 4096)]   # one 9B layer
+    gs = [_gemm(m, K, N, seed=500 + i) for i, (K, N) in enumerate(shapes)]
+    p = sv.sv_w4_pass_plan([g["dev"] for g in gs])
+    sv.sv_qgemm_w4_pass(p)
+    first = [g["dev"][4].clone() for g in gs]
+    sv.sv_qgemm_w4_pass(p)
+    torch.cuda.synchronize()
+    for g, y1 in zip(gs, first):
+        x, pc, ps, N, y = g["dev"]
+        assert torch.equal(y, y1)                       # deterministic
+        ref = sv.sv_qgemm_w4_packed(x, pc, ps, N)
+        torch.cuda.synchronize()
+        rel = (y - ref).norm(dim=1) / ref.norm(dim=1)   # same product, other summation order
+        assert float(rel.max()) < 1e-5
+
+
+def test_pass_in_a_graph_replays_like_eager():
+    sv = _sv()
+    gs = [_gemm(16, K, N, seed=700 + i) for i, (K, N) in enumerate([(1024, 4096), (2048, 1024)])]
+    p = sv.sv_w4_pass_plan([g["dev"] for g in gs])
+    sv.sv_qgemm_w4_pass(p)
+    torch.cuda.synchronize()
+    eager = [g["dev"][4].clone() for g in gs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            sv.sv_qgemm_w4_pass(p, stream=s)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for g in gs:
+            g["dev"][4].fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for g, e in zip(gs, eager):
+            assert torch.equal(g["dev"][4], e)
+
+
+def test_full_9b_stack_pass_sampled_channels():
+    """The 32-layer, 3.93 GB W4 stack at k = 16 in the launch configuration of
+    the benchmark (one pass, one launch); 16 sampled channels per GEMM are
+    checked against the oracle."""
+    sv = _sv()
+    H, F, m = 4096, 12288, 16
+    x_h = synth.activations(m, H, seed=11, device=DEV)
+    x_f = synth.activations(m, F, seed=12, device=DEV)
+    shapes = [(3 * H, H), (H, H), (2 * F, H), (H, F)]
+    gemms, samples = [], []
+    rng = np.random.default_rng(2024)
+    for layer in range(32):
+        for i, (N, K) in enumerate(shapes):
+            c, s, z = synth.w4_matrix(N, K, seed=1000 * layer + i, device=DEV)
+            pc, ps = sv.sv_w4_pack(c, s, z)
+            rows = np.sort(rng.choice(N, size=16, replace=False))
+            ri = torch.as_tensor(rows, device=DEV)
+            samples.append((rows, c[ri].cpu(), s[ri].cpu(), z[ri].cpu()))
+            del c, s, z
+            y = torch.full((m, N), float("nan"), dtype=torch.float32, device=DEV)
+            gemms.append((x_h if K == H else x_f, pc, ps, N, y))
+    p = sv.sv_w4_pass_plan(gemms)
+    sv.sv_qgemm_w4_pass(p)
+    torch.cuda.synchronize()
+    xb = {H: bf16_bits(x_h.cpu()), F: bf16_bits(x_f.cpu())}
+    for (x, pc, ps, N, y), (rows, c, s, z) in zip(gemms, samples):
+        K = x.shape[1]
+        got = y.cpu().numpy()
+        assert np.isfinite(got).all()
+        ref = oracle.qgemm_w4(xb[K], c.numpy(), s.numpy(), z.numpy())
+        assert_rows_close(got[:, rows], ref, what=f"stack N={N} K={K}")
+
+
+def test_pass_argument_errors():
+    sv = _sv()
+    g = _gemm(4, 512, 64, seed=31)
+    x, pc, ps, N, y = g["dev"]
+    with pytest.raises(ValueError):
+        sv.sv_w4_pass_plan([])
+    with pytest.raises(ValueError):      # rows must agree across the pass
+        sv.sv_w4_pass_plan([g["dev"], (x[:2].contiguous(), pc, ps, N, y[:2].contiguous())])
+    with pytest.raises(TypeError):
+        sv.sv_w4_pass_plan([(x.float(), pc, ps, N, y)])

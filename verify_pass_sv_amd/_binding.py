@@ -20,10 +20,25 @@ EXPORTED_SYMBOLS = (
     "sv_qgemm_w4_i8", "sv_verify_accept_workspace_bytes", "sv_verify_accept",
     "sv_philox4x32_10", "sv_read_probe_sink_words", "sv_read_bandwidth_probe",
     "sv_w4_packed_codes_bytes", "sv_w4_packed_sz_bytes", "sv_w4_pack", "sv_qgemm_w4_packed",
+    "sv_w4_pass_plan_bytes", "sv_w4_pass_plan", "sv_qgemm_w4_pass",
 )
 
 _STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_INVALID_ARG", 3: "SV_ERR_ALIGN",
            4: "SV_ERR_UNSUPPORTED", 5: "SV_ERR_WORKSPACE", 6: "SV_ERR_HIP"}
+
+
+class SvW4Gemm(ctypes.Structure):
+    """C struct sv_w4_gemm: one GEMM of a verify pass."""
+    _fields_ = [("x", ctypes.c_void_p), ("packed_codes", ctypes.c_void_p),
+                ("packed_sz", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("K", ctypes.c_int), ("N", ctypes.c_int)]
+
+
+class SvW4Pass(ctypes.Structure):
+    """C struct sv_w4_pass: host descriptor of a planned pass."""
+    _fields_ = [("plan", ctypes.c_void_p), ("m", ctypes.c_int), ("count", ctypes.c_int),
+                ("grid", ctypes.c_int), ("items", ctypes.c_int), ("max_steps", ctypes.c_int),
+                ("reserved", ctypes.c_int)]
 
 
 class SvError(RuntimeError):
@@ -57,6 +72,10 @@ def _load():
         "sv_w4_packed_sz_bytes": (sz, [i32, i32, i32]),
         "sv_w4_pack": (i32, [vp, vp, vp, i32, i32, i32, vp, vp, vp]),
         "sv_qgemm_w4_packed": (i32, [vp, i32, i32, vp, vp, i32, i32, vp, vp]),
+        "sv_w4_pass_plan_bytes": (sz, [ctypes.POINTER(SvW4Gemm), i32, i32]),
+        "sv_w4_pass_plan": (i32, [ctypes.POINTER(SvW4Gemm), i32, i32, i32, vp, sz,
+                                  ctypes.POINTER(SvW4Pass), vp]),
+        "sv_qgemm_w4_pass": (i32, [ctypes.POINTER(SvW4Pass), vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -151,6 +170,66 @@ def sv_qgemm_w4_packed(x, packed_codes, packed_sz, N, y=None, group=64, stream=N
     _check("sv_qgemm_w4_packed", lib.sv_qgemm_w4_packed(
         _ptr(x), m, K, _ptr(packed_codes), _ptr(packed_sz), N, group, _ptr(y), _stream(stream)))
     return y
+
+
+class W4Pass:
+    """A planned verify pass: the device plan, its host descriptor and the
+    tensors it points to (kept alive as long as the plan)."""
+
+    def __init__(self, plan, info, tensors):
+        self.plan = plan
+        self.info = info
+        self._tensors = tensors
+
+    @property
+    def grid(self):
+        return self.info.grid
+
+    @property
+    def items(self):
+        return self.info.items
+
+
+def _w4_gemm_array(gemms, group):
+    arr = (SvW4Gemm * len(gemms))()
+    m = None
+    keep = []
+    for i, (x, pc, ps, N, y) in enumerate(gemms):
+        mm, K = x.shape
+        m = mm if m is None else m
+        if mm != m:
+            raise ValueError("every GEMM of a pass has the same number of rows m")
+        _need(x, "x", torch.bfloat16)
+        _need(pc, "packed_codes", torch.uint8, (N * K // 2,))
+        _need(ps, "packed_sz", torch.float16, (N * (K // group) * 2,))
+        _need(y, "y", torch.float32, (m, N))
+        arr[i] = SvW4Gemm(x.data_ptr(), pc.data_ptr(), ps.data_ptr(), y.data_ptr(), K, N)
+        keep += [x, pc, ps, y]
+    return arr, m, keep
+
+
+def sv_w4_pass_plan(gemms, group=64, stream=None):
+    """Plan one verify pass over packed W4 GEMMs.
+
+    gemms: sequence of (x bf16 [m, K], packed_codes, packed_sz, N, y f32 [m, N]).
+    Returns a W4Pass for sv_qgemm_w4_pass.  Synchronizes `stream`.
+    """
+    if len(gemms) == 0:
+        raise ValueError("a pass needs at least one GEMM")
+    arr, m, keep = _w4_gemm_array(gemms, group)
+    nbytes = int(lib.sv_w4_pass_plan_bytes(arr, len(gemms), m))
+    if nbytes == 0:
+        raise SvError("sv_w4_pass_plan_bytes", 2)
+    plan = torch.empty((nbytes,), dtype=torch.uint8, device=keep[0].device)
+    info = SvW4Pass()
+    _check("sv_w4_pass_plan", lib.sv_w4_pass_plan(arr, len(gemms), m, group, _ptr(plan),
+                                                  nbytes, ctypes.byref(info), _stream(stream)))
+    return W4Pass(plan, info, keep)
+
+
+def sv_qgemm_w4_pass(w4pass, stream=None):
+    """Run every GEMM of a planned pass in one launch."""
+    _check("sv_qgemm_w4_pass", lib.sv_qgemm_w4_pass(ctypes.byref(w4pass.info), _stream(stream)))
 
 
 def sv_qgemm_w8(x, codes, scales, y=None, stream=None):

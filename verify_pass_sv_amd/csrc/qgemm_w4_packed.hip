@@ -38,7 +38,7 @@
 //    zero point and scale in binary32 (exact (c - z) * s for a one-hot row
 //    and integer z).
 //  * Split-K partials of the 8 waves are summed through LDS in a fixed order.
-#include "sv_common.h"
+#include "w4_packed_dev.h"
 
 namespace {
 
@@ -98,39 +98,6 @@ __global__ void pack_sz_kernel(const uint16_t* __restrict__ scales,
 }
 
 // ---- GEMM ---------------------------------------------------------------------
-__device__ __forceinline__ unsigned int opaque_u32(unsigned int v) {
-  unsigned int r;
-  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
-  return r;
-}
-
-// Packed word (byte b = codes b | b+4 << 4) -> bf16 pairs (128 + c), natural k order.
-__device__ __forceinline__ sv_u32x4 dequant8(unsigned int w, unsigned int magic) {
-  const unsigned int lo = w & 0x0F0F0F0Fu;          // codes 0..3
-  const unsigned int hi = (w >> 4) & 0x0F0F0F0Fu;   // codes 4..7
-  sv_u32x4 o;
-  o.x = __builtin_amdgcn_perm(magic, lo, 0x04010400u);
-  o.y = __builtin_amdgcn_perm(magic, lo, 0x04030402u);
-  o.z = __builtin_amdgcn_perm(magic, hi, 0x04010400u);
-  o.w = __builtin_amdgcn_perm(magic, hi, 0x04030402u);
-  return o;
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Workgroup barrier without the memory fence of __syncthreads (which would
-// wait for every outstanding global load); the "memory" clobber keeps the
-// compiler from moving LDS accesses across it.  LDS data written by the
-// global->LDS loads is covered by the explicit vmcnt wait before it.
-__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
-
-// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n only.
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt out of range");
-  __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14));
-}
-
 // MT: 16-row activation tiles (m <= 16 * MT); T: row tiles per workgroup;
 // PPW: 128-wide k blocks per wave per chunk (chunk = 8 * PPW * 128 k);
 // P: pipeline slots (P - 1 chunks in flight while one computes).
@@ -164,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
   const int t0 = blockIdx.x * T;
   const int KB = K / 128;
   const int nchunk = (K + KC - 1) / KC;
-  const unsigned int magic = opaque_u32(0x43434343u);
+  const unsigned int magic = sv_opaque_u32(0x43434343u);
   const sv_u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const sv_f32x4 fz = {0.f, 0.f, 0.f, 0.f};
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -187,10 +154,10 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
   // (registers), D pieces of the activation chunk and DS of the chunk's
   // scale/zero blocks (1 KiB per tile: 8 k blocks x 16 rows x 8 bytes, already
   // contiguous in the packed layout), both buffer -> LDS.  Every
-  // load is a bounds-checked buffer load, so the count is the same for every
-  // wave and step, including the steps past the last chunk, whose loads fall
-  // outside the buffers and only zero-fill registers and an idle LDS slot.
-  // That keeps the vmcnt waits below exact.
+  // load is a range-checked buffer load, so the count is the same for every
+  // wave and step, including the steps past the last chunk, whose loads carry
+  // an out-of-range offset and touch no memory (their register or LDS
+  // destinations are never consumed).  That keeps the vmcnt waits exact.
   auto issue = [&](const int slot, int c) {
     const bool live = c < nchunk;
     const int jb = c * (KC / 128) + wave * PPW;
@@ -199,16 +166,20 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
 #pragma unroll
       for (int p = 0; p < PPW; ++p) {
         const bool ok = live && (t0 + t < ntile) && (jb + p < KB);
-        const int blk = ok ? (t0 + t) * KB + jb + p : 0x3FFFFF;   // past the end -> zeros
-        wb[slot][t][p] = __builtin_amdgcn_raw_buffer_load_b128(wrs, lane * 16, blk * 1024, 0);
+        const int blk = ok ? (t0 + t) * KB + jb + p : 0;
+        wb[slot][t][p] = __builtin_amdgcn_raw_buffer_load_b128(
+            wrs, ok ? lane * 16 : kSvOutOfRange, blk * 1024, 0);
       }
 #pragma unroll
     for (int i = 0; i < DS; ++i) {
       const int t = wave + kWaves * i;            // this piece's tile (>= T: dummy)
       const bool ok = live && t < T && (t0 + t < ntile);
-      const int sblk = ok ? ((t0 + t) * KB + c * (KC / 128)) * 128 : 0x7FFFFFF0;
+      // the whole offset is per-lane so the range check also covers the
+      // tail of the last tile's last chunk
+      const unsigned int off =
+          ok ? ((t0 + t) * KB + c * (KC / 128)) * 128 + lane * 16 : kSvOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          srs, (lds_void*)(szl + slot * SZB + (t < T ? t : T) * 512), 16, lane * 16, sblk, 0, 0);
+          srs, (sv_lds_void*)(szl + slot * SZB + (t < T ? t : T) * 512), 16, off, 0, 0, 0);
     }
     const int k0 = c * KC;
     uint16_t* dst = lds + slot * BUF;
@@ -216,11 +187,13 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
     for (int i = 0; i < D; ++i) {
       const int piece = wave + kWaves * i;
       const int r = piece / SEGS, seg = piece - r * SEGS;
-      const int rr = min(r, m - 1);                 // rows >= m re-read row m-1
-      // lanes past K land past the row (ignored) or past the buffer (zeros)
-      const int soff = live ? (rr * K + k0) * 2 : 0x7FFFFFF0;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void*)(dst + r * PITCH + seg * 512), 16,
-                                               seg * 1024 + lane * 16, soff, 0, 0);
+      // rows >= m are not read (their LDS rows only feed discarded output
+      // rows); lanes past K land in the next row (ignored) or fail the range
+      // check past the end of x
+      const unsigned int off =
+          live && r < m ? (r * K + k0) * 2 + seg * 1024 + lane * 16 : kSvOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (sv_lds_void*)(dst + r * PITCH + seg * 512), 16,
+                                               off, 0, 0, 0);
     }
   };
 
@@ -251,8 +224,8 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
 #pragma unroll
         for (int t = 0; t < T; ++t) {
           const sv_u32x4 w = wb[slot][t][p];
-          const sv_u32x4 b0 = dequant8(h ? w.z : w.x, magic);
-          const sv_u32x4 b1 = dequant8(h ? w.w : w.y, magic);
+          const sv_u32x4 b0 = sv_w4_dequant8(h ? w.z : w.x, magic);
+          const sv_u32x4 b1 = sv_w4_dequant8(h ? w.w : w.y, magic);
 #pragma unroll
           for (int a = 0; a < MT; ++a) {
             acc[t][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -289,8 +262,8 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
 #pragma unroll
     for (int s = 0; s < P; ++s) {
       const int c = c0 + s;
-      wait_vmcnt<L * (P - 2)>();
-      barrier_no_fence();
+      sv_wait_vmcnt<L * (P - 2)>();
+      sv_barrier_no_fence();
       issue((s + P - 1) % P, c + P - 1);
       if (c < nchunk) compute(s, c);
     }
