@@ -91,8 +91,8 @@ def test_pass_plan_validation_before_any_hip_call():
 
     good = gemms((4096, 12288), (4096, 4096), (12288, 4096), (128, 16))
     nb = L.sv_w4_pass_plan_bytes(good, 4, 16)
-    # header + per-workgroup tables + 48 bytes per 256-channel item
-    items = 48 + 16 + 16 + 1
+    # header + per-workgroup tables + 48 bytes per 512-channel item
+    items = 24 + 8 + 8 + 1
     assert nb >= items * 48 and nb < items * 48 + 64 * 1024
     assert L.sv_w4_pass_plan_bytes(good, 4, 0) == 0
     assert L.sv_w4_pass_plan_bytes(good, 4, 33) == 0

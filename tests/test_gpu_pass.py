@@ -38,7 +38,7 @@ def _oracle(host, rows=None):
 
 
 # Shapes: several chunks and item boundaries, a K that is not a multiple of the
-# 512-wide chunk, N that is not a multiple of the 256-channel item, the
+# 256-wide chunk, N that is not a multiple of the 512-channel item, the
 # smallest legal matrix, and more items than compute units in total.
 MIXED = [(512, 1024), (2176, 48), (640, 4160), (128, 16), (4096, 272), (1152, 8192)]
 
@@ -48,7 +48,7 @@ def test_pass_matches_oracle_mixed_shapes(m):
     sv = _sv()
     gs = [_gemm(m, K, N, seed=300 + 10 * i + m) for i, (K, N) in enumerate(MIXED)]
     p = sv.sv_w4_pass_plan([g["dev"] for g in gs])
-    assert p.items == sum((N // 16 + 15) // 16 for _, N in MIXED)
+    assert p.items == sum((N // 16 + 31) // 32 for _, N in MIXED)   # 512-channel items
     sv.sv_qgemm_w4_pass(p)
     torch.cuda.synchronize()
     for (K, N), g in zip(MIXED, gs):
@@ -65,7 +65,7 @@ def test_pass_tiny_configuration():
     sv = _sv()
     g = _gemm(4, 512, 1024, seed=0)
     p = sv.sv_w4_pass_plan([g["dev"]])
-    assert p.grid == 4 and p.items == 4
+    assert p.grid == 2 and p.items == 2
     sv.sv_qgemm_w4_pass(p)
     torch.cuda.synchronize()
     assert_rows_close(g["dev"][4].cpu().numpy(), _oracle(g["host"]), what="tiny")

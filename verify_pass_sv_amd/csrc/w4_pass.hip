@@ -51,10 +51,11 @@ constexpr uint32_t kPlanVersion = 1;
 constexpr int kMaxGrid = 2048;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kNB = 4;                          // 128-wide k blocks per chunk
+constexpr int kNB = 2;                          // 128-wide k blocks per chunk
 constexpr int kKC = 128 * kNB;                  // k per chunk
-constexpr int kTW = 2;                          // row tiles per wave
-constexpr int kItemTiles = kWaves * kTW;        // row tiles per item
+constexpr int kRowBytes = 2 * kKC;              // bytes of one activation row of a chunk
+constexpr int kTW = 4;                          // row tiles per wave
+constexpr int kItemTiles = kWaves * kTW;        // row tiles per item (512 channels)
 constexpr int kGroup = 64;
 
 struct PlanHeader {                             // 64 bytes
@@ -79,30 +80,29 @@ constexpr size_t kItemsOff = (kStepsOff + sizeof(int32_t) * kMaxGrid + 63) / 64 
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// LDS bytes of one instantiation: P activation slots + P x 8 waves x 1 KiB
-// of scales/zeros.
+// LDS bytes of one instantiation: P activation slots, P scale/zero slots of
+// 1 KiB per wave, and a 1 KiB output-transpose area per wave.
 template <int MT, int P>
 constexpr int pass_lds_bytes() {
-  return P * 16 * MT * (kKC + 8) * 2 + P * kWaves * 1024;
+  return P * 16 * MT * kRowBytes + P * kWaves * 1024 + kWaves * 1024;
 }
 
 template <int MT, int P>
 __global__ __launch_bounds__(kThreads) void w4_pass_kernel(const uint8_t* __restrict__ plan,
                                                             int m) {
-  constexpr int PITCH = kKC + 8;                // bf16 per LDS activation row (16 B pad)
-  constexpr int XBUF = 16 * MT * PITCH;         // bf16 per activation slot
-  constexpr int SZW = 512;                      // u16 per wave per scale/zero slot (1 KiB)
-  constexpr int XD = 16 * MT / kWaves;          // activation rows (1 KiB each) per wave
+  constexpr int XBUF = 16 * MT * kRowBytes;     // bytes per activation slot
+  constexpr int SZBUF = kWaves * 1024;          // bytes per scale/zero slot
+  constexpr int XD = MT;                        // activation pieces (1 KiB = 2 rows) per wave
   constexpr int L = kTW * kNB + XD + 1;         // loads per wave per step
-  constexpr int NS = kTW * MT * 4;              // stores per wave per step
+  constexpr int NS = kTW * MT;                  // 16-byte stores per wave per step
   // At the wait before computing chunk c, the operations issued after chunk
   // c's loads are the stores of that same step and the loads and stores of
   // the P - 2 steps after it.
   constexpr int WAITN = NS + (P - 2) * (L + NS);
   static_assert(WAITN < 64, "too many memory operations in flight for vmcnt");
-  static_assert(kTW == 2 && kNB * 128 == 32 * 16,
-                "one 1 KiB scale/zero load per wave: 32 lanes x 16 bytes per tile");
-  extern __shared__ __align__(16) uint16_t lds[];
+  static_assert(kTW * kNB * 128 == 1024 && kRowBytes == 512,
+                "one 1 KiB scale/zero load per wave; two activation rows per 1 KiB piece");
+  extern __shared__ __align__(16) uint8_t lds[];
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(plan);
   if (hdr->magic != kPlanMagic || hdr->m != m || hdr->grid != static_cast<int>(gridDim.x))
@@ -121,7 +121,19 @@ __global__ __launch_bounds__(kThreads) void w4_pass_kernel(const uint8_t* __rest
   const unsigned int magic = sv_opaque_u32(0x43434343u);
   const sv_u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const sv_f32x4 fz = {0.f, 0.f, 0.f, 0.f};
-  uint16_t* const szl = lds + P * XBUF;
+  uint8_t* const szl = lds + P * XBUF;
+  float* const tpose = reinterpret_cast<float*>(lds + P * XBUF + P * SZBUF) + wave * 256;
+
+  // Activation rows sit in LDS at 512-byte pitch with their 16-byte columns
+  // permuted: column j of row r is stored at column j ^ (r & 15).  The 16
+  // lanes that read one MFMA operand (rows r..r+15, same column) then hit 16
+  // different bank groups.  Byte offset of this lane's A operand for group
+  // half h and k-octet e inside a 128-wide block:
+  int aoff[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) aoff[h][e] = col * kRowBytes + (((8 * h + 2 * q + e) ^ col) << 4);
 
   // ---- issue cursor: the item and chunk whose loads go out next ----
   int i_item = ib, i_c = 0;
@@ -183,25 +195,31 @@ __global__ __launch_bounds__(kThreads) void w4_pass_kernel(const uint8_t* __rest
       }
     }
     {
-      // scales/zeros of this wave's two tiles for the chunk: lanes 0-31 the
-      // first tile's kNB x 128 bytes, lanes 32-63 the second's.  Past the
-      // last k block the bytes belong to the next tile (never read).
-      const int tile = i_t0 + wave * kTW + (lane >> 5);
-      const bool ok = live && tile < ntile;
-      const unsigned int off = ok ? (tile * KB + jb) * 128 + (lane & 31) * 16 : kSvOutOfRange;
+      // scales/zeros of this wave's tiles for the chunk, one 128-byte record
+      // per (tile, k block): lane -> tile lane / 16, block (lane / 8) % 2,
+      // 16-byte piece lane % 8
+      const int tw = lane >> 4, bb = (lane >> 3) & 1;
+      const int tile = i_t0 + wave * kTW + tw;
+      const bool ok = live && tile < ntile && jb + bb < KB;
+      const unsigned int off =
+          ok ? (tile * KB + jb + bb) * 128 + (lane & 7) * 16 : kSvOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          srs, (sv_lds_void*)(szl + slot * (kWaves * SZW) + wave * SZW), 16, off, 0, 0, 0);
+          srs, (sv_lds_void*)(szl + slot * SZBUF + wave * 1024), 16, off, 0, 0, 0);
     }
     const int k0 = i_c * kKC;
 #pragma unroll
     for (int i = 0; i < XD; ++i) {
-      const int r = wave + kWaves * i;          // activation row of this piece
-      // rows >= m are not read (they only feed discarded output rows); lanes
-      // past K land in the next row (never read) or fail the range check
+      // rows 2p and 2p + 1 of the chunk; lane -> row 2p + lane / 32, stored
+      // column lane % 32, read from column (lane % 32) ^ (row % 16).  Rows
+      // >= m are not read (they only feed discarded output rows); columns
+      // past K land in the next row (never read) or fail the range check.
+      const int piece = wave + kWaves * i;
+      const int r = 2 * piece + (lane >> 5);
+      const int jj = (lane & 31) ^ (r & 15);
       const unsigned int off =
-          live && r < m ? (r * i_K + k0) * 2 + lane * 16 : kSvOutOfRange;
+          live && r < m ? (r * i_K + k0) * 2 + jj * 16 : kSvOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xrs, (sv_lds_void*)(lds + slot * XBUF + r * PITCH), 16, off, 0, 0, 0);
+          xrs, (sv_lds_void*)(lds + slot * XBUF + piece * 1024), 16, off, 0, 0, 0);
     }
   };
   auto advance_issue = [&]() {
@@ -214,8 +232,8 @@ __global__ __launch_bounds__(kThreads) void w4_pass_kernel(const uint8_t* __rest
   auto compute = [&](const int slot) {
     const int KB = c_K >> 7;
     const int jb = c_c * kNB;
-    const uint16_t* xb = lds + slot * XBUF;
-    const uint16_t* sp = szl + slot * (kWaves * SZW) + wave * SZW + col * 4;
+    const uint8_t* xb = lds + slot * XBUF;
+    const uint8_t* sp = szl + slot * SZBUF + wave * 1024 + col * 8;
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
       if (jb + b >= KB) break;
@@ -225,9 +243,9 @@ __global__ __launch_bounds__(kThreads) void w4_pass_kernel(const uint8_t* __rest
         sv_f32x4 xs[MT];
 #pragma unroll
         for (int a = 0; a < MT; ++a) {
-          const uint16_t* ap = xb + (col + 16 * a) * PITCH + b * 128 + 64 * h + 16 * q;
-          a0[a] = *reinterpret_cast<const sv_u32x4*>(ap);
-          a1[a] = *reinterpret_cast<const sv_u32x4*>(ap + 8);
+          const uint8_t* ap = xb + a * 16 * kRowBytes + b * 256;
+          a0[a] = *reinterpret_cast<const sv_u32x4*>(ap + aoff[h][0]);
+          a1[a] = *reinterpret_cast<const sv_u32x4*>(ap + aoff[h][1]);
           xs[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a0[a]),
                                                           sv_as_bf16x8(ones), fz, 0, 0, 0);
           xs[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a1[a]),
@@ -238,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void w4_pass_kernel(const uint8_t* __rest
           const sv_u32x4 w = wb[slot][tw][b];
           const sv_u32x4 b0 = sv_w4_dequant8(h ? w.z : w.x, magic);
           const sv_u32x4 b1 = sv_w4_dequant8(h ? w.w : w.y, magic);
-          const sv_u32x2 sbt = *reinterpret_cast<const sv_u32x2*>(sp + tw * kNB * 64 + b * 64);
+          const sv_u32x2 sbt = *reinterpret_cast<const sv_u32x2*>(sp + (tw * kNB + b) * 128);
           const unsigned int sz = h ? sbt.y : sbt.x;
           const float s = sv_half_lo(sz);
           const float zb = 128.0f + sv_half_hi(sz);
@@ -257,32 +275,40 @@ __global__ __launch_bounds__(kThreads) void w4_pass_kernel(const uint8_t* __rest
     }
   };
 
-  // NS stores every step: the finished item's outputs on its last chunk,
-  // out-of-range offsets otherwise.  Lane (col, q) of an MFMA output holds
-  // rows 4q .. 4q+3 (plus 16a) of channel 16 * tile + col.
+  // NS stores every step.  On an item's last chunk: each 16x16 output tile
+  // goes through the wave's LDS transpose area (lane (col, q) of an MFMA
+  // output holds rows 4q .. 4q+3 of channel col) so that lane l stores
+  // channels 4 (l % 4) .. +3 of row l / 4 as one 16-byte write.  Otherwise
+  // the same number of stores with out-of-range offsets.
   auto store = [&](const bool at_end) {
-#pragma unroll
-    for (int tw = 0; tw < kTW; ++tw) {
-      const int tile = c_t0 + wave * kTW + tw;
-      const bool ok = at_end && tile < (c_N >> 4);
-#pragma unroll
-      for (int a = 0; a < MT; ++a)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * a + 4 * q + i;
-          const unsigned int off =
-              ok && r < m ? (r * c_N + 16 * tile + col) * 4 : kSvOutOfRange;
-          // (copy the element out first: a bit cast applied directly to a
-          // vector element reads element 0 with this compiler)
-          const float v = yacc[tw][a][i];
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yrs, off, 0, 0);
-        }
-    }
     if (at_end) {
+#pragma unroll
+      for (int tw = 0; tw < kTW; ++tw) {
+        const int tile = c_t0 + wave * kTW + tw;
+#pragma unroll
+        for (int a = 0; a < MT; ++a) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tpose[(4 * q + i) * 16 + col] = yacc[tw][a][i];
+          const sv_u32x4 v =
+              *reinterpret_cast<const sv_u32x4*>(tpose + (lane >> 2) * 16 + 4 * (lane & 3));
+          const int r = 16 * a + (lane >> 2);
+          const bool ok = tile < (c_N >> 4) && r < m;
+          const unsigned int off =
+              ok ? (r * c_N + 16 * tile + 4 * (lane & 3)) * 4 : kSvOutOfRange;
+          __builtin_amdgcn_raw_buffer_store_b128(v, yrs, off, 0, 0);
+        }
+      }
 #pragma unroll
       for (int t = 0; t < kTW; ++t)
 #pragma unroll
         for (int a = 0; a < MT; ++a) yacc[t][a] = fz;
+    } else {
+#pragma unroll
+      for (int tw = 0; tw < kTW; ++tw)
+#pragma unroll
+        for (int a = 0; a < MT; ++a)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(sv_u32x4, yacc[tw][a]), yrs,
+                                                 kSvOutOfRange, 0, 0);
     }
   };
   auto advance_compute = [&]() {
@@ -466,6 +492,6 @@ extern "C" sv_status sv_qgemm_w4_pass(const sv_w4_pass* pass, hipStream_t stream
   if (pass->m < 1 || pass->m > SV_MAX_ROWS || pass->grid < 1 || pass->grid > kMaxGrid)
     return SV_ERR_INVALID_ARG;
   // Two activation tiles for m > 16; the ring keeps two chunks in flight.
-  if (pass->m <= 16) return launch_pass<1, 3>(pass->plan, pass->m, pass->grid, stream);
-  return launch_pass<2, 3>(pass->plan, pass->m, pass->grid, stream);
+  if (pass->m <= 16) return launch_pass<1, 4>(pass->plan, pass->m, pass->grid, stream);
+  return launch_pass<2, 4>(pass->plan, pass->m, pass->grid, stream);
 }
