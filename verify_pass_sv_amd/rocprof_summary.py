@@ -1,0 +1,145 @@
+"""Summarize rocprofv3 CSV output into the short text kept under profiles/.
+
+    python -m verify_pass_sv_amd.rocprof_summary \
+        --trace gpurun_out/prof_kt --pmc gpurun_out/prof_pmc \
+        --kernel w4_pass_kernel --copy-bytes 268435456 \
+        --command "<the rocprofv3 command lines>" --out profiles/<name>
+
+Reads `*_kernel_stats.csv` (rocprofv3 --kernel-trace --stats) and every
+`*_counter_collection.csv` under the PMC directory (one rocprofv3 --pmc run
+per subdirectory), and writes <name>.md (tables) and <name>.json (the
+numbers the benchmark reports: average duration of the kernel, FETCH_SIZE /
+WRITE_SIZE per dispatch scaled by what the same counters read for the plain
+copy kernel of known size, and the SHA-256 of the kernel's sources so a
+stale figure is recognised).
+"""
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+# Sources whose change makes recorded counters stale, per kernel family.
+KERNEL_SOURCES = {
+    "w4_pass_kernel": ["csrc/w4_pass.hip", "csrc/w4_packed_dev.h", "csrc/sv_common.h"],
+}
+
+
+def sources_sha256(kernel):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def short_name(name, width=72):
+    n = name.replace("(anonymous namespace)::", "")
+    return n if len(n) <= width else n[: width - 3] + "..."
+
+
+def read_stats(trace_dir):
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*_kernel_stats.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["TotalDurationNs"]) / 1e3, float(r["Percentage"])))
+    rows.sort(key=lambda r: -r[3])
+    return rows
+
+
+def read_counters(pmc_dir):
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*_counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            agg[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in agg.items()}
+
+
+def pick(d, key):
+    for name, val in d.items():
+        if key in name:
+            return name, val
+    raise KeyError(f"no kernel matching {key!r}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--pmc", required=True)
+    ap.add_argument("--kernel", required=True, help="substring of the kernel of interest")
+    ap.add_argument("--copy-bytes", type=int, required=True,
+                    help="bytes read (and written) by the plain copy kernel in the run")
+    ap.add_argument("--algo-bytes", type=float, required=True,
+                    help="algorithmic bytes per dispatch of the kernel of interest")
+    ap.add_argument("--command", required=True)
+    ap.add_argument("--title", required=True)
+    ap.add_argument("--out", required=True, help="output path without extension")
+    a = ap.parse_args()
+
+    stats = read_stats(a.trace)
+    kname, kstat = None, None
+    for r in stats:
+        if a.kernel in r[0]:
+            kname, kstat = r[0], r
+            break
+    cnt = read_counters(a.pmc)
+    kc_name, kc = pick(cnt, a.kernel)
+    _, cc = pick(cnt, COPY_KERNEL)
+    copy_kib = a.copy_bytes / 1024.0
+    f_fetch = copy_kib / cc["FETCH_SIZE"]
+    f_write = copy_kib / cc["WRITE_SIZE"]
+    fetch_b = kc["FETCH_SIZE"] * f_fetch * 1024
+    write_b = kc["WRITE_SIZE"] * f_write * 1024
+    avg_us = kstat[2]
+    out = {
+        "kernel": short_name(kname, 200),
+        "sources_sha256": sources_sha256(a.kernel.split("<")[0]),
+        "avg_duration_us": round(avg_us, 3),
+        "calls": kstat[1],
+        "algorithmic_bytes": a.algo_bytes,
+        "achieved_GBps_rocprof": round(a.algo_bytes / (avg_us * 1e-6) / 1e9, 1),
+        "fetch_size_kib_per_dispatch": round(kc["FETCH_SIZE"], 1),
+        "write_size_kib_per_dispatch": round(kc["WRITE_SIZE"], 1),
+        "copy_kernel_bytes": a.copy_bytes,
+        "copy_fetch_scale": round(f_fetch, 4),
+        "copy_write_scale": round(f_write, 4),
+        "traffic_bytes": round(fetch_b + write_b),
+        "traffic_read_bytes": round(fetch_b),
+        "traffic_write_bytes": round(write_b),
+        "counters": {k: round(v, 1) for k, v in sorted(kc.items())},
+    }
+    with open(a.out + ".json", "w") as f:
+        json.dump(out, f, indent=1)
+    L = [f"# {a.title}", "", "Commands (run from /tmp with TMPDIR=/tmp; one PMC pass per run):", "",
+         "```", a.command.strip(), "```", "",
+         "## Kernel trace (rocprofv3 --kernel-trace --stats), top kernels", "",
+         "| kernel | calls | avg us | total us | % |", "|---|---:|---:|---:|---:|"]
+    for r in stats[:12]:
+        L.append(f"| `{short_name(r[0])}` | {r[1]} | {r[2]:.2f} | {r[3]:.1f} | {r[4]:.2f} |")
+    L += ["", f"## `{short_name(kname)}`", "",
+          f"- average duration: **{avg_us:.1f} us** over {kstat[1]} dispatches",
+          f"- algorithmic bytes per dispatch: {a.algo_bytes:.4g} -> "
+          f"{out['achieved_GBps_rocprof']} GB/s",
+          f"- FETCH_SIZE {kc['FETCH_SIZE']:.0f} KiB x {f_fetch:.4f} (copy-kernel scale: "
+          f"{a.copy_bytes} B copy read as {cc['FETCH_SIZE']:.0f} KiB) = {fetch_b:.4g} B",
+          f"- WRITE_SIZE {kc['WRITE_SIZE']:.0f} KiB x {f_write:.4f} (copy wrote "
+          f"{cc['WRITE_SIZE']:.0f} KiB) = {write_b:.4g} B",
+          f"- HBM traffic per dispatch: **{fetch_b + write_b:.4g} B** "
+          f"({(fetch_b + write_b) / a.algo_bytes:.3f} x algorithmic)",
+          f"- sources SHA-256: `{out['sources_sha256']}`", "",
+          "| counter | per dispatch |", "|---|---:|"]
+    for c, v in sorted(kc.items()):
+        L.append(f"| {c} | {v:.4g} |")
+    with open(a.out + ".md", "w") as f:
+        f.write("\n".join(L) + "\n")
+    print(json.dumps({k: out[k] for k in ("avg_duration_us", "traffic_bytes",
+                                          "achieved_GBps_rocprof")}))
+
+
+if __name__ == "__main__":
+    main()
