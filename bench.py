@@ -15,7 +15,7 @@ roofline of the pass kernel, the accept latency, the k sweep (W4 and W8), the
 per-GEMM-launch variant, the int8 path, accept statistics over 4096 trials
 per noise level, the measured HBM read peak, and the CPU oracle baseline.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--quick]
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 200] [--quick]
        python bench.py --profile-pass   (short run for rocprofv3 counters)
 """
 import argparse
@@ -174,8 +174,10 @@ def cpu_baseline(k=16):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # The clock and power controller of the GPU settles over a few hundred
+    # passes; the defaults time the settled state (about 0.4 s in total).
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--k", type=int, default=16)
     ap.add_argument("--quick", action="store_true", help="skip sweeps, stats and cpu baseline")
     ap.add_argument("--no-cpu", action="store_true")
@@ -266,7 +268,7 @@ def main():
     # own launch latency) ----
     REPS = 8
     ms_rep, _ = time_graph(torch, lambda: [sv.sv_qgemm_w4_pass(plan) for _ in range(REPS)],
-                           max(2, args.steps // 4), 1)
+                           max(2, args.steps // REPS), max(1, args.warmup // REPS))
     ms_pass = ms_rep / REPS
     weight_gbps = pass_bytes / (ms_pass * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(weight_gbps, 1), "peak": HBM_PEAK_GBPS,

@@ -110,22 +110,34 @@ __device__ __forceinline__ void stat_merge(float& m, float& s, float m2, float s
   m = mm;
 }
 
-__host__ __device__ inline int stat_chunks(int B, int k, int V) {
-  const long long rows = static_cast<long long>(B) * (2 * k + 1);
-  long long c = (2048 + rows - 1) / rows;
-  long long cmax = V / 2048;
-  if (cmax < 1) cmax = 1;
-  if (cmax > 64) cmax = 64;
-  if (c > cmax) c = cmax;
-  return static_cast<int>(c < 1 ? 1 : c);
-}
+// Vocabulary tiling shared by the kernels.
+//  * Statistics: each row is cut into C1 <= kMaxC1 spans of whole 2048-float
+//    batches; one wave reduces one (trial, row, span).
+//  * Residual: the vocabulary is cut into blocks of kBlk floats; block
+//    totals, and inside a block 16 groups of 16 thread ranges of 8 floats,
+//    are summed in one fixed order everywhere, so the inverse-CDF search of
+//    kernel 3 walks exactly the sums that kernel 2 produced.
+constexpr int kBatch = 2048;                    // floats per wave per statistics batch
+constexpr int kMaxC1 = 80;                      // statistics spans per row
+constexpr int kBlk = 2048;                      // floats per residual block
+constexpr int kPerThread = kBlk / kThreads;     // 8
+constexpr int kGroups = 16;                     // thread groups per block
+constexpr int kGroupThreads = kThreads / kGroups;
 
-__host__ __device__ inline int resid_chunks(int B, int V) {
+__host__ __device__ inline int stat_spans(int V) {
+  const int batches = (V + kBatch - 1) / kBatch;
+  return batches < kMaxC1 ? batches : kMaxC1;
+}
+__host__ __device__ inline int stat_span_len(int V, int C1) {
+  const int batches = (V + kBatch - 1) / kBatch;
+  return ((batches + C1 - 1) / C1) * kBatch;
+}
+__host__ __device__ inline int resid_blocks(int V) { return (V + kBlk - 1) / kBlk; }
+// Workgroups of kernel 2 per trial: enough for about 256 in total.
+__host__ __device__ inline int resid_wgs(int B, int V) {
   long long c = (256 + static_cast<long long>(B) - 1) / B;
-  long long cmax = V / 2048;
-  if (cmax < 1) cmax = 1;
-  if (cmax > 64) cmax = 64;
-  if (c > cmax) c = cmax;
+  const long long nb = resid_blocks(V);
+  if (c > nb) c = nb;
   return static_cast<int>(c < 1 ? 1 : c);
 }
 
@@ -138,9 +150,9 @@ __host__ inline WsLayout ws_layout(int B, int k, int V) {
   WsLayout L;
   const size_t R = 2 * static_cast<size_t>(k) + 1;
   L.partial_off = 0;
-  L.decision_off = up(static_cast<size_t>(B) * R * stat_chunks(B, k, V) * sizeof(StatPartial));
+  L.decision_off = up(static_cast<size_t>(B) * R * stat_spans(V) * sizeof(StatPartial));
   L.total_off = L.decision_off + up(static_cast<size_t>(B) * sizeof(Decision));
-  L.bytes = L.total_off + up(static_cast<size_t>(B) * resid_chunks(B, V) * sizeof(double));
+  L.bytes = L.total_off + up(static_cast<size_t>(B) * resid_blocks(V) * sizeof(double));
   return L;
 }
 
@@ -150,11 +162,13 @@ __device__ __forceinline__ const float* row_ptr(const float* tgt, const float* d
   return dft + (static_cast<size_t>(b) * k + (j - k - 1)) * V;
 }
 
-// ---- kernel 1: per-chunk softmax statistics --------------------------------
+// ---- kernel 1: per-span softmax statistics ---------------------------------
+// All loads of a 2048-float batch are issued before any is used (8 float4 or
+// 32 floats per lane), so a wave pays one memory latency per batch.
 template <bool VEC>
 __global__ __launch_bounds__(64 * kStatsWaves) void stats_kernel(
     const float* __restrict__ tgt, const float* __restrict__ dft, int B, int k, int V, int C1,
-    StatPartial* __restrict__ part) {
+    int span, StatPartial* __restrict__ part) {
   const int lane = threadIdx.x & 63;
   const long long item = static_cast<long long>(blockIdx.x) * kStatsWaves + (threadIdx.x >> 6);
   const int R = 2 * k + 1;
@@ -164,17 +178,47 @@ __global__ __launch_bounds__(64 * kStatsWaves) void stats_kernel(
   const int j = static_cast<int>(br % R);
   const int b = static_cast<int>(br / R);
   const float* row = row_ptr(tgt, dft, b, j, k, V);
-  int L = (V + C1 - 1) / C1;
-  L = (L + 3) & ~3;
-  const int lo = min(V, c * L);
-  const int hi = min(V, lo + L);
+  const int lo = min(V, c * span);
+  const int hi = min(V, lo + span);
   float m = -INFINITY, s = 0.f;
   int bad = 0;
-  if (VEC) {
-    for (int i = lo + lane * 4; i < hi; i += 256)
-      stat_add4(m, s, bad, *reinterpret_cast<const float4*>(row + i));
-  } else {
-    for (int i = lo + lane; i < hi; i += 64) stat_add1(m, s, bad, row[i]);
+  for (int base = lo; base < hi; base += kBatch) {
+    constexpr int NV = VEC ? kBatch / 256 : kBatch / 64;
+    float v[VEC ? 4 * NV : NV];
+    if (VEC) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int e = base + 256 * i + 4 * lane;
+        float4 t = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        if (e < hi) t = *reinterpret_cast<const float4*>(row + e);
+        v[4 * i] = t.x;
+        v[4 * i + 1] = t.y;
+        v[4 * i + 2] = t.z;
+        v[4 * i + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int e = base + 64 * i + lane;
+        v[i] = e < hi ? row[e] : -INFINITY;
+      }
+    }
+    float vm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < (VEC ? 4 * NV : NV); ++i) {
+      bad |= (v[i] != v[i]) | (v[i] == INFINITY);
+      vm = fmaxf(vm, v[i]);
+    }
+    if (vm > m) {
+      s *= exp2_fast((m - vm) * kLog2e);
+      m = vm;
+    }
+    if (m != -INFINITY) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < (VEC ? 4 * NV : NV); ++i) acc += exp2_fast((v[i] - m) * kLog2e);
+      s += acc;
+    }
   }
   for (int off = 32; off > 0; off >>= 1) {
     const float m2 = __shfl_xor(m, off);
@@ -185,36 +229,66 @@ __global__ __launch_bounds__(64 * kStatsWaves) void stats_kernel(
   if (lane == 0) part[item] = StatPartial{m, s, bad, 0};
 }
 
-// Residual / bonus weight of vocab entry v (binary32), shared by kernels 2
-// and 3 so that both see bit-identical weights.
-__device__ __noinline__ float resid_weight(const float* pt, float lt, const float* pd, float ld,
-                                           int v) {
-  const float p = expf(pt[v] - lt);
-  if (pd == nullptr) return p;
-  const float q = expf(pd[v] - ld);
+// Residual / bonus weight of one vocabulary entry from its two logits
+// (binary32), shared by kernels 2 and 3 so that both see bit-identical
+// weights.
+__device__ __noinline__ float resid_weight(float tl, float lt, float dl, float ld, bool bonus) {
+  const float p = expf(tl - lt);
+  if (bonus) return p;
+  const float q = expf(dl - ld);
   return fmaxf(0.f, p - q);
 }
 
-__device__ __noinline__ double range_sum(const float* pt, float lt, const float* pd, float ld,
-                                         int a, int e) {
+// Stages block `blk` of the residual rows (target row pt, draft row pd) into
+// LDS: every thread issues its 2 x 8 coalesced loads before storing any.
+__device__ __forceinline__ void stage_block(const float* pt, const float* pd, int V, int blk,
+                                            float* st, float* sd) {
+  const int lo = blk * kBlk;
+  float a[kPerThread], d[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int e = lo + i * kThreads + threadIdx.x;
+    a[i] = e < V ? pt[e] : -INFINITY;
+    d[i] = (pd != nullptr && e < V) ? pd[e] : -INFINITY;
+  }
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    st[i * kThreads + threadIdx.x] = a[i];
+    sd[i * kThreads + threadIdx.x] = d[i];
+  }
+}
+
+// Sum of this thread's 8 consecutive weights of the staged block, in order.
+__device__ __forceinline__ double thread_sum(const float* st, const float* sd, int n_valid,
+                                             float lt, float ld, bool bonus) {
   double acc = 0.0;
-  for (int v = a; v < e; ++v) acc += static_cast<double>(resid_weight(pt, lt, pd, ld, v));
+  const int a = threadIdx.x * kPerThread;
+  for (int v = a; v < a + kPerThread && v < n_valid; ++v)
+    acc += static_cast<double>(resid_weight(st[v], lt, sd[v], ld, bonus));
   return acc;
 }
 
-__device__ __forceinline__ void chunk_range(int V, int C2, int c, int& lo, int& hi) {
-  const int L = (V + C2 - 1) / C2;
-  lo = min(V, c * L);
-  hi = min(V, lo + L);
+// Group sums (16 consecutive threads, in order) and the block total (groups
+// in order) from the per-thread sums in tsum; gsum receives the group sums.
+__device__ __forceinline__ void block_sums(const double* tsum, double* gsum, double* total) {
+  if (threadIdx.x < kGroups) {
+    double g = 0.0;
+    for (int t = 0; t < kGroupThreads; ++t) g += tsum[threadIdx.x * kGroupThreads + t];
+    gsum[threadIdx.x] = g;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double T = 0.0;
+    for (int g = 0; g < kGroups; ++g) T += gsum[g];
+    *total = T;
+  }
+  __syncthreads();
 }
 
-__device__ __forceinline__ void thread_range(int lo, int hi, int t, int& a, int& e) {
-  const long long len = hi - lo;
-  a = lo + static_cast<int>(len * t / kThreads);
-  e = lo + static_cast<int>(len * (t + 1) / kThreads);
-}
-
-// ---- kernel 2: decide + residual chunk totals ------------------------------
+// ---- kernel 2: decide + residual block totals ------------------------------
+// Every workgroup of a trial merges the trial's statistics and takes the same
+// decisions (identical inputs and order); workgroup 0 writes the per-trial
+// outputs.  Then each workgroup sums its share of the residual blocks.
 __global__ __launch_bounds__(kThreads) void decide_kernel(
     const float* __restrict__ tgt, const float* __restrict__ dft, const int32_t* __restrict__ toks,
     int B, int k, int V, int C1, int C2, unsigned int key0, unsigned int key1, unsigned int offset,
@@ -222,29 +296,85 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_n_acc,
     int32_t* __restrict__ out_status, float* __restrict__ p_at, float* __restrict__ q_at,
     float* __restrict__ lse_out) {
+  __shared__ float pm[(2 * SV_MAX_ROWS + 1) * kMaxC1];
+  __shared__ float ps[(2 * SV_MAX_ROWS + 1) * kMaxC1];
+  __shared__ int pb[(2 * SV_MAX_ROWS + 1) * kMaxC1];
   __shared__ float lse_sh[2 * SV_MAX_ROWS + 1];
+  __shared__ float row_m[2 * SV_MAX_ROWS + 1];
   __shared__ int bad_sh[2 * SV_MAX_ROWS + 1];
+  __shared__ float red_m[kThreads];
+  __shared__ int red_b[kThreads];
   __shared__ Decision dec;
+  __shared__ float st[kBlk], sd[kBlk];
   __shared__ double tsum[kThreads];
+  __shared__ double gsum[kGroups];
+  __shared__ double btot;
   const int b = blockIdx.x / C2;
   const int c = blockIdx.x % C2;
   const int R = 2 * k + 1;
   const int tid = threadIdx.x;
 
-  if (tid < R) {
-    const StatPartial* pp = part + (static_cast<size_t>(b) * R + tid) * C1;
-    float m = -INFINITY, s = 0.f;
-    int bad = 0;
-    for (int i = 0; i < C1; ++i) {
-      bad |= pp[i].bad;
-      stat_merge(m, s, pp[i].m, pp[i].s);
+  // 1. the trial's R x C1 statistics partials -> LDS (coalesced)
+  {
+    const StatPartial* pp = part + static_cast<size_t>(b) * R * C1;
+    const int n = R * C1;
+#pragma unroll 4
+    for (int e = tid; e < n; e += kThreads) {
+      const StatPartial q = pp[e];
+      pm[e] = q.m;
+      ps[e] = q.s;
+      pb[e] = q.bad;
     }
-    bad |= (m == -INFINITY) || !(s > 0.f);
-    lse_sh[tid] = bad ? NAN : m + logf(s);
-    bad_sh[tid] = bad;
+  }
+  __syncthreads();
+  // 2. merge each row's spans: TPR threads per row take every TPR-th span;
+  //    the row maximum first, then the sum rescaled to it, each combined
+  //    across the row's threads in a fixed order
+  {
+    const int TPR = R >= kThreads ? 1 : kThreads / R;
+    const int j = tid / TPR, sub = tid - j * TPR;
+    const bool own = j < R;
+    float m = -INFINITY;
+    int bad = 0;
+    if (own) {
+      for (int i = sub; i < C1; i += TPR) {
+        m = fmaxf(m, pm[j * C1 + i]);
+        bad |= pb[j * C1 + i];
+      }
+      red_m[tid] = m;
+      red_b[tid] = bad;
+    }
+    __syncthreads();
+    if (own && sub == 0) {
+      for (int t = 1; t < TPR; ++t) {
+        m = fmaxf(m, red_m[tid + t]);
+        bad |= red_b[tid + t];
+      }
+      row_m[j] = m;
+      bad_sh[j] = bad;
+    }
+    __syncthreads();
+    if (own) {
+      const float mr = row_m[j];
+      float sum = 0.f;
+      if (mr != -INFINITY)
+        for (int i = sub; i < C1; i += TPR)
+          sum += ps[j * C1 + i] * exp2_fast((pm[j * C1 + i] - mr) * kLog2e);
+      red_m[tid] = sum;
+    }
+    __syncthreads();
+    if (own && sub == 0) {
+      const float mr = row_m[j];
+      float sum = 0.f;
+      for (int t = 0; t < TPR; ++t) sum += red_m[tid + t];
+      const int bd = bad_sh[j] | (mr == -INFINITY) | !(sum > 0.f);
+      lse_sh[j] = bd ? NAN : mr + logf(sum);
+      bad_sh[j] = bd;
+    }
   }
   __syncthreads();
 
+  // 3. decisions (wave 0): accept iff u_i q_i(d_i) < p_i(d_i), first rejection
   if (tid < 64) {
     const int i = tid;
     const bool has_draft = i < k;
@@ -307,34 +437,40 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
   __syncthreads();
   if (c == 0 && tid == 0) decs[b] = dec;
 
-  double* tot = totals + static_cast<size_t>(b) * C2 + c;
+  // 4. residual block totals of this workgroup's blocks
+  const int nb = resid_blocks(V);
+  const int b0 = static_cast<int>(static_cast<long long>(nb) * c / C2);
+  const int b1 = static_cast<int>(static_cast<long long>(nb) * (c + 1) / C2);
+  double* tot = totals + static_cast<size_t>(b) * nb;
   if (dec.status != 0) {
-    if (tid == 0) *tot = 0.0;
+    for (int blk = b0 + tid; blk < b1; blk += kThreads) tot[blk] = 0.0;
     return;
   }
   const int r = dec.n_acc;
+  const bool bonus = r == k;
   const float* pt = tgt + (static_cast<size_t>(b) * (k + 1) + r) * V;
-  const float* pd = r < k ? dft + (static_cast<size_t>(b) * k + r) * V : nullptr;
-  int lo, hi, a, e;
-  chunk_range(V, C2, c, lo, hi);
-  thread_range(lo, hi, tid, a, e);
-  tsum[tid] = range_sum(pt, dec.lse_t, pd, dec.lse_d, a, e);
-  __syncthreads();
-  if (tid == 0) {
-    double acc = 0.0;
-    for (int t = 0; t < kThreads; ++t) acc += tsum[t];
-    *tot = acc;
+  const float* pd = bonus ? nullptr : dft + (static_cast<size_t>(b) * k + r) * V;
+  for (int blk = b0; blk < b1; ++blk) {
+    stage_block(pt, pd, V, blk, st, sd);
+    __syncthreads();
+    tsum[tid] = thread_sum(st, sd, min(kBlk, V - blk * kBlk), dec.lse_t, dec.lse_d, bonus);
+    __syncthreads();
+    block_sums(tsum, gsum, &btot);
+    if (tid == 0) tot[blk] = btot;
   }
 }
 
 // ---- kernel 3: select the replacement / bonus token ------------------------
 __global__ __launch_bounds__(kThreads) void select_kernel(
-    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V, int C2,
+    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V,
     const Decision* __restrict__ decs, const double* __restrict__ totals,
     int32_t* __restrict__ out_tokens) {
+  __shared__ float st[kBlk], sd[kBlk];
   __shared__ double tsum[kThreads];
-  __shared__ double sh_thr, sh_pc, sh_qt;
-  __shared__ int sh_c, sh_t, sh_usep;
+  __shared__ double gsum[kGroups];
+  __shared__ double btot;
+  __shared__ double sh_S, sh_pc;
+  __shared__ int sh_blk, sh_usep;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const Decision dec = decs[b];
@@ -342,98 +478,115 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   const int r = dec.n_acc;
   const float* pt = tgt + (static_cast<size_t>(b) * (k + 1) + r) * V;
   const float* pd = r < k ? dft + (static_cast<size_t>(b) * k + r) * V : nullptr;
+  bool bonus = r == k;
+  const int nb = resid_blocks(V);
+  const double* T = totals + static_cast<size_t>(b) * nb;
 
+  // block totals -> LDS in one parallel pass (dyn_tot), then summed in order
+  extern __shared__ double dyn_tot[];   // nb doubles
+  for (int i = tid; i < nb; i += kThreads) dyn_tot[i] = T[i];
+  __syncthreads();
   if (tid == 0) {
-    const double* T = totals + static_cast<size_t>(b) * C2;
     double S = 0.0;
-    for (int c = 0; c < C2; ++c) S += T[c];
+    for (int i = 0; i < nb; ++i) S += dyn_tot[i];
+    sh_S = S;
     sh_usep = !(S > 0.0);
   }
   __syncthreads();
+  // Rounding left no residual mass: sample from p_r instead, with block
+  // totals recomputed here (a rare path, so one block at a time).
   const bool usep = sh_usep != 0;
-  if (usep) pd = nullptr;  // rounding left no residual mass: sample from p_r
-
-  // Chunk totals: from kernel 2, or recomputed here for the p_r fallback.
-  double* ctot = nullptr;
-  __shared__ double ctot_sh[64];
   if (usep) {
-    for (int c = 0; c < C2; ++c) {
-      int lo, hi, a, e;
-      chunk_range(V, C2, c, lo, hi);
-      thread_range(lo, hi, tid, a, e);
-      tsum[tid] = range_sum(pt, dec.lse_t, pd, dec.lse_d, a, e);
+    bonus = true;
+    pd = nullptr;
+    for (int blk = 0; blk < nb; ++blk) {
+      stage_block(pt, pd, V, blk, st, sd);
       __syncthreads();
-      if (tid == 0) {
-        double acc = 0.0;
-        for (int t = 0; t < kThreads; ++t) acc += tsum[t];
-        ctot_sh[c] = acc;
-      }
+      tsum[tid] = thread_sum(st, sd, min(kBlk, V - blk * kBlk), dec.lse_t, dec.lse_d, true);
+      __syncthreads();
+      block_sums(tsum, gsum, &btot);
+      if (tid == 0) dyn_tot[blk] = btot;
       __syncthreads();
     }
-    ctot = ctot_sh;
   }
+  T = dyn_tot;
   if (tid == 0) {
-    const double* T = usep ? ctot : totals + static_cast<size_t>(b) * C2;
     double S = 0.0;
-    for (int c = 0; c < C2; ++c) S += T[c];
+    for (int i = 0; i < nb; ++i) S += T[i];
     const double thr = dec.u2 * S;
-    double P = 0.0;
-    int cs = C2 - 1;
-    double pc = 0.0;
-    for (int c = 0; c < C2; ++c) {
-      const double nxt = P + T[c];
+    double P = 0.0, pc = 0.0;
+    int bs = nb - 1;
+    for (int i = 0; i < nb; ++i) {
+      const double nxt = P + T[i];
       if (nxt > thr) {
-        cs = c;
+        bs = i;
         pc = P;
         break;
       }
       P = nxt;
       pc = P;
     }
-    sh_thr = thr;
-    sh_c = cs;
+    sh_S = thr;
+    sh_blk = bs;
     sh_pc = pc;
   }
   __syncthreads();
-  const double thr = sh_thr, pc = sh_pc;
-  int lo, hi, a, e;
-  chunk_range(V, C2, sh_c, lo, hi);
-  thread_range(lo, hi, tid, a, e);
-  tsum[tid] = range_sum(pt, dec.lse_t, pd, dec.lse_d, a, e);
+  const double thr = sh_S, pc = sh_pc;
+  const int blk = sh_blk;
+  const int n_valid = min(kBlk, V - blk * kBlk);
+  stage_block(pt, pd, V, blk, st, sd);
   __syncthreads();
+  tsum[tid] = thread_sum(st, sd, n_valid, dec.lse_t, dec.lse_d, bonus);
+  __syncthreads();
+  block_sums(tsum, gsum, &btot);
   if (tid == 0) {
-    double Q = 0.0;
-    int ts = kThreads - 1;
-    double qt = 0.0;
-    for (int t = 0; t < kThreads; ++t) {
-      const double nxt = Q + tsum[t];
-      if (pc + nxt > thr) {
-        ts = t;
-        qt = Q;
-        break;
+    // groups, then threads inside the group, then the thread's 8 entries;
+    // every comparison is pc + (group prefix + (thread prefix + run)), the
+    // association under which the block total was formed
+    int gs = kGroups - 1;
+    double qg = 0.0;
+    {
+      double Q = 0.0;
+      for (int g = 0; g < kGroups; ++g) {
+        const double nxt = Q + gsum[g];
+        if (pc + nxt > thr) {
+          gs = g;
+          qg = Q;
+          break;
+        }
+        Q = nxt;
+        qg = Q;
       }
-      Q = nxt;
-      qt = Q;
     }
-    sh_t = ts;
-    sh_qt = qt;
-  }
-  __syncthreads();
-  if (tid == sh_t) {
-    const double qt = sh_qt;
+    int ts = gs * kGroupThreads + kGroupThreads - 1;
+    double qt = 0.0;
+    {
+      double Q = 0.0;
+      for (int t = 0; t < kGroupThreads; ++t) {
+        const double nxt = Q + tsum[gs * kGroupThreads + t];
+        if (pc + (qg + nxt) > thr) {
+          ts = gs * kGroupThreads + t;
+          qt = Q;
+          break;
+        }
+        Q = nxt;
+        qt = Q;
+      }
+    }
+    const int a = ts * kPerThread;
     int tok = -1, last_pos = -1;
     double run = 0.0;
-    for (int v = a; v < e; ++v) {
-      const float w = resid_weight(pt, dec.lse_t, pd, dec.lse_d, v);
+    for (int v = a; v < a + kPerThread && v < n_valid; ++v) {
+      const float w = resid_weight(st[v], dec.lse_t, sd[v], dec.lse_d, bonus);
       run += static_cast<double>(w);
       if (w > 0.f) last_pos = v;
-      if (pc + (qt + run) > thr) {
+      if (pc + (qg + (qt + run)) > thr) {
         tok = v;
         break;
       }
     }
-    if (tok < 0) tok = last_pos >= 0 ? last_pos : (e > a ? e - 1 : lo);
-    out_tokens[static_cast<size_t>(b) * (k + 1) + r] = tok;
+    if (tok < 0) tok = last_pos >= 0 ? last_pos : min(a, n_valid - 1);
+    out_tokens[static_cast<size_t>(b) * (k + 1) + r] = blk * kBlk + tok;
   }
 }
 
@@ -479,21 +632,25 @@ extern "C" sv_status sv_verify_accept(const float* target_logits, const float* d
   StatPartial* part = reinterpret_cast<StatPartial*>(ws + L.partial_off);
   Decision* decs = reinterpret_cast<Decision*>(ws + L.decision_off);
   double* totals = reinterpret_cast<double*>(ws + L.total_off);
-  const int C1 = stat_chunks(B, k, V);
-  const int C2 = resid_chunks(B, V);
+  const int C1 = stat_spans(V);
+  const int span = stat_span_len(V, C1);
+  const int C2 = resid_wgs(B, V);
   const long long items = static_cast<long long>(B) * (2 * k + 1) * C1;
   const long long blocks1 = (items + kStatsWaves - 1) / kStatsWaves;
   if (blocks1 >= (1LL << 31) || static_cast<long long>(B) * C2 >= (1LL << 31))
     return SV_ERR_INVALID_ARG;
+  // dynamic LDS of kernel 3: block totals for its rare p_r fallback
+  const size_t dyn = static_cast<size_t>(resid_blocks(V)) * sizeof(double);
+  if (dyn > 32 * 1024) return SV_ERR_UNSUPPORTED;
 
   if (V % 4 == 0)
     hipLaunchKernelGGL((stats_kernel<true>), dim3(static_cast<unsigned>(blocks1)),
                        dim3(64 * kStatsWaves), 0, stream, target_logits, draft_logits, B, k, V,
-                       C1, part);
+                       C1, span, part);
   else
     hipLaunchKernelGGL((stats_kernel<false>), dim3(static_cast<unsigned>(blocks1)),
                        dim3(64 * kStatsWaves), 0, stream, target_logits, draft_logits, B, k, V,
-                       C1, part);
+                       C1, span, part);
   SV_LAUNCH_CHECK();
   hipLaunchKernelGGL(decide_kernel, dim3(static_cast<unsigned>(B) * C2), dim3(kThreads), 0,
                      stream, target_logits, draft_logits, draft_tokens, B, k, V, C1, C2,
@@ -501,8 +658,8 @@ extern "C" sv_status sv_verify_accept(const float* target_logits, const float* d
                      static_cast<unsigned int>(seed >> 32), offset, part, decs, totals,
                      out_tokens, out_n_acc, out_status, p_at, q_at, lse);
   SV_LAUNCH_CHECK();
-  hipLaunchKernelGGL(select_kernel, dim3(static_cast<unsigned>(B)), dim3(kThreads), 0, stream,
-                     target_logits, draft_logits, k, V, C2, decs, totals, out_tokens);
+  hipLaunchKernelGGL(select_kernel, dim3(static_cast<unsigned>(B)), dim3(kThreads), dyn, stream,
+                     target_logits, draft_logits, k, V, decs, totals, out_tokens);
   SV_LAUNCH_CHECK();
   return SV_OK;
 }
