@@ -130,7 +130,7 @@ def recorded_traffic(name, k):
     except (OSError, ValueError):
         return None
     if f"_k{k}" not in name or rec.get("sources_sha256") != rocprof_summary.sources_sha256(
-            "w4_pass_kernel"):
+            "pass_kernel"):
         return None
     return rec.get("traffic_bytes")
 
@@ -211,7 +211,7 @@ def main():
         gemms = [(xh if K == HIDDEN else xf, pc, ps, N, y_own[li][gi][:kk])
                  for li, layer in enumerate(w4)
                  for gi, (name, N, K, c, s, z, pc, ps) in enumerate(layer)]
-        return sv.sv_w4_pass_plan(gemms)
+        return sv.sv_pass_plan("w4", gemms)
 
     def w4_launches(kk, packed=True):
         xh, xf = x_h[:kk].contiguous(), x_f[:kk].contiguous()
@@ -240,7 +240,7 @@ def main():
         sv.sv_read_bandwidth_probe(src, sink)
         p = w4_pass(k)
         for _ in range(2):
-            sv.sv_qgemm_w4_pass(p)
+            sv.sv_pass_run(p)
         torch.cuda.synchronize()
         log("profile pass done")
         return
@@ -255,7 +255,7 @@ def main():
     plan = w4_pass(k)
 
     def step():
-        sv.sv_qgemm_w4_pass(plan)
+        sv.sv_pass_run(plan)
         sv.sv_verify_accept(tgt, dft, tok, seed=0, out=acc_out, workspace=acc_ws)
 
     log(f"timing the step (graph replay); pass plan: {plan.items} items on {plan.grid} "
@@ -267,14 +267,14 @@ def main():
     # graph replays of REPS back-to-back launches (amortizing the replay's
     # own launch latency) ----
     REPS = 8
-    ms_rep, _ = time_graph(torch, lambda: [sv.sv_qgemm_w4_pass(plan) for _ in range(REPS)],
+    ms_rep, _ = time_graph(torch, lambda: [sv.sv_pass_run(plan) for _ in range(REPS)],
                            max(2, args.steps // REPS), max(1, args.warmup // REPS))
     ms_pass = ms_rep / REPS
     weight_gbps = pass_bytes / (ms_pass * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(weight_gbps, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(weight_gbps / HBM_PEAK_GBPS, 4),
                 "traffic": recorded_traffic("w4_pass_9b_k16", k),
-                "kernel": "w4_pass_kernel (all 128 GEMMs of the pass in one launch)",
+                "kernel": "pass_kernel<W4> (all 128 GEMMs of the pass in one launch)",
                 "bytes_per_launch": pass_bytes, "launch_us": round(ms_pass * 1e3, 2)}
 
     # ---- accept latency at k = 32 (B = 1) and throughput at B = 64 ----
@@ -320,7 +320,7 @@ def main():
         sweep = {}
         for kk in (1, 4, 8, 16, 32):
             pk = w4_pass(kk)
-            ms, _ = time_graph(torch, lambda pk=pk: sv.sv_qgemm_w4_pass(pk), 10, 2)
+            ms, _ = time_graph(torch, lambda pk=pk: sv.sv_pass_run(pk), 10, 2)
             sweep[kk] = {"pass_ms": round(ms, 4), "GBps": round(pass_bytes / (ms * 1e-3) / 1e9, 1),
                          "drafted_tok_s": round(kk / (ms * 1e-3), 1)}
         extra["w4_k_sweep"] = sweep

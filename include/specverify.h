@@ -133,67 +133,90 @@ sv_status sv_qgemm_w4_packed(const void* x, int m, int K, const uint8_t* packed_
                              hipStream_t stream);
 
 /*
- * Verify-pass executor: every W4 GEMM of one verify pass in ONE launch.
+ * sv_w8_pack -- rewrites row-major W8 codes (int8 [N, K]) into the streaming
+ * layout of the pass executor: for 16-row tile t and 64-wide k block j, one
+ * 1 KiB block at byte (t * K/64 + j) * 1024 whose bytes [16l, 16l+16) hold
+ * row 16t + (l & 15), k = 64j + 16 (l >> 4) + [0, 16) in natural order.
+ * packed_codes: N*K bytes, 16-byte aligned; N % 16 == 0, K % 64 == 0.
+ * The per-channel scales stay as they are (f16 [N]).
+ */
+sv_status sv_w8_pack(const int8_t* codes, int N, int K, uint8_t* packed_codes,
+                     hipStream_t stream);
+
+/*
+ * Verify-pass executor: every GEMM of one verify pass in ONE launch.
  *
  * A pass reads every weight of the stack once for all m draft rows (Karpathy's
  * Trick ..., "Why batch-one decoding is memory-bound": the pass time is the
  * weight bytes divided by bandwidth; Speculative Decoding Clearly Explained,
  * "Check the guesses together").  Launching each GEMM separately stops the
- * HBM stream at every GEMM boundary; the executor streams all of them
- * back to back from one persistent kernel.
+ * HBM stream at every GEMM boundary; the executor streams all of them back to
+ * back from one persistent kernel.  Formats (Karpathy's Trick ..., "How Uzu
+ * optimizes bytes and tokens per pass"; Local LLM 4x Faster, int8 path):
  *
- * sv_w4_gemm describes one product Y = X * W^T with W in the packed layout of
- * sv_w4_pack (group 64):
- *   x             bf16 [m, K]  activations (device)
- *   packed_codes  sv_w4_pack codes of W [N, K] (device)
- *   packed_sz     sv_w4_pack scales/zeros of W (device)
- *   y             f32 [m, N]   output, fully overwritten (device)
- *   K, N          K % 128 == 0, N % 16 == 0; N*K/2, m*K*2 and m*N*4 < 2^31
- * The GEMMs of one pass are independent: no y may overlap another GEMM's x
- * or y (their order of execution inside the launch is unspecified).
+ *   SV_PASS_W4     Y = X W^T, X bf16, W 4-bit asymmetric group 64 (the
+ *                  product of sv_qgemm_w4)
+ *   SV_PASS_W8     Y = X W^T, X bf16, W 8-bit symmetric per channel (the
+ *                  product of sv_qgemm_w8)
+ *   SV_PASS_W4_I8  Y[r, n] = xscale[r] sum_g S (I - Z Xg), X int8 with
+ *                  per-row scales, W 4-bit (the product of sv_qgemm_w4_i8)
  *
- * sv_w4_pass_plan_bytes(gemms, count, m): bytes of the device plan buffer,
- *   0 if an argument is invalid.
- * sv_w4_pass_plan(gemms, count, m, group, plan, plan_bytes, pass, stream):
+ * sv_pass_gemm describes one product (all pointers device, 16-byte aligned):
+ *   x        bf16 [m, K] (W4, W8) or int8 [m, K] (W4_I8)
+ *   xscale   f32 [m] row scales for W4_I8; NULL otherwise
+ *   codes    sv_w4_pack codes (W4, W4_I8) or sv_w8_pack codes (W8) of W [N, K]
+ *   scales   sv_w4_pack scales/zeros (W4, W4_I8) or f16 [N] scales (W8)
+ *   y        f32 [m, N], fully overwritten
+ *   K, N     N % 16 == 0; K % 128 == 0 (W4, W4_I8) or K % 64 == 0 (W8);
+ *            codes, m*K activation bytes and m*N*4 below 2^31 bytes
+ * The GEMMs of one pass are independent: no y may overlap another GEMM's
+ * inputs or outputs (their order inside the launch is unspecified).
+ *
+ * sv_pass_plan_bytes(format, gemms, count, m): bytes of the device plan
+ *   buffer, 0 if an argument is invalid.
+ * sv_pass_plan(format, gemms, count, m, group, plan, plan_bytes, pass, stream):
  *   validates every descriptor (SV_ERR_NULL / _INVALID_ARG / _ALIGN /
- *   _UNSUPPORTED as for sv_qgemm_w4_packed; SV_ERR_WORKSPACE if plan_bytes is
- *   too small), splits the GEMMs into work items of 256 output channels,
- *   assigns them to one workgroup per compute unit of the current device,
- *   writes the plan into `plan` (caller-owned device memory, 16-byte aligned)
- *   and fills the host struct *pass.  This is a setup call: it copies the
- *   plan with `stream` and synchronizes that stream before returning.
- *   The plan stores the descriptors' pointers; it stays valid while those
- *   buffers and `plan` live, for any number of launches.
- * sv_qgemm_w4_pass(pass, stream): enqueues the whole pass as one kernel
- *   launch on `stream` (capturable in a HIP graph).  A plan buffer that no
- *   longer holds the plan described by *pass makes the kernel return without
- *   writing anything.
- * Results equal sv_qgemm_w4_packed's up to the order of the binary32
- * accumulation over K (deterministic from run to run).
+ *   _UNSUPPORTED; group must be 64 for the 4-bit formats; SV_ERR_WORKSPACE if
+ *   plan_bytes is too small), splits the GEMMs into work items of 512 output
+ *   channels, assigns them to one workgroup per compute unit of the current
+ *   device, writes the plan into `plan` (caller-owned device memory) and fills
+ *   the host struct *pass.  A setup call: it copies the plan with `stream` and
+ *   synchronizes that stream before returning.  The plan stores the
+ *   descriptors' pointers; it stays valid while those buffers and `plan`
+ *   live, for any number of launches.
+ * sv_pass_run(pass, stream): enqueues the whole pass as one kernel launch on
+ *   `stream` (capturable in a HIP graph).  A plan buffer that no longer holds
+ *   the plan described by *pass makes the kernel return without writing.
+ * Results are deterministic; they equal the single-GEMM entry points' up to
+ * the order of the binary32 accumulation over K (the int32 group partials of
+ * W4_I8 are exact).
  */
-typedef struct sv_w4_gemm {
+typedef enum { SV_PASS_W4 = 0, SV_PASS_W8 = 1, SV_PASS_W4_I8 = 2 } sv_pass_format;
+
+typedef struct sv_pass_gemm {
   const void* x;
-  const uint8_t* packed_codes;
-  const void* packed_sz;
+  const float* xscale;
+  const uint8_t* codes;
+  const void* scales;
   float* y;
   int K;
   int N;
-} sv_w4_gemm;
+} sv_pass_gemm;
 
-typedef struct sv_w4_pass {
-  void* plan;       /* device plan buffer given to sv_w4_pass_plan */
-  int m;            /* draft rows of every GEMM in the pass        */
-  int count;        /* number of GEMMs                             */
-  int grid;         /* workgroups of the launch                    */
-  int items;        /* work items over all GEMMs                   */
-  int max_steps;    /* longest per-workgroup chunk count           */
-  int reserved;
-} sv_w4_pass;
+typedef struct sv_pass {
+  void* plan;       /* device plan buffer given to sv_pass_plan   */
+  int format;       /* sv_pass_format                             */
+  int m;            /* draft rows of every GEMM in the pass       */
+  int count;        /* number of GEMMs                            */
+  int grid;         /* workgroups of the launch                   */
+  int items;        /* work items over all GEMMs                  */
+  int max_steps;    /* longest per-workgroup chunk count          */
+} sv_pass;
 
-size_t sv_w4_pass_plan_bytes(const sv_w4_gemm* gemms, int count, int m);
-sv_status sv_w4_pass_plan(const sv_w4_gemm* gemms, int count, int m, int group, void* plan,
-                          size_t plan_bytes, sv_w4_pass* pass, hipStream_t stream);
-sv_status sv_qgemm_w4_pass(const sv_w4_pass* pass, hipStream_t stream);
+size_t sv_pass_plan_bytes(int format, const sv_pass_gemm* gemms, int count, int m);
+sv_status sv_pass_plan(int format, const sv_pass_gemm* gemms, int count, int m, int group,
+                       void* plan, size_t plan_bytes, sv_pass* pass, hipStream_t stream);
+sv_status sv_pass_run(const sv_pass* pass, hipStream_t stream);
 
 /*
  * sv_qgemm_w8 -- verify GEMM over 8-bit symmetric per-output-channel weights.

@@ -82,39 +82,55 @@ def test_pass_plan_validation_before_any_hip_call():
     import verify_pass_sv_amd as sv
     L = sv.lib
     a = 0x100000                                   # aligned, never dereferenced
+    W4, W8, I8 = 0, 1, 2
 
-    def gemms(*shapes, x=a):
-        arr = (sv.SvW4Gemm * len(shapes))()
+    def gemms(*shapes, x=a, xscale=None):
+        arr = (sv.SvPassGemm * len(shapes))()
         for i, (K, N) in enumerate(shapes):
-            arr[i] = sv.SvW4Gemm(x, a, a, a, K, N)
+            arr[i] = sv.SvPassGemm(x, xscale, a, a, a, K, N)
         return arr
 
     good = gemms((4096, 12288), (4096, 4096), (12288, 4096), (128, 16))
-    nb = L.sv_w4_pass_plan_bytes(good, 4, 16)
-    # header + per-workgroup tables + 48 bytes per 512-channel item
+    nb = L.sv_pass_plan_bytes(W4, good, 4, 16)
+    # header + per-workgroup tables + 64 bytes per 512-channel item
     items = 24 + 8 + 8 + 1
-    assert nb >= items * 48 and nb < items * 48 + 64 * 1024
-    assert L.sv_w4_pass_plan_bytes(good, 4, 0) == 0
-    assert L.sv_w4_pass_plan_bytes(good, 4, 33) == 0
-    assert L.sv_w4_pass_plan_bytes(good, 0, 16) == 0
-    assert L.sv_w4_pass_plan_bytes(gemms((4096, 40)), 1, 16) == 0     # N % 16
-    assert L.sv_w4_pass_plan_bytes(gemms((4000, 64)), 1, 16) == 0     # K % 128
-    info = sv.SvW4Pass()
+    assert nb >= items * 64 and nb < items * 64 + 64 * 1024
+    assert L.sv_pass_plan_bytes(W8, good, 4, 16) == nb
+    assert L.sv_pass_plan_bytes(7, good, 4, 16) == 0                  # unknown format
+    assert L.sv_pass_plan_bytes(W4, good, 4, 0) == 0
+    assert L.sv_pass_plan_bytes(W4, good, 4, 33) == 0
+    assert L.sv_pass_plan_bytes(W4, good, 0, 16) == 0
+    assert L.sv_pass_plan_bytes(W4, gemms((4096, 40)), 1, 16) == 0     # N % 16
+    assert L.sv_pass_plan_bytes(W4, gemms((4032, 64)), 1, 16) == 0     # K % 128 (4-bit)
+    assert L.sv_pass_plan_bytes(W8, gemms((4032, 64)), 1, 16) > 0      # K % 64 (8-bit)
+    # the int8 path needs row scales, the others must not get any
+    assert L.sv_pass_plan_bytes(I8, good, 4, 16) == 0
+    assert L.sv_pass_plan_bytes(I8, gemms((4096, 64), xscale=a), 1, 16) > 0
+    assert L.sv_pass_plan_bytes(W4, gemms((4096, 64), xscale=a), 1, 16) == 0
+    info = sv.SvPass()
     plan = ctypes.c_void_p(a)
-    assert L.sv_w4_pass_plan(good, 4, 16, 64, None, nb, ctypes.byref(info), None) == 1
-    assert L.sv_w4_pass_plan(good, 4, 16, 64, plan, nb, None, None) == 1
-    assert L.sv_w4_pass_plan(good, 4, 16, 32, plan, nb, ctypes.byref(info), None) == 4
-    assert L.sv_w4_pass_plan(good, 4, 16, 64, plan, nb - 1, ctypes.byref(info), None) == 5
-    assert L.sv_w4_pass_plan(good, 4, 16, 64, ctypes.c_void_p(a + 8), nb,
-                             ctypes.byref(info), None) == 3
-    assert L.sv_w4_pass_plan(gemms((4096, 64), x=a + 2), 1, 16, 64, plan, nb,
-                             ctypes.byref(info), None) == 3
-    assert L.sv_w4_pass_plan(gemms((4096, 64), x=0), 1, 16, 64, plan, nb,
-                             ctypes.byref(info), None) == 1
+    assert L.sv_pass_plan(W4, good, 4, 16, 64, None, nb, ctypes.byref(info), None) == 1
+    assert L.sv_pass_plan(W4, good, 4, 16, 64, plan, nb, None, None) == 1
+    assert L.sv_pass_plan(W4, good, 4, 16, 32, plan, nb, ctypes.byref(info), None) == 4
+    assert L.sv_pass_plan(W4, good, 4, 16, 64, plan, nb - 1, ctypes.byref(info), None) == 5
+    assert L.sv_pass_plan(W4, good, 4, 16, 64, ctypes.c_void_p(a + 8), nb,
+                          ctypes.byref(info), None) == 3
+    assert L.sv_pass_plan(W4, gemms((4096, 64), x=a + 2), 1, 16, 64, plan, nb,
+                          ctypes.byref(info), None) == 3
+    assert L.sv_pass_plan(W4, gemms((4096, 64), x=0), 1, 16, 64, plan, nb,
+                          ctypes.byref(info), None) == 1
+    assert L.sv_pass_plan(I8, gemms((4096, 64)), 1, 16, 64, plan, nb,
+                          ctypes.byref(info), None) == 1
     # a single matrix with 2 GiB of codes does not fit 32-bit buffer offsets
-    assert L.sv_w4_pass_plan_bytes(gemms((65536, 65536)), 1, 1) == 0
-    assert L.sv_qgemm_w4_pass(None, None) == 1
-    bad = sv.SvW4Pass(plan=a, m=0, count=1, grid=256, items=1, max_steps=1, reserved=0)
-    assert L.sv_qgemm_w4_pass(ctypes.byref(bad), None) == 2
-    bad = sv.SvW4Pass(plan=a, m=16, count=1, grid=0, items=1, max_steps=1, reserved=0)
-    assert L.sv_qgemm_w4_pass(ctypes.byref(bad), None) == 2
+    assert L.sv_pass_plan_bytes(W4, gemms((65536, 65536)), 1, 1) == 0
+    assert L.sv_pass_run(None, None) == 1
+    bad = sv.SvPass(plan=a, format=W4, m=0, count=1, grid=256, items=1, max_steps=1)
+    assert L.sv_pass_run(ctypes.byref(bad), None) == 2
+    bad = sv.SvPass(plan=a, format=W4, m=16, count=1, grid=0, items=1, max_steps=1)
+    assert L.sv_pass_run(ctypes.byref(bad), None) == 2
+    bad = sv.SvPass(plan=a, format=9, m=16, count=1, grid=1, items=1, max_steps=1)
+    assert L.sv_pass_run(ctypes.byref(bad), None) == 2
+    # W8 packing arguments
+    assert L.sv_w8_pack(None, 64, 64, plan, None) == 1
+    assert L.sv_w8_pack(plan, 40, 64, plan, None) == 2
+    assert L.sv_w8_pack(plan, 64, 96, plan, None) == 2

@@ -1,4 +1,4 @@
-"""GPU parity of the verify-pass executor (sv_w4_pass_plan + sv_qgemm_w4_pass).
+"""GPU parity of the verify-pass executor (sv_pass_plan + sv_pass_run).
 
 Every GEMM of a planned pass runs in one launch; each output is compared
 with the binary64 oracle (dequantize + matmul) on the same seeded inputs.
@@ -47,9 +47,9 @@ MIXED = [(512, 1024), (2176, 48), (640, 4160), (128, 16), (4096, 272), (1152, 81
 def test_pass_matches_oracle_mixed_shapes(m):
     sv = _sv()
     gs = [_gemm(m, K, N, seed=300 + 10 * i + m) for i, (K, N) in enumerate(MIXED)]
-    p = sv.sv_w4_pass_plan([g["dev"] for g in gs])
+    p = sv.sv_pass_plan("w4", [g["dev"] for g in gs])
     assert p.items == sum((N // 16 + 31) // 32 for _, N in MIXED)   # 512-channel items
-    sv.sv_qgemm_w4_pass(p)
+    sv.sv_pass_run(p)
     torch.cuda.synchronize()
     for (K, N), g in zip(MIXED, gs):
         y = g["dev"][4].cpu().numpy()
@@ -64,9 +64,9 @@ def test_pass_tiny_configuration():
     # one linear layer K=512, N=1024 at m=4: fewer items than compute units
     sv = _sv()
     g = _gemm(4, 512, 1024, seed=0)
-    p = sv.sv_w4_pass_plan([g["dev"]])
+    p = sv.sv_pass_plan("w4", [g["dev"]])
     assert p.grid == 2 and p.items == 2
-    sv.sv_qgemm_w4_pass(p)
+    sv.sv_pass_run(p)
     torch.cuda.synchronize()
     assert_rows_close(g["dev"][4].cpu().numpy(), _oracle(g["host"]), what="tiny")
 
@@ -87,8 +87,8 @@ def test_pass_one_hot_rows_exact(m):
         y = torch.empty((m, N), dtype=torch.float32, device=DEV)
         gs.append(((codes, scales, zeros), (x.to(DEV), pc, ps, N, y)))
         cols.append(c)
-    p = sv.sv_w4_pass_plan([d for _, d in gs])
-    sv.sv_qgemm_w4_pass(p)
+    p = sv.sv_pass_plan("w4", [d for _, d in gs])
+    sv.sv_pass_run(p)
     torch.cuda.synchronize()
     for ((codes, scales, zeros), d), c in zip(gs, cols):
         W = oracle.dequant_w4(codes.numpy(), scales.numpy(), zeros.numpy())
@@ -103,10 +103,10 @@ def test_pass_agrees_with_per_gemm_entry_point_and_is_deterministic():
     m = 16
     shapes = [(4096, 12288), (4096, 4096), (4096, 24576), (12288, 4096)]   # one 9B layer
     gs = [_gemm(m, K, N, seed=500 + i) for i, (K, N) in enumerate(shapes)]
-    p = sv.sv_w4_pass_plan([g["dev"] for g in gs])
-    sv.sv_qgemm_w4_pass(p)
+    p = sv.sv_pass_plan("w4", [g["dev"] for g in gs])
+    sv.sv_pass_run(p)
     first = [g["dev"][4].clone() for g in gs]
-    sv.sv_qgemm_w4_pass(p)
+    sv.sv_pass_run(p)
     torch.cuda.synchronize()
     for g, y1 in zip(gs, first):
         x, pc, ps, N, y = g["dev"]
@@ -120,8 +120,8 @@ def test_pass_agrees_with_per_gemm_entry_point_and_is_deterministic():
 def test_pass_in_a_graph_replays_like_eager():
     sv = _sv()
     gs = [_gemm(16, K, N, seed=700 + i) for i, (K, N) in enumerate([(1024, 4096), (2048, 1024)])]
-    p = sv.sv_w4_pass_plan([g["dev"] for g in gs])
-    sv.sv_qgemm_w4_pass(p)
+    p = sv.sv_pass_plan("w4", [g["dev"] for g in gs])
+    sv.sv_pass_run(p)
     torch.cuda.synchronize()
     eager = [g["dev"][4].clone() for g in gs]
     s = torch.cuda.Stream()
@@ -129,7 +129,7 @@ def test_pass_in_a_graph_replays_like_eager():
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
         with torch.cuda.graph(graph, stream=s):
-            sv.sv_qgemm_w4_pass(p, stream=s)
+            sv.sv_pass_run(p, stream=s)
     torch.cuda.synchronize()
     for _ in range(3):
         for g in gs:
@@ -161,8 +161,8 @@ def test_full_9b_stack_pass_sampled_channels():
             del c, s, z
             y = torch.full((m, N), float("nan"), dtype=torch.float32, device=DEV)
             gemms.append((x_h if K == H else x_f, pc, ps, N, y))
-    p = sv.sv_w4_pass_plan(gemms)
-    sv.sv_qgemm_w4_pass(p)
+    p = sv.sv_pass_plan("w4", gemms)
+    sv.sv_pass_run(p)
     torch.cuda.synchronize()
     xb = {H: bf16_bits(x_h.cpu()), F: bf16_bits(x_f.cpu())}
     for (x, pc, ps, N, y), (rows, c, s, z) in zip(gemms, samples):
@@ -178,8 +178,180 @@ def test_pass_argument_errors():
     g = _gemm(4, 512, 64, seed=31)
     x, pc, ps, N, y = g["dev"]
     with pytest.raises(ValueError):
-        sv.sv_w4_pass_plan([])
+        sv.sv_pass_plan("w4", [])
     with pytest.raises(ValueError):      # rows must agree across the pass
-        sv.sv_w4_pass_plan([g["dev"], (x[:2].contiguous(), pc, ps, N, y[:2].contiguous())])
+        sv.sv_pass_plan("w4", [g["dev"], (x[:2].contiguous(), pc, ps, N, y[:2].contiguous())])
     with pytest.raises(TypeError):
-        sv.sv_w4_pass_plan([(x.float(), pc, ps, N, y)])
+        sv.sv_pass_plan("w4", [(x.float(), pc, ps, N, y)])
+
+
+# ---- W8 and int8 formats of the executor --------------------------------------
+
+def _w8_gemm(m, K, N, seed):
+    sv = _sv()
+    codes, scales = synth.w8_matrix(N, K, seed=seed)
+    x = synth.activations(m, K, seed=seed + 1)
+    pc = sv.sv_w8_pack(codes.to(DEV))
+    y = torch.full((m, N), float("nan"), dtype=torch.float32, device=DEV)
+    return dict(host=(x, codes, scales), dev=(x.to(DEV), pc, scales.to(DEV), N, y))
+
+
+def _i8_gemm(m, K, N, seed):
+    sv = _sv()
+    codes, scales, zeros = synth.w4_matrix(N, K, seed=seed)
+    xq, xs = synth.int8_activations(m, K, seed=seed + 1)
+    pc, ps = sv.sv_w4_pack(*to_dev(codes, scales, zeros))
+    y = torch.full((m, N), float("nan"), dtype=torch.float32, device=DEV)
+    return dict(host=(xq, xs, codes, scales, zeros),
+                dev=(xq.to(DEV), xs.to(DEV), pc, ps, N, y))
+
+
+def test_w8_pack_layout_matches_contract():
+    sv = _sv()
+    N, K = 32, 192
+    codes, _ = synth.w8_matrix(N, K, seed=5)
+    pc = sv.sv_w8_pack(codes.to(DEV)).cpu().numpy().reshape(N // 16, K // 64, 64, 16)
+    c = codes.numpy().view(np.uint8)
+    for t in range(N // 16):
+        for j in range(K // 64):
+            for l in range(64):
+                n, q = 16 * t + (l & 15), l >> 4
+                assert np.array_equal(pc[t, j, l], c[n, 64 * j + 16 * q: 64 * j + 16 * q + 16])
+
+
+W8_MIXED = [(512, 1024), (192, 48), (640, 4160), (64, 16), (4096, 272), (1088, 8192)]
+
+
+@pytest.mark.parametrize("m", [1, 5, 16, 17, 32])
+def test_w8_pass_matches_oracle(m):
+    sv = _sv()
+    gs = [_w8_gemm(m, K, N, seed=900 + 10 * i + m) for i, (K, N) in enumerate(W8_MIXED)]
+    p = sv.sv_pass_plan("w8", [g["dev"] for g in gs])
+    sv.sv_pass_run(p)
+    torch.cuda.synchronize()
+    for (K, N), g in zip(W8_MIXED, gs):
+        x, codes, scales = g["host"]
+        y = g["dev"][4].cpu().numpy()
+        assert np.isfinite(y).all(), f"unwritten outputs K={K} N={N}"
+        rows = np.arange(N) if N <= 1024 else np.sort(
+            np.random.default_rng(N + K).choice(N, size=512, replace=False))
+        ref = oracle.qgemm_w8(bf16_bits(x), codes.numpy()[rows], scales.numpy()[rows])
+        assert_rows_close(y[:, rows], ref, what=f"w8 pass m={m} K={K} N={N}")
+
+
+@pytest.mark.parametrize("m", [1, 32])
+def test_w8_pass_one_hot_rows_exact(m):
+    sv = _sv()
+    K, N = 4096, 1040
+    codes, scales = synth.w8_matrix(N, K, seed=77)
+    cols = np.random.default_rng(m).choice(K, size=m, replace=False)
+    x = torch.zeros((m, K), dtype=torch.bfloat16)
+    x[torch.arange(m), torch.as_tensor(cols)] = 1.0
+    y = torch.empty((m, N), dtype=torch.float32, device=DEV)
+    pc = sv.sv_w8_pack(codes.to(DEV))
+    p = sv.sv_pass_plan("w8", [(x.to(DEV), pc, scales.to(DEV), N, y)])
+    sv.sv_pass_run(p)
+    torch.cuda.synchronize()
+    W = oracle.dequant_w8(codes.numpy(), scales.numpy())
+    assert np.array_equal(y.cpu().numpy(), W[:, cols].T.astype(np.float32))
+
+
+def test_w8_pass_agrees_with_single_gemm_entry_point():
+    sv = _sv()
+    g = _w8_gemm(16, 12288, 4096, seed=31)
+    x, pc, sc, N, y = g["dev"]
+    _, codes, _ = g["host"]
+    p = sv.sv_pass_plan("w8", [g["dev"]])
+    sv.sv_pass_run(p)
+    ref = sv.sv_qgemm_w8(x, codes.to(DEV), sc)
+    torch.cuda.synchronize()
+    rel = (y - ref).norm(dim=1) / ref.norm(dim=1)
+    assert float(rel.max()) < 1e-5
+
+
+I8_MIXED = [(512, 1024), (2176, 48), (640, 4160), (128, 16), (4096, 272), (1152, 8192)]
+
+
+@pytest.mark.parametrize("m", [1, 4, 16, 17, 32])
+def test_w4_i8_pass_matches_oracle(m):
+    sv = _sv()
+    gs = [_i8_gemm(m, K, N, seed=700 + 10 * i + m) for i, (K, N) in enumerate(I8_MIXED)]
+    p = sv.sv_pass_plan("w4_i8", [g["dev"] for g in gs])
+    sv.sv_pass_run(p)
+    torch.cuda.synchronize()
+    for (K, N), g in zip(I8_MIXED, gs):
+        xq, xs, codes, scales, zeros = g["host"]
+        y = g["dev"][5].cpu().numpy()
+        assert np.isfinite(y).all(), f"unwritten outputs K={K} N={N}"
+        rows = np.arange(N) if N <= 1024 else np.sort(
+            np.random.default_rng(N + K).choice(N, size=512, replace=False))
+        ref = oracle.qgemm_w4_i8(xq.numpy(), xs.numpy(), codes.numpy()[rows],
+                                 scales.numpy()[rows], zeros.numpy()[rows])
+        assert_rows_close(y[:, rows], ref, what=f"w4_i8 pass m={m} K={K} N={N}")
+
+
+def test_w4_i8_pass_one_hot_rows_exact():
+    sv = _sv()
+    m, K, N = 32, 4096, 528
+    codes, scales, zeros = synth.w4_matrix(N, K, seed=78)
+    cols = np.random.default_rng(3).choice(K, size=m, replace=False)
+    xq = torch.zeros((m, K), dtype=torch.int8)
+    xq[torch.arange(m), torch.as_tensor(cols)] = 1
+    xs = torch.ones((m,), dtype=torch.float32)
+    pc, ps = sv.sv_w4_pack(*to_dev(codes, scales, zeros))
+    y = torch.empty((m, N), dtype=torch.float32, device=DEV)
+    p = sv.sv_pass_plan("w4_i8", [(xq.to(DEV), xs.to(DEV), pc, ps, N, y)])
+    sv.sv_pass_run(p)
+    torch.cuda.synchronize()
+    W = oracle.dequant_w4(codes.numpy(), scales.numpy(), zeros.numpy())
+    assert np.array_equal(y.cpu().numpy(), W[:, cols].T.astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt", ["w8", "w4_i8"])
+def test_full_9b_stack_pass_other_formats_sampled(fmt):
+    """The 32-layer stack in the W8 and int8 formats at k = 16, one launch, in
+    the benchmark's configuration; 8 sampled channels per GEMM against the
+    oracle."""
+    sv = _sv()
+    H, F, m = 4096, 12288, 16
+    shapes = [(3 * H, H), (H, H), (2 * F, H), (H, F)]
+    if fmt == "w8":
+        xs = {H: synth.activations(m, H, seed=11, device=DEV),
+              F: synth.activations(m, F, seed=12, device=DEV)}
+    else:
+        xs = {H: synth.int8_activations(m, H, seed=13, device=DEV),
+              F: synth.int8_activations(m, F, seed=14, device=DEV)}
+    gemms, samples = [], []
+    rng = np.random.default_rng(99)
+    for layer in range(32):
+        for i, (N, K) in enumerate(shapes):
+            rows = np.sort(rng.choice(N, size=8, replace=False))
+            ri = torch.as_tensor(rows, device=DEV)
+            y = torch.full((m, N), float("nan"), dtype=torch.float32, device=DEV)
+            if fmt == "w8":
+                c, s = synth.w8_matrix(N, K, seed=5000 + 1000 * layer + i, device=DEV)
+                pc = sv.sv_w8_pack(c)
+                samples.append((rows, c[ri].cpu(), s[ri].cpu()))
+                gemms.append((xs[K], pc, s, N, y))
+                del c
+            else:
+                c, s, z = synth.w4_matrix(N, K, seed=1000 * layer + i, device=DEV)
+                pc, ps = sv.sv_w4_pack(c, s, z)
+                samples.append((rows, c[ri].cpu(), s[ri].cpu(), z[ri].cpu()))
+                gemms.append((xs[K][0], xs[K][1], pc, ps, N, y))
+                del c, s, z
+    p = sv.sv_pass_plan(fmt, gemms)
+    sv.sv_pass_run(p)
+    torch.cuda.synchronize()
+    for g, smp in zip(gemms, samples):
+        y = g[-1].cpu().numpy()
+        assert np.isfinite(y).all()
+        rows = smp[0]
+        if fmt == "w8":
+            K = g[0].shape[1]
+            ref = oracle.qgemm_w8(bf16_bits(g[0].cpu()), smp[1].numpy(), smp[2].numpy())
+        else:
+            K = g[0].shape[1]
+            ref = oracle.qgemm_w4_i8(g[0].cpu().numpy(), g[1].cpu().numpy(), smp[1].numpy(),
+                                     smp[2].numpy(), smp[3].numpy())
+        assert_rows_close(y[:, rows], ref, what=f"{fmt} stack K={K}")

@@ -12,7 +12,8 @@ _BINDING_NAMES = (
     "sv_hadamard_i8", "sv_qgemm_w4_i8", "sv_verify_accept", "sv_verify_accept_workspace_bytes",
     "sv_philox4x32_10", "sv_read_bandwidth_probe", "sv_read_probe_sink_words",
     "EXPORTED_SYMBOLS", "SV_MAX_ROWS", "sv_w4_pack", "sv_qgemm_w4_packed",
-    "sv_w4_pass_plan", "sv_qgemm_w4_pass", "W4Pass", "SvW4Gemm", "SvW4Pass",
+    "sv_w8_pack", "sv_pass_plan", "sv_pass_run", "Pass", "SvPassGemm", "SvPass",
+    "PASS_FORMATS",
 )
 
 __all__ = list(_BINDING_NAMES)

@@ -20,25 +20,28 @@ EXPORTED_SYMBOLS = (
     "sv_qgemm_w4_i8", "sv_verify_accept_workspace_bytes", "sv_verify_accept",
     "sv_philox4x32_10", "sv_read_probe_sink_words", "sv_read_bandwidth_probe",
     "sv_w4_packed_codes_bytes", "sv_w4_packed_sz_bytes", "sv_w4_pack", "sv_qgemm_w4_packed",
-    "sv_w4_pass_plan_bytes", "sv_w4_pass_plan", "sv_qgemm_w4_pass",
+    "sv_w8_pack", "sv_pass_plan_bytes", "sv_pass_plan", "sv_pass_run",
 )
 
 _STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_INVALID_ARG", 3: "SV_ERR_ALIGN",
            4: "SV_ERR_UNSUPPORTED", 5: "SV_ERR_WORKSPACE", 6: "SV_ERR_HIP"}
 
 
-class SvW4Gemm(ctypes.Structure):
-    """C struct sv_w4_gemm: one GEMM of a verify pass."""
-    _fields_ = [("x", ctypes.c_void_p), ("packed_codes", ctypes.c_void_p),
-                ("packed_sz", ctypes.c_void_p), ("y", ctypes.c_void_p),
-                ("K", ctypes.c_int), ("N", ctypes.c_int)]
+class SvPassGemm(ctypes.Structure):
+    """C struct sv_pass_gemm: one GEMM of a verify pass."""
+    _fields_ = [("x", ctypes.c_void_p), ("xscale", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("y", ctypes.c_void_p), ("K", ctypes.c_int),
+                ("N", ctypes.c_int)]
 
 
-class SvW4Pass(ctypes.Structure):
-    """C struct sv_w4_pass: host descriptor of a planned pass."""
-    _fields_ = [("plan", ctypes.c_void_p), ("m", ctypes.c_int), ("count", ctypes.c_int),
-                ("grid", ctypes.c_int), ("items", ctypes.c_int), ("max_steps", ctypes.c_int),
-                ("reserved", ctypes.c_int)]
+class SvPass(ctypes.Structure):
+    """C struct sv_pass: host descriptor of a planned pass."""
+    _fields_ = [("plan", ctypes.c_void_p), ("format", ctypes.c_int), ("m", ctypes.c_int),
+                ("count", ctypes.c_int), ("grid", ctypes.c_int), ("items", ctypes.c_int),
+                ("max_steps", ctypes.c_int)]
+
+
+PASS_FORMATS = {"w4": 0, "w8": 1, "w4_i8": 2}
 
 
 class SvError(RuntimeError):
@@ -72,10 +75,11 @@ def _load():
         "sv_w4_packed_sz_bytes": (sz, [i32, i32, i32]),
         "sv_w4_pack": (i32, [vp, vp, vp, i32, i32, i32, vp, vp, vp]),
         "sv_qgemm_w4_packed": (i32, [vp, i32, i32, vp, vp, i32, i32, vp, vp]),
-        "sv_w4_pass_plan_bytes": (sz, [ctypes.POINTER(SvW4Gemm), i32, i32]),
-        "sv_w4_pass_plan": (i32, [ctypes.POINTER(SvW4Gemm), i32, i32, i32, vp, sz,
-                                  ctypes.POINTER(SvW4Pass), vp]),
-        "sv_qgemm_w4_pass": (i32, [ctypes.POINTER(SvW4Pass), vp]),
+        "sv_w8_pack": (i32, [vp, i32, i32, vp, vp]),
+        "sv_pass_plan_bytes": (sz, [i32, ctypes.POINTER(SvPassGemm), i32, i32]),
+        "sv_pass_plan": (i32, [i32, ctypes.POINTER(SvPassGemm), i32, i32, i32, vp, sz,
+                               ctypes.POINTER(SvPass), vp]),
+        "sv_pass_run": (i32, [ctypes.POINTER(SvPass), vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -172,7 +176,16 @@ def sv_qgemm_w4_packed(x, packed_codes, packed_sz, N, y=None, group=64, stream=N
     return y
 
 
-class W4Pass:
+def sv_w8_pack(codes, stream=None):
+    """Row-major W8 codes int8 [N, K] -> packed streaming layout (uint8 [N*K])."""
+    N, K = codes.shape
+    _need(codes, "codes", torch.int8, (N, K))
+    out = torch.empty((N * K,), dtype=torch.uint8, device=codes.device)
+    _check("sv_w8_pack", lib.sv_w8_pack(_ptr(codes), N, K, _ptr(out), _stream(stream)))
+    return out
+
+
+class Pass:
     """A planned verify pass: the device plan, its host descriptor and the
     tensors it points to (kept alive as long as the plan)."""
 
@@ -190,46 +203,65 @@ class W4Pass:
         return self.info.items
 
 
-def _w4_gemm_array(gemms, group):
-    arr = (SvW4Gemm * len(gemms))()
+def _pass_gemms(fmt, gemms, group):
+    arr = (SvPassGemm * len(gemms))()
     m = None
     keep = []
-    for i, (x, pc, ps, N, y) in enumerate(gemms):
+    for i, g in enumerate(gemms):
+        if fmt == "w4_i8":
+            x, xscale, codes, sc, N, y = g
+        else:
+            x, codes, sc, N, y = g
+            xscale = None
         mm, K = x.shape
         m = mm if m is None else m
         if mm != m:
             raise ValueError("every GEMM of a pass has the same number of rows m")
-        _need(x, "x", torch.bfloat16)
-        _need(pc, "packed_codes", torch.uint8, (N * K // 2,))
-        _need(ps, "packed_sz", torch.float16, (N * (K // group) * 2,))
+        if fmt == "w8":
+            _need(x, "x", torch.bfloat16)
+            _need(codes, "packed_codes", torch.uint8, (N * K,))
+            _need(sc, "scales", torch.float16, (N,))
+        else:
+            _need(x, "x", torch.int8 if fmt == "w4_i8" else torch.bfloat16)
+            _need(codes, "packed_codes", torch.uint8, (N * K // 2,))
+            _need(sc, "packed_sz", torch.float16, (N * (K // group) * 2,))
+        if xscale is not None:
+            _need(xscale, "xscale", torch.float32, (m,))
         _need(y, "y", torch.float32, (m, N))
-        arr[i] = SvW4Gemm(x.data_ptr(), pc.data_ptr(), ps.data_ptr(), y.data_ptr(), K, N)
-        keep += [x, pc, ps, y]
+        arr[i] = SvPassGemm(x.data_ptr(), None if xscale is None else xscale.data_ptr(),
+                            codes.data_ptr(), sc.data_ptr(), y.data_ptr(), K, N)
+        keep += [t for t in (x, xscale, codes, sc, y) if t is not None]
     return arr, m, keep
 
 
-def sv_w4_pass_plan(gemms, group=64, stream=None):
-    """Plan one verify pass over packed W4 GEMMs.
+def sv_pass_plan(fmt, gemms, group=64, stream=None):
+    """Plan one verify pass; `fmt` is "w4", "w8" or "w4_i8".
 
-    gemms: sequence of (x bf16 [m, K], packed_codes, packed_sz, N, y f32 [m, N]).
-    Returns a W4Pass for sv_qgemm_w4_pass.  Synchronizes `stream`.
+    gemms: sequence of
+      w4:    (x bf16 [m, K], packed_codes, packed_sz, N, y f32 [m, N])
+      w8:    (x bf16 [m, K], packed_codes (sv_w8_pack), scales f16 [N], N, y)
+      w4_i8: (xq int8 [m, K], xscale f32 [m], packed_codes, packed_sz, N, y)
+    Returns a Pass for sv_pass_run.  Synchronizes `stream`.
     """
+    if fmt not in PASS_FORMATS:
+        raise ValueError(f"unknown pass format {fmt!r}")
     if len(gemms) == 0:
         raise ValueError("a pass needs at least one GEMM")
-    arr, m, keep = _w4_gemm_array(gemms, group)
-    nbytes = int(lib.sv_w4_pass_plan_bytes(arr, len(gemms), m))
+    arr, m, keep = _pass_gemms(fmt, gemms, group)
+    f = PASS_FORMATS[fmt]
+    nbytes = int(lib.sv_pass_plan_bytes(f, arr, len(gemms), m))
     if nbytes == 0:
-        raise SvError("sv_w4_pass_plan_bytes", 2)
+        raise SvError("sv_pass_plan_bytes", 2)
     plan = torch.empty((nbytes,), dtype=torch.uint8, device=keep[0].device)
-    info = SvW4Pass()
-    _check("sv_w4_pass_plan", lib.sv_w4_pass_plan(arr, len(gemms), m, group, _ptr(plan),
-                                                  nbytes, ctypes.byref(info), _stream(stream)))
-    return W4Pass(plan, info, keep)
+    info = SvPass()
+    _check("sv_pass_plan", lib.sv_pass_plan(f, arr, len(gemms), m, group, _ptr(plan), nbytes,
+                                            ctypes.byref(info), _stream(stream)))
+    return Pass(plan, info, keep)
 
 
-def sv_qgemm_w4_pass(w4pass, stream=None):
+def sv_pass_run(p, stream=None):
     """Run every GEMM of a planned pass in one launch."""
-    _check("sv_qgemm_w4_pass", lib.sv_qgemm_w4_pass(ctypes.byref(w4pass.info), _stream(stream)))
+    _check("sv_pass_run", lib.sv_pass_run(ctypes.byref(p.info), _stream(stream)))
 
 
 def sv_qgemm_w8(x, codes, scales, y=None, stream=None):

@@ -17,7 +17,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "qgemm_w4.hip", "qgemm_w4_packed.hip", "w4_pass.hip", "qgemm_w8.hip", "qgemm_w4_i8.hip",
+SOURCES = ["api.hip", "qgemm_w4.hip", "qgemm_w4_packed.hip", "pass.hip", "qgemm_w8.hip", "qgemm_w4_i8.hip",
            "hadamard_i8.hip", "verify_accept.hip"]
 
 CXXFLAGS = [

@@ -1,0 +1,721 @@
+// Verify-pass executor: every GEMM of one verify pass in a single persistent
+// launch, for the three weight paths of the method:
+//   SV_PASS_W4     bf16 activations x 4-bit asymmetric group-64 weights
+//   SV_PASS_W8     bf16 activations x 8-bit symmetric per-channel weights
+//   SV_PASS_W4_I8  int8 activations (per-row scale) x 4-bit weights, exact
+//                  int32 group partials
+//
+// Source: Karpathy's Trick for Faster Local LLMs, "Why batch-one decoding is
+// memory-bound" (a pass streams every weight once, so its speed is bandwidth
+// divided by the weight bytes) and "How Uzu optimizes bytes and tokens per
+// pass" (the 4-bit asymmetric and 8-bit symmetric checkpoint tiers; activations
+// quantized to 8 bits so both operands are integers; format and kernels
+// designed together); Local LLM 4x Faster (the int8 matrix path); Speculative
+// Decoding Clearly Explained, "Check the guesses together" (all draft
+// positions scored in one pass).
+//
+// Why one launch: a pass of a 9B-class stack is ~128 GEMMs of 9-57 MB.
+// Launched one by one, each pays the ramp-up and drain of a kernel over 256
+// compute units and the HBM stream stops at every boundary.  Here each
+// workgroup owns a fixed list of work items from all GEMMs and streams them
+// back to back through one software pipeline.
+//
+// Work item = one GEMM x 32 row tiles (512 output channels) x all of K.  Each
+// of the 8 waves owns 4 row tiles for the whole K (no cross-wave reduction).
+// The item advances in chunks of two 1 KiB weight blocks per tile (256 k for
+// 4-bit codes, 128 k for 8-bit codes).  Per step a wave issues:
+//   * 8 weight loads of 1 KiB (one fully contiguous 16-byte-per-lane load each,
+//     already in MFMA operand order: the packed layouts of sv_w4_pack and
+//     sv_w8_pack) into registers;
+//   * for 4-bit weights one 1 KiB buffer -> LDS load of its tiles' scale/zero
+//     records; for W8 / W4_I8 one small buffer -> LDS load of the channel
+//     scales / row scales needed when an item ends;
+//   * its share of the activation chunk (16 or 32 rows), copied once per
+//     workgroup into LDS by buffer -> LDS loads and shared by the 32 tiles.
+// Activation rows sit in LDS with XOR-swizzled 16-byte columns (column j of
+// row r at j ^ (r % 16)), so the 16 lanes reading one MFMA operand hit 16
+// different bank groups.  Chunks flow through a ring of P slots (P - 1 chunks
+// in flight while one computes).  Every step issues the same number of vector
+// memory instructions (out-of-range per-lane offsets where a tile, block or
+// row does not exist; the item's output stores every step, out of range except
+// on its last chunk), so one compile-time vmcnt wait is exact: vector memory
+// operations of a wave complete in issue order.
+//
+// Arithmetic:
+//   W4:    bf16 128 + c from a mask and a byte permute against 0x43;
+//          v_mfma_f32_16x16x32_bf16 per group, an all-ones MFMA for the group
+//          row sums, fold y += s (acc - (128 + z) xsum) in binary32 (exact
+//          (c - z) s for a one-hot row and integer z).
+//   W8:    bf16 128 + c from the biased byte (v_cvt_f32_ubyte, upper half);
+//          the MFMA accumulates over all of K; at the item end
+//          y = s (acc - 128 xsum).
+//   W4_I8: v_mfma_i32_16x16x64_i8 (K depth = one group) gives the exact int32
+//          partial I = sum c xq and, against all-ones bytes, Xg = sum xq;
+//          y += s (I - z Xg) in binary32; at the item end y *= xscale[row].
+#include <algorithm>
+#include <functional>
+#include <queue>
+#include <vector>
+
+#include "w4_packed_dev.h"
+
+namespace {
+
+constexpr uint32_t kPlanMagic = 0x50565653u;   // "SVVP"
+constexpr uint32_t kPlanVersion = 2;
+constexpr int kMaxGrid = 2048;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kNB = 2;                          // 1 KiB weight blocks per tile per step
+constexpr int kTW = 4;                          // row tiles per wave
+constexpr int kItemTiles = kWaves * kTW;        // row tiles per item (512 channels)
+constexpr int kGroup = 64;
+
+template <int F>
+struct Fmt;
+template <>
+struct Fmt<SV_PASS_W4> {
+  static constexpr int KPB = 128;   // k per 1 KiB weight block (16 rows)
+  static constexpr int XE = 2;      // activation bytes per element (bf16)
+  static constexpr int SZD = 1;     // per-step scale/zero load
+  static constexpr int AUXD = 0;    // per-step item-end data load
+};
+template <>
+struct Fmt<SV_PASS_W8> {
+  static constexpr int KPB = 64;
+  static constexpr int XE = 2;
+  static constexpr int SZD = 0;
+  static constexpr int AUXD = 1;    // channel scales
+};
+template <>
+struct Fmt<SV_PASS_W4_I8> {
+  static constexpr int KPB = 128;
+  static constexpr int XE = 1;      // int8 activations
+  static constexpr int SZD = 1;
+  static constexpr int AUXD = 1;    // row scales
+};
+
+inline int fmt_kpb(int f) { return f == SV_PASS_W8 ? 64 : 128; }
+inline int fmt_xe(int f) { return f == SV_PASS_W4_I8 ? 1 : 2; }
+
+struct PlanHeader {                             // 64 bytes
+  uint32_t magic, version;
+  int32_t format, m, count, grid, items, max_steps, reserved0;
+  uint64_t reserved[3];
+};
+struct PlanItem {                               // 64 bytes
+  const void* x;
+  const float* xscale;
+  const uint8_t* codes;
+  const void* sz;
+  float* y;
+  int32_t K, N, tile0, nchunk;
+  uint64_t reserved;
+};
+static_assert(sizeof(PlanHeader) == 64, "plan header layout");
+static_assert(sizeof(PlanItem) == 64, "plan item layout");
+
+// Plan image: header | wg_begin[kMaxGrid + 1] | wg_steps[kMaxGrid] | items.
+constexpr size_t kBeginOff = sizeof(PlanHeader);
+constexpr size_t kStepsOff = kBeginOff + sizeof(int32_t) * (kMaxGrid + 1);
+constexpr size_t kItemsOff = (kStepsOff + sizeof(int32_t) * kMaxGrid + 63) / 64 * 64;
+
+__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+template <int F, int MT>
+struct Geo {
+  static constexpr int KC = kNB * Fmt<F>::KPB;                 // k per chunk
+  static constexpr int XROW = KC * Fmt<F>::XE;                 // LDS bytes per activation row
+  static constexpr int CPR = XROW / 16;                        // 16-byte columns per row
+  static constexpr int RPP = 1024 / XROW;                      // rows per 1 KiB load
+  static constexpr int XPIECES = 16 * MT * XROW / 1024;        // 1 KiB loads per chunk
+  static constexpr int XD = XPIECES >= kWaves ? XPIECES / kWaves : 1;   // per wave
+  static constexpr int XBUF = kWaves * XD * 1024;              // bytes per activation slot
+  static constexpr int SZBUF = Fmt<F>::SZD ? kWaves * 1024 : 0;
+  static constexpr int AUXBUF = Fmt<F>::AUXD ? kWaves * 1024 : 0;
+  static constexpr int SLOT = XBUF + SZBUF + AUXBUF;
+  static_assert(XPIECES % kWaves == 0 || XPIECES < kWaves, "uneven activation split");
+  static_assert(CPR == 16 || CPR == 32, "activation row of 16 or 32 columns");
+};
+
+template <int F, int MT, int P>
+constexpr int pass_lds_bytes() {
+  return P * Geo<F, MT>::SLOT + kWaves * 1024;   // + per-wave output transpose
+}
+
+// 4 int8 codes (one dword) -> 2 dwords of bf16 pairs holding 128 + c.
+__device__ __forceinline__ sv_u32x2 w8_cvt4(unsigned int d) {
+  const unsigned int u = d ^ 0x80808080u;
+  const unsigned int f0 = __float_as_uint(static_cast<float>(u & 0xFFu));
+  const unsigned int f1 = __float_as_uint(static_cast<float>((u >> 8) & 0xFFu));
+  const unsigned int f2 = __float_as_uint(static_cast<float>((u >> 16) & 0xFFu));
+  const unsigned int f3 = __float_as_uint(static_cast<float>(u >> 24));
+  sv_u32x2 r;
+  r.x = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+  r.y = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+  return r;
+}
+
+template <int F, int MT, int P>
+__global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restrict__ plan, int m) {
+  using G = Geo<F, MT>;
+  constexpr int L = kTW * kNB + Fmt<F>::SZD + Fmt<F>::AUXD + G::XD;   // loads per wave per step
+  constexpr int NS = kTW * MT;                  // 16-byte stores per wave per step
+  // At the wait before computing chunk c, the operations issued after chunk
+  // c's loads are the stores of that same step and the loads and stores of
+  // the P - 2 steps after it.
+  constexpr int WAITN = NS + (P - 2) * (L + NS);
+  static_assert(WAITN < 64, "too many memory operations in flight for vmcnt");
+  static_assert(kTW * kNB * 128 == 1024, "one 1 KiB scale/zero load per wave per step");
+  extern __shared__ __align__(16) uint8_t lds[];
+
+  const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(plan);
+  if (hdr->magic != kPlanMagic || hdr->format != F || hdr->m != m ||
+      hdr->grid != static_cast<int>(gridDim.x))
+    return;                                     // stale or foreign plan: touch nothing
+  const int32_t* wg_begin = reinterpret_cast<const int32_t*>(plan + kBeginOff);
+  const int32_t* wg_steps = reinterpret_cast<const int32_t*>(plan + kStepsOff);
+  const PlanItem* items = reinterpret_cast<const PlanItem*>(plan + kItemsOff);
+  const int ib = wg_begin[blockIdx.x];
+  const int ie = wg_begin[blockIdx.x + 1];
+  const int steps = wg_steps[blockIdx.x];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15;
+  const int q = lane >> 4;
+  const unsigned int magic = sv_opaque_u32(0x43434343u);
+  const sv_u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const sv_u32x4 ones8 = {0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
+  const sv_f32x4 fz = {0.f, 0.f, 0.f, 0.f};
+  const sv_i32x4 iz = {0, 0, 0, 0};
+  float* const tpose = reinterpret_cast<float*>(lds + P * G::SLOT) + wave * 256;
+
+  // ---- issue cursor: the item and chunk whose loads go out next ----
+  int i_item = ib, i_c = 0;
+  int i_K = 128, i_N = 16, i_t0 = 0, i_nchunk = 1;
+  __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0x00020000);
+  __amdgpu_buffer_rsrc_t srs = wrs, xrs = wrs, ars = wrs;
+  auto load_issue_item = [&](int idx) {
+    const PlanItem it = items[idx];
+    i_K = it.K;
+    i_N = it.N;
+    i_t0 = it.tile0;
+    i_nchunk = it.nchunk;
+    wrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(it.codes), 0,
+                                            F == SV_PASS_W8 ? it.N * it.K : it.N * (it.K / 2),
+                                            0x00020000);
+    if constexpr (Fmt<F>::SZD)
+      srs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(it.sz), 0,
+                                              it.N * (it.K / kGroup) * 4, 0x00020000);
+    if constexpr (F == SV_PASS_W8)
+      ars = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(it.sz), 0, it.N * 2, 0x00020000);
+    if constexpr (F == SV_PASS_W4_I8)
+      ars = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(it.xscale), 0, m * 4,
+                                              0x00020000);
+    xrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(it.x), 0, m * it.K * Fmt<F>::XE,
+                                            0x00020000);
+  };
+  // ---- compute cursor: the item and chunk computed next ----
+  int c_item = ib, c_c = 0;
+  int c_K = 128, c_N = 16, c_t0 = 0, c_nchunk = 1;
+  __amdgpu_buffer_rsrc_t yrs = wrs;
+  auto load_compute_item = [&](int idx) {
+    const PlanItem it = items[idx];
+    c_K = it.K;
+    c_N = it.N;
+    c_t0 = it.tile0;
+    c_nchunk = it.nchunk;
+    yrs = __builtin_amdgcn_make_buffer_rsrc(it.y, 0, m * it.N * 4, 0x00020000);
+  };
+  if (ib < ie) {
+    load_issue_item(ib);
+    load_compute_item(ib);
+  }
+
+  sv_u32x4 wb[P][kTW][kNB];
+  sv_f32x4 yacc[kTW][MT];
+  sv_f32x4 xacc[MT];                            // W8: running activation row sums
+#pragma unroll
+  for (int a = 0; a < MT; ++a) {
+    xacc[a] = fz;
+#pragma unroll
+    for (int t = 0; t < kTW; ++t) yacc[t][a] = fz;
+  }
+
+  // All L loads of the issue cursor's chunk into `slot` (out-of-range
+  // offsets once the cursor has run past the last item).
+  auto issue = [&](const int slot) {
+    const bool live = i_item < ie;
+    const int KB = i_K / Fmt<F>::KPB;           // weight blocks per tile row
+    const int jb = i_c * kNB;
+    const int ntile = i_N >> 4;
+    uint8_t* const sl = lds + slot * G::SLOT;
+#pragma unroll
+    for (int tw = 0; tw < kTW; ++tw) {
+      const int tile = i_t0 + wave * kTW + tw;
+#pragma unroll
+      for (int b = 0; b < kNB; ++b) {
+        const bool ok = live && tile < ntile && jb + b < KB;
+        wb[slot][tw][b] = __builtin_amdgcn_raw_buffer_load_b128(
+            wrs, ok ? lane * 16 : kSvOutOfRange, ok ? (tile * KB + jb + b) * 1024 : 0, 0);
+      }
+    }
+    if constexpr (Fmt<F>::SZD) {
+      // scale/zero records of this wave's tiles, one 128-byte record per
+      // (tile, 128-wide k block): lane -> tile lane / 16, block (lane / 8) % 2,
+      // 16-byte piece lane % 8
+      const int tw = lane >> 4, bb = (lane >> 3) & 1;
+      const int tile = i_t0 + wave * kTW + tw;
+      const bool ok = live && tile < ntile && jb + bb < KB;
+      const unsigned int off =
+          ok ? (tile * KB + jb + bb) * 128 + (lane & 7) * 16 : kSvOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          srs, (sv_lds_void*)(sl + G::XBUF + wave * 1024), 16, off, 0, 0, 0);
+    }
+    if constexpr (F == SV_PASS_W8) {
+      // the 64 channel scales of this wave's tiles (lanes 0-7, 16 bytes each)
+      const bool ok = live && lane < 8 && i_t0 + wave * kTW + (lane >> 1) < ntile;
+      const unsigned int off = ok ? (i_t0 + wave * kTW) * 32 + lane * 16 : kSvOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ars, (sv_lds_void*)(sl + G::XBUF + G::SZBUF + wave * 1024), 16, off, 0, 0, 0);
+    }
+    if constexpr (F == SV_PASS_W4_I8) {
+      // the row scales (lanes 0 .. 4 MT - 1, four rows each)
+      const bool ok = live && lane < 4 * MT;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ars, (sv_lds_void*)(sl + G::XBUF + G::SZBUF + wave * 1024), 16,
+          ok ? lane * 16 : kSvOutOfRange, 0, 0, 0);
+    }
+    const int k0 = i_c * G::KC;
+#pragma unroll
+    for (int i = 0; i < G::XD; ++i) {
+      // rows RPP p .. RPP p + RPP - 1 of the chunk; lane -> row RPP p +
+      // lane / CPR, stored column lane % CPR, read from column
+      // (lane % CPR) ^ (row % 16).  Rows >= m are not read (they only feed
+      // discarded output rows); columns past K land in the next row (never
+      // read) or fail the range check.
+      const int piece = wave + kWaves * i;
+      const int r = G::RPP * piece + lane / G::CPR;
+      const int jj = (lane % G::CPR) ^ (r & 15);
+      const unsigned int off = live && r < m && r < 16 * MT
+                                   ? (r * i_K + k0) * Fmt<F>::XE + jj * 16
+                                   : kSvOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (sv_lds_void*)(sl + piece * 1024), 16, off,
+                                               0, 0, 0);
+    }
+  };
+  auto advance_issue = [&]() {
+    if (++i_c == i_nchunk) {
+      i_c = 0;
+      if (++i_item < ie) load_issue_item(i_item);
+    }
+  };
+
+  // Byte offset of this lane's 16-byte A operand for logical column j of
+  // row col (+ 16 a rows): swizzled column j ^ col.
+  auto aaddr = [&](const int j) { return col * G::XROW + ((j ^ col) << 4); };
+
+  auto compute = [&](const int slot) {
+    const int KB = c_K / Fmt<F>::KPB;
+    const int jb = c_c * kNB;
+    const uint8_t* const sl = lds + slot * G::SLOT;
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+      if (jb + b >= KB) break;
+      if constexpr (F == SV_PASS_W4) {
+        const uint8_t* sp = sl + G::XBUF + wave * 1024 + col * 8;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {           // the two groups of the block
+          sv_u32x4 a0[MT], a1[MT];
+          sv_f32x4 xs[MT];
+#pragma unroll
+          for (int a = 0; a < MT; ++a) {
+            const uint8_t* ap = sl + a * 16 * G::XROW;
+            a0[a] = *reinterpret_cast<const sv_u32x4*>(ap + aaddr(16 * b + 8 * h + 2 * q));
+            a1[a] = *reinterpret_cast<const sv_u32x4*>(ap + aaddr(16 * b + 8 * h + 2 * q + 1));
+            xs[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a0[a]),
+                                                            sv_as_bf16x8(ones), fz, 0, 0, 0);
+            xs[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a1[a]),
+                                                            sv_as_bf16x8(ones), xs[a], 0, 0, 0);
+          }
+#pragma unroll
+          for (int tw = 0; tw < kTW; ++tw) {
+            const sv_u32x4 w = wb[slot][tw][b];
+            const sv_u32x4 b0 = sv_w4_dequant8(h ? w.z : w.x, magic);
+            const sv_u32x4 b1 = sv_w4_dequant8(h ? w.w : w.y, magic);
+            const sv_u32x2 sbt =
+                *reinterpret_cast<const sv_u32x2*>(sp + (tw * kNB + b) * 128);
+            const unsigned int sz = h ? sbt.y : sbt.x;
+            const float s = sv_half_lo(sz);
+            const float zb = 128.0f + sv_half_hi(sz);
+#pragma unroll
+            for (int a = 0; a < MT; ++a) {
+              sv_f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  sv_as_bf16x8(a0[a]), sv_as_bf16x8(b0), fz, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a1[a]),
+                                                            sv_as_bf16x8(b1), acc, 0, 0, 0);
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                yacc[tw][a][i] = fmaf(s, fmaf(-zb, xs[a][i], acc[i]), yacc[tw][a][i]);
+            }
+          }
+        }
+      } else if constexpr (F == SV_PASS_W8) {
+        sv_u32x4 a0[MT], a1[MT];
+#pragma unroll
+        for (int a = 0; a < MT; ++a) {
+          const uint8_t* ap = sl + a * 16 * G::XROW;
+          a0[a] = *reinterpret_cast<const sv_u32x4*>(ap + aaddr(8 * b + 2 * q));
+          a1[a] = *reinterpret_cast<const sv_u32x4*>(ap + aaddr(8 * b + 2 * q + 1));
+          xacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a0[a]),
+                                                            sv_as_bf16x8(ones), xacc[a], 0, 0, 0);
+          xacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a1[a]),
+                                                            sv_as_bf16x8(ones), xacc[a], 0, 0, 0);
+        }
+#pragma unroll
+        for (int tw = 0; tw < kTW; ++tw) {
+          const sv_u32x4 w = wb[slot][tw][b];
+          const sv_u32x2 l0 = w8_cvt4(w.x), l1 = w8_cvt4(w.y);
+          const sv_u32x2 h0 = w8_cvt4(w.z), h1 = w8_cvt4(w.w);
+          const sv_u32x4 b0 = {l0.x, l0.y, l1.x, l1.y};
+          const sv_u32x4 b1 = {h0.x, h0.y, h1.x, h1.y};
+#pragma unroll
+          for (int a = 0; a < MT; ++a) {
+            yacc[tw][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                sv_as_bf16x8(a0[a]), sv_as_bf16x8(b0), yacc[tw][a], 0, 0, 0);
+            yacc[tw][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                sv_as_bf16x8(a1[a]), sv_as_bf16x8(b1), yacc[tw][a], 0, 0, 0);
+          }
+        }
+      } else {                                  // SV_PASS_W4_I8
+        const uint8_t* sp = sl + G::XBUF + wave * 1024 + col * 8;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          sv_u32x4 a8[MT];
+          sv_f32x4 xg[MT];
+#pragma unroll
+          for (int a = 0; a < MT; ++a) {
+            a8[a] = *reinterpret_cast<const sv_u32x4*>(sl + a * 16 * G::XROW +
+                                                       aaddr(8 * b + 4 * h + q));
+            const sv_i32x4 g = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                sv_as_i32x4(a8[a]), sv_as_i32x4(ones8), iz, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xg[a][i] = static_cast<float>(g[i]);
+          }
+#pragma unroll
+          for (int tw = 0; tw < kTW; ++tw) {
+            const sv_u32x4 w = wb[slot][tw][b];
+            const unsigned int wx = h ? w.z : w.x, wy = h ? w.w : w.y;
+            // packed word (byte b = codes b | b+4 << 4): low nibbles are codes
+            // 0..3, high nibbles 4..7, as bytes in natural order
+            const sv_u32x4 bw = {wx & 0x0F0F0F0Fu, (wx >> 4) & 0x0F0F0F0Fu, wy & 0x0F0F0F0Fu,
+                                 (wy >> 4) & 0x0F0F0F0Fu};
+            const sv_u32x2 sbt =
+                *reinterpret_cast<const sv_u32x2*>(sp + (tw * kNB + b) * 128);
+            const unsigned int sz = h ? sbt.y : sbt.x;
+            const float s = sv_half_lo(sz);
+            const float z = sv_half_hi(sz);
+#pragma unroll
+            for (int a = 0; a < MT; ++a) {
+              const sv_i32x4 I = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                  sv_as_i32x4(a8[a]), sv_as_i32x4(bw), iz, 0, 0, 0);
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                yacc[tw][a][i] =
+                    fmaf(s, fmaf(-z, xg[a][i], static_cast<float>(I[i])), yacc[tw][a][i]);
+            }
+          }
+        }
+      }
+    }
+  };
+
+  // NS stores every step.  On an item's last chunk: the epilogue of the
+  // format, then each 16x16 output tile goes through the wave's LDS
+  // transpose area (lane (col, q) of an MFMA output holds rows 4q .. 4q+3 of
+  // channel col) so that lane l stores channels 4 (l % 4) .. +3 of row l / 4
+  // as one 16-byte write.  Otherwise the same number of stores with
+  // out-of-range offsets.
+  auto store = [&](const int slot, const bool at_end) {
+    if (at_end) {
+      const uint8_t* aux = lds + slot * G::SLOT + G::XBUF + G::SZBUF + wave * 1024;
+#pragma unroll
+      for (int tw = 0; tw < kTW; ++tw) {
+        const int tile = c_t0 + wave * kTW + tw;
+#pragma unroll
+        for (int a = 0; a < MT; ++a) {
+          sv_f32x4 v = yacc[tw][a];
+          if constexpr (F == SV_PASS_W8) {
+            const float s = __half2float(
+                *reinterpret_cast<const __half*>(aux + (tw * 16 + col) * 2));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = s * fmaf(-128.0f, xacc[a][i], v[i]);
+          }
+          if constexpr (F == SV_PASS_W4_I8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              v[i] *= *reinterpret_cast<const float*>(aux + (16 * a + 4 * q + i) * 4);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tpose[(4 * q + i) * 16 + col] = v[i];
+          const sv_u32x4 o =
+              *reinterpret_cast<const sv_u32x4*>(tpose + (lane >> 2) * 16 + 4 * (lane & 3));
+          const int r = 16 * a + (lane >> 2);
+          const bool ok = tile < (c_N >> 4) && r < m;
+          const unsigned int off =
+              ok ? (r * c_N + 16 * tile + 4 * (lane & 3)) * 4 : kSvOutOfRange;
+          __builtin_amdgcn_raw_buffer_store_b128(o, yrs, off, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < MT; ++a) {
+        xacc[a] = fz;
+#pragma unroll
+        for (int t = 0; t < kTW; ++t) yacc[t][a] = fz;
+      }
+    } else {
+#pragma unroll
+      for (int tw = 0; tw < kTW; ++tw)
+#pragma unroll
+        for (int a = 0; a < MT; ++a)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(sv_u32x4, yacc[tw][a]), yrs,
+                                                 kSvOutOfRange, 0, 0);
+    }
+  };
+  auto advance_compute = [&]() {
+    if (++c_c == c_nchunk) {
+      c_c = 0;
+      if (++c_item < ie) load_compute_item(c_item);
+    }
+  };
+
+  // Prologue: P - 1 chunks in flight, each followed by a step's worth of
+  // (out-of-range) stores so every step sees the same operation pattern.
+#pragma unroll
+  for (int i = 0; i < P - 1; ++i) {
+    issue(i);
+    advance_issue();
+    sv_compiler_fence();
+    store(0, false);
+  }
+  for (int s0 = 0; s0 < steps; s0 += P) {
+#pragma unroll
+    for (int s = 0; s < P; ++s) {
+      // chunk s0 + s has landed in slot s (registers and LDS) for every wave,
+      // and every wave has finished the chunk that last used slot s + P - 1
+      sv_wait_vmcnt<WAITN>();
+      sv_barrier_no_fence();
+      issue((s + P - 1) % P);
+      advance_issue();
+      sv_compiler_fence();
+      const bool run = s0 + s < steps;
+      const bool at_end = run && c_c == c_nchunk - 1;
+      if (run) compute(s);
+      store(s, at_end);
+      if (run) advance_compute();
+    }
+  }
+  // Drain every outstanding load (including buffer -> LDS copies) before the
+  // workgroup's LDS can be handed to another workgroup.
+  sv_wait_vmcnt<0>();
+  sv_barrier_no_fence();
+}
+
+template <int F, int MT, int P>
+sv_status launch_pass(const void* plan, int m, int grid, hipStream_t st) {
+  auto kern = pass_kernel<F, MT, P>;
+  constexpr int kLds = pass_lds_bytes<F, MT, P>();
+  static_assert(kLds <= 160 * 1024, "LDS budget of a gfx950 workgroup");
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess)
+    return SV_ERR_HIP;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), kLds, st,
+                     static_cast<const uint8_t*>(plan), m);
+  SV_LAUNCH_CHECK();
+  return SV_OK;
+}
+
+sv_status check_gemms(int format, const sv_pass_gemm* gemms, int count, int m,
+                      long long* n_items) {
+  if (format != SV_PASS_W4 && format != SV_PASS_W8 && format != SV_PASS_W4_I8)
+    return SV_ERR_INVALID_ARG;
+  if (!gemms) return SV_ERR_NULL;
+  if (count < 1 || m < 1 || m > SV_MAX_ROWS) return SV_ERR_INVALID_ARG;
+  const int kpb = fmt_kpb(format), xe = fmt_xe(format);
+  long long items = 0;
+  for (int g = 0; g < count; ++g) {
+    const sv_pass_gemm& e = gemms[g];
+    if (!e.x || !e.codes || !e.scales || !e.y) return SV_ERR_NULL;
+    if ((format == SV_PASS_W4_I8) != (e.xscale != nullptr))
+      return e.xscale ? SV_ERR_INVALID_ARG : SV_ERR_NULL;
+    if (e.N < 16 || e.N % 16 != 0 || e.K < kpb || e.K % kpb != 0) return SV_ERR_INVALID_ARG;
+    // buffer ranges are 32-bit: codes, activations and outputs below 2 GiB
+    const long long code_bytes = static_cast<long long>(e.N) * e.K / (format == SV_PASS_W8 ? 1 : 2);
+    if (code_bytes >= (1LL << 31) || static_cast<long long>(m) * e.K * xe >= (1LL << 31) ||
+        static_cast<long long>(m) * e.N * 4 >= (1LL << 31))
+      return SV_ERR_UNSUPPORTED;
+    if (!sv_aligned16(e.x) || !sv_aligned16(e.codes) || !sv_aligned16(e.scales) ||
+        !sv_aligned16(e.y) || (e.xscale && !sv_aligned16(e.xscale)))
+      return SV_ERR_ALIGN;
+    items += ceil_div(e.N / 16, kItemTiles);
+  }
+  if (items >= (1LL << 30)) return SV_ERR_UNSUPPORTED;
+  *n_items = items;
+  return SV_OK;
+}
+
+}  // namespace
+
+extern "C" size_t sv_pass_plan_bytes(int format, const sv_pass_gemm* gemms, int count, int m) {
+  long long items = 0;
+  if (check_gemms(format, gemms, count, m, &items) != SV_OK) return 0;
+  return kItemsOff + static_cast<size_t>(items) * sizeof(PlanItem);
+}
+
+extern "C" sv_status sv_pass_plan(int format, const sv_pass_gemm* gemms, int count, int m,
+                                  int group, void* plan, size_t plan_bytes, sv_pass* pass,
+                                  hipStream_t stream) {
+  long long n_items = 0;
+  const sv_status st = check_gemms(format, gemms, count, m, &n_items);
+  if (st != SV_OK) return st;
+  if (!plan || !pass) return SV_ERR_NULL;
+  if (format != SV_PASS_W8 && group != kGroup) return SV_ERR_UNSUPPORTED;
+  if (!sv_aligned16(plan)) return SV_ERR_ALIGN;
+  const size_t need = kItemsOff + static_cast<size_t>(n_items) * sizeof(PlanItem);
+  if (plan_bytes < need) return SV_ERR_WORKSPACE;
+
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    return SV_ERR_HIP;
+  // One workgroup of 8 waves per compute unit; never more workgroups than items.
+  const int grid = static_cast<int>(std::min<long long>({cus, kMaxGrid, n_items}));
+  const int kc = kNB * fmt_kpb(format);
+
+  // Items in pass order.
+  std::vector<PlanItem> items;
+  items.reserve(static_cast<size_t>(n_items));
+  for (int g = 0; g < count; ++g) {
+    const sv_pass_gemm& e = gemms[g];
+    const int tiles = e.N / 16;
+    for (int t0 = 0; t0 < tiles; t0 += kItemTiles)
+      items.push_back(PlanItem{e.x, e.xscale, e.codes, e.scales, e.y, e.K, e.N, t0,
+                               ceil_div(e.K, kc), 0});
+  }
+  // Longest-first greedy: each item (by chunk count, ties in pass order) goes
+  // to the workgroup with the fewest chunks so far (ties: lowest index).
+  std::vector<int> order(items.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = static_cast<int>(i);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int a, int b) { return items[a].nchunk > items[b].nchunk; });
+  typedef std::pair<long long, int> Load;
+  std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
+  for (int w = 0; w < grid; ++w) heap.push(Load(0, w));
+  std::vector<std::vector<int>> owned(grid);
+  for (int i : order) {
+    Load l = heap.top();
+    heap.pop();
+    owned[l.second].push_back(i);
+    l.first += items[i].nchunk;
+    heap.push(l);
+  }
+
+  std::vector<uint8_t> image(need, 0);
+  PlanHeader* hdr = reinterpret_cast<PlanHeader*>(image.data());
+  int32_t* wg_begin = reinterpret_cast<int32_t*>(image.data() + kBeginOff);
+  int32_t* wg_steps = reinterpret_cast<int32_t*>(image.data() + kStepsOff);
+  PlanItem* out = reinterpret_cast<PlanItem*>(image.data() + kItemsOff);
+  int pos = 0, max_steps = 0;
+  for (int w = 0; w < grid; ++w) {
+    std::sort(owned[w].begin(), owned[w].end());   // pass order inside a workgroup
+    wg_begin[w] = pos;
+    long long s = 0;
+    for (int i : owned[w]) {
+      out[pos++] = items[i];
+      s += items[i].nchunk;
+    }
+    if (s >= (1LL << 30)) return SV_ERR_UNSUPPORTED;
+    wg_steps[w] = static_cast<int32_t>(s);
+    max_steps = std::max(max_steps, static_cast<int>(s));
+  }
+  wg_begin[grid] = pos;
+  hdr->magic = kPlanMagic;
+  hdr->version = kPlanVersion;
+  hdr->format = format;
+  hdr->m = m;
+  hdr->count = count;
+  hdr->grid = grid;
+  hdr->items = static_cast<int32_t>(n_items);
+  hdr->max_steps = max_steps;
+
+  // Plan upload: a setup step (like packing the weights), synchronous so the
+  // host image can be released.
+  if (hipMemcpyAsync(plan, image.data(), need, hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return SV_ERR_HIP;
+  pass->plan = plan;
+  pass->format = format;
+  pass->m = m;
+  pass->count = count;
+  pass->grid = grid;
+  pass->items = static_cast<int>(n_items);
+  pass->max_steps = max_steps;
+  return SV_OK;
+}
+
+extern "C" sv_status sv_pass_run(const sv_pass* pass, hipStream_t stream) {
+  if (!pass || !pass->plan) return SV_ERR_NULL;
+  if (!sv_aligned16(pass->plan)) return SV_ERR_ALIGN;
+  if (pass->m < 1 || pass->m > SV_MAX_ROWS || pass->grid < 1 || pass->grid > kMaxGrid)
+    return SV_ERR_INVALID_ARG;
+  // Two activation tiles for m > 16.  The ring keeps three chunks in flight
+  // (two for the 4-bit bf16 path at m > 16, whose registers would not hold a
+  // third).
+  const bool two = pass->m > 16;
+  switch (pass->format) {
+    case SV_PASS_W4:
+      return two ? launch_pass<SV_PASS_W4, 2, 3>(pass->plan, pass->m, pass->grid, stream)
+                 : launch_pass<SV_PASS_W4, 1, 4>(pass->plan, pass->m, pass->grid, stream);
+    case SV_PASS_W8:
+      return two ? launch_pass<SV_PASS_W8, 2, 4>(pass->plan, pass->m, pass->grid, stream)
+                 : launch_pass<SV_PASS_W8, 1, 4>(pass->plan, pass->m, pass->grid, stream);
+    case SV_PASS_W4_I8:
+      return two ? launch_pass<SV_PASS_W4_I8, 2, 4>(pass->plan, pass->m, pass->grid, stream)
+                 : launch_pass<SV_PASS_W4_I8, 1, 4>(pass->plan, pass->m, pass->grid, stream);
+    default:
+      return SV_ERR_INVALID_ARG;
+  }
+}
+
+// ---- W8 packing -------------------------------------------------------------
+namespace {
+// One 16-byte piece per thread: block (t, j), lane l of the wave that reads it.
+__global__ void pack_w8_kernel(const int8_t* __restrict__ codes, int N, int K,
+                               uint8_t* __restrict__ out) {
+  const size_t piece = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int KB = K / 64;
+  const size_t total = static_cast<size_t>(N / 16) * KB * 64;
+  if (piece >= total) return;
+  const int l = static_cast<int>(piece & 63);
+  const size_t blk = piece >> 6;
+  const int j = static_cast<int>(blk % KB);
+  const int t = static_cast<int>(blk / KB);
+  const int n = 16 * t + (l & 15), q = l >> 4;
+  const sv_u32x4 v = sv_ld16(codes + static_cast<size_t>(n) * K + 64 * j + 16 * q);
+  *reinterpret_cast<sv_u32x4*>(out + piece * 16) = v;
+}
+}  // namespace
+
+extern "C" sv_status sv_w8_pack(const int8_t* codes, int N, int K, uint8_t* packed_codes,
+                                hipStream_t stream) {
+  if (!codes || !packed_codes) return SV_ERR_NULL;
+  if (N < 16 || N % 16 != 0 || K < 64 || K % 64 != 0) return SV_ERR_INVALID_ARG;
+  if (!sv_aligned16(codes) || !sv_aligned16(packed_codes)) return SV_ERR_ALIGN;
+  const size_t pieces = static_cast<size_t>(N / 16) * (K / 64) * 64;
+  hipLaunchKernelGGL(pack_w8_kernel, dim3(static_cast<unsigned>((pieces + 255) / 256)),
+                     dim3(256), 0, stream, codes, N, K, packed_codes);
+  SV_LAUNCH_CHECK();
+  return SV_OK;
+}

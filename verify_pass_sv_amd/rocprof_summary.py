@@ -2,7 +2,7 @@
 
     python -m verify_pass_sv_amd.rocprof_summary \
         --trace gpurun_out/prof_kt --pmc gpurun_out/prof_pmc \
-        --kernel w4_pass_kernel --copy-bytes 268435456 \
+        --kernel pass_kernel --copy-bytes 268435456 \
         --command "<the rocprofv3 command lines>" --out profiles/<name>
 
 Reads `*_kernel_stats.csv` (rocprofv3 --kernel-trace --stats) and every
@@ -25,7 +25,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 # Sources whose change makes recorded counters stale, per kernel family.
 KERNEL_SOURCES = {
-    "w4_pass_kernel": ["csrc/w4_pass.hip", "csrc/w4_packed_dev.h", "csrc/sv_common.h"],
+    "pass_kernel": ["csrc/pass.hip", "csrc/w4_packed_dev.h", "csrc/sv_common.h"],
 }
 
 
