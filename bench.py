@@ -101,24 +101,6 @@ def time_graph(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps, g
 
 
-def per_launch_durations(torch, launches, reps):
-    """Event-bracketed duration of each launch (stream order), averaged over reps."""
-    import collections
-    acc = collections.defaultdict(list)
-    for _ in range(reps):
-        evs = []
-        for key, fn in launches:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            evs.append((key, a, b))
-        torch.cuda.synchronize()
-        for key, a, b in evs:
-            acc[key].append(a.elapsed_time(b))
-    return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) // reps for k, v in acc.items()}
-
-
 def recorded_traffic(name, k):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel reading), or None
@@ -313,64 +295,82 @@ def main():
         # the same pass as 128 separate launches (packed and row-major layouts)
         for key, packed in (("w4_per_gemm_launches", True), ("w4_row_major_launches", False)):
             Ls = w4_launches(k, packed=packed)
-            ms_l, _ = time_graph(torch, lambda Ls=Ls: [fn() for _, fn in Ls], 10, 2)
+            ms_l, _ = time_graph(torch, lambda Ls=Ls: [fn() for _, fn in Ls], 20, 20)
             extra[key] = {"pass_ms": round(ms_l, 4),
                           "GBps": round(pass_bytes / (ms_l * 1e-3) / 1e9, 1)}
         # W4 k sweep: memory-bound to MFMA crossover, latency ratio
         sweep = {}
         for kk in (1, 4, 8, 16, 32):
             pk = w4_pass(kk)
-            ms, _ = time_graph(torch, lambda pk=pk: sv.sv_pass_run(pk), 10, 2)
+            ms, _ = time_graph(torch, lambda pk=pk: sv.sv_pass_run(pk), 60, 60)
             sweep[kk] = {"pass_ms": round(ms, 4), "GBps": round(pass_bytes / (ms * 1e-3) / 1e9, 1),
                          "drafted_tok_s": round(kk / (ms * 1e-3), 1)}
         extra["w4_k_sweep"] = sweep
         extra["w4_latency_ratio_k32_over_k1"] = round(sweep[32]["pass_ms"] / sweep[1]["pass_ms"], 3)
         log("int8 path")
-        # int8 path: Hadamard (block 4096) + int8 W4 GEMM per input, 32 layers
+        # int8 path: every activation row of the pass (4 inputs per layer, 41 or
+        # 123 outlier channels x50) rotated by the block-4096 Hadamard and
+        # quantized per token -- batched into one call per input width -- then
+        # all 128 int8 x W4 GEMMs in one executor launch
+        n_h, n_f = 3 * LAYERS, LAYERS               # qkv, o, gate|up inputs; down inputs
         signs_h = synth.hadamard_signs(HIDDEN, seed=3, device=dev)
         signs_f = synth.hadamard_signs(FFN, seed=4, device=dev)
-        xo_h, _ = synth.outlier_activations(k, HIDDEN, seed=5, device=dev)
-        xo_f, _ = synth.outlier_activations(k, FFN, seed=6, device=dev)
-        xq_h = torch.empty((k, HIDDEN), dtype=torch.int8, device=dev)
-        xq_f = torch.empty((k, FFN), dtype=torch.int8, device=dev)
-        sc_h = torch.empty((k,), dtype=torch.float32, device=dev)
-        sc_f = torch.empty((k,), dtype=torch.float32, device=dev)
+        xo_h = torch.cat([synth.outlier_activations(k, HIDDEN, seed=500 + i, device=dev)[0]
+                          for i in range(n_h)])
+        xo_f = torch.cat([synth.outlier_activations(k, FFN, seed=700 + i, device=dev)[0]
+                          for i in range(n_f)])
+        xq_h = torch.empty((n_h * k, HIDDEN), dtype=torch.int8, device=dev)
+        xq_f = torch.empty((n_f * k, FFN), dtype=torch.int8, device=dev)
+        sc_h = torch.empty((n_h * k,), dtype=torch.float32, device=dev)
+        sc_f = torch.empty((n_f * k,), dtype=torch.float32, device=dev)
+        gi8, ih, jf = [], 0, 0
+        for li, layer in enumerate(w4):
+            for gi, (name, N, K, c, s, z, pc, ps) in enumerate(layer):
+                if K == HIDDEN:
+                    xq, xs = xq_h[ih * k:(ih + 1) * k], sc_h[ih * k:(ih + 1) * k]
+                    ih += 1
+                else:
+                    xq, xs = xq_f[jf * k:(jf + 1) * k], sc_f[jf * k:(jf + 1) * k]
+                    jf += 1
+                gi8.append((xq, xs, pc, ps, N, y_own[li][gi][:k]))
+        p8 = sv.sv_pass_plan("w4_i8", gi8)
+
+        def rotate():
+            sv.sv_hadamard_i8(xo_h, signs_h, 4096, xq_h, sc_h)
+            sv.sv_hadamard_i8(xo_f, signs_f, 4096, xq_f, sc_f)
 
         def int8_pass():
-            for layer in w4:
-                for (name, N, K, c, s, z, _pc, _ps) in layer:
-                    if K == HIDDEN:
-                        sv.sv_hadamard_i8(xo_h, signs_h, 4096, xq_h, sc_h)
-                        sv.sv_qgemm_w4_i8(xq_h, sc_h, c, s, z, ys[N][:k])
-                    else:
-                        sv.sv_hadamard_i8(xo_f, signs_f, 4096, xq_f, sc_f)
-                        sv.sv_qgemm_w4_i8(xq_f, sc_f, c, s, z, ys[N][:k])
+            rotate()
+            sv.sv_pass_run(p8)
 
-        ms_i8, _ = time_graph(torch, int8_pass, 10, 2)
-        had = [(("had", K, 0), (lambda xx=xx, sg=sg, q=q, sc=sc: sv.sv_hadamard_i8(xx, sg, 4096, q, sc)))
-               for xx, sg, q, sc, K in ((xo_h, signs_h, xq_h, sc_h, HIDDEN),
-                                         (xo_f, signs_f, xq_f, sc_f, FFN))]
-        hd, _ = per_launch_durations(torch, had * 8, reps=2)
+        ms_i8, _ = time_graph(torch, int8_pass, 60, 60)
+        ms_i8g, _ = time_graph(torch, lambda: sv.sv_pass_run(p8), 60, 60)
+        ms_rot, _ = time_graph(torch, rotate, 20, 5)
         extra["int8_path"] = {"pass_ms": round(ms_i8, 4),
                               "GBps": round(pass_bytes / (ms_i8 * 1e-3) / 1e9, 1),
-                              "hadamard_us": {f"K{key[1]}": round(v * 1e3, 2)
-                                              for key, v in hd.items()}}
+                              "gemm_launch_ms": round(ms_i8g, 4),
+                              "gemm_GBps": round(pass_bytes / (ms_i8g * 1e-3) / 1e9, 1),
+                              "hadamard_ms_all_rows": round(ms_rot, 4),
+                              "hadamard_rows": int((n_h + n_f) * k)}
+        del xo_h, xo_f
         log("W8 k sweep")
-        # W8 k sweep
+        # W8 k sweep on the executor (8-bit stack packed once)
         w8 = make_w8_stack(torch, synth, dev)
         b8 = w8_bytes(w8)
+        w8p = [[(N, K, sv.sv_w8_pack(c), s) for (name, N, K, c, s) in layer] for layer in w8]
+        del w8
         sweep8 = {}
         for kk in (1, 4, 8, 16, 32):
             xh, xf = x_h[:kk].contiguous(), x_f[:kk].contiguous()
-            L = []
-            for layer in w8:
-                for (name, N, K, c, s) in layer:
-                    L.append((xh if K == HIDDEN else xf, c, s, ys[N][:kk]))
-            ms, _ = time_graph(torch, lambda L=L: [sv.sv_qgemm_w8(a, c, s, y) for a, c, s, y in L],
-                               10, 2)
+            g8 = [(xh if K == HIDDEN else xf, pc, s, N, y_own[li][gi][:kk])
+                  for li, layer in enumerate(w8p) for gi, (N, K, pc, s) in enumerate(layer)]
+            pk = sv.sv_pass_plan("w8", g8)
+            ms, _ = time_graph(torch, lambda pk=pk: sv.sv_pass_run(pk), 40, 40)
             sweep8[kk] = {"pass_ms": round(ms, 4), "GBps": round(b8 / (ms * 1e-3) / 1e9, 1)}
         extra["w8_k_sweep"] = sweep8
-        del w8
+        extra["w8_latency_ratio_k32_over_k1"] = round(sweep8[32]["pass_ms"] /
+                                                      sweep8[1]["pass_ms"], 3)
+        del w8p
         log("accept statistics")
         # accept statistics: 4096 trials per noise level, k = 32
         stats = {}

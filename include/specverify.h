@@ -226,7 +226,8 @@ sv_status sv_pass_run(const sv_pass* pass, hipStream_t stream);
  *
  *   Y[r, n] = S[n] * sum_k X[r, k] * C[n, k]
  *
- *   x       bf16 [m, K], m in 1 .. SV_MAX_ROWS, K % 64 == 0
+ *   x       bf16 [m, K], m in 1 .. 2^20 (rows are independent tokens; a
+ *           verify pass may batch all its activation rows in one call), K % 64 == 0
  *   codes   int8 [N, K], values in [-127, 127] (-128 is rejected by nothing
  *           but is outside the format; it dequantizes as -128 * S)
  *   scales  f16 [N]
@@ -252,7 +253,8 @@ sv_status sv_qgemm_w8(const void* x, int m, int K, const int8_t* codes,
  * The rotation is summed in binary64 and rounded once to binary32; the scale
  * and the rounding decision are binary32.
  *
- *   x       bf16 [m, K], m in 1 .. SV_MAX_ROWS
+ *   x       bf16 [m, K], m in 1 .. 2^20 (rows are independent tokens; a
+ *           verify pass may batch all its activation rows in one call)
  *   signs   int8 [K], each +1 or -1 (other values are used as given)
  *   block   power of two, 2 <= block <= 4096, block divides K
  *   K       K % 64 == 0, K <= 16384

@@ -86,7 +86,8 @@ __global__ __launch_bounds__(kThreads) void hadamard_i8_kernel(
 extern "C" sv_status sv_hadamard_i8(const void* x, int m, int K, const int8_t* signs,
                                     int block, int8_t* xq, float* xscale, hipStream_t stream) {
   if (!x || !signs || !xq || !xscale) return SV_ERR_NULL;
-  if (m < 1 || m > SV_MAX_ROWS || K < 64 || K % 64 != 0 || K > kMaxK) return SV_ERR_INVALID_ARG;
+  // one workgroup per row: any number of token rows (up to 2^20) in one call
+  if (m < 1 || m > (1 << 20) || K < 64 || K % 64 != 0 || K > kMaxK) return SV_ERR_INVALID_ARG;
   if (block < 2 || block > 4096 || (block & (block - 1)) != 0 || K % block != 0)
     return SV_ERR_INVALID_ARG;
   if (!sv_aligned16(x) || !sv_aligned16(signs) || !sv_aligned16(xq) || !sv_aligned16(xscale))
