@@ -16,7 +16,9 @@ per-GEMM-launch variant, the int8 path, accept statistics over 4096 trials
 per noise level, the measured HBM read peak, and the CPU oracle baseline.
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 200] [--quick]
-       python bench.py --profile-pass   (short run for rocprofv3 counters)
+       python bench.py --profile-pass [--format w4|w8|w4_i8] [--k K]
+                        (copy kernel, read probe and two executor passes, for
+                         rocprofv3 counters)
 """
 import argparse
 import json
@@ -163,6 +165,8 @@ def main():
     ap.add_argument("--k", type=int, default=16)
     ap.add_argument("--quick", action="store_true", help="skip sweeps, stats and cpu baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--format", default="w4", choices=("w4", "w8", "w4_i8"),
+                    help="weight path of --profile-pass")
     ap.add_argument("--profile-pass", action="store_true",
                     help="copy kernel + read probe + 2 eager W4 passes, then exit")
     args = ap.parse_args()
@@ -220,7 +224,22 @@ def main():
         dst.copy_(src)  # plain copy kernel of 256 MiB (counter scale reference)
         sink = torch.empty(sv.sv_read_probe_sink_words(), dtype=torch.int32, device=dev)
         sv.sv_read_bandwidth_probe(src, sink)
-        p = w4_pass(k)
+        if args.format == "w4":
+            p = w4_pass(k)
+        elif args.format == "w4_i8":
+            xi = {K: synth.int8_activations(k, K, seed=13 + K, device=dev) for K in (HIDDEN, FFN)}
+            p = sv.sv_pass_plan("w4_i8", [(xi[K][0], xi[K][1], pc, ps, N, y_own[li][gi][:k])
+                                          for li, layer in enumerate(w4)
+                                          for gi, (nm, N, K, c, s_, z, pc, ps) in enumerate(layer)])
+        else:
+            xh, xf = x_h[:k].contiguous(), x_f[:k].contiguous()
+            g8 = []
+            for li, layer in enumerate(make_w8_stack(torch, synth, dev)):
+                for gi, (nm, N, K, c, s_) in enumerate(layer):
+                    g8.append((xh if K == HIDDEN else xf, sv.sv_w8_pack(c), s_, N,
+                               y_own[li][gi][:k]))
+                    del c
+            p = sv.sv_pass_plan("w8", g8)
         for _ in range(2):
             sv.sv_pass_run(p)
         torch.cuda.synchronize()
