@@ -140,7 +140,7 @@ struct Geo {
 
 template <int F, int MT, int P>
 constexpr int pass_lds_bytes() {
-  return P * Geo<F, MT>::SLOT + kWaves * 1024;   // + per-wave output transpose
+  return P * Geo<F, MT>::SLOT + kWaves * 4096;   // + per-wave output transpose
 }
 
 // 4 int8 codes (one dword) -> 2 dwords of bf16 pairs holding 128 + c.
@@ -160,13 +160,14 @@ template <int F, int MT, int P>
 __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restrict__ plan, int m) {
   using G = Geo<F, MT>;
   constexpr int L = kTW * kNB + Fmt<F>::SZD + Fmt<F>::AUXD + G::XD;   // loads per wave per step
-  constexpr int NS = kTW * MT;                  // 16-byte stores per wave per step
+  constexpr int NS = 4 * MT;                    // 16-byte stores per wave per step
   // At the wait before computing chunk c, the operations issued after chunk
   // c's loads are the stores of that same step and the loads and stores of
   // the P - 2 steps after it.
   constexpr int WAITN = NS + (P - 2) * (L + NS);
   static_assert(WAITN < 64, "too many memory operations in flight for vmcnt");
   static_assert(kTW * kNB * 128 == 1024, "one 1 KiB scale/zero load per wave per step");
+  static_assert(kTW == 4, "the output transpose covers a wave's 4 tiles = 64 channels");
   extern __shared__ __align__(16) uint8_t lds[];
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(plan);
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
   const sv_u32x4 ones8 = {0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
   const sv_f32x4 fz = {0.f, 0.f, 0.f, 0.f};
   const sv_i32x4 iz = {0, 0, 0, 0};
-  float* const tpose = reinterpret_cast<float*>(lds + P * G::SLOT) + wave * 256;
+  float* const tpose = reinterpret_cast<float*>(lds + P * G::SLOT) + wave * 1024;
 
   // ---- issue cursor: the item and chunk whose loads go out next ----
   int i_item = ib, i_c = 0;
@@ -432,25 +433,27 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
   };
 
   // NS stores every step.  On an item's last chunk: the epilogue of the
-  // format, then each 16x16 output tile goes through the wave's LDS
-  // transpose area (lane (col, q) of an MFMA output holds rows 4q .. 4q+3 of
-  // channel col) so that lane l stores channels 4 (l % 4) .. +3 of row l / 4
-  // as one 16-byte write.  Otherwise the same number of stores with
-  // out-of-range offsets.
+  // format, then the wave's 16 rows x 64 channels (its 4 tiles; lane (col, q)
+  // of an MFMA output holds rows 4q .. 4q+3 of channel col) go through the
+  // wave's LDS transpose area so that each store writes 4 whole rows of 256
+  // contiguous bytes (lane l: row l / 16, channels 4 (l % 16) .. +3), i.e.
+  // full cache lines.  Otherwise the same number of stores with out-of-range
+  // offsets.
   auto store = [&](const int slot, const bool at_end) {
     if (at_end) {
       const uint8_t* aux = lds + slot * G::SLOT + G::XBUF + G::SZBUF + wave * 1024;
+      const int ch = 4 * (lane & 15);           // this lane's 4 channels in the wave's 64
+      const bool ch_ok = c_t0 + wave * kTW + (ch >> 4) < (c_N >> 4);
 #pragma unroll
-      for (int tw = 0; tw < kTW; ++tw) {
-        const int tile = c_t0 + wave * kTW + tw;
+      for (int a = 0; a < MT; ++a) {
 #pragma unroll
-        for (int a = 0; a < MT; ++a) {
+        for (int tw = 0; tw < kTW; ++tw) {
           sv_f32x4 v = yacc[tw][a];
           if constexpr (F == SV_PASS_W8) {
-            const float s = __half2float(
+            const float sc = __half2float(
                 *reinterpret_cast<const __half*>(aux + (tw * 16 + col) * 2));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = s * fmaf(-128.0f, xacc[a][i], v[i]);
+            for (int i = 0; i < 4; ++i) v[i] = sc * fmaf(-128.0f, xacc[a][i], v[i]);
           }
           if constexpr (F == SV_PASS_W4_I8) {
 #pragma unroll
@@ -458,15 +461,22 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
               v[i] *= *reinterpret_cast<const float*>(aux + (16 * a + 4 * q + i) * 4);
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) tpose[(4 * q + i) * 16 + col] = v[i];
-          const sv_u32x4 o =
-              *reinterpret_cast<const sv_u32x4*>(tpose + (lane >> 2) * 16 + 4 * (lane & 3));
-          const int r = 16 * a + (lane >> 2);
-          const bool ok = tile < (c_N >> 4) && r < m;
+          for (int i = 0; i < 4; ++i) tpose[(4 * q + i) * 64 + tw * 16 + col] = v[i];
+        }
+        // Lanes read what other lanes wrote: LDS operations of a wave execute
+        // in order, so it is enough that the compiler keeps program order
+        // (it may not move these accesses across the fence).
+        sv_compiler_fence();
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int row = 4 * rr + (lane >> 4);
+          const sv_u32x4 o = *reinterpret_cast<const sv_u32x4*>(tpose + row * 64 + ch);
+          const int r = 16 * a + row;
           const unsigned int off =
-              ok ? (r * c_N + 16 * tile + 4 * (lane & 3)) * 4 : kSvOutOfRange;
+              ch_ok && r < m ? (r * c_N + 16 * (c_t0 + wave * kTW) + ch) * 4 : kSvOutOfRange;
           __builtin_amdgcn_raw_buffer_store_b128(o, yrs, off, 0, 0);
         }
+        sv_compiler_fence();                    // before the next 16 rows overwrite the area
       }
 #pragma unroll
       for (int a = 0; a < MT; ++a) {
