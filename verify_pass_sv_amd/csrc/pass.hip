@@ -321,6 +321,11 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
     const int KB = c_K / Fmt<F>::KPB;
     const int jb = c_c * kNB;
     const uint8_t* const sl = lds + slot * G::SLOT;
+    // W4: row sums of the step's 4 groups, lane (col, q) holding row col of
+    // group q (the A operand layout of v_mfma_f32_16x16x4_f32)
+    float xsum[MT];
+#pragma unroll
+    for (int a = 0; a < MT; ++a) xsum[a] = 0.f;
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
       if (jb + b >= KB) break;
@@ -329,16 +334,19 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
 #pragma unroll
         for (int h = 0; h < 2; ++h) {           // the two groups of the block
           sv_u32x4 a0[MT], a1[MT];
-          sv_f32x4 xs[MT];
 #pragma unroll
           for (int a = 0; a < MT; ++a) {
             const uint8_t* ap = sl + a * 16 * G::XROW;
             a0[a] = *reinterpret_cast<const sv_u32x4*>(ap + aaddr(16 * b + 8 * h + 2 * q));
             a1[a] = *reinterpret_cast<const sv_u32x4*>(ap + aaddr(16 * b + 8 * h + 2 * q + 1));
-            xs[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a0[a]),
-                                                            sv_as_bf16x8(ones), fz, 0, 0, 0);
-            xs[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a1[a]),
-                                                            sv_as_bf16x8(ones), xs[a], 0, 0, 0);
+            // group row sums with the rows along N (all-ones A operand): lane
+            // (col, q) receives the sum of row col; the lanes with q = group
+            // index of the step keep it as their A operand of the correction
+            sv_f32x4 xt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                sv_as_bf16x8(ones), sv_as_bf16x8(a0[a]), fz, 0, 0, 0);
+            xt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(ones),
+                                                         sv_as_bf16x8(a1[a]), xt, 0, 0, 0);
+            if (q == 2 * b + h) xsum[a] = xt[0];
           }
 #pragma unroll
           for (int tw = 0; tw < kTW; ++tw) {
@@ -347,18 +355,17 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
             const sv_u32x4 b1 = sv_w4_dequant8(h ? w.w : w.y, magic);
             const sv_u32x2 sbt =
                 *reinterpret_cast<const sv_u32x2*>(sp + (tw * kNB + b) * 128);
-            const unsigned int sz = h ? sbt.y : sbt.x;
-            const float s = sv_half_lo(sz);
-            const float zb = 128.0f + sv_half_hi(sz);
+            const float sc = sv_half_lo(h ? sbt.y : sbt.x);
 #pragma unroll
             for (int a = 0; a < MT; ++a) {
               sv_f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                   sv_as_bf16x8(a0[a]), sv_as_bf16x8(b0), fz, 0, 0, 0);
               acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a1[a]),
                                                             sv_as_bf16x8(b1), acc, 0, 0, 0);
+              // acc = sum x (128 + c): the bias and zero point leave through
+              // the correction below
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                yacc[tw][a][i] = fmaf(s, fmaf(-zb, xs[a][i], acc[i]), yacc[tw][a][i]);
+              for (int i = 0; i < 4; ++i) yacc[tw][a][i] = fmaf(sc, acc[i], yacc[tw][a][i]);
             }
           }
         }
@@ -428,6 +435,23 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
             }
           }
         }
+      }
+    }
+    if constexpr (F == SV_PASS_W4) {
+      // Zero point and bias of the step's 4 groups in one rank-4 update:
+      // yacc -= sum_g xsum[row, g] * s[n, g] (128 + z[n, g]), with lane
+      // (col, q) supplying channel col of group q as the B operand.  Products
+      // and sums are binary32; for a one-hot row the result is exactly
+      // (c - z) s (both terms are exact and within a factor two).
+      const int bq = q >> 1;
+      const uint8_t* sp = sl + G::XBUF + wave * 1024 + col * 8 + (q & 1) * 4;
+#pragma unroll
+      for (int tw = 0; tw < kTW; ++tw) {
+        const unsigned int szq = *reinterpret_cast<const unsigned int*>(sp + (tw * kNB + bq) * 128);
+        const float nsz = jb + bq < KB ? -(sv_half_lo(szq) * (128.0f + sv_half_hi(szq))) : 0.f;
+#pragma unroll
+        for (int a = 0; a < MT; ++a)
+          yacc[tw][a] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum[a], nsz, yacc[tw][a], 0, 0, 0);
       }
     }
   };
