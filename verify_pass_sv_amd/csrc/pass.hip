@@ -43,15 +43,21 @@
 //
 // Arithmetic:
 //   W4:    bf16 128 + c from a mask and a byte permute against 0x43;
-//          v_mfma_f32_16x16x32_bf16 per group, an all-ones MFMA for the group
-//          row sums, fold y += s (acc - (128 + z) xsum) in binary32 (exact
-//          (c - z) s for a one-hot row and integer z).
+//          v_mfma_f32_16x16x32_bf16 gives acc = sum x (128 + c) per group and
+//          tile, folded as y += s acc (one VALU per output).  The bias and the
+//          zero point leave once per 4 groups through one rank-4 binary32
+//          update y -= sum_g xsum[r, g] s[n, g] (128 + z[n, g])
+//          (v_mfma_f32_16x16x4_f32), whose row-sum operand comes straight
+//          out of an all-ones-A MFMA in the required lane layout.  For a
+//          one-hot row and integer z both terms are exact, so is
+//          (c - z) s.
 //   W8:    bf16 128 + c from the biased byte (v_cvt_f32_ubyte, upper half);
 //          the MFMA accumulates over all of K; at the item end
 //          y = s (acc - 128 xsum).
 //   W4_I8: v_mfma_i32_16x16x64_i8 (K depth = one group) gives the exact int32
-//          partial I = sum c xq and, against all-ones bytes, Xg = sum xq;
-//          y += s (I - z Xg) in binary32; at the item end y *= xscale[row].
+//          partial I = sum c xq, folded as y += s I; the zero point leaves
+//          through the same rank-4 update with the exact int32 group sums
+//          Xg = sum xq; at the item end y *= xscale[row].
 #include <algorithm>
 #include <functional>
 #include <queue>
@@ -401,15 +407,16 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           sv_u32x4 a8[MT];
-          sv_f32x4 xg[MT];
 #pragma unroll
           for (int a = 0; a < MT; ++a) {
             a8[a] = *reinterpret_cast<const sv_u32x4*>(sl + a * 16 * G::XROW +
                                                        aaddr(8 * b + 4 * h + q));
+            // exact group sums Xg with the rows along N (all-ones A operand):
+            // lane (col, q) receives row col; the lanes with q = group index
+            // of the step keep it for the correction below
             const sv_i32x4 g = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                sv_as_i32x4(a8[a]), sv_as_i32x4(ones8), iz, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) xg[a][i] = static_cast<float>(g[i]);
+                sv_as_i32x4(ones8), sv_as_i32x4(a8[a]), iz, 0, 0, 0);
+            if (q == 2 * b + h) xsum[a] = static_cast<float>(g[0]);
           }
 #pragma unroll
           for (int tw = 0; tw < kTW; ++tw) {
@@ -421,34 +428,34 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
                                  (wy >> 4) & 0x0F0F0F0Fu};
             const sv_u32x2 sbt =
                 *reinterpret_cast<const sv_u32x2*>(sp + (tw * kNB + b) * 128);
-            const unsigned int sz = h ? sbt.y : sbt.x;
-            const float s = sv_half_lo(sz);
-            const float z = sv_half_hi(sz);
+            const float sc = sv_half_lo(h ? sbt.y : sbt.x);
 #pragma unroll
             for (int a = 0; a < MT; ++a) {
               const sv_i32x4 I = __builtin_amdgcn_mfma_i32_16x16x64_i8(
                   sv_as_i32x4(a8[a]), sv_as_i32x4(bw), iz, 0, 0, 0);
+              // I = sum c xq exactly; the zero point leaves through the
+              // correction below
 #pragma unroll
               for (int i = 0; i < 4; ++i)
-                yacc[tw][a][i] =
-                    fmaf(s, fmaf(-z, xg[a][i], static_cast<float>(I[i])), yacc[tw][a][i]);
+                yacc[tw][a][i] = fmaf(sc, static_cast<float>(I[i]), yacc[tw][a][i]);
             }
           }
         }
       }
     }
-    if constexpr (F == SV_PASS_W4) {
-      // Zero point and bias of the step's 4 groups in one rank-4 update:
-      // yacc -= sum_g xsum[row, g] * s[n, g] (128 + z[n, g]), with lane
-      // (col, q) supplying channel col of group q as the B operand.  Products
-      // and sums are binary32; for a one-hot row the result is exactly
-      // (c - z) s (both terms are exact and within a factor two).
+    if constexpr (F != SV_PASS_W8) {
+      // Zero point (and, for bf16 codes, the 128 bias) of the step's 4
+      // groups in one rank-4 update: yacc -= sum_g xsum[row, g] * s[n, g]
+      // (bias + z[n, g]), with lane (col, q) supplying channel col of group q
+      // as the B operand.  Binary32 products and sums; for a one-hot row
+      // both terms are exact and so is their difference (c - z) s.
+      constexpr float kBias = F == SV_PASS_W4 ? 128.0f : 0.0f;
       const int bq = q >> 1;
       const uint8_t* sp = sl + G::XBUF + wave * 1024 + col * 8 + (q & 1) * 4;
 #pragma unroll
       for (int tw = 0; tw < kTW; ++tw) {
         const unsigned int szq = *reinterpret_cast<const unsigned int*>(sp + (tw * kNB + bq) * 128);
-        const float nsz = jb + bq < KB ? -(sv_half_lo(szq) * (128.0f + sv_half_hi(szq))) : 0.f;
+        const float nsz = jb + bq < KB ? -(sv_half_lo(szq) * (kBias + sv_half_hi(szq))) : 0.f;
 #pragma unroll
         for (int a = 0; a < MT; ++a)
           yacc[tw][a] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum[a], nsz, yacc[tw][a], 0, 0, 0);
