@@ -7,20 +7,24 @@
 // draft is accepted the target supplies one more token); Karpathy's Trick for
 // Faster Local LLMs, "Producing several tokens from one model pass".
 //
-// Three launches on the caller's stream:
-//  1. stats   one wave per (trial, row, vocab chunk): online max / sum of
-//             exp over 128-bit loads -> partial (max, sum, invalid flag).
-//  2. decide  one workgroup per (trial, residual chunk): combines the
-//             partials into log-sum-exp values, evaluates p_i(d_i), q_i(d_i),
-//             draws Philox uniforms, takes the accept decisions with one
-//             wave ballot (first rejection = first zero bit), then sums the
-//             residual weights max(0, p_r - q_r) (or p_k for the bonus) of
-//             its chunk in binary64.  Every workgroup of a trial reaches the
-//             same decision; workgroup 0 writes the per-trial outputs.
-//  3. select  one workgroup per trial: prefix over chunk totals, then inside
-//             the chosen chunk over per-thread sums, then a walk inside one
-//             thread's range.  Totals, prefixes and the walk use the same
-//             binary64 addition order, so the chosen bin always exists.
+// Two launches on the caller's stream:
+//  1. stats   one wave per (trial, row, vocabulary span): max and sum of exp
+//             over a span, with all loads of a 2048-float batch in flight
+//             before any is used -> partial (max, sum, invalid flag).  It also
+//             zeroes the per-trial completion counters of launch 2.
+//  2. decide  one workgroup per (trial, residual share): merges the trial's
+//             partials into log-sum-exp values (staged in LDS, several threads
+//             per row, fixed order), evaluates p_i(d_i), q_i(d_i), draws the
+//             Philox uniforms and takes the accept decisions with one wave
+//             ballot (first rejection = first zero bit), then sums the
+//             residual weights max(0, p_r - q_r) (or p_k for the bonus) of its
+//             2048-float blocks in binary64: blocks staged in LDS, 16 groups of
+//             16 threads of 8 entries each, always in the same order.  Every
+//             workgroup of a trial reaches the same decision; workgroup 0
+//             writes the per-trial outputs.  The last workgroup of the trial
+//             to finish (a device-scope counter) runs the inverse-CDF
+//             selection over the block totals and replays the same sums inside
+//             the chosen block, so the chosen bin always exists.
 #include "sv_common.h"
 
 #include <math.h>
@@ -142,7 +146,7 @@ __host__ __device__ inline int resid_wgs(int B, int V) {
 }
 
 struct WsLayout {
-  size_t partial_off, decision_off, total_off, bytes;
+  size_t partial_off, decision_off, total_off, done_off, bytes;
 };
 
 __host__ inline WsLayout ws_layout(int B, int k, int V) {
@@ -152,7 +156,8 @@ __host__ inline WsLayout ws_layout(int B, int k, int V) {
   L.partial_off = 0;
   L.decision_off = up(static_cast<size_t>(B) * R * stat_spans(V) * sizeof(StatPartial));
   L.total_off = L.decision_off + up(static_cast<size_t>(B) * sizeof(Decision));
-  L.bytes = L.total_off + up(static_cast<size_t>(B) * resid_blocks(V) * sizeof(double));
+  L.done_off = L.total_off + up(static_cast<size_t>(B) * resid_blocks(V) * sizeof(double));
+  L.bytes = L.done_off + up(static_cast<size_t>(B) * sizeof(int));
   return L;
 }
 
@@ -168,7 +173,10 @@ __device__ __forceinline__ const float* row_ptr(const float* tgt, const float* d
 template <bool VEC>
 __global__ __launch_bounds__(64 * kStatsWaves) void stats_kernel(
     const float* __restrict__ tgt, const float* __restrict__ dft, int B, int k, int V, int C1,
-    int span, StatPartial* __restrict__ part) {
+    int span, StatPartial* __restrict__ part, int* __restrict__ done) {
+  // the per-trial completion counters of kernel 2 start at zero every call
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < B; i += blockDim.x) done[i] = 0;
   const int lane = threadIdx.x & 63;
   const long long item = static_cast<long long>(blockIdx.x) * kStatsWaves + (threadIdx.x >> 6);
   const int R = 2 * k + 1;
@@ -285,7 +293,13 @@ __device__ __forceinline__ void block_sums(const double* tsum, double* gsum, dou
   __syncthreads();
 }
 
-// ---- kernel 2: decide + residual block totals ------------------------------
+__device__ void select_trial(const float* __restrict__ tgt, const float* __restrict__ dft, int k,
+                             int V, int b, const Decision dec,
+                             const double* __restrict__ totals,
+                             int32_t* __restrict__ out_tokens, float* st, float* sd,
+                             double* tsum, double* gsum, double* btot_p, double* dyn_tot);
+
+// ---- kernel 2: decide + residual block totals + select-----------------------------
 // Every workgroup of a trial merges the trial's statistics and takes the same
 // decisions (identical inputs and order); workgroup 0 writes the per-trial
 // outputs.  Then each workgroup sums its share of the residual blocks.
@@ -295,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
     const StatPartial* __restrict__ part, Decision* __restrict__ decs, double* __restrict__ totals,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_n_acc,
     int32_t* __restrict__ out_status, float* __restrict__ p_at, float* __restrict__ q_at,
-    float* __restrict__ lse_out) {
+    float* __restrict__ lse_out, int* __restrict__ done) {
   __shared__ float pm[(2 * SV_MAX_ROWS + 1) * kMaxC1];
   __shared__ float ps[(2 * SV_MAX_ROWS + 1) * kMaxC1];
   __shared__ int pb[(2 * SV_MAX_ROWS + 1) * kMaxC1];
@@ -458,23 +472,37 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
     block_sums(tsum, gsum, &btot);
     if (tid == 0) tot[blk] = btot;
   }
+
+  // The last workgroup of the trial to finish (device-scope counter, zeroed
+  // by kernel 1 of this call) selects the token: release the block totals
+  // before counting, acquire them after seeing the final count.
+  __shared__ int is_last;
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    is_last = atomicAdd(&done[b], 1) == C2 - 1;
+    if (is_last) __threadfence();
+  }
+  __syncthreads();
+  if (!is_last) return;
+  extern __shared__ double dyn_tot[];   // resid_blocks(V) doubles
+  select_trial(tgt, dft, k, V, b, dec, totals, out_tokens, st, sd, tsum, gsum, &btot, dyn_tot);
 }
 
-// ---- kernel 3: select the replacement / bonus token ------------------------
-__global__ __launch_bounds__(kThreads) void select_kernel(
-    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V,
-    const Decision* __restrict__ decs, const double* __restrict__ totals,
-    int32_t* __restrict__ out_tokens) {
-  __shared__ float st[kBlk], sd[kBlk];
-  __shared__ double tsum[kThreads];
-  __shared__ double gsum[kGroups];
-  __shared__ double btot;
+// ---- select the replacement / bonus token ------------------------------------
+// Run by the last workgroup of kernel 2 to finish a trial, on the LDS arrays
+// of that workgroup: inverse CDF over the block totals, then inside the
+// chosen block over groups, threads and a thread's 8 entries, replaying the
+// exact sums kernel 2 formed.
+__device__ void select_trial(const float* __restrict__ tgt, const float* __restrict__ dft, int k,
+                             int V, int b, const Decision dec,
+                             const double* __restrict__ totals,
+                             int32_t* __restrict__ out_tokens, float* st, float* sd,
+                             double* tsum, double* gsum, double* btot_p, double* dyn_tot) {
   __shared__ double sh_S, sh_pc;
   __shared__ int sh_blk, sh_usep;
-  const int b = blockIdx.x;
+  double& btot = *btot_p;
   const int tid = threadIdx.x;
-  const Decision dec = decs[b];
-  if (dec.status != 0) return;
   const int r = dec.n_acc;
   const float* pt = tgt + (static_cast<size_t>(b) * (k + 1) + r) * V;
   const float* pd = r < k ? dft + (static_cast<size_t>(b) * k + r) * V : nullptr;
@@ -483,7 +511,6 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   const double* T = totals + static_cast<size_t>(b) * nb;
 
   // block totals -> LDS in one parallel pass (dyn_tot), then summed in order
-  extern __shared__ double dyn_tot[];   // nb doubles
   for (int i = tid; i < nb; i += kThreads) dyn_tot[i] = T[i];
   __syncthreads();
   if (tid == 0) {
@@ -632,6 +659,7 @@ extern "C" sv_status sv_verify_accept(const float* target_logits, const float* d
   StatPartial* part = reinterpret_cast<StatPartial*>(ws + L.partial_off);
   Decision* decs = reinterpret_cast<Decision*>(ws + L.decision_off);
   double* totals = reinterpret_cast<double*>(ws + L.total_off);
+  int* done = reinterpret_cast<int*>(ws + L.done_off);
   const int C1 = stat_spans(V);
   const int span = stat_span_len(V, C1);
   const int C2 = resid_wgs(B, V);
@@ -639,27 +667,24 @@ extern "C" sv_status sv_verify_accept(const float* target_logits, const float* d
   const long long blocks1 = (items + kStatsWaves - 1) / kStatsWaves;
   if (blocks1 >= (1LL << 31) || static_cast<long long>(B) * C2 >= (1LL << 31))
     return SV_ERR_INVALID_ARG;
-  // dynamic LDS of kernel 3: block totals for its rare p_r fallback
+  // dynamic LDS of kernel 2: block totals of the selecting workgroup
   const size_t dyn = static_cast<size_t>(resid_blocks(V)) * sizeof(double);
   if (dyn > 32 * 1024) return SV_ERR_UNSUPPORTED;
 
   if (V % 4 == 0)
     hipLaunchKernelGGL((stats_kernel<true>), dim3(static_cast<unsigned>(blocks1)),
                        dim3(64 * kStatsWaves), 0, stream, target_logits, draft_logits, B, k, V,
-                       C1, span, part);
+                       C1, span, part, done);
   else
     hipLaunchKernelGGL((stats_kernel<false>), dim3(static_cast<unsigned>(blocks1)),
                        dim3(64 * kStatsWaves), 0, stream, target_logits, draft_logits, B, k, V,
-                       C1, span, part);
+                       C1, span, part, done);
   SV_LAUNCH_CHECK();
-  hipLaunchKernelGGL(decide_kernel, dim3(static_cast<unsigned>(B) * C2), dim3(kThreads), 0,
+  hipLaunchKernelGGL(decide_kernel, dim3(static_cast<unsigned>(B) * C2), dim3(kThreads), dyn,
                      stream, target_logits, draft_logits, draft_tokens, B, k, V, C1, C2,
                      static_cast<unsigned int>(seed & 0xFFFFFFFFu),
                      static_cast<unsigned int>(seed >> 32), offset, part, decs, totals,
-                     out_tokens, out_n_acc, out_status, p_at, q_at, lse);
-  SV_LAUNCH_CHECK();
-  hipLaunchKernelGGL(select_kernel, dim3(static_cast<unsigned>(B)), dim3(kThreads), dyn, stream,
-                     target_logits, draft_logits, k, V, decs, totals, out_tokens);
+                     out_tokens, out_n_acc, out_status, p_at, q_at, lse, done);
   SV_LAUNCH_CHECK();
   return SV_OK;
 }
