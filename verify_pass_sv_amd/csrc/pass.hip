@@ -452,10 +452,17 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
       constexpr float kBias = F == SV_PASS_W4 ? 128.0f : 0.0f;
       const int bq = q >> 1;
       const uint8_t* sp = sl + G::XBUF + wave * 1024 + col * 8 + (q & 1) * 4;
+      // all records are read (the slot always holds them, stale past K) and
+      // groups past K select 0, so no lane-dependent branch splits the reads
+      const float gmask = jb + bq < KB ? 1.0f : 0.0f;
+      unsigned int szq[kTW];
+#pragma unroll
+      for (int tw = 0; tw < kTW; ++tw)
+        szq[tw] = *reinterpret_cast<const unsigned int*>(sp + (tw * kNB + bq) * 128);
 #pragma unroll
       for (int tw = 0; tw < kTW; ++tw) {
-        const unsigned int szq = *reinterpret_cast<const unsigned int*>(sp + (tw * kNB + bq) * 128);
-        const float nsz = jb + bq < KB ? -(sv_half_lo(szq) * (kBias + sv_half_hi(szq))) : 0.f;
+        const float v = -(sv_half_lo(szq[tw]) * (kBias + sv_half_hi(szq[tw])));
+        const float nsz = gmask != 0.0f ? v : 0.0f;   // not v * 0: stale bits may be inf/NaN
 #pragma unroll
         for (int a = 0; a < MT; ++a)
           yacc[tw][a] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum[a], nsz, yacc[tw][a], 0, 0, 0);
