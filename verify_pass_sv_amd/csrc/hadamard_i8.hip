@@ -8,12 +8,20 @@
 // kernel mixes 32-value blocks to match a 32-thread SIMD group; here the
 // block is a parameter (up to 4096) and one workgroup owns one token row.
 //
-// Design: the row is staged in LDS as binary64 after the sign flip, an
-// in-place fast Walsh-Hadamard transform (log2(block) butterfly stages, all
-// blocks of the row at once) runs in binary64, and each value is rounded once
-// to binary32 after the b^-1/2 scale.  The row maximum, the scale amax/127
-// and the round-half-to-even decision are binary32.  Negligible bytes:
-// latency-bound.
+// Design: one workgroup per token row.  The rotation is a fast
+// Walsh-Hadamard transform (log2(block) butterfly stages) in binary64 after
+// the sign flip; each value is rounded once to binary32 after the b^-1/2
+// scale.  The row maximum, the scale amax/127 and the round-half-to-even
+// decision are binary32.  Negligible bytes: latency-bound.
+//   * block 4096 (the verify pass's block): one wave per 4096-wide block.
+//     Each lane holds 64 contiguous values in registers; the six stages with
+//     partners inside a lane run in registers, a padded LDS transpose then
+//     gives each lane the values 64 apart, and the last six stages run in
+//     registers again.  No workgroup barrier until the row maximum.
+//   * other blocks: the row is staged in LDS and all blocks of the row are
+//     transformed in place, stage by stage.
+// Both orders of butterflies are the same, so both give identical binary64
+// values.
 #include "sv_common.h"
 
 namespace {
@@ -81,6 +89,97 @@ __global__ __launch_bounds__(kThreads) void hadamard_i8_kernel(
   }
 }
 
+
+// ---- block 4096: registers + one LDS transpose ---------------------------------
+constexpr int kB4 = 4096;
+constexpr int kPadRow = kB4 + 64;               // doubles per wave of transpose area
+
+__device__ __forceinline__ void bfly(double& a, double& b) {
+  const double s = a + b, d = a - b;
+  a = s;
+  b = d;
+}
+
+__global__ __launch_bounds__(256) void hadamard4096_i8_kernel(
+    const uint16_t* __restrict__ x, int K, const int8_t* __restrict__ signs,
+    int8_t* __restrict__ xq, float* __restrict__ xscale) {
+  extern __shared__ double tbuf[];               // kPadRow doubles per wave
+  __shared__ float wmax[4];
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;                // K / 4096 blocks in the row
+  const int base = wv * kB4;
+
+  // 64 contiguous values per lane (element 64 lane + i of the block)
+  double v[64];
+  {
+    const uint16_t* xr = x + static_cast<size_t>(r) * K + base + lane * 64;
+    const int8_t* sg = signs + base + lane * 64;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const sv_u32x4 w = sv_ld16(xr + 8 * t);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * t + 2 * e] = static_cast<double>(__uint_as_float(w[e] << 16));
+        v[8 * t + 2 * e + 1] = static_cast<double>(__uint_as_float(w[e] & 0xFFFF0000u));
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const sv_u32x4 sw = sv_ld16(sg + 16 * t);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int sgn = static_cast<int8_t>((sw[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+        v[16 * t + e] *= static_cast<double>(sgn);
+      }
+    }
+  }
+  // stages h = 1 .. 32: partners inside the lane
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+      if ((i & h) == 0) bfly(v[i], v[i + h]);
+  // transpose: element e = 64 lane + i -> padded slot e + e / 64; read back
+  // elements lane + 64 j (slot lane + 65 j)
+  double* tb = tbuf + wv * kPadRow;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) tb[65 * lane + i] = v[i];
+  // lanes read what other lanes wrote: LDS operations of a wave execute in
+  // order, the compiler must only keep program order
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < 64; ++j) v[j] = tb[lane + 65 * j];
+  // stages h = 64 .. 2048: element lane + 64 j pairs with j ^ (h / 64)
+#pragma unroll
+  for (int hj = 1; hj < 64; hj <<= 1)
+#pragma unroll
+    for (int j = 0; j < 64; ++j)
+      if ((j & hj) == 0) bfly(v[j], v[j + hj]);
+
+  float f[64];
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 64; ++j) {
+    f[j] = static_cast<float>(v[j] / 64.0);      // 4096^-1/2, exact
+    amax = fmaxf(amax, fabsf(f[j]));
+  }
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if (lane == 0) wmax[wv] = amax;
+  __syncthreads();
+  float rmax = 0.f;
+  for (int w = 0; w < nw; ++w) rmax = fmaxf(rmax, wmax[w]);
+  const float scale = rmax > 0.f ? rmax / 127.0f : 1.0f;
+  if (threadIdx.x == 0) xscale[r] = scale;
+  int8_t* out = xq + static_cast<size_t>(r) * K + base + lane;
+#pragma unroll
+  for (int j = 0; j < 64; ++j) {
+    const float q = rintf(f[j] / scale);
+    out[64 * j] = static_cast<int8_t>(fminf(127.f, fmaxf(-127.f, q)));
+  }
+}
+
 }  // namespace
 
 extern "C" sv_status sv_hadamard_i8(const void* x, int m, int K, const int8_t* signs,
@@ -92,6 +191,19 @@ extern "C" sv_status sv_hadamard_i8(const void* x, int m, int K, const int8_t* s
     return SV_ERR_INVALID_ARG;
   if (!sv_aligned16(x) || !sv_aligned16(signs) || !sv_aligned16(xq) || !sv_aligned16(xscale))
     return SV_ERR_ALIGN;
+  if (block == kB4 && K % kB4 == 0) {
+    const int nw = K / kB4;
+    const size_t lds4 = static_cast<size_t>(nw) * kPadRow * sizeof(double);
+    if (lds4 > 65536 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(hadamard4096_i8_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(4 * kPadRow * sizeof(double))) != hipSuccess)
+      return SV_ERR_HIP;
+    hipLaunchKernelGGL(hadamard4096_i8_kernel, dim3(m), dim3(64 * nw), lds4, stream,
+                       static_cast<const uint16_t*>(x), K, signs, xq, xscale);
+    SV_LAUNCH_CHECK();
+    return SV_OK;
+  }
   int log2b = 0;
   while ((1 << log2b) < block) ++log2b;
   const size_t lds = static_cast<size_t>(K) * sizeof(double);
