@@ -98,15 +98,18 @@ sv_status sv_qgemm_w4(const void* x, int m, int K,
  * (Karpathy's Trick ..., "How Uzu optimizes bytes and tokens per pass";
  * @trymirai timeline).  sv_w4_pack rewrites row-major W4 weights (the
  * sv_qgemm_w4 format) once into a tile-major layout whose every 1 KiB block
- * is one wave load in MFMA operand order:
+ * is one wave load in MFMA operand order.  With ntile = N/16, KB = K/128 and
+ * block(t, j) = 32*g*KB + j*gt + (t % 32), where g = t / 32 and
+ * gt = min(32, ntile - 32*g) (tiles grouped by 32; inside a group the blocks
+ * of one k block are consecutive):
  *   packed_codes uint8, N*K/2 bytes: for 16-row tile t and 128-wide k block j,
- *     the block at byte (t*K/128 + j)*1024 holds, at bytes [16l, 16l+16),
+ *     the block at byte block(t, j)*1024 holds, at bytes [16l, 16l+16),
  *     row 16t + (l & 15) with q = l >> 4: its codes for k = 128j + 16q + [0,16)
  *     (bytes 0-7) and k = 128j + 64 + 16q + [0,16) (bytes 8-15); inside each
  *     4-byte word covering k0..k0+7, byte b holds code k0+b in its low nibble
  *     and code k0+b+4 in its high nibble.
- *   packed_sz f16, N*(K/group)*4 bytes: for (t, j) a 128-byte block at
- *     (t*K/128 + j)*128; row n of the tile owns 8 bytes
+ *   packed_sz f16, N*(K/group)*4 bytes: for (t, j) a 128-byte record at
+ *     block(t, j)*128; row n of the tile owns 8 bytes
  *     [S(2j), Z(2j), S(2j+1), Z(2j+1)].
  * Requirements: group == 64, N % 16 == 0, K % 128 == 0, N*K/2 < 2^31.  The
  * pack enqueues
@@ -135,8 +138,9 @@ sv_status sv_qgemm_w4_packed(const void* x, int m, int K, const uint8_t* packed_
 /*
  * sv_w8_pack -- rewrites row-major W8 codes (int8 [N, K]) into the streaming
  * layout of the pass executor: for 16-row tile t and 64-wide k block j, one
- * 1 KiB block at byte (t * K/64 + j) * 1024 whose bytes [16l, 16l+16) hold
- * row 16t + (l & 15), k = 64j + 16 (l >> 4) + [0, 16) in natural order.
+ * 1 KiB block at byte block(t, j) * 1024 (block() as for sv_w4_pack, with
+ * KB = K/64) whose bytes [16l, 16l+16) hold row 16t + (l & 15),
+ * k = 64j + 16 (l >> 4) + [0, 16) in natural order.
  * packed_codes: N*K bytes, 16-byte aligned; N % 16 == 0, K % 64 == 0.
  * The per-channel scales stay as they are (f16 [N]).
  */

@@ -206,17 +206,20 @@ def _i8_gemm(m, K, N, seed):
                 dev=(xq.to(DEV), xs.to(DEV), pc, ps, N, y))
 
 
-def test_w8_pack_layout_matches_contract():
+@pytest.mark.parametrize("N,K", [(32, 192), (544, 128)])   # one partial group of tiles
+def test_w8_pack_layout_matches_contract(N, K):
+    from test_gpu_qgemm import packed_block
     sv = _sv()
-    N, K = 32, 192
     codes, _ = synth.w8_matrix(N, K, seed=5)
-    pc = sv.sv_w8_pack(codes.to(DEV)).cpu().numpy().reshape(N // 16, K // 64, 64, 16)
+    KB, nt = K // 64, N // 16
+    pc = sv.sv_w8_pack(codes.to(DEV)).cpu().numpy().reshape(nt * KB, 64, 16)
     c = codes.numpy().view(np.uint8)
-    for t in range(N // 16):
-        for j in range(K // 64):
+    for t in range(nt):
+        for j in range(KB):
+            blk = packed_block(t, j, KB, nt)
             for l in range(64):
                 n, q = 16 * t + (l & 15), l >> 4
-                assert np.array_equal(pc[t, j, l], c[n, 64 * j + 16 * q: 64 * j + 16 * q + 16])
+                assert np.array_equal(pc[blk, l], c[n, 64 * j + 16 * q: 64 * j + 16 * q + 16])
 
 
 W8_MIXED = [(512, 1024), (192, 48), (640, 4160), (64, 16), (4096, 272), (1088, 8192)]

@@ -165,30 +165,37 @@ def _packed(codes, scales, zeros):
     return sv.sv_w4_pack(*to_dev(codes, scales, zeros))
 
 
-def test_w4_pack_layout_matches_contract():
+def packed_block(t, j, KB, ntile):
+    """The documented block index of tile t, k block j (tiles grouped by 32)."""
+    g = t // 32
+    gt = min(32, ntile - 32 * g)
+    return 32 * g * KB + j * gt + t % 32
+
+
+@pytest.mark.parametrize("N,K", [(32, 256), (560, 384)])   # one partial group of tiles
+def test_w4_pack_layout_matches_contract(N, K):
     # the documented tile-major layout, rebuilt independently from the contract
-    N, K = 32, 256
     codes, scales, zeros = synth.w4_matrix(N, K, seed=77)
     pc, ps = _packed(codes, scales, zeros)
     torch.cuda.synchronize()
     cu = oracle.unpack_w4(codes.numpy())            # [N, K] codes in natural k order
-    pcn = pc.cpu().numpy().reshape(N // 16, K // 128, 64, 4, 4)
-    for t in range(N // 16):
-        for j in range(K // 128):
+    KB, nt = K // 128, N // 16
+    pcn = pc.cpu().numpy().reshape(nt * KB, 64, 4, 4)
+    s, z = scales.numpy(), zeros.numpy()
+    psn = ps.cpu().numpy().reshape(nt * KB, 16, 4)
+    for t in range(nt):
+        for j in range(KB):
+            blk = packed_block(t, j, KB, nt)
             for l in range(64):
                 n, q = 16 * t + (l & 15), l >> 4
                 for wd in range(4):
                     k0 = 128 * j + 64 * (wd // 2) + 16 * q + 8 * (wd % 2)
                     exp = [cu[n, k0 + b] | (cu[n, k0 + b + 4] << 4) for b in range(4)]
-                    assert pcn[t, j, l, wd].tolist() == exp, (t, j, l, wd)
-    s, z = scales.numpy(), zeros.numpy()
-    psn = ps.cpu().numpy().reshape(N // 16, K // 128, 16, 4)
-    for t in range(N // 16):
-        for j in range(K // 128):
+                    assert pcn[blk, l, wd].tolist() == exp, (t, j, l, wd)
             for n in range(16):
                 row = 16 * t + n
                 exp = np.array([s[row, 2 * j], z[row, 2 * j], s[row, 2 * j + 1], z[row, 2 * j + 1]])
-                assert np.array_equal(psn[t, j, n], exp)
+                assert np.array_equal(psn[blk, n], exp)
 
 
 @pytest.mark.parametrize("m,K,N", [(4, 512, 1024),     # the tiny configuration

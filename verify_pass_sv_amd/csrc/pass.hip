@@ -265,7 +265,8 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
       for (int b = 0; b < kNB; ++b) {
         const bool ok = live && tile < ntile && jb + b < KB;
         wb[slot][tw][b] = __builtin_amdgcn_raw_buffer_load_b128(
-            wrs, ok ? lane * 16 : kSvOutOfRange, ok ? (tile * KB + jb + b) * 1024 : 0, 0);
+            wrs, ok ? lane * 16 : kSvOutOfRange,
+            ok ? sv_pk_block(tile, jb + b, KB, ntile) * 1024 : 0, 0);
       }
     }
     if constexpr (Fmt<F>::SZD) {
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
       const int tile = i_t0 + wave * kTW + tw;
       const bool ok = live && tile < ntile && jb + bb < KB;
       const unsigned int off =
-          ok ? (tile * KB + jb + bb) * 128 + (lane & 7) * 16 : kSvOutOfRange;
+          ok ? sv_pk_block(tile, jb + bb, KB, ntile) * 128 + (lane & 7) * 16 : kSvOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           srs, (sv_lds_void*)(sl + G::XBUF + wave * 1024), 16, off, 0, 0, 0);
     }
@@ -752,7 +753,8 @@ __global__ void pack_w8_kernel(const int8_t* __restrict__ codes, int N, int K,
   const int t = static_cast<int>(blk / KB);
   const int n = 16 * t + (l & 15), q = l >> 4;
   const sv_u32x4 v = sv_ld16(codes + static_cast<size_t>(n) * K + 64 * j + 16 * q);
-  *reinterpret_cast<sv_u32x4*>(out + piece * 16) = v;
+  const size_t dst = static_cast<size_t>(sv_pk_block(t, j, KB, N / 16)) * 1024 + l * 16;
+  *reinterpret_cast<sv_u32x4*>(out + dst) = v;
 }
 }  // namespace
 

@@ -8,16 +8,19 @@
 // Speculative Decoding Clearly Explained, "Check the guesses together".
 //
 // Packed layout (made once from the row-major codes by sv_w4_pack):
-//   codes: for each 16-row tile t and each 128-wide k block j, one 1 KiB block
-//          at byte (t * K/128 + j) * 1024.  Bytes [16l, 16l+16) of the block
-//          belong to lane l of a wave: row 16t + (l & 15), slice q = l >> 4;
-//          bytes 0-7 hold the row's codes for k = 128j + 16q + [0, 16), bytes
-//          8-15 for k = 128j + 64 + 16q + [0, 16).  Inside each 4-byte word
-//          covering k0..k0+7, byte b holds code k0+b in its low nibble and
-//          code k0+b+4 in its high nibble, so masking the low and the high
-//          nibbles yields codes in natural k order.
-//   sz:    for each (t, j) a 128-byte block at (t * K/128 + j) * 128; row n
-//          of the tile owns 8 bytes [s(2j), z(2j), s(2j+1), z(2j+1)] (fp16).
+//   codes: one 1 KiB block per 16-row tile t and 128-wide k block j, at
+//          byte sv_pk_block(t, j, K/128, N/16) * 1024 (tiles grouped by 32;
+//          inside a group the blocks of one k block are consecutive).  Bytes
+//          [16l, 16l+16) of the block belong to lane l of a wave: row
+//          16t + (l & 15), slice q = l >> 4; bytes 0-7 hold the row's codes
+//          for k = 128j + 16q + [0, 16), bytes 8-15 for k = 128j + 64 + 16q +
+//          [0, 16).  Inside each 4-byte word covering k0..k0+7, byte b holds
+//          code k0+b in its low nibble and code k0+b+4 in its high nibble, so
+//          masking the low and the high nibbles yields codes in natural k
+//          order.
+//   sz:    a 128-byte record per (t, j) at sv_pk_block(t, j, K/128, N/16) *
+//          128; row n of the tile owns 8 bytes [s(2j), z(2j), s(2j+1),
+//          z(2j+1)] (fp16).
 // A wave reads every code byte once with fully contiguous 1 KiB loads,
 // already in the lane order of the MFMA B operand.
 //
@@ -75,7 +78,8 @@ __global__ void pack_codes_kernel(const uint8_t* __restrict__ codes, int N, int 
   const sv_u32x2 lo = sv_ld8(row + 64 * j + 8 * q);
   const sv_u32x2 hi = sv_ld8(row + 64 * j + 32 + 8 * q);
   sv_u32x4 v = {regroup8(lo.x), regroup8(lo.y), regroup8(hi.x), regroup8(hi.y)};
-  *reinterpret_cast<sv_u32x4*>(out + piece * 16) = v;
+  const size_t dst = static_cast<size_t>(sv_pk_block(t, j, KB, N / 16)) * 1024 + l * 16;
+  *reinterpret_cast<sv_u32x4*>(out + dst) = v;
 }
 
 __global__ void pack_sz_kernel(const uint16_t* __restrict__ scales,
@@ -90,7 +94,7 @@ __global__ void pack_sz_kernel(const uint16_t* __restrict__ scales,
   const int j = static_cast<int>(blk % KB);
   const int t = static_cast<int>(blk / KB);
   const size_t src = static_cast<size_t>(16 * t + n16) * G + 2 * j;
-  uint16_t* o = out + item * 4;
+  uint16_t* o = out + static_cast<size_t>(sv_pk_block(t, j, KB, N / 16)) * 64 + n16 * 4;
   o[0] = scales[src];
   o[1] = zeros[src];
   o[2] = scales[src + 1];
@@ -166,18 +170,18 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
 #pragma unroll
       for (int p = 0; p < PPW; ++p) {
         const bool ok = live && (t0 + t < ntile) && (jb + p < KB);
-        const int blk = ok ? (t0 + t) * KB + jb + p : 0;
+        const int blk = ok ? sv_pk_block(t0 + t, jb + p, KB, ntile) : 0;
         wb[slot][t][p] = __builtin_amdgcn_raw_buffer_load_b128(
             wrs, ok ? lane * 16 : kSvOutOfRange, blk * 1024, 0);
       }
 #pragma unroll
     for (int i = 0; i < DS; ++i) {
       const int t = wave + kWaves * i;            // this piece's tile (>= T: dummy)
-      const bool ok = live && t < T && (t0 + t < ntile);
-      // the whole offset is per-lane so the range check also covers the
-      // tail of the last tile's last chunk
+      // lane -> k block c * 8 + lane / 8 of the tile, 16-byte piece lane % 8
+      const int jj = c * (KC / 128) + (lane >> 3);
+      const bool ok = live && t < T && (t0 + t < ntile) && jj < KB;
       const unsigned int off =
-          ok ? ((t0 + t) * KB + c * (KC / 128)) * 128 + lane * 16 : kSvOutOfRange;
+          ok ? sv_pk_block(t0 + t, jj, KB, ntile) * 128 + (lane & 7) * 16 : kSvOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           srs, (sv_lds_void*)(szl + slot * SZB + (t < T ? t : T) * 512), 16, off, 0, 0, 0);
     }

@@ -7,6 +7,18 @@
 
 typedef __attribute__((address_space(3))) void sv_lds_void;
 
+// Index of the 1 KiB weight block (and of the scale/zero record) of 16-row
+// tile t and k block j in the packed layouts.  Tiles are grouped by 32
+// (512 output rows); inside a group the blocks of one k block are
+// consecutive, so the 32 tiles of a work item read one contiguous range per
+// k block.  The last group of a matrix may hold fewer than 32 tiles.
+//   KB: k blocks per row (K/128 for 4-bit codes, K/64 for 8-bit codes)
+__host__ __device__ __forceinline__ int sv_pk_block(int t, int j, int KB, int ntile) {
+  const int g = t >> 5;
+  const int gt = ntile - 32 * g < 32 ? ntile - 32 * g : 32;
+  return 32 * g * KB + j * gt + (t & 31);
+}
+
 // A constant materialised in a VGPR by an opaque move, so the compiler keeps
 // it in a register instead of folding it into every v_perm.
 __device__ __forceinline__ unsigned int sv_opaque_u32(unsigned int v) {
