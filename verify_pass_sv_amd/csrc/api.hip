@@ -13,16 +13,23 @@ constexpr int kProbeThreads = 256;
 __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const sv_u32x4* __restrict__ src,
                                                                    size_t n16,
                                                                    uint32_t* __restrict__ sink) {
+  // Each workgroup streams one contiguous share with non-temporal 16-byte
+  // loads, eight in flight per lane -- the access pattern of the verify-pass
+  // weight stream.
   unsigned int acc = 0;
-  const size_t stride = static_cast<size_t>(gridDim.x) * kProbeThreads;
-  size_t i = static_cast<size_t>(blockIdx.x) * kProbeThreads + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const sv_u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride],
-                   d = src[i + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^
-           d.z ^ d.w;
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t lo = static_cast<size_t>(blockIdx.x) * per;
+  const size_t hi = lo + per < n16 ? lo + per : n16;
+  size_t i = lo + threadIdx.x;
+  constexpr int U = 8;
+  for (; i + (U - 1) * kProbeThreads < hi; i += U * kProbeThreads) {
+    sv_u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * kProbeThreads);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < n16; i += stride) {
+  for (; i < hi; i += kProbeThreads) {
     const sv_u32x4 a = src[i];
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
