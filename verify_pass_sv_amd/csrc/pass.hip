@@ -148,9 +148,18 @@ struct Geo {
   static_assert(CPR == 16 || CPR == 32, "activation row of 16 or 32 columns");
 };
 
+// W4: group row sums of each slot's activation chunk (MT row tiles x 4
+// groups x 16 rows, binary32), written once per workgroup and shared by the
+// waves.
+template <int F, int MT>
+constexpr int xsum_bytes() {
+  return F == SV_PASS_W4 ? MT * 4 * 16 * 4 : 0;
+}
+
 template <int F, int MT, int P>
 constexpr int pass_lds_bytes() {
-  return P * Geo<F, MT>::SLOT + kWaves * 4096;   // + per-wave output transpose
+  // slots + per-wave output transpose + per-slot row sums
+  return P * Geo<F, MT>::SLOT + kWaves * 4096 + P * xsum_bytes<F, MT>();
 }
 
 // 4 int8 codes (one dword) -> 2 dwords of bf16 pairs holding 128 + c.
@@ -175,7 +184,15 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
   // c's loads are the stores of that same step and the loads and stores of
   // the P - 2 steps after it.
   constexpr int WAITN = NS + (P - 2) * (L + NS);
-  static_assert(WAITN < 64, "too many memory operations in flight for vmcnt");
+  // W4 also needs the activations of chunk c + 1 (the first XD loads of that
+  // chunk) at that wait: after them come the rest of chunk c + 1's loads,
+  // the stores of its step and the loads and stores of the P - 3 steps after.
+  constexpr int WAITX = (L - G::XD) + NS + (P - 3) * (L + NS);
+  constexpr int WAITS = F == SV_PASS_W4 ? WAITX : WAITN;
+  // Before the first step (W4): the activations of chunk 0.
+  constexpr int WAIT0 = (L - G::XD) + NS + (P - 2) * (L + NS);
+  static_assert(P >= 3, "row sums of chunk c + 1 are formed while chunk c computes");
+  static_assert(WAITN < 64 && WAIT0 < 64, "too many memory operations in flight for vmcnt");
   static_assert(kTW * kNB * 128 == 1024, "one 1 KiB scale/zero load per wave per step");
   static_assert(kTW == 4, "the output transpose covers a wave's 4 tiles = 64 channels");
   extern __shared__ __align__(16) uint8_t lds[];
@@ -201,6 +218,7 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
   const sv_f32x4 fz = {0.f, 0.f, 0.f, 0.f};
   const sv_i32x4 iz = {0, 0, 0, 0};
   float* const tpose = reinterpret_cast<float*>(lds + P * G::SLOT) + wave * 1024;
+  float* const xsb = reinterpret_cast<float*>(lds + P * G::SLOT + kWaves * 4096);
 
   // ---- issue cursor: the item and chunk whose loads go out next ----
   int i_item = ib, i_c = 0;
@@ -256,12 +274,34 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
 
   // All L loads of the issue cursor's chunk into `slot` (out-of-range
   // offsets once the cursor has run past the last item).
+  int nvalid[P];                                // weight blocks of the chunk in each slot within K
+#pragma unroll
+  for (int i = 0; i < P; ++i) nvalid[i] = 0;
   auto issue = [&](const int slot) {
     const bool live = i_item < ie;
     const int KB = i_K / Fmt<F>::KPB;           // weight blocks per tile row
     const int jb = i_c * kNB;
     const int ntile = i_N >> 4;
     uint8_t* const sl = lds + slot * G::SLOT;
+    nvalid[slot] = live ? (KB - jb < kNB ? KB - jb : kNB) : 0;
+    // activations first: W4 waits for them one step ahead of the rest
+    const int k0 = i_c * G::KC;
+#pragma unroll
+    for (int i = 0; i < G::XD; ++i) {
+      // rows RPP p .. RPP p + RPP - 1 of the chunk; lane -> row RPP p +
+      // lane / CPR, stored column lane % CPR, read from column
+      // (lane % CPR) ^ (row % 16).  Rows >= m are not read (they only feed
+      // discarded output rows); columns past K land in the next row (never
+      // read) or fail the range check.
+      const int piece = wave + kWaves * i;
+      const int r = G::RPP * piece + lane / G::CPR;
+      const int jj = (lane % G::CPR) ^ (r & 15);
+      const unsigned int off = live && r < m && r < 16 * MT
+                                   ? (r * i_K + k0) * Fmt<F>::XE + jj * 16
+                                   : kSvOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (sv_lds_void*)(sl + piece * 1024), 16, off,
+                                               0, 0, 0);
+    }
 #pragma unroll
     for (int tw = 0; tw < kTW; ++tw) {
       const int tile = i_t0 + wave * kTW + tw;
@@ -299,23 +339,6 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
           ars, (sv_lds_void*)(sl + G::XBUF + G::SZBUF + wave * 1024), 16,
           ok ? lane * 16 : kSvOutOfRange, 0, 0, 0);
     }
-    const int k0 = i_c * G::KC;
-#pragma unroll
-    for (int i = 0; i < G::XD; ++i) {
-      // rows RPP p .. RPP p + RPP - 1 of the chunk; lane -> row RPP p +
-      // lane / CPR, stored column lane % CPR, read from column
-      // (lane % CPR) ^ (row % 16).  Rows >= m are not read (they only feed
-      // discarded output rows); columns past K land in the next row (never
-      // read) or fail the range check.
-      const int piece = wave + kWaves * i;
-      const int r = G::RPP * piece + lane / G::CPR;
-      const int jj = (lane % G::CPR) ^ (r & 15);
-      const unsigned int off = live && r < m && r < 16 * MT
-                                   ? (r * i_K + k0) * Fmt<F>::XE + jj * 16
-                                   : kSvOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (sv_lds_void*)(sl + piece * 1024), 16, off,
-                                               0, 0, 0);
-    }
   };
   auto advance_issue = [&]() {
     if (++i_c == i_nchunk) {
@@ -328,12 +351,36 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
   // row col (+ 16 a rows): swizzled column j ^ col.
   auto aaddr = [&](const int j) { return col * G::XROW + ((j ^ col) << 4); };
 
+  // W4: the group row sums of the activation chunk in `slot`, formed once per
+  // workgroup: wave w < 4 MT takes row tile w / 4 and group w % 4 of the
+  // chunk (two MFMAs with an all-ones A operand put the sum of row col on
+  // lane (col, q)) and writes 16 binary32 sums; groups past K are 0.  Read
+  // by every wave after the next barrier.
+  auto row_sums = [&](const int slot) {
+    if constexpr (F == SV_PASS_W4) {
+      if (wave < 4 * MT) {
+        const int a = wave >> 2, g = wave & 3, b = g >> 1, h = g & 1;
+        const uint8_t* ap = lds + slot * G::SLOT + a * 16 * G::XROW;
+        const sv_u32x4 x0 =
+            *reinterpret_cast<const sv_u32x4*>(ap + aaddr(16 * b + 8 * h + 2 * q));
+        const sv_u32x4 x1 =
+            *reinterpret_cast<const sv_u32x4*>(ap + aaddr(16 * b + 8 * h + 2 * q + 1));
+        sv_f32x4 xt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(ones),
+                                                              sv_as_bf16x8(x0), fz, 0, 0, 0);
+        xt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(ones), sv_as_bf16x8(x1), xt, 0,
+                                                     0, 0);
+        const float v = b < nvalid[slot] ? xt[0] : 0.0f;
+        if (q == 0) xsb[slot * MT * 64 + (a * 4 + g) * 16 + col] = v;
+      }
+    }
+  };
+
   auto compute = [&](const int slot) {
     const int KB = c_K / Fmt<F>::KPB;
     const int jb = c_c * kNB;
     const uint8_t* const sl = lds + slot * G::SLOT;
-    // W4: row sums of the step's 4 groups, lane (col, q) holding row col of
-    // group q (the A operand layout of v_mfma_f32_16x16x4_f32)
+    // W4_I8: row sums of the step's 4 groups, lane (col, q) holding row col
+    // of group q (the A operand layout of v_mfma_f32_16x16x4_f32)
     float xsum[MT];
 #pragma unroll
     for (int a = 0; a < MT; ++a) xsum[a] = 0.f;
@@ -350,14 +397,6 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
             const uint8_t* ap = sl + a * 16 * G::XROW;
             a0[a] = *reinterpret_cast<const sv_u32x4*>(ap + aaddr(16 * b + 8 * h + 2 * q));
             a1[a] = *reinterpret_cast<const sv_u32x4*>(ap + aaddr(16 * b + 8 * h + 2 * q + 1));
-            // group row sums with the rows along N (all-ones A operand): lane
-            // (col, q) receives the sum of row col; the lanes with q = group
-            // index of the step keep it as their A operand of the correction
-            sv_f32x4 xt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                sv_as_bf16x8(ones), sv_as_bf16x8(a0[a]), fz, 0, 0, 0);
-            xt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(ones),
-                                                         sv_as_bf16x8(a1[a]), xt, 0, 0, 0);
-            if (q == 2 * b + h) xsum[a] = xt[0];
           }
 #pragma unroll
           for (int tw = 0; tw < kTW; ++tw) {
@@ -460,6 +499,12 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
       // all records are read (the slot always holds them, stale past K) and
       // groups past K select 0, so no lane-dependent branch splits the reads
       const float gmask = jb + bq < KB ? 1.0f : 0.0f;
+      if constexpr (F == SV_PASS_W4) {
+        // the shared group row sums of this chunk (zero past K): lane
+        // (col, q) takes row col of group q
+#pragma unroll
+        for (int a = 0; a < MT; ++a) xsum[a] = xsb[slot * MT * 64 + (a * 4 + q) * 16 + col];
+      }
       unsigned int szq[kTW];
 #pragma unroll
       for (int tw = 0; tw < kTW; ++tw)
@@ -475,18 +520,21 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
     }
   };
 
-  // NS stores every step.  On an item's last chunk: the epilogue of the
+  // NS stores every step, the same instructions on every path: a store inside
+  // a branch leaves a path without it in the compiler's own count of
+  // outstanding operations, which then waits for more than it must (for
+  // loads of later chunks).  On an item's last chunk: the epilogue of the
   // format, then the wave's 16 rows x 64 channels (its 4 tiles; lane (col, q)
   // of an MFMA output holds rows 4q .. 4q+3 of channel col) go through the
-  // wave's LDS transpose area so that each store writes 4 whole rows of 256
-  // contiguous bytes (lane l: row l / 16, channels 4 (l % 16) .. +3), i.e.
-  // full cache lines.  Otherwise the same number of stores with out-of-range
-  // offsets.
+  // wave's LDS transpose area and come back into yacc so that each store
+  // writes 4 whole rows of 256 contiguous bytes (lane l: row l / 16, channels
+  // 4 (l % 16) .. +3), i.e. full cache lines.  Otherwise the stores carry
+  // whatever yacc holds to distinct out-of-range offsets (stores to one
+  // address could be merged or dropped as dead by the compiler).
   auto store = [&](const int slot, const bool at_end) {
+    const int ch = 4 * (lane & 15);             // this lane's 4 channels in the wave's 64
     if (at_end) {
       const uint8_t* aux = lds + slot * G::SLOT + G::XBUF + G::SZBUF + wave * 1024;
-      const int ch = 4 * (lane & 15);           // this lane's 4 channels in the wave's 64
-      const bool ch_ok = c_t0 + wave * kTW + (ch >> 4) < (c_N >> 4);
 #pragma unroll
       for (int a = 0; a < MT; ++a) {
 #pragma unroll
@@ -511,29 +559,31 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
         // (it may not move these accesses across the fence).
         sv_compiler_fence();
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int row = 4 * rr + (lane >> 4);
-          const sv_u32x4 o = *reinterpret_cast<const sv_u32x4*>(tpose + row * 64 + ch);
-          const int r = 16 * a + row;
-          const unsigned int off =
-              ch_ok && r < m ? (r * c_N + 16 * (c_t0 + wave * kTW) + ch) * 4 : kSvOutOfRange;
-          __builtin_amdgcn_raw_buffer_store_b128(o, yrs, off, 0, kStream);
-        }
+        for (int rr = 0; rr < 4; ++rr)
+          yacc[rr][a] = *reinterpret_cast<const sv_f32x4*>(tpose + (4 * rr + (lane >> 4)) * 64 + ch);
         sv_compiler_fence();                    // before the next 16 rows overwrite the area
       }
+    }
+    const bool ch_ok = at_end && c_t0 + wave * kTW + (ch >> 4) < (c_N >> 4);
+#pragma unroll
+    for (int a = 0; a < MT; ++a) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = 16 * a + 4 * rr + (lane >> 4);
+        const unsigned int off = ch_ok && r < m
+                                     ? (r * c_N + 16 * (c_t0 + wave * kTW) + ch) * 4
+                                     : kSvOutOfRange + (rr * MT + a) * 64;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(sv_u32x4, yacc[rr][a]), yrs, off,
+                                               0, kStream);
+      }
+    }
+    if (at_end) {
 #pragma unroll
       for (int a = 0; a < MT; ++a) {
         xacc[a] = fz;
 #pragma unroll
         for (int t = 0; t < kTW; ++t) yacc[t][a] = fz;
       }
-    } else {
-#pragma unroll
-      for (int tw = 0; tw < kTW; ++tw)
-#pragma unroll
-        for (int a = 0; a < MT; ++a)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(sv_u32x4, yacc[tw][a]), yrs,
-                                                 kSvOutOfRange, 0, 0);
     }
   };
   auto advance_compute = [&]() {
@@ -552,16 +602,24 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
     sv_compiler_fence();
     store(0, false);
   }
+  if constexpr (F == SV_PASS_W4) {
+    sv_wait_vmcnt<WAIT0>();                     // activations of chunk 0, every wave
+    sv_barrier_no_fence();
+    row_sums(0);
+  }
   for (int s0 = 0; s0 < steps; s0 += P) {
 #pragma unroll
     for (int s = 0; s < P; ++s) {
       // chunk s0 + s has landed in slot s (registers and LDS) for every wave,
-      // and every wave has finished the chunk that last used slot s + P - 1
-      sv_wait_vmcnt<WAITN>();
+      // and every wave has finished the chunk that last used slot s + P - 1;
+      // W4: the activations of chunk s0 + s + 1 have landed too, and the
+      // row sums of chunk s0 + s (formed in the previous step) are visible
+      sv_wait_vmcnt<WAITS>();
       sv_barrier_no_fence();
       issue((s + P - 1) % P);
       advance_issue();
       sv_compiler_fence();
+      row_sums((s + 1) % P);                    // W4: activations of chunk s0 + s + 1 have landed
       const bool run = s0 + s < steps;
       const bool at_end = run && c_c == c_nchunk - 1;
       if (run) compute(s);
