@@ -134,3 +134,21 @@ def test_pass_plan_validation_before_any_hip_call():
     assert L.sv_w8_pack(None, 64, 64, plan, None) == 1
     assert L.sv_w8_pack(plan, 40, 64, plan, None) == 2
     assert L.sv_w8_pack(plan, 64, 96, plan, None) == 2
+
+
+def test_build_rejects_scratch_in_counted_kernels():
+    # The executor and the packed GEMM wait on exact counts of their own
+    # memory operations; the build refuses a kernel of theirs that spills.
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "sv_build", os.path.join(ROOT, "verify_pass_sv_amd", "csrc", "build.py"))
+    build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(build)
+    ok = ("a.hip:1:1: remark: Function Name: k0 [-R]\n"
+          "a.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-R]\n")
+    build._check_no_scratch("pass.hip", ok)
+    bad = ok + ("a.hip:2:1: remark: Function Name: k1 [-R]\n"
+                "a.hip:2:1: remark:     ScratchSize [bytes/lane]: 16 [-R]\n")
+    with pytest.raises(RuntimeError, match="k1 uses 16 bytes/lane"):
+        build._check_no_scratch("pass.hip", bad)
+    assert {"pass.hip", "qgemm_w4_packed.hip"} <= build.NO_SCRATCH

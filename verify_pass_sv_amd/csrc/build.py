@@ -5,6 +5,7 @@ and linked into verify_pass_sv_amd/libspecverify.so.  Always recompiles.
 """
 import concurrent.futures
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -36,12 +37,33 @@ def _hipcc():
     raise RuntimeError("hipcc not found; install ROCm or set HIPCC")
 
 
-def _run(cmd, verbose):
+# Kernels that wait on exact counts of their own outstanding vector memory
+# operations: a register spill would add scratch loads and stores to that
+# count, so their build fails if any kernel of the file uses scratch.
+NO_SCRATCH = {"pass.hip", "qgemm_w4_packed.hip"}
+RESOURCE_REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
+
+
+def _check_no_scratch(src, text):
+    kernel = None
+    for line in text.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            kernel = m.group(1)
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) != 0:
+            raise RuntimeError(f"{src}: kernel {kernel} uses {m.group(1)} bytes/lane of scratch "
+                               "(register spills break its exact memory-operation count)")
+
+
+def _run(cmd, verbose, src=None):
     if verbose:
         print(" ".join(cmd), flush=True)
     p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if src in NO_SCRATCH and p.returncode == 0:
+        _check_no_scratch(src, p.stdout)
     out = "\n".join(l for l in p.stdout.splitlines()
-                    if "packed-fp32-ops" not in l or "error" in l)
+                    if ("packed-fp32-ops" not in l and "remark:" not in l) or "error" in l)
     if p.returncode != 0:
         raise RuntimeError(f"command failed ({p.returncode}): {' '.join(cmd)}\n{out}")
     if verbose and out.strip():
@@ -57,10 +79,11 @@ def build(verbose=False, jobs=None):
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([hipcc, *CXXFLAGS, "-c", os.path.join(HERE, src), "-o", obj])
+        extra = RESOURCE_REMARKS if src in NO_SCRATCH else []
+        cmds.append(([hipcc, *CXXFLAGS, *extra, "-c", os.path.join(HERE, src), "-o", obj], src))
     jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 2) // 2))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        list(ex.map(lambda c: _run(c, verbose), cmds))
+        list(ex.map(lambda c: _run(c[0], verbose, c[1]), cmds))
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)

@@ -405,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
             const sv_u32x4 b1 = sv_w4_dequant8(h ? w.w : w.y, magic);
             const sv_u32x2 sbt =
                 *reinterpret_cast<const sv_u32x2*>(sp + (tw * kNB + b) * 128);
-            const float sc = sv_half_lo(h ? sbt.y : sbt.x);
+            const float sc = sv_materialize(sv_half_lo(h ? sbt.y : sbt.x));
 #pragma unroll
             for (int a = 0; a < MT; ++a) {
               sv_f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -472,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
                                  (wy >> 4) & 0x0F0F0F0Fu};
             const sv_u32x2 sbt =
                 *reinterpret_cast<const sv_u32x2*>(sp + (tw * kNB + b) * 128);
-            const float sc = sv_half_lo(h ? sbt.y : sbt.x);
+            const float sc = sv_materialize(sv_half_lo(h ? sbt.y : sbt.x));
 #pragma unroll
             for (int a = 0; a < MT; ++a) {
               const sv_i32x4 I = __builtin_amdgcn_mfma_i32_16x16x64_i8(

@@ -27,6 +27,15 @@ __device__ __forceinline__ unsigned int sv_opaque_u32(unsigned int v) {
   return r;
 }
 
+// A binary32 value the compiler must keep as it is: it cannot fold the
+// conversion that produced it into its users.  On gfx950 v_fma_mix_f32 (an
+// f16 operand converted inside the FMA) issues at half the rate of v_fma_f32,
+// so a scale used by many FMAs is converted once instead.
+__device__ __forceinline__ float sv_materialize(float v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
 // Packed word (byte b = codes b | b+4 << 4) -> four bf16 pairs holding
 // 128 + c in natural k order: a mask isolates the nibbles and one byte
 // permute against the 0x43 exponent byte in `magic` makes bf16 0x43cc.
