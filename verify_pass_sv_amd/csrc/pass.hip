@@ -179,18 +179,22 @@ template <int F, int MT, int P>
 __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restrict__ plan, int m) {
   using G = Geo<F, MT>;
   constexpr int L = kTW * kNB + Fmt<F>::SZD + Fmt<F>::AUXD + G::XD;   // loads per wave per step
-  constexpr int NS = 4 * MT;                    // 16-byte stores per wave per step
-  // At the wait before computing chunk c, the operations issued after chunk
-  // c's loads are the stores of that same step and the loads and stores of
-  // the P - 2 steps after it.
-  constexpr int WAITN = NS + (P - 2) * (L + NS);
+  // Waits count only loads.  Vector memory operations of a wave complete in
+  // issue order, and the output stores (4 MT per wave, on an item's last
+  // chunk only) come on top of the counted ones, so each wait is exact
+  // except after an item end, where it is stricter than needed.  (A store
+  // issued every step to keep the count exact costs as much address
+  // processing as a real one.)
+  // At the wait before computing chunk c, the loads issued after chunk c's
+  // are those of the P - 2 steps after it.
+  constexpr int WAITN = (P - 2) * L;
   // W4 also needs the activations of chunk c + 1 (the first XD loads of that
-  // chunk) at that wait: after them come the rest of chunk c + 1's loads,
-  // the stores of its step and the loads and stores of the P - 3 steps after.
-  constexpr int WAITX = (L - G::XD) + NS + (P - 3) * (L + NS);
+  // chunk) at that wait: after them come the rest of chunk c + 1's loads and
+  // the loads of the P - 3 steps after.
+  constexpr int WAITX = (L - G::XD) + (P - 3) * L;
   constexpr int WAITS = F == SV_PASS_W4 ? WAITX : WAITN;
   // Before the first step (W4): the activations of chunk 0.
-  constexpr int WAIT0 = (L - G::XD) + NS + (P - 2) * (L + NS);
+  constexpr int WAIT0 = (L - G::XD) + (P - 2) * L;
   static_assert(P >= 3, "row sums of chunk c + 1 are formed while chunk c computes");
   static_assert(WAITN < 64 && WAIT0 < 64, "too many memory operations in flight for vmcnt");
   static_assert(kTW * kNB * 128 == 1024, "one 1 KiB scale/zero load per wave per step");
@@ -520,51 +524,44 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
     }
   };
 
-  // NS stores every step, the same instructions on every path: a store inside
-  // a branch leaves a path without it in the compiler's own count of
-  // outstanding operations, which then waits for more than it must (for
-  // loads of later chunks).  On an item's last chunk: the epilogue of the
-  // format, then the wave's 16 rows x 64 channels (its 4 tiles; lane (col, q)
-  // of an MFMA output holds rows 4q .. 4q+3 of channel col) go through the
-  // wave's LDS transpose area and come back into yacc so that each store
-  // writes 4 whole rows of 256 contiguous bytes (lane l: row l / 16, channels
-  // 4 (l % 16) .. +3), i.e. full cache lines.  Otherwise the stores carry
-  // whatever yacc holds to distinct out-of-range offsets (stores to one
-  // address could be merged or dropped as dead by the compiler).
-  auto store = [&](const int slot, const bool at_end) {
+  // On an item's last chunk: the epilogue of the format, then the wave's
+  // 16 rows x 64 channels (its 4 tiles; lane (col, q) of an MFMA output holds
+  // rows 4q .. 4q+3 of channel col) go through the wave's LDS transpose area
+  // and come back into yacc so that each of the 4 MT stores writes 4 whole
+  // rows of 256 contiguous bytes (lane l: row l / 16, channels 4 (l % 16) ..
+  // +3), i.e. full cache lines.
+  auto store = [&](const int slot) {
     const int ch = 4 * (lane & 15);             // this lane's 4 channels in the wave's 64
-    if (at_end) {
-      const uint8_t* aux = lds + slot * G::SLOT + G::XBUF + G::SZBUF + wave * 1024;
+    const uint8_t* aux = lds + slot * G::SLOT + G::XBUF + G::SZBUF + wave * 1024;
 #pragma unroll
-      for (int a = 0; a < MT; ++a) {
+    for (int a = 0; a < MT; ++a) {
 #pragma unroll
-        for (int tw = 0; tw < kTW; ++tw) {
-          sv_f32x4 v = yacc[tw][a];
-          if constexpr (F == SV_PASS_W8) {
-            const float sc = __half2float(
-                *reinterpret_cast<const __half*>(aux + (tw * 16 + col) * 2));
+      for (int tw = 0; tw < kTW; ++tw) {
+        sv_f32x4 v = yacc[tw][a];
+        if constexpr (F == SV_PASS_W8) {
+          const float sc = __half2float(
+              *reinterpret_cast<const __half*>(aux + (tw * 16 + col) * 2));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = sc * fmaf(-128.0f, xacc[a][i], v[i]);
-          }
-          if constexpr (F == SV_PASS_W4_I8) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              v[i] *= *reinterpret_cast<const float*>(aux + (16 * a + 4 * q + i) * 4);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) tpose[(4 * q + i) * 64 + tw * 16 + col] = v[i];
+          for (int i = 0; i < 4; ++i) v[i] = sc * fmaf(-128.0f, xacc[a][i], v[i]);
         }
-        // Lanes read what other lanes wrote: LDS operations of a wave execute
-        // in order, so it is enough that the compiler keeps program order
-        // (it may not move these accesses across the fence).
-        sv_compiler_fence();
+        if constexpr (F == SV_PASS_W4_I8) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          yacc[rr][a] = *reinterpret_cast<const sv_f32x4*>(tpose + (4 * rr + (lane >> 4)) * 64 + ch);
-        sv_compiler_fence();                    // before the next 16 rows overwrite the area
+          for (int i = 0; i < 4; ++i)
+            v[i] *= *reinterpret_cast<const float*>(aux + (16 * a + 4 * q + i) * 4);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tpose[(4 * q + i) * 64 + tw * 16 + col] = v[i];
       }
+      // Lanes read what other lanes wrote: LDS operations of a wave execute
+      // in order, so it is enough that the compiler keeps program order
+      // (it may not move these accesses across the fence).
+      sv_compiler_fence();
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        yacc[rr][a] = *reinterpret_cast<const sv_f32x4*>(tpose + (4 * rr + (lane >> 4)) * 64 + ch);
+      sv_compiler_fence();                    // before the next 16 rows overwrite the area
     }
-    const bool ch_ok = at_end && c_t0 + wave * kTW + (ch >> 4) < (c_N >> 4);
+    const bool ch_ok = c_t0 + wave * kTW + (ch >> 4) < (c_N >> 4);
 #pragma unroll
     for (int a = 0; a < MT; ++a) {
 #pragma unroll
@@ -572,18 +569,16 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
         const int r = 16 * a + 4 * rr + (lane >> 4);
         const unsigned int off = ch_ok && r < m
                                      ? (r * c_N + 16 * (c_t0 + wave * kTW) + ch) * 4
-                                     : kSvOutOfRange + (rr * MT + a) * 64;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(sv_u32x4, yacc[rr][a]), yrs, off,
-                                               0, kStream);
+                                     : kSvOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(sv_u32x4, yacc[rr][a]), yrs,
+                                               off, 0, kStream);
       }
     }
-    if (at_end) {
 #pragma unroll
-      for (int a = 0; a < MT; ++a) {
-        xacc[a] = fz;
+    for (int a = 0; a < MT; ++a) {
+      xacc[a] = fz;
 #pragma unroll
-        for (int t = 0; t < kTW; ++t) yacc[t][a] = fz;
-      }
+      for (int t = 0; t < kTW; ++t) yacc[t][a] = fz;
     }
   };
   auto advance_compute = [&]() {
@@ -593,14 +588,12 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
     }
   };
 
-  // Prologue: P - 1 chunks in flight, each followed by a step's worth of
-  // (out-of-range) stores so every step sees the same operation pattern.
+  // Prologue: P - 1 chunks in flight.
 #pragma unroll
   for (int i = 0; i < P - 1; ++i) {
     issue(i);
     advance_issue();
     sv_compiler_fence();
-    store(0, false);
   }
   if constexpr (F == SV_PASS_W4) {
     sv_wait_vmcnt<WAIT0>();                     // activations of chunk 0, every wave
@@ -623,7 +616,7 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
       const bool run = s0 + s < steps;
       const bool at_end = run && c_c == c_nchunk - 1;
       if (run) compute(s);
-      store(s, at_end);
+      if (at_end) store(s);
       if (run) advance_compute();
     }
   }
