@@ -185,15 +185,23 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
   // except after an item end, where it is stricter than needed.  (A store
   // issued every step to keep the count exact costs as much address
   // processing as a real one.)
-  // At the wait before computing chunk c, the loads issued after chunk c's
-  // are those of the P - 2 steps after it.
-  constexpr int WAITN = (P - 2) * L;
-  // W4 also needs the activations of chunk c + 1 (the first XD loads of that
-  // chunk) at that wait: after them come the rest of chunk c + 1's loads and
-  // the loads of the P - 3 steps after.
+  // Chunk c's loads go out in two parts: its weights (LW loads, into the
+  // registers chunk c - P has just freed) at the end of step c - P, its LDS
+  // loads (activations first) at the start of step c - P + 1, after the
+  // barrier that frees their slot.  So the weights run a full step further
+  // ahead than the LDS data without more registers.  At the wait before
+  // computing chunk c, the loads issued after chunk c's are the weights of
+  // chunk c + 1 and the loads of the P - 2 steps after.
+  constexpr int LW = kTW * kNB;
+  constexpr int WAITN = LW + (P - 2) * L;
+  // W4 also needs the activations of chunk c + 1 (the first XD loads of its
+  // LDS part) at that wait: after them come the rest of that part, the
+  // weights of chunk c + 2 and the loads of the P - 3 steps after.
   constexpr int WAITX = (L - G::XD) + (P - 3) * L;
   constexpr int WAITS = F == SV_PASS_W4 ? WAITX : WAITN;
-  // Before the first step (W4): the activations of chunk 0.
+  // Before the first step (W4): the activations of chunk 0 (the prologue
+  // issues weights, then LDS loads, chunk by chunk, and the weights of chunk
+  // P - 1 last).
   constexpr int WAIT0 = (L - G::XD) + (P - 2) * L;
   static_assert(P >= 3, "row sums of chunk c + 1 are formed while chunk c computes");
   static_assert(WAITN < 64 && WAIT0 < 64, "too many memory operations in flight for vmcnt");
@@ -224,10 +232,24 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
   float* const tpose = reinterpret_cast<float*>(lds + P * G::SLOT) + wave * 1024;
   float* const xsb = reinterpret_cast<float*>(lds + P * G::SLOT + kWaves * 4096);
 
-  // ---- issue cursor: the item and chunk whose loads go out next ----
+  // ---- weight cursor: the item and chunk whose weight loads go out next ----
+  int w_item = ib, w_c = 0;
+  int w_K = 128, w_N = 16, w_t0 = 0, w_nchunk = 1;
+  __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0x00020000);
+  auto load_w_item = [&](int idx) {
+    const PlanItem it = items[idx];
+    w_K = it.K;
+    w_N = it.N;
+    w_t0 = it.tile0;
+    w_nchunk = it.nchunk;
+    wrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(it.codes), 0,
+                                            F == SV_PASS_W8 ? it.N * it.K : it.N * (it.K / 2),
+                                            0x00020000);
+  };
+  // ---- LDS cursor: the item and chunk whose activation / record loads go
+  // out next (one chunk behind the weight cursor in steady state) ----
   int i_item = ib, i_c = 0;
   int i_K = 128, i_N = 16, i_t0 = 0, i_nchunk = 1;
-  __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0x00020000);
   __amdgpu_buffer_rsrc_t srs = wrs, xrs = wrs, ars = wrs;
   auto load_issue_item = [&](int idx) {
     const PlanItem it = items[idx];
@@ -235,9 +257,6 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
     i_N = it.N;
     i_t0 = it.tile0;
     i_nchunk = it.nchunk;
-    wrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(it.codes), 0,
-                                            F == SV_PASS_W8 ? it.N * it.K : it.N * (it.K / 2),
-                                            0x00020000);
     if constexpr (Fmt<F>::SZD)
       srs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(it.sz), 0,
                                               it.N * (it.K / kGroup) * 4, 0x00020000);
@@ -262,6 +281,7 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
     yrs = __builtin_amdgcn_make_buffer_rsrc(it.y, 0, m * it.N * 4, 0x00020000);
   };
   if (ib < ie) {
+    load_w_item(ib);
     load_issue_item(ib);
     load_compute_item(ib);
   }
@@ -276,12 +296,13 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
     for (int t = 0; t < kTW; ++t) yacc[t][a] = fz;
   }
 
-  // All L loads of the issue cursor's chunk into `slot` (out-of-range
-  // offsets once the cursor has run past the last item).
+  // The activation, record and item-end loads of the LDS cursor's chunk into
+  // `slot` (out-of-range offsets once the cursor has run past the last
+  // item), activations first.
   int nvalid[P];                                // weight blocks of the chunk in each slot within K
 #pragma unroll
   for (int i = 0; i < P; ++i) nvalid[i] = 0;
-  auto issue = [&](const int slot) {
+  auto issue_lds = [&](const int slot) {
     const bool live = i_item < ie;
     const int KB = i_K / Fmt<F>::KPB;           // weight blocks per tile row
     const int jb = i_c * kNB;
@@ -305,17 +326,6 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
                                    : kSvOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (sv_lds_void*)(sl + piece * 1024), 16, off,
                                                0, 0, 0);
-    }
-#pragma unroll
-    for (int tw = 0; tw < kTW; ++tw) {
-      const int tile = i_t0 + wave * kTW + tw;
-#pragma unroll
-      for (int b = 0; b < kNB; ++b) {
-        const bool ok = live && tile < ntile && jb + b < KB;
-        wb[slot][tw][b] = __builtin_amdgcn_raw_buffer_load_b128(
-            wrs, ok ? lane * 16 : kSvOutOfRange,
-            ok ? sv_pk_block(tile, jb + b, KB, ntile) * 1024 : 0, kStream);
-      }
     }
     if constexpr (Fmt<F>::SZD) {
       // scale/zero records of this wave's tiles, one 128-byte record per
@@ -342,6 +352,31 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ars, (sv_lds_void*)(sl + G::XBUF + G::SZBUF + wave * 1024), 16,
           ok ? lane * 16 : kSvOutOfRange, 0, 0, 0);
+    }
+  };
+  // The weight loads of the weight cursor's chunk into `slot`'s registers:
+  // one 1 KiB block per tile and k block, already in MFMA operand order.
+  auto issue_w = [&](const int slot) {
+    const bool live = w_item < ie;
+    const int KB = w_K / Fmt<F>::KPB;           // weight blocks per tile row
+    const int jb = w_c * kNB;
+    const int ntile = w_N >> 4;
+#pragma unroll
+    for (int tw = 0; tw < kTW; ++tw) {
+      const int tile = w_t0 + wave * kTW + tw;
+#pragma unroll
+      for (int b = 0; b < kNB; ++b) {
+        const bool ok = live && tile < ntile && jb + b < KB;
+        wb[slot][tw][b] = __builtin_amdgcn_raw_buffer_load_b128(
+            wrs, ok ? lane * 16 : kSvOutOfRange,
+            ok ? sv_pk_block(tile, jb + b, KB, ntile) * 1024 : 0, kStream);
+      }
+    }
+  };
+  auto advance_w = [&]() {
+    if (++w_c == w_nchunk) {
+      w_c = 0;
+      if (++w_item < ie) load_w_item(w_item);
     }
   };
   auto advance_issue = [&]() {
@@ -588,13 +623,18 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
     }
   };
 
-  // Prologue: P - 1 chunks in flight.
+  // Prologue: chunks 0 .. P - 2 in flight, and the weights of chunk P - 1.
 #pragma unroll
   for (int i = 0; i < P - 1; ++i) {
-    issue(i);
+    issue_w(i);
+    advance_w();
+    issue_lds(i);
     advance_issue();
     sv_compiler_fence();
   }
+  issue_w(P - 1);
+  advance_w();
+  sv_compiler_fence();
   if constexpr (F == SV_PASS_W4) {
     sv_wait_vmcnt<WAIT0>();                     // activations of chunk 0, every wave
     sv_barrier_no_fence();
@@ -604,18 +644,23 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
 #pragma unroll
     for (int s = 0; s < P; ++s) {
       // chunk s0 + s has landed in slot s (registers and LDS) for every wave,
-      // and every wave has finished the chunk that last used slot s + P - 1;
+      // and every wave has finished the chunk that last used the LDS of
+      // slot s + P - 1;
       // W4: the activations of chunk s0 + s + 1 have landed too, and the
       // row sums of chunk s0 + s (formed in the previous step) are visible
       sv_wait_vmcnt<WAITS>();
       sv_barrier_no_fence();
-      issue((s + P - 1) % P);
+      issue_lds((s + P - 1) % P);
       advance_issue();
       sv_compiler_fence();
       row_sums((s + 1) % P);                    // W4: activations of chunk s0 + s + 1 have landed
       const bool run = s0 + s < steps;
       const bool at_end = run && c_c == c_nchunk - 1;
       if (run) compute(s);
+      sv_compiler_fence();
+      issue_w(s);                               // chunk s0 + s + P into the registers just freed
+      advance_w();
+      sv_compiler_fence();
       if (at_end) store(s);
       if (run) advance_compute();
     }
