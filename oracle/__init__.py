@@ -31,7 +31,9 @@ from .qgemm import (unpack_w4, dequant_w4, qgemm_w4, dequant_w8, qgemm_w8,
                     qgemm_w4_i8, group_int_partials)
 from .hadamard import sylvester, rht, quantize_per_token, hadamard_i8
 from .accept import (row_lse, accept_trial, verify_accept, AcceptResult,
-                     NEAR_TIE_ACCEPT)
+                     NEAR_TIE_ACCEPT, accept_on_probs)
+from .sampling import (truncated_probs, greedy_choice, accept_trial_sampled,
+                       verify_accept_sampled, sample_drafts, NEAR_TIE_TOP_P)
 from .roofline import (tokens_per_s_bound, w4_bytes_per_weight,
                        decoder_stack_shapes, stack_weight_count,
                        stack_weight_bytes_w4, stack_weight_bytes_w8)
@@ -41,7 +43,9 @@ __all__ = [
     "accept_uniforms", "unpack_w4", "dequant_w4", "qgemm_w4", "dequant_w8",
     "qgemm_w8", "qgemm_w4_i8", "group_int_partials", "sylvester", "rht",
     "quantize_per_token", "hadamard_i8", "row_lse", "accept_trial",
-    "verify_accept", "AcceptResult", "NEAR_TIE_ACCEPT", "tokens_per_s_bound",
+    "verify_accept", "AcceptResult", "NEAR_TIE_ACCEPT", "accept_on_probs",
+    "truncated_probs", "greedy_choice", "accept_trial_sampled",
+    "verify_accept_sampled", "sample_drafts", "NEAR_TIE_TOP_P", "tokens_per_s_bound",
     "w4_bytes_per_weight", "decoder_stack_shapes", "stack_weight_count",
     "stack_weight_bytes_w4", "stack_weight_bytes_w8",
 ]

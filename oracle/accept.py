@@ -109,9 +109,29 @@ def accept_trial(target_logits, draft_logits, draft_tokens, u, u2):
         return AcceptResult(status=2, n_acc=-1, tokens=[],
                             lse_target=lse_t, lse_draft=lse_d)
 
+    P = probs(t, lse_t[:, None])
+    Q = probs(d, lse_d[:, None])
+    res = accept_on_probs(P, Q, toks, u, u2)
+    res.lse_target = lse_t
+    res.lse_draft = lse_d
+    return res
+
+
+def accept_on_probs(P, Q, draft_tokens, u, u2):
+    """The accept scan and the replacement/bonus draw on explicit rows.
+
+    P [k + 1, V]: the target's distributions (row k for the bonus), Q [k, V]:
+    the draft's, both binary64 and normalised; draft tokens in [0, V).  The
+    rule is the one of accept_trial (readings 2, 4 and 6).
+    """
+    P = np.asarray(P, dtype=np.float64)
+    Q = np.asarray(Q, dtype=np.float64)
+    toks = np.asarray(draft_tokens, dtype=np.int64)
+    k = toks.shape[0]
+    V = P.shape[-1]
     idx = np.arange(k)
-    p_at = np.exp(t[idx, toks] - lse_t[:k])
-    q_at = np.exp(d[idx, toks] - lse_d)
+    p_at = P[idx, toks]
+    q_at = Q[idx, toks]
 
     # Left to right, stop at the first rejection.
     n_acc = k
@@ -124,9 +144,9 @@ def accept_trial(target_logits, draft_logits, draft_tokens, u, u2):
             break
 
     r = n_acc
-    p_r = probs(t[r], lse_t[r])
+    p_r = P[r]
     if r < k:
-        w = np.maximum(0.0, p_r - probs(d[r], lse_d[r]))
+        w = np.maximum(0.0, p_r - Q[r])
     else:
         w = p_r
     csum = np.cumsum(w)
@@ -142,8 +162,8 @@ def accept_trial(target_logits, draft_logits, draft_tokens, u, u2):
             (abs(csum[v] - thr) < NEAR_TIE_RESIDUAL * S)
     return AcceptResult(status=0, n_acc=n_acc,
                         tokens=[int(x) for x in toks[:n_acc]] + [v],
-                        p_at=p_at, q_at=q_at, lse_target=lse_t,
-                        lse_draft=lse_d, accept_flags=flags[:min(n_acc + 1, k)],
+                        p_at=p_at, q_at=q_at,
+                        accept_flags=flags[:min(n_acc + 1, k)],
                         residual_flag=bool(rflag), residual_row=r,
                         weights_sum=float(S))
 
