@@ -31,7 +31,8 @@ Readings taken where the pages are silent:
 6. Near-tie flags: an accept decision with |u q - p| < 1e-6, or a residual
    draw whose threshold lies within 1e-6 * S of the chosen bin's edges, is
    marked; a binary32 implementation may legitimately decide it the other
-   way.
+   way.  A decision with p = 0 (always rejected) or q = 0 < p (always
+   accepted) is exact in any precision and is not marked.
 
 Parity: pinned -- worked examples (tests/golden), exact output law by
 quadrature over the uniforms on tiny vocabularies, chi-square on Philox-driven
@@ -138,7 +139,7 @@ def accept_on_probs(P, Q, draft_tokens, u, u2):
     flags = np.zeros(k, dtype=bool)
     for i in range(k):
         lhs = u[i] * q_at[i]
-        flags[i] = abs(lhs - p_at[i]) < NEAR_TIE_ACCEPT
+        flags[i] = abs(lhs - p_at[i]) < NEAR_TIE_ACCEPT and p_at[i] > 0.0 and q_at[i] > 0.0
         if not (lhs < p_at[i]):
             n_acc = i
             break

@@ -16,7 +16,8 @@ Readings taken where the pages are silent:
    the target's choice at position i is the argmax of its row i (the smallest
    index among equal maxima); a draft is accepted iff it equals that choice,
    the first mismatch is replaced by the choice, and after k matches the bonus
-   is the argmax of row k.  No uniforms are used.
+   is the argmax of row k.  No uniforms are used and the draft rows are not
+   consulted (an invalid draft row does not invalidate the trial).
 2. Order: temperature, then top-k, then top-p on the renormalised top-k
    distribution.  top-k and top-p act on ranks, which a positive temperature
    does not change.
@@ -29,9 +30,11 @@ Readings taken where the pages are silent:
    and the residual/bonus draw of accept.py then run on those distributions.
    A draft token outside the draft's kept set has q = 0 and is accepted iff
    p > 0 (u * 0 < p).
-6. Near-tie flag: a top-p boundary whose running sum lies within 1e-6 of
-   top_p (either side of the crossing token) may be drawn the other way by a
-   binary32 implementation.
+6. Masses are compared in binary64.  Near-tie flag: a top-p boundary whose
+   running sum lies within 1e-9 of top_p (either side of the crossing token)
+   may be drawn the other way by a binary64 implementation that sums in
+   another order.  The settings are the binary32 values an implementation
+   receives; callers pass them rounded.
 
 Parity: pinned -- the default settings reproduce accept.py exactly; top_k = 1
 and greedy verification agree for any uniforms; hand-worked truncations
@@ -45,7 +48,7 @@ import numpy as np
 from .accept import AcceptResult, accept_on_probs, row_lse
 from .philox import accept_uniforms
 
-NEAR_TIE_TOP_P = 1e-6
+NEAR_TIE_TOP_P = 1e-9
 
 
 def check_settings(temperature, top_k, top_p):
@@ -121,7 +124,8 @@ def accept_trial_sampled(target_logits, draft_logits, draft_tokens, u, u2,
         return AcceptResult(status=1, n_acc=-1, tokens=[])
     _, ok_t = row_lse(t)
     _, ok_d = row_lse(d)
-    if not (ok_t.all() and ok_d.all()):
+    # greedy verification does not depend on the draft rows
+    if not (ok_t.all() and (ok_d.all() or temperature == 0.0)):
         return AcceptResult(status=2, n_acc=-1, tokens=[])
     if temperature == 0.0:
         g = [greedy_choice(t[i]) for i in range(k + 1)]
