@@ -337,6 +337,55 @@ sv_status sv_verify_accept(const float* target_logits, const float* draft_logits
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * sv_verify_sampled -- verification under a request's sampling settings:
+ * temperature, top-k and top-p, or greedy verification at temperature 0.
+ *
+ * Settings (Karpathy's Trick for Faster Local LLMs, "Call Uzu through a local
+ * application endpoint": the server honours temperature, top_p and top_k;
+ * "Use one client for Uzu, MLX, and llama.cpp": temperature 0):
+ *   temperature T  0: greedy; > 0 (finite): logits are divided by T
+ *   top_k          0 (or >= V): no truncation; else keep the top_k largest
+ *                  logits, smaller indices first among equal logits
+ *   top_p          in (0, 1]; 1: no truncation; else, on the renormalised
+ *                  top-k row, keep the shortest prefix of tokens in
+ *                  decreasing probability (ties by ascending index) whose
+ *                  sum reaches top_p (the crossing token is kept)
+ * Defines, per independent trial b (Speculative Decoding Clearly Explained,
+ * "Accept from left to right" and "Correct and continue"):
+ *   T > 0: p'_i, q'_i = the target and draft rows after temperature, top-k
+ *   and top-p, renormalised; then exactly the rule of sv_verify_accept on
+ *   p', q' with the same Philox uniforms (a draft token outside q's kept set
+ *   has q' = 0 and is accepted iff p' > 0).
+ *   T = 0: g_i = argmax of target row i (smallest index among equal
+ *   maxima); accept d_i iff d_i == g_i, stop at the first mismatch r and
+ *   emit g_r; after k matches emit g_k.  No random numbers; draft rows are
+ *   not read.
+ *   Outputs as sv_verify_accept; p_at / q_at hold p'_i(d_i), q'_i(d_i)
+ *   (greedy: 1 if d_i == g_i else 0, and 1).
+ *
+ *   target_logits, draft_logits, draft_tokens, B, k, V, seed, offset,
+ *   out_tokens, out_n_acc, out_status, p_at, q_at: as sv_verify_accept
+ *   (B <= 65535)
+ *   sampling   host pointer to the settings; invalid settings return
+ *              SV_ERR_INVALID_ARG before any launch
+ *   workspace  device scratch of at least
+ *              sv_verify_sampled_workspace_bytes(B, k, V) bytes; contents need
+ *              no initialization and are clobbered.
+ */
+typedef struct sv_sampling {
+  float temperature;
+  int top_k;
+  float top_p;
+} sv_sampling;
+size_t sv_verify_sampled_workspace_bytes(int B, int k, int V);
+sv_status sv_verify_sampled(const float* target_logits, const float* draft_logits,
+                            const int32_t* draft_tokens, int B, int k, int V,
+                            const sv_sampling* sampling, uint64_t seed, uint32_t offset,
+                            int32_t* out_tokens, int32_t* out_n_acc, int32_t* out_status,
+                            float* p_at, float* q_at, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
  * sv_philox4x32_10 -- the device Philox4x32-10 bijection used by
  * sv_verify_accept, exposed so callers can check it against the published
  * known-answer vectors.  ctr uint32 [n, 4], key uint32 [n, 2], out uint32

@@ -152,3 +152,25 @@ def test_build_rejects_scratch_in_counted_kernels():
     with pytest.raises(RuntimeError, match="k1 uses 16 bytes/lane"):
         build._check_no_scratch("pass.hip", bad)
     assert {"pass.hip", "qgemm_w4_packed.hip"} <= build.NO_SCRATCH
+
+
+def test_sampled_verification_validation_before_launch():
+    import verify_pass_sv_amd as sv
+    L = sv.lib
+    fake = ctypes.c_void_p(0x100000)     # aligned, never dereferenced
+    ws = sv.sv_verify_sampled_workspace_bytes(4, 8, 1000)
+    assert ws > 0 and sv.sv_verify_sampled_workspace_bytes(4, 33, 1000) == 0
+    assert sv.sv_verify_sampled_workspace_bytes(64, 32, 152000) > ws
+
+    def call(cfg, ws_bytes=ws, workspace=fake, k=8):
+        ref = ctypes.byref(cfg) if cfg is not None else None
+        return L.sv_verify_sampled(fake, fake, fake, 4, k, 1000, ref, 0, 0, fake, fake, fake,
+                                   None, None, workspace, ws_bytes, None)
+    S = sv.SvSampling
+    assert call(None) == 1
+    for bad in [S(-1.0, 0, 1.0), S(float("inf"), 0, 1.0), S(float("nan"), 0, 1.0),
+                S(1.0, -1, 1.0), S(1.0, 0, 0.0), S(1.0, 0, 1.5), S(1.0, 0, float("nan"))]:
+        assert call(bad) == 2
+    assert call(S(1.0, 0, 1.0), k=0) == 2
+    assert call(S(0.7, 40, 0.9), ws_bytes=ws - 1) == 5
+    assert call(S(0.7, 40, 0.9), workspace=None) == 5

@@ -13,7 +13,7 @@ _BINDING_NAMES = (
     "sv_philox4x32_10", "sv_read_bandwidth_probe", "sv_read_probe_sink_words",
     "EXPORTED_SYMBOLS", "SV_MAX_ROWS", "sv_w4_pack", "sv_qgemm_w4_packed",
     "sv_w8_pack", "sv_pass_plan", "sv_pass_run", "Pass", "SvPassGemm", "SvPass",
-    "PASS_FORMATS",
+    "PASS_FORMATS", "sv_verify_sampled", "sv_verify_sampled_workspace_bytes", "SvSampling",
 )
 
 __all__ = list(_BINDING_NAMES)

@@ -21,6 +21,7 @@ EXPORTED_SYMBOLS = (
     "sv_philox4x32_10", "sv_read_probe_sink_words", "sv_read_bandwidth_probe",
     "sv_w4_packed_codes_bytes", "sv_w4_packed_sz_bytes", "sv_w4_pack", "sv_qgemm_w4_packed",
     "sv_w8_pack", "sv_pass_plan_bytes", "sv_pass_plan", "sv_pass_run",
+    "sv_verify_sampled_workspace_bytes", "sv_verify_sampled",
 )
 
 _STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_INVALID_ARG", 3: "SV_ERR_ALIGN",
@@ -42,6 +43,12 @@ class SvPass(ctypes.Structure):
 
 
 PASS_FORMATS = {"w4": 0, "w8": 1, "w4_i8": 2}
+
+
+class SvSampling(ctypes.Structure):
+    """C struct sv_sampling: temperature (0 = greedy), top_k (0 = off), top_p (1 = off)."""
+    _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int),
+                ("top_p", ctypes.c_float)]
 
 
 class SvError(RuntimeError):
@@ -80,6 +87,9 @@ def _load():
         "sv_pass_plan": (i32, [i32, ctypes.POINTER(SvPassGemm), i32, i32, i32, vp, sz,
                                ctypes.POINTER(SvPass), vp]),
         "sv_pass_run": (i32, [ctypes.POINTER(SvPass), vp]),
+        "sv_verify_sampled_workspace_bytes": (sz, [i32, i32, i32]),
+        "sv_verify_sampled": (i32, [vp, vp, vp, i32, i32, i32, ctypes.POINTER(SvSampling), u64,
+                                    u32, vp, vp, vp, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -345,6 +355,46 @@ def sv_verify_accept(target_logits, draft_logits, draft_tokens, seed, offset=0, 
         ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), ctypes.c_uint32(int(offset) & 0xFFFFFFFF),
         _ptr(out["tokens"]), _ptr(out["n_acc"]), _ptr(out["status"]), _ptr(out.get("p_at")),
         _ptr(out.get("q_at")), _ptr(out.get("lse")), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel()), _stream(stream)))
+    return out
+
+
+def sv_verify_sampled_workspace_bytes(B, k, V):
+    return int(lib.sv_verify_sampled_workspace_bytes(int(B), int(k), int(V)))
+
+
+def sv_verify_sampled(target_logits, draft_logits, draft_tokens, seed, offset=0,
+                      temperature=1.0, top_k=0, top_p=1.0, out=None, diagnostics=False,
+                      workspace=None, stream=None):
+    """Verification under sampling settings (temperature 0 = greedy) for B trials.
+
+    Returns dict(tokens [B, k+1] int32, n_acc [B], status [B]) plus p_at, q_at
+    [B, k] when diagnostics=True.
+    """
+    B, k1, V = target_logits.shape
+    k = k1 - 1
+    dev = target_logits.device
+    _need(target_logits, "target_logits", torch.float32, (B, k + 1, V))
+    _need(draft_logits, "draft_logits", torch.float32, (B, k, V))
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, k))
+    if out is None:
+        out = {
+            "tokens": torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+            "n_acc": torch.empty((B,), dtype=torch.int32, device=dev),
+            "status": torch.empty((B,), dtype=torch.int32, device=dev),
+        }
+        if diagnostics:
+            out["p_at"] = torch.empty((B, k), dtype=torch.float32, device=dev)
+            out["q_at"] = torch.empty((B, k), dtype=torch.float32, device=dev)
+    need = sv_verify_sampled_workspace_bytes(B, k, V)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    cfg = SvSampling(float(temperature), int(top_k), float(top_p))
+    _check("sv_verify_sampled", lib.sv_verify_sampled(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), B, k, V,
+        ctypes.byref(cfg), ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+        ctypes.c_uint32(int(offset) & 0xFFFFFFFF), _ptr(out["tokens"]), _ptr(out["n_acc"]),
+        _ptr(out["status"]), _ptr(out.get("p_at")), _ptr(out.get("q_at")), _ptr(workspace),
         ctypes.c_size_t(workspace.numel()), _stream(stream)))
     return out
 

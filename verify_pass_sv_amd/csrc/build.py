@@ -19,7 +19,8 @@ LIB = os.path.join(PKG, "libspecverify.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "qgemm_w4.hip", "qgemm_w4_packed.hip", "pass.hip", "qgemm_w8.hip", "qgemm_w4_i8.hip",
-           "hadamard_i8.hip", "verify_accept.hip"]
+           "hadamard_i8.hip", "verify_accept.hip",
+           "verify_sampled.hip"]
 
 CXXFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -26,6 +26,7 @@
 //             selection over the block totals and replays the same sums inside
 //             the chosen block, so the chosen bin always exists.
 #include "sv_common.h"
+#include "sv_philox.h"
 
 #include <math.h>
 
@@ -50,32 +51,6 @@ struct Decision {
   double u2;
   double pad;
 };
-
-// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32
-// multiplies with the published multipliers, key bumped by the published
-// Weyl constants between rounds.
-__device__ __forceinline__ void philox4x32_10(unsigned int c[4], unsigned int k0,
-                                              unsigned int k1) {
-#pragma unroll
-  for (int rnd = 0; rnd < 10; ++rnd) {
-    const unsigned int lo0 = 0xD2511F53u * c[0];
-    const unsigned int hi0 = __umulhi(0xD2511F53u, c[0]);
-    const unsigned int lo1 = 0xCD9E8D57u * c[2];
-    const unsigned int hi1 = __umulhi(0xCD9E8D57u, c[2]);
-    const unsigned int n0 = hi1 ^ c[1] ^ k0;
-    const unsigned int n2 = hi0 ^ c[3] ^ k1;
-    c[0] = n0;
-    c[1] = lo1;
-    c[2] = n2;
-    c[3] = lo0;
-    k0 += 0x9E3779B9u;
-    k1 += 0xBB67AE85u;
-  }
-}
-
-__device__ __forceinline__ float u24(unsigned int w) {
-  return static_cast<float>(w >> 8) * (1.0f / 16777216.0f);
-}
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -407,9 +382,9 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
     bool accepted = true;
     if (i <= k) {
       unsigned int ctr[4] = {static_cast<unsigned int>(i), static_cast<unsigned int>(b), offset, 0u};
-      philox4x32_10(ctr, key0, key1);
-      const float u = u24(ctr[0]);
-      u2 = u24(ctr[1]);
+      sv_philox_rounds(ctr, key0, key1);
+      const float u = sv_u24(ctr[0]);
+      u2 = sv_u24(ctr[1]);
       if (has_draft && status == 0) {
         const float tl = tgt[(static_cast<size_t>(b) * (k + 1) + i) * V + tok];
         const float dl = dft[(static_cast<size_t>(b) * k + i) * V + tok];
@@ -624,7 +599,7 @@ __global__ void philox_kernel(const unsigned int* __restrict__ ctr,
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   unsigned int c[4] = {ctr[4 * i], ctr[4 * i + 1], ctr[4 * i + 2], ctr[4 * i + 3]};
-  philox4x32_10(c, key[2 * i], key[2 * i + 1]);
+  sv_philox_rounds(c, key[2 * i], key[2 * i + 1]);
   for (int j = 0; j < 4; ++j) out[4 * i + j] = c[j];
 }
 
