@@ -410,6 +410,26 @@ def main():
             stats[str(sigma)] = {"mean_accepted": round(mean_acc, 3),
                                  "tokens_per_pass": round(mean_acc + 1, 3)}
         extra["accept_stats_k32"] = stats
+        log("sampled verification")
+        # verification under sampling settings (sv_verify_sampled), k = 32
+        sampled = {}
+        for name, cfg in (("greedy", (0.0, 0, 1.0)), ("T0.7_p0.9", (0.7, 0, 0.9)),
+                          ("k50", (1.0, 50, 1.0)), ("T0.8_k100_p0.95", (0.8, 100, 0.95))):
+            row = {}
+            for B in (1, 64):
+                t, d, tk = synth.accept_inputs(B, 32, VOCAB, seed=41 + B, sigma=1.0, device=dev)
+                out = {"tokens": torch.empty((B, 33), dtype=torch.int32, device=dev),
+                       "n_acc": torch.empty((B,), dtype=torch.int32, device=dev),
+                       "status": torch.empty((B,), dtype=torch.int32, device=dev)}
+                ws = torch.empty(max(16, sv.sv_verify_sampled_workspace_bytes(B, 32, VOCAB)),
+                                 dtype=torch.uint8, device=dev)
+                ms, _ = time_graph(torch, lambda: sv.sv_verify_sampled(
+                    t, d, tk, 0, 0, *cfg, out=out, workspace=ws), 20, 3)
+                row["us_B1" if B == 1 else "us_per_trial_B64"] = round(
+                    ms * 1e3 / B, 3 if B > 1 else 2)
+                del t, d, tk
+            sampled[name] = row
+        extra["sampled_verify_k32"] = sampled
 
     cpu = None
     if not (args.quick or args.no_cpu):

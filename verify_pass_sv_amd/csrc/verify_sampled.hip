@@ -8,28 +8,31 @@
 // from left to right" and "Correct and continue", applied to the truncated
 // distributions.
 //
-// Two launches on the caller's stream:
+// Four launches on the caller's stream:
 //  1. rows    one workgroup per (trial, row), target rows 0..k then draft rows
 //             0..k-1.  It checks the row and takes its maximum; for greedy
 //             settings also the argmax (smallest index among equal maxima).
 //             Otherwise it describes the kept set by a key threshold and a
 //             tie cut: token v is kept iff key(l_v) > tau, or key(l_v) == tau
 //             and v <= tie, where key() maps binary32 order to unsigned order.
-//               top-k: radix selection of the top_k-th largest key (4 passes
-//                 of 8-bit digits, integer histograms), then one ordered pass
-//                 for the tie cut;
-//               top-p: an 8-bit-digit search of the boundary key on binary64
-//                 mass sums (4 passes), the number of tied tokens at the
-//                 boundary from its mass, then an ordered pass.
-//             Then the kept mass S (binary64, fixed order) and the kept
-//             probability of the row's draft token.  Masses are exp((l - m)
-//             / T) in binary64 throughout.
+//             One pass bins the row below its maximum (1/32 logit, counts and
+//             binary64 masses); the boundary bin of top-k (count) and of top-p
+//             (mass, on the renormalised top-k row) is resolved exactly from
+//             its tokens, gathered and sorted in LDS (logit down, index up).
+//             A boundary bin larger than the LDS list falls back to radix
+//             passes over the whole row.  Then the kept mass S and the kept
+//             probability of the row's draft token.  Masses are
+//             exp((l - m) / T) in binary64 throughout.
 //  2. decide  one workgroup per trial: the accept scan on the kept
 //             probabilities (binary64) with the Philox uniforms of
-//             sv_verify_accept, then
-//             the replacement/bonus draw over the kept rows: per-thread
-//             contiguous chunks summed in binary64, an exclusive scan, and the
-//             chosen chunk replayed in the same order.
+//             sv_verify_accept; writes the outputs except the drawn token
+//             (greedy: also that one).
+//  3. resid   one workgroup per (8192-entry vocabulary block, trial): block
+//             totals of the residual weights max(0, p'_r - q'_r) (or p'_k for
+//             the bonus), per-thread ranges of 16 entries added in order.
+//  4. select  one workgroup per trial: S, the block whose running sum
+//             exceeds u' S, then the thread range and the entry inside it,
+//             replaying the same sums in the same order.
 #include "sv_common.h"
 #include "sv_philox.h"
 
@@ -37,7 +40,7 @@
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 
 struct SampledRow {                 // per (trial, row), written by launch 1
   float m;                          // row maximum
@@ -64,9 +67,11 @@ __device__ __forceinline__ bool kept_by(unsigned int key, int v, unsigned int ta
 }
 // Unnormalised probability exp((x - m) / T) in binary64: the difference of two
 // binary32 values is exact there, so the masses that place the top-p
-// boundary and the probabilities of the accept test carry binary64 accuracy.
+// boundary and the probabilities of the accept test carry binary64 accuracy
+// (the product with the binary64 reciprocal of T adds one rounding).
 __device__ __forceinline__ double mass(float x, float m, float T) {
-  return exp((static_cast<double>(x) - static_cast<double>(m)) / static_cast<double>(T));
+  return exp((static_cast<double>(x) - static_cast<double>(m)) *
+             (1.0 / static_cast<double>(T)));
 }
 
 // Fixed-order workgroup reductions (every thread gets the result).
@@ -137,71 +142,222 @@ __device__ int ordered_tie(const float* row, int V, unsigned int tau, int want,
   return r;
 }
 
-__global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
-    const float* __restrict__ tgt, const float* __restrict__ dft, const int32_t* __restrict__ toks,
-    int k, int V, float temperature, int top_k, float top_p, SampledRow* __restrict__ rows) {
-  __shared__ double dsh[kThreads];
-  __shared__ double above_sh;
-  __shared__ int ish[kThreads + 1];
-  __shared__ float fsh[kThreads];
-  __shared__ int ash[kThreads];
+// Binned selection: bins of 1/32 logit below the row maximum (the bin index
+// is monotone in the logit), counted and massed in one pass; the boundary
+// bin of a truncation is then resolved exactly from its tokens, gathered and
+// sorted in LDS.
+constexpr int kBins = 2048;
+constexpr float kBinsPerUnit = 32.f;
+constexpr int kCap = 2048;                      // tokens of one bin resolved in LDS
+constexpr int kPer = kBins / kThreads;          // bins (and candidate slots) per thread
+static_assert(kCap / kThreads == kPer, "one range size for bins and candidates");
+
+__device__ __forceinline__ int bin_of(float x, float mx) {
+  const float d = (mx - x) * kBinsPerUnit;      // >= 0; +inf for x = -inf
+  return d < static_cast<float>(kBins - 1) ? static_cast<int>(d) : kBins - 1;
+}
+
+// f(x, v) for every token of the row; each thread visits its tokens in
+// ascending index order, with 32 values in flight when rows allow 16-byte
+// loads.
+template <typename F>
+__device__ __forceinline__ void scan_row(const float* row, int V, F&& f) {
   const int tid = threadIdx.x;
-  const int rho = blockIdx.x;                   // 0..k target rows, k+1..2k draft rows
-  const int b = blockIdx.y;
-  const int R = 2 * k + 1;
-  const bool is_t = rho <= k;
-  const int i = is_t ? rho : rho - k - 1;
-  const float* row = is_t ? tgt + (static_cast<size_t>(b) * (k + 1) + i) * V
-                          : dft + (static_cast<size_t>(b) * k + i) * V;
-  const int tok = i < k ? toks[static_cast<size_t>(b) * k + i] : -1;
-  SampledRow out = {};
-
-  // maximum, argmax (smallest index among equal maxima), validity
-  float mx = -INFINITY;
-  int am = V;
-  int bad = 0;
-  for (int v = tid; v < V; v += kThreads) {
-    const float x = row[v];
-    bad |= (x != x) | (x == INFINITY);
-    if (x > mx) {
-      mx = x;
-      am = v;
-    }
-  }
-  fsh[tid] = mx;
-  ash[tid] = am;
-  ish[tid] = bad;
-  __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) {
-      const float o = fsh[tid + w];
-      const int oa = ash[tid + w];
-      if (o > fsh[tid] || (o == fsh[tid] && oa < ash[tid])) {
-        fsh[tid] = o;
-        ash[tid] = oa;
+  if ((V & 3) == 0) {
+    const float4* r4 = reinterpret_cast<const float4*>(row);
+    const int V4 = V >> 2;
+    int v = tid;
+    for (; v + 7 * kThreads < V4; v += 8 * kThreads) {
+      float4 a[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] = r4[v + u * kThreads];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int base = 4 * (v + u * kThreads);
+        f(a[u].x, base);
+        f(a[u].y, base + 1);
+        f(a[u].z, base + 2);
+        f(a[u].w, base + 3);
       }
-      ish[tid] |= ish[tid + w];
     }
-    __syncthreads();
+    for (; v < V4; v += kThreads) {
+      const float4 a = r4[v];
+      f(a.x, 4 * v);
+      f(a.y, 4 * v + 1);
+      f(a.z, 4 * v + 2);
+      f(a.w, 4 * v + 3);
+    }
+  } else {
+    for (int v = tid; v < V; v += kThreads) f(row[v], v);
   }
-  mx = fsh[0];
-  am = ash[0];
-  bad = ish[0] | (mx == -INFINITY);
-  __syncthreads();
-  out.m = mx;
-  out.argmax = am;
-  out.status = bad ? 2 : 0;
-  out.tau = 0u;                                 // every non-NaN key exceeds 0
-  out.tie = -1;
-  out.temp = temperature;
-  if (bad || temperature == 0.f) {
-    if (tid == 0) rows[static_cast<size_t>(b) * R + rho] = out;
-    return;
-  }
-  const float T = temperature;
-  unsigned int tau = 0u;
-  int tie = -1;
+}
 
+// Exclusive scan of one int per thread (thread order); returns this thread's
+// prefix.
+__device__ int scan_int(int c, int* ish) {
+  const int tid = threadIdx.x;
+  ish[tid] = c;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int t = 0; t < kThreads; ++t) {
+      const int n = ish[t];
+      ish[t] = run;
+      run += n;
+    }
+  }
+  __syncthreads();
+  const int pre = ish[tid];
+  __syncthreads();
+  return pre;
+}
+__device__ double scan_double(double c, double* dsh) {
+  const int tid = threadIdx.x;
+  dsh[tid] = c;
+  __syncthreads();
+  if (tid == 0) {
+    double run = 0.0;
+    for (int t = 0; t < kThreads; ++t) {
+      const double n = dsh[t];
+      dsh[t] = run;
+      run += n;
+    }
+  }
+  __syncthreads();
+  const double pre = dsh[tid];
+  __syncthreads();
+  return pre;
+}
+
+// First bin where the count from the top reaches `want`; `above` = tokens in
+// the bins before it.
+__device__ int bins_cross_count(const int* hcnt, int want, int& above, int* ish) {
+  const int tid = threadIdx.x;
+  const int b0 = tid * kPer;
+  int c = 0;
+  for (int j = 0; j < kPer; ++j) c += hcnt[b0 + j];
+  const int pre = scan_int(c, ish);
+  if (tid == 0) ish[kThreads] = kBins;
+  __syncthreads();
+  if (pre < want && want <= pre + c) {
+    int run = pre;
+    for (int j = 0; j < kPer; ++j) {
+      if (run + hcnt[b0 + j] >= want) {
+        ish[kThreads] = b0 + j;
+        ish[0] = run;
+        break;
+      }
+      run += hcnt[b0 + j];
+    }
+  }
+  __syncthreads();
+  const int bn = ish[kThreads];
+  above = ish[0];
+  __syncthreads();
+  return bn;
+}
+
+// Sum of m[0 .. n) (bins or candidates), in a fixed order.
+__device__ double sum_before(const double* m, int n, double* dsh) {
+  const int tid = threadIdx.x;
+  double c = 0.0;
+  for (int j = 0; j < kPer; ++j) {
+    const int i = tid * kPer + j;
+    if (i < n) c += m[i];
+  }
+  return block_sum(c, dsh);
+}
+
+// First index j < n (with mass > 0) where the running sum of m[0..j] reaches
+// `need`; n if none.  `above` = running sum before it (or of all n).  Each
+// thread replays its range after the scan, so the decision uses one
+// association of the sums.
+__device__ int cross_mass(const double* m, int n, double need, double& above, double* dsh,
+                          int* ish) {
+  const int tid = threadIdx.x;
+  const int j0 = tid * kPer;
+  double c = 0.0;
+  for (int j = 0; j < kPer; ++j)
+    if (j0 + j < n) c += m[j0 + j];
+  const double pre = scan_double(c, dsh);
+  if (tid == 0) ish[kThreads] = n;
+  __syncthreads();
+  double run = pre;
+  int found = -1;
+  double before = 0.0;
+  for (int j = 0; j < kPer && j0 + j < n; ++j) {
+    const double mj = m[j0 + j];
+    if (mj > 0.0 && run + mj >= need) {
+      found = j0 + j;
+      before = run;
+      break;
+    }
+    run += mj;
+  }
+  if (found >= 0) atomicMin(&ish[kThreads], found);
+  __syncthreads();
+  const int r = ish[kThreads];
+  if (r < n && found == r) dsh[0] = before;
+  if (r == n && tid == kThreads - 1) dsh[0] = run;   // all of them: the last running sum
+  __syncthreads();
+  above = dsh[0];
+  __syncthreads();
+  return r;
+}
+
+// The tokens of bin bn, sorted by decreasing logit then increasing index (as
+// key << 32 | ~index), with their masses; their number, or -1 past kCap.
+__device__ int gather_bin(const float* row, int V, float mx, float T, int bn,
+                          unsigned long long* cand, double* cmass, int* ish) {
+  const int tid = threadIdx.x;
+  if (tid == 0) ish[kThreads] = 0;
+  __syncthreads();
+  scan_row(row, V, [&](float x, int v) {
+    if (bin_of(x, mx) == bn) {
+      const int slot = atomicAdd(&ish[kThreads], 1);
+      if (slot < kCap)
+        cand[slot] = (static_cast<unsigned long long>(order_key(x)) << 32) |
+                     static_cast<unsigned int>(~v);
+    }
+  });
+  __syncthreads();
+  const int n = ish[kThreads];
+  __syncthreads();
+  if (n > kCap) return -1;
+  int npow = 1;
+  while (npow < n) npow <<= 1;
+  for (int j = n + tid; j < npow; j += kThreads) cand[j] = 0ull;   // sorts last
+  __syncthreads();
+  for (int size = 2; size <= npow; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int j = tid; j < npow; j += kThreads) {
+        const int o = j ^ stride;
+        if (o > j) {
+          const unsigned long long a = cand[j], c = cand[o];
+          const bool desc = (j & size) == 0;
+          if (desc ? a < c : a > c) {
+            cand[j] = c;
+            cand[o] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int j = tid; j < n; j += kThreads)
+    cmass[j] = mass(key_value(static_cast<unsigned int>(cand[j] >> 32)), mx, T);
+  __syncthreads();
+  return n;
+}
+
+// Exact selection by radix passes over the whole row, for a boundary bin that
+// holds more tokens than the LDS candidate list: top-k by 8-bit digits of the
+// key with integer histograms, top-p by 8-bit digits on binary64 masses.
+// Updates (tau, tie).
+__device__ void radix_select(const float* row, int V, float mx, float T, int top_k, float top_p,
+                             unsigned int& tau, int& tie, double* dsh, double& above_sh,
+                             int* ish) {
+  const int tid = threadIdx.x;
   // top-k: the top_k-th largest key, then the tie cut among equal keys
   if (top_k > 0 && top_k < V) {
     unsigned int prefix = 0u, pmask = 0u;
@@ -300,13 +456,146 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
     tau = prefix;
   }
 
-  // kept mass and the kept probability of the row's draft token
-  double s = 0.0;
-  for (int v = tid; v < V; v += kThreads) {
-    const float x = row[v];
-    if (kept_by(order_key(x), v, tau, tie)) s += mass(x, mx, T);
+}
+
+__global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
+    const float* __restrict__ tgt, const float* __restrict__ dft, const int32_t* __restrict__ toks,
+    int k, int V, float temperature, int top_k, float top_p, SampledRow* __restrict__ rows) {
+  __shared__ double dsh[kThreads];
+  __shared__ double above_sh;
+  __shared__ int ish[kThreads + 1];
+  __shared__ int hcnt[kBins];
+  __shared__ double hmass[kBins];
+  __shared__ unsigned long long cand[kCap];
+  __shared__ double cmass[kCap];
+  const int tid = threadIdx.x;
+  const int rho = blockIdx.x;                   // 0..k target rows, k+1..2k draft rows
+  const int b = blockIdx.y;
+  const int R = 2 * k + 1;
+  const bool is_t = rho <= k;
+  const int i = is_t ? rho : rho - k - 1;
+  const float* row = is_t ? tgt + (static_cast<size_t>(b) * (k + 1) + i) * V
+                          : dft + (static_cast<size_t>(b) * k + i) * V;
+  const int tok = i < k ? toks[static_cast<size_t>(b) * k + i] : -1;
+  SampledRow out = {};
+
+  // maximum, argmax (smallest index among equal maxima), validity
+  float mx = -INFINITY;
+  int am = V;
+  int bad = 0;
+  scan_row(row, V, [&](float x, int v) {
+    bad |= (x != x) | (x == INFINITY);
+    if (x > mx || (x == mx && v < am)) {
+      mx = x;
+      am = v;
+    }
+  });
+  // (the maxima go through dsh, the indices through hcnt, both free here)
+  dsh[tid] = mx;
+  hcnt[tid] = am;
+  ish[tid] = bad;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) {
+      const double o = dsh[tid + w];
+      const int oa = hcnt[tid + w];
+      if (o > dsh[tid] || (o == dsh[tid] && oa < hcnt[tid])) {
+        dsh[tid] = o;
+        hcnt[tid] = oa;
+      }
+      ish[tid] |= ish[tid + w];
+    }
+    __syncthreads();
   }
-  s = block_sum(s, dsh);
+  mx = static_cast<float>(dsh[0]);
+  am = hcnt[0];
+  bad = ish[0] | (mx == -INFINITY);
+  __syncthreads();
+  out.m = mx;
+  out.argmax = am;
+  out.status = bad ? 2 : 0;
+  out.tau = 0u;                                 // every non-NaN key exceeds 0
+  out.tie = -1;
+  out.temp = temperature;
+  if (bad || temperature == 0.f) {
+    if (tid == 0) rows[static_cast<size_t>(b) * R + rho] = out;
+    return;
+  }
+  const float T = temperature;
+  unsigned int tau = 0u;
+  int tie = -1;
+
+  const bool trunc_k = top_k > 0 && top_k < V;
+  const bool trunc_p = top_p < 1.f;
+  double s = 0.0;                               // kept mass
+  if (!trunc_k && !trunc_p) {
+    scan_row(row, V, [&](float x, int) { s += mass(x, mx, T); });
+    s = block_sum(s, dsh);
+  } else {
+    // Bins of 1/32 logit below the maximum (monotone in the logit): counts
+    // and binary64 masses.  The boundary bin of each truncation is then
+    // resolved exactly from its tokens, sorted in LDS.
+    for (int j = tid; j < kBins; j += kThreads) {
+      hcnt[j] = 0;
+      hmass[j] = 0.0;
+    }
+    __syncthreads();
+    scan_row(row, V, [&](float x, int) {
+      const int bn = bin_of(x, mx);
+      atomicAdd(&hcnt[bn], 1);
+      atomicAdd(&hmass[bn], mass(x, mx, T));
+    });
+    __syncthreads();
+    bool exact = true;
+    int bk = kBins, rk = 0;                     // top-k: boundary bin, kept tokens in it
+    double mass_k = 0.0;                        // kept mass after top-k
+    if (trunc_k) {
+      int above = 0;
+      bk = bins_cross_count(hcnt, top_k, above, ish);
+      rk = top_k - above;
+      exact = bk < kBins && gather_bin(row, V, mx, T, bk, cand, cmass, ish) >= rk;
+      if (exact) {
+        tau = static_cast<unsigned int>(cand[rk - 1] >> 32);
+        tie = static_cast<int>(~static_cast<unsigned int>(cand[rk - 1]));
+        mass_k = sum_before(hmass, bk, dsh) + sum_before(cmass, rk, dsh);
+        s = mass_k;
+      }
+    }
+    if (exact && trunc_p) {
+      const double s1 = trunc_k ? mass_k : sum_before(hmass, kBins, dsh);
+      const double need = static_cast<double>(top_p) * s1;
+      // the boundary among the bins wholly kept by top-k (those before bk)
+      double above = 0.0;
+      const int bp = cross_mass(hmass, bk, need, above, dsh, ish);
+      int n = 0;
+      if (bp < bk) {
+        n = gather_bin(row, V, mx, T, bp, cand, cmass, ish);
+      } else if (trunc_k) {
+        n = rk;                                 // inside the top-k boundary bin, still sorted
+      }
+      exact = n > 0;
+      if (exact) {
+        double before = 0.0;
+        const int j = cross_mass(cmass, n, need - above, before, dsh, ish);
+        const int r = j < n ? j + 1 : n;        // tokens kept from the boundary bin
+        tau = static_cast<unsigned int>(cand[r - 1] >> 32);
+        tie = static_cast<int>(~static_cast<unsigned int>(cand[r - 1]));
+        s = sum_before(hmass, bp < bk ? bp : bk, dsh) + sum_before(cmass, r, dsh);
+      }
+    }
+    if (!exact) {
+      tau = 0u;
+      tie = -1;
+      radix_select(row, V, mx, T, top_k, top_p, tau, tie, dsh, above_sh, ish);
+      s = 0.0;
+      scan_row(row, V, [&](float x, int v) {
+        if (kept_by(order_key(x), v, tau, tie)) s += mass(x, mx, T);
+      });
+      s = block_sum(s, dsh);
+    }
+  }
+
+  // the kept probability of the row's draft token
   if (tid == 0) {
     out.tau = tau;
     out.tie = tie;
@@ -321,22 +610,25 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
   }
 }
 
-// Kept probability of token v of a row described by its record (binary64).
-__device__ __forceinline__ double kept_prob(const float* row, int v, const SampledRow& r) {
-  const float x = row[v];
-  return kept_by(order_key(x), v, r.tau, r.tie) ? mass(x, r.m, r.temp) / r.s : 0.0;
-}
+struct SampledDecision {             // per trial, written by launch 2
+  int status;
+  int n_acc;
+  int plain;                        // draw from p_r alone (bonus position)
+  int pad;
+  double u2;                        // the uniform of the replacement / bonus draw
+};
+
+constexpr int kResPer = 16;                     // residual weights per thread per block
+constexpr int kResBlk = kThreads * kResPer;     // 8192 vocabulary entries per block
+__host__ __device__ inline int res_blocks(int V) { return (V + kResBlk - 1) / kResBlk; }
 
 __global__ __launch_bounds__(kThreads) void sampled_decide_kernel(
-    const float* __restrict__ tgt, const float* __restrict__ dft, const int32_t* __restrict__ toks,
-    int k, int V, bool greedy, const SampledRow* __restrict__ rows, unsigned int key0,
-    unsigned int key1, unsigned int offset, int32_t* __restrict__ out_tokens,
+    const int32_t* __restrict__ toks, int k, int V, bool greedy,
+    const SampledRow* __restrict__ rows, unsigned int key0, unsigned int key1,
+    unsigned int offset, SampledDecision* __restrict__ decs, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ out_n_acc, int32_t* __restrict__ out_status, float* __restrict__ p_at,
     float* __restrict__ q_at) {
-  __shared__ double wsh[kThreads];
-  __shared__ double dsc[2];                     // threshold, running sum before the owner
-  __shared__ int ish[4];
-  __shared__ float u2sh;
+  __shared__ int ish[2];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int R = 2 * k + 1;
@@ -379,116 +671,218 @@ __global__ __launch_bounds__(kThreads) void sampled_decide_kernel(
       if (p_at) p_at[static_cast<size_t>(b) * k + i] = static_cast<float>(p);
       if (q_at) q_at[static_cast<size_t>(b) * k + i] = static_cast<float>(q);
     }
+    SampledDecision dec;
+    dec.status = status;
+    dec.n_acc = status == 0 ? n_acc : -1;
+    dec.plain = n_acc == k;
+    dec.pad = 0;
+    dec.u2 = static_cast<double>(u2r);
+    decs[b] = dec;
     ish[0] = status;
     ish[1] = n_acc;
-    ish[3] = -1;
-    u2sh = u2r;
   }
   __syncthreads();
   const int status = ish[0];
   const int n_acc = ish[1];
   int32_t* ot = out_tokens + static_cast<size_t>(b) * (k + 1);
-  if (status != 0) {
-    for (int i = tid; i <= k; i += kThreads) ot[i] = -1;
-    if (tid == 0) {
-      out_n_acc[b] = -1;
-      out_status[b] = status;
-    }
-    return;
+  for (int i = tid; i <= k; i += kThreads) ot[i] = status == 0 && i < n_acc ? tk[i] : -1;
+  if (tid == 0) {
+    out_n_acc[b] = status == 0 ? n_acc : -1;
+    out_status[b] = status;
+    if (status == 0 && greedy) ot[n_acc] = rr[n_acc].argmax;   // else written by launch 4
   }
-  for (int i = tid; i <= k; i += kThreads) ot[i] = i < n_acc ? tk[i] : -1;
-  if (greedy) {
-    if (tid == 0) {
-      ot[n_acc] = rr[n_acc].argmax;
-      out_n_acc[b] = n_acc;
-      out_status[b] = 0;
-    }
-    return;
-  }
+}
 
-  // replacement (r < k: max(0, p_r - q_r)) or bonus (r = k: p_k) draw
-  const int r = n_acc;
-  const float* trow = tgt + (static_cast<size_t>(b) * (k + 1) + r) * V;
-  const float* drow = r < k ? dft + (static_cast<size_t>(b) * k + r) * V : trow;
-  const SampledRow rt = rr[r];
-  const SampledRow rd = r < k ? rr[k + 1 + r] : rt;
-  const int chunk = (V + kThreads - 1) / kThreads;
-  const int v0 = tid * chunk, v1 = min(V, v0 + chunk);
-  auto weight = [&](int v, bool plain) {
-    const double pv = kept_prob(trow, v, rt);
-    return plain ? pv : fmax(0.0, pv - kept_prob(drow, v, rd));
-  };
-  bool plain = r == k;
-  for (int pass = 0; pass < 2; ++pass) {
-    double local = 0.0;
-    for (int v = v0; v < v1; ++v) local += weight(v, plain);
-    wsh[tid] = local;
-    __syncthreads();
-    if (tid == 0) {
-      // S, the threshold u' S, and the chunk whose running sum crosses it
-      double run = 0.0;
-      for (int t = 0; t < kThreads; ++t) run += wsh[t];
-      const double S = run;
-      const double thr = static_cast<double>(u2sh) * S;
-      int owner = -1, lastnz = -1;
-      double pre = 0.0, lastnz_pre = 0.0;
-      run = 0.0;
-      for (int t = 0; t < kThreads; ++t) {
-        const double w = wsh[t];
-        if (w > 0.0) {
-          lastnz = t;
-          lastnz_pre = run;
-        }
-        if (owner < 0 && run + w > thr) {
-          owner = t;
-          pre = run;
-        }
-        run += w;
-      }
-      if (owner < 0) {                          // rounding left the threshold past the end
-        owner = lastnz;
-        pre = lastnz_pre;
-      }
-      ish[2] = S > 0.0 ? owner : -2;
-      dsc[0] = thr;
-      dsc[1] = pre;
-    }
-    __syncthreads();
-    if (ish[2] != -2) break;
-    plain = true;                               // S = 0 only through rounding: w = p_r
-    __syncthreads();
+// The residual weights of trial b (plain: p_r alone) over one thread's 16
+// entries of vocabulary block blk, summed in ascending order.
+struct ResidualRows {
+  const float* trow;
+  const float* drow;
+  float tm, dm, temp;
+  unsigned int ttau, dtau;
+  int ttie, dtie;
+  double ts, ds;
+};
+__device__ __forceinline__ double res_weight(const ResidualRows& q, int v, bool plain) {
+  const float x = q.trow[v];
+  const double pv =
+      kept_by(order_key(x), v, q.ttau, q.ttie) ? mass(x, q.tm, q.temp) / q.ts : 0.0;
+  if (plain) return pv;
+  const float y = q.drow[v];
+  const double qv =
+      kept_by(order_key(y), v, q.dtau, q.dtie) ? mass(y, q.dm, q.temp) / q.ds : 0.0;
+  return fmax(0.0, pv - qv);
+}
+__device__ __forceinline__ ResidualRows residual_rows(const float* tgt, const float* dft,
+                                                      const SampledRow* rows, int b, int k,
+                                                      int V, int r) {
+  ResidualRows q;
+  const SampledRow* rr = rows + static_cast<size_t>(b) * (2 * k + 1);
+  const SampledRow* rt = rr + r;
+  const SampledRow* rd = r < k ? rr + k + 1 + r : rt;
+  q.trow = tgt + (static_cast<size_t>(b) * (k + 1) + r) * V;
+  q.drow = r < k ? dft + (static_cast<size_t>(b) * k + r) * V : q.trow;
+  q.tm = rt->m;
+  q.dm = rd->m;
+  q.temp = rt->temp;
+  q.ttau = rt->tau;
+  q.dtau = rd->tau;
+  q.ttie = rt->tie;
+  q.dtie = rd->tie;
+  q.ts = rt->s;
+  q.ds = rd->s;
+  return q;
+}
+__device__ __forceinline__ double thread_res_sum(const ResidualRows& q, int V, int blk, bool plain) {
+  const int v0 = blk * kResBlk + threadIdx.x * kResPer;
+  double s = 0.0;
+  for (int j = 0; j < kResPer; ++j)
+    if (v0 + j < V) s += res_weight(q, v0 + j, plain);
+  return s;
+}
+
+// Launch 3: block totals of the residual weights (and of p_r alone, for the
+// S = 0 fallback), per-thread sums added in thread order.
+__global__ __launch_bounds__(kThreads) void sampled_resid_kernel(
+    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V, bool greedy,
+    const SampledRow* __restrict__ rows, const SampledDecision* __restrict__ decs,
+    double* __restrict__ totals) {
+  __shared__ double wsh[2][kThreads];
+  const int tid = threadIdx.x;
+  const int blk = blockIdx.x;
+  const int b = blockIdx.y;
+  const int G = gridDim.x;
+  const SampledDecision dec = decs[b];
+  if (greedy || dec.status != 0) return;
+  const ResidualRows q = residual_rows(tgt, dft, rows, b, k, V, dec.n_acc);
+  wsh[0][tid] = thread_res_sum(q, V, blk, dec.plain != 0);
+  wsh[1][tid] = dec.plain ? 0.0 : thread_res_sum(q, V, blk, true);
+  __syncthreads();
+  if (tid < 2) {
+    double run = 0.0;
+    for (int t = 0; t < kThreads; ++t) run += wsh[tid][t];
+    totals[(static_cast<size_t>(b) * 2 + tid) * G + blk] = run;
   }
+}
+
+// Launch 4: S = sum of the block totals; the block whose running sum first
+// exceeds u' S; inside it, the thread whose running sum does; that thread
+// replays its entries with the same association.
+__global__ __launch_bounds__(kThreads) void sampled_select_kernel(
+    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V, bool greedy,
+    const SampledRow* __restrict__ rows, const SampledDecision* __restrict__ decs,
+    const double* __restrict__ totals, int G, int32_t* __restrict__ out_tokens) {
+  __shared__ double wsh[kThreads];
+  __shared__ double run_sh, thr_sh;
+  __shared__ int ish[3];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const SampledDecision dec = decs[b];
+  if (greedy || dec.status != 0) return;
+  if (tid == 0) {
+    const double* tot = totals + static_cast<size_t>(b) * 2 * G;
+    int which = 0;
+    double S = 0.0;
+    for (int g = 0; g < G; ++g) S += tot[g];
+    if (!(S > 0.0)) {                           // only through rounding: w = p_r
+      which = 1;
+      S = 0.0;
+      for (int g = 0; g < G; ++g) S += tot[G + g];
+    }
+    const double thr = dec.u2 * S;
+    double run = 0.0;
+    int blk = -1, lastnz = -1;
+    double lastnz_run = 0.0;
+    for (int g = 0; g < G; ++g) {
+      const double w = tot[which * G + g];
+      if (w > 0.0) {
+        lastnz = g;
+        lastnz_run = run;
+      }
+      if (run + w > thr) {
+        blk = g;
+        break;
+      }
+      run += w;
+    }
+    if (blk < 0) {                              // rounding left the threshold past the end
+      blk = lastnz;
+      run = lastnz_run;
+    }
+    ish[0] = blk;
+    ish[1] = which;
+    run_sh = run;
+    thr_sh = thr;
+  }
+  __syncthreads();
+  const int blk = ish[0];
+  const bool plain = dec.plain != 0 || ish[1] == 1;
+  const ResidualRows q = residual_rows(tgt, dft, rows, b, k, V, dec.n_acc);
+  const double mine = thread_res_sum(q, V, blk, plain);
+  wsh[tid] = mine;
+  __syncthreads();
+  if (tid == 0) {
+    double run = run_sh;
+    int owner = -1, lastnz = -1;
+    double pre = 0.0, lastnz_pre = 0.0;
+    for (int t = 0; t < kThreads; ++t) {
+      const double w = wsh[t];
+      if (w > 0.0) {
+        lastnz = t;
+        lastnz_pre = run;
+      }
+      if (owner < 0 && run + w > thr_sh) {
+        owner = t;
+        pre = run;
+      }
+      run += w;
+    }
+    if (owner < 0) {
+      owner = lastnz;
+      pre = lastnz_pre;
+    }
+    ish[2] = owner;
+    run_sh = pre;
+  }
+  __syncthreads();
   if (tid == ish[2]) {
-    // replay the owner's chunk with the same association as its sum
-    const double thr = dsc[0], pre = dsc[1];
+    const int v0 = blk * kResBlk + tid * kResPer;
+    const double thr = thr_sh, pre = run_sh;
     double local = 0.0;
     int pick = -1, last = -1;
-    for (int v = v0; v < v1; ++v) {
-      const double w = weight(v, plain);
-      if (w > 0.0) last = v;
+    for (int j = 0; j < kResPer && v0 + j < V; ++j) {
+      const double w = res_weight(q, v0 + j, plain);
+      if (w > 0.0) last = v0 + j;
       local += w;
       if (pre + local > thr) {
-        pick = v;
+        pick = v0 + j;
         break;
       }
     }
-    ish[3] = pick >= 0 ? pick : last;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    ot[n_acc] = ish[3];
-    out_n_acc[b] = n_acc;
-    out_status[b] = 0;
+    out_tokens[static_cast<size_t>(b) * (k + 1) + dec.n_acc] = pick >= 0 ? pick : last;
   }
 }
 
 }  // namespace
 
+namespace {
+struct SampledWs {
+  size_t rows_off, dec_off, tot_off, bytes;
+};
+SampledWs sampled_ws(int B, int k, int V) {
+  SampledWs w;
+  w.rows_off = 0;
+  w.dec_off = (static_cast<size_t>(B) * (2 * k + 1) * sizeof(SampledRow) + 255) / 256 * 256;
+  w.tot_off = (w.dec_off + static_cast<size_t>(B) * sizeof(SampledDecision) + 255) / 256 * 256;
+  w.bytes = w.tot_off + static_cast<size_t>(B) * 2 * res_blocks(V) * sizeof(double);
+  return w;
+}
+}  // namespace
+
 extern "C" size_t sv_verify_sampled_workspace_bytes(int B, int k, int V) {
   if (B < 1 || k < 1 || k > SV_MAX_ROWS || V < 1) return 0;
-  return static_cast<size_t>(B) * (2 * k + 1) * sizeof(SampledRow);
+  return sampled_ws(B, k, V).bytes;
 }
-
 extern "C" sv_status sv_verify_sampled(const float* target_logits, const float* draft_logits,
                                        const int32_t* draft_tokens, int B, int k, int V,
                                        const sv_sampling* sampling, uint64_t seed,
@@ -513,18 +907,30 @@ extern "C" sv_status sv_verify_sampled(const float* target_logits, const float* 
   const size_t need = sv_verify_sampled_workspace_bytes(B, k, V);
   if (!workspace || workspace_bytes < need) return SV_ERR_WORKSPACE;
   if (!sv_aligned16(workspace)) return SV_ERR_ALIGN;
-  SampledRow* rows = static_cast<SampledRow*>(workspace);
+  const SampledWs L = sampled_ws(B, k, V);
+  char* ws = static_cast<char*>(workspace);
+  SampledRow* rows = reinterpret_cast<SampledRow*>(ws + L.rows_off);
+  SampledDecision* decs = reinterpret_cast<SampledDecision*>(ws + L.dec_off);
+  double* totals = reinterpret_cast<double*>(ws + L.tot_off);
+  const int G = res_blocks(V);
   const bool greedy = T == 0.f;
   // greedy settings need only the target rows' maxima
   hipLaunchKernelGGL(sampled_rows_kernel, dim3(greedy ? k + 1 : 2 * k + 1, B), dim3(kThreads), 0,
                      stream, target_logits, draft_logits, draft_tokens, k, V, T, sampling->top_k,
                      sampling->top_p, rows);
   SV_LAUNCH_CHECK();
-  hipLaunchKernelGGL(sampled_decide_kernel, dim3(B), dim3(kThreads), 0, stream, target_logits,
-                     draft_logits, draft_tokens, k, V, greedy, rows,
-                     static_cast<unsigned int>(seed & 0xFFFFFFFFu),
-                     static_cast<unsigned int>(seed >> 32), offset, out_tokens, out_n_acc,
+  hipLaunchKernelGGL(sampled_decide_kernel, dim3(B), dim3(kThreads), 0, stream, draft_tokens, k,
+                     V, greedy, rows, static_cast<unsigned int>(seed & 0xFFFFFFFFu),
+                     static_cast<unsigned int>(seed >> 32), offset, decs, out_tokens, out_n_acc,
                      out_status, p_at, q_at);
   SV_LAUNCH_CHECK();
+  if (!greedy) {
+    hipLaunchKernelGGL(sampled_resid_kernel, dim3(G, B), dim3(kThreads), 0, stream,
+                       target_logits, draft_logits, k, V, greedy, rows, decs, totals);
+    SV_LAUNCH_CHECK();
+    hipLaunchKernelGGL(sampled_select_kernel, dim3(B), dim3(kThreads), 0, stream, target_logits,
+                       draft_logits, k, V, greedy, rows, decs, totals, G, out_tokens);
+    SV_LAUNCH_CHECK();
+  }
   return SV_OK;
 }
