@@ -179,3 +179,25 @@ def test_argument_errors():
         sv.sv_verify_sampled(tgt, dft, tok, 0, top_p=0.0)
     with pytest.raises(sv.SvError):
         sv.sv_verify_sampled(tgt, dft, tok, 0, top_k=-2)
+
+
+@pytest.mark.parametrize("n_tied,settings", [
+    (1500, (1.0, 2600, 1.0)),       # boundary bin of 1500+ tokens: sorted in LDS
+    (5000, (1.0, 2600, 1.0)),       # more than the LDS list: radix fallback
+    (5000, (0.9, 0, 0.3)),          # top-p boundary inside a 5000-token tie
+    (5000, (1.0, 4000, 0.5)),       # both, the top-p boundary in the top-k bin
+], ids=["sorted_1500", "radix_topk_5000", "radix_topp_5000", "radix_both_5000"])
+def test_large_tied_boundary_bins(n_tied, settings):
+    # many tokens share one logit near the top of each row, so the boundary
+    # bin holds n_tied tokens at least
+    B, k, V = 4, 3, 20000
+    tgt, dft, _ = synth.accept_inputs(B, k, V, seed=23, sigma=0.5)
+    g = torch.Generator().manual_seed(7)
+    for t in (tgt, dft):
+        for b in range(B):
+            for i in range(t.shape[1]):
+                idx = torch.randperm(V, generator=g)[:n_tied]
+                t[b, i, idx] = 3.0
+    tok = torch.from_numpy(oracle.sample_drafts(dft.numpy(), 5, *settings))
+    out, res = _run(tgt, dft, tok, seed=8, settings=settings)
+    assert _compare(out, res) <= 1
