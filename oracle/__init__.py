@@ -34,6 +34,8 @@ from .accept import (row_lse, accept_trial, verify_accept, AcceptResult,
                      NEAR_TIE_ACCEPT, accept_on_probs)
 from .sampling import (truncated_probs, greedy_choice, accept_trial_sampled,
                        verify_accept_sampled, sample_drafts, NEAR_TIE_TOP_P)
+from .coupled import (gumbel_noise, coupled_choice, coupled_trial, verify_coupled,
+                      coupled_drafts, NEAR_TIE_COUPLED)
 from .roofline import (tokens_per_s_bound, w4_bytes_per_weight,
                        decoder_stack_shapes, stack_weight_count,
                        stack_weight_bytes_w4, stack_weight_bytes_w8)
@@ -45,7 +47,9 @@ __all__ = [
     "quantize_per_token", "hadamard_i8", "row_lse", "accept_trial",
     "verify_accept", "AcceptResult", "NEAR_TIE_ACCEPT", "accept_on_probs",
     "truncated_probs", "greedy_choice", "accept_trial_sampled",
-    "verify_accept_sampled", "sample_drafts", "NEAR_TIE_TOP_P", "tokens_per_s_bound",
+    "verify_accept_sampled", "sample_drafts", "NEAR_TIE_TOP_P", "gumbel_noise",
+    "coupled_choice", "coupled_trial", "verify_coupled", "coupled_drafts",
+    "NEAR_TIE_COUPLED", "tokens_per_s_bound",
     "w4_bytes_per_weight", "decoder_stack_shapes", "stack_weight_count",
     "stack_weight_bytes_w4", "stack_weight_bytes_w8",
 ]
