@@ -386,6 +386,43 @@ sv_status sv_verify_sampled(const float* target_logits, const float* draft_logit
                             hipStream_t stream);
 
 /*
+ * sv_verify_coupled -- Gumbel-max coupled verification: the drafter and the
+ * target draw with the same noise, so matching distributions give matching
+ * tokens (@trymirai timeline, the post on speculators rejected although they
+ * predict the distribution correctly; Speculative Decoding Clearly
+ * Explained, "Accept from left to right" and "Correct and continue").
+ *
+ * Defines, per independent trial b and position i = 0..k:
+ *   u_i[v] = Philox4x32-10 word 0 with key = (seed & 0xffffffff, seed >> 32)
+ *            and counter (v, i, b, 3 + 256 * offset), as (word >> 8) * 2^-24
+ *   g_i[v] = -log(-log u_i[v])  (binary64; u = 0 gives -inf)
+ *   c_i    = argmax_v (target[b, i, v] + g_i[v]), the smallest index among
+ *            equal scores (a draw from softmax(target[b, i, :]))
+ *   Accept d_i iff d_i == c_i; stop at the first disagreement r and emit c_r;
+ *   after k agreements emit c_k.  The drafter is expected to have drawn d_i
+ *   as the argmax of its own logits plus the same g_i.
+ *
+ *   target_logits  f32 [B, k+1, V]
+ *   draft_tokens   int32 [B, k]
+ *   B 1..65535, 1 <= k <= SV_MAX_ROWS, V >= 1, (k+1)*V < 2^31,
+ *   offset < 2^24
+ *   out_tokens     int32 [B, k+1]: d_0..d_{n_acc-1}, then c_{n_acc}, then -1
+ *   out_n_acc      int32 [B]  (-1 when out_status[b] != 0)
+ *   out_status     int32 [B]  0 ok; 1 a draft token outside [0, V);
+ *                             2 a target row holds NaN or +inf or no finite
+ *                             logit
+ *   choices        int32 [B, k+1] optional (NULL to skip): c_0..c_k
+ *   workspace      device scratch of at least
+ *                  sv_verify_coupled_workspace_bytes(B, k, V) bytes; contents
+ *                  need no initialization and are clobbered.
+ */
+size_t sv_verify_coupled_workspace_bytes(int B, int k, int V);
+sv_status sv_verify_coupled(const float* target_logits, const int32_t* draft_tokens, int B,
+                            int k, int V, uint64_t seed, uint32_t offset, int32_t* out_tokens,
+                            int32_t* out_n_acc, int32_t* out_status, int32_t* choices,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * sv_philox4x32_10 -- the device Philox4x32-10 bijection used by
  * sv_verify_accept, exposed so callers can check it against the published
  * known-answer vectors.  ctr uint32 [n, 4], key uint32 [n, 2], out uint32

@@ -174,3 +174,19 @@ def test_sampled_verification_validation_before_launch():
     assert call(S(1.0, 0, 1.0), k=0) == 2
     assert call(S(0.7, 40, 0.9), ws_bytes=ws - 1) == 5
     assert call(S(0.7, 40, 0.9), workspace=None) == 5
+
+
+def test_coupled_verification_validation_before_launch():
+    import verify_pass_sv_amd as sv
+    L = sv.lib
+    fake = ctypes.c_void_p(0x100000)     # aligned, never dereferenced
+    ws = sv.sv_verify_coupled_workspace_bytes(4, 8, 1000)
+    assert ws > 0 and sv.sv_verify_coupled_workspace_bytes(4, 33, 1000) == 0
+
+    def call(k=8, offset=0, ws_bytes=ws, workspace=fake, tokens=fake):
+        return L.sv_verify_coupled(fake, tokens, 4, k, 1000, 0, offset, fake, fake, fake, None,
+                                   workspace, ws_bytes, None)
+    assert call(tokens=None) == 1
+    assert call(k=0) == 2 and call(k=33) == 2
+    assert call(offset=1 << 24) == 2
+    assert call(ws_bytes=ws - 1) == 5 and call(workspace=None) == 5

@@ -22,6 +22,7 @@ EXPORTED_SYMBOLS = (
     "sv_w4_packed_codes_bytes", "sv_w4_packed_sz_bytes", "sv_w4_pack", "sv_qgemm_w4_packed",
     "sv_w8_pack", "sv_pass_plan_bytes", "sv_pass_plan", "sv_pass_run",
     "sv_verify_sampled_workspace_bytes", "sv_verify_sampled",
+    "sv_verify_coupled_workspace_bytes", "sv_verify_coupled",
 )
 
 _STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_INVALID_ARG", 3: "SV_ERR_ALIGN",
@@ -90,6 +91,9 @@ def _load():
         "sv_verify_sampled_workspace_bytes": (sz, [i32, i32, i32]),
         "sv_verify_sampled": (i32, [vp, vp, vp, i32, i32, i32, ctypes.POINTER(SvSampling), u64,
                                     u32, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "sv_verify_coupled_workspace_bytes": (sz, [i32, i32, i32]),
+        "sv_verify_coupled": (i32, [vp, vp, i32, i32, i32, u64, u32, vp, vp, vp, vp, vp, sz,
+                                    vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -396,6 +400,41 @@ def sv_verify_sampled(target_logits, draft_logits, draft_tokens, seed, offset=0,
         ctypes.c_uint32(int(offset) & 0xFFFFFFFF), _ptr(out["tokens"]), _ptr(out["n_acc"]),
         _ptr(out["status"]), _ptr(out.get("p_at")), _ptr(out.get("q_at")), _ptr(workspace),
         ctypes.c_size_t(workspace.numel()), _stream(stream)))
+    return out
+
+
+def sv_verify_coupled_workspace_bytes(B, k, V):
+    return int(lib.sv_verify_coupled_workspace_bytes(int(B), int(k), int(V)))
+
+
+def sv_verify_coupled(target_logits, draft_tokens, seed, offset=0, out=None, choices=False,
+                      workspace=None, stream=None):
+    """Gumbel-max coupled verification for B trials.
+
+    Returns dict(tokens [B, k+1] int32, n_acc [B], status [B]) plus the
+    target's choices [B, k+1] when choices=True.
+    """
+    B, k1, V = target_logits.shape
+    k = k1 - 1
+    dev = target_logits.device
+    _need(target_logits, "target_logits", torch.float32, (B, k + 1, V))
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, k))
+    if out is None:
+        out = {
+            "tokens": torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+            "n_acc": torch.empty((B,), dtype=torch.int32, device=dev),
+            "status": torch.empty((B,), dtype=torch.int32, device=dev),
+        }
+        if choices:
+            out["choices"] = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    need = sv_verify_coupled_workspace_bytes(B, k, V)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _check("sv_verify_coupled", lib.sv_verify_coupled(
+        _ptr(target_logits), _ptr(draft_tokens), B, k, V,
+        ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), ctypes.c_uint32(int(offset) & 0xFFFFFFFF),
+        _ptr(out["tokens"]), _ptr(out["n_acc"]), _ptr(out["status"]), _ptr(out.get("choices")),
+        _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream)))
     return out
 
 

@@ -20,7 +20,7 @@ ARCH = "gfx950"
 
 SOURCES = ["api.hip", "qgemm_w4.hip", "qgemm_w4_packed.hip", "pass.hip", "qgemm_w8.hip", "qgemm_w4_i8.hip",
            "hadamard_i8.hip", "verify_accept.hip",
-           "verify_sampled.hip"]
+           "verify_sampled.hip", "verify_coupled.hip"]
 
 CXXFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -1,0 +1,176 @@
+// sv_verify_coupled: Gumbel-max coupled verification.
+//
+// Source: @trymirai timeline, the post on speculators that predict the
+// distribution correctly and are still rejected: sample both the speculator
+// and the LLM with the same seed through the Gumbel-max trick, so matching
+// distributions give matching tokens; Speculative Decoding Clearly Explained,
+// "Accept from left to right" and "Correct and continue" (keep the drafts up
+// to the first disagreement, emit the target's token there, one more after k
+// agreements).
+//
+// Two launches on the caller's stream:
+//  1. choose  one workgroup per (4096-entry vocabulary span, target row,
+//             trial): the best score l + g over the span, with the Gumbel
+//             noise g = -log(-log u) in binary64 from the Philox uniform of
+//             counter (v, i, b, 3 + 256 offset); partial (score, index,
+//             validity).
+//  2. decide  one wave per trial: lane i merges the spans of target row i
+//             (score down, index up), then the status checks, the first
+//             disagreement (one ballot) and the outputs.
+#include "sv_common.h"
+#include "sv_philox.h"
+
+#include <math.h>
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kSpan = 4096;                     // vocabulary entries per span
+constexpr unsigned int kTagCoupled = 3u;
+
+struct CoupledPartial {
+  double score;                                 // best l + g of the span (-inf if none)
+  int index;                                    // its smallest index
+  int flags;                                    // bit 0: NaN or +inf seen; bit 1: finite logit seen
+};
+static_assert(sizeof(CoupledPartial) == 16, "partial layout");
+
+__host__ __device__ inline int coupled_spans(int V) { return (V + kSpan - 1) / kSpan; }
+
+__device__ __forceinline__ bool better(double s, int v, double bs, int bv) {
+  return s > bs || (s == bs && v < bv);
+}
+
+__global__ __launch_bounds__(kThreads) void coupled_choose_kernel(
+    const float* __restrict__ tgt, int k, int V, unsigned int key0, unsigned int key1,
+    unsigned int tagword, CoupledPartial* __restrict__ parts) {
+  __shared__ double ssh[kThreads];
+  __shared__ int ish[kThreads];
+  __shared__ int fsh[kThreads];
+  const int tid = threadIdx.x;
+  const int span = blockIdx.x;
+  const int i = blockIdx.y;
+  const int b = blockIdx.z;
+  const float* row = tgt + (static_cast<size_t>(b) * (k + 1) + i) * V;
+  const int v0 = span * kSpan;
+  const int v1 = min(V, v0 + kSpan);
+  double best = -INFINITY;
+  int bi = V;
+  int flags = 0;
+  for (int v = v0 + tid; v < v1; v += kThreads) {
+    const float x = row[v];
+    flags |= ((x != x) | (x == INFINITY)) ? 1 : 0;
+    flags |= (x > -INFINITY && x < INFINITY) ? 2 : 0;
+    unsigned int c[4] = {static_cast<unsigned int>(v), static_cast<unsigned int>(i),
+                         static_cast<unsigned int>(b), tagword};
+    sv_philox_rounds(c, key0, key1);
+    const double u = static_cast<double>(sv_u24(c[0]));   // 24 bits: exact
+    const double g = -log(-log(u));                        // u = 0: -inf
+    const double sc = static_cast<double>(x) + g;
+    if (better(sc, v, best, bi)) {
+      best = sc;
+      bi = v;
+    }
+  }
+  ssh[tid] = best;
+  ish[tid] = bi;
+  fsh[tid] = flags;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) {
+      if (better(ssh[tid + w], ish[tid + w], ssh[tid], ish[tid])) {
+        ssh[tid] = ssh[tid + w];
+        ish[tid] = ish[tid + w];
+      }
+      fsh[tid] |= fsh[tid + w];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    CoupledPartial p;
+    p.score = ssh[0];
+    p.index = ish[0];
+    p.flags = fsh[0];
+    parts[(static_cast<size_t>(b) * (k + 1) + i) * gridDim.x + span] = p;
+  }
+}
+
+__global__ __launch_bounds__(64) void coupled_decide_kernel(
+    const int32_t* __restrict__ toks, int k, int V, int spans,
+    const CoupledPartial* __restrict__ parts, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ out_n_acc, int32_t* __restrict__ out_status,
+    int32_t* __restrict__ choices) {
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x;
+  const bool is_row = lane <= k;
+  double best = -INFINITY;
+  int bi = V;
+  int flags = 0;
+  if (is_row) {
+    const CoupledPartial* p = parts + (static_cast<size_t>(b) * (k + 1) + lane) * spans;
+    for (int s = 0; s < spans; ++s) {
+      const CoupledPartial q = p[s];
+      if (better(q.score, q.index, best, bi)) {
+        best = q.score;
+        bi = q.index;
+      }
+      flags |= q.flags;
+    }
+  }
+  const bool row_bad = is_row && ((flags & 1) || !(flags & 2));
+  int tok = 0;
+  bool tok_bad = false;
+  if (lane < k) {
+    tok = toks[static_cast<size_t>(b) * k + lane];
+    tok_bad = tok < 0 || tok >= V;
+  }
+  const int status = __any(tok_bad) ? 1 : (__any(row_bad) ? 2 : 0);
+  const unsigned long long mism = __ballot(lane < k && tok != bi);
+  const int n_acc = mism ? (__ffsll(static_cast<long long>(mism)) - 1) : k;
+  const int pick = __shfl(bi, n_acc);
+  int32_t* ot = out_tokens + static_cast<size_t>(b) * (k + 1);
+  if (is_row) {
+    ot[lane] = status != 0 ? -1 : (lane < n_acc ? tok : (lane == n_acc ? pick : -1));
+    if (choices) choices[static_cast<size_t>(b) * (k + 1) + lane] = status != 0 ? -1 : bi;
+  }
+  if (lane == 0) {
+    out_n_acc[b] = status == 0 ? n_acc : -1;
+    out_status[b] = status;
+  }
+}
+
+}  // namespace
+
+extern "C" size_t sv_verify_coupled_workspace_bytes(int B, int k, int V) {
+  if (B < 1 || k < 1 || k > SV_MAX_ROWS || V < 1) return 0;
+  return static_cast<size_t>(B) * (k + 1) * coupled_spans(V) * sizeof(CoupledPartial);
+}
+
+extern "C" sv_status sv_verify_coupled(const float* target_logits, const int32_t* draft_tokens,
+                                       int B, int k, int V, uint64_t seed, uint32_t offset,
+                                       int32_t* out_tokens, int32_t* out_n_acc,
+                                       int32_t* out_status, int32_t* choices, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  if (!target_logits || !draft_tokens || !out_tokens || !out_n_acc || !out_status)
+    return SV_ERR_NULL;
+  if (B < 1 || B > 65535 || k < 1 || k > SV_MAX_ROWS || V < 1 || offset >= (1u << 24))
+    return SV_ERR_INVALID_ARG;
+  if (static_cast<long long>(k + 1) * V >= (1LL << 31)) return SV_ERR_INVALID_ARG;
+  if (!sv_aligned16(target_logits) || !sv_aligned16(draft_tokens) || !sv_aligned16(out_tokens) ||
+      !sv_aligned16(out_n_acc) || !sv_aligned16(out_status) ||
+      (choices && !sv_aligned16(choices)))
+    return SV_ERR_ALIGN;
+  if (!workspace || workspace_bytes < sv_verify_coupled_workspace_bytes(B, k, V))
+    return SV_ERR_WORKSPACE;
+  if (!sv_aligned16(workspace)) return SV_ERR_ALIGN;
+  const int spans = coupled_spans(V);
+  CoupledPartial* parts = static_cast<CoupledPartial*>(workspace);
+  hipLaunchKernelGGL(coupled_choose_kernel, dim3(spans, k + 1, B), dim3(kThreads), 0, stream,
+                     target_logits, k, V, static_cast<unsigned int>(seed & 0xFFFFFFFFu),
+                     static_cast<unsigned int>(seed >> 32), kTagCoupled + (offset << 8), parts);
+  SV_LAUNCH_CHECK();
+  hipLaunchKernelGGL(coupled_decide_kernel, dim3(B), dim3(64), 0, stream, draft_tokens, k, V,
+                     spans, parts, out_tokens, out_n_acc, out_status, choices);
+  SV_LAUNCH_CHECK();
+  return SV_OK;
+}
