@@ -430,6 +430,38 @@ def main():
                 del t, d, tk
             sampled[name] = row
         extra["sampled_verify_k32"] = sampled
+        log("coupled verification")
+        # Gumbel-max coupled verification (sv_verify_coupled), k = 32: timing,
+        # and the mean accepted drafts when the drafter draws with the same
+        # noise (its draws: the kernel's choices on the draft rows)
+        coupled = {}
+        for B in (1, 64):
+            t, d, tk = synth.accept_inputs(B, 32, VOCAB, seed=51 + B, sigma=1.0, device=dev)
+            out = {"tokens": torch.empty((B, 33), dtype=torch.int32, device=dev),
+                   "n_acc": torch.empty((B,), dtype=torch.int32, device=dev),
+                   "status": torch.empty((B,), dtype=torch.int32, device=dev)}
+            ws = torch.empty(max(16, sv.sv_verify_coupled_workspace_bytes(B, 32, VOCAB)),
+                             dtype=torch.uint8, device=dev)
+            ms, _ = time_graph(torch, lambda: sv.sv_verify_coupled(t, tk, 0, 0, out=out,
+                                                                   workspace=ws), 20, 3)
+            coupled["us_B1" if B == 1 else "us_per_trial_B64"] = round(ms * 1e3 / B, 3)
+            del t, d, tk
+        stats = {}
+        B = 64
+        for sigma in (0.1, 1.0, 3.0):
+            tot = 0
+            for rep in range(8):
+                t, d, _ = synth.accept_inputs(B, 32, VOCAB, seed=200000 * int(sigma * 10) + rep,
+                                              sigma=sigma, device=dev)
+                dpad = torch.cat([d, d[:, :1]], dim=1).contiguous()
+                zeros = torch.zeros((B, 32), dtype=torch.int32, device=dev)
+                drafts = sv.sv_verify_coupled(dpad, zeros, 0, rep, choices=True)["choices"]
+                res = sv.sv_verify_coupled(t, drafts[:, :32].contiguous(), 0, rep)
+                tot += int(res["n_acc"].sum().item())
+            stats[str(sigma)] = {"mean_accepted": round(tot / (8 * B), 3),
+                                 "tokens_per_pass": round(tot / (8 * B) + 1, 3)}
+        coupled["accept_stats"] = stats
+        extra["coupled_verify_k32"] = coupled
 
     cpu = None
     if not (args.quick or args.no_cpu):
