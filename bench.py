@@ -462,6 +462,27 @@ def main():
                                  "tokens_per_pass": round(tot / (8 * B) + 1, 3)}
         coupled["accept_stats"] = stats
         extra["coupled_verify_k32"] = coupled
+        log("tree verification")
+        # greedy verification of a 16-node and a 32-node draft tree
+        # (sv_verify_tree) over the full vocabulary
+        tree = {}
+        for n in (16, 32):
+            row = {}
+            for B in (1, 64):
+                t, tk, par = synth.tree_inputs(B, n, VOCAB, seed=61 + B + n, device=dev)
+                out = {"tokens": torch.empty((B, n + 1), dtype=torch.int32, device=dev),
+                       "n_acc": torch.empty((B,), dtype=torch.int32, device=dev),
+                       "status": torch.empty((B,), dtype=torch.int32, device=dev)}
+                ws = torch.empty(max(16, sv.sv_verify_tree_workspace_bytes(B, n, VOCAB)),
+                                 dtype=torch.uint8, device=dev)
+                ms, _ = time_graph(torch, lambda: sv.sv_verify_tree(t, tk, par, out=out,
+                                                                    workspace=ws), 20, 3)
+                row["us_B1" if B == 1 else "us_per_trial_B64"] = round(ms * 1e3 / B, 3)
+                if B == 64:
+                    row["mean_path"] = round(float(out["n_acc"].float().mean().item()), 3)
+                del t, tk, par
+            tree["n%d" % n] = row
+        extra["tree_verify"] = tree
 
     cpu = None
     if not (args.quick or args.no_cpu):

@@ -423,6 +423,49 @@ sv_status sv_verify_coupled(const float* target_logits, const int32_t* draft_tok
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * sv_verify_tree -- greedy verification of a draft tree.
+ *
+ * Source: Karpathy's Trick for Faster Local LLMs, "Issue with parallel draft
+ * generation" (the main model verifies the drafted tree and accepts its
+ * longest valid path) and "Verifying a draft tree without restoring model
+ * state" (one target pass scores every branch); Local LLM 4x Faster (the
+ * whole tree verified at once, every output token confirmed by the target).
+ *
+ * Defines, per independent trial b, for a tree of n draft nodes (node j: token
+ * tok[j], parent par[j], -1 for a child of the last accepted token; parents
+ * come before children):
+ *   row 0 of the target is its distribution at the root's children, row j+1
+ *   its distribution after node j;
+ *   c_r    = argmax_v target[b, r, v], the smallest index among equal maxima
+ *   node j is valid iff par[j] is -1 or a valid node, and tok[j] == c_{par[j]+1}
+ *   The accepted path is the longest chain of valid nodes from the root; among
+ *   equally long chains the one ending at the smallest node index.  Emitted:
+ *   the path's tokens, then c at the row after its last node (c_0 if empty).
+ *
+ *   target_logits  f32 [B, n+1, V]
+ *   tokens         int32 [B, n]
+ *   parents        int32 [B, n]
+ *   B 1..65535, 1 <= n <= SV_MAX_ROWS, V >= 1, (n+1)*V < 2^31
+ *   out_tokens     int32 [B, n+1]: the path's tokens, the bonus, then -1
+ *   out_n_acc      int32 [B]  path length (-1 when out_status[b] != 0)
+ *   out_status     int32 [B]  0 ok; 1 a token outside [0, V); 2 a target row
+ *                             holds NaN or +inf or no finite logit; 3 a parent
+ *                             outside [-1, j) (checked in this order)
+ *   out_path       int32 [B, n] optional (NULL to skip): the accepted node
+ *                  indices from the root, then -1
+ *   workspace      device scratch of at least
+ *                  sv_verify_tree_workspace_bytes(B, n, V) bytes; contents need
+ *                  no initialization and are clobbered.
+ * All pointers are device memory, 16-byte aligned; the call is asynchronous
+ * on `stream`.  Errors are returned before any launch.
+ */
+size_t sv_verify_tree_workspace_bytes(int B, int n, int V);
+sv_status sv_verify_tree(const float* target_logits, const int32_t* tokens,
+                         const int32_t* parents, int B, int n, int V, int32_t* out_tokens,
+                         int32_t* out_n_acc, int32_t* out_status, int32_t* out_path,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * sv_philox4x32_10 -- the device Philox4x32-10 bijection used by
  * sv_verify_accept, exposed so callers can check it against the published
  * known-answer vectors.  ctr uint32 [n, 4], key uint32 [n, 2], out uint32

@@ -190,3 +190,19 @@ def test_coupled_verification_validation_before_launch():
     assert call(k=0) == 2 and call(k=33) == 2
     assert call(offset=1 << 24) == 2
     assert call(ws_bytes=ws - 1) == 5 and call(workspace=None) == 5
+
+
+def test_tree_verification_validation_before_launch():
+    import verify_pass_sv_amd as sv
+    L = sv.lib
+    fake = ctypes.c_void_p(0x100000)     # aligned, never dereferenced
+    ws = sv.sv_verify_tree_workspace_bytes(4, 8, 1000)
+    assert ws > 0 and sv.sv_verify_tree_workspace_bytes(4, 33, 1000) == 0
+
+    def call(n=8, B=4, ws_bytes=ws, workspace=fake, parents=fake, path=None):
+        return L.sv_verify_tree(fake, fake, parents, B, n, 1000, fake, fake, fake, path,
+                                workspace, ws_bytes, None)
+    assert call(parents=None) == 1
+    assert call(n=0) == 2 and call(n=33) == 2 and call(B=0) == 2 and call(B=65536) == 2
+    assert call(path=ctypes.c_void_p(0x100004)) == 3
+    assert call(ws_bytes=ws - 1) == 5 and call(workspace=None) == 5

@@ -14,7 +14,8 @@ _BINDING_NAMES = (
     "EXPORTED_SYMBOLS", "SV_MAX_ROWS", "sv_w4_pack", "sv_qgemm_w4_packed",
     "sv_w8_pack", "sv_pass_plan", "sv_pass_run", "Pass", "SvPassGemm", "SvPass",
     "PASS_FORMATS", "sv_verify_sampled", "sv_verify_sampled_workspace_bytes", "SvSampling",
-    "sv_verify_coupled", "sv_verify_coupled_workspace_bytes",
+    "sv_verify_coupled", "sv_verify_coupled_workspace_bytes", "sv_verify_tree",
+    "sv_verify_tree_workspace_bytes",
 )
 
 __all__ = list(_BINDING_NAMES)

@@ -23,6 +23,7 @@ EXPORTED_SYMBOLS = (
     "sv_w8_pack", "sv_pass_plan_bytes", "sv_pass_plan", "sv_pass_run",
     "sv_verify_sampled_workspace_bytes", "sv_verify_sampled",
     "sv_verify_coupled_workspace_bytes", "sv_verify_coupled",
+    "sv_verify_tree_workspace_bytes", "sv_verify_tree",
 )
 
 _STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_INVALID_ARG", 3: "SV_ERR_ALIGN",
@@ -94,6 +95,8 @@ def _load():
         "sv_verify_coupled_workspace_bytes": (sz, [i32, i32, i32]),
         "sv_verify_coupled": (i32, [vp, vp, i32, i32, i32, u64, u32, vp, vp, vp, vp, vp, sz,
                                     vp]),
+        "sv_verify_tree_workspace_bytes": (sz, [i32, i32, i32]),
+        "sv_verify_tree": (i32, [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -435,6 +438,41 @@ def sv_verify_coupled(target_logits, draft_tokens, seed, offset=0, out=None, cho
         ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), ctypes.c_uint32(int(offset) & 0xFFFFFFFF),
         _ptr(out["tokens"]), _ptr(out["n_acc"]), _ptr(out["status"]), _ptr(out.get("choices")),
         _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream)))
+    return out
+
+
+def sv_verify_tree_workspace_bytes(B, n, V):
+    return int(lib.sv_verify_tree_workspace_bytes(int(B), int(n), int(V)))
+
+
+def sv_verify_tree(target_logits, tokens, parents, out=None, path=False, workspace=None,
+                   stream=None):
+    """Greedy verification of B draft trees of n nodes.
+
+    Returns dict(tokens [B, n+1] int32, n_acc [B], status [B]) plus the
+    accepted node indices path [B, n] when path=True.
+    """
+    B, n1, V = target_logits.shape
+    n = n1 - 1
+    dev = target_logits.device
+    _need(target_logits, "target_logits", torch.float32, (B, n + 1, V))
+    _need(tokens, "tokens", torch.int32, (B, n))
+    _need(parents, "parents", torch.int32, (B, n))
+    if out is None:
+        out = {
+            "tokens": torch.empty((B, n + 1), dtype=torch.int32, device=dev),
+            "n_acc": torch.empty((B,), dtype=torch.int32, device=dev),
+            "status": torch.empty((B,), dtype=torch.int32, device=dev),
+        }
+        if path:
+            out["path"] = torch.empty((B, n), dtype=torch.int32, device=dev)
+    need = sv_verify_tree_workspace_bytes(B, n, V)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _check("sv_verify_tree", lib.sv_verify_tree(
+        _ptr(target_logits), _ptr(tokens), _ptr(parents), B, n, V, _ptr(out["tokens"]),
+        _ptr(out["n_acc"]), _ptr(out["status"]), _ptr(out.get("path")), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel()), _stream(stream)))
     return out
 
 

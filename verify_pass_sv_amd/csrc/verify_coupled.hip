@@ -1,4 +1,5 @@
-// sv_verify_coupled: Gumbel-max coupled verification.
+// Verification by target choices: sv_verify_coupled (Gumbel-max coupled
+// verification) and sv_verify_tree (greedy verification of a draft tree).
 //
 // Source: @trymirai timeline, the post on speculators that predict the
 // distribution correctly and are still rejected: sample both the speculator
@@ -8,15 +9,21 @@
 // to the first disagreement, emit the target's token there, one more after k
 // agreements).
 //
+// Tree source: Karpathy's Trick for Faster Local LLMs, "Issue with parallel
+// draft generation" and "Verifying a draft tree without restoring model
+// state" (the main model verifies the tree and accepts the longest valid
+// path); Local LLM 4x Faster (the whole tree verified at once).
+//
 // Two launches on the caller's stream:
 //  1. choose  one workgroup per (4096-entry vocabulary span, target row,
-//             trial): the best score l + g over the span, with the Gumbel
+//             trial): the best score over the span -- l + g with the Gumbel
 //             noise g = -log(-log u) in binary64 from the Philox uniform of
-//             counter (v, i, b, 3 + 256 offset); partial (score, index,
-//             validity).
-//  2. decide  one wave per trial: lane i merges the spans of target row i
-//             (score down, index up), then the status checks, the first
-//             disagreement (one ballot) and the outputs.
+//             counter (v, i, b, 3 + 256 offset) for coupled verification, l
+//             alone for the tree; partial (score, index, validity).
+//  2. decide  one wave per trial: lane r merges the spans of target row r
+//             (score down, index up), then the status checks and
+//             coupled: the first disagreement (one ballot);
+//             tree: the valid nodes, the longest valid chain and its bonus.
 #include "sv_common.h"
 #include "sv_philox.h"
 
@@ -41,7 +48,9 @@ __device__ __forceinline__ bool better(double s, int v, double bs, int bv) {
   return s > bs || (s == bs && v < bv);
 }
 
-__global__ __launch_bounds__(kThreads) void coupled_choose_kernel(
+// Rows of [B, rows, V] logits: rows = k + 1 (coupled) or n + 1 (tree).
+template <bool NOISE>
+__global__ __launch_bounds__(kThreads) void choose_kernel(
     const float* __restrict__ tgt, int k, int V, unsigned int key0, unsigned int key1,
     unsigned int tagword, CoupledPartial* __restrict__ parts) {
   __shared__ double ssh[kThreads];
@@ -61,12 +70,14 @@ __global__ __launch_bounds__(kThreads) void coupled_choose_kernel(
     const float x = row[v];
     flags |= ((x != x) | (x == INFINITY)) ? 1 : 0;
     flags |= (x > -INFINITY && x < INFINITY) ? 2 : 0;
-    unsigned int c[4] = {static_cast<unsigned int>(v), static_cast<unsigned int>(i),
-                         static_cast<unsigned int>(b), tagword};
-    sv_philox_rounds(c, key0, key1);
-    const double u = static_cast<double>(sv_u24(c[0]));   // 24 bits: exact
-    const double g = -log(-log(u));                        // u = 0: -inf
-    const double sc = static_cast<double>(x) + g;
+    double sc = static_cast<double>(x);
+    if constexpr (NOISE) {
+      unsigned int c[4] = {static_cast<unsigned int>(v), static_cast<unsigned int>(i),
+                           static_cast<unsigned int>(b), tagword};
+      sv_philox_rounds(c, key0, key1);
+      const double u = static_cast<double>(sv_u24(c[0]));   // 24 bits: exact
+      sc += -log(-log(u));                                   // u = 0: -inf
+    }
     if (better(sc, v, best, bi)) {
       best = sc;
       bi = v;
@@ -139,6 +150,77 @@ __global__ __launch_bounds__(64) void coupled_decide_kernel(
   }
 }
 
+__global__ __launch_bounds__(64) void tree_decide_kernel(
+    const int32_t* __restrict__ toks, const int32_t* __restrict__ pars, int n, int V, int spans,
+    const CoupledPartial* __restrict__ parts, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ out_n_acc, int32_t* __restrict__ out_status,
+    int32_t* __restrict__ out_path) {
+  __shared__ int choice[SV_MAX_ROWS + 1];
+  __shared__ int tok_sh[SV_MAX_ROWS], par_sh[SV_MAX_ROWS], path[SV_MAX_ROWS];
+  __shared__ int depth[SV_MAX_ROWS];            // valid chain length ending at a node, 0 if invalid
+  __shared__ int res[3];                        // status, path length, bonus row
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x;
+  const bool is_row = lane <= n;
+  double best = -INFINITY;
+  int bi = V;
+  int flags = 0;
+  if (is_row) {
+    const CoupledPartial* p = parts + (static_cast<size_t>(b) * (n + 1) + lane) * spans;
+    for (int s = 0; s < spans; ++s) {
+      const CoupledPartial q = p[s];
+      if (better(q.score, q.index, best, bi)) {
+        best = q.score;
+        bi = q.index;
+      }
+      flags |= q.flags;
+    }
+    choice[lane] = bi;
+  }
+  const bool row_bad = is_row && ((flags & 1) || !(flags & 2));
+  int tok = 0, par = -1;
+  bool tok_bad = false, par_bad = false;
+  if (lane < n) {
+    tok = toks[static_cast<size_t>(b) * n + lane];
+    par = pars[static_cast<size_t>(b) * n + lane];
+    tok_bad = tok < 0 || tok >= V;
+    par_bad = par < -1 || par >= lane;
+    tok_sh[lane] = tok;
+    par_sh[lane] = par;
+  }
+  const int status = __any(tok_bad) ? 1 : (__any(row_bad) ? 2 : (__any(par_bad) ? 3 : 0));
+  __syncthreads();
+  if (lane == 0) {
+    // parents come before children, so one pass in node order settles every depth
+    int end = -1;
+    for (int j = 0; j < n && status == 0; ++j) {
+      const int p = par_sh[j];
+      const bool parent_ok = p < 0 || depth[p] > 0;
+      depth[j] = parent_ok && tok_sh[j] == choice[p + 1] ? 1 + (p >= 0 ? depth[p] : 0) : 0;
+      if (depth[j] > 0 && (end < 0 || depth[j] > depth[end])) end = j;
+    }
+    int len = end >= 0 ? depth[end] : 0;
+    for (int j = end, d = len - 1; j >= 0; j = par_sh[j], --d) path[d] = j;
+    res[0] = status;
+    res[1] = status == 0 ? len : -1;
+    res[2] = end + 1;
+  }
+  __syncthreads();
+  const int len = res[1];
+  int32_t* ot = out_tokens + static_cast<size_t>(b) * (n + 1);
+  if (lane <= n) {
+    int v = -1;
+    if (status == 0) v = lane < len ? tok_sh[path[lane]] : (lane == len ? choice[res[2]] : -1);
+    ot[lane] = v;
+  }
+  if (out_path && lane < n)
+    out_path[static_cast<size_t>(b) * n + lane] = status == 0 && lane < len ? path[lane] : -1;
+  if (lane == 0) {
+    out_n_acc[b] = len;
+    out_status[b] = status;
+  }
+}
+
 }  // namespace
 
 extern "C" size_t sv_verify_coupled_workspace_bytes(int B, int k, int V) {
@@ -165,12 +247,44 @@ extern "C" sv_status sv_verify_coupled(const float* target_logits, const int32_t
   if (!sv_aligned16(workspace)) return SV_ERR_ALIGN;
   const int spans = coupled_spans(V);
   CoupledPartial* parts = static_cast<CoupledPartial*>(workspace);
-  hipLaunchKernelGGL(coupled_choose_kernel, dim3(spans, k + 1, B), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL(choose_kernel<true>, dim3(spans, k + 1, B), dim3(kThreads), 0, stream,
                      target_logits, k, V, static_cast<unsigned int>(seed & 0xFFFFFFFFu),
                      static_cast<unsigned int>(seed >> 32), kTagCoupled + (offset << 8), parts);
   SV_LAUNCH_CHECK();
   hipLaunchKernelGGL(coupled_decide_kernel, dim3(B), dim3(64), 0, stream, draft_tokens, k, V,
                      spans, parts, out_tokens, out_n_acc, out_status, choices);
+  SV_LAUNCH_CHECK();
+  return SV_OK;
+}
+
+extern "C" size_t sv_verify_tree_workspace_bytes(int B, int n, int V) {
+  if (B < 1 || n < 1 || n > SV_MAX_ROWS || V < 1) return 0;
+  return static_cast<size_t>(B) * (n + 1) * coupled_spans(V) * sizeof(CoupledPartial);
+}
+
+extern "C" sv_status sv_verify_tree(const float* target_logits, const int32_t* tokens,
+                                    const int32_t* parents, int B, int n, int V,
+                                    int32_t* out_tokens, int32_t* out_n_acc,
+                                    int32_t* out_status, int32_t* out_path, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  if (!target_logits || !tokens || !parents || !out_tokens || !out_n_acc || !out_status)
+    return SV_ERR_NULL;
+  if (B < 1 || B > 65535 || n < 1 || n > SV_MAX_ROWS || V < 1) return SV_ERR_INVALID_ARG;
+  if (static_cast<long long>(n + 1) * V >= (1LL << 31)) return SV_ERR_INVALID_ARG;
+  if (!sv_aligned16(target_logits) || !sv_aligned16(tokens) || !sv_aligned16(parents) ||
+      !sv_aligned16(out_tokens) || !sv_aligned16(out_n_acc) || !sv_aligned16(out_status) ||
+      (out_path && !sv_aligned16(out_path)))
+    return SV_ERR_ALIGN;
+  if (!workspace || workspace_bytes < sv_verify_tree_workspace_bytes(B, n, V))
+    return SV_ERR_WORKSPACE;
+  if (!sv_aligned16(workspace)) return SV_ERR_ALIGN;
+  const int spans = coupled_spans(V);
+  CoupledPartial* parts = static_cast<CoupledPartial*>(workspace);
+  hipLaunchKernelGGL(choose_kernel<false>, dim3(spans, n + 1, B), dim3(kThreads), 0, stream,
+                     target_logits, n, V, 0u, 0u, 0u, parts);
+  SV_LAUNCH_CHECK();
+  hipLaunchKernelGGL(tree_decide_kernel, dim3(B), dim3(64), 0, stream, tokens, parents, n, V,
+                     spans, parts, out_tokens, out_n_acc, out_status, out_path);
   SV_LAUNCH_CHECK();
   return SV_OK;
 }

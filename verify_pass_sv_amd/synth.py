@@ -19,6 +19,11 @@ Workload shapes and distributions:
 * Accept inputs: draft logits N(0, sd); target = draft + N(0, sigma) noise
   (with an extra independent target row for the bonus position); draft
   tokens sampled from the draft distribution with the Gumbel-max trick.
+* Draft trees: node j hangs under node j - 1 with probability `chain`, else
+  under a uniform pick of the root or an earlier node; target rows are
+  N(0, sd) with one planted token per row lifted by 12 sd; a node's token is
+  the planted token of its parent's row with probability `agree`, else
+  uniform over the vocabulary.
 """
 
 import torch
@@ -114,3 +119,25 @@ def accept_inputs(B, k, V, seed, sigma=1.0, sd=2.0, device="cpu"):
         target = base + torch.randn((B, k + 1, V), generator=g, device=device) * sigma
     tokens = gumbel_max_tokens(draft, seed + 0x5bd1e995, device=device)
     return target.contiguous(), draft, tokens
+
+
+def tree_inputs(B, n, V, seed, chain=0.7, agree=0.8, sd=2.0, device="cpu"):
+    """Synthetic draft trees of n nodes for greedy tree verification.
+
+    Returns (target fp32 [B, n+1, V], tokens int32 [B, n], parents int32
+    [B, n]).  Row 0 of the target belongs to the root, row j+1 to node j;
+    parents precede children.
+    """
+    g = _gen(seed, device)
+    target = torch.randn((B, n + 1, V), generator=g, device=device) * sd
+    planted = torch.randint(0, V, (B, n + 1), generator=g, device=device)
+    target.scatter_(2, planted.unsqueeze(-1), 12.0 * sd)
+    j = torch.arange(n, device=device).expand(B, n)
+    pick = (torch.rand((B, n), generator=g, device=device) * (j + 1)).floor().long() - 1
+    use_chain = torch.rand((B, n), generator=g, device=device) < chain
+    parents = torch.where(use_chain, j - 1, pick)
+    follow = torch.gather(planted, 1, parents + 1)
+    other = torch.randint(0, V, (B, n), generator=g, device=device)
+    hit = torch.rand((B, n), generator=g, device=device) < agree
+    tokens = torch.where(hit, follow, other)
+    return target.contiguous(), tokens.to(torch.int32), parents.to(torch.int32)
