@@ -37,6 +37,8 @@ from .sampling import (truncated_probs, greedy_choice, accept_trial_sampled,
 from .coupled import (gumbel_noise, coupled_choice, coupled_trial, verify_coupled,
                       coupled_drafts, NEAR_TIE_COUPLED)
 from .tree import tree_trial, verify_tree
+from .lmhead import (group_softmax_stats, merge_group_stats, lm_head_logits, lm_head_verify,
+                     NEAR_TIE_LMHEAD)
 from .roofline import (tokens_per_s_bound, w4_bytes_per_weight,
                        decoder_stack_shapes, stack_weight_count,
                        stack_weight_bytes_w4, stack_weight_bytes_w8)
@@ -50,7 +52,9 @@ __all__ = [
     "truncated_probs", "greedy_choice", "accept_trial_sampled",
     "verify_accept_sampled", "sample_drafts", "NEAR_TIE_TOP_P", "gumbel_noise",
     "coupled_choice", "coupled_trial", "verify_coupled", "coupled_drafts",
-    "NEAR_TIE_COUPLED", "tree_trial", "verify_tree", "tokens_per_s_bound",
+    "NEAR_TIE_COUPLED", "tree_trial", "verify_tree", "group_softmax_stats",
+    "merge_group_stats", "lm_head_logits", "lm_head_verify", "NEAR_TIE_LMHEAD",
+    "tokens_per_s_bound",
     "w4_bytes_per_weight", "decoder_stack_shapes", "stack_weight_count",
     "stack_weight_bytes_w4", "stack_weight_bytes_w8",
 ]

@@ -88,7 +88,7 @@ class AcceptResult:
         return self.n_acc + 1 if self.status == 0 else 0
 
 
-def accept_trial(target_logits, draft_logits, draft_tokens, u, u2):
+def accept_trial(target_logits, draft_logits, draft_tokens, u, u2, ties=None):
     """One trial of the accept/correct step with explicit uniforms.
 
     target_logits [k + 1, V], draft_logits [k, V], draft_tokens [k];
@@ -112,19 +112,22 @@ def accept_trial(target_logits, draft_logits, draft_tokens, u, u2):
 
     P = probs(t, lse_t[:, None])
     Q = probs(d, lse_d[:, None])
-    res = accept_on_probs(P, Q, toks, u, u2)
+    res = accept_on_probs(P, Q, toks, u, u2, ties)
     res.lse_target = lse_t
     res.lse_draft = lse_d
     return res
 
 
-def accept_on_probs(P, Q, draft_tokens, u, u2):
+def accept_on_probs(P, Q, draft_tokens, u, u2, ties=None):
     """The accept scan and the replacement/bonus draw on explicit rows.
 
     P [k + 1, V]: the target's distributions (row k for the bonus), Q [k, V]:
     the draft's, both binary64 and normalised; draft tokens in [0, V).  The
-    rule is the one of accept_trial (readings 2, 4 and 6).
+    rule is the one of accept_trial (readings 2, 4 and 6).  ties = (accept,
+    residual) replaces the two near-tie widths of reading 6 (flags only; the
+    decisions do not depend on it).
     """
+    tie_a, tie_r = (NEAR_TIE_ACCEPT, NEAR_TIE_RESIDUAL) if ties is None else ties
     P = np.asarray(P, dtype=np.float64)
     Q = np.asarray(Q, dtype=np.float64)
     toks = np.asarray(draft_tokens, dtype=np.int64)
@@ -139,7 +142,7 @@ def accept_on_probs(P, Q, draft_tokens, u, u2):
     flags = np.zeros(k, dtype=bool)
     for i in range(k):
         lhs = u[i] * q_at[i]
-        flags[i] = abs(lhs - p_at[i]) < NEAR_TIE_ACCEPT and p_at[i] > 0.0 and q_at[i] > 0.0
+        flags[i] = abs(lhs - p_at[i]) < tie_a and p_at[i] > 0.0 and q_at[i] > 0.0
         if not (lhs < p_at[i]):
             n_acc = i
             break
@@ -159,8 +162,7 @@ def accept_on_probs(P, Q, draft_tokens, u, u2):
     v = int(np.searchsorted(csum, thr, side="right"))
     v = min(v, V - 1)
     lo = csum[v - 1] if v > 0 else 0.0
-    rflag = (abs(thr - lo) < NEAR_TIE_RESIDUAL * S) or \
-            (abs(csum[v] - thr) < NEAR_TIE_RESIDUAL * S)
+    rflag = (abs(thr - lo) < tie_r * S) or (abs(csum[v] - thr) < tie_r * S)
     return AcceptResult(status=0, n_acc=n_acc,
                         tokens=[int(x) for x in toks[:n_acc]] + [v],
                         p_at=p_at, q_at=q_at,
@@ -170,7 +172,7 @@ def accept_on_probs(P, Q, draft_tokens, u, u2):
 
 
 def verify_accept(target_logits, draft_logits, draft_tokens, seed, offset=0,
-                  trial_base=0):
+                  trial_base=0, ties=None):
     """Batch of independent trials; trial b draws Philox counter (i, b, offset, 0).
 
     target_logits [B, k + 1, V], draft_logits [B, k, V], draft_tokens [B, k].
@@ -183,5 +185,5 @@ def verify_accept(target_logits, draft_logits, draft_tokens, seed, offset=0,
     out = []
     for b in range(B):
         u, u2 = accept_uniforms(seed, trial_base + b, k, offset=offset)
-        out.append(accept_trial(t[b], d[b], toks[b], u, u2))
+        out.append(accept_trial(t[b], d[b], toks[b], u, u2, ties))
     return out
