@@ -192,12 +192,14 @@ def main():
     y_own = [[torch.empty((32, N), dtype=torch.float32, device=dev)
               for (_, N, *_r) in layer] for layer in w4]
 
-    def w4_pass(kk):
+    def w4_gemms(kk):
         xh, xf = x_h[:kk].contiguous(), x_f[:kk].contiguous()
-        gemms = [(xh if K == HIDDEN else xf, pc, ps, N, y_own[li][gi][:kk])
-                 for li, layer in enumerate(w4)
-                 for gi, (name, N, K, c, s, z, pc, ps) in enumerate(layer)]
-        return sv.sv_pass_plan("w4", gemms)
+        return [(xh if K == HIDDEN else xf, pc, ps, N, y_own[li][gi][:kk])
+                for li, layer in enumerate(w4)
+                for gi, (name, N, K, c, s, z, pc, ps) in enumerate(layer)]
+
+    def w4_pass(kk):
+        return sv.sv_pass_plan("w4", w4_gemms(kk))
 
     def w4_launches(kk, packed=True):
         xh, xf = x_h[:kk].contiguous(), x_f[:kk].contiguous()
@@ -483,6 +485,49 @@ def main():
                 del t, tk, par
             tree["n%d" % n] = row
         extra["tree_verify"] = tree
+        log("fused LM-head verify")
+        # the vocabulary projection (W4, 4096 -> 152 000) as one more GEMM of
+        # the pass, 16 scored rows (k = 15 drafts); fused: its epilogue writes
+        # the softmax statistics and sv_verify_accept_stats merges them;
+        # unfused: the plain GEMM and sv_verify_accept re-reading the logits
+        kk, G = 15, (VOCAB + 63) // 64
+        hc, hs, hz = synth.w4_matrix(VOCAB, HIDDEN, seed=90, device=dev)
+        hpc, hps = sv.sv_w4_pack(hc, hs, hz)
+        del hc, hs, hz
+        hh = synth.activations(kk + 1, HIDDEN, seed=91, device=dev, scale=0.15)
+        lg = torch.empty((kk + 1, VOCAB), dtype=torch.float32, device=dev)
+        lst = torch.empty((kk + 1, G, 2), dtype=torch.float32, device=dev)
+        ldft, ltok = synth.lm_head_drafts(1, kk, VOCAB, seed=92, device=dev)
+        lout = {"tokens": torch.empty((1, kk + 1), dtype=torch.int32, device=dev),
+                "n_acc": torch.empty((1,), dtype=torch.int32, device=dev),
+                "status": torch.empty((1,), dtype=torch.int32, device=dev)}
+        lws = torch.empty(sv.sv_verify_accept_workspace_bytes(1, kk, VOCAB), dtype=torch.uint8,
+                          device=dev)
+        stack = w4_gemms(kk + 1)
+        p_fused = sv.sv_pass_plan("w4", stack + [(hh, hpc, hps, VOCAB, lg, lst)])
+        p_plain = sv.sv_pass_plan("w4", stack + [(hh, hpc, hps, VOCAB, lg)])
+        lg3, lst4 = lg.view(1, kk + 1, VOCAB), lst.view(1, kk + 1, G, 2)
+
+        def acc_fused():
+            sv.sv_verify_accept_stats(lg3, lst4, ldft, ltok, 0, out=lout, workspace=lws)
+
+        def acc_plain():
+            sv.sv_verify_accept(lg3, ldft, ltok, 0, out=lout, workspace=lws)
+
+        n = max(20, args.steps // 4)
+        fused = {"k": kk, "rows": kk + 1, "vocab": VOCAB, "hidden": HIDDEN,
+                 "head_weight_bytes": VOCAB * HIDDEN // 2 + VOCAB * (HIDDEN // GROUP) * 4}
+        for name, fn in (("step_fused_ms", lambda: (sv.sv_pass_run(p_fused), acc_fused())),
+                         ("step_unfused_ms", lambda: (sv.sv_pass_run(p_plain), acc_plain())),
+                         ("pass_with_head_stats_ms", lambda: sv.sv_pass_run(p_fused)),
+                         ("pass_with_head_ms", lambda: sv.sv_pass_run(p_plain))):
+            ms, _ = time_graph(torch, fn, n, n)
+            fused[name] = round(ms, 4)
+        for name, fn in (("accept_stats_us", acc_fused), ("accept_us", acc_plain)):
+            ms, _ = time_graph(torch, fn, 50, 5)
+            fused[name] = round(ms * 1e3, 2)
+        extra["lm_head_verify_k15"] = fused
+        del hpc, hps, lg, lst, p_fused, p_plain
 
     cpu = None
     if not (args.quick or args.no_cpu):

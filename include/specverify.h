@@ -173,6 +173,15 @@ sv_status sv_w8_pack(const int8_t* codes, int N, int K, uint8_t* packed_codes,
  *   y        f32 [m, N], fully overwritten
  *   K, N     N % 16 == 0; K % 128 == 0 (W4, W4_I8) or K % 64 == 0 (W8);
  *            codes, m*K activation bytes and m*N*4 below 2^31 bytes
+ *   stats    NULL, or f32 pairs [m, G, 2] with G = ceil(N / 64), fully
+ *            overwritten: stats[r, g] = (M, S), M = max of y[r, n] and
+ *            S = sum of exp(y[r, n] - M) over n in [64g, min(64g + 64, N))
+ *            (binary32, hardware exp2; S = 0 when M = -inf; S = NaN when
+ *            one of those y is NaN or +inf).  The online-softmax epilogue
+ *            of a vocabulary projection: sv_verify_accept_stats merges these
+ *            pairs instead of reading the logits back (Speculative Decoding
+ *            Clearly Explained, "Check the guesses together" and "Accept
+ *            from left to right").
  * The GEMMs of one pass are independent: no y may overlap another GEMM's
  * inputs or outputs (their order inside the launch is unspecified).
  *
@@ -205,6 +214,7 @@ typedef struct sv_pass_gemm {
   float* y;
   int K;
   int N;
+  float* stats;     /* optional (NULL: none): softmax statistics of y       */
 } sv_pass_gemm;
 
 typedef struct sv_pass {
@@ -215,6 +225,7 @@ typedef struct sv_pass {
   int grid;         /* workgroups of the launch                   */
   int items;        /* work items over all GEMMs                  */
   int max_steps;    /* longest per-workgroup chunk count          */
+  int stats;        /* 1 if some GEMM writes softmax statistics   */
 } sv_pass;
 
 size_t sv_pass_plan_bytes(int format, const sv_pass_gemm* gemms, int count, int m);
@@ -335,6 +346,33 @@ sv_status sv_verify_accept(const float* target_logits, const float* draft_logits
                            int32_t* out_tokens, int32_t* out_n_acc, int32_t* out_status,
                            float* p_at, float* q_at, float* lse,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sv_verify_accept_stats -- sv_verify_accept whose target softmax statistics
+ * come from the vocabulary projection's epilogue (the sv_pass_gemm `stats`
+ * output) instead of a read of the target logits: the fused LM-head verify.
+ *
+ * Defines exactly what sv_verify_accept defines (Speculative Decoding Clearly
+ * Explained, "Check the guesses together", "Accept from left to right",
+ * "Correct and continue"); only the log-sum-exp of each target row is formed
+ * by merging its (max, sum of exp) pairs of 64 logits.
+ *
+ *   target_logits  f32 [B, k+1, V]: still read at the draft tokens and along
+ *                  the one residual / bonus row
+ *   target_stats   f32 pairs [B, k+1, ceil(V/64), 2] (not NULL): the stats of
+ *                  a pass GEMM with N = V over m = B (k+1) rows, trial-major
+ *   every other argument, the outputs, the workspace
+ *   (sv_verify_accept_workspace_bytes) and the errors as sv_verify_accept.
+ * A pair with a NaN sum marks its row invalid (status 2), as a NaN or +inf
+ * logit does.  Decisions equal sv_verify_accept's on the same logits up to
+ * the binary32 rounding of the row normalizers.
+ */
+sv_status sv_verify_accept_stats(const float* target_logits, const float* target_stats,
+                                 const float* draft_logits, const int32_t* draft_tokens, int B,
+                                 int k, int V, uint64_t seed, uint32_t offset,
+                                 int32_t* out_tokens, int32_t* out_n_acc, int32_t* out_status,
+                                 float* p_at, float* q_at, float* lse,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * sv_verify_sampled -- verification under a request's sampling settings:

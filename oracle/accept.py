@@ -124,10 +124,12 @@ def accept_on_probs(P, Q, draft_tokens, u, u2, ties=None):
     P [k + 1, V]: the target's distributions (row k for the bonus), Q [k, V]:
     the draft's, both binary64 and normalised; draft tokens in [0, V).  The
     rule is the one of accept_trial (readings 2, 4 and 6).  ties = (accept,
-    residual) replaces the two near-tie widths of reading 6 (flags only; the
-    decisions do not depend on it).
+    residual[, accept relative to p]) replaces the near-tie widths of
+    reading 6: an accept decision is flagged when |u q - p| is below
+    max(accept, relative * p) (flags only; the decisions do not depend on it).
     """
-    tie_a, tie_r = (NEAR_TIE_ACCEPT, NEAR_TIE_RESIDUAL) if ties is None else ties
+    tie_a, tie_r, tie_p = ((NEAR_TIE_ACCEPT, NEAR_TIE_RESIDUAL, 0.0) if ties is None
+                           else (tuple(ties) + (0.0,))[:3])
     P = np.asarray(P, dtype=np.float64)
     Q = np.asarray(Q, dtype=np.float64)
     toks = np.asarray(draft_tokens, dtype=np.int64)
@@ -142,7 +144,8 @@ def accept_on_probs(P, Q, draft_tokens, u, u2, ties=None):
     flags = np.zeros(k, dtype=bool)
     for i in range(k):
         lhs = u[i] * q_at[i]
-        flags[i] = abs(lhs - p_at[i]) < tie_a and p_at[i] > 0.0 and q_at[i] > 0.0
+        flags[i] = (abs(lhs - p_at[i]) < max(tie_a, tie_p * p_at[i]) and p_at[i] > 0.0
+                    and q_at[i] > 0.0)
         if not (lhs < p_at[i]):
             n_acc = i
             break
@@ -168,7 +171,8 @@ def accept_on_probs(P, Q, draft_tokens, u, u2, ties=None):
                         p_at=p_at, q_at=q_at,
                         accept_flags=flags[:min(n_acc + 1, k)],
                         residual_flag=bool(rflag), residual_row=r,
-                        weights_sum=float(S))
+                        weights_sum=float(S),
+                        extra={"residual_csum": csum, "residual_thr": float(thr)})
 
 
 def verify_accept(target_logits, draft_logits, draft_tokens, seed, offset=0,

@@ -206,3 +206,23 @@ def test_tree_verification_validation_before_launch():
     assert call(n=0) == 2 and call(n=33) == 2 and call(B=0) == 2 and call(B=65536) == 2
     assert call(path=ctypes.c_void_p(0x100004)) == 3
     assert call(ws_bytes=ws - 1) == 5 and call(workspace=None) == 5
+
+
+def test_softmax_statistics_arguments_before_launch():
+    import verify_pass_sv_amd as sv
+    L = sv.lib
+    a = 0x100000                                   # aligned, never dereferenced
+    arr = (sv.SvPassGemm * 1)()
+    arr[0] = sv.SvPassGemm(a, None, a, a, a, 4096, 152000, a)
+    assert L.sv_pass_plan_bytes(0, arr, 1, 16) > 0
+    arr[0] = sv.SvPassGemm(a, None, a, a, a, 4096, 152000, a + 8)   # stats misaligned
+    assert L.sv_pass_plan_bytes(0, arr, 1, 16) == 0
+    fake = ctypes.c_void_p(a)
+    ws = sv.sv_verify_accept_workspace_bytes(1, 4, 1000)
+
+    def call(stats=fake, k=4):
+        return L.sv_verify_accept_stats(fake, stats, fake, fake, 1, k, 1000, 0, 0, fake, fake,
+                                        fake, None, None, None, fake, ws, None)
+    assert call(stats=None) == 1
+    assert call(stats=ctypes.c_void_p(a + 4)) == 3
+    assert call(k=0) == 2 and call(k=33) == 2

@@ -99,3 +99,17 @@ def test_fused_verify_equals_accept_on_the_projected_logits():
         assert a.status == b.status == 0
         assert a.n_acc == b.n_acc and a.tokens == b.tokens
     assert np.array_equal(logits, lm_head_logits(h, codes, scales, zeros, B, k))
+
+
+def test_residual_draw_lies_in_its_bin():
+    # the running sums and threshold the fused-verify comparison uses: the
+    # emitted token's bin [C_{v-1}, C_v) holds the threshold u' S
+    rng = np.random.default_rng(12)
+    B, k, V = 6, 3, 500
+    t = rng.normal(0, 2, (B, k + 1, V))
+    d = rng.normal(0, 2, (B, k, V))
+    toks = rng.integers(0, V, (B, k))
+    for r in verify_accept(t, d, toks, seed=2):
+        c, thr, v = r.extra["residual_csum"], r.extra["residual_thr"], r.tokens[-1]
+        assert (c[v - 1] if v > 0 else 0.0) <= thr < c[v]
+        assert abs(c[-1] - r.weights_sum) == 0.0

@@ -15,7 +15,7 @@ _BINDING_NAMES = (
     "sv_w8_pack", "sv_pass_plan", "sv_pass_run", "Pass", "SvPassGemm", "SvPass",
     "PASS_FORMATS", "sv_verify_sampled", "sv_verify_sampled_workspace_bytes", "SvSampling",
     "sv_verify_coupled", "sv_verify_coupled_workspace_bytes", "sv_verify_tree",
-    "sv_verify_tree_workspace_bytes",
+    "sv_verify_tree_workspace_bytes", "sv_verify_accept_stats",
 )
 
 __all__ = list(_BINDING_NAMES)

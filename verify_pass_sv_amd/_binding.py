@@ -23,7 +23,7 @@ EXPORTED_SYMBOLS = (
     "sv_w8_pack", "sv_pass_plan_bytes", "sv_pass_plan", "sv_pass_run",
     "sv_verify_sampled_workspace_bytes", "sv_verify_sampled",
     "sv_verify_coupled_workspace_bytes", "sv_verify_coupled",
-    "sv_verify_tree_workspace_bytes", "sv_verify_tree",
+    "sv_verify_tree_workspace_bytes", "sv_verify_tree", "sv_verify_accept_stats",
 )
 
 _STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_INVALID_ARG", 3: "SV_ERR_ALIGN",
@@ -34,14 +34,14 @@ class SvPassGemm(ctypes.Structure):
     """C struct sv_pass_gemm: one GEMM of a verify pass."""
     _fields_ = [("x", ctypes.c_void_p), ("xscale", ctypes.c_void_p), ("codes", ctypes.c_void_p),
                 ("scales", ctypes.c_void_p), ("y", ctypes.c_void_p), ("K", ctypes.c_int),
-                ("N", ctypes.c_int)]
+                ("N", ctypes.c_int), ("stats", ctypes.c_void_p)]
 
 
 class SvPass(ctypes.Structure):
     """C struct sv_pass: host descriptor of a planned pass."""
     _fields_ = [("plan", ctypes.c_void_p), ("format", ctypes.c_int), ("m", ctypes.c_int),
                 ("count", ctypes.c_int), ("grid", ctypes.c_int), ("items", ctypes.c_int),
-                ("max_steps", ctypes.c_int)]
+                ("max_steps", ctypes.c_int), ("stats", ctypes.c_int)]
 
 
 PASS_FORMATS = {"w4": 0, "w8": 1, "w4_i8": 2}
@@ -77,6 +77,8 @@ def _load():
         "sv_verify_accept_workspace_bytes": (sz, [i32, i32, i32]),
         "sv_verify_accept": (i32, [vp, vp, vp, i32, i32, i32, u64, u32, vp, vp, vp, vp, vp,
                                    vp, vp, sz, vp]),
+        "sv_verify_accept_stats": (i32, [vp, vp, vp, vp, i32, i32, i32, u64, u32, vp, vp, vp,
+                                         vp, vp, vp, vp, sz, vp]),
         "sv_philox4x32_10": (i32, [vp, vp, vp, i32, vp]),
         "sv_read_probe_sink_words": (i32, []),
         "sv_read_bandwidth_probe": (i32, [vp, sz, vp, vp]),
@@ -225,10 +227,12 @@ def _pass_gemms(fmt, gemms, group):
     m = None
     keep = []
     for i, g in enumerate(gemms):
+        base = 6 if fmt == "w4_i8" else 5
+        stats = g[base] if len(g) > base else None
         if fmt == "w4_i8":
-            x, xscale, codes, sc, N, y = g
+            x, xscale, codes, sc, N, y = g[:base]
         else:
-            x, codes, sc, N, y = g
+            x, codes, sc, N, y = g[:base]
             xscale = None
         mm, K = x.shape
         m = mm if m is None else m
@@ -245,9 +249,12 @@ def _pass_gemms(fmt, gemms, group):
         if xscale is not None:
             _need(xscale, "xscale", torch.float32, (m,))
         _need(y, "y", torch.float32, (m, N))
+        if stats is not None:
+            _need(stats, "stats", torch.float32, (m, (N + 63) // 64, 2))
         arr[i] = SvPassGemm(x.data_ptr(), None if xscale is None else xscale.data_ptr(),
-                            codes.data_ptr(), sc.data_ptr(), y.data_ptr(), K, N)
-        keep += [t for t in (x, xscale, codes, sc, y) if t is not None]
+                            codes.data_ptr(), sc.data_ptr(), y.data_ptr(), K, N,
+                            None if stats is None else stats.data_ptr())
+        keep += [t for t in (x, xscale, codes, sc, y, stats) if t is not None]
     return arr, m, keep
 
 
@@ -258,6 +265,8 @@ def sv_pass_plan(fmt, gemms, group=64, stream=None):
       w4:    (x bf16 [m, K], packed_codes, packed_sz, N, y f32 [m, N])
       w8:    (x bf16 [m, K], packed_codes (sv_w8_pack), scales f16 [N], N, y)
       w4_i8: (xq int8 [m, K], xscale f32 [m], packed_codes, packed_sz, N, y)
+    each optionally followed by stats f32 [m, ceil(N/64), 2], which receives
+    the softmax statistics (max, sum of exp) of every 64 outputs of a row.
     Returns a Pass for sv_pass_run.  Synchronizes `stream`.
     """
     if fmt not in PASS_FORMATS:
@@ -363,6 +372,39 @@ def sv_verify_accept(target_logits, draft_logits, draft_tokens, seed, offset=0, 
         _ptr(out["tokens"]), _ptr(out["n_acc"]), _ptr(out["status"]), _ptr(out.get("p_at")),
         _ptr(out.get("q_at")), _ptr(out.get("lse")), _ptr(workspace),
         ctypes.c_size_t(workspace.numel()), _stream(stream)))
+    return out
+
+
+def sv_verify_accept_stats(target_logits, target_stats, draft_logits, draft_tokens, seed,
+                           offset=0, out=None, diagnostics=False, workspace=None, stream=None):
+    """sv_verify_accept with the target rows' softmax statistics taken from
+    target_stats f32 [B, k+1, ceil(V/64), 2] (a pass GEMM's stats output)."""
+    B, k1, V = target_logits.shape
+    k = k1 - 1
+    dev = target_logits.device
+    _need(target_logits, "target_logits", torch.float32, (B, k + 1, V))
+    _need(target_stats, "target_stats", torch.float32, (B, k + 1, (V + 63) // 64, 2))
+    _need(draft_logits, "draft_logits", torch.float32, (B, k, V))
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, k))
+    if out is None:
+        out = {
+            "tokens": torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+            "n_acc": torch.empty((B,), dtype=torch.int32, device=dev),
+            "status": torch.empty((B,), dtype=torch.int32, device=dev),
+        }
+        if diagnostics:
+            out["p_at"] = torch.empty((B, k), dtype=torch.float32, device=dev)
+            out["q_at"] = torch.empty((B, k), dtype=torch.float32, device=dev)
+            out["lse"] = torch.empty((B, 2 * k + 1), dtype=torch.float32, device=dev)
+    need = sv_verify_accept_workspace_bytes(B, k, V)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    _check("sv_verify_accept_stats", lib.sv_verify_accept_stats(
+        _ptr(target_logits), _ptr(target_stats), _ptr(draft_logits), _ptr(draft_tokens), B, k,
+        V, ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+        ctypes.c_uint32(int(offset) & 0xFFFFFFFF), _ptr(out["tokens"]), _ptr(out["n_acc"]),
+        _ptr(out["status"]), _ptr(out.get("p_at")), _ptr(out.get("q_at")), _ptr(out.get("lse")),
+        _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream)))
     return out
 
 

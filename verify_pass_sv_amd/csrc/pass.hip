@@ -58,6 +58,14 @@
 //          partial I = sum c xq, folded as y += s I; the zero point leaves
 //          through the same rank-4 update with the exact int32 group sums
 //          Xg = sum xq; at the item end y *= xscale[row].
+//
+// Optional softmax-statistics epilogue (any format, per GEMM): with a stats
+// buffer, the item end also writes, for each row and each 64 output channels
+// (one wave's share), the maximum of y and the sum of exp(y - max) -- the
+// online-softmax pieces of a vocabulary projection, so a following accept
+// step need not read the logits back to normalize them (Speculative Decoding
+// Clearly Explained, "Check the guesses together": the target scores every
+// draft position in the pass; "Accept from left to right" needs p = softmax).
 #include <algorithm>
 #include <functional>
 #include <queue>
@@ -68,7 +76,7 @@
 namespace {
 
 constexpr uint32_t kPlanMagic = 0x50565653u;   // "SVVP"
-constexpr uint32_t kPlanVersion = 2;
+constexpr uint32_t kPlanVersion = 3;
 constexpr int kMaxGrid = 2048;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -110,7 +118,7 @@ inline int fmt_xe(int f) { return f == SV_PASS_W4_I8 ? 1 : 2; }
 
 struct PlanHeader {                             // 64 bytes
   uint32_t magic, version;
-  int32_t format, m, count, grid, items, max_steps, reserved0;
+  int32_t format, m, count, grid, items, max_steps, stats;   // stats: some GEMM has a stats buffer
   uint64_t reserved[3];
 };
 struct PlanItem {                               // 64 bytes
@@ -120,7 +128,7 @@ struct PlanItem {                               // 64 bytes
   const void* sz;
   float* y;
   int32_t K, N, tile0, nchunk;
-  uint64_t reserved;
+  float* stats;                                 // [m, ceil(N / 64)] (max, sum) pairs, or null
 };
 static_assert(sizeof(PlanHeader) == 64, "plan header layout");
 static_assert(sizeof(PlanItem) == 64, "plan item layout");
@@ -175,7 +183,9 @@ __device__ __forceinline__ sv_u32x2 w8_cvt4(unsigned int d) {
   return r;
 }
 
-template <int F, int MT, int P>
+// ST: the plan has GEMMs with a softmax-statistics buffer.  Plans without
+// any run the ST = false kernel, which holds no trace of the epilogue.
+template <int F, int MT, int P, bool ST>
 __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restrict__ plan, int m) {
   using G = Geo<F, MT>;
   constexpr int L = kTW * kNB + Fmt<F>::SZD + Fmt<F>::AUXD + G::XD;   // loads per wave per step
@@ -210,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
   extern __shared__ __align__(16) uint8_t lds[];
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(plan);
-  if (hdr->magic != kPlanMagic || hdr->format != F || hdr->m != m ||
+  if (hdr->magic != kPlanMagic || hdr->format != F || hdr->m != m || (hdr->stats != 0) != ST ||
       hdr->grid != static_cast<int>(gridDim.x))
     return;                                     // stale or foreign plan: touch nothing
   const int32_t* wg_begin = reinterpret_cast<const int32_t*>(plan + kBeginOff);
@@ -271,7 +281,8 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
   // ---- compute cursor: the item and chunk computed next ----
   int c_item = ib, c_c = 0;
   int c_K = 128, c_N = 16, c_t0 = 0, c_nchunk = 1;
-  __amdgpu_buffer_rsrc_t yrs = wrs;
+  bool c_stats = false;
+  __amdgpu_buffer_rsrc_t yrs = wrs, zrs = wrs;
   auto load_compute_item = [&](int idx) {
     const PlanItem it = items[idx];
     c_K = it.K;
@@ -279,6 +290,11 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
     c_t0 = it.tile0;
     c_nchunk = it.nchunk;
     yrs = __builtin_amdgcn_make_buffer_rsrc(it.y, 0, m * it.N * 4, 0x00020000);
+    if constexpr (ST) {
+      c_stats = it.stats != nullptr;
+      zrs = __builtin_amdgcn_make_buffer_rsrc(it.stats, 0, m * ceil_div(it.N, 64) * 8,
+                                              0x00020000);
+    }
   };
   if (ib < ie) {
     load_w_item(ib);
@@ -609,6 +625,47 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
                                                off, 0, kStream);
       }
     }
+    if (ST && c_stats) {
+      // Row r's 64 channels of this wave sit in the 16 lanes of lane >> 4 ==
+      // (r % 16) / 4 ... (4 each): max, then sum of exp(y - max) over the
+      // 16 lanes.  A NaN or +inf makes the sum NaN (the row is invalid);
+      // missing channels count as -inf.
+      const int grp = (c_t0 + wave * kTW) >> 2;
+      const int ngrp = ceil_div(c_N, 64);
+#pragma unroll
+      for (int a = 0; a < MT; ++a) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = 16 * a + 4 * rr + (lane >> 4);
+          sv_f32x4 v = yacc[rr][a];
+          bool bad = false;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            bad |= (v[i] != v[i]) | (v[i] == INFINITY);
+            v[i] = ch_ok ? v[i] : -INFINITY;
+          }
+          float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+          float sm = 0.f;
+          if (mx != -INFINITY) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sm += __builtin_amdgcn_exp2f((v[i] - mx) * 1.4426950408889634f);
+          }
+          sm = ch_ok && bad ? __builtin_nanf("") : sm;
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) sm += __shfl_xor(sm, o);
+          const unsigned int off = (lane & 15) == 0 && r < m && grp < ngrp
+                                       ? static_cast<unsigned int>(r * ngrp + grp) * 8
+                                       : kSvOutOfRange;
+          sv_u32x2 pr;
+          pr.x = __float_as_uint(mx);
+          pr.y = __float_as_uint(sm);
+          __builtin_amdgcn_raw_buffer_store_b64(pr, zrs, off, 0, kStream);
+        }
+      }
+    }
 #pragma unroll
     for (int a = 0; a < MT; ++a) {
       xacc[a] = fz;
@@ -671,9 +728,9 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
   sv_barrier_no_fence();
 }
 
-template <int F, int MT, int P>
+template <int F, int MT, int P, bool ST>
 sv_status launch_pass(const void* plan, int m, int grid, hipStream_t st) {
-  auto kern = pass_kernel<F, MT, P>;
+  auto kern = pass_kernel<F, MT, P, ST>;
   constexpr int kLds = pass_lds_bytes<F, MT, P>();
   static_assert(kLds <= 160 * 1024, "LDS budget of a gfx950 workgroup");
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -704,8 +761,11 @@ sv_status check_gemms(int format, const sv_pass_gemm* gemms, int count, int m,
     if (code_bytes >= (1LL << 31) || static_cast<long long>(m) * e.K * xe >= (1LL << 31) ||
         static_cast<long long>(m) * e.N * 4 >= (1LL << 31))
       return SV_ERR_UNSUPPORTED;
+    if (e.stats && static_cast<long long>(m) * ceil_div(e.N, 64) * 8 >= (1LL << 31))
+      return SV_ERR_UNSUPPORTED;
     if (!sv_aligned16(e.x) || !sv_aligned16(e.codes) || !sv_aligned16(e.scales) ||
-        !sv_aligned16(e.y) || (e.xscale && !sv_aligned16(e.xscale)))
+        !sv_aligned16(e.y) || (e.xscale && !sv_aligned16(e.xscale)) ||
+        (e.stats && !sv_aligned16(e.stats)))
       return SV_ERR_ALIGN;
     items += ceil_div(e.N / 16, kItemTiles);
   }
@@ -743,6 +803,8 @@ extern "C" sv_status sv_pass_plan(int format, const sv_pass_gemm* gemms, int cou
   const int grid = static_cast<int>(std::min<long long>({cus, kMaxGrid, n_items}));
   const int kc = kNB * fmt_kpb(format);
 
+  int any_stats = 0;
+  for (int g = 0; g < count; ++g) any_stats |= gemms[g].stats != nullptr;
   // Items in pass order.
   std::vector<PlanItem> items;
   items.reserve(static_cast<size_t>(n_items));
@@ -751,7 +813,7 @@ extern "C" sv_status sv_pass_plan(int format, const sv_pass_gemm* gemms, int cou
     const int tiles = e.N / 16;
     for (int t0 = 0; t0 < tiles; t0 += kItemTiles)
       items.push_back(PlanItem{e.x, e.xscale, e.codes, e.scales, e.y, e.K, e.N, t0,
-                               ceil_div(e.K, kc), 0});
+                               ceil_div(e.K, kc), e.stats});
   }
   // Longest-first greedy: each item (by chunk count, ties in pass order) goes
   // to the workgroup with the fewest chunks so far (ties: lowest index).
@@ -798,6 +860,7 @@ extern "C" sv_status sv_pass_plan(int format, const sv_pass_gemm* gemms, int cou
   hdr->grid = grid;
   hdr->items = static_cast<int32_t>(n_items);
   hdr->max_steps = max_steps;
+  hdr->stats = any_stats;
 
   // Plan upload: a setup step (like packing the weights), synchronous so the
   // host image can be released.
@@ -811,31 +874,39 @@ extern "C" sv_status sv_pass_plan(int format, const sv_pass_gemm* gemms, int cou
   pass->grid = grid;
   pass->items = static_cast<int>(n_items);
   pass->max_steps = max_steps;
+  pass->stats = any_stats;
   return SV_OK;
 }
 
-extern "C" sv_status sv_pass_run(const sv_pass* pass, hipStream_t stream) {
-  if (!pass || !pass->plan) return SV_ERR_NULL;
-  if (!sv_aligned16(pass->plan)) return SV_ERR_ALIGN;
-  if (pass->m < 1 || pass->m > SV_MAX_ROWS || pass->grid < 1 || pass->grid > kMaxGrid)
-    return SV_ERR_INVALID_ARG;
+namespace {
+template <bool ST>
+sv_status dispatch_pass(const sv_pass* pass, hipStream_t stream) {
   // Two activation tiles for m > 16.  The ring keeps three chunks in flight
   // (two for the 4-bit bf16 path at m > 16, whose registers would not hold a
   // third).
   const bool two = pass->m > 16;
   switch (pass->format) {
     case SV_PASS_W4:
-      return two ? launch_pass<SV_PASS_W4, 2, 3>(pass->plan, pass->m, pass->grid, stream)
-                 : launch_pass<SV_PASS_W4, 1, 4>(pass->plan, pass->m, pass->grid, stream);
+      return two ? launch_pass<SV_PASS_W4, 2, 3, ST>(pass->plan, pass->m, pass->grid, stream)
+                 : launch_pass<SV_PASS_W4, 1, 4, ST>(pass->plan, pass->m, pass->grid, stream);
     case SV_PASS_W8:
-      return two ? launch_pass<SV_PASS_W8, 2, 4>(pass->plan, pass->m, pass->grid, stream)
-                 : launch_pass<SV_PASS_W8, 1, 4>(pass->plan, pass->m, pass->grid, stream);
+      return two ? launch_pass<SV_PASS_W8, 2, 4, ST>(pass->plan, pass->m, pass->grid, stream)
+                 : launch_pass<SV_PASS_W8, 1, 4, ST>(pass->plan, pass->m, pass->grid, stream);
     case SV_PASS_W4_I8:
-      return two ? launch_pass<SV_PASS_W4_I8, 2, 4>(pass->plan, pass->m, pass->grid, stream)
-                 : launch_pass<SV_PASS_W4_I8, 1, 4>(pass->plan, pass->m, pass->grid, stream);
+      return two ? launch_pass<SV_PASS_W4_I8, 2, 4, ST>(pass->plan, pass->m, pass->grid, stream)
+                 : launch_pass<SV_PASS_W4_I8, 1, 4, ST>(pass->plan, pass->m, pass->grid, stream);
     default:
       return SV_ERR_INVALID_ARG;
   }
+}
+}  // namespace
+
+extern "C" sv_status sv_pass_run(const sv_pass* pass, hipStream_t stream) {
+  if (!pass || !pass->plan) return SV_ERR_NULL;
+  if (!sv_aligned16(pass->plan)) return SV_ERR_ALIGN;
+  if (pass->m < 1 || pass->m > SV_MAX_ROWS || pass->grid < 1 || pass->grid > kMaxGrid)
+    return SV_ERR_INVALID_ARG;
+  return pass->stats ? dispatch_pass<true>(pass, stream) : dispatch_pass<false>(pass, stream);
 }
 
 // ---- W8 packing -------------------------------------------------------------

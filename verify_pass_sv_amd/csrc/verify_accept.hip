@@ -12,6 +12,9 @@
 //             over a span, with all loads of a 2048-float batch in flight
 //             before any is used -> partial (max, sum, invalid flag).  It also
 //             zeroes the per-trial completion counters of launch 2.
+//             sv_verify_accept_stats: for the target rows the wave merges the
+//             (max, sum) pairs of 64 logits that the vocabulary projection's
+//             epilogue wrote, instead of reading the logits.
 //  2. decide  one workgroup per (trial, residual share): merges the trial's
 //             partials into log-sum-exp values (staged in LDS, several threads
 //             per row, fixed order), evaluates p_i(d_i), q_i(d_i), draws the
@@ -145,10 +148,11 @@ __device__ __forceinline__ const float* row_ptr(const float* tgt, const float* d
 // ---- kernel 1: per-span softmax statistics ---------------------------------
 // All loads of a 2048-float batch are issued before any is used (8 float4 or
 // 32 floats per lane), so a wave pays one memory latency per batch.
-template <bool VEC>
+template <bool VEC, bool PRE>
 __global__ __launch_bounds__(64 * kStatsWaves) void stats_kernel(
-    const float* __restrict__ tgt, const float* __restrict__ dft, int B, int k, int V, int C1,
-    int span, StatPartial* __restrict__ part, int* __restrict__ done) {
+    const float* __restrict__ tgt, const float* __restrict__ dft,
+    const float2* __restrict__ tstats, int B, int k, int V, int C1, int span,
+    StatPartial* __restrict__ part, int* __restrict__ done) {
   // the per-trial completion counters of kernel 2 start at zero every call
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < B; i += blockDim.x) done[i] = 0;
@@ -165,6 +169,16 @@ __global__ __launch_bounds__(64 * kStatsWaves) void stats_kernel(
   const int hi = min(V, lo + span);
   float m = -INFINITY, s = 0.f;
   int bad = 0;
+  if (PRE && j <= k) {
+    // the span's pairs of 64 logits (span and lo are multiples of 64)
+    const int G = (V + 63) / 64;
+    const float2* st = tstats + (static_cast<size_t>(b) * (k + 1) + j) * G;
+    for (int g = lo / 64 + lane; g < (hi + 63) / 64; g += 64) {
+      const float2 pr = st[g];
+      bad |= pr.y != pr.y;
+      if (pr.y == pr.y) stat_merge(m, s, pr.x, pr.y);
+    }
+  } else
   for (int base = lo; base < hi; base += kBatch) {
     constexpr int NV = VEC ? kBatch / 256 : kBatch / 64;
     float v[VEC ? 4 * NV : NV];
@@ -610,15 +624,17 @@ extern "C" size_t sv_verify_accept_workspace_bytes(int B, int k, int V) {
   return ws_layout(B, k, V).bytes;
 }
 
-extern "C" sv_status sv_verify_accept(const float* target_logits, const float* draft_logits,
-                                      const int32_t* draft_tokens, int B, int k, int V,
-                                      uint64_t seed, uint32_t offset, int32_t* out_tokens,
-                                      int32_t* out_n_acc, int32_t* out_status, float* p_at,
-                                      float* q_at, float* lse, void* workspace,
-                                      size_t workspace_bytes, hipStream_t stream) {
+namespace {
+sv_status verify_accept(const float* target_logits, const float* target_stats,
+                        const float* draft_logits, const int32_t* draft_tokens, int B, int k,
+                        int V, uint64_t seed, uint32_t offset, int32_t* out_tokens,
+                        int32_t* out_n_acc, int32_t* out_status, float* p_at, float* q_at,
+                        float* lse, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
   if (!target_logits || !draft_logits || !draft_tokens || !out_tokens || !out_n_acc ||
       !out_status)
     return SV_ERR_NULL;
+  if (target_stats && !sv_aligned16(target_stats)) return SV_ERR_ALIGN;
   if (B < 1 || k < 1 || k > SV_MAX_ROWS || V < 1) return SV_ERR_INVALID_ARG;
   if (static_cast<long long>(k + 1) * V >= (1LL << 31)) return SV_ERR_INVALID_ARG;
   if (!sv_aligned16(target_logits) || !sv_aligned16(draft_logits) ||
@@ -646,14 +662,23 @@ extern "C" sv_status sv_verify_accept(const float* target_logits, const float* d
   const size_t dyn = static_cast<size_t>(resid_blocks(V)) * sizeof(double);
   if (dyn > 32 * 1024) return SV_ERR_UNSUPPORTED;
 
-  if (V % 4 == 0)
-    hipLaunchKernelGGL((stats_kernel<true>), dim3(static_cast<unsigned>(blocks1)),
-                       dim3(64 * kStatsWaves), 0, stream, target_logits, draft_logits, B, k, V,
-                       C1, span, part, done);
+  const float2* tst = reinterpret_cast<const float2*>(target_stats);
+  if (tst && V % 4 == 0)
+    hipLaunchKernelGGL((stats_kernel<true, true>), dim3(static_cast<unsigned>(blocks1)),
+                       dim3(64 * kStatsWaves), 0, stream, target_logits, draft_logits, tst, B, k,
+                       V, C1, span, part, done);
+  else if (tst)
+    hipLaunchKernelGGL((stats_kernel<false, true>), dim3(static_cast<unsigned>(blocks1)),
+                       dim3(64 * kStatsWaves), 0, stream, target_logits, draft_logits, tst, B, k,
+                       V, C1, span, part, done);
+  else if (V % 4 == 0)
+    hipLaunchKernelGGL((stats_kernel<true, false>), dim3(static_cast<unsigned>(blocks1)),
+                       dim3(64 * kStatsWaves), 0, stream, target_logits, draft_logits, tst, B, k,
+                       V, C1, span, part, done);
   else
-    hipLaunchKernelGGL((stats_kernel<false>), dim3(static_cast<unsigned>(blocks1)),
-                       dim3(64 * kStatsWaves), 0, stream, target_logits, draft_logits, B, k, V,
-                       C1, span, part, done);
+    hipLaunchKernelGGL((stats_kernel<false, false>), dim3(static_cast<unsigned>(blocks1)),
+                       dim3(64 * kStatsWaves), 0, stream, target_logits, draft_logits, tst, B, k,
+                       V, C1, span, part, done);
   SV_LAUNCH_CHECK();
   hipLaunchKernelGGL(decide_kernel, dim3(static_cast<unsigned>(B) * C2), dim3(kThreads), dyn,
                      stream, target_logits, draft_logits, draft_tokens, B, k, V, C1, C2,
@@ -662,6 +687,31 @@ extern "C" sv_status sv_verify_accept(const float* target_logits, const float* d
                      out_tokens, out_n_acc, out_status, p_at, q_at, lse, done);
   SV_LAUNCH_CHECK();
   return SV_OK;
+}
+}  // namespace
+
+extern "C" sv_status sv_verify_accept(const float* target_logits, const float* draft_logits,
+                                      const int32_t* draft_tokens, int B, int k, int V,
+                                      uint64_t seed, uint32_t offset, int32_t* out_tokens,
+                                      int32_t* out_n_acc, int32_t* out_status, float* p_at,
+                                      float* q_at, float* lse, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  return verify_accept(target_logits, nullptr, draft_logits, draft_tokens, B, k, V, seed, offset,
+                       out_tokens, out_n_acc, out_status, p_at, q_at, lse, workspace,
+                       workspace_bytes, stream);
+}
+
+extern "C" sv_status sv_verify_accept_stats(const float* target_logits, const float* target_stats,
+                                            const float* draft_logits,
+                                            const int32_t* draft_tokens, int B, int k, int V,
+                                            uint64_t seed, uint32_t offset, int32_t* out_tokens,
+                                            int32_t* out_n_acc, int32_t* out_status, float* p_at,
+                                            float* q_at, float* lse, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream) {
+  if (!target_stats) return SV_ERR_NULL;
+  return verify_accept(target_logits, target_stats, draft_logits, draft_tokens, B, k, V, seed,
+                       offset, out_tokens, out_n_acc, out_status, p_at, q_at, lse, workspace,
+                       workspace_bytes, stream);
 }
 
 extern "C" sv_status sv_philox4x32_10(const uint32_t* ctr, const uint32_t* key, uint32_t* out,

@@ -48,6 +48,29 @@ __device__ __forceinline__ bool better(double s, int v, double bs, int bv) {
   return s > bs || (s == bs && v < bv);
 }
 
+// Merges the span partials of one target row in span order (score down,
+// index up), loading 8 partials at a time so their latencies overlap.
+__device__ __forceinline__ void merge_spans(const CoupledPartial* __restrict__ p, int spans,
+                                            double& best, int& bi, int& flags) {
+  constexpr int kUnroll = 8;
+  for (int s0 = 0; s0 < spans; s0 += kUnroll) {
+    CoupledPartial q[kUnroll];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j)
+      if (s0 + j < spans) q[j] = p[s0 + j];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      if (s0 + j < spans) {
+        if (better(q[j].score, q[j].index, best, bi)) {
+          best = q[j].score;
+          bi = q[j].index;
+        }
+        flags |= q[j].flags;
+      }
+    }
+  }
+}
+
 // Rows of [B, rows, V] logits: rows = k + 1 (coupled) or n + 1 (tree).
 template <bool NOISE>
 __global__ __launch_bounds__(kThreads) void choose_kernel(
@@ -66,8 +89,19 @@ __global__ __launch_bounds__(kThreads) void choose_kernel(
   double best = -INFINITY;
   int bi = V;
   int flags = 0;
-  for (int v = v0 + tid; v < v1; v += kThreads) {
-    const float x = row[v];
+  // every load of the thread's 16 entries goes out before any is used
+  constexpr int kPer = kSpan / kThreads;
+  float xs[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int v = v0 + tid + j * kThreads;
+    xs[j] = v < v1 ? row[v] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int v = v0 + tid + j * kThreads;
+    if (v >= v1) break;
+    const float x = xs[j];
     flags |= ((x != x) | (x == INFINITY)) ? 1 : 0;
     flags |= (x > -INFINITY && x < INFINITY) ? 2 : 0;
     double sc = static_cast<double>(x);
@@ -117,17 +151,9 @@ __global__ __launch_bounds__(64) void coupled_decide_kernel(
   double best = -INFINITY;
   int bi = V;
   int flags = 0;
-  if (is_row) {
-    const CoupledPartial* p = parts + (static_cast<size_t>(b) * (k + 1) + lane) * spans;
-    for (int s = 0; s < spans; ++s) {
-      const CoupledPartial q = p[s];
-      if (better(q.score, q.index, best, bi)) {
-        best = q.score;
-        bi = q.index;
-      }
-      flags |= q.flags;
-    }
-  }
+  if (is_row)
+    merge_spans(parts + (static_cast<size_t>(b) * (k + 1) + lane) * spans, spans, best, bi,
+                flags);
   const bool row_bad = is_row && ((flags & 1) || !(flags & 2));
   int tok = 0;
   bool tok_bad = false;
@@ -166,15 +192,8 @@ __global__ __launch_bounds__(64) void tree_decide_kernel(
   int bi = V;
   int flags = 0;
   if (is_row) {
-    const CoupledPartial* p = parts + (static_cast<size_t>(b) * (n + 1) + lane) * spans;
-    for (int s = 0; s < spans; ++s) {
-      const CoupledPartial q = p[s];
-      if (better(q.score, q.index, best, bi)) {
-        best = q.score;
-        bi = q.index;
-      }
-      flags |= q.flags;
-    }
+    merge_spans(parts + (static_cast<size_t>(b) * (n + 1) + lane) * spans, spans, best, bi,
+                flags);
     choice[lane] = bi;
   }
   const bool row_bad = is_row && ((flags & 1) || !(flags & 2));

@@ -19,6 +19,10 @@ Workload shapes and distributions:
 * Accept inputs: draft logits N(0, sd); target = draft + N(0, sigma) noise
   (with an extra independent target row for the bonus position); draft
   tokens sampled from the draft distribution with the Gumbel-max trick.
+* LM-head verify: hidden rows N(0, 0.15^2) in bf16 (with the W4 weights
+  above the logits then have a standard deviation near 2, as the accept
+  inputs); draft logits N(0, 2) independent of the target; draft tokens
+  uniform over the vocabulary (so p/q spreads on both sides of 1).
 * Draft trees: node j hangs under node j - 1 with probability `chain`, else
   under a uniform pick of the root or an earlier node; target rows are
   N(0, sd) with one planted token per row lifted by 12 sd; a node's token is
@@ -57,10 +61,10 @@ def w8_matrix(N, K, seed, device="cpu"):
     return codes, scales
 
 
-def activations(m, K, seed, device="cpu"):
-    """bf16 [m, K] ~ N(0, 1)."""
+def activations(m, K, seed, device="cpu", scale=1.0):
+    """bf16 [m, K] ~ N(0, scale^2)."""
     g = _gen(seed, device)
-    return torch.randn((m, K), generator=g, device=device).to(torch.bfloat16)
+    return (torch.randn((m, K), generator=g, device=device) * scale).to(torch.bfloat16)
 
 
 def outlier_activations(m, K, seed, device="cpu", frac=0.01, factor=50.0):
@@ -141,3 +145,12 @@ def tree_inputs(B, n, V, seed, chain=0.7, agree=0.8, sd=2.0, device="cpu"):
     hit = torch.rand((B, n), generator=g, device=device) < agree
     tokens = torch.where(hit, follow, other)
     return target.contiguous(), tokens.to(torch.int32), parents.to(torch.int32)
+
+
+def lm_head_drafts(B, k, V, seed, sd=2.0, device="cpu"):
+    """Draft side of an LM-head verify: (draft logits fp32 [B, k, V] ~ N(0, sd),
+    draft tokens int32 [B, k] uniform over the vocabulary)."""
+    g = _gen(seed, device)
+    draft = torch.randn((B, k, V), generator=g, device=device) * sd
+    tokens = torch.randint(0, V, (B, k), generator=g, device=device, dtype=torch.int32)
+    return draft, tokens
