@@ -115,7 +115,7 @@ def main():
     }
     with open(a.out + ".json", "w") as f:
         json.dump(out, f, indent=1)
-    L = [f"# {a.title}", "", "Commands (run from /tmp with TMPDIR=/tmp; one PMC pass per run):", "",
+    L = [f"# {a.title}", "", "Commands (run from the repository root with TMPDIR=/tmp; one PMC pass per run):", "",
          "```", a.command.strip(), "```", "",
          "## Kernel trace (rocprofv3 --kernel-trace --stats), top kernels", "",
          "| kernel | calls | avg us | total us | % |", "|---|---:|---:|---:|---:|"]
