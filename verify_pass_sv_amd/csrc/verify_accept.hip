@@ -15,9 +15,11 @@
 //             sv_verify_accept_stats: for the target rows the wave merges the
 //             (max, sum) pairs of 64 logits that the vocabulary projection's
 //             epilogue wrote, instead of reading the logits.
-//  2. decide  one workgroup per (trial, residual share): merges the trial's
-//             partials into log-sum-exp values (staged in LDS, several threads
-//             per row, fixed order), evaluates p_i(d_i), q_i(d_i), draws the
+//  2. decide  one workgroup per (trial, residual share): fetches the draft
+//             tokens' two logits first (their latency overlaps what follows),
+//             merges the trial's partials into log-sum-exp values (all loads
+//             in flight at once, staged in LDS, several threads per row, fixed
+//             order), evaluates p_i(d_i), q_i(d_i), draws the
 //             Philox uniforms and takes the accept decisions with one wave
 //             ballot (first rejection = first zero bit), then sums the
 //             residual weights max(0, p_r - q_r) (or p_k for the bonus) of its
@@ -98,7 +100,7 @@ __device__ __forceinline__ void stat_merge(float& m, float& s, float m2, float s
 //  * Residual: the vocabulary is cut into blocks of kBlk floats; block
 //    totals, and inside a block 16 groups of 16 thread ranges of 8 floats,
 //    are summed in one fixed order everywhere, so the inverse-CDF search of
-//    kernel 3 walks exactly the sums that kernel 2 produced.
+//    the selection walks exactly the sums that kernel 2 produced.
 constexpr int kBatch = 2048;                    // floats per wave per statistics batch
 constexpr int kMaxC1 = 80;                      // statistics spans per row
 constexpr int kBlk = 2048;                      // floats per residual block
@@ -317,16 +319,41 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
   const int R = 2 * k + 1;
   const int tid = threadIdx.x;
 
-  // 1. the trial's R x C1 statistics partials -> LDS (coalesced)
+  // 0./1. The trial's R x C1 statistics partials -> LDS (coalesced), and for
+  //    wave 0 the draft token of position tid with its two logits.  Loads go
+  //    out in the order token, partials, logits (the logits need the token),
+  //    and every load of a thread before its first LDS store: the partials
+  //    cost one memory latency and the logits overlap the merge below.
+  const bool has_draft = tid < k;
+  int tok = 0;
+  bool tok_bad = false;
+  float tl = 0.f, dl = 0.f;
+  if (has_draft) tok = toks[static_cast<size_t>(b) * k + tid];
   {
-    const StatPartial* pp = part + static_cast<size_t>(b) * R * C1;
+    constexpr int kPer = ((2 * SV_MAX_ROWS + 1) * kMaxC1 + kThreads - 1) / kThreads;
+    const int4* pp = reinterpret_cast<const int4*>(part + static_cast<size_t>(b) * R * C1);
     const int n = R * C1;
-#pragma unroll 4
-    for (int e = tid; e < n; e += kThreads) {
-      const StatPartial q = pp[e];
-      pm[e] = q.m;
-      ps[e] = q.s;
-      pb[e] = q.bad;
+    int4 q[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + u * kThreads;
+      if (e < n) q[u] = pp[e];
+    }
+    if (has_draft) {
+      tok_bad = tok < 0 || tok >= V;
+      if (!tok_bad) {
+        tl = tgt[(static_cast<size_t>(b) * (k + 1) + tid) * V + tok];
+        dl = dft[(static_cast<size_t>(b) * k + tid) * V + tok];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + u * kThreads;
+      if (e < n) {
+        pm[e] = __int_as_float(q[u].x);
+        ps[e] = __int_as_float(q[u].y);
+        pb[e] = q[u].z;
+      }
     }
   }
   __syncthreads();
@@ -340,6 +367,7 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
     float m = -INFINITY;
     int bad = 0;
     if (own) {
+#pragma unroll 8
       for (int i = sub; i < C1; i += TPR) {
         m = fmaxf(m, pm[j * C1 + i]);
         bad |= pb[j * C1 + i];
@@ -361,6 +389,7 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
       const float mr = row_m[j];
       float sum = 0.f;
       if (mr != -INFINITY)
+#pragma unroll 8
         for (int i = sub; i < C1; i += TPR)
           sum += ps[j * C1 + i] * exp2_fast((pm[j * C1 + i] - mr) * kLog2e);
       red_m[tid] = sum;
@@ -380,13 +409,6 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
   // 3. decisions (wave 0): accept iff u_i q_i(d_i) < p_i(d_i), first rejection
   if (tid < 64) {
     const int i = tid;
-    const bool has_draft = i < k;
-    int tok = 0;
-    bool tok_bad = false;
-    if (has_draft) {
-      tok = toks[static_cast<size_t>(b) * k + i];
-      tok_bad = tok < 0 || tok >= V;
-    }
     const bool row_bad = (i < R && bad_sh[i]) || (i + 64 < R && bad_sh[i + 64]);
     const bool any_tok_bad = __any(tok_bad);
     const bool any_row_bad = __any(row_bad);
@@ -400,8 +422,6 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
       const float u = sv_u24(ctr[0]);
       u2 = sv_u24(ctr[1]);
       if (has_draft && status == 0) {
-        const float tl = tgt[(static_cast<size_t>(b) * (k + 1) + i) * V + tok];
-        const float dl = dft[(static_cast<size_t>(b) * k + i) * V + tok];
         p = expf(tl - lse_sh[i]);
         q = expf(dl - lse_sh[k + 1 + i]);
         accepted = u * q < p;
