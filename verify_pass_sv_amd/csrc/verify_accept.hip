@@ -10,16 +10,17 @@
 // Two launches on the caller's stream:
 //  1. stats   one wave per (trial, row, vocabulary span): max and sum of exp
 //             over a span, with all loads of a 2048-float batch in flight
-//             before any is used -> partial (max, sum, invalid flag).  It also
+//             before any is used; the workgroup's 4 spans are merged into one
+//             partial (max, sum, invalid flag, and the row's logit at its
+//             draft token when the token lies in those spans).  It also
 //             zeroes the per-trial completion counters of launch 2.
 //             sv_verify_accept_stats: for the target rows the wave merges the
 //             (max, sum) pairs of 64 logits that the vocabulary projection's
 //             epilogue wrote, instead of reading the logits.
-//  2. decide  one workgroup per (trial, residual share): fetches the draft
-//             tokens' two logits first (their latency overlaps what follows),
-//             merges the trial's partials into log-sum-exp values (all loads
-//             in flight at once, staged in LDS, several threads per row, fixed
-//             order), evaluates p_i(d_i), q_i(d_i), draws the
+//  2. decide  one workgroup per (trial, residual share): merges the trial's
+//             partials into log-sum-exp values (all loads in flight at once,
+//             staged in LDS, 4 lanes per row, fixed order), evaluates
+//             p_i(d_i), q_i(d_i) from the recorded token logits, draws the
 //             Philox uniforms and takes the accept decisions with one wave
 //             ballot (first rejection = first zero bit), then sums the
 //             residual weights max(0, p_r - q_r) (or p_k for the bonus) of its
@@ -28,8 +29,9 @@
 //             workgroup of a trial reaches the same decision; workgroup 0
 //             writes the per-trial outputs.  The last workgroup of the trial
 //             to finish (a device-scope counter) runs the inverse-CDF
-//             selection over the block totals and replays the same sums inside
-//             the chosen block, so the chosen bin always exists.
+//             selection over the running sums of the block totals (formed in
+//             order, searched by a wave ballot) and replays the same sums
+//             inside the chosen block, so the chosen bin always exists.
 #include "sv_common.h"
 #include "sv_philox.h"
 
@@ -45,7 +47,8 @@ struct StatPartial {
   float m;
   float s;
   int bad;
-  int pad;
+  float tok_logit;   // the row's logit at its draft token if the token lies in
+                     // this span, else 0 (no draft token: the bonus row)
 };
 
 struct Decision {
@@ -58,6 +61,28 @@ struct Decision {
 };
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Reductions over the 4 lanes of a quad, in VALU latency (a lane shuffle
+// goes through the LDS pipe): the DPP quad permutes [1,0,3,2] and [2,3,0,1].
+// Every lane of the quad ends with the same bits (binary32 max and add are
+// commutative, and each step pairs the same two values).
+template <int CTRL>
+__device__ __forceinline__ int dpp_quad(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E;
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __int_as_float(dpp_quad<kDppXor1>(__float_as_int(v))));
+  return fmaxf(v, __int_as_float(dpp_quad<kDppXor2>(__float_as_int(v))));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __int_as_float(dpp_quad<kDppXor1>(__float_as_int(v)));
+  return v + __int_as_float(dpp_quad<kDppXor2>(__float_as_int(v)));
+}
+__device__ __forceinline__ int quad_or(int v) {
+  v |= dpp_quad<kDppXor1>(v);
+  return v | dpp_quad<kDppXor2>(v);
+}
 
 // Online softmax statistics: running max m and sum s of exp(v - m).
 __device__ __forceinline__ void stat_add4(float& m, float& s, int& bad, float4 v) {
@@ -96,13 +121,17 @@ __device__ __forceinline__ void stat_merge(float& m, float& s, float m2, float s
 
 // Vocabulary tiling shared by the kernels.
 //  * Statistics: each row is cut into C1 <= kMaxC1 spans of whole 2048-float
-//    batches; one wave reduces one (trial, row, span).
+//    batches; one wave reduces one (trial, row, span), and a workgroup of
+//    kStatsWaves waves merges its spans into one partial (CG per row).
 //  * Residual: the vocabulary is cut into blocks of kBlk floats; block
 //    totals, and inside a block 16 groups of 16 thread ranges of 8 floats,
 //    are summed in one fixed order everywhere, so the inverse-CDF search of
 //    the selection walks exactly the sums that kernel 2 produced.
 constexpr int kBatch = 2048;                    // floats per wave per statistics batch
 constexpr int kMaxC1 = 80;                      // statistics spans per row
+// partials per row: one per statistics workgroup of kStatsWaves spans
+constexpr int kMaxCG = (kMaxC1 + kStatsWaves - 1) / kStatsWaves;
+__host__ __device__ inline int stat_groups(int C1) { return (C1 + kStatsWaves - 1) / kStatsWaves; }
 constexpr int kBlk = 2048;                      // floats per residual block
 constexpr int kPerThread = kBlk / kThreads;     // 8
 constexpr int kGroups = 16;                     // thread groups per block
@@ -134,7 +163,8 @@ __host__ inline WsLayout ws_layout(int B, int k, int V) {
   WsLayout L;
   const size_t R = 2 * static_cast<size_t>(k) + 1;
   L.partial_off = 0;
-  L.decision_off = up(static_cast<size_t>(B) * R * stat_spans(V) * sizeof(StatPartial));
+  L.decision_off =
+      up(static_cast<size_t>(B) * R * stat_groups(stat_spans(V)) * sizeof(StatPartial));
   L.total_off = L.decision_off + up(static_cast<size_t>(B) * sizeof(Decision));
   L.done_off = L.total_off + up(static_cast<size_t>(B) * resid_blocks(V) * sizeof(double));
   L.bytes = L.done_off + up(static_cast<size_t>(B) * sizeof(int));
@@ -153,29 +183,42 @@ __device__ __forceinline__ const float* row_ptr(const float* tgt, const float* d
 template <bool VEC, bool PRE>
 __global__ __launch_bounds__(64 * kStatsWaves) void stats_kernel(
     const float* __restrict__ tgt, const float* __restrict__ dft,
-    const float2* __restrict__ tstats, int B, int k, int V, int C1, int span,
-    StatPartial* __restrict__ part, int* __restrict__ done) {
+    const float2* __restrict__ tstats, const int32_t* __restrict__ toks, int B, int k, int V,
+    int CG, int span, StatPartial* __restrict__ part, int* __restrict__ done) {
   // the per-trial completion counters of kernel 2 start at zero every call
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < B; i += blockDim.x) done[i] = 0;
+  __shared__ StatPartial wp[kStatsWaves];
   const int lane = threadIdx.x & 63;
-  const long long item = static_cast<long long>(blockIdx.x) * kStatsWaves + (threadIdx.x >> 6);
+  const int w = threadIdx.x >> 6;
+  // workgroup = (trial, row, group of kStatsWaves spans); the grid is exact,
+  // and a span past the row's last (c >= C1) is empty
   const int R = 2 * k + 1;
-  if (item >= static_cast<long long>(B) * R * C1) return;
-  const int c = static_cast<int>(item % C1);
-  const long long br = item / C1;
+  const int g = static_cast<int>(blockIdx.x % CG);
+  const long long br = blockIdx.x / CG;
   const int j = static_cast<int>(br % R);
   const int b = static_cast<int>(br / R);
+  const int c = g * kStatsWaves + w;
   const float* row = row_ptr(tgt, dft, b, j, k, V);
   const int lo = min(V, c * span);
   const int hi = min(V, lo + span);
+  // the draft token of this row (target row i < k and draft row i share d_i;
+  // the bonus row k has none); its logit is recorded by the wave whose span
+  // holds it, so the decide launch reads it with the statistics
+  const int ti = j < k ? j : j - k - 1;
+  const int tok = j == k ? -1 : toks[static_cast<size_t>(b) * k + ti];
+  const bool tok_here = tok >= lo && tok < hi;
+  float tok_logit = 0.f;
   float m = -INFINITY, s = 0.f;
   int bad = 0;
   if (PRE && j <= k) {
-    // the span's pairs of 64 logits (span and lo are multiples of 64)
+    if (tok_here) tok_logit = row[tok];
+    // the span's pairs of 64 logits (span and lo are multiples of 64; an
+    // empty span past the row's end has lo = hi = V and reads none)
     const int G = (V + 63) / 64;
     const float2* st = tstats + (static_cast<size_t>(b) * (k + 1) + j) * G;
-    for (int g = lo / 64 + lane; g < (hi + 63) / 64; g += 64) {
+    const int g_end = lo < hi ? (hi + 63) / 64 : 0;
+    for (int g = lo / 64 + lane; g < g_end; g += 64) {
       const float2 pr = st[g];
       bad |= pr.y != pr.y;
       if (pr.y == pr.y) stat_merge(m, s, pr.x, pr.y);
@@ -202,6 +245,16 @@ __global__ __launch_bounds__(64 * kStatsWaves) void stats_kernel(
         v[i] = e < hi ? row[e] : -INFINITY;
       }
     }
+    if (tok_here && tok >= base && tok < base + kBatch) {
+      // lane and register holding the token's logit (wave-uniform branch)
+      const int off = tok - base;
+      const int want = VEC ? 4 * (off >> 8) + (off & 3) : off >> 6;
+      const int src = VEC ? (off >> 2) & 63 : off & 63;
+      float val = v[0];
+#pragma unroll
+      for (int i = 1; i < (VEC ? 4 * NV : NV); ++i) val = i == want ? v[i] : val;
+      tok_logit = __shfl(val, src);
+    }
     float vm = -INFINITY;
 #pragma unroll
     for (int i = 0; i < (VEC ? 4 * NV : NV); ++i) {
@@ -225,7 +278,22 @@ __global__ __launch_bounds__(64 * kStatsWaves) void stats_kernel(
     bad |= __shfl_xor(bad, off);
     stat_merge(m, s, m2, s2);
   }
-  if (lane == 0) part[item] = StatPartial{m, s, bad, 0};
+  // the workgroup's kStatsWaves partials merged in wave order; the token
+  // logit is the one of the wave whose span holds the token
+  if (lane == 0) wp[w] = StatPartial{m, s, bad, tok_logit};
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = wp[0].m, S = wp[0].s;
+    int bd = wp[0].bad;
+#pragma unroll
+    for (int u = 1; u < kStatsWaves; ++u) {
+      stat_merge(M, S, wp[u].m, wp[u].s);
+      bd |= wp[u].bad;
+    }
+    const int ut = tok >= 0 ? tok / span - g * kStatsWaves : -1;
+    const float tl = ut >= 0 && ut < kStatsWaves ? wp[ut].tok_logit : 0.f;
+    part[static_cast<size_t>(blockIdx.x)] = StatPartial{M, S, bd, tl};
+  }
 }
 
 // Residual / bonus weight of one vocabulary entry from its two logits
@@ -296,19 +364,18 @@ __device__ void select_trial(const float* __restrict__ tgt, const float* __restr
 // outputs.  Then each workgroup sums its share of the residual blocks.
 __global__ __launch_bounds__(kThreads) void decide_kernel(
     const float* __restrict__ tgt, const float* __restrict__ dft, const int32_t* __restrict__ toks,
-    int B, int k, int V, int C1, int C2, unsigned int key0, unsigned int key1, unsigned int offset,
+    int B, int k, int V, int CG, int span, int C2, unsigned int key0, unsigned int key1,
+    unsigned int offset,
     const StatPartial* __restrict__ part, Decision* __restrict__ decs, double* __restrict__ totals,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_n_acc,
     int32_t* __restrict__ out_status, float* __restrict__ p_at, float* __restrict__ q_at,
     float* __restrict__ lse_out, int* __restrict__ done) {
-  __shared__ float pm[(2 * SV_MAX_ROWS + 1) * kMaxC1];
-  __shared__ float ps[(2 * SV_MAX_ROWS + 1) * kMaxC1];
-  __shared__ int pb[(2 * SV_MAX_ROWS + 1) * kMaxC1];
+  __shared__ float pm[(2 * SV_MAX_ROWS + 1) * kMaxCG];
+  __shared__ float ps[(2 * SV_MAX_ROWS + 1) * kMaxCG];
+  __shared__ int pb[(2 * SV_MAX_ROWS + 1) * kMaxCG];
+  __shared__ float pl[(2 * SV_MAX_ROWS + 1) * kMaxCG];
   __shared__ float lse_sh[2 * SV_MAX_ROWS + 1];
-  __shared__ float row_m[2 * SV_MAX_ROWS + 1];
   __shared__ int bad_sh[2 * SV_MAX_ROWS + 1];
-  __shared__ float red_m[kThreads];
-  __shared__ int red_b[kThreads];
   __shared__ Decision dec;
   __shared__ float st[kBlk], sd[kBlk];
   __shared__ double tsum[kThreads];
@@ -319,32 +386,22 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
   const int R = 2 * k + 1;
   const int tid = threadIdx.x;
 
-  // 0./1. The trial's R x C1 statistics partials -> LDS (coalesced), and for
-  //    wave 0 the draft token of position tid with its two logits.  Loads go
-  //    out in the order token, partials, logits (the logits need the token),
-  //    and every load of a thread before its first LDS store: the partials
-  //    cost one memory latency and the logits overlap the merge below.
+  // 1. The trial's R x CG statistics partials -> LDS (coalesced), each
+  //    thread's loads all issued before its first store (one memory
+  //    latency); wave 0 also loads the draft tokens.  The tokens' logits come
+  //    with the partials (the statistics launch recorded them).
   const bool has_draft = tid < k;
   int tok = 0;
-  bool tok_bad = false;
-  float tl = 0.f, dl = 0.f;
   if (has_draft) tok = toks[static_cast<size_t>(b) * k + tid];
   {
-    constexpr int kPer = ((2 * SV_MAX_ROWS + 1) * kMaxC1 + kThreads - 1) / kThreads;
-    const int4* pp = reinterpret_cast<const int4*>(part + static_cast<size_t>(b) * R * C1);
-    const int n = R * C1;
+    constexpr int kPer = ((2 * SV_MAX_ROWS + 1) * kMaxCG + kThreads - 1) / kThreads;
+    const int4* pp = reinterpret_cast<const int4*>(part + static_cast<size_t>(b) * R * CG);
+    const int n = R * CG;
     int4 q[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int e = tid + u * kThreads;
       if (e < n) q[u] = pp[e];
-    }
-    if (has_draft) {
-      tok_bad = tok < 0 || tok >= V;
-      if (!tok_bad) {
-        tl = tgt[(static_cast<size_t>(b) * (k + 1) + tid) * V + tok];
-        dl = dft[(static_cast<size_t>(b) * k + tid) * V + tok];
-      }
     }
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
@@ -353,55 +410,44 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
         pm[e] = __int_as_float(q[u].x);
         ps[e] = __int_as_float(q[u].y);
         pb[e] = q[u].z;
+        pl[e] = __int_as_float(q[u].w);
       }
     }
   }
+  const bool tok_bad = has_draft && (tok < 0 || tok >= V);
   __syncthreads();
-  // 2. merge each row's spans: TPR threads per row take every TPR-th span;
-  //    the row maximum first, then the sum rescaled to it, each combined
-  //    across the row's threads in a fixed order
+  // 2. merge each row's partials: 4 lanes (one quad) per row, 64 rows per
+  //    round of the workgroup, lane sub taking partials sub, sub + 4, ..; the
+  //    row maximum first, then the sum rescaled to it, each combined over the
+  //    quad in a fixed order
   {
-    const int TPR = R >= kThreads ? 1 : kThreads / R;
-    const int j = tid / TPR, sub = tid - j * TPR;
-    const bool own = j < R;
-    float m = -INFINITY;
-    int bad = 0;
-    if (own) {
-#pragma unroll 8
-      for (int i = sub; i < C1; i += TPR) {
-        m = fmaxf(m, pm[j * C1 + i]);
-        bad |= pb[j * C1 + i];
+    const int sub = tid & 3;
+    for (int j0 = 0; j0 < R; j0 += kThreads / 4) {
+      const int j = j0 + (tid >> 2);
+      const bool own = j < R;
+      float m = -INFINITY;
+      int bad = 0;
+      if (own) {
+#pragma unroll 5
+        for (int i = sub; i < CG; i += 4) {
+          m = fmaxf(m, pm[j * CG + i]);
+          bad |= pb[j * CG + i];
+        }
       }
-      red_m[tid] = m;
-      red_b[tid] = bad;
-    }
-    __syncthreads();
-    if (own && sub == 0) {
-      for (int t = 1; t < TPR; ++t) {
-        m = fmaxf(m, red_m[tid + t]);
-        bad |= red_b[tid + t];
+      m = quad_max(m);
+      bad = quad_or(bad);
+      float sum = 0.f;
+      if (own && m != -INFINITY) {
+#pragma unroll 5
+        for (int i = sub; i < CG; i += 4)
+          sum += ps[j * CG + i] * exp2_fast((pm[j * CG + i] - m) * kLog2e);
       }
-      row_m[j] = m;
-      bad_sh[j] = bad;
-    }
-    __syncthreads();
-    if (own) {
-      const float mr = row_m[j];
-      float sum = 0.f;
-      if (mr != -INFINITY)
-#pragma unroll 8
-        for (int i = sub; i < C1; i += TPR)
-          sum += ps[j * C1 + i] * exp2_fast((pm[j * C1 + i] - mr) * kLog2e);
-      red_m[tid] = sum;
-    }
-    __syncthreads();
-    if (own && sub == 0) {
-      const float mr = row_m[j];
-      float sum = 0.f;
-      for (int t = 0; t < TPR; ++t) sum += red_m[tid + t];
-      const int bd = bad_sh[j] | (mr == -INFINITY) | !(sum > 0.f);
-      lse_sh[j] = bd ? NAN : mr + logf(sum);
-      bad_sh[j] = bd;
+      sum = quad_sum(sum);
+      if (own && sub == 0) {
+        const int bd = bad | (m == -INFINITY) | !(sum > 0.f);
+        lse_sh[j] = bd ? NAN : m + logf(sum);
+        bad_sh[j] = bd;
+      }
     }
   }
   __syncthreads();
@@ -422,6 +468,9 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
       const float u = sv_u24(ctr[0]);
       u2 = sv_u24(ctr[1]);
       if (has_draft && status == 0) {
+        const int ct = tok / span / kStatsWaves;   // the partial whose spans hold the token
+        const float tl = pl[i * CG + ct];
+        const float dl = pl[(k + 1 + i) * CG + ct];
         p = expf(tl - lse_sh[i]);
         q = expf(dl - lse_sh[k + 1 + i]);
         accepted = u * q < p;
@@ -508,8 +557,8 @@ __device__ void select_trial(const float* __restrict__ tgt, const float* __restr
                              const double* __restrict__ totals,
                              int32_t* __restrict__ out_tokens, float* st, float* sd,
                              double* tsum, double* gsum, double* btot_p, double* dyn_tot) {
-  __shared__ double sh_S, sh_pc;
-  __shared__ int sh_blk, sh_usep;
+  __shared__ double sh_S, sh_pc, sh_thr;
+  __shared__ int sh_blk;
   double& btot = *btot_p;
   const int tid = threadIdx.x;
   const int r = dec.n_acc;
@@ -519,19 +568,37 @@ __device__ void select_trial(const float* __restrict__ tgt, const float* __restr
   const int nb = resid_blocks(V);
   const double* T = totals + static_cast<size_t>(b) * nb;
 
-  // block totals -> LDS in one parallel pass (dyn_tot), then summed in order
+  // Block totals -> LDS (dyn_tot), then replaced in place by their running
+  // sums in vocabulary order.  Thread 0 adds them one after another, exactly
+  // the additions of a sequential walk, with its LDS loads batched 8 at a time.
+  auto running_sums = [&]() {
+    if (tid == 0) {
+      double P = 0.0;
+      int i = 0;
+      for (; i + 8 <= nb; i += 8) {
+        double t8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t8[u] = dyn_tot[i + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          P += t8[u];
+          dyn_tot[i + u] = P;
+        }
+      }
+      for (; i < nb; ++i) {
+        P += dyn_tot[i];
+        dyn_tot[i] = P;
+      }
+      sh_S = P;
+    }
+    __syncthreads();
+  };
   for (int i = tid; i < nb; i += kThreads) dyn_tot[i] = T[i];
   __syncthreads();
-  if (tid == 0) {
-    double S = 0.0;
-    for (int i = 0; i < nb; ++i) S += dyn_tot[i];
-    sh_S = S;
-    sh_usep = !(S > 0.0);
-  }
-  __syncthreads();
+  running_sums();
   // Rounding left no residual mass: sample from p_r instead, with block
   // totals recomputed here (a rare path, so one block at a time).
-  const bool usep = sh_usep != 0;
+  const bool usep = !(sh_S > 0.0);
   if (usep) {
     bonus = true;
     pd = nullptr;
@@ -544,30 +611,31 @@ __device__ void select_trial(const float* __restrict__ tgt, const float* __restr
       if (tid == 0) dyn_tot[blk] = btot;
       __syncthreads();
     }
+    running_sums();
   }
-  T = dyn_tot;
-  if (tid == 0) {
-    double S = 0.0;
-    for (int i = 0; i < nb; ++i) S += T[i];
-    const double thr = dec.u2 * S;
-    double P = 0.0, pc = 0.0;
-    int bs = nb - 1;
-    for (int i = 0; i < nb; ++i) {
-      const double nxt = P + T[i];
-      if (nxt > thr) {
-        bs = i;
-        pc = P;
+  // The first block whose running sum exceeds thr = u' S (wave 0 ballots over
+  // 64 blocks at a time); pc = the running sum before it.  None: the last
+  // block, with pc = S.
+  if (tid < 64) {
+    const double S = sh_S;
+    const double thr_w = dec.u2 * S;
+    int bs = -1;
+    for (int c0 = 0; c0 < nb; c0 += 64) {
+      const int i = c0 + tid;
+      const unsigned long long hit = __ballot(i < nb && dyn_tot[i] > thr_w);
+      if (hit) {
+        bs = c0 + __ffsll(static_cast<long long>(hit)) - 1;
         break;
       }
-      P = nxt;
-      pc = P;
     }
-    sh_S = thr;
-    sh_blk = bs;
-    sh_pc = pc;
+    if (tid == 0) {
+      sh_thr = thr_w;
+      sh_blk = bs < 0 ? nb - 1 : bs;
+      sh_pc = bs < 0 ? S : (bs > 0 ? dyn_tot[bs - 1] : 0.0);
+    }
   }
   __syncthreads();
-  const double thr = sh_S, pc = sh_pc;
+  const double thr = sh_thr, pc = sh_pc;
   const int blk = sh_blk;
   const int n_valid = min(kBlk, V - blk * kBlk);
   stage_block(pt, pd, V, blk, st, sd);
@@ -578,35 +646,51 @@ __device__ void select_trial(const float* __restrict__ tgt, const float* __restr
   if (tid == 0) {
     // groups, then threads inside the group, then the thread's 8 entries;
     // every comparison is pc + (group prefix + (thread prefix + run)), the
-    // association under which the block total was formed
+    // association under which the block total was formed.  The sums of a
+    // level are read into registers first; the walk stops updating at the
+    // first crossing.
     int gs = kGroups - 1;
     double qg = 0.0;
     {
+      double gv[kGroups];
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) gv[g] = gsum[g];
       double Q = 0.0;
+      bool found = false;
+#pragma unroll
       for (int g = 0; g < kGroups; ++g) {
-        const double nxt = Q + gsum[g];
-        if (pc + nxt > thr) {
+        const double nxt = Q + gv[g];
+        if (!found && pc + nxt > thr) {
           gs = g;
           qg = Q;
-          break;
+          found = true;
         }
-        Q = nxt;
-        qg = Q;
+        if (!found) {
+          Q = nxt;
+          qg = Q;
+        }
       }
     }
     int ts = gs * kGroupThreads + kGroupThreads - 1;
     double qt = 0.0;
     {
+      double tv[kGroupThreads];
+#pragma unroll
+      for (int t = 0; t < kGroupThreads; ++t) tv[t] = tsum[gs * kGroupThreads + t];
       double Q = 0.0;
+      bool found = false;
+#pragma unroll
       for (int t = 0; t < kGroupThreads; ++t) {
-        const double nxt = Q + tsum[gs * kGroupThreads + t];
-        if (pc + (qg + nxt) > thr) {
+        const double nxt = Q + tv[t];
+        if (!found && pc + (qg + nxt) > thr) {
           ts = gs * kGroupThreads + t;
           qt = Q;
-          break;
+          found = true;
         }
-        Q = nxt;
-        qt = Q;
+        if (!found) {
+          Q = nxt;
+          qt = Q;
+        }
       }
     }
     const int a = ts * kPerThread;
@@ -673,9 +757,9 @@ sv_status verify_accept(const float* target_logits, const float* target_stats,
   int* done = reinterpret_cast<int*>(ws + L.done_off);
   const int C1 = stat_spans(V);
   const int span = stat_span_len(V, C1);
+  const int CG = stat_groups(C1);
   const int C2 = resid_wgs(B, V);
-  const long long items = static_cast<long long>(B) * (2 * k + 1) * C1;
-  const long long blocks1 = (items + kStatsWaves - 1) / kStatsWaves;
+  const long long blocks1 = static_cast<long long>(B) * (2 * k + 1) * CG;
   if (blocks1 >= (1LL << 31) || static_cast<long long>(B) * C2 >= (1LL << 31))
     return SV_ERR_INVALID_ARG;
   // dynamic LDS of kernel 2: block totals of the selecting workgroup
@@ -685,23 +769,23 @@ sv_status verify_accept(const float* target_logits, const float* target_stats,
   const float2* tst = reinterpret_cast<const float2*>(target_stats);
   if (tst && V % 4 == 0)
     hipLaunchKernelGGL((stats_kernel<true, true>), dim3(static_cast<unsigned>(blocks1)),
-                       dim3(64 * kStatsWaves), 0, stream, target_logits, draft_logits, tst, B, k,
-                       V, C1, span, part, done);
+                       dim3(64 * kStatsWaves), 0, stream, target_logits, draft_logits, tst,
+                       draft_tokens, B, k, V, CG, span, part, done);
   else if (tst)
     hipLaunchKernelGGL((stats_kernel<false, true>), dim3(static_cast<unsigned>(blocks1)),
-                       dim3(64 * kStatsWaves), 0, stream, target_logits, draft_logits, tst, B, k,
-                       V, C1, span, part, done);
+                       dim3(64 * kStatsWaves), 0, stream, target_logits, draft_logits, tst,
+                       draft_tokens, B, k, V, CG, span, part, done);
   else if (V % 4 == 0)
     hipLaunchKernelGGL((stats_kernel<true, false>), dim3(static_cast<unsigned>(blocks1)),
-                       dim3(64 * kStatsWaves), 0, stream, target_logits, draft_logits, tst, B, k,
-                       V, C1, span, part, done);
+                       dim3(64 * kStatsWaves), 0, stream, target_logits, draft_logits, tst,
+                       draft_tokens, B, k, V, CG, span, part, done);
   else
     hipLaunchKernelGGL((stats_kernel<false, false>), dim3(static_cast<unsigned>(blocks1)),
-                       dim3(64 * kStatsWaves), 0, stream, target_logits, draft_logits, tst, B, k,
-                       V, C1, span, part, done);
+                       dim3(64 * kStatsWaves), 0, stream, target_logits, draft_logits, tst,
+                       draft_tokens, B, k, V, CG, span, part, done);
   SV_LAUNCH_CHECK();
   hipLaunchKernelGGL(decide_kernel, dim3(static_cast<unsigned>(B) * C2), dim3(kThreads), dyn,
-                     stream, target_logits, draft_logits, draft_tokens, B, k, V, C1, C2,
+                     stream, target_logits, draft_logits, draft_tokens, B, k, V, CG, span, C2,
                      static_cast<unsigned int>(seed & 0xFFFFFFFFu),
                      static_cast<unsigned int>(seed >> 32), offset, part, decs, totals,
                      out_tokens, out_n_acc, out_status, p_at, q_at, lse, done);
