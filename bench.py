@@ -19,6 +19,9 @@ Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 200] [--quick]
        python bench.py --profile-pass [--format w4|w8|w4_i8] [--k K]
                         (copy kernel, read probe and two executor passes, for
                          rocprofv3 counters)
+       python bench.py --profile-accept [--k K] [--trials B]
+                        (copy kernel and accept calls at V = 152000, for
+                         rocprofv3 counters)
 """
 import argparse
 import json
@@ -169,6 +172,9 @@ def main():
                     help="weight path of --profile-pass")
     ap.add_argument("--profile-pass", action="store_true",
                     help="copy kernel + read probe + 2 eager W4 passes, then exit")
+    ap.add_argument("--profile-accept", action="store_true",
+                    help="copy kernel + eager sv_verify_accept calls (V=152000), then exit")
+    ap.add_argument("--trials", type=int, default=1, help="B of --profile-accept")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -182,6 +188,24 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     k = args.k
+
+    if args.profile_accept:
+        src = torch.empty(1 << 28, dtype=torch.uint8, device=dev).random_(0, 255)
+        dst = torch.empty_like(src)
+        dst.copy_(src)  # plain copy kernel of 256 MiB (counter scale reference)
+        B = args.trials
+        t, d, tk = synth.accept_inputs(B, k, VOCAB, seed=31 + B, sigma=1.0, device=dev)
+        out = {"tokens": torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+               "n_acc": torch.empty((B,), dtype=torch.int32, device=dev),
+               "status": torch.empty((B,), dtype=torch.int32, device=dev)}
+        ws = torch.empty(sv.sv_verify_accept_workspace_bytes(B, k, VOCAB), dtype=torch.uint8,
+                         device=dev)
+        calls = 20 if B == 1 else 4
+        for i in range(calls):
+            sv.sv_verify_accept(t, d, tk, seed=i, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        log(f"profile-accept: {calls} calls at B={B}, k={k}, V={VOCAB}")
+        return
     log(f"device {torch.cuda.get_device_name(0)}; building W4 stack")
     w4 = make_w4_stack(torch, synth, sv, dev)
     x_h = synth.activations(32, HIDDEN, seed=11, device=dev)

@@ -26,6 +26,8 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 # Sources whose change makes recorded counters stale, per kernel family.
 KERNEL_SOURCES = {
     "pass_kernel": ["csrc/pass.hip", "csrc/w4_packed_dev.h", "csrc/sv_common.h"],
+    "stats_kernel": ["csrc/verify_accept.hip", "csrc/sv_common.h", "csrc/sv_philox.h"],
+    "decide_kernel": ["csrc/verify_accept.hip", "csrc/sv_common.h", "csrc/sv_philox.h"],
 }
 
 
