@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 
 METRIC = ("verify-pass weight GB/s and drafted tokens/s at k=16, 9B-shape W4; accept µs")
 HBM_PEAK_GBPS = 8000.0
+BF16_DENSE_PEAK_TFLOPS = 2500.0
 LAYERS, HIDDEN, FFN, GROUP = 32, 4096, 12288, 64
 VOCAB = 152000
 
@@ -120,6 +121,20 @@ def recorded_traffic(name, k):
             "pass_kernel"):
         return None
     return rec.get("traffic_bytes")
+
+
+def recorded_counters(name):
+    """The committed rocprofv3 summary's counters for the pass kernel (dict),
+    or None when it was taken on other kernel sources."""
+    from verify_pass_sv_amd import rocprof_summary
+    path = os.path.join(ROOT, "profiles", name + ".json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != rocprof_summary.sources_sha256("pass_kernel"):
+        return None
+    return rec
 
 
 # --------------------------------------------------------------- cpu oracle --
@@ -352,6 +367,27 @@ def main():
                          "drafted_tok_s": round(kk / (ms * 1e-3), 1)}
         extra["w4_k_sweep"] = sweep
         extra["w4_latency_ratio_k32_over_k1"] = round(sweep[32]["pass_ms"] / sweep[1]["pass_ms"], 3)
+        # MFMA utilisation of the W4 pass at k = 16 and 32: the useful flops
+        # (2 k per weight) over the measured pass time against the dense bf16
+        # peak, and from the recorded counters the fraction of cycles the
+        # MFMA pipe was busy (SQ_VALU_MFMA_BUSY_CYCLES per SIMD over the
+        # active cycles GRBM_GUI_ACTIVE per XCD) with the clock they imply
+        n_weights = sum(N * K for layer in w4 for (_, N, K, *_r) in layer)
+        n_simd = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+        mfma = {}
+        for kk in (16, 32):
+            tf = 2.0 * kk * n_weights / (sweep[kk]["pass_ms"] * 1e-3) / 1e12
+            row = {"useful_TFLOPs": round(tf, 1),
+                   "frac_of_bf16_dense_peak": round(tf / BF16_DENSE_PEAK_TFLOPS, 4)}
+            rec = recorded_counters(f"w4_pass_9b_k{kk}")
+            if rec:
+                c = rec["counters"]
+                active = c["GRBM_GUI_ACTIVE"] / 8
+                row["mfma_busy_frac"] = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / n_simd / active, 4)
+                row["clock_GHz"] = round(active / (rec["avg_duration_us"] * 1e3), 3)
+                row["mfma_instructions"] = c["SQ_INSTS_MFMA"]
+            mfma[f"k{kk}"] = row
+        extra["w4_mfma"] = mfma
         log("int8 path")
         # int8 path: every activation row of the pass (4 inputs per layer, 41 or
         # 123 outlier channels x50) rotated by the block-4096 Hadamard and
