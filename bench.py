@@ -329,17 +329,26 @@ def main():
                          device=dev)
         ms, _ = time_graph(torch, lambda: sv.sv_verify_accept(t, d, tk, seed=0, out=out,
                                                               workspace=ws), 50, 5)
+        # host wall time of one eager call: launch through synchronize (median)
+        walls = []
+        for i in range(60):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            sv.sv_verify_accept(t, d, tk, seed=i, out=out, workspace=ws)
+            torch.cuda.synchronize()
+            walls.append(time.perf_counter() - t0)
         del t, d, tk
-        return ms * 1e3
+        return ms * 1e3, sorted(walls[10:])[len(walls[10:]) // 2] * 1e6
 
     log(f"step {ms_step:.3f} ms, pass {ms_pass:.3f} ms ({weight_gbps:.0f} GB/s); timing accept")
-    accept_us_b1 = accept_bench(1, 32)
-    accept_us_b64 = accept_bench(64, 32)
+    accept_us_b1, accept_host_us_b1 = accept_bench(1, 32)
+    accept_us_b64, _ = accept_bench(64, 32)
     accept_bytes = ((2 * 32 + 1) * VOCAB * 4 + 2 * VOCAB * 4)
     extra = {"weight_GBps": round(weight_gbps, 1),
              "weight_frac_of_8TBps": round(weight_gbps / HBM_PEAK_GBPS, 4),
              "pass_ms": round(ms_pass, 4), "pass_weight_bytes": pass_bytes,
              "accept_us_k32_B1": round(accept_us_b1, 2),
+             "accept_host_wall_us_k32_B1": round(accept_host_us_b1, 1),
              "accept_us_per_trial_k32_B64": round(accept_us_b64 / 64, 3),
              "accept_GBps_B64": round(64 * accept_bytes / (accept_us_b64 * 1e-6) / 1e9, 1)}
 
