@@ -137,6 +137,47 @@ def recorded_counters(name):
     return rec
 
 
+def int8_quant_error(torch, sv, synth, layer, k, dev):
+    """Relative error (Frobenius, over the layer's 4 products at k rows) of the
+    int8 path against the bf16 path, with and without the rotation.  The
+    stored 4-bit weights play the weights in the basis the activations are
+    quantized in (rotated offline when the activations are rotated), so:
+      with:    int8 path (sv_hadamard_i8 + sv_qgemm_w4_i8) vs sv_qgemm_w4 on
+               the rotated activations rounded to bf16;
+      without: per-token int8 of the raw activations + sv_qgemm_w4_i8 vs
+               sv_qgemm_w4 on the raw activations.
+    Torch forms only the measurement's baselines here (the rotation in
+    binary32, by the Sylvester matrix, and the unrotated quantization); both
+    products run in the library."""
+    B4 = 4096
+    idx = torch.arange(B4, device=dev)
+    pc = torch.zeros((B4, B4), dtype=torch.int64, device=dev)
+    a = idx[:, None] & idx[None, :]
+    for _ in range(12):                         # popcount(i & j) parity
+        pc ^= a & 1
+        a = a >> 1
+    H = (1 - 2 * pc).to(torch.float32) / 64.0   # orthonormal Sylvester matrix
+    num = {"with_rotation": 0.0, "without_rotation": 0.0}
+    den = {"with_rotation": 0.0, "without_rotation": 0.0}
+    for i, (name, N, K, c, s_, z, *_r) in enumerate(layer):
+        x = synth.outlier_activations(k, K, seed=900 + i, device=dev)[0]
+        signs = synth.hadamard_signs(K, seed=901 + i, device=dev)
+        xq, xs = sv.sv_hadamard_i8(x, signs, B4)
+        y_q = sv.sv_qgemm_w4_i8(xq, xs, c, s_, z)
+        xr = ((x.float() * signs.float()).view(k, K // B4, B4) @ H).view(k, K)
+        y_r = sv.sv_qgemm_w4(xr.to(torch.bfloat16), c, s_, z)
+        xf = x.float()
+        s0 = (xf.abs().amax(dim=1) / 127.0).clamp_min(1e-30)
+        xq0 = torch.round(xf / s0[:, None]).clamp(-127, 127).to(torch.int8)
+        y_q0 = sv.sv_qgemm_w4_i8(xq0, s0.contiguous(), c, s_, z)
+        y_0 = sv.sv_qgemm_w4(x, c, s_, z)
+        for key, (yq, yr) in (("with_rotation", (y_q, y_r)), ("without_rotation", (y_q0, y_0))):
+            num[key] += float(((yq - yr).double() ** 2).sum())
+            den[key] += float((yr.double() ** 2).sum())
+    torch.cuda.synchronize()
+    return {key: round((num[key] / den[key]) ** 0.5, 5) for key in num}
+
+
 # --------------------------------------------------------------- cpu oracle --
 def cpu_baseline(k=16):
     """The binary64 oracle on the host: one full layer of the W4 stack at k rows
@@ -442,6 +483,7 @@ def main():
                               "gemm_GBps": round(pass_bytes / (ms_i8g * 1e-3) / 1e9, 1),
                               "hadamard_ms_all_rows": round(ms_rot, 4),
                               "hadamard_rows": int((n_h + n_f) * k)}
+        extra["int8_path"]["quant_error"] = int8_quant_error(torch, sv, synth, w4[0], k, dev)
         del xo_h, xo_f
         log("W8 k sweep")
         # W8 k sweep on the executor (8-bit stack packed once)
