@@ -92,7 +92,10 @@ __global__ __launch_bounds__(kThreads) void hadamard_i8_kernel(
 
 // ---- block 4096: registers + one LDS transpose ---------------------------------
 constexpr int kB4 = 4096;
-constexpr int kPadRow = kB4 + 64;               // doubles per wave of transpose area
+// doubles per wave of transpose area: the transpose runs in two phases of 32
+// publishing lanes (65 doubles each, padded), so a 4096-block holds 16.6 KB
+// of LDS and two waves fit per SIMD
+constexpr int kPadRow = 32 * 65;
 
 __device__ __forceinline__ void bfly(double& a, double& b) {
   const double s = a + b, d = a - b;
@@ -141,16 +144,31 @@ __global__ __launch_bounds__(256) void hadamard4096_i8_kernel(
 #pragma unroll
     for (int i = 0; i < 64; ++i)
       if ((i & h) == 0) bfly(v[i], v[i + h]);
-  // transpose: element e = 64 lane + i -> padded slot e + e / 64; read back
-  // elements lane + 64 j (slot lane + 65 j)
+  // transpose: lane L takes elements L + 64 j, held by lane j in register L.
+  // Phase A: lanes 0..31 publish (slot 65 lane + i) and every lane reads
+  // j < 32 into w; phase B: lanes 32..63 publish into the same slots and
+  // every lane reads j >= 32.  LDS operations of a wave execute in order, so
+  // a lane reads what other lanes wrote, and phase B's writes follow phase A's
+  // reads; the compiler must only keep program order.
   double* tb = tbuf + wv * kPadRow;
+  double w[32];
+  if (lane < 32) {
 #pragma unroll
-  for (int i = 0; i < 64; ++i) tb[65 * lane + i] = v[i];
-  // lanes read what other lanes wrote: LDS operations of a wave execute in
-  // order, the compiler must only keep program order
+    for (int i = 0; i < 64; ++i) tb[65 * lane + i] = v[i];
+  }
   asm volatile("" ::: "memory");
 #pragma unroll
-  for (int j = 0; j < 64; ++j) v[j] = tb[lane + 65 * j];
+  for (int j = 0; j < 32; ++j) w[j] = tb[lane + 65 * j];
+  asm volatile("" ::: "memory");
+  if (lane >= 32) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) tb[65 * (lane - 32) + i] = v[i];
+  }
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < 32; ++j) v[32 + j] = tb[lane + 65 * j];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) v[j] = w[j];
   // stages h = 64 .. 2048: element lane + 64 j pairs with j ^ (h / 64)
 #pragma unroll
   for (int hj = 1; hj < 64; hj <<= 1)
