@@ -49,10 +49,11 @@ __device__ __forceinline__ bool better(double s, int v, double bs, int bv) {
 }
 
 // Merges the span partials of one target row in span order (score down,
-// index up), loading 8 partials at a time so their latencies overlap.
+// index up), loading up to 40 partials at a time (every span of a vocabulary
+// up to 163 840 entries) so that one memory latency covers them.
 __device__ __forceinline__ void merge_spans(const CoupledPartial* __restrict__ p, int spans,
                                             double& best, int& bi, int& flags) {
-  constexpr int kUnroll = 8;
+  constexpr int kUnroll = 40;
   for (int s0 = 0; s0 < spans; s0 += kUnroll) {
     CoupledPartial q[kUnroll];
 #pragma unroll
