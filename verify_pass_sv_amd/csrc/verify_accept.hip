@@ -297,9 +297,10 @@ __global__ __launch_bounds__(64 * kStatsWaves) void stats_kernel(
 }
 
 // Residual / bonus weight of one vocabulary entry from its two logits
-// (binary32), shared by kernels 2 and 3 so that both see bit-identical
-// weights.
-__device__ __noinline__ float resid_weight(float tl, float lt, float dl, float ld, bool bonus) {
+// (binary32).  The residual sums and the selection's replay evaluate it with
+// the same IEEE operations in the same order, so both see bit-identical
+// weights; inlined, a thread's 8 evaluations overlap.
+__device__ __forceinline__ float resid_weight(float tl, float lt, float dl, float ld, bool bonus) {
   const float p = expf(tl - lt);
   if (bonus) return p;
   const float q = expf(dl - ld);
