@@ -494,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
         if (q_at) q_at[static_cast<size_t>(b) * k + i] = status == 0 ? q : NAN;
       }
       if (i <= k) {
-        // accepted drafts; position n_acc is written by the select kernel
+        // accepted drafts; position n_acc is written by the selection
         const bool keep = status == 0 && i < n_acc;
         out_tokens[static_cast<size_t>(b) * (k + 1) + i] = keep ? tok : -1;
       }

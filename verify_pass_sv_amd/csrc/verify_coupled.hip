@@ -23,7 +23,9 @@
 //  2. decide  one wave per trial: lane r merges the spans of target row r
 //             (score down, index up), then the status checks and
 //             coupled: the first disagreement (one ballot);
-//             tree: the valid nodes, the longest valid chain and its bonus.
+//             tree: the valid nodes and their depths by pointer jumping over
+//             the parent links, the longest valid chain (a wave maximum) and
+//             its bonus.
 #include "sv_common.h"
 #include "sv_philox.h"
 
@@ -183,8 +185,7 @@ __global__ __launch_bounds__(64) void tree_decide_kernel(
     int32_t* __restrict__ out_n_acc, int32_t* __restrict__ out_status,
     int32_t* __restrict__ out_path) {
   __shared__ int choice[SV_MAX_ROWS + 1];
-  __shared__ int tok_sh[SV_MAX_ROWS], par_sh[SV_MAX_ROWS], path[SV_MAX_ROWS];
-  __shared__ int depth[SV_MAX_ROWS];            // valid chain length ending at a node, 0 if invalid
+  __shared__ int tok_sh[SV_MAX_ROWS], path[SV_MAX_ROWS];
   __shared__ int res[3];                        // status, path length, bonus row
   const int lane = threadIdx.x;
   const int b = blockIdx.x;
@@ -206,23 +207,54 @@ __global__ __launch_bounds__(64) void tree_decide_kernel(
     tok_bad = tok < 0 || tok >= V;
     par_bad = par < -1 || par >= lane;
     tok_sh[lane] = tok;
-    par_sh[lane] = par;
   }
   const int status = __any(tok_bad) ? 1 : (__any(row_bad) ? 2 : (__any(par_bad) ? 3 : 0));
-  __syncthreads();
-  if (lane == 0) {
-    // parents come before children, so one pass in node order settles every depth
-    int end = -1;
-    for (int j = 0; j < n && status == 0; ++j) {
-      const int p = par_sh[j];
-      const bool parent_ok = p < 0 || depth[p] > 0;
-      depth[j] = parent_ok && tok_sh[j] == choice[p + 1] ? 1 + (p >= 0 ? depth[p] : 0) : 0;
-      if (depth[j] > 0 && (end < 0 || depth[j] > depth[end])) end = j;
+  // Node j on lane j.  It matches when its token is the target's choice at
+  // its parent's row (lane p + 1 holds row p + 1's choice).  Pointer jumping
+  // over the parent links (5 rounds cover depths up to 32): ok becomes the
+  // AND of the matches from the root down to the node, d the node's depth,
+  // and jmp[r] keeps each node's 2^r-th ancestor for the path below.
+  static_assert(SV_MAX_ROWS <= 32, "5 jumping rounds cover trees of at most 32 nodes");
+  const int pchoice = __shfl(bi, par + 1 < 0 ? 0 : par + 1);
+  int ok = lane < n && status == 0 && tok == pchoice;
+  int a = lane < n ? par : -1;
+  int d = lane < n ? 1 : 0;
+  int jmp[5];
+#pragma unroll
+  for (int r = 0; r < 5; ++r) {
+    jmp[r] = a;
+    const int src = a < 0 ? lane : a;
+    const int ok_a = __shfl(ok, src);
+    const int d_a = __shfl(d, src);
+    const int a_a = __shfl(a, src);
+    if (a >= 0) {
+      ok &= ok_a;
+      d += d_a;
+      a = a_a;
     }
-    int len = end >= 0 ? depth[end] : 0;
-    for (int j = end, d = len - 1; j >= 0; j = par_sh[j], --d) path[d] = j;
+  }
+  const int depth = ok ? d : 0;
+  // the deepest valid node, the smallest index among equal depths
+  int key = depth > 0 ? (depth << 6) | (63 - lane) : 0;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) key = max(key, __shfl_xor(key, off));
+  const int end = key > 0 ? 63 - (key & 63) : -1;
+  const int len_v = key >> 6;
+  // node j lies on the chosen path iff it is end's ancestor at distance
+  // len - depth (binary lifting with the jump pointers)
+  {
+    const int dist = len_v - depth;
+    int x = end;
+#pragma unroll
+    for (int r = 0; r < 5; ++r) {
+      const int nx = __shfl(jmp[r], x < 0 ? 0 : x);
+      if (((dist >> r) & 1) && x >= 0) x = nx;
+    }
+    if (depth > 0 && dist >= 0 && x == lane) path[depth - 1] = lane;
+  }
+  if (lane == 0) {
     res[0] = status;
-    res[1] = status == 0 ? len : -1;
+    res[1] = status == 0 ? len_v : -1;
     res[2] = end + 1;
   }
   __syncthreads();
