@@ -179,11 +179,14 @@ __global__ __launch_bounds__(64) void coupled_decide_kernel(
   }
 }
 
+// pars == nullptr: a chain (node j's parent is node j - 1), which is greedy
+// verification of n drafts; p_at / q_at (nullable) then receive 1 or 0 for
+// d_j == argmax of target row j, and 1 (NaN for both when status != 0).
 __global__ __launch_bounds__(64) void tree_decide_kernel(
     const int32_t* __restrict__ toks, const int32_t* __restrict__ pars, int n, int V, int spans,
     const CoupledPartial* __restrict__ parts, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ out_n_acc, int32_t* __restrict__ out_status,
-    int32_t* __restrict__ out_path) {
+    int32_t* __restrict__ out_path, float* __restrict__ p_at, float* __restrict__ q_at) {
   __shared__ int choice[SV_MAX_ROWS + 1];
   __shared__ int tok_sh[SV_MAX_ROWS], path[SV_MAX_ROWS];
   __shared__ int res[3];                        // status, path length, bonus row
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(64) void tree_decide_kernel(
   bool tok_bad = false, par_bad = false;
   if (lane < n) {
     tok = toks[static_cast<size_t>(b) * n + lane];
-    par = pars[static_cast<size_t>(b) * n + lane];
+    par = pars ? pars[static_cast<size_t>(b) * n + lane] : lane - 1;
     tok_bad = tok < 0 || tok >= V;
     par_bad = par < -1 || par >= lane;
     tok_sh[lane] = tok;
@@ -217,6 +220,10 @@ __global__ __launch_bounds__(64) void tree_decide_kernel(
   static_assert(SV_MAX_ROWS <= 32, "5 jumping rounds cover trees of at most 32 nodes");
   const int pchoice = __shfl(bi, par + 1 < 0 ? 0 : par + 1);
   int ok = lane < n && status == 0 && tok == pchoice;
+  if (lane < n) {
+    if (p_at) p_at[static_cast<size_t>(b) * n + lane] = status == 0 ? (ok ? 1.f : 0.f) : NAN;
+    if (q_at) q_at[static_cast<size_t>(b) * n + lane] = status == 0 ? 1.f : NAN;
+  }
   int a = lane < n ? par : -1;
   int d = lane < n ? 1 : 0;
   int jmp[5];
@@ -336,7 +343,30 @@ extern "C" sv_status sv_verify_tree(const float* target_logits, const int32_t* t
                      target_logits, n, V, 0u, 0u, 0u, parts);
   SV_LAUNCH_CHECK();
   hipLaunchKernelGGL(tree_decide_kernel, dim3(B), dim3(64), 0, stream, tokens, parents, n, V,
-                     spans, parts, out_tokens, out_n_acc, out_status, out_path);
+                     spans, parts, out_tokens, out_n_acc, out_status, out_path, nullptr,
+                     nullptr);
+  SV_LAUNCH_CHECK();
+  return SV_OK;
+}
+
+// Greedy verification of k drafts (sv_verify_sampled at temperature 0) as the
+// chain tree d_0 <- d_1 <- ..: the argmax of target row i is node i's parent
+// choice, the longest valid chain is the matching prefix and the bonus is the
+// argmax of the row after it.  Arguments are validated by the caller; the
+// workspace holds sv_greedy_chain_workspace_bytes(B, k, V) bytes.
+size_t sv_greedy_chain_workspace_bytes(int B, int k, int V) {
+  return static_cast<size_t>(B) * (k + 1) * coupled_spans(V) * sizeof(CoupledPartial);
+}
+sv_status sv_greedy_chain(const float* target_logits, const int32_t* draft_tokens, int B, int k,
+                          int V, int32_t* out_tokens, int32_t* out_n_acc, int32_t* out_status,
+                          float* p_at, float* q_at, void* workspace, hipStream_t stream) {
+  const int spans = coupled_spans(V);
+  CoupledPartial* parts = static_cast<CoupledPartial*>(workspace);
+  hipLaunchKernelGGL(choose_kernel<false>, dim3(spans, k + 1, B), dim3(kThreads), 0, stream,
+                     target_logits, k, V, 0u, 0u, 0u, parts);
+  SV_LAUNCH_CHECK();
+  hipLaunchKernelGGL(tree_decide_kernel, dim3(B), dim3(64), 0, stream, draft_tokens, nullptr, k,
+                     V, spans, parts, out_tokens, out_n_acc, out_status, nullptr, p_at, q_at);
   SV_LAUNCH_CHECK();
   return SV_OK;
 }

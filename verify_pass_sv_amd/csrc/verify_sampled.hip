@@ -8,11 +8,14 @@
 // from left to right" and "Correct and continue", applied to the truncated
 // distributions.
 //
-// Four launches on the caller's stream:
+// Temperature 0 (greedy verification) runs as the chain tree d_0 <- d_1 <- ..
+// through the draft-tree kernels (sv_verify_tree's row maxima over many
+// workgroups per row, then one wave per trial).  Other settings take four
+// launches on the caller's stream:
 //  1. rows    one workgroup per (trial, row), target rows 0..k then draft rows
-//             0..k-1.  It checks the row and takes its maximum; for greedy
-//             settings also the argmax (smallest index among equal maxima).
-//             Otherwise it describes the kept set by a key threshold and a
+//             0..k-1.  It checks the row and takes its maximum (and the
+//             argmax, smallest index among equal maxima, into the record).
+//             It describes the kept set by a key threshold and a
 //             tie cut: token v is kept iff key(l_v) > tau, or key(l_v) == tau
 //             and v <= tie, where key() maps binary32 order to unsigned order.
 //             One pass bins the row below its maximum (1/32 logit, counts and
@@ -25,8 +28,7 @@
 //             exp((l - m) / T) in binary64 throughout.
 //  2. decide  one workgroup per trial: the accept scan on the kept
 //             probabilities (binary64) with the Philox uniforms of
-//             sv_verify_accept; writes the outputs except the drawn token
-//             (greedy: also that one).
+//             sv_verify_accept; writes the outputs except the drawn token.
 //  3. resid   one workgroup per (8192-entry vocabulary block, trial): block
 //             totals of the residual weights max(0, p'_r - q'_r) (or p'_k for
 //             the bonus), per-thread ranges of 16 entries added in order.
@@ -517,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
   out.tau = 0u;                                 // every non-NaN key exceeds 0
   out.tie = -1;
   out.temp = temperature;
-  if (bad || temperature == 0.f) {
+  if (bad) {
     if (tid == 0) rows[static_cast<size_t>(b) * R + rho] = out;
     return;
   }
@@ -623,8 +625,7 @@ constexpr int kResBlk = kThreads * kResPer;     // 8192 vocabulary entries per b
 __host__ __device__ inline int res_blocks(int V) { return (V + kResBlk - 1) / kResBlk; }
 
 __global__ __launch_bounds__(kThreads) void sampled_decide_kernel(
-    const int32_t* __restrict__ toks, int k, int V, bool greedy,
-    const SampledRow* __restrict__ rows, unsigned int key0, unsigned int key1,
+    const int32_t* __restrict__ toks, int k, int V, const SampledRow* __restrict__ rows, unsigned int key0, unsigned int key1,
     unsigned int offset, SampledDecision* __restrict__ decs, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ out_n_acc, int32_t* __restrict__ out_status, float* __restrict__ p_at,
     float* __restrict__ q_at) {
@@ -641,8 +642,7 @@ __global__ __launch_bounds__(kThreads) void sampled_decide_kernel(
     for (int i = 0; i < k; ++i)
       if (tk[i] < 0 || tk[i] >= V) status = 1;
     if (status == 0) {
-      // greedy settings read only the target rows
-      for (int j = 0; j < (greedy ? k + 1 : R); ++j)
+      for (int j = 0; j < R; ++j)
         if (rr[j].status != 0) status = 2;
     }
     int n_acc = k;
@@ -657,11 +657,11 @@ __global__ __launch_bounds__(kThreads) void sampled_decide_kernel(
       }
       double p = NAN, q = NAN;
       if (status == 0) {
-        p = greedy ? (tk[i] == rr[i].argmax ? 1.0 : 0.0) : rr[i].pd;
-        q = greedy ? 1.0 : rr[k + 1 + i].pd;
+        p = rr[i].pd;
+        q = rr[k + 1 + i].pd;
         if (n_acc == k) {
           // u carries 24 bits: exact in binary32 and binary64
-          const bool acc = greedy ? p > 0.0 : static_cast<double>(sv_u24(ctr[0])) * q < p;
+          const bool acc = static_cast<double>(sv_u24(ctr[0])) * q < p;
           if (!acc) {
             n_acc = i;
             u2r = sv_u24(ctr[1]);
@@ -689,7 +689,6 @@ __global__ __launch_bounds__(kThreads) void sampled_decide_kernel(
   if (tid == 0) {
     out_n_acc[b] = status == 0 ? n_acc : -1;
     out_status[b] = status;
-    if (status == 0 && greedy) ot[n_acc] = rr[n_acc].argmax;   // else written by launch 4
   }
 }
 
@@ -744,7 +743,7 @@ __device__ __forceinline__ double thread_res_sum(const ResidualRows& q, int V, i
 // Launch 3: block totals of the residual weights (and of p_r alone, for the
 // S = 0 fallback), per-thread sums added in thread order.
 __global__ __launch_bounds__(kThreads) void sampled_resid_kernel(
-    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V, bool greedy,
+    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V,
     const SampledRow* __restrict__ rows, const SampledDecision* __restrict__ decs,
     double* __restrict__ totals) {
   __shared__ double wsh[2][kThreads];
@@ -753,7 +752,7 @@ __global__ __launch_bounds__(kThreads) void sampled_resid_kernel(
   const int b = blockIdx.y;
   const int G = gridDim.x;
   const SampledDecision dec = decs[b];
-  if (greedy || dec.status != 0) return;
+  if (dec.status != 0) return;
   const ResidualRows q = residual_rows(tgt, dft, rows, b, k, V, dec.n_acc);
   wsh[0][tid] = thread_res_sum(q, V, blk, dec.plain != 0);
   wsh[1][tid] = dec.plain ? 0.0 : thread_res_sum(q, V, blk, true);
@@ -769,7 +768,7 @@ __global__ __launch_bounds__(kThreads) void sampled_resid_kernel(
 // exceeds u' S; inside it, the thread whose running sum does; that thread
 // replays its entries with the same association.
 __global__ __launch_bounds__(kThreads) void sampled_select_kernel(
-    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V, bool greedy,
+    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V,
     const SampledRow* __restrict__ rows, const SampledDecision* __restrict__ decs,
     const double* __restrict__ totals, int G, int32_t* __restrict__ out_tokens) {
   __shared__ double wsh[kThreads];
@@ -778,7 +777,7 @@ __global__ __launch_bounds__(kThreads) void sampled_select_kernel(
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const SampledDecision dec = decs[b];
-  if (greedy || dec.status != 0) return;
+  if (dec.status != 0) return;
   if (tid == 0) {
     const double* tot = totals + static_cast<size_t>(b) * 2 * G;
     int which = 0;
@@ -875,6 +874,9 @@ SampledWs sampled_ws(int B, int k, int V) {
   w.dec_off = (static_cast<size_t>(B) * (2 * k + 1) * sizeof(SampledRow) + 255) / 256 * 256;
   w.tot_off = (w.dec_off + static_cast<size_t>(B) * sizeof(SampledDecision) + 255) / 256 * 256;
   w.bytes = w.tot_off + static_cast<size_t>(B) * 2 * res_blocks(V) * sizeof(double);
+  // temperature 0 runs as a chain tree, whose span partials share the space
+  const size_t chain = sv_greedy_chain_workspace_bytes(B, k, V);
+  if (chain > w.bytes) w.bytes = chain;
   return w;
 }
 }  // namespace
@@ -913,24 +915,26 @@ extern "C" sv_status sv_verify_sampled(const float* target_logits, const float* 
   SampledDecision* decs = reinterpret_cast<SampledDecision*>(ws + L.dec_off);
   double* totals = reinterpret_cast<double*>(ws + L.tot_off);
   const int G = res_blocks(V);
-  const bool greedy = T == 0.f;
-  // greedy settings need only the target rows' maxima
-  hipLaunchKernelGGL(sampled_rows_kernel, dim3(greedy ? k + 1 : 2 * k + 1, B), dim3(kThreads), 0,
-                     stream, target_logits, draft_logits, draft_tokens, k, V, T, sampling->top_k,
+  // Greedy verification (T = 0) is the chain tree d_0 <- d_1 <- .. of the
+  // draft-tree kernels: row maxima over many workgroups per row, then one
+  // wave per trial.
+  if (T == 0.f)
+    return sv_greedy_chain(target_logits, draft_tokens, B, k, V, out_tokens, out_n_acc,
+                           out_status, p_at, q_at, workspace, stream);
+  hipLaunchKernelGGL(sampled_rows_kernel, dim3(2 * k + 1, B), dim3(kThreads), 0, stream,
+                     target_logits, draft_logits, draft_tokens, k, V, T, sampling->top_k,
                      sampling->top_p, rows);
   SV_LAUNCH_CHECK();
   hipLaunchKernelGGL(sampled_decide_kernel, dim3(B), dim3(kThreads), 0, stream, draft_tokens, k,
-                     V, greedy, rows, static_cast<unsigned int>(seed & 0xFFFFFFFFu),
+                     V, rows, static_cast<unsigned int>(seed & 0xFFFFFFFFu),
                      static_cast<unsigned int>(seed >> 32), offset, decs, out_tokens, out_n_acc,
                      out_status, p_at, q_at);
   SV_LAUNCH_CHECK();
-  if (!greedy) {
-    hipLaunchKernelGGL(sampled_resid_kernel, dim3(G, B), dim3(kThreads), 0, stream,
-                       target_logits, draft_logits, k, V, greedy, rows, decs, totals);
-    SV_LAUNCH_CHECK();
-    hipLaunchKernelGGL(sampled_select_kernel, dim3(B), dim3(kThreads), 0, stream, target_logits,
-                       draft_logits, k, V, greedy, rows, decs, totals, G, out_tokens);
-    SV_LAUNCH_CHECK();
-  }
+  hipLaunchKernelGGL(sampled_resid_kernel, dim3(G, B), dim3(kThreads), 0, stream, target_logits,
+                     draft_logits, k, V, rows, decs, totals);
+  SV_LAUNCH_CHECK();
+  hipLaunchKernelGGL(sampled_select_kernel, dim3(B), dim3(kThreads), 0, stream, target_logits,
+                     draft_logits, k, V, rows, decs, totals, G, out_tokens);
+  SV_LAUNCH_CHECK();
   return SV_OK;
 }
