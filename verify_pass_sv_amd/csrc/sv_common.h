@@ -46,11 +46,3 @@ __device__ __forceinline__ float sv_half_lo(unsigned int w) {
 __device__ __forceinline__ float sv_half_hi(unsigned int w) {
   return __half2float(__ushort_as_half(static_cast<unsigned short>(w >> 16)));
 }
-
-// Greedy verification of k drafts as a chain tree, shared by
-// sv_verify_sampled at temperature 0 (defined with the tree kernels).
-// Arguments are validated by the caller.
-size_t sv_greedy_chain_workspace_bytes(int B, int k, int V);
-sv_status sv_greedy_chain(const float* target_logits, const int32_t* draft_tokens, int B, int k,
-                          int V, int32_t* out_tokens, int32_t* out_n_acc, int32_t* out_status,
-                          float* p_at, float* q_at, void* workspace, hipStream_t stream);

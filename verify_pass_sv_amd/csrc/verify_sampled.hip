@@ -38,6 +38,14 @@
 #include "sv_common.h"
 #include "sv_philox.h"
 
+// Greedy verification of k drafts as a chain tree (defined with the
+// draft-tree kernels in verify_coupled.hip).  Arguments are validated by the
+// caller.
+size_t sv_greedy_chain_workspace_bytes(int B, int k, int V);
+sv_status sv_greedy_chain(const float* target_logits, const int32_t* draft_tokens, int B, int k,
+                          int V, int32_t* out_tokens, int32_t* out_n_acc, int32_t* out_status,
+                          float* p_at, float* q_at, void* workspace, hipStream_t stream);
+
 #include <math.h>
 
 namespace {
