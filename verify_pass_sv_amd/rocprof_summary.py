@@ -1,7 +1,7 @@
 """Summarize rocprofv3 CSV output into the short text kept under profiles/.
 
     python -m verify_pass_sv_amd.rocprof_summary \
-        --trace gpurun_out/prof_kt --pmc gpurun_out/prof_pmc \
+        --trace out/prof_kt --pmc out/prof_pmc \
         --kernel pass_kernel --copy-bytes 268435456 \
         --command "<the rocprofv3 command lines>" --out profiles/<name>
 
