@@ -233,7 +233,7 @@ def main():
     ap.add_argument("--trials", type=int, default=1, help="B of --profile-accept")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
 

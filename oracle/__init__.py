@@ -1,7 +1,7 @@
 """Plain fp64 CPU oracle for the speculative-decoding verify pass.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls, links
-or executes this package: only the test suite, the graft smoke entry point and
+or executes this package: only the test suite, ``__graft_entry__.smoke()`` and
 the benchmark's ``cpu_baseline`` leg use it.  It shares no code, header,
 table or constant generator with the HIP library (``verify_pass_sv_amd``) and
 never imports it.
