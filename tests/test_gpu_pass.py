@@ -140,12 +140,13 @@ def test_pass_in_a_graph_replays_like_eager():
             assert torch.equal(g["dev"][4], e)
 
 
-def test_full_9b_stack_pass_sampled_channels():
-    """The 32-layer, 3.93 GB W4 stack at k = 16 in the launch configuration of
-    the benchmark (one pass, one launch); 16 sampled channels per GEMM are
-    checked against the oracle."""
+@pytest.mark.parametrize("m", [16, 1, 32])
+def test_full_9b_stack_pass_sampled_channels(m):
+    """The 32-layer, 3.93 GB W4 stack in the launch configuration of the
+    benchmark (one pass, one launch) at k = 16, and at the two ends of its k
+    sweep; 16 sampled channels per GEMM are checked against the oracle."""
     sv = _sv()
-    H, F, m = 4096, 12288, 16
+    H, F = 4096, 12288
     x_h = synth.activations(m, H, seed=11, device=DEV)
     x_f = synth.activations(m, F, seed=12, device=DEV)
     shapes = [(3 * H, H), (H, H), (2 * F, H), (H, F)]
@@ -310,13 +311,13 @@ def test_w4_i8_pass_one_hot_rows_exact():
     assert np.array_equal(y.cpu().numpy(), W[:, cols].T.astype(np.float32))
 
 
-@pytest.mark.parametrize("fmt", ["w8", "w4_i8"])
-def test_full_9b_stack_pass_other_formats_sampled(fmt):
-    """The 32-layer stack in the W8 and int8 formats at k = 16, one launch, in
-    the benchmark's configuration; 8 sampled channels per GEMM against the
-    oracle."""
+@pytest.mark.parametrize("fmt,m", [("w8", 16), ("w4_i8", 16), ("w8", 32)])
+def test_full_9b_stack_pass_other_formats_sampled(fmt, m):
+    """The 32-layer stack in the W8 and int8 formats at k = 16 (and W8 at the
+    top of its k sweep), one launch, in the benchmark's configuration; 8
+    sampled channels per GEMM against the oracle."""
     sv = _sv()
-    H, F, m = 4096, 12288, 16
+    H, F = 4096, 12288
     shapes = [(3 * H, H), (H, H), (2 * F, H), (H, F)]
     if fmt == "w8":
         xs = {H: synth.activations(m, H, seed=11, device=DEV),
