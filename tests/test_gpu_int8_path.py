@@ -25,7 +25,8 @@ def _near_tie(xt, scale, tol=1e-6):
 @pytest.mark.parametrize("m,K,block,outliers", [
     (4, 4096, 4096, False), (16, 4096, 4096, True), (16, 12288, 4096, True),
     (3, 1024, 32, False), (32, 4096, 256, True), (1, 64, 64, False), (5, 192, 2, False),
-    (300, 4096, 4096, True)])                      # many token rows in one call
+    (300, 4096, 4096, True),                       # many token rows in one call
+    (8, 8192, 4096, False), (8, 16384, 4096, True)])   # 2 and 4 blocks (above 64 KiB of LDS)
 def test_hadamard_codes_and_scales(m, K, block, outliers):
     sv = _sv()
     if outliers:
