@@ -29,9 +29,10 @@
 //  2. decide  one workgroup per trial: the accept scan on the kept
 //             probabilities (binary64) with the Philox uniforms of
 //             sv_verify_accept; writes the outputs except the drawn token.
-//  3. resid   one workgroup per (8192-entry vocabulary block, trial): block
+//  3. resid   one workgroup per (2048-entry vocabulary block, trial): block
 //             totals of the residual weights max(0, p'_r - q'_r) (or p'_k for
-//             the bonus), per-thread ranges of 16 entries added in order.
+//             the bonus), per-thread ranges of 4 entries added in order and
+//             their running sums formed in one fixed association.
 //  4. select  one workgroup per trial: S, the block whose running sum
 //             exceeds u' S, then the thread range and the entry inside it,
 //             replaying the same sums in the same order.
@@ -628,8 +629,8 @@ struct SampledDecision {             // per trial, written by launch 2
   double u2;                        // the uniform of the replacement / bonus draw
 };
 
-constexpr int kResPer = 16;                     // residual weights per thread per block
-constexpr int kResBlk = kThreads * kResPer;     // 8192 vocabulary entries per block
+constexpr int kResPer = 4;                      // residual weights per thread per block
+constexpr int kResBlk = kThreads * kResPer;     // 2048 vocabulary entries per block
 __host__ __device__ inline int res_blocks(int V) { return (V + kResBlk - 1) / kResBlk; }
 
 __global__ __launch_bounds__(kThreads) void sampled_decide_kernel(
@@ -644,50 +645,48 @@ __global__ __launch_bounds__(kThreads) void sampled_decide_kernel(
   const SampledRow* rr = rows + static_cast<size_t>(b) * R;
   const int32_t* tk = toks + static_cast<size_t>(b) * k;
 
-  // status, kept probabilities of the drafts, and the accept scan (thread 0)
-  if (tid == 0) {
-    int status = 0;
-    for (int i = 0; i < k; ++i)
-      if (tk[i] < 0 || tk[i] >= V) status = 1;
-    if (status == 0) {
-      for (int j = 0; j < R; ++j)
-        if (rr[j].status != 0) status = 2;
-    }
-    int n_acc = k;
-    float u2r = 0.f;
-    for (int i = 0; i <= k; ++i) {
+  // status, kept probabilities of the drafts and the accept scan: wave 0,
+  // lane i for draft i (its Philox uniforms, p'_i(d_i), q'_i(d_i)); the first
+  // rejection is the first set bit of one ballot
+  if (tid < 64) {
+    const int i = tid;
+    const bool tbad = i < k && (tk[i] < 0 || tk[i] >= V);
+    const bool rbad = (i < R && rr[i].status != 0) || (i + 64 < R && rr[i + 64].status != 0);
+    const int status = __any(tbad) ? 1 : (__any(rbad) ? 2 : 0);
+    float u = 0.f, u2 = 0.f;
+    if (i <= k) {
       unsigned int ctr[4] = {static_cast<unsigned int>(i), static_cast<unsigned int>(b), offset,
                              0u};
       sv_philox_rounds(ctr, key0, key1);
-      if (i == k) {
-        if (n_acc == k) u2r = sv_u24(ctr[1]);
-        break;
-      }
-      double p = NAN, q = NAN;
-      if (status == 0) {
-        p = rr[i].pd;
-        q = rr[k + 1 + i].pd;
-        if (n_acc == k) {
-          // u carries 24 bits: exact in binary32 and binary64
-          const bool acc = static_cast<double>(sv_u24(ctr[0])) * q < p;
-          if (!acc) {
-            n_acc = i;
-            u2r = sv_u24(ctr[1]);
-          }
-        }
-      }
+      u = sv_u24(ctr[0]);
+      u2 = sv_u24(ctr[1]);
+    }
+    double p = NAN, q = NAN;
+    bool acc = true;
+    if (i < k && status == 0) {
+      p = rr[i].pd;
+      q = rr[k + 1 + i].pd;
+      // u carries 24 bits: exact in binary32 and binary64
+      acc = static_cast<double>(u) * q < p;
+    }
+    const unsigned long long rej = __ballot(!acc);
+    const int n_acc = rej ? (__ffsll(static_cast<long long>(rej)) - 1) : k;
+    const float u2r = __shfl(u2, n_acc);
+    if (i < k) {
       if (p_at) p_at[static_cast<size_t>(b) * k + i] = static_cast<float>(p);
       if (q_at) q_at[static_cast<size_t>(b) * k + i] = static_cast<float>(q);
     }
-    SampledDecision dec;
-    dec.status = status;
-    dec.n_acc = status == 0 ? n_acc : -1;
-    dec.plain = n_acc == k;
-    dec.pad = 0;
-    dec.u2 = static_cast<double>(u2r);
-    decs[b] = dec;
-    ish[0] = status;
-    ish[1] = n_acc;
+    if (i == 0) {
+      SampledDecision dec;
+      dec.status = status;
+      dec.n_acc = status == 0 ? n_acc : -1;
+      dec.plain = n_acc == k;
+      dec.pad = 0;
+      dec.u2 = static_cast<double>(u2r);
+      decs[b] = dec;
+      ish[0] = status;
+      ish[1] = n_acc;
+    }
   }
   __syncthreads();
   const int status = ish[0];
@@ -710,15 +709,28 @@ struct ResidualRows {
   int ttie, dtie;
   double ts, ds;
 };
-__device__ __forceinline__ double res_weight(const ResidualRows& q, int v, bool plain) {
-  const float x = q.trow[v];
+// The weight of entry v from its target logit x and draft logit y.
+__device__ __forceinline__ double res_weight(const ResidualRows& q, float x, float y, int v,
+                                             bool plain) {
   const double pv =
       kept_by(order_key(x), v, q.ttau, q.ttie) ? mass(x, q.tm, q.temp) / q.ts : 0.0;
   if (plain) return pv;
-  const float y = q.drow[v];
   const double qv =
       kept_by(order_key(y), v, q.dtau, q.dtie) ? mass(y, q.dm, q.temp) / q.ds : 0.0;
   return fmax(0.0, pv - qv);
+}
+
+// A thread's kResPer target and draft logits of block blk, all loads issued
+// before any is used (entries past V read as 0 and are never weighed).
+__device__ __forceinline__ void res_load(const ResidualRows& q, int V, int blk, bool plain,
+                                         float* xs, float* ys) {
+  const int v0 = blk * kResBlk + threadIdx.x * kResPer;
+#pragma unroll
+  for (int j = 0; j < kResPer; ++j) {
+    const bool in = v0 + j < V;
+    xs[j] = in ? q.trow[v0 + j] : 0.f;
+    ys[j] = in && !plain ? q.drow[v0 + j] : 0.f;
+  }
 }
 __device__ __forceinline__ ResidualRows residual_rows(const float* tgt, const float* dft,
                                                       const SampledRow* rows, int b, int k,
@@ -742,14 +754,31 @@ __device__ __forceinline__ ResidualRows residual_rows(const float* tgt, const fl
 }
 __device__ __forceinline__ double thread_res_sum(const ResidualRows& q, int V, int blk, bool plain) {
   const int v0 = blk * kResBlk + threadIdx.x * kResPer;
+  float xs[kResPer], ys[kResPer];
+  res_load(q, V, blk, plain, xs, ys);
   double s = 0.0;
+#pragma unroll
   for (int j = 0; j < kResPer; ++j)
-    if (v0 + j < V) s += res_weight(q, v0 + j, plain);
+    if (v0 + j < V) s += res_weight(q, xs[j], ys[j], v0 + j, plain);
   return s;
 }
 
+// Inclusive running sums of a[0 .. kThreads) in place (binary64, every thread
+// of the workgroup takes part): the same fixed association on every call, so
+// the block total that launch 3 forms (a[kThreads - 1]) is bit-identical to
+// the one launch 4 reaches when it forms the same sums again.
+__device__ void scan_inclusive(double* a) {
+  const int tid = threadIdx.x;
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const double v = tid >= off ? a[tid - off] : 0.0;
+    __syncthreads();
+    a[tid] += v;
+    __syncthreads();
+  }
+}
+
 // Launch 3: block totals of the residual weights (and of p_r alone, for the
-// S = 0 fallback), per-thread sums added in thread order.
+// S = 0 fallback): the last of the per-thread sums' running sums.
 __global__ __launch_bounds__(kThreads) void sampled_resid_kernel(
     const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V,
     const SampledRow* __restrict__ rows, const SampledDecision* __restrict__ decs,
@@ -765,11 +794,9 @@ __global__ __launch_bounds__(kThreads) void sampled_resid_kernel(
   wsh[0][tid] = thread_res_sum(q, V, blk, dec.plain != 0);
   wsh[1][tid] = dec.plain ? 0.0 : thread_res_sum(q, V, blk, true);
   __syncthreads();
-  if (tid < 2) {
-    double run = 0.0;
-    for (int t = 0; t < kThreads; ++t) run += wsh[tid][t];
-    totals[(static_cast<size_t>(b) * 2 + tid) * G + blk] = run;
-  }
+  scan_inclusive(wsh[0]);
+  scan_inclusive(wsh[1]);
+  if (tid < 2) totals[(static_cast<size_t>(b) * 2 + tid) * G + blk] = wsh[tid][kThreads - 1];
 }
 
 // Launch 4: S = sum of the block totals; the block whose running sum first
@@ -786,8 +813,14 @@ __global__ __launch_bounds__(kThreads) void sampled_select_kernel(
   const int b = blockIdx.x;
   const SampledDecision dec = decs[b];
   if (dec.status != 0) return;
+  // the trial's block totals, staged in LDS by every thread when they fit
+  const double* tot = totals + static_cast<size_t>(b) * 2 * G;
+  if (2 * G <= kThreads) {
+    for (int i = tid; i < 2 * G; i += kThreads) wsh[i] = tot[i];
+    tot = wsh;
+  }
+  __syncthreads();
   if (tid == 0) {
-    const double* tot = totals + static_cast<size_t>(b) * 2 * G;
     int which = 0;
     double S = 0.0;
     for (int g = 0; g < G; ++g) S += tot[g];
@@ -828,37 +861,38 @@ __global__ __launch_bounds__(kThreads) void sampled_select_kernel(
   const double mine = thread_res_sum(q, V, blk, plain);
   wsh[tid] = mine;
   __syncthreads();
+  // the running sums of the thread sums as launch 3 formed them; the owner
+  // is the first thread whose running sum crosses the threshold (they never
+  // decrease); rounding that leaves none: the last thread with weight
+  scan_inclusive(wsh);
   if (tid == 0) {
-    double run = run_sh;
-    int owner = -1, lastnz = -1;
-    double pre = 0.0, lastnz_pre = 0.0;
-    for (int t = 0; t < kThreads; ++t) {
-      const double w = wsh[t];
-      if (w > 0.0) {
-        lastnz = t;
-        lastnz_pre = run;
-      }
-      if (owner < 0 && run + w > thr_sh) {
-        owner = t;
-        pre = run;
-      }
-      run += w;
-    }
-    if (owner < 0) {
-      owner = lastnz;
-      pre = lastnz_pre;
-    }
+    ish[2] = kThreads;
+    ish[0] = -1;
+  }
+  __syncthreads();
+  {
+    const double run = run_sh, thr = thr_sh;
+    const double before = tid > 0 ? wsh[tid - 1] : 0.0;
+    if (run + wsh[tid] > thr && !(run + before > thr)) atomicMin(&ish[2], tid);
+    if (mine > 0.0) atomicMax(&ish[0], tid);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int owner = ish[2];
+    if (owner == kThreads) owner = ish[0];
     ish[2] = owner;
-    run_sh = pre;
+    run_sh = run_sh + (owner > 0 ? wsh[owner - 1] : 0.0);
   }
   __syncthreads();
   if (tid == ish[2]) {
     const int v0 = blk * kResBlk + tid * kResPer;
     const double thr = thr_sh, pre = run_sh;
+    float xs[kResPer], ys[kResPer];
+    res_load(q, V, blk, plain, xs, ys);
     double local = 0.0;
     int pick = -1, last = -1;
     for (int j = 0; j < kResPer && v0 + j < V; ++j) {
-      const double w = res_weight(q, v0 + j, plain);
+      const double w = res_weight(q, xs[j], ys[j], v0 + j, plain);
       if (w > 0.0) last = v0 + j;
       local += w;
       if (pre + local > thr) {
