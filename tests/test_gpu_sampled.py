@@ -130,6 +130,19 @@ def test_full_vocab_k32(settings):
     assert _compare(out, res) <= 1
 
 
+@pytest.mark.parametrize("settings", [(0.9, 5, 0.8), (0.0, 0, 1.0), (1.0, 0, 1.0)],
+                         ids=["T0.9_k5_p0.8", "greedy", "plain"])
+def test_many_trials_in_one_call(settings):
+    # 3000 trials: grids well past one row of workgroups per launch (the rows
+    # launch's y dimension, the greedy chain's z dimension); vocabulary 33 (a
+    # ragged residual block and span)
+    B, k, V = 3000, 2, 33
+    tgt, dft, tok = synth.accept_inputs(B, k, V, seed=41, sigma=1.0)
+    out, res = _run(tgt, dft, tok, seed=9, settings=settings)
+    flagged = _compare(out, res)
+    assert flagged <= B // 50
+
+
 def test_greedy_on_the_page_example():
     ex = load_worked_example("worked_example_page1.txt")
     t = torch.from_numpy(ex["target"]).float()[None]
