@@ -62,6 +62,16 @@ def test_matches_oracle(sigma):
     assert any(r.n_acc < k for r in res)
 
 
+def test_many_trials_in_one_call():
+    # 3000 trials: the choose launch's z dimension and one decide wave per
+    # trial well past one row of workgroups; vocabulary 33 (one ragged span)
+    B, k, V = 3000, 2, 33
+    tgt, dft, _ = synth.accept_inputs(B, k, V, seed=43, sigma=1.0)
+    tok = torch.from_numpy(oracle.coupled_drafts(dft.numpy(), 5, offset=1))
+    out, res = _run(tgt, tok, seed=5, offset=1)
+    assert _compare(out, res) <= B // 50
+
+
 def test_equal_distributions_accept_every_draft():
     B, k, V = 32, 6, 3000
     tgt, _, _ = synth.accept_inputs(B, k, V, seed=4, sigma=1.0)
