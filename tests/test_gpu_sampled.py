@@ -171,6 +171,28 @@ def test_invalid_inputs_report_status():
         assert st[4] == (0 if settings[0] == 0.0 else 2)
 
 
+@pytest.mark.parametrize("V", [20000, 20001])
+@pytest.mark.parametrize("settings", [(1.0, 0, 1.0), (0.9, 10, 0.8), (1.3, 1, 1.0)],
+                         ids=["plain", "k10_p0.8", "k1"])
+def test_rows_split_over_slices(V, settings):
+    # few rows of a long vocabulary: each row's full passes run over several
+    # workgroups and merge in slice order; invalid rows, equal maxima in the
+    # first and last slice, and a row length that is not a multiple of 4
+    B, k = 4, 3
+    tgt, dft, tok = synth.accept_inputs(B, k, V, seed=12, sigma=1.0)
+    tgt[1, 1, V - 2] = float("nan")
+    dft[2, 0, :] = float("-inf")
+    tgt[3, 3, V // 2] = float("inf")
+    for t in (tgt, dft):
+        t[0, 0, 3] = 40.0
+        t[0, 0, V - 1] = 40.0
+    tok[0, 0] = V - 1
+    out, res = _run(tgt, dft, tok, seed=3, settings=settings)
+    assert _compare(out, res) <= 1
+    st = out["status"].cpu().tolist()
+    assert st == [0, 2, 2, 2]
+
+
 def test_default_settings_agree_with_the_plain_entry_point():
     sv = _sv()
     B, k, V = 32, 5, 2000

@@ -11,7 +11,10 @@
 // Temperature 0 (greedy verification) runs as the chain tree d_0 <- d_1 <- ..
 // through the draft-tree kernels (sv_verify_tree's row maxima over many
 // workgroups per row, then one wave per trial).  Other settings take four
-// launches on the caller's stream:
+// launches on the caller's stream (six when a call has fewer rows than
+// compute units: two slice launches then take each row's full passes --
+// maximum, argmax and validity, then the bins or the whole mass -- over W
+// workgroups per row, merged by the rows launch in slice order):
 //  1. rows    one workgroup per (trial, row), target rows 0..k then draft rows
 //             0..k-1.  It checks the row and takes its maximum (and the
 //             argmax, smallest index among equal maxima, into the record).
@@ -168,77 +171,65 @@ __device__ __forceinline__ int bin_of(float x, float mx) {
   return d < static_cast<float>(kBins - 1) ? static_cast<int>(d) : kBins - 1;
 }
 
-// f(x, v) for every token of the row; each thread visits its tokens in
-// ascending index order, with 32 values in flight when rows allow 16-byte
-// loads.
-template <typename F>
-__device__ __forceinline__ void scan_row(const float* row, int V, F&& f) {
+// f(x, v) for the n tokens at p (v counted from p); each thread visits its
+// tokens in ascending index order, with 32 values in flight when `vec` (p is
+// 16-byte aligned and n a multiple of 4) allows 16-byte loads.
+template <int U = 8, typename F>
+__device__ __forceinline__ void scan_span(const float* p, int n, bool vec, F&& f) {
   const int tid = threadIdx.x;
-  if ((V & 3) == 0) {
-    const float4* r4 = reinterpret_cast<const float4*>(row);
-    const int V4 = V >> 2;
-    int v = tid;
-    for (; v + 7 * kThreads < V4; v += 8 * kThreads) {
-      float4 a[8];
+  if (vec) {
+    const float4* r4 = reinterpret_cast<const float4*>(p);
+    const int V4 = n >> 2;
+    // the ragged last round loads clamped indices (in bounds: V4 >= 1 inside
+    // the loop), so its loads are in flight together, and skips them
+    for (int v = tid; v < V4; v += U * kThreads) {
+      float4 a[U];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) a[u] = r4[v + u * kThreads];
+      for (int u = 0; u < U; ++u) a[u] = r4[min(v + u * kThreads, V4 - 1)];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int base = 4 * (v + u * kThreads);
-        f(a[u].x, base);
-        f(a[u].y, base + 1);
-        f(a[u].z, base + 2);
-        f(a[u].w, base + 3);
+      for (int u = 0; u < U; ++u) {
+        if (v + u * kThreads < V4) {
+          const int base = 4 * (v + u * kThreads);
+          f(a[u].x, base);
+          f(a[u].y, base + 1);
+          f(a[u].z, base + 2);
+          f(a[u].w, base + 3);
+        }
       }
     }
-    for (; v < V4; v += kThreads) {
-      const float4 a = r4[v];
-      f(a.x, 4 * v);
-      f(a.y, 4 * v + 1);
-      f(a.z, 4 * v + 2);
-      f(a.w, 4 * v + 3);
-    }
   } else {
-    for (int v = tid; v < V; v += kThreads) f(row[v], v);
+    for (int v = tid; v < n; v += kThreads) f(p[v], v);
   }
+}
+// The whole row (rows start 16-byte aligned when V is a multiple of 4).
+template <int U = 8, typename F>
+__device__ __forceinline__ void scan_row(const float* row, int V, F&& f) {
+  scan_span<U>(row, V, (V & 3) == 0, f);
 }
 
-// Exclusive scan of one int per thread (thread order); returns this thread's
-// prefix.
-__device__ int scan_int(int c, int* ish) {
-  const int tid = threadIdx.x;
-  ish[tid] = c;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int t = 0; t < kThreads; ++t) {
-      const int n = ish[t];
-      ish[t] = run;
-      run += n;
-    }
+// Exclusive scan of one value per thread (thread order); returns this
+// thread's prefix.  Lanes scan within their wave by shuffles, then each
+// thread adds the totals of the waves before it, in wave order: one fixed
+// association, the same on every call.
+template <typename X>
+__device__ X scan_excl(X c, X* sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  X x = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const X y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
   }
+  X e = __shfl_up(x, 1, 64);                   // the lanes before this one
+  if (lane == 0) e = 0;
+  if (lane == 63) sh[wv] = x;
   __syncthreads();
-  const int pre = ish[tid];
+  X base = 0;
+  for (int w = 0; w < wv; ++w) base += sh[w];
   __syncthreads();
-  return pre;
+  return base + e;
 }
-__device__ double scan_double(double c, double* dsh) {
-  const int tid = threadIdx.x;
-  dsh[tid] = c;
-  __syncthreads();
-  if (tid == 0) {
-    double run = 0.0;
-    for (int t = 0; t < kThreads; ++t) {
-      const double n = dsh[t];
-      dsh[t] = run;
-      run += n;
-    }
-  }
-  __syncthreads();
-  const double pre = dsh[tid];
-  __syncthreads();
-  return pre;
-}
+__device__ int scan_int(int c, int* ish) { return scan_excl<int>(c, ish); }
 
 // First bin where the count from the top reaches `want`; `above` = tokens in
 // the bins before it.
@@ -290,7 +281,7 @@ __device__ int cross_mass(const double* m, int n, double need, double& above, do
   double c = 0.0;
   for (int j = 0; j < kPer; ++j)
     if (j0 + j < n) c += m[j0 + j];
-  const double pre = scan_double(c, dsh);
+  const double pre = scan_excl<double>(c, dsh);
   if (tid == 0) ish[kThreads] = n;
   __syncthreads();
   double run = pre;
@@ -469,9 +460,163 @@ __device__ void radix_select(const float* row, int V, float mx, float T, int top
 
 }
 
+// Rows split into W slices (few rows per call): the row statistics that need
+// a full pass -- maximum, argmax, validity, then the bins (or the whole mass
+// when nothing truncates) -- are taken per slice by W workgroups per row.
+// Maxima and whole masses merge in slice order; each slice adds its nonzero
+// bins into the row's histogram with device atomics (counts exactly; the
+// binary64 masses in arrival order, which moves a bin's mass only in its last
+// bits, as the LDS atomics inside a workgroup already do).
+struct SlicePart {
+  float m;                          // slice maximum (-inf when empty)
+  int am;                           // smallest index of it (V when empty)
+  int bad;                          // NaN or +inf seen
+  int pad;
+};
+static_assert(sizeof(SlicePart) == 16, "slice record layout");
+constexpr int kMaxSlices = 16;
+constexpr size_t kRowHistBytes = kBins * (sizeof(int) + sizeof(double));
+
+__host__ __device__ inline int slice_len(int V, int W) { return ((V + W - 1) / W + 3) & ~3; }
+
+__device__ __forceinline__ const float* row_ptr(const float* tgt, const float* dft, int b, int rho,
+                                                int k, int V) {
+  return rho <= k ? tgt + (static_cast<size_t>(b) * (k + 1) + rho) * V
+                  : dft + (static_cast<size_t>(b) * k + (rho - k - 1)) * V;
+}
+
+// The row's maximum, argmax and validity from its W slice records, merged in
+// slice order (the same in every thread and launch).
+__device__ __forceinline__ void merge_slices(const SlicePart* part, int W, float& mx, int& am,
+                                             int& bad) {
+  mx = -INFINITY;
+  am = 0x7FFFFFFF;
+  bad = 0;
+  for (int w = 0; w < W; ++w) {
+    const SlicePart q = part[w];
+    if (q.m > mx || (q.m == mx && q.am < am)) {
+      mx = q.m;
+      am = q.am;
+    }
+    bad |= q.bad;
+  }
+  bad |= mx == -INFINITY;
+}
+
+// grid (W, 2k+1, B): slice maximum, argmax, validity; clears the row's
+// histogram.
+__global__ __launch_bounds__(kThreads) void sampled_slice_max_kernel(
+    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V, int W,
+    SlicePart* __restrict__ parts, char* __restrict__ hist) {
+  __shared__ float msh[kThreads];
+  __shared__ int ash[kThreads];
+  __shared__ int bsh[kThreads];
+  const int tid = threadIdx.x;
+  const int w = blockIdx.x, rho = blockIdx.y, b = blockIdx.z;
+  const int L = slice_len(V, W);
+  const int v0 = w * L;
+  const int n = v0 < V ? min(L, V - v0) : 0;
+  const float* row = row_ptr(tgt, dft, b, rho, k, V);
+  {
+    char* h = hist + (static_cast<size_t>(b) * gridDim.y + rho) * kRowHistBytes;
+    for (int j = w * kThreads + tid; j < kBins; j += W * kThreads) {
+      reinterpret_cast<int*>(h)[j] = 0;
+      reinterpret_cast<double*>(h + kBins * sizeof(int))[j] = 0.0;
+    }
+  }
+  float mx = -INFINITY;
+  int am = V;
+  int bad = 0;
+  scan_span(row + v0, n, (V & 3) == 0, [&](float x, int v) {
+    bad |= (x != x) | (x == INFINITY);
+    if (x > mx || (x == mx && v0 + v < am)) {
+      mx = x;
+      am = v0 + v;
+    }
+  });
+  msh[tid] = mx;
+  ash[tid] = am;
+  bsh[tid] = bad;
+  __syncthreads();
+  for (int h = kThreads / 2; h > 0; h >>= 1) {
+    if (tid < h) {
+      const float o = msh[tid + h];
+      const int oa = ash[tid + h];
+      if (o > msh[tid] || (o == msh[tid] && oa < ash[tid])) {
+        msh[tid] = o;
+        ash[tid] = oa;
+      }
+      bsh[tid] |= bsh[tid + h];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    SlicePart q;
+    q.m = msh[0];
+    q.am = ash[0];
+    q.bad = bsh[0];
+    q.pad = 0;
+    parts[(static_cast<size_t>(b) * gridDim.y + rho) * W + w] = q;
+  }
+}
+
+// grid (W, 2k+1, B): with truncation, the slice's bin counts and binary64
+// masses below the row maximum, added into the row's histogram; without, the
+// slice's whole mass.  Nothing for a row that fails its check.
+__global__ __launch_bounds__(kThreads) void sampled_slice_bins_kernel(
+    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V, int W, float T,
+    int trunc, const SlicePart* __restrict__ parts, double* __restrict__ slice_s,
+    char* __restrict__ hist) {
+  __shared__ int hcnt[kBins];
+  __shared__ double hmass[kBins];
+  __shared__ double dsh[kThreads];
+  const int tid = threadIdx.x;
+  const int w = blockIdx.x, rho = blockIdx.y, b = blockIdx.z;
+  const size_t rid = static_cast<size_t>(b) * gridDim.y + rho;
+  float mx;
+  int am, bad;
+  merge_slices(parts + rid * W, W, mx, am, bad);
+  if (bad) return;
+  const int L = slice_len(V, W);
+  const int v0 = w * L;
+  const int n = v0 < V ? min(L, V - v0) : 0;
+  const float* row = row_ptr(tgt, dft, b, rho, k, V) + v0;
+  const bool vec = (V & 3) == 0;
+  if (!trunc) {
+    double s = 0.0;
+    scan_span(row, n, vec, [&](float x, int) { s += mass(x, mx, T); });
+    s = block_sum(s, dsh);
+    if (tid == 0) slice_s[rid * W + w] = s;
+    return;
+  }
+  for (int j = tid; j < kBins; j += kThreads) {
+    hcnt[j] = 0;
+    hmass[j] = 0.0;
+  }
+  __syncthreads();
+  scan_span(row, n, vec, [&](float x, int) {
+    const int bn = bin_of(x, mx);
+    atomicAdd(&hcnt[bn], 1);
+    atomicAdd(&hmass[bn], mass(x, mx, T));
+  });
+  __syncthreads();
+  char* h = hist + rid * kRowHistBytes;
+  int* gc = reinterpret_cast<int*>(h);
+  double* gm = reinterpret_cast<double*>(h + kBins * sizeof(int));
+  for (int j = tid; j < kBins; j += kThreads) {
+    const int c = hcnt[j];
+    if (c != 0) {
+      atomicAdd(&gc[j], c);
+      atomicAdd(&gm[j], hmass[j]);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
     const float* __restrict__ tgt, const float* __restrict__ dft, const int32_t* __restrict__ toks,
-    int k, int V, float temperature, int top_k, float top_p, SampledRow* __restrict__ rows) {
+    int k, int V, float temperature, int top_k, float top_p, int W,
+    const SlicePart* __restrict__ parts, const double* __restrict__ slice_s,
+    const char* __restrict__ hist, SampledRow* __restrict__ rows) {
   __shared__ double dsh[kThreads];
   __shared__ double above_sh;
   __shared__ int ish[kThreads + 1];
@@ -491,37 +636,42 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
   SampledRow out = {};
 
   // maximum, argmax (smallest index among equal maxima), validity
+  const size_t rid = static_cast<size_t>(b) * R + rho;
   float mx = -INFINITY;
   int am = V;
   int bad = 0;
-  scan_row(row, V, [&](float x, int v) {
-    bad |= (x != x) | (x == INFINITY);
-    if (x > mx || (x == mx && v < am)) {
-      mx = x;
-      am = v;
-    }
-  });
-  // (the maxima go through dsh, the indices through hcnt, both free here)
-  dsh[tid] = mx;
-  hcnt[tid] = am;
-  ish[tid] = bad;
-  __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) {
-      const double o = dsh[tid + w];
-      const int oa = hcnt[tid + w];
-      if (o > dsh[tid] || (o == dsh[tid] && oa < hcnt[tid])) {
-        dsh[tid] = o;
-        hcnt[tid] = oa;
+  if (W > 1) {
+    merge_slices(parts + rid * W, W, mx, am, bad);
+  } else {
+    scan_row(row, V, [&](float x, int v) {
+      bad |= (x != x) | (x == INFINITY);
+      if (x > mx || (x == mx && v < am)) {
+        mx = x;
+        am = v;
       }
-      ish[tid] |= ish[tid + w];
+    });
+    // (the maxima go through dsh, the indices through hcnt, both free here)
+    dsh[tid] = mx;
+    hcnt[tid] = am;
+    ish[tid] = bad;
+    __syncthreads();
+    for (int w = kThreads / 2; w > 0; w >>= 1) {
+      if (tid < w) {
+        const double o = dsh[tid + w];
+        const int oa = hcnt[tid + w];
+        if (o > dsh[tid] || (o == dsh[tid] && oa < hcnt[tid])) {
+          dsh[tid] = o;
+          hcnt[tid] = oa;
+        }
+        ish[tid] |= ish[tid + w];
+      }
+      __syncthreads();
     }
+    mx = static_cast<float>(dsh[0]);
+    am = hcnt[0];
+    bad = ish[0] | (mx == -INFINITY);
     __syncthreads();
   }
-  mx = static_cast<float>(dsh[0]);
-  am = hcnt[0];
-  bad = ish[0] | (mx == -INFINITY);
-  __syncthreads();
   out.m = mx;
   out.argmax = am;
   out.status = bad ? 2 : 0;
@@ -540,22 +690,34 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
   const bool trunc_p = top_p < 1.f;
   double s = 0.0;                               // kept mass
   if (!trunc_k && !trunc_p) {
-    scan_row(row, V, [&](float x, int) { s += mass(x, mx, T); });
-    s = block_sum(s, dsh);
+    if (W > 1) {
+      for (int w = 0; w < W; ++w) s += slice_s[rid * W + w];
+    } else {
+      scan_row(row, V, [&](float x, int) { s += mass(x, mx, T); });
+      s = block_sum(s, dsh);
+    }
   } else {
     // Bins of 1/32 logit below the maximum (monotone in the logit): counts
     // and binary64 masses.  The boundary bin of each truncation is then
     // resolved exactly from its tokens, sorted in LDS.
-    for (int j = tid; j < kBins; j += kThreads) {
-      hcnt[j] = 0;
-      hmass[j] = 0.0;
+    if (W > 1) {
+      const char* h = hist + rid * kRowHistBytes;
+      for (int j = tid; j < kBins; j += kThreads) {
+        hcnt[j] = reinterpret_cast<const int*>(h)[j];
+        hmass[j] = reinterpret_cast<const double*>(h + kBins * sizeof(int))[j];
+      }
+    } else {
+      for (int j = tid; j < kBins; j += kThreads) {
+        hcnt[j] = 0;
+        hmass[j] = 0.0;
+      }
+      __syncthreads();
+      scan_row(row, V, [&](float x, int) {
+        const int bn = bin_of(x, mx);
+        atomicAdd(&hcnt[bn], 1);
+        atomicAdd(&hmass[bn], mass(x, mx, T));
+      });
     }
-    __syncthreads();
-    scan_row(row, V, [&](float x, int) {
-      const int bn = bin_of(x, mx);
-      atomicAdd(&hcnt[bn], 1);
-      atomicAdd(&hmass[bn], mass(x, mx, T));
-    });
     __syncthreads();
     bool exact = true;
     int bk = kBins, rk = 0;                     // top-k: boundary bin, kept tokens in it
@@ -907,15 +1069,37 @@ __global__ __launch_bounds__(kThreads) void sampled_select_kernel(
 }  // namespace
 
 namespace {
+// Slices per row: enough workgroups to cover the chip when a call has fewer
+// rows than compute units and rows are long; else one workgroup per row.
+// (about four workgroups per compute unit, slices of 2048 tokens at least).
+int row_slices(int B, int k, int V) {
+  const long long rows = static_cast<long long>(B) * (2 * k + 1);
+  if (rows >= 256 || V < 16384) return 1;
+  long long w = (1024 + rows - 1) / rows;
+  if (w > kMaxSlices) w = kMaxSlices;
+  if (w > V / 2048) w = V / 2048;
+  return static_cast<int>(w);
+}
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 struct SampledWs {
-  size_t rows_off, dec_off, tot_off, bytes;
+  size_t rows_off, dec_off, tot_off, part_off, ss_off, hist_off, bytes;
+  int W;
 };
 SampledWs sampled_ws(int B, int k, int V) {
   SampledWs w;
+  const size_t nrow = static_cast<size_t>(B) * (2 * k + 1);
+  w.W = row_slices(B, k, V);
   w.rows_off = 0;
-  w.dec_off = (static_cast<size_t>(B) * (2 * k + 1) * sizeof(SampledRow) + 255) / 256 * 256;
-  w.tot_off = (w.dec_off + static_cast<size_t>(B) * sizeof(SampledDecision) + 255) / 256 * 256;
+  w.dec_off = align256(nrow * sizeof(SampledRow));
+  w.tot_off = align256(w.dec_off + static_cast<size_t>(B) * sizeof(SampledDecision));
   w.bytes = w.tot_off + static_cast<size_t>(B) * 2 * res_blocks(V) * sizeof(double);
+  w.part_off = w.ss_off = w.hist_off = 0;
+  if (w.W > 1) {
+    w.part_off = align256(w.bytes);
+    w.ss_off = align256(w.part_off + nrow * w.W * sizeof(SlicePart));
+    w.hist_off = align256(w.ss_off + nrow * w.W * sizeof(double));
+    w.bytes = w.hist_off + nrow * kRowHistBytes;
+  }
   // temperature 0 runs as a chain tree, whose span partials share the space
   const size_t chain = sv_greedy_chain_workspace_bytes(B, k, V);
   if (chain > w.bytes) w.bytes = chain;
@@ -963,9 +1147,22 @@ extern "C" sv_status sv_verify_sampled(const float* target_logits, const float* 
   if (T == 0.f)
     return sv_greedy_chain(target_logits, draft_tokens, B, k, V, out_tokens, out_n_acc,
                            out_status, p_at, q_at, workspace, stream);
+  SlicePart* parts = reinterpret_cast<SlicePart*>(ws + L.part_off);
+  double* slice_s = reinterpret_cast<double*>(ws + L.ss_off);
+  char* hist = ws + L.hist_off;
+  if (L.W > 1) {
+    const int trunc = (sampling->top_k > 0 && sampling->top_k < V) || sampling->top_p < 1.f;
+    hipLaunchKernelGGL(sampled_slice_max_kernel, dim3(L.W, 2 * k + 1, B), dim3(kThreads), 0,
+                       stream, target_logits, draft_logits, k, V, L.W, parts, hist);
+    SV_LAUNCH_CHECK();
+    hipLaunchKernelGGL(sampled_slice_bins_kernel, dim3(L.W, 2 * k + 1, B), dim3(kThreads), 0,
+                       stream, target_logits, draft_logits, k, V, L.W, T, trunc, parts, slice_s,
+                       hist);
+    SV_LAUNCH_CHECK();
+  }
   hipLaunchKernelGGL(sampled_rows_kernel, dim3(2 * k + 1, B), dim3(kThreads), 0, stream,
                      target_logits, draft_logits, draft_tokens, k, V, T, sampling->top_k,
-                     sampling->top_p, rows);
+                     sampling->top_p, L.W, parts, slice_s, hist, rows);
   SV_LAUNCH_CHECK();
   hipLaunchKernelGGL(sampled_decide_kernel, dim3(B), dim3(kThreads), 0, stream, draft_tokens, k,
                      V, rows, static_cast<unsigned int>(seed & 0xFFFFFFFFu),
