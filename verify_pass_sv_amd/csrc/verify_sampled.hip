@@ -475,6 +475,7 @@ struct SlicePart {
 };
 static_assert(sizeof(SlicePart) == 16, "slice record layout");
 constexpr int kMaxSlices = 16;
+static_assert(kMaxSlices <= 64, "one slice record per lane");
 constexpr size_t kRowHistBytes = kBins * (sizeof(int) + sizeof(double));
 
 __host__ __device__ inline int slice_len(int V, int W) { return ((V + W - 1) / W + 3) & ~3; }
@@ -486,19 +487,25 @@ __device__ __forceinline__ const float* row_ptr(const float* tgt, const float* d
 }
 
 // The row's maximum, argmax and validity from its W slice records, merged in
-// slice order (the same in every thread and launch).
+// slice order (the same in every thread and launch).  Called by whole waves.
 __device__ __forceinline__ void merge_slices(const SlicePart* part, int W, float& mx, int& am,
                                              int& bad) {
+  // lane w loads slice w's record (all W loads in flight at once); every
+  // lane then merges the W records in order
+  const int lane = threadIdx.x & 63;
+  SlicePart mine = {-INFINITY, 0x7FFFFFFF, 0, 0};
+  if (lane < W) mine = part[lane];
   mx = -INFINITY;
   am = 0x7FFFFFFF;
   bad = 0;
   for (int w = 0; w < W; ++w) {
-    const SlicePart q = part[w];
-    if (q.m > mx || (q.m == mx && q.am < am)) {
-      mx = q.m;
-      am = q.am;
+    const float m = __shfl(mine.m, w, 64);
+    const int a = __shfl(mine.am, w, 64);
+    if (m > mx || (m == mx && a < am)) {
+      mx = m;
+      am = a;
     }
-    bad |= q.bad;
+    bad |= __shfl(mine.bad, w, 64);
   }
   bad |= mx == -INFINITY;
 }
@@ -1071,11 +1078,12 @@ __global__ __launch_bounds__(kThreads) void sampled_select_kernel(
 namespace {
 // Slices per row: enough workgroups to cover the chip when a call has fewer
 // rows than compute units and rows are long; else one workgroup per row.
-// (about four workgroups per compute unit, slices of 2048 tokens at least).
+// (up to four 512-thread workgroups per compute unit, which one round of the
+// chip holds; slices of 2048 tokens at least).
 int row_slices(int B, int k, int V) {
   const long long rows = static_cast<long long>(B) * (2 * k + 1);
   if (rows >= 256 || V < 16384) return 1;
-  long long w = (1024 + rows - 1) / rows;
+  long long w = 1024 / rows;
   if (w > kMaxSlices) w = kMaxSlices;
   if (w > V / 2048) w = V / 2048;
   return static_cast<int>(w);
