@@ -431,8 +431,9 @@ sv_status sv_verify_sampled(const float* target_logits, const float* draft_logit
  * Explained, "Accept from left to right" and "Correct and continue").
  *
  * Defines, per independent trial b and position i = 0..k:
- *   u_i[v] = Philox4x32-10 word 0 with key = (seed & 0xffffffff, seed >> 32)
- *            and counter (v, i, b, 3 + 256 * offset), as (word >> 8) * 2^-24
+ *   u_i[v] = Philox4x32-10 word (v mod 4) with key = (seed & 0xffffffff,
+ *            seed >> 32) and counter (v / 4, i, b, 3 + 256 * offset), as
+ *            (word >> 8) * 2^-24: one counter serves four consecutive entries
  *   g_i[v] = -log(-log u_i[v])  (binary64; u = 0 gives -inf)
  *   c_i    = argmax_v (target[b, i, v] + g_i[v]), the smallest index among
  *            equal scores (a draw from softmax(target[b, i, :]))

@@ -12,9 +12,11 @@ there; after k agreements the target supplies one more.
 Readings taken where the pages are silent:
 
 1. Noise: position i of trial b draws one uniform per vocabulary entry v from
-   Philox4x32-10 (the generator of philox.py) with key = seed and counter
-   (v, i, b, 3 + 256 * offset), word 0, u = (w >> 8) 2^-24.  The Gumbel noise
-   is g = -log(-log(u)) in binary64; u = 0 gives g = -inf (never chosen).
+   Philox4x32-10 (the generator of philox.py) with key = seed: entry v takes
+   word v mod 4 of counter (floor(v / 4), i, b, 3 + 256 * offset), as
+   u = (w >> 8) 2^-24, so one counter serves four consecutive entries.  The
+   Gumbel noise is g = -log(-log(u)) in binary64; u = 0 gives g = -inf
+   (never chosen).
 2. The target's choice at position i is argmax_v (l_i[v] + g_i[v]) with the
    logit in binary64, the smallest index among equal scores.  The Gumbel-max
    trick makes it a draw from softmax(l_i).  The drafter draws its token with
@@ -47,13 +49,14 @@ NEAR_TIE_COUPLED = 1e-9
 def gumbel_noise(seed, trial, position, V, offset=0):
     """Binary64 Gumbel noise of one position (reading 1), length V."""
     seed = int(seed)
-    v = np.arange(V, dtype=np.uint64)
-    ctr = np.stack([v,
-                    np.full_like(v, int(position) & 0xFFFFFFFF),
-                    np.full_like(v, int(trial) & 0xFFFFFFFF),
-                    np.full_like(v, (TAG_COUPLED + 256 * int(offset)) & 0xFFFFFFFF)], axis=-1)
+    g = np.arange((V + 3) // 4, dtype=np.uint64)          # counter of entries 4g .. 4g+3
+    ctr = np.stack([g,
+                    np.full_like(g, int(position) & 0xFFFFFFFF),
+                    np.full_like(g, int(trial) & 0xFFFFFFFF),
+                    np.full_like(g, (TAG_COUPLED + 256 * int(offset)) & 0xFFFFFFFF)], axis=-1)
     key = np.array([seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF], dtype=np.uint64)
-    u = uniforms24(philox4x32_10(ctr, key)[:, 0])
+    words = philox4x32_10(ctr, key)                       # [counters, 4]: word v mod 4
+    u = uniforms24(words.reshape(-1)[:V])
     with np.errstate(divide="ignore"):
         return -np.log(-np.log(u))
 

@@ -76,6 +76,20 @@ def test_noise_is_standard_gumbel_and_varies_with_the_counter():
         assert not np.array_equal(base, other)
 
 
+def test_noise_takes_four_words_per_counter():
+    # entry v: word v mod 4 of counter (v // 4, position, trial, tag), so the
+    # four entries of one counter differ and entry 4 starts the next counter
+    from oracle.philox import philox4x32_10, uniforms24
+    seed, trial, pos = 11, 2, 5
+    g = gumbel_noise(seed, trial, pos, 10)
+    key = np.array([seed, 0], dtype=np.uint64)
+    for v in (0, 3, 4, 9):
+        w = philox4x32_10(np.array([[v // 4, pos, trial, 3]], dtype=np.uint64), key)[0, v % 4]
+        u = float(uniforms24(np.array([w]))[0])
+        assert abs(g[v] + math.log(-math.log(u))) <= 1e-14 * max(1.0, abs(g[v]))
+    assert len(set(g[:4].tolist())) == 4
+
+
 def test_dominant_logits_give_the_emit_rule():
     k, V = 4, 12
     t = np.zeros((k + 1, V))

@@ -18,8 +18,9 @@
 //  1. choose  one workgroup per (4096-entry vocabulary span, target row,
 //             trial): the best score over the span -- l + g with the Gumbel
 //             noise g = -log(-log u) in binary64 from the Philox uniform of
-//             counter (v, i, b, 3 + 256 offset) for coupled verification, l
-//             alone for the tree; partial (score, index, validity).
+//             word v mod 4 of counter (v / 4, i, b, 3 + 256 offset) for
+//             coupled verification, l alone for the tree; partial (score,
+//             index, validity).
 //  2. decide  one wave per trial: lane r merges the spans of target row r
 //             (score down, index up), then the status checks and
 //             coupled: the first disagreement (one ballot);
@@ -92,32 +93,51 @@ __global__ __launch_bounds__(kThreads) void choose_kernel(
   double best = -INFINITY;
   int bi = V;
   int flags = 0;
-  // every load of the thread's 16 entries goes out before any is used
-  constexpr int kPer = kSpan / kThreads;
-  float xs[kPer];
+  // the thread's 16 entries are 4 runs of 4 consecutive ones (one Philox
+  // counter each, its four words for the four entries); every load goes out
+  // before any is used
+  constexpr int kRuns = kSpan / (4 * kThreads);
+  const bool vec = (V & 3) == 0;                // rows 16-byte aligned
+  float xs[kRuns][4];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int v = v0 + tid + j * kThreads;
-    xs[j] = v < v1 ? row[v] : 0.f;
+  for (int g = 0; g < kRuns; ++g) {
+    const int vb = v0 + 4 * (tid + g * kThreads);
+    if (vec) {
+      // V % 4 == 0 makes v1 a multiple of 4: the whole run is in the span
+      const float4 a = vb < v1 ? *reinterpret_cast<const float4*>(row + vb)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+      xs[g][0] = a.x;
+      xs[g][1] = a.y;
+      xs[g][2] = a.z;
+      xs[g][3] = a.w;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xs[g][q] = vb + q < v1 ? row[vb + q] : 0.f;
+    }
   }
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int v = v0 + tid + j * kThreads;
-    if (v >= v1) break;
-    const float x = xs[j];
-    flags |= ((x != x) | (x == INFINITY)) ? 1 : 0;
-    flags |= (x > -INFINITY && x < INFINITY) ? 2 : 0;
-    double sc = static_cast<double>(x);
-    if constexpr (NOISE) {
-      unsigned int c[4] = {static_cast<unsigned int>(v), static_cast<unsigned int>(i),
-                           static_cast<unsigned int>(b), tagword};
-      sv_philox_rounds(c, key0, key1);
-      const double u = static_cast<double>(sv_u24(c[0]));   // 24 bits: exact
-      sc += -log(-log(u));                                   // u = 0: -inf
-    }
-    if (better(sc, v, best, bi)) {
-      best = sc;
-      bi = v;
+  for (int g = 0; g < kRuns; ++g) {
+    const int vb = v0 + 4 * (tid + g * kThreads);
+    if (vb >= v1) break;
+    unsigned int c[4] = {static_cast<unsigned int>(vb >> 2), static_cast<unsigned int>(i),
+                         static_cast<unsigned int>(b), tagword};
+    if constexpr (NOISE) sv_philox_rounds(c, key0, key1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int v = vb + q;
+      if (v >= v1) break;
+      const float x = xs[g][q];
+      flags |= ((x != x) | (x == INFINITY)) ? 1 : 0;
+      flags |= (x > -INFINITY && x < INFINITY) ? 2 : 0;
+      double sc = static_cast<double>(x);
+      if constexpr (NOISE) {
+        const double u = static_cast<double>(sv_u24(c[q]));  // 24 bits: exact
+        sc += -log(-log(u));                                 // u = 0: -inf
+      }
+      if (better(sc, v, best, bi)) {
+        best = sc;
+        bi = v;
+      }
     }
   }
   ssh[tid] = best;
