@@ -91,6 +91,24 @@ def test_full_vocab_k32():
     assert _compare(out, res) == 0
 
 
+@pytest.mark.parametrize("V", [5000, 4099])
+def test_screened_noise_edge_rows(V):
+    # the choose launch screens entries in binary32 before the binary64
+    # noise: large scores (the margin's relative part), widely spread
+    # logits, rows of -inf with a few equal finite entries, all-equal rows
+    # (the noise alone decides), and a ragged last span
+    B, k = 8, 3
+    tgt, dft, _ = synth.accept_inputs(B, k, V, seed=29, sigma=1.0)
+    tgt[0] += 1.0e6
+    tgt[1] = -tgt[1].abs() * 1.0e4
+    tgt[2, :, :] = float("-inf")
+    tgt[2, :, ::97] = 0.5
+    tgt[3] = 2.0
+    tok = torch.from_numpy(oracle.coupled_drafts(dft.numpy(), 9))
+    out, res = _run(tgt, tok, seed=9)
+    assert _compare(out, res) <= 1
+
+
 def test_invalid_inputs_report_status():
     B, k, V = 5, 3, 50
     tgt, _, tok = synth.accept_inputs(B, k, V, seed=5, sigma=1.0)

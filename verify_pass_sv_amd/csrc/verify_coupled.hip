@@ -83,6 +83,7 @@ __global__ __launch_bounds__(kThreads) void choose_kernel(
   __shared__ double ssh[kThreads];
   __shared__ int ish[kThreads];
   __shared__ int fsh[kThreads];
+  __shared__ double wmax[kThreads / 64];
   const int tid = threadIdx.x;
   const int span = blockIdx.x;
   const int i = blockIdx.y;
@@ -115,28 +116,80 @@ __global__ __launch_bounds__(kThreads) void choose_kernel(
       for (int q = 0; q < 4; ++q) xs[g][q] = vb + q < v1 ? row[vb + q] : 0.f;
     }
   }
+  if constexpr (NOISE) {
+    // Screen in binary32: g32 = -logf(-logf(u)) is within 4e-6 of the
+    // binary64 noise for every 24-bit u (logf within 1 ulp; -log u in
+    // [6e-8, 16.7]).  With M the workgroup's best screened score, the
+    // binary64 winner's screened score is at least M - 2 margin, so only
+    // entries at or above that take the binary64 logarithms.
+    double ap[kRuns][4];
+    unsigned int wd[kRuns][4];
+    double m = -INFINITY;
 #pragma unroll
-  for (int g = 0; g < kRuns; ++g) {
-    const int vb = v0 + 4 * (tid + g * kThreads);
-    if (vb >= v1) break;
-    unsigned int c[4] = {static_cast<unsigned int>(vb >> 2), static_cast<unsigned int>(i),
-                         static_cast<unsigned int>(b), tagword};
-    if constexpr (NOISE) sv_philox_rounds(c, key0, key1);
+    for (int g = 0; g < kRuns; ++g) {
+      const int vb = v0 + 4 * (tid + g * kThreads);
+      unsigned int c[4] = {static_cast<unsigned int>(vb >> 2), static_cast<unsigned int>(i),
+                           static_cast<unsigned int>(b), tagword};
+      sv_philox_rounds(c, key0, key1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int v = vb + q;
-      if (v >= v1) break;
-      const float x = xs[g][q];
-      flags |= ((x != x) | (x == INFINITY)) ? 1 : 0;
-      flags |= (x > -INFINITY && x < INFINITY) ? 2 : 0;
-      double sc = static_cast<double>(x);
-      if constexpr (NOISE) {
-        const double u = static_cast<double>(sv_u24(c[q]));  // 24 bits: exact
-        sc += -log(-log(u));                                 // u = 0: -inf
+      for (int q = 0; q < 4; ++q) {
+        const float x = xs[g][q];
+        const bool in = vb + q < v1;
+        wd[g][q] = c[q];
+        const float g32 = -logf(-logf(sv_u24(c[q])));
+        const double a = static_cast<double>(x) + static_cast<double>(g32);
+        ap[g][q] = a;
+        if (in) {
+          flags |= ((x != x) | (x == INFINITY)) ? 1 : 0;
+          flags |= (x > -INFINITY && x < INFINITY) ? 2 : 0;
+          if (a > m) m = a;                       // NaN never
+        }
       }
-      if (better(sc, v, best, bi)) {
-        best = sc;
-        bi = v;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const double t = __shfl_xor(m, o, 64);
+      if (t > m) m = t;
+    }
+    if ((tid & 63) == 0) wmax[tid >> 6] = m;
+    __syncthreads();
+    double M = wmax[0];
+    for (int w = 1; w < kThreads / 64; ++w)
+      if (wmax[w] > M) M = wmax[w];
+    const double thr = isinf(M) ? M : M - 2.0 * (1e-4 + fabs(M) * 0x1p-40);
+#pragma unroll
+    for (int g = 0; g < kRuns; ++g) {
+      const int vb = v0 + 4 * (tid + g * kThreads);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int v = vb + q;
+        if (v < v1 && ap[g][q] >= thr) {
+          const double u = static_cast<double>(sv_u24(wd[g][q]));  // 24 bits: exact
+          const double sc = static_cast<double>(xs[g][q]) - log(-log(u));   // u = 0: -inf
+          if (better(sc, v, best, bi)) {
+            best = sc;
+            bi = v;
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < kRuns; ++g) {
+      const int vb = v0 + 4 * (tid + g * kThreads);
+      if (vb >= v1) break;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int v = vb + q;
+        if (v >= v1) break;
+        const float x = xs[g][q];
+        flags |= ((x != x) | (x == INFINITY)) ? 1 : 0;
+        flags |= (x > -INFINITY && x < INFINITY) ? 2 : 0;
+        const double sc = static_cast<double>(x);
+        if (better(sc, v, best, bi)) {
+          best = sc;
+          bi = v;
+        }
       }
     }
   }
