@@ -240,7 +240,12 @@ def main():
                     help="copy kernel + read probe + 2 eager W4 passes, then exit")
     ap.add_argument("--profile-accept", action="store_true",
                     help="copy kernel + eager sv_verify_accept calls (V=152000), then exit")
-    ap.add_argument("--trials", type=int, default=1, help="B of --profile-accept")
+    ap.add_argument("--trials", type=int, default=1,
+                    help="B of --profile-accept and --profile-verify")
+    ap.add_argument("--profile-verify", choices=("sampled", "coupled", "tree"),
+                    help="copy kernel + eager calls of one verification rule "
+                         "(V=152000; sampled at T=0.7, top-p 0.9; tree with --k nodes), "
+                         "then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
@@ -271,6 +276,36 @@ def main():
             sv.sv_verify_accept(t, d, tk, seed=i, out=out, workspace=ws)
         torch.cuda.synchronize()
         log(f"profile-accept: {calls} calls at B={B}, k={k}, V={VOCAB}")
+        return
+    if args.profile_verify:
+        src = torch.empty(1 << 28, dtype=torch.uint8, device=dev).random_(0, 255)
+        dst = torch.empty_like(src)
+        dst.copy_(src)  # plain copy kernel of 256 MiB (counter scale reference)
+        B, rule = args.trials, args.profile_verify
+        out = {"tokens": torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+               "n_acc": torch.empty((B,), dtype=torch.int32, device=dev),
+               "status": torch.empty((B,), dtype=torch.int32, device=dev)}
+        if rule == "tree":
+            t, tk, par = synth.tree_inputs(B, k, VOCAB, seed=61 + B + k, device=dev)
+            ws = torch.empty(max(16, sv.sv_verify_tree_workspace_bytes(B, k, VOCAB)),
+                             dtype=torch.uint8, device=dev)
+            call = lambda i: sv.sv_verify_tree(t, tk, par, out=out, workspace=ws)
+        else:
+            t, d, tk = synth.accept_inputs(B, k, VOCAB, seed=41 + B, sigma=1.0, device=dev)
+            if rule == "sampled":
+                ws = torch.empty(max(16, sv.sv_verify_sampled_workspace_bytes(B, k, VOCAB)),
+                                 dtype=torch.uint8, device=dev)
+                call = lambda i: sv.sv_verify_sampled(t, d, tk, i, 0, 0.7, 0, 0.9, out=out,
+                                                      workspace=ws)
+            else:
+                ws = torch.empty(max(16, sv.sv_verify_coupled_workspace_bytes(B, k, VOCAB)),
+                                 dtype=torch.uint8, device=dev)
+                call = lambda i: sv.sv_verify_coupled(t, tk, i, 0, out=out, workspace=ws)
+        calls = 20 if B == 1 else 4
+        for i in range(calls):
+            call(i)
+        torch.cuda.synchronize()
+        log(f"profile-verify: {calls} {rule} calls at B={B}, k={k}, V={VOCAB}")
         return
     log(f"device {torch.cuda.get_device_name(0)}; building W4 stack")
     w4 = make_w4_stack(torch, synth, sv, dev)

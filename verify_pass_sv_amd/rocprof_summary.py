@@ -28,6 +28,7 @@ KERNEL_SOURCES = {
     "pass_kernel": ["csrc/pass.hip", "csrc/w4_packed_dev.h", "csrc/sv_common.h"],
     "stats_kernel": ["csrc/verify_accept.hip", "csrc/sv_common.h", "csrc/sv_philox.h"],
     "decide_kernel": ["csrc/verify_accept.hip", "csrc/sv_common.h", "csrc/sv_philox.h"],
+    "sampled_rows_kernel": ["csrc/verify_sampled.hip", "csrc/sv_common.h", "csrc/sv_philox.h"],
 }
 
 
