@@ -39,6 +39,7 @@ from .coupled import (gumbel_noise, coupled_choice, coupled_trial, verify_couple
 from .tree import tree_trial, verify_tree
 from .lmhead import (group_softmax_stats, merge_group_stats, lm_head_logits, lm_head_verify,
                      NEAR_TIE_LMHEAD)
+from .chain import bf16_rne, glue as chain_glue, glue_candidates as chain_glue_candidates
 from .roofline import (tokens_per_s_bound, w4_bytes_per_weight,
                        decoder_stack_shapes, stack_weight_count,
                        stack_weight_bytes_w4, stack_weight_bytes_w8)
@@ -54,7 +55,7 @@ __all__ = [
     "coupled_choice", "coupled_trial", "verify_coupled", "coupled_drafts",
     "NEAR_TIE_COUPLED", "tree_trial", "verify_tree", "group_softmax_stats",
     "merge_group_stats", "lm_head_logits", "lm_head_verify", "NEAR_TIE_LMHEAD",
-    "tokens_per_s_bound",
+    "tokens_per_s_bound", "bf16_rne", "chain_glue", "chain_glue_candidates",
     "w4_bytes_per_weight", "decoder_stack_shapes", "stack_weight_count",
     "stack_weight_bytes_w4", "stack_weight_bytes_w8",
 ]

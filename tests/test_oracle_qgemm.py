@@ -7,6 +7,7 @@ activations, and the agreement of the integer route with the float route.
 import numpy as np
 import pytest
 
+from oracle import f16_to_f64
 from oracle import (unpack_w4, dequant_w4, qgemm_w4, dequant_w8, qgemm_w8,
                     qgemm_w4_i8, group_int_partials, bf16_bits_to_f64)
 
@@ -28,6 +29,20 @@ def test_bf16_decode_bit_patterns():
     assert v[0] == 1.0 and v[1] == -2.0
     assert v[2] == 2.0 ** -126 and v[3] == 2.0 ** -133
     assert np.isinf(v[4]) and v[5] == 0.0
+
+
+def test_f16_decode_raw_bit_patterns():
+    """f16_to_f64 on raw binary16 words (uint16 and int16 views) and on
+    numpy float16: 1.0, -2.0, the smallest normal 2^-14 and the smallest
+    subnormal 2^-24, +inf and -0."""
+    words = [0x3C00, 0xC000, 0x0400, 0x0001, 0x7C00, 0x8000]
+    want = [1.0, -2.0, 2.0 ** -14, 2.0 ** -24, np.inf, -0.0]
+    for arr in (np.array(words, dtype=np.uint16), np.array(words, dtype=np.uint16).view(np.int16),
+                np.array(words, dtype=np.uint16).view(np.float16)):
+        v = f16_to_f64(arr)
+        assert v.dtype == np.float64
+        assert v.tolist() == want
+        assert np.signbit(v[5])
 
 
 def test_w4_bruteforce_from_raw_bytes():
