@@ -22,7 +22,8 @@
  *     argument returns SV_ERR_* and nothing is enqueued.
  *   - Work is enqueued asynchronously on `stream` (NULL = the default
  *     stream).  A failed launch returns SV_ERR_HIP.
- *   - No global mutable state; calls are thread-safe.  Calls that share an
+ *   - Calls are thread-safe.  The only process-wide state is the registry of
+ *     plan ids (sv_pass_run), guarded by a mutex.  Calls that share an
  *     output or workspace buffer on one device must be ordered by the caller.
  *   - bf16 = bfloat16 (upper half of an IEEE binary32), f16 = IEEE binary16,
  *     passed as `const void*`.
@@ -198,8 +199,13 @@ sv_status sv_w8_pack(const int8_t* codes, int N, int K, uint8_t* packed_codes,
  *   descriptors' pointers; it stays valid while those buffers and `plan`
  *   live, for any number of launches.
  * sv_pass_run(pass, stream): enqueues the whole pass as one kernel launch on
- *   `stream` (capturable in a HIP graph).  A plan buffer that no longer holds
- *   the plan described by *pass makes the kernel return without writing.
+ *   `stream` (capturable in a HIP graph).  It returns SV_ERR_INVALID_ARG,
+ *   enqueuing nothing, when the plan buffer has been planned again since
+ *   *pass was filled (the library keeps, per plan buffer, the id of the last
+ *   plan written into it: process-wide state behind a mutex).  A kernel that
+ *   finds in the buffer a plan other than *pass describes (the caller
+ *   overwrote the buffer) computes nothing; a chain kernel also sets the
+ *   status word below.
  * Results are deterministic; they equal the single-GEMM entry points' up to
  * the order of the binary32 accumulation over K (the int32 group partials of
  * W4_I8 are exact).
@@ -221,17 +227,102 @@ typedef struct sv_pass {
   void* plan;       /* device plan buffer given to sv_pass_plan   */
   int format;       /* sv_pass_format                             */
   int m;            /* draft rows of every GEMM in the pass       */
-  int count;        /* number of GEMMs                            */
+  int count;        /* number of GEMMs (links of a chain)         */
   int grid;         /* workgroups of the launch                   */
-  int items;        /* work items over all GEMMs                  */
+  int items;        /* work items (rounds of a chain)             */
   int max_steps;    /* longest per-workgroup chunk count          */
   int stats;        /* 1 if some GEMM writes softmax statistics   */
+  int chain;        /* 1: planned by sv_pass_chain_plan           */
+  uint32_t id;      /* this plan's id in its buffer (see below)   */
 } sv_pass;
 
 size_t sv_pass_plan_bytes(int format, const sv_pass_gemm* gemms, int count, int m);
 sv_status sv_pass_plan(int format, const sv_pass_gemm* gemms, int count, int m, int group,
                        void* plan, size_t plan_bytes, sv_pass* pass, hipStream_t stream);
 sv_status sv_pass_run(const sv_pass* pass, hipStream_t stream);
+
+/*
+ * Plan status word.  The chain kernel of sv_pass_run writes it, in the plan
+ * buffer, when it cannot run the plan:
+ *   SV_PASS_STATUS_STALE    the buffer holds a chain plan other than the one
+ *                           *pass describes (format, m or grid differ);
+ *                           nothing was computed
+ *   SV_PASS_STATUS_TIMEOUT  a phase barrier of a chain waited longer than
+ *                           its bound (workgroups not resident together);
+ *                           the launch ended early, outputs are undefined,
+ *                           and the plan must be made again
+ * A buffer that holds no plan at all (its first word is not a plan's
+ * magic number) is not written.  sv_pass_status reads the word
+ * (synchronizes `stream`); sv_pass_plan and sv_pass_chain_plan clear it.
+ */
+#define SV_PASS_STATUS_STALE 1u
+#define SV_PASS_STATUS_TIMEOUT 2u
+#define SV_PASS_STATUS_OFFSET 36
+sv_status sv_pass_status(const sv_pass* pass, uint32_t* status, hipStream_t stream);
+
+/*
+ * Verify pass in model order: sv_pass_chain_plan / sv_pass_run.
+ *
+ * One forward pass hands each layer's output to the next layer (Karpathy's
+ * Trick ..., "How Uzu optimizes bytes and tokens per pass": the activations
+ * are the intermediate values passed between layers; "Why batch-one decoding
+ * is memory-bound": the pass reads every layer's weight blocks once).  A
+ * chain is an ordered array of links, each one W4 GEMM
+ *   y = x W^T                         (y f32 [m, N], fully overwritten)
+ * that may also write the bf16 input of a later link
+ *   xo = bf16_rne(alpha * y[:, :xo_cols])     (xo bf16 [m, xo_cols]).
+ * A link whose x IS an earlier link's xo (same pointer, K == xo_cols) starts
+ * only after every earlier link is complete on the whole device; other links
+ * follow without waiting.  The launch is one persistent kernel of one
+ * workgroup per compute unit; every link is spread over all of them, and
+ * the weights of later links stream while a link waits.  Every workgroup
+ * must be resident at once: run a chain alone on its device (a barrier that
+ * waits past its bound sets SV_PASS_STATUS_TIMEOUT).
+ *
+ * sv_pass_link (all pointers device):
+ *   x        bf16 [m, K], 16-byte aligned
+ *   codes    sv_w4_pack codes of W [N, K];  scales: sv_w4_pack scales/zeros
+ *   y        f32 [m, N]
+ *   xo       NULL (xo_cols == 0) or bf16 [m, xo_cols], 128-byte aligned
+ *   alpha    scale applied before the bf16 rounding of xo
+ *   K, N     K % 128 == 0, N % 16 == 0; xo_cols % 64 == 0, xo_cols <= N
+ * Buffer rules (SV_ERR_INVALID_ARG otherwise): an x that overlaps an earlier
+ * link's xo is exactly that xo; no xo overlaps the x of its own or an
+ * earlier link, or another xo; no y overlaps any x, xo or other y.  Later
+ * links may read only xo, never y, of earlier links.
+ * Formats: SV_PASS_W4 (W8 and W4_I8 return SV_ERR_UNSUPPORTED); group 64.
+ * sv_pass_chain_bytes: plan buffer bytes (0 if an argument is invalid); the
+ * plan buffer must be 256-byte aligned.  sv_pass_chain_plan validates,
+ * writes the plan (its barrier counters included) with `stream`,
+ * synchronizes, and fills *pass; the plan stays valid for any number of
+ * sv_pass_run launches on that stream order.  Results are deterministic:
+ * each y equals the single-GEMM product up to the order of the binary32
+ * accumulation over K, and xo is the binary32 product alpha * y rounded to
+ * nearest even in bf16.
+ */
+typedef struct sv_pass_link {
+  const void* x;
+  const uint8_t* codes;
+  const void* scales;
+  float* y;
+  void* xo;
+  float alpha;
+  int K;
+  int N;
+  int xo_cols;
+} sv_pass_link;
+
+size_t sv_pass_chain_bytes(int format, const sv_pass_link* links, int count, int m);
+/* The plan image sv_pass_chain_plan would upload, built on the host for a
+ * device of `cus` compute units into caller-owned HOST memory `image`
+ * (image_bytes >= the size sv_pass_chain_bytes reports for such a device);
+ * *grid receives the workgroup count.  Touches no device: for inspecting
+ * and testing the plan (its layout is internal to this library).  Same
+ * validation and status codes as sv_pass_chain_plan. */
+sv_status sv_pass_chain_image(int format, const sv_pass_link* links, int count, int m, int group,
+                              int cus, void* image, size_t image_bytes, int* grid);
+sv_status sv_pass_chain_plan(int format, const sv_pass_link* links, int count, int m, int group,
+                             void* plan, size_t plan_bytes, sv_pass* pass, hipStream_t stream);
 
 /*
  * sv_qgemm_w8 -- verify GEMM over 8-bit symmetric per-output-channel weights.

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     import verify_pass_sv_amd as sv
-    assert sv.sv_version() == 100
+    assert sv.sv_version() == 200
     assert sv.sv_status_str(0) == "SV_OK"
     assert sv.sv_status_str(5) == "SV_ERR_WORKSPACE"
     assert sv.sv_status_str(99) == "SV_ERR_UNKNOWN"

@@ -1,0 +1,286 @@
+"""GPU parity of the verify pass in model order (sv_pass_chain_plan +
+sv_pass_run): a chain of W4 GEMMs, each handing bf16(alpha * y) to the next,
+run in one launch with device-wide phase barriers.
+
+Source: Karpathy's Trick for Faster Local LLMs, "How Uzu optimizes bytes and
+tokens per pass" (the forward pass hands intermediate values from layer to
+layer) and "Why batch-one decoding is memory-bound".
+
+What is compared how:
+* Links whose x is a seeded input (every link of the independent-link test,
+  the first link of every chain): y against the binary64 oracle row-wise at
+  2e-3, and xo bit-exactly against the oracle's hand-off wherever the
+  binary64 result leaves the bf16 rounding unique; where the binary32
+  accumulation may fall on either side of a rounding boundary the GPU value
+  must be one of the two neighbours.
+* Links of a chain after the first: the trajectory of a chain is not unique
+  (bf16 re-rounding of binary32 sums differs from the binary64 chain in
+  about 1e-3 of the elements of the first hand-off, and the difference
+  grows to the bf16 noise level within a few links), so each later link is
+  checked for validity: its y against the oracle's product of the x the
+  chain handed to it, its xo bit-exactly against the oracle's hand-off of
+  its y.  The xo buffers are filled with NaN before the launch, so a link
+  that ran before its input was written fails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from verify_pass_sv_amd import synth
+from gpu_util import DEV, to_dev, bf16_bits, assert_rows_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _sv():
+    import verify_pass_sv_amd as sv
+    return sv
+
+
+def alpha_for(K):
+    """Keeps chained activations near unit scale for the synthetic weights:
+    E[w^2] = E[(c - z)^2] E[s^2] with c, z ~ U{0..15}, s ~ U(0.01, 0.05)."""
+    ew2 = (2 * 255 / 12.0) * ((0.05 ** 3 - 0.01 ** 3) / (3 * 0.04))
+    return float(np.float32(1.0 / np.sqrt(K * ew2)))
+
+
+def _weights(N, K, seed):
+    sv = _sv()
+    codes, scales, zeros = synth.w4_matrix(N, K, seed=seed)
+    pc, ps = sv.sv_w4_pack(*to_dev(codes, scales, zeros))
+    return (codes.numpy(), scales.numpy(), zeros.numpy()), pc, ps
+
+
+def _nan(shape, dtype):
+    return torch.full(shape, float("nan"), dtype=dtype, device=DEV)
+
+
+def _check_xo(xo_gpu, y64, x_bits, host, alpha, cols, what):
+    """xo of a link with seeded input: unique bf16 values exactly, boundary
+    cases one of the two neighbours.  The accumulation error bound is 2^-20
+    of the sum of |x w| per output."""
+    c, s, z = host
+    absw = np.abs(oracle.dequant_w4(c, s, z))
+    err = np.abs(oracle.bf16_bits_to_f64(x_bits)) @ absw.T * 2.0 ** -20
+    lo, hi = oracle.chain_glue_candidates(y64, err, alpha, cols)
+    got = bf16_bits(xo_gpu)
+    uniq = lo == hi
+    assert np.array_equal(got[uniq], lo[uniq]), f"{what}: xo differs where it is unique"
+    amb = ~uniq
+    assert np.all((got[amb] == lo[amb]) | (got[amb] == hi[amb])), f"{what}: xo off both sides"
+    assert amb.mean() < 0.05, f"{what}: {amb.mean():.3f} of xo near a boundary"
+
+
+# (K, N, xo_cols): one 128-k block (7 of 8 waves idle), a partial window of 5
+# blocks, two partial windows, four full windows; 40 to 240 tiles (the grid
+# is 40 workgroups: 1 to 6 tiles each, two rounds at m > 16)
+LINKS = [(640, 1920, 640), (128, 640, 640), (1920, 640, 0), (4096, 3840, 1920),
+         (1152, 1280, 1280)]
+
+
+@pytest.mark.parametrize("m", [1, 5, 16, 17, 32])
+def test_chain_links_match_oracle(m):
+    """Independent links (no barrier): every y and xo from seeded inputs."""
+    sv = _sv()
+    links, refs = [], []
+    for i, (K, N, cols) in enumerate(LINKS):
+        host, pc, ps = _weights(N, K, seed=700 + 13 * i + m)
+        x = synth.activations(m, K, seed=800 + i + m)
+        y = _nan((m, N), torch.float32)
+        xo = _nan((m, cols), torch.bfloat16) if cols else None
+        a = alpha_for(K)
+        links.append((x.to(DEV), pc, ps, N, y, xo, a))
+        refs.append((x, host, a, cols))
+    p = sv.sv_pass_chain_plan(links)
+    assert p.grid == 40 and p.info.chain == 1
+    sv.sv_pass_run(p)
+    torch.cuda.synchronize()
+    assert sv.sv_pass_status(p) == 0
+    for (K, N, cols), (x, pc, ps, _, y, xo, a), (xh, host, _a, _c) in zip(LINKS, links, refs):
+        xb = bf16_bits(xh)
+        y64 = oracle.qgemm_w4(xb, *host)
+        got = y.cpu().numpy()
+        assert np.isfinite(got).all()
+        assert_rows_close(got, y64, what=f"chain link m={m} K={K} N={N}")
+        if cols:
+            _check_xo(xo.cpu(), y64, xb, host, a, cols, f"m={m} K={K} N={N}")
+
+
+def _decoder_chain(layers, m, H, F, seed, h0=None):
+    """qkv -> o -> gate|up -> down per layer; each link's x is the previous
+    link's xo (q, gate and down part as the hand-off)."""
+    h = h0 if h0 is not None else synth.activations(m, H, seed=seed).to(DEV)
+    links, hosts = [], []
+    for layer in range(layers):
+        for i, (N, K, cols) in enumerate(((3 * H, H, H), (H, H, H), (2 * F, H, F), (H, F, H))):
+            host, pc, ps = _weights(N, K, seed=seed + 1000 * layer + i)
+            xo = _nan((m, cols), torch.bfloat16)
+            links.append((h, pc, ps, N, _nan((m, N), torch.float32), xo, alpha_for(K)))
+            hosts.append(host)
+            h = xo
+    return links, hosts
+
+
+def _check_chain(links, hosts, rows_per_link=None, rng=None):
+    for j, ((x, pc, ps, N, y, xo, a), host) in enumerate(zip(links, hosts)):
+        xb = bf16_bits(x)
+        c, s, z = host
+        rows = np.arange(N) if rows_per_link is None else np.sort(
+            rng.choice(N, size=rows_per_link, replace=False))
+        got = y.cpu().numpy()
+        assert np.isfinite(got).all(), f"link {j}: unwritten or NaN-fed outputs"
+        ref = oracle.qgemm_w4(xb, c[rows], s[rows], z[rows])
+        assert_rows_close(got[:, rows], ref, what=f"chain link {j} N={N}")
+        want = oracle.chain_glue(got, a, xo.shape[1])
+        assert np.array_equal(bf16_bits(xo), want), f"link {j}: xo is not the hand-off of y"
+
+
+@pytest.mark.parametrize("m", [1, 16, 32])
+def test_chain_two_layers_in_order(m):
+    sv = _sv()
+    H, F = 640, 1920
+    links, hosts = _decoder_chain(2, m, H, F, seed=900 + m)
+    p = sv.sv_pass_chain_plan(links)
+    sv.sv_pass_run(p)
+    torch.cuda.synchronize()
+    assert sv.sv_pass_status(p) == 0
+    _check_chain(links, hosts)
+    # the first link from its seeded input, its xo from the binary64 result
+    x0 = links[0][0].cpu()
+    y64 = oracle.qgemm_w4(bf16_bits(x0), *hosts[0])
+    _check_xo(links[0][5].cpu(), y64, bf16_bits(x0), hosts[0], links[0][6], H, "first link")
+    # launches again: same bits (fixed-order sums; the barrier counters carry
+    # over from launch to launch)
+    first = [(l[4].clone(), l[5].clone()) for l in links]
+    for l in links:
+        l[5].fill_(float("nan"))
+    for _ in range(2):
+        sv.sv_pass_run(p)
+    torch.cuda.synchronize()
+    assert sv.sv_pass_status(p) == 0
+    for (y0, xo0), l in zip(first, links):
+        assert torch.equal(y0, l[4]) and torch.equal(xo0.view(torch.int16), l[5].view(torch.int16))
+
+
+def test_chain_graph_replays():
+    """Captured once, replayed three times with eager work in between; every
+    replay reproduces the eager result bit for bit."""
+    sv = _sv()
+    links, hosts = _decoder_chain(2, 16, 640, 1920, seed=1700)
+    p = sv.sv_pass_chain_plan(links)
+    sv.sv_pass_run(p)
+    torch.cuda.synchronize()
+    want = [(l[4].clone(), l[5].view(torch.int16).clone()) for l in links]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            sv.sv_pass_run(p, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        for l in links:
+            l[4].fill_(float("nan"))
+            l[5].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _ = torch.randn(1024, device=DEV).sum().item()     # eager work between replays
+        for (y0, xo0), l in zip(want, links):
+            assert torch.equal(y0, l[4]), f"replay {rep}"
+            assert torch.equal(xo0, l[5].view(torch.int16)), f"replay {rep}"
+    assert sv.sv_pass_status(p) == 0
+
+
+def test_chain_9b_stack_k16_sampled():
+    """The 32-layer, 3.93 GB stack chained in model order at k = 16, in the
+    launch configuration of the benchmark: 16 sampled channels of every y
+    against the oracle's product of the link's actual input, every xo
+    bit-exactly against the oracle's hand-off of its y."""
+    sv = _sv()
+    H, F, m = 4096, 12288, 16
+    h = synth.activations(m, H, seed=11, device=DEV)
+    links, hosts, samples = [], [], []
+    rng = np.random.default_rng(2025)
+    for layer in range(32):
+        for i, (N, K, cols) in enumerate(((3 * H, H, H), (H, H, H), (2 * F, H, F), (H, F, H))):
+            c, s, z = synth.w4_matrix(N, K, seed=1000 * layer + i, device=DEV)
+            pc, ps = sv.sv_w4_pack(c, s, z)
+            rows = np.sort(rng.choice(N, size=16, replace=False))
+            ri = torch.as_tensor(rows, device=DEV)
+            samples.append((rows, c[ri].cpu().numpy(), s[ri].cpu().numpy(), z[ri].cpu().numpy()))
+            del c, s, z
+            xo = _nan((m, cols), torch.bfloat16)
+            links.append((h, pc, ps, N, _nan((m, N), torch.float32), xo, alpha_for(K)))
+            h = xo
+    p = sv.sv_pass_chain_plan(links)
+    assert p.grid == torch.cuda.get_device_properties(0).multi_processor_count
+    for _ in range(2):
+        sv.sv_pass_run(p)
+    torch.cuda.synchronize()
+    assert sv.sv_pass_status(p) == 0
+    for j, ((x, pc, ps, N, y, xo, a), (rows, c, s, z)) in enumerate(zip(links, samples)):
+        got = y.cpu().numpy()
+        assert np.isfinite(got).all(), f"link {j}"
+        ref = oracle.qgemm_w4(bf16_bits(x), c, s, z)
+        assert_rows_close(got[:, rows], ref, what=f"9B chain link {j} N={N}")
+        assert np.array_equal(bf16_bits(xo), oracle.chain_glue(got, a, xo.shape[1])), j
+    # the hand-offs stay at unit scale through 128 links
+    last = oracle.bf16_bits_to_f64(bf16_bits(links[-1][5]))
+    assert 0.2 < np.sqrt((last ** 2).mean()) < 5.0
+
+
+def test_stale_plan_is_refused_and_reported():
+    sv = _sv()
+    m = 5
+    links, _ = _decoder_chain(1, m, 640, 1920, seed=77)
+    p1 = sv.sv_pass_chain_plan(links)
+    # (1) the buffer planned again (other rows): the old descriptor is refused
+    # before any launch
+    links3, _ = _decoder_chain(1, 3, 640, 1920, seed=78)
+    buf = p1.plan[(-p1.plan.data_ptr()) % 256:]
+    p2 = sv.sv_pass_chain_plan(links3, plan=buf)
+    with pytest.raises(sv.SvError):
+        sv.sv_pass_run(p1)
+    sv.sv_pass_run(p2)
+    torch.cuda.synchronize()
+    assert sv.sv_pass_status(p2) == 0
+    # (2) a descriptor that no longer matches the plan in its buffer (here
+    # its row count): the kernel computes nothing and reports it
+    for l in links3:
+        l[4].fill_(float("nan"))
+    p2.info.m = 4
+    sv.sv_pass_run(p2)
+    torch.cuda.synchronize()
+    assert sv.sv_pass_status(p2) == sv.PASS_STATUS_STALE
+    assert all(torch.isnan(l[4]).all() for l in links3)
+    # (3) the unordered executor refuses a re-planned buffer as well
+    g = [(links[0][0], links[0][1], links[0][2], links[0][3], links[0][4])]
+    q1 = sv.sv_pass_plan("w4", g)
+    sv.sv_pass_plan("w4", g, plan=q1.plan)
+    with pytest.raises(sv.SvError):
+        sv.sv_pass_run(q1)
+
+
+def test_barrier_timeout_is_reported_and_the_launch_ends():
+    """Forced from the host: the plan's barrier targets are raised past what
+    the launch can reach and its poll bound lowered to 64, so the first
+    waiting link gives up; every workgroup ends, the status word says so, and
+    a plan made again runs normally."""
+    sv = _sv()
+    links, hosts = _decoder_chain(1, 16, 640, 1920, seed=91)
+    p = sv.sv_pass_chain_plan(links)
+    base = (-p.plan.data_ptr()) % 256
+    hdr = p.plan[base:base + 128]
+    words = hdr.view(torch.int32)
+    words[8] = 64                                   # spin_limit
+    words[10:26] = 1 << 20                          # workgroups per barrier counter
+    sv.sv_pass_run(p)
+    torch.cuda.synchronize()
+    assert sv.sv_pass_status(p) & sv.PASS_STATUS_TIMEOUT
+    p = sv.sv_pass_chain_plan(links)
+    sv.sv_pass_run(p)
+    torch.cuda.synchronize()
+    assert sv.sv_pass_status(p) == 0
+    _check_chain(links, hosts)

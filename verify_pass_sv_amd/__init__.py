@@ -15,7 +15,9 @@ _BINDING_NAMES = (
     "sv_w8_pack", "sv_pass_plan", "sv_pass_run", "Pass", "SvPassGemm", "SvPass",
     "PASS_FORMATS", "sv_verify_sampled", "sv_verify_sampled_workspace_bytes", "SvSampling",
     "sv_verify_coupled", "sv_verify_coupled_workspace_bytes", "sv_verify_tree",
-    "sv_verify_tree_workspace_bytes", "sv_verify_accept_stats",
+    "sv_verify_tree_workspace_bytes", "sv_verify_accept_stats", "sv_pass_status",
+    "sv_pass_chain_plan", "sv_pass_chain_image", "SvPassLink", "PASS_STATUS_STALE",
+    "PASS_STATUS_TIMEOUT",
 )
 
 __all__ = list(_BINDING_NAMES)

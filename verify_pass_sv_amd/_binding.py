@@ -24,6 +24,7 @@ EXPORTED_SYMBOLS = (
     "sv_verify_sampled_workspace_bytes", "sv_verify_sampled",
     "sv_verify_coupled_workspace_bytes", "sv_verify_coupled",
     "sv_verify_tree_workspace_bytes", "sv_verify_tree", "sv_verify_accept_stats",
+    "sv_pass_status", "sv_pass_chain_bytes", "sv_pass_chain_image", "sv_pass_chain_plan",
 )
 
 _STATUS = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_INVALID_ARG", 3: "SV_ERR_ALIGN",
@@ -41,7 +42,19 @@ class SvPass(ctypes.Structure):
     """C struct sv_pass: host descriptor of a planned pass."""
     _fields_ = [("plan", ctypes.c_void_p), ("format", ctypes.c_int), ("m", ctypes.c_int),
                 ("count", ctypes.c_int), ("grid", ctypes.c_int), ("items", ctypes.c_int),
-                ("max_steps", ctypes.c_int), ("stats", ctypes.c_int)]
+                ("max_steps", ctypes.c_int), ("stats", ctypes.c_int), ("chain", ctypes.c_int),
+                ("id", ctypes.c_uint32)]
+
+
+class SvPassLink(ctypes.Structure):
+    """C struct sv_pass_link: one GEMM of a chain (verify pass in model order)."""
+    _fields_ = [("x", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("xo", ctypes.c_void_p), ("alpha", ctypes.c_float),
+                ("K", ctypes.c_int), ("N", ctypes.c_int), ("xo_cols", ctypes.c_int)]
+
+
+PASS_STATUS_STALE = 1
+PASS_STATUS_TIMEOUT = 2
 
 
 PASS_FORMATS = {"w4": 0, "w8": 1, "w4_i8": 2}
@@ -91,6 +104,12 @@ def _load():
         "sv_pass_plan": (i32, [i32, ctypes.POINTER(SvPassGemm), i32, i32, i32, vp, sz,
                                ctypes.POINTER(SvPass), vp]),
         "sv_pass_run": (i32, [ctypes.POINTER(SvPass), vp]),
+        "sv_pass_status": (i32, [ctypes.POINTER(SvPass), ctypes.POINTER(u32), vp]),
+        "sv_pass_chain_bytes": (sz, [i32, ctypes.POINTER(SvPassLink), i32, i32]),
+        "sv_pass_chain_image": (i32, [i32, ctypes.POINTER(SvPassLink), i32, i32, i32, i32, vp,
+                                      sz, ctypes.POINTER(i32)]),
+        "sv_pass_chain_plan": (i32, [i32, ctypes.POINTER(SvPassLink), i32, i32, i32, vp, sz,
+                                     ctypes.POINTER(SvPass), vp]),
         "sv_verify_sampled_workspace_bytes": (sz, [i32, i32, i32]),
         "sv_verify_sampled": (i32, [vp, vp, vp, i32, i32, i32, ctypes.POINTER(SvSampling), u64,
                                     u32, vp, vp, vp, vp, vp, vp, sz, vp]),
@@ -258,7 +277,7 @@ def _pass_gemms(fmt, gemms, group):
     return arr, m, keep
 
 
-def sv_pass_plan(fmt, gemms, group=64, stream=None):
+def sv_pass_plan(fmt, gemms, group=64, stream=None, plan=None):
     """Plan one verify pass; `fmt` is "w4", "w8" or "w4_i8".
 
     gemms: sequence of
@@ -267,7 +286,8 @@ def sv_pass_plan(fmt, gemms, group=64, stream=None):
       w4_i8: (xq int8 [m, K], xscale f32 [m], packed_codes, packed_sz, N, y)
     each optionally followed by stats f32 [m, ceil(N/64), 2], which receives
     the softmax statistics (max, sum of exp) of every 64 outputs of a row.
-    Returns a Pass for sv_pass_run.  Synchronizes `stream`.
+    `plan`: an optional uint8 device buffer to plan into (e.g. one that held
+    an earlier plan).  Returns a Pass for sv_pass_run.  Synchronizes `stream`.
     """
     if fmt not in PASS_FORMATS:
         raise ValueError(f"unknown pass format {fmt!r}")
@@ -278,7 +298,11 @@ def sv_pass_plan(fmt, gemms, group=64, stream=None):
     nbytes = int(lib.sv_pass_plan_bytes(f, arr, len(gemms), m))
     if nbytes == 0:
         raise SvError("sv_pass_plan_bytes", 2)
-    plan = torch.empty((nbytes,), dtype=torch.uint8, device=keep[0].device)
+    if plan is None:
+        plan = torch.empty((nbytes,), dtype=torch.uint8, device=keep[0].device)
+    else:
+        _need(plan, "plan", torch.uint8)
+        nbytes = plan.numel()
     info = SvPass()
     _check("sv_pass_plan", lib.sv_pass_plan(f, arr, len(gemms), m, group, _ptr(plan), nbytes,
                                             ctypes.byref(info), _stream(stream)))
@@ -286,8 +310,87 @@ def sv_pass_plan(fmt, gemms, group=64, stream=None):
 
 
 def sv_pass_run(p, stream=None):
-    """Run every GEMM of a planned pass in one launch."""
+    """Run every GEMM of a planned pass (or every link of a chain) in one launch."""
     _check("sv_pass_run", lib.sv_pass_run(ctypes.byref(p.info), _stream(stream)))
+
+
+def sv_pass_status(p, stream=None):
+    """The plan's status word (PASS_STATUS_* bits; 0 = ok).  Synchronizes."""
+    v = ctypes.c_uint32(0)
+    _check("sv_pass_status", lib.sv_pass_status(ctypes.byref(p.info), ctypes.byref(v),
+                                                _stream(stream)))
+    return int(v.value)
+
+
+def _chain_links(links, group):
+    """links: sequence of (x bf16 [m, K], packed_codes, packed_sz, N, y f32 [m, N],
+    xo bf16 [m, xo_cols] or None, alpha)."""
+    arr = (SvPassLink * len(links))()
+    m, keep = None, []
+    for i, (x, codes, sc, N, y, xo, alpha) in enumerate(links):
+        mm, K = x.shape
+        m = mm if m is None else m
+        if mm != m:
+            raise ValueError("every link of a chain has the same number of rows m")
+        _need(x, "x", torch.bfloat16)
+        _need(codes, "packed_codes", torch.uint8, (N * K // 2,))
+        _need(sc, "packed_sz", torch.float16, (N * (K // group) * 2,))
+        _need(y, "y", torch.float32, (m, N))
+        xo_cols = 0
+        if xo is not None:
+            _need(xo, "xo", torch.bfloat16)
+            if xo.dim() != 2 or xo.shape[0] != m:
+                raise ValueError("xo must be bf16 [m, xo_cols]")
+            xo_cols = xo.shape[1]
+        arr[i] = SvPassLink(x.data_ptr(), codes.data_ptr(), sc.data_ptr(), y.data_ptr(),
+                            None if xo is None else xo.data_ptr(), float(alpha), K, N, xo_cols)
+        keep += [t for t in (x, codes, sc, y, xo) if t is not None]
+    return arr, m, keep
+
+
+def sv_pass_chain_plan(links, group=64, stream=None, plan=None):
+    """Plan a verify pass in model order (W4).  links: sequence of
+    (x, packed_codes, packed_sz, N, y, xo, alpha) -- see _chain_links; a link
+    whose x is an earlier link's xo waits for every earlier link.  `plan`: an
+    optional uint8 device buffer to plan into (256-byte aligned), e.g. one
+    that held an earlier plan.  Returns a Pass for sv_pass_run.
+    Synchronizes `stream`."""
+    if len(links) == 0:
+        raise ValueError("a chain needs at least one link")
+    arr, m, keep = _chain_links(links, group)
+    nbytes = int(lib.sv_pass_chain_bytes(PASS_FORMATS["w4"], arr, len(links), m))
+    if nbytes == 0:
+        raise SvError("sv_pass_chain_bytes", 2)
+    if plan is None:
+        # 256-byte aligned plan buffer
+        raw = torch.empty((nbytes + 256,), dtype=torch.uint8, device=keep[0].device)
+        off = (-raw.data_ptr()) % 256
+        plan = raw[off:off + nbytes]
+    else:
+        _need(plan, "plan", torch.uint8)
+        raw = plan
+        nbytes = plan.numel()
+    info = SvPass()
+    _check("sv_pass_chain_plan", lib.sv_pass_chain_plan(
+        PASS_FORMATS["w4"], arr, len(links), m, group, _ptr(plan), nbytes, ctypes.byref(info),
+        _stream(stream)))
+    return Pass(raw, info, keep)
+
+
+def sv_pass_chain_image(fmt, links, m, cus, group=64):
+    """Host-only plan image of a chain for a device of `cus` compute units.
+    links: sequence of dicts with integer addresses x, codes, scales, y, xo
+    (0 = none) and alpha, K, N, xo_cols.  Returns (status, grid, bytes)."""
+    arr = (SvPassLink * len(links))()
+    for i, d in enumerate(links):
+        arr[i] = SvPassLink(d["x"], d["codes"], d["scales"], d["y"], d.get("xo") or None,
+                            float(d.get("alpha", 1.0)), d["K"], d["N"], d.get("xo_cols", 0))
+    cap = 1 << 24
+    buf = (ctypes.c_uint8 * cap)()
+    grid = ctypes.c_int(0)
+    st = lib.sv_pass_chain_image(PASS_FORMATS[fmt], arr, len(links), m, group, cus, buf, cap,
+                                 ctypes.byref(grid))
+    return int(st), int(grid.value), bytes(buf) if st == 0 else b""
 
 
 def sv_qgemm_w8(x, codes, scales, y=None, stream=None):

@@ -59,7 +59,7 @@ extern "C" const char* sv_status_str(sv_status status) {
   return "SV_ERR_UNKNOWN";
 }
 
-extern "C" int sv_version(void) { return 100; }  // 0.1.0
+extern "C" int sv_version(void) { return 200; }  // 0.2.0: chains, plan status
 
 extern "C" int sv_read_probe_sink_words(void) { return kProbeBlocks; }
 

@@ -18,7 +18,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "qgemm_w4.hip", "qgemm_w4_packed.hip", "pass.hip", "qgemm_w8.hip", "qgemm_w4_i8.hip",
+SOURCES = ["api.hip", "qgemm_w4.hip", "qgemm_w4_packed.hip", "pass.hip", "pass_chain.hip",
+           "qgemm_w8.hip", "qgemm_w4_i8.hip",
            "hadamard_i8.hip", "verify_accept.hip",
            "verify_sampled.hip", "verify_coupled.hip"]
 
@@ -41,7 +42,7 @@ def _hipcc():
 # Kernels that wait on exact counts of their own outstanding vector memory
 # operations: a register spill would add scratch loads and stores to that
 # count, so their build fails if any kernel of the file uses scratch.
-NO_SCRATCH = {"pass.hip", "qgemm_w4_packed.hip"}
+NO_SCRATCH = {"pass.hip", "pass_chain.hip", "qgemm_w4_packed.hip"}
 RESOURCE_REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
 
 

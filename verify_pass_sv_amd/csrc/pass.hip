@@ -67,8 +67,11 @@
 // Clearly Explained, "Check the guesses together": the target scores every
 // draft position in the pass; "Accept from left to right" needs p = softmax).
 #include <algorithm>
+#include <cstddef>
 #include <functional>
+#include <mutex>
 #include <queue>
+#include <unordered_map>
 #include <vector>
 
 #include "w4_packed_dev.h"
@@ -119,6 +122,7 @@ inline int fmt_xe(int f) { return f == SV_PASS_W4_I8 ? 1 : 2; }
 struct PlanHeader {                             // 64 bytes
   uint32_t magic, version;
   int32_t format, m, count, grid, items, max_steps, stats;   // stats: some GEMM has a stats buffer
+  uint32_t status;                              // SV_PASS_STATUS_* bits set by the kernel
   uint64_t reserved[3];
 };
 struct PlanItem {                               // 64 bytes
@@ -132,6 +136,7 @@ struct PlanItem {                               // 64 bytes
 };
 static_assert(sizeof(PlanHeader) == 64, "plan header layout");
 static_assert(sizeof(PlanItem) == 64, "plan item layout");
+static_assert(offsetof(PlanHeader, status) == SV_PASS_STATUS_OFFSET, "status word offset");
 
 // Plan image: header | wg_begin[kMaxGrid + 1] | wg_steps[kMaxGrid] | items.
 constexpr size_t kBeginOff = sizeof(PlanHeader);
@@ -219,10 +224,14 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const uint8_t* __restric
   static_assert(kTW == 4, "the output transpose covers a wave's 4 tiles = 64 channels");
   extern __shared__ __align__(16) uint8_t lds[];
 
+  // A plan buffer that does not hold the plan this launch was made for:
+  // compute nothing.  (sv_pass_run has already refused a plan that was made
+  // again into the same buffer; this check covers a buffer the caller
+  // overwrote.)
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(plan);
   if (hdr->magic != kPlanMagic || hdr->format != F || hdr->m != m || (hdr->stats != 0) != ST ||
       hdr->grid != static_cast<int>(gridDim.x))
-    return;                                     // stale or foreign plan: touch nothing
+    return;
   const int32_t* wg_begin = reinterpret_cast<const int32_t*>(plan + kBeginOff);
   const int32_t* wg_steps = reinterpret_cast<const int32_t*>(plan + kStepsOff);
   const PlanItem* items = reinterpret_cast<const PlanItem*>(plan + kItemsOff);
@@ -742,6 +751,13 @@ sv_status launch_pass(const void* plan, int m, int grid, hipStream_t st) {
   return SV_OK;
 }
 
+// Plans made by this library, by buffer: the id of the last plan written into
+// each plan buffer.  sv_pass_run refuses an sv_pass whose plan buffer has
+// since been planned again (its id is no longer the buffer's).
+std::mutex g_plan_mu;
+std::unordered_map<const void*, uint32_t> g_plan_ids;
+uint32_t g_plan_next = 0;
+
 sv_status check_gemms(int format, const sv_pass_gemm* gemms, int count, int m,
                       long long* n_items) {
   if (format != SV_PASS_W4 && format != SV_PASS_W8 && format != SV_PASS_W4_I8)
@@ -775,6 +791,8 @@ sv_status check_gemms(int format, const sv_pass_gemm* gemms, int count, int m,
 }
 
 }  // namespace
+
+uint32_t sv_register_plan(const void* plan);
 
 extern "C" size_t sv_pass_plan_bytes(int format, const sv_pass_gemm* gemms, int count, int m) {
   long long items = 0;
@@ -875,6 +893,8 @@ extern "C" sv_status sv_pass_plan(int format, const sv_pass_gemm* gemms, int cou
   pass->items = static_cast<int>(n_items);
   pass->max_steps = max_steps;
   pass->stats = any_stats;
+  pass->chain = 0;
+  pass->id = sv_register_plan(plan);
   return SV_OK;
 }
 
@@ -901,12 +921,44 @@ sv_status dispatch_pass(const sv_pass* pass, hipStream_t stream) {
 }
 }  // namespace
 
+sv_status sv_chain_run(const sv_pass* pass, hipStream_t stream);   // pass_chain.hip
+
+uint32_t sv_register_plan(const void* plan) {
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  if (++g_plan_next == 0) ++g_plan_next;        // ids are never 0
+  g_plan_ids[plan] = g_plan_next;
+  return g_plan_next;
+}
+
+static bool plan_is_current(const sv_pass* pass) {
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  const auto it = g_plan_ids.find(pass->plan);
+  return it != g_plan_ids.end() && it->second == pass->id;
+}
+
 extern "C" sv_status sv_pass_run(const sv_pass* pass, hipStream_t stream) {
   if (!pass || !pass->plan) return SV_ERR_NULL;
   if (!sv_aligned16(pass->plan)) return SV_ERR_ALIGN;
+  if (!plan_is_current(pass)) return SV_ERR_INVALID_ARG;   // stale: the buffer was re-planned
+  if (pass->chain) {
+    if (pass->m < 1 || pass->m > SV_MAX_ROWS) return SV_ERR_INVALID_ARG;
+    return sv_chain_run(pass, stream);
+  }
   if (pass->m < 1 || pass->m > SV_MAX_ROWS || pass->grid < 1 || pass->grid > kMaxGrid)
     return SV_ERR_INVALID_ARG;
   return pass->stats ? dispatch_pass<true>(pass, stream) : dispatch_pass<false>(pass, stream);
+}
+
+extern "C" sv_status sv_pass_status(const sv_pass* pass, uint32_t* status, hipStream_t stream) {
+  if (!pass || !pass->plan || !status) return SV_ERR_NULL;
+  if (!sv_aligned16(pass->plan)) return SV_ERR_ALIGN;
+  uint32_t v = 0;
+  if (hipMemcpyAsync(&v, static_cast<const uint8_t*>(pass->plan) + SV_PASS_STATUS_OFFSET,
+                     sizeof(v), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return SV_ERR_HIP;
+  *status = v;
+  return SV_OK;
 }
 
 // ---- W8 packing -------------------------------------------------------------

@@ -1,0 +1,782 @@
+// Verify pass in model order: a chain of W4 GEMMs run by one persistent
+// launch, each GEMM complete before a later GEMM that reads its output starts.
+//
+// Source: Karpathy's Trick for Faster Local LLMs, "How Uzu optimizes bytes and
+// tokens per pass" (a forward pass hands intermediate values from layer to
+// layer) and "Why batch-one decoding is memory-bound" (the runtime reads the
+// weight blocks of every layer once and computes the next-token scores);
+// Speculative Decoding Clearly Explained, "Check the guesses together" (all
+// draft positions are scored in that one pass).
+//
+// A chain is an ordered list of links.  Link i computes
+//   y_i = x_i W_i^T                      (f32 [m, N_i], 4-bit group-64 weights)
+// and, optionally, the input of a later link
+//   xo_i = bf16_rne(alpha_i * y_i[:, :xo_cols_i])   (bf16 [m, xo_cols_i]).
+// A link whose x is an earlier link's xo waits, at a device-wide phase
+// barrier, until every earlier link is complete; any other link follows its
+// predecessor without a barrier.  The weights do not depend on activations,
+// so the weight stream runs ahead across barriers: only the activation loads
+// and the arithmetic wait.
+//
+// Work split (every link spans the whole grid, one workgroup per compute
+// unit): tile i (16 output channels) of a link belongs to workgroup i mod G.
+// A link with more than 6 G tiles runs as several rounds of at most 6 tiles
+// per workgroup.  Inside a workgroup the 8 stream waves split K: in each
+// window of 8 blocks of 128 k, wave j takes block j for every tile of the
+// round, so one activation operand (read once from LDS) feeds up to 6 tiles.
+// Partial sums of the 8 waves meet in LDS at the end of the round and are
+// added in a fixed order (deterministic results).
+//
+// Wave roles:
+//   * 8 stream waves: weight + scale/zero loads (a ring of kR 1 KiB units per
+//     wave, issued kR units ahead, across rounds and barriers), dequantization,
+//     bf16 MFMAs, the per-group fold and zero-point correction, the
+//     reduction, and the y stores (not waited for inside the launch).
+//   * 1 IO wave: activation windows into LDS (buffer -> LDS loads, issued up
+//     to S - 1 windows ahead), the xo stores, the phase barrier (arrive and
+//     a bounded poll).  Its vector-memory queue holds no weight loads, so
+//     waiting for its xo stores before it arrives costs only their latency.
+//
+// Phase barrier: 16 counters (64-bit, 4 KiB apart); workgroup w adds 1 to
+// counter w mod 16 after its part of a link that a waiting link follows, and
+// a waiting workgroup polls all 16 (agent-scope loads) until each reaches its
+// target.  Counters only grow; the launch index is recovered from the
+// counter value at entry.  The xo data are written with agent-scope (sc1)
+// stores and completed (s_waitcnt vmcnt(0)) before the arrival; consumers
+// read them with plain loads, which is safe because no xo buffer is read
+// before the link that writes it is complete (the plan checks that each xo
+// is a whole number of 128-byte lines and is not read by an earlier link),
+// and every workgroup invalidates its caches at entry (stale lines from an
+// earlier launch).  A poll that exceeds its bound sets the plan's status word
+// and the launch ends early.
+//
+// Arithmetic per 1 KiB unit (tile t, block b; the packed layout of
+// sv_w4_pack): bf16 128 + c from a mask and a byte permute, two
+// v_mfma_f32_16x16x32_bf16 per group give acc = sum x (128 + c), the fold
+// t = s0 acc0 + s1 acc1, and the bias and zero point leave through one
+// rank-2 v_mfma_f32_16x16x4_f32 update t -= sum_g xsum[r, g] s[n, g]
+// (128 + z[n, g]) whose row sums come from all-ones MFMAs on the same
+// activation operand.  For a one-hot row and integer z every step is exact.
+#include <algorithm>
+#include <cstddef>
+#include <type_traits>
+#include <vector>
+
+#include "w4_packed_dev.h"
+
+namespace {
+
+constexpr uint32_t kChainMagic = 0x4F565653u;   // "SVVO"
+constexpr uint32_t kChainVersion = 1;
+constexpr int kSW = 8;                          // stream waves
+constexpr int kThreadsC = 64 * (kSW + 1);       // + the IO wave
+constexpr int kTmax = 6;                        // tile accumulators (switch cases)
+// tiles per workgroup per round: 6 at m <= 16; 4 at m > 16, where the two
+// row tiles double every accumulator
+__host__ __device__ constexpr int round_tiles(int mt) { return mt == 1 ? 6 : 4; }
+// ring units per stream wave: 9 waves per workgroup leave 168 registers per
+// wave, which hold 12 units at m <= 16 and 6 at m > 16
+template <int MT>
+constexpr int ring_units() {
+  return MT == 1 ? 12 : 6;
+}
+constexpr int kNG = 16;                         // barrier counters
+constexpr int kSyncStride = 4096;               // bytes between counters
+constexpr int kMaxGridC = 1024;
+constexpr int kSpinLimit = 1 << 20;             // polls before a barrier gives up (~1 s)
+constexpr int kStreamC = 2;                     // non-temporal (weights, records, y)
+constexpr int kSc1 = 16;                        // agent-scope coherent (xo stores)
+
+constexpr uint32_t kFlagWait = 1;               // round waits for all earlier links
+constexpr uint32_t kFlagSignal = 2;             // workgroups arrive after this round
+
+struct ChainHeader {                            // 128 bytes
+  uint32_t magic, version;
+  int32_t format, m, grid, nrounds, nlinks, nsignals;
+  int32_t spin_limit;                           // polls before a barrier gives up
+  uint32_t status;                              // byte 36, as in the pass plan header
+  int32_t group_size[kNG];                      // workgroups per counter
+  uint32_t pad[6];
+};
+struct ChainRound {                             // 128 bytes
+  const uint8_t* codes;
+  const void* sz;
+  const void* x;
+  float* y;
+  void* xo;
+  float alpha;
+  int32_t K, N, xo_cols;
+  int32_t tile0, ntiles;                        // tiles [tile0, tile0 + ntiles) of the link
+  int32_t signal_index;                         // waiting rounds: arrivals to wait for (per launch)
+  uint32_t flags;
+  int32_t pad[14];
+};
+static_assert(sizeof(ChainHeader) == 128, "chain header layout");
+static_assert(sizeof(ChainRound) == 128, "chain round layout");
+static_assert(offsetof(ChainHeader, status) == SV_PASS_STATUS_OFFSET, "status word offset");
+
+constexpr size_t kRoundsOff = sizeof(ChainHeader);
+__host__ __device__ inline size_t sync_off(int nrounds) {
+  return (kRoundsOff + sizeof(ChainRound) * static_cast<size_t>(nrounds) + kSyncStride - 1) /
+         kSyncStride * kSyncStride;
+}
+__host__ __device__ inline size_t chain_bytes(int nrounds) { return sync_off(nrounds) + kNG * kSyncStride; }
+
+template <int MT>
+struct ChainGeo {
+  static constexpr int S = MT == 1 ? 3 : 2;              // activation window slots
+  static constexpr int ROWB = 2048;                      // 1024 k of bf16 per row
+  static constexpr int WINB = 16 * MT * ROWB;            // bytes per window
+  static constexpr int WLOADS = WINB / 1024;             // 1 KiB loads per window
+  static constexpr int STAGE = S * WINB;                 // xo staging (IO wave)
+  static constexpr int TPOSE = STAGE + kTmax * MT * 512; // per-wave transposes
+  static constexpr int FLAG = TPOSE + kSW * 1024;        // abort flag
+  static constexpr int LDS = FLAG + 16;
+  static_assert(kSW * kTmax * MT * 1024 <= S * WINB, "reduction area fits the windows");
+  static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 workgroup");
+};
+
+__device__ __forceinline__ unsigned int bf16_rne(float f) {
+  const unsigned int u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;   // NaN stays NaN
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// s_waitcnt vmcnt(n) with n clamped to the 6-bit field (a clamped wait is
+// only stricter).
+__device__ __forceinline__ void wait_vm_upto(int n) {
+  if (n >= 63) sv_wait_vmcnt<63>();
+  else if (n >= 32) sv_wait_vmcnt<32>();
+  else if (n >= 16) sv_wait_vmcnt<16>();
+  else sv_wait_vmcnt<0>();
+}
+
+template <int MT>
+__global__ __launch_bounds__(kThreadsC) void chain_kernel(uint8_t* __restrict__ plan, int m) {
+  using G = ChainGeo<MT>;
+  constexpr int kR = ring_units<MT>();
+  extern __shared__ __align__(16) uint8_t lds[];
+  ChainHeader* hdr = reinterpret_cast<ChainHeader*>(plan);
+  if (hdr->magic != kChainMagic) return;                 // not a chain plan: touch nothing
+  if (hdr->version != kChainVersion || hdr->format != SV_PASS_W4 || hdr->m != m ||
+      hdr->grid != static_cast<int>(gridDim.x)) {
+    if (threadIdx.x == 0) atomicOr(&hdr->status, SV_PASS_STATUS_STALE);
+    return;
+  }
+  const ChainRound* rounds = reinterpret_cast<const ChainRound*>(plan + kRoundsOff);
+  const int nrounds = hdr->nrounds;
+  uint64_t* const counters = reinterpret_cast<uint64_t*>(plan + sync_off(nrounds));
+  const int wg = blockIdx.x, grid = gridDim.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, q = lane >> 4;
+  volatile int* const abort_flag = reinterpret_cast<volatile int*>(lds + G::FLAG);
+
+  // Stale lines of buffers that an earlier launch read and a later one
+  // rewrote (agent-scope acquire: invalidates this compute unit's L1 and its
+  // L2 lines that are not coherent across the device).
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (threadIdx.x == 0) *abort_flag = 0;
+  __syncthreads();
+
+  // Tiles of this workgroup in a round: wg, wg + grid, ... below ntiles.
+  constexpr int TM = round_tiles(MT);
+  auto tiles_of = [&](const ChainRound& r) {
+    const int t = (r.ntiles - wg + grid - 1) / grid;
+    return t < TM ? t : TM;
+  };
+
+  if (wave == kSW) {
+    // ======================= IO wave =======================
+    uint64_t epoch = 0;
+    const int g = wg % kNG;
+    const int nsig = hdr->nsignals;
+    if (nsig > 0) {
+      const uint64_t c = __hip_atomic_load(counters + g * (kSyncStride / 8), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      epoch = c / (static_cast<uint64_t>(nsig) * hdr->group_size[g]);
+    }
+    int ws = 0;                                   // window steps so far (slot = ws % S)
+    for (int ri = 0; ri < nrounds; ++ri) {
+      const ChainRound& rd = rounds[ri];
+      const int T = tiles_of(rd);
+      const int K = rd.K;
+      const int W = (K / 128 + kSW - 1) / kSW;
+      if (rd.flags & kFlagWait) {
+        // every earlier link complete on every workgroup
+        const int gi = lane < kNG ? lane : 0;
+        const uint64_t target =
+            (epoch * nsig + rd.signal_index) * static_cast<uint64_t>(hdr->group_size[gi]);
+        bool ok = false;
+        const int limit = hdr->spin_limit;
+        for (int n = 0; n < limit; ++n) {
+          const uint64_t c = lane < kNG ? __hip_atomic_load(counters + gi * (kSyncStride / 8),
+                                                             __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT)
+                                        : target;
+          if (__all(c >= target)) {
+            ok = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (!ok) {
+          if (lane == 0) atomicOr(&hdr->status, SV_PASS_STATUS_TIMEOUT);
+          *abort_flag = 1;
+          sv_barrier_no_fence();                  // the stream waves wait at window 0
+          sv_wait_vmcnt<0>();
+          return;
+        }
+      }
+      __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<void*>(rd.x), 0, m * K * 2, 0x00020000);
+      // Window w: rows 0 .. 16 MT - 1, k in [1024 w, 1024 w + 1024).  Load L
+      // covers half a row (64 columns of 16 bytes); LDS position c of row r
+      // holds global column c ^ (r % 16), so the 16 rows of an MFMA operand
+      // read 16 different bank groups.
+      auto issue_window = [&](int w, int slot) {
+        uint8_t* const base = lds + slot * G::WINB;
+#pragma unroll 4
+        for (int L = 0; L < G::WLOADS; ++L) {
+          const int r = L >> 1;
+          const int c = ((L & 1) << 6) + lane;
+          const int k = w * 1024 + 8 * (c ^ (r & 15));
+          const unsigned int off =
+              r < m && k < K ? static_cast<unsigned int>((r * K + k) * 2) : kSvOutOfRange;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              xrs, (sv_lds_void*)(base + r * G::ROWB + (L & 1) * 1024), 16, off, 0, 0, 0);
+        }
+      };
+      if (T > 0) {
+        const int first = W < G::S ? W : G::S;
+        for (int w = 0; w < first; ++w) issue_window(w, (ws + w) % G::S);
+        for (int w = 0; w < W; ++w) {
+          // windows issued after w: up to w + S - 1 at w = 0, w + S - 2 later
+          const int last = w == 0 ? first - 1 : (w + G::S - 2 < W - 1 ? w + G::S - 2 : W - 1);
+          wait_vm_upto((last - w) * G::WLOADS);
+          sv_barrier_no_fence();                  // A: window w is in its slot
+          if (w >= 1 && w + G::S - 1 < W) issue_window(w + G::S - 1, (ws + w - 1) % G::S);
+        }
+        ws += W;
+      }
+      sv_barrier_no_fence();                      // E1: partial sums may overwrite the windows
+      sv_barrier_no_fence();                      // E2: partial sums written
+      sv_barrier_no_fence();                      // E3: xo staged
+      if (rd.xo != nullptr) {
+        __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+            rd.xo, 0, m * rd.xo_cols * 2, 0x00020000);
+        for (int v = 0; v < T * MT; ++v) {
+          const int tile = rd.tile0 + wg + (v / MT) * grid;
+          const int n0 = 16 * tile;
+          if (n0 >= rd.xo_cols) continue;
+          const sv_u32x2 val =
+              *reinterpret_cast<const sv_u32x2*>(lds + G::STAGE + v * 512 + lane * 8);
+          const int row = 16 * (v % MT) + (lane >> 2);
+          const unsigned int off = row < m ? static_cast<unsigned int>(
+                                                 (row * rd.xo_cols + n0 + 4 * (lane & 3)) * 2)
+                                           : kSvOutOfRange;
+          __builtin_amdgcn_raw_buffer_store_b64(val, ors, off, 0, kSc1);
+        }
+      }
+      if (rd.flags & kFlagSignal) {
+        sv_wait_vmcnt<0>();                       // xo stores complete at agent scope
+        if (lane == 0)
+          __hip_atomic_fetch_add(counters + g * (kSyncStride / 8), static_cast<uint64_t>(1),
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    sv_wait_vmcnt<0>();
+    return;
+  }
+
+  // ======================= stream waves =======================
+  const unsigned int magic = sv_opaque_u32(0x43434343u);
+  const sv_u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const sv_f32x4 fz = {0.f, 0.f, 0.f, 0.f};
+
+  // ---- weight cursor: unit (round, window, tile slot) whose loads go out next
+  int w_r = 0, w_w = 0, w_i = 0, w_T = 0, w_W = 1, w_KB = 1, w_ntile = 1, w_t0 = 0;
+  __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0x00020000);
+  __amdgpu_buffer_rsrc_t srs = crs;
+  auto w_load_round = [&]() {
+    while (w_r < nrounds) {
+      const ChainRound& rd = rounds[w_r];
+      w_T = tiles_of(rd);
+      if (w_T > 0) {
+        w_KB = rd.K / 128;
+        w_W = (w_KB + kSW - 1) / kSW;
+        w_ntile = rd.N / 16;
+        w_t0 = rd.tile0 + wg;
+        crs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(rd.codes), 0,
+                                                rd.N * (rd.K / 2), 0x00020000);
+        srs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(rd.sz), 0,
+                                                rd.N * (rd.K / 64) * 4, 0x00020000);
+        return;
+      }
+      ++w_r;                                      // (never: every round gives each workgroup a tile)
+    }
+  };
+  w_load_round();
+  sv_u32x4 wb[kR];
+  sv_u32x2 szr[kR];
+  auto issue = [&](sv_u32x4& wv, sv_u32x2& sv) {
+    const bool live = w_r < nrounds;
+    const int b = w_w * kSW + wave;
+    const bool ok = live && b < w_KB;
+    const int blk = ok ? sv_pk_block(w_t0 + w_i * grid, b, w_KB, w_ntile) : 0;
+    wv = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? lane * 16 : kSvOutOfRange, blk * 1024,
+                                               kStreamC);
+    sv = __builtin_amdgcn_raw_buffer_load_b64(srs, ok ? col * 8 : kSvOutOfRange, blk * 128,
+                                              kStreamC);
+    if (live && ++w_i == w_T) {
+      w_i = 0;
+      if (++w_w == w_W) {
+        w_w = 0;
+        ++w_r;
+        w_load_round();
+      }
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < kR; ++k) issue(wb[k], szr[k]);
+
+  sv_f32x4 yacc[TM][MT];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int a = 0; a < MT; ++a) yacc[i][a] = fz;
+
+  int slot = 0;                                   // ring slot of the next unit computed
+  int ws = 0;
+  float* const tpose = reinterpret_cast<float*>(lds + G::TPOSE) + wave * 256;
+  for (int ri = 0; ri < nrounds; ++ri) {
+    const ChainRound& rd = rounds[ri];
+    const int T = tiles_of(rd);
+    const int KB = rd.K / 128;
+    const int W = (KB + kSW - 1) / kSW;
+    if (T > 0) {
+      for (int w = 0; w < W; ++w) {
+        sv_barrier_no_fence();                    // A: window w landed (or abort)
+        if (*abort_flag) {
+          sv_wait_vmcnt<0>();
+          return;
+        }
+        const int b = w * kSW + wave;
+        const bool valid = b < KB;                // wave-uniform
+        const uint8_t* const win = lds + ((ws + w) % G::S) * G::WINB;
+        // activation operands of block b: row tile a, group h, two 32-k slices
+        sv_u32x4 a0[2][MT], a1[2][MT];
+        float xsA[MT];
+        if (valid) {
+#pragma unroll
+          for (int a = 0; a < MT; ++a) {
+            const uint8_t* rp = win + (16 * a + col) * G::ROWB;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int c0 = 16 * wave + 8 * h + 2 * q;   // 16-byte column in the window row
+              a0[h][a] = *reinterpret_cast<const sv_u32x4*>(rp + ((c0 ^ col) << 4));
+              a1[h][a] = *reinterpret_cast<const sv_u32x4*>(rp + (((c0 + 1) ^ col) << 4));
+            }
+            // group row sums: an all-ones A operand puts the sum of row col on
+            // lane (col, q); the correction wants group q on lane (col, q)
+            sv_f32x4 g0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(ones),
+                                                                  sv_as_bf16x8(a0[0][a]), fz,
+                                                                  0, 0, 0);
+            g0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(ones),
+                                                         sv_as_bf16x8(a1[0][a]), g0, 0, 0, 0);
+            sv_f32x4 g1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(ones),
+                                                                  sv_as_bf16x8(a0[1][a]), fz,
+                                                                  0, 0, 0);
+            g1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(ones),
+                                                         sv_as_bf16x8(a1[1][a]), g1, 0, 0, 0);
+            xsA[a] = q == 0 ? g0[0] : (q == 1 ? g1[0] : 0.0f);
+          }
+        }
+        // T units of this window, ring slots slot .. slot + T - 1 (mod kR):
+        // a switch into the unrolled ring keeps every register index static.
+        int rem = T, ti = 0;
+        auto unit = [&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          sv_wait_vmcnt<2 * (kR - 1)>();          // unit k's two loads have landed
+          if (valid) {
+            const sv_u32x4 wv = wb[k];
+            const sv_u32x2 sv = szr[k];
+            sv_f32x4 t[MT];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const sv_u32x4 b0 = sv_w4_dequant8(h ? wv.z : wv.x, magic);
+              const sv_u32x4 b1 = sv_w4_dequant8(h ? wv.w : wv.y, magic);
+              const float sc = sv_materialize(sv_half_lo(h ? sv.y : sv.x));
+#pragma unroll
+              for (int a = 0; a < MT; ++a) {
+                sv_f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    sv_as_bf16x8(a0[h][a]), sv_as_bf16x8(b0), fz, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a1[h][a]),
+                                                              sv_as_bf16x8(b1), acc, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) t[a][i] = h ? fmaf(sc, acc[i], t[a][i]) : sc * acc[i];
+              }
+            }
+            // bias and zero point of the block's two groups (lanes q >= 2 add 0)
+            const unsigned int szq = q == 0 ? sv.x : sv.y;
+            const float v = -(sv_half_lo(szq) * (128.0f + sv_half_hi(szq)));
+            const float nsz = q < 2 ? v : 0.0f;
+#pragma unroll
+            for (int a = 0; a < MT; ++a)
+              t[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsA[a], nsz, t[a], 0, 0, 0);
+            switch (ti) {
+#define SV_ACC_CASE(I)                                                     \
+  case I:                                                                  \
+    if constexpr (I < TM) {                                                \
+      _Pragma("unroll") for (int a = 0; a < MT; ++a) yacc[I][a] += t[a];   \
+    }                                                                      \
+    break;
+              SV_ACC_CASE(0)
+              SV_ACC_CASE(1)
+              SV_ACC_CASE(2)
+              SV_ACC_CASE(3)
+              SV_ACC_CASE(4)
+              SV_ACC_CASE(5)
+#undef SV_ACC_CASE
+              default:
+                break;
+            }
+          }
+          sv_compiler_fence();
+          issue(wb[k], szr[k]);                   // the unit kR ahead into the freed slot
+          sv_compiler_fence();
+          ++ti;
+          --rem;
+        };
+        for (;;) {
+          switch (slot) {
+#define SV_UNIT_CASE(K)                              \
+  case K:                                            \
+    if (rem == 0) goto window_done;                  \
+    unit(std::integral_constant<int, K>{});          \
+    slot = (K + 1) % kR;                             \
+    [[fallthrough]];
+            SV_UNIT_CASE(0)
+            SV_UNIT_CASE(1)
+            SV_UNIT_CASE(2)
+            SV_UNIT_CASE(3)
+            SV_UNIT_CASE(4)
+            SV_UNIT_CASE(5)
+#undef SV_UNIT_CASE
+#define SV_UNIT_CASE(K)                              \
+  case K:                                            \
+    if constexpr (K < kR) {                          \
+      if (rem == 0) goto window_done;                \
+      unit(std::integral_constant<int, K>{});        \
+      slot = (K + 1) % kR;                           \
+    }                                                \
+    [[fallthrough]];
+            SV_UNIT_CASE(6)
+            SV_UNIT_CASE(7)
+            SV_UNIT_CASE(8)
+            SV_UNIT_CASE(9)
+            SV_UNIT_CASE(10)
+            SV_UNIT_CASE(11)
+#undef SV_UNIT_CASE
+            default:
+              break;
+          }
+        }
+      window_done:;
+      }
+      ws += W;
+    }
+    // ---- end of the round: fixed-order sum of the 8 waves' partial sums ----
+    sv_barrier_no_fence();                        // E1: every wave done with the windows
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (i < T) {
+#pragma unroll
+        for (int a = 0; a < MT; ++a)
+          *reinterpret_cast<sv_f32x4*>(lds + (((i * MT + a) * kSW + wave) * 1024) + lane * 16) =
+              yacc[i][a];
+      }
+#pragma unroll
+      for (int a = 0; a < MT; ++a) yacc[i][a] = fz;
+    }
+    sv_barrier_no_fence();                        // E2: partial sums in LDS
+    if (T > 0) {
+      __amdgpu_buffer_rsrc_t yrs =
+          __builtin_amdgcn_make_buffer_rsrc(rd.y, 0, m * rd.N * 4, 0x00020000);
+      for (int v = wave; v < T * MT; v += kSW) {
+        sv_f32x4 s = *reinterpret_cast<const sv_f32x4*>(lds + (v * kSW) * 1024 + lane * 16);
+#pragma unroll
+        for (int j = 1; j < kSW; ++j) {
+          const sv_f32x4 p =
+              *reinterpret_cast<const sv_f32x4*>(lds + (v * kSW + j) * 1024 + lane * 16);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[i] += p[i];
+        }
+        // MFMA layout (lane (col, q): rows 4q .. 4q + 3 of channel col) ->
+        // lane l: row l / 4, channels 4 (l % 4) .. + 3
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tpose[(4 * q + i) * 16 + col] = s[i];
+        sv_compiler_fence();
+        const sv_f32x4 o = *reinterpret_cast<const sv_f32x4*>(tpose + (lane >> 2) * 16 +
+                                                               4 * (lane & 3));
+        sv_compiler_fence();
+        const int tile = rd.tile0 + wg + (v / MT) * grid;
+        const int n0 = 16 * tile;
+        const int row = 16 * (v % MT) + (lane >> 2);
+        const unsigned int off =
+            row < m ? static_cast<unsigned int>((row * rd.N + n0 + 4 * (lane & 3)) * 4)
+                    : kSvOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(sv_u32x4, o), yrs, off, 0,
+                                               kStreamC);
+        if (rd.xo != nullptr && n0 < rd.xo_cols) {
+          sv_u32x2 pk;
+          pk.x = bf16_rne(rd.alpha * o[0]) | (bf16_rne(rd.alpha * o[1]) << 16);
+          pk.y = bf16_rne(rd.alpha * o[2]) | (bf16_rne(rd.alpha * o[3]) << 16);
+          *reinterpret_cast<sv_u32x2*>(lds + G::STAGE + v * 512 + lane * 8) = pk;
+        }
+      }
+    }
+    sv_barrier_no_fence();                        // E3: xo staged for the IO wave
+  }
+  sv_wait_vmcnt<0>();
+}
+
+template <int MT>
+sv_status launch_chain(void* plan, int m, int grid, hipStream_t st) {
+  auto kern = chain_kernel<MT>;
+  constexpr int kLds = ChainGeo<MT>::LDS;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess)
+    return SV_ERR_HIP;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreadsC), kLds, st, static_cast<uint8_t*>(plan),
+                     m);
+  SV_LAUNCH_CHECK();
+  return SV_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
+
+// Validates the links and counts the rounds (0 on error, status in *st).
+int chain_rounds(int format, const sv_pass_link* links, int count, int m, int grid,
+                 sv_status* st) {
+  const int tm = round_tiles(m > 16 ? 2 : 1);
+  *st = SV_OK;
+  if (format != SV_PASS_W4) {
+    *st = format == SV_PASS_W8 || format == SV_PASS_W4_I8 ? SV_ERR_UNSUPPORTED
+                                                          : SV_ERR_INVALID_ARG;
+    return 0;
+  }
+  if (!links) {
+    *st = SV_ERR_NULL;
+    return 0;
+  }
+  if (count < 1 || m < 1 || m > SV_MAX_ROWS) {
+    *st = SV_ERR_INVALID_ARG;
+    return 0;
+  }
+  long long nr = 0;
+  for (int i = 0; i < count; ++i) {
+    const sv_pass_link& e = links[i];
+    if (!e.x || !e.codes || !e.scales || !e.y || (e.xo_cols > 0) != (e.xo != nullptr)) {
+      *st = SV_ERR_NULL;
+      return 0;
+    }
+    if (e.N < 16 || e.N % 16 != 0 || e.K < 128 || e.K % 128 != 0 || e.xo_cols < 0 ||
+        e.xo_cols > e.N || e.xo_cols % 64 != 0) {
+      *st = SV_ERR_INVALID_ARG;
+      return 0;
+    }
+    if (static_cast<long long>(e.N) * e.K / 2 >= (1LL << 31) ||
+        static_cast<long long>(m) * e.N * 4 >= (1LL << 31) ||
+        static_cast<long long>(m) * e.K * 2 >= (1LL << 31)) {
+      *st = SV_ERR_UNSUPPORTED;
+      return 0;
+    }
+    if (!sv_aligned16(e.x) || !sv_aligned16(e.codes) || !sv_aligned16(e.scales) ||
+        !sv_aligned16(e.y) || (e.xo && (reinterpret_cast<uintptr_t>(e.xo) & 127u) != 0)) {
+      *st = SV_ERR_ALIGN;
+      return 0;
+    }
+    const int tiles = e.N / 16;
+    const int per = tm * grid;
+    nr += (tiles + per - 1) / per;
+  }
+  // Buffer rules (byte ranges): an x that meets an earlier xo is exactly that
+  // xo; no xo meets the x of its own or an earlier link, another xo, or a y;
+  // no y meets any x, xo or other y.
+  for (int i = 0; i < count; ++i) {
+    const sv_pass_link& e = links[i];
+    const size_t xb = static_cast<size_t>(m) * e.K * 2, yb = static_cast<size_t>(m) * e.N * 4;
+    for (int j = 0; j < count; ++j) {
+      const sv_pass_link& f = links[j];
+      const size_t fxo = static_cast<size_t>(m) * f.xo_cols * 2;
+      const size_t fyb = static_cast<size_t>(m) * f.N * 4, fxb = static_cast<size_t>(m) * f.K * 2;
+      if (overlap(e.x, xb, f.xo, fxo) &&
+          (j >= i || e.x != f.xo || e.K != f.xo_cols)) {
+        *st = SV_ERR_INVALID_ARG;
+        return 0;
+      }
+      if (overlap(e.y, yb, f.x, fxb) || overlap(e.y, yb, f.xo, fxo) ||
+          (j != i && overlap(e.y, yb, f.y, fyb))) {
+        *st = SV_ERR_INVALID_ARG;
+        return 0;
+      }
+      if (j != i && overlap(e.xo, static_cast<size_t>(m) * e.xo_cols * 2, f.xo, fxo)) {
+        *st = SV_ERR_INVALID_ARG;
+        return 0;
+      }
+    }
+  }
+  if (nr >= (1 << 24)) {
+    *st = SV_ERR_UNSUPPORTED;
+    return 0;
+  }
+  return static_cast<int>(nr);
+}
+
+int chain_grid(const sv_pass_link* links, int count, int cus) {
+  int g = std::min(cus, kMaxGridC);
+  for (int i = 0; i < count; ++i) g = std::min(g, links[i].N / 16);
+  return std::max(g, 1);
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus;
+}
+
+// The plan image for a device of `cus` compute units (host only).
+sv_status build_chain_image(int format, const sv_pass_link* links, int count, int m, int group,
+                            int cus, std::vector<uint8_t>* image, int* grid_out, int* nr_out) {
+  if (!links) return SV_ERR_NULL;
+  if (cus < 1) return SV_ERR_INVALID_ARG;
+  if (count < 1) return SV_ERR_INVALID_ARG;
+  const int grid = chain_grid(links, count, cus);
+  sv_status st;
+  const int nr = chain_rounds(format, links, count, m, grid, &st);
+  if (nr == 0) return st;
+  if (group != 64) return SV_ERR_UNSUPPORTED;
+  image->assign(chain_bytes(nr), 0);
+  ChainHeader* hdr = reinterpret_cast<ChainHeader*>(image->data());
+  ChainRound* rounds = reinterpret_cast<ChainRound*>(image->data() + kRoundsOff);
+  // A link waits iff its x is an earlier link's xo; the link before a waiting
+  // link raises the arrivals (a workgroup that arrives has finished every
+  // earlier link: it runs the links in order).
+  std::vector<int> waits(count, 0);
+  for (int i = 0; i < count; ++i)
+    for (int j = 0; j < i; ++j)
+      if (links[j].xo && links[i].x == links[j].xo) waits[i] = 1;
+  const int per = round_tiles(m > 16 ? 2 : 1) * grid;
+  int nsig = 0, r = 0;
+  for (int i = 0; i < count; ++i) {
+    const sv_pass_link& e = links[i];
+    if (waits[i]) ++nsig;
+    const bool signal = i + 1 < count && waits[i + 1];
+    const int tiles = e.N / 16;
+    const int nround = (tiles + per - 1) / per;
+    const int each = (tiles + nround - 1) / nround;
+    for (int k = 0; k < nround; ++k) {
+      ChainRound& rd = rounds[r++];
+      rd.codes = e.codes;
+      rd.sz = e.scales;
+      rd.x = e.x;
+      rd.y = e.y;
+      rd.xo = e.xo;
+      rd.alpha = e.alpha;
+      rd.K = e.K;
+      rd.N = e.N;
+      rd.xo_cols = e.xo_cols;
+      rd.tile0 = k * each;
+      rd.ntiles = std::min(each, tiles - k * each);
+      rd.signal_index = nsig;
+      rd.flags = (k == 0 && waits[i] ? kFlagWait : 0u) |
+                 (k + 1 == nround && signal ? kFlagSignal : 0u);
+      if (rd.ntiles < grid) return SV_ERR_UNSUPPORTED;   // every workgroup owns a tile
+    }
+  }
+  hdr->magic = kChainMagic;
+  hdr->version = kChainVersion;
+  hdr->format = format;
+  hdr->m = m;
+  hdr->grid = grid;
+  hdr->nrounds = nr;
+  hdr->nlinks = count;
+  hdr->nsignals = nsig;
+  hdr->spin_limit = kSpinLimit;
+  hdr->status = 0;
+  for (int g = 0; g < kNG; ++g) hdr->group_size[g] = grid / kNG + (g < grid % kNG ? 1 : 0);
+  *grid_out = grid;
+  *nr_out = nr;
+  return SV_OK;
+}
+
+}  // namespace
+
+uint32_t sv_register_plan(const void* plan);   // pass.hip
+
+extern "C" size_t sv_pass_chain_bytes(int format, const sv_pass_link* links, int count, int m) {
+  const int cus = device_cus();
+  if (cus < 1 || !links || count < 1) return 0;
+  sv_status st;
+  const int nr = chain_rounds(format, links, count, m, chain_grid(links, count, cus), &st);
+  return nr > 0 ? chain_bytes(nr) : 0;
+}
+
+extern "C" sv_status sv_pass_chain_image(int format, const sv_pass_link* links, int count, int m,
+                                         int group, int cus, void* image, size_t image_bytes,
+                                         int* grid) {
+  if (!image || !grid) return SV_ERR_NULL;
+  std::vector<uint8_t> img;
+  int g = 0, nr = 0;
+  const sv_status st = build_chain_image(format, links, count, m, group, cus, &img, &g, &nr);
+  if (st != SV_OK) return st;
+  if (image_bytes < img.size()) return SV_ERR_WORKSPACE;
+  std::copy(img.begin(), img.end(), static_cast<uint8_t*>(image));
+  *grid = g;
+  return SV_OK;
+}
+
+extern "C" sv_status sv_pass_chain_plan(int format, const sv_pass_link* links, int count, int m,
+                                        int group, void* plan, size_t plan_bytes, sv_pass* pass,
+                                        hipStream_t stream) {
+  const int cus = device_cus();
+  if (cus < 1) return SV_ERR_HIP;
+  std::vector<uint8_t> image;
+  int grid = 0, nr = 0;
+  const sv_status st = build_chain_image(format, links, count, m, group, cus, &image, &grid, &nr);
+  if (st != SV_OK) return st;
+  if (!plan || !pass) return SV_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(plan) & 255u) != 0) return SV_ERR_ALIGN;
+  if (plan_bytes < image.size()) return SV_ERR_WORKSPACE;
+  if (hipMemcpyAsync(plan, image.data(), image.size(), hipMemcpyHostToDevice, stream) !=
+          hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return SV_ERR_HIP;
+  pass->plan = plan;
+  pass->format = format;
+  pass->m = m;
+  pass->count = count;
+  pass->grid = grid;
+  pass->items = nr;
+  pass->max_steps = 0;
+  pass->stats = 0;
+  pass->chain = 1;
+  pass->id = sv_register_plan(plan);
+  return SV_OK;
+}
+
+// Called by sv_pass_run for chain plans.
+sv_status sv_chain_run(const sv_pass* pass, hipStream_t stream) {
+  if (pass->format != SV_PASS_W4) return SV_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(pass->plan) & 255u) != 0) return SV_ERR_ALIGN;
+  if (pass->grid < 1 || pass->grid > kMaxGridC || pass->grid > device_cus())
+    return SV_ERR_INVALID_ARG;
+  return pass->m > 16 ? launch_chain<2>(pass->plan, pass->m, pass->grid, stream)
+                      : launch_chain<1>(pass->plan, pass->m, pass->grid, stream);
+}
