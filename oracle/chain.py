@@ -61,7 +61,10 @@ def glue_candidates(y64, err, alpha, cols):
     result a binary32 accumulation inside the interval can give; where they
     agree the result is unique."""
     y = np.asarray(y64, dtype=np.float64)[:, :cols]
-    e = np.broadcast_to(np.asarray(err, dtype=np.float64), y.shape)
+    e = np.asarray(err, dtype=np.float64)
+    if e.ndim == 2:
+        e = e[:, :cols]                         # per-element bounds of the whole y
+    e = np.broadcast_to(e, y.shape)
     lo = bf16_rne(np.float32(alpha) * (y - e).astype(np.float32))
     hi = bf16_rne(np.float32(alpha) * (y + e).astype(np.float32))
     return lo, hi
