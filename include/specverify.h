@@ -252,12 +252,14 @@ sv_status sv_pass_run(const sv_pass* pass, hipStream_t stream);
  *                           the launch ended early, outputs are undefined,
  *                           and the plan must be made again
  * A buffer that holds no plan at all (its first word is not a plan's
- * magic number) is not written.  sv_pass_status reads the word
- * (synchronizes `stream`); sv_pass_plan and sv_pass_chain_plan clear it.
+ * magic number) is not written.  sv_pass_status reads the word (its place in
+ * the plan buffer is internal; synchronizes `stream`); sv_pass_plan and
+ * sv_pass_chain_plan clear it.  The unordered executor never sets it (its
+ * stale plans are refused by sv_pass_run).
  */
 #define SV_PASS_STATUS_STALE 1u
 #define SV_PASS_STATUS_TIMEOUT 2u
-#define SV_PASS_STATUS_OFFSET 36
+#define SV_PASS_STATUS_OFFSET 36   /* status word of an sv_pass_plan plan */
 sv_status sv_pass_status(const sv_pass* pass, uint32_t* status, hipStream_t stream);
 
 /*

@@ -13,7 +13,7 @@ import pytest
 
 HDR = np.dtype([("magic", "<u4"), ("version", "<u4"), ("format", "<i4"), ("m", "<i4"),
                 ("grid", "<i4"), ("nrounds", "<i4"), ("nlinks", "<i4"), ("nsignals", "<i4"),
-                ("spin_limit", "<i4"), ("status", "<u4"), ("group_size", "<i4", (16,)),
+                ("spin_limit", "<i4"), ("reserved1", "<u4"), ("group_size", "<i4", (16,)),
                 ("pad", "<u4", (6,))])
 RND = np.dtype([("codes", "<u8"), ("sz", "<u8"), ("x", "<u8"), ("y", "<u8"), ("xo", "<u8"),
                 ("alpha", "<f4"), ("K", "<i4"), ("N", "<i4"), ("xo_cols", "<i4"),
@@ -62,7 +62,7 @@ def test_decoder_chain_rounds_and_barriers():
     assert st == 0 and grid == 256
     hdr, rounds = _parse(blob)
     assert hdr["magic"] == 0x4F565653 and hdr["nlinks"] == 12 and hdr["m"] == 16
-    assert hdr["spin_limit"] == 1 << 20 and hdr["status"] == 0
+    assert hdr["spin_limit"] == 1 << 20
     assert hdr["group_size"].sum() == 256 and set(hdr["group_size"]) == {16}
     # one round per link (qkv 768 tiles = 3 per workgroup, gate|up 1536 = 6)
     assert len(rounds) == 12
@@ -87,7 +87,7 @@ def test_two_row_tiles_split_wide_links_into_rounds():
     st, grid, blob = sv.sv_pass_chain_image("w4", links, 32, 256)
     assert st == 0 and grid == 256
     hdr, rounds = _parse(blob)
-    # at m > 16 a round holds at most 4 tiles per workgroup: gate|up (1536
+    # at m > 16 a round holds at most 3 tiles per workgroup: gate|up (1536
     # tiles) runs as two rounds of 768; only its first round waits and only
     # its last raises the arrivals
     assert [(int(r["tile0"]), int(r["ntiles"])) for r in rounds] == \

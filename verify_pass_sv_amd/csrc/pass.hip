@@ -922,6 +922,7 @@ sv_status dispatch_pass(const sv_pass* pass, hipStream_t stream) {
 }  // namespace
 
 sv_status sv_chain_run(const sv_pass* pass, hipStream_t stream);   // pass_chain.hip
+size_t sv_chain_status_offset(const sv_pass* pass);                 // pass_chain.hip
 
 uint32_t sv_register_plan(const void* plan) {
   std::lock_guard<std::mutex> lock(g_plan_mu);
@@ -953,7 +954,8 @@ extern "C" sv_status sv_pass_status(const sv_pass* pass, uint32_t* status, hipSt
   if (!pass || !pass->plan || !status) return SV_ERR_NULL;
   if (!sv_aligned16(pass->plan)) return SV_ERR_ALIGN;
   uint32_t v = 0;
-  if (hipMemcpyAsync(&v, static_cast<const uint8_t*>(pass->plan) + SV_PASS_STATUS_OFFSET,
+  const size_t off = pass->chain ? sv_chain_status_offset(pass) : SV_PASS_STATUS_OFFSET;
+  if (hipMemcpyAsync(&v, static_cast<const uint8_t*>(pass->plan) + off,
                      sizeof(v), hipMemcpyDeviceToHost, stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess)
     return SV_ERR_HIP;

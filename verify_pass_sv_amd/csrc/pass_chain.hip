@@ -28,14 +28,16 @@
 // added in a fixed order (deterministic results).
 //
 // Wave roles:
-//   * 8 stream waves: weight + scale/zero loads (a ring of kR 1 KiB units per
-//     wave, issued kR units ahead, across rounds and barriers), dequantization,
-//     bf16 MFMAs, the per-group fold and zero-point correction, the
-//     reduction, and the y stores (not waited for inside the launch).
-//   * 1 IO wave: activation windows into LDS (buffer -> LDS loads, issued up
-//     to S - 1 windows ahead), the xo stores, the phase barrier (arrive and
-//     a bounded poll).  Its vector-memory queue holds no weight loads, so
-//     waiting for its xo stores before it arrives costs only their latency.
+//   * 8 stream waves: weight + scale/zero loads (a ring of 4 to 6 units of
+//     1 KiB per wave, its first units issued before the round's barrier is
+//     passed), dequantization, bf16 MFMAs, the per-group fold and zero-point
+//     correction, the reduction, and the y and xo stores.  A round's ring is
+//     consumed when it ends, so waiting for the xo stores there waits for
+//     nothing else.
+//   * 1 IO wave: activation windows into LDS (buffer -> LDS loads, all 128 KiB
+//     of window slots at once, then one window per freed slot) and the phase
+//     barrier (arrive, bounded poll).  Its vector-memory queue holds no weight
+//     loads.
 //
 // Phase barrier: 16 counters (64-bit, 4 KiB apart); workgroup w adds 1 to
 // counter w mod 16 after its part of a link that a waiting link follows, and
@@ -71,15 +73,9 @@ constexpr uint32_t kChainVersion = 1;
 constexpr int kSW = 8;                          // stream waves
 constexpr int kThreadsC = 64 * (kSW + 1);       // + the IO wave
 constexpr int kTmax = 6;                        // tile accumulators (switch cases)
-// tiles per workgroup per round: 6 at m <= 16; 4 at m > 16, where the two
-// row tiles double every accumulator
-__host__ __device__ constexpr int round_tiles(int mt) { return mt == 1 ? 6 : 4; }
-// ring units per stream wave: 9 waves per workgroup leave 168 registers per
-// wave, which hold 12 units at m <= 16 and 6 at m > 16
-template <int MT>
-constexpr int ring_units() {
-  return MT == 1 ? 12 : 6;
-}
+// tiles per workgroup per round: 6 at m <= 16; 3 at m > 16, where the two
+// row tiles double the accumulators and activation operands
+__host__ __device__ constexpr int round_tiles(int mt) { return mt == 1 ? 6 : 3; }
 constexpr int kNG = 16;                         // barrier counters
 constexpr int kSyncStride = 4096;               // bytes between counters
 constexpr int kMaxGridC = 1024;
@@ -94,7 +90,7 @@ struct ChainHeader {                            // 128 bytes
   uint32_t magic, version;
   int32_t format, m, grid, nrounds, nlinks, nsignals;
   int32_t spin_limit;                           // polls before a barrier gives up
-  uint32_t status;                              // byte 36, as in the pass plan header
+  uint32_t reserved1;
   int32_t group_size[kNG];                      // workgroups per counter
   uint32_t pad[6];
 };
@@ -113,28 +109,41 @@ struct ChainRound {                             // 128 bytes
 };
 static_assert(sizeof(ChainHeader) == 128, "chain header layout");
 static_assert(sizeof(ChainRound) == 128, "chain round layout");
-static_assert(offsetof(ChainHeader, status) == SV_PASS_STATUS_OFFSET, "status word offset");
 
 constexpr size_t kRoundsOff = sizeof(ChainHeader);
 __host__ __device__ inline size_t sync_off(int nrounds) {
   return (kRoundsOff + sizeof(ChainRound) * static_cast<size_t>(nrounds) + kSyncStride - 1) /
          kSyncStride * kSyncStride;
 }
-__host__ __device__ inline size_t chain_bytes(int nrounds) { return sync_off(nrounds) + kNG * kSyncStride; }
+// Sync area: kNG barrier counters, then the status word, each on its own 4 KiB.
+constexpr size_t kStatusOff = kNG * kSyncStride;
+__host__ __device__ inline size_t chain_bytes(int nrounds) {
+  return sync_off(nrounds) + (kNG + 1) * kSyncStride;
+}
 
 template <int MT>
 struct ChainGeo {
-  static constexpr int S = MT == 1 ? 3 : 2;              // activation window slots
+  static constexpr int S = MT == 1 ? 4 : 2;              // activation window slots (128 KiB)
   static constexpr int ROWB = 2048;                      // 1024 k of bf16 per row
   static constexpr int WINB = 16 * MT * ROWB;            // bytes per window
   static constexpr int WLOADS = WINB / 1024;             // 1 KiB loads per window
-  static constexpr int STAGE = S * WINB;                 // xo staging (IO wave)
-  static constexpr int TPOSE = STAGE + kTmax * MT * 512; // per-wave transposes
-  static constexpr int FLAG = TPOSE + kSW * 1024;        // abort flag
-  static constexpr int LDS = FLAG + 16;
+  static constexpr int TPOSE = S * WINB;                 // per-wave transposes
+  static constexpr int LDS = TPOSE + kSW * 1024;
   static_assert(kSW * kTmax * MT * 1024 <= S * WINB, "reduction area fits the windows");
   static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 workgroup");
 };
+
+// Wave-uniform copies (scalar registers) of values the compiler cannot prove
+// uniform: buffer descriptors built from them need no per-lane loop, and the
+// loads of the plan they index go through the scalar cache.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <class T>
+__device__ __forceinline__ T* uni(T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(u)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(u >> 32)));
+  return reinterpret_cast<T*>(lo | (hi << 32));
+}
 
 __device__ __forceinline__ unsigned int bf16_rne(float f) {
   const unsigned int u = __float_as_uint(f);
@@ -152,39 +161,42 @@ __device__ __forceinline__ void wait_vm_upto(int n) {
 }
 
 template <int MT>
-__global__ __launch_bounds__(kThreadsC) void chain_kernel(uint8_t* __restrict__ plan, int m) {
+// `plan` (header and rounds) is only read; `sync` (counters and status, at
+// plan + sync_off(nrounds)) is written.  Kept as two restrict pointers so the
+// plan's uniform fields load through the scalar cache.
+__global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restrict__ plan,
+                                                          uint8_t* __restrict__ sync, int m,
+                                                          int nrounds) {
   using G = ChainGeo<MT>;
-  constexpr int kR = ring_units<MT>();
   extern __shared__ __align__(16) uint8_t lds[];
-  ChainHeader* hdr = reinterpret_cast<ChainHeader*>(plan);
+  const ChainHeader* hdr = reinterpret_cast<const ChainHeader*>(plan);
+  unsigned int* const status = reinterpret_cast<unsigned int*>(sync + kStatusOff);
   if (hdr->magic != kChainMagic) return;                 // not a chain plan: touch nothing
   if (hdr->version != kChainVersion || hdr->format != SV_PASS_W4 || hdr->m != m ||
-      hdr->grid != static_cast<int>(gridDim.x)) {
-    if (threadIdx.x == 0) atomicOr(&hdr->status, SV_PASS_STATUS_STALE);
+      hdr->grid != static_cast<int>(gridDim.x) || hdr->nrounds != nrounds) {
+    if (threadIdx.x == 0) atomicOr(status, SV_PASS_STATUS_STALE);
     return;
   }
   const ChainRound* rounds = reinterpret_cast<const ChainRound*>(plan + kRoundsOff);
-  const int nrounds = hdr->nrounds;
-  uint64_t* const counters = reinterpret_cast<uint64_t*>(plan + sync_off(nrounds));
+  uint64_t* const counters = reinterpret_cast<uint64_t*>(sync);
   const int wg = blockIdx.x, grid = gridDim.x;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, q = lane >> 4;
-  volatile int* const abort_flag = reinterpret_cast<volatile int*>(lds + G::FLAG);
+  // Abort flag of the workgroup, an LDS word (its reads wait on lgkmcnt only,
+  // never on the weight loads in flight).
+  __shared__ int abort_flag;                    // read after barriers (their asm clobbers memory)
 
   // Stale lines of buffers that an earlier launch read and a later one
   // rewrote (agent-scope acquire: invalidates this compute unit's L1 and its
   // L2 lines that are not coherent across the device).
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  if (threadIdx.x == 0) *abort_flag = 0;
+  if (threadIdx.x == 0) abort_flag = 0;
   __syncthreads();
 
-  // Tiles of this workgroup in a round: wg, wg + grid, ... below ntiles.
+  // Tiles of this workgroup in a round: wg, wg + grid, ... below ntiles
+  // (at most TM: the plan's rounds hold at most TM per workgroup).
   constexpr int TM = round_tiles(MT);
-  auto tiles_of = [&](const ChainRound& r) {
-    const int t = (r.ntiles - wg + grid - 1) / grid;
-    return t < TM ? t : TM;
-  };
 
   if (wave == kSW) {
     // ======================= IO wave =======================
@@ -197,16 +209,30 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(uint8_t* __restrict__ 
       epoch = c / (static_cast<uint64_t>(nsig) * hdr->group_size[g]);
     }
     int ws = 0;                                   // window steps so far (slot = ws % S)
+    // The fields of the round, read one round ahead so their scalar loads
+    // are not waited for when the round starts.
+    struct Cur {
+      const void* x;
+      int K, ntiles, tile0, sig;
+      uint32_t flags;
+    };
+    auto fetch = [&](int ri) {
+      const ChainRound& rd = rounds[ri < nrounds ? ri : nrounds - 1];
+      return Cur{uni(rd.x), uni(rd.K), uni(rd.ntiles), uni(rd.tile0), uni(rd.signal_index),
+                 static_cast<uint32_t>(uni(static_cast<int>(rd.flags)))};
+    };
+    Cur cur = fetch(0);
     for (int ri = 0; ri < nrounds; ++ri) {
-      const ChainRound& rd = rounds[ri];
-      const int T = tiles_of(rd);
-      const int K = rd.K;
+      const Cur nxt = fetch(ri + 1);
+      const int tt = (cur.ntiles - wg + grid - 1) / grid;
+      const int T = tt < TM ? tt : TM;
+      const int K = cur.K;
       const int W = (K / 128 + kSW - 1) / kSW;
-      if (rd.flags & kFlagWait) {
+      if (cur.flags & kFlagWait) {
         // every earlier link complete on every workgroup
         const int gi = lane < kNG ? lane : 0;
         const uint64_t target =
-            (epoch * nsig + rd.signal_index) * static_cast<uint64_t>(hdr->group_size[gi]);
+            (epoch * nsig + cur.sig) * static_cast<uint64_t>(hdr->group_size[gi]);
         bool ok = false;
         const int limit = hdr->spin_limit;
         for (int n = 0; n < limit; ++n) {
@@ -221,21 +247,21 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(uint8_t* __restrict__ 
           __builtin_amdgcn_s_sleep(1);
         }
         if (!ok) {
-          if (lane == 0) atomicOr(&hdr->status, SV_PASS_STATUS_TIMEOUT);
-          *abort_flag = 1;
+          if (lane == 0) atomicOr(status, SV_PASS_STATUS_TIMEOUT);
+          abort_flag = 1;
           sv_barrier_no_fence();                  // the stream waves wait at window 0
           sv_wait_vmcnt<0>();
           return;
         }
       }
-      __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<void*>(rd.x), 0, m * K * 2, 0x00020000);
+      const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<void*>(cur.x), 0, m * K * 2, 0x00020000);
       // Window w: rows 0 .. 16 MT - 1, k in [1024 w, 1024 w + 1024).  Load L
       // covers half a row (64 columns of 16 bytes); LDS position c of row r
       // holds global column c ^ (r % 16), so the 16 rows of an MFMA operand
       // read 16 different bank groups.
-      auto issue_window = [&](int w, int slot) {
-        uint8_t* const base = lds + slot * G::WINB;
+      auto issue_window = [&](int w) {
+        uint8_t* const base = lds + ((ws + w) % G::S) * G::WINB;
 #pragma unroll 4
         for (int L = 0; L < G::WLOADS; ++L) {
           const int r = L >> 1;
@@ -248,42 +274,28 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(uint8_t* __restrict__ 
         }
       };
       if (T > 0) {
-        const int first = W < G::S ? W : G::S;
-        for (int w = 0; w < first; ++w) issue_window(w, (ws + w) % G::S);
+        // LA windows in flight: window w + LA goes out once barrier A(w) has
+        // freed the slot of window w - 1 (S >= LA + 2 slots hold w - 1 .. w + LA)
+        constexpr int LA = G::S >= 4 ? 2 : 1;
+        for (int w = 0; w < LA && w < W; ++w) issue_window(w);
         for (int w = 0; w < W; ++w) {
-          // windows issued after w: up to w + S - 1 at w = 0, w + S - 2 later
-          const int last = w == 0 ? first - 1 : (w + G::S - 2 < W - 1 ? w + G::S - 2 : W - 1);
-          wait_vm_upto((last - w) * G::WLOADS);
+          // windows issued after w: w + 1 .. min(w + LA - 1, W - 1)
+          const int after = (w + LA - 1 < W - 1 ? w + LA - 1 : W - 1) - w;
+          wait_vm_upto(after * G::WLOADS);
           sv_barrier_no_fence();                  // A: window w is in its slot
-          if (w >= 1 && w + G::S - 1 < W) issue_window(w + G::S - 1, (ws + w - 1) % G::S);
+          if (w + LA < W) issue_window(w + LA);
         }
         ws += W;
       }
       sv_barrier_no_fence();                      // E1: partial sums may overwrite the windows
       sv_barrier_no_fence();                      // E2: partial sums written
-      sv_barrier_no_fence();                      // E3: xo staged
-      if (rd.xo != nullptr) {
-        __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
-            rd.xo, 0, m * rd.xo_cols * 2, 0x00020000);
-        for (int v = 0; v < T * MT; ++v) {
-          const int tile = rd.tile0 + wg + (v / MT) * grid;
-          const int n0 = 16 * tile;
-          if (n0 >= rd.xo_cols) continue;
-          const sv_u32x2 val =
-              *reinterpret_cast<const sv_u32x2*>(lds + G::STAGE + v * 512 + lane * 8);
-          const int row = 16 * (v % MT) + (lane >> 2);
-          const unsigned int off = row < m ? static_cast<unsigned int>(
-                                                 (row * rd.xo_cols + n0 + 4 * (lane & 3)) * 2)
-                                           : kSvOutOfRange;
-          __builtin_amdgcn_raw_buffer_store_b64(val, ors, off, 0, kSc1);
-        }
-      }
-      if (rd.flags & kFlagSignal) {
-        sv_wait_vmcnt<0>();                       // xo stores complete at agent scope
+      sv_barrier_no_fence();                      // E3: every stream wave's xo stores complete
+      if (cur.flags & kFlagSignal) {
         if (lane == 0)
           __hip_atomic_fetch_add(counters + g * (kSyncStride / 8), static_cast<uint64_t>(1),
                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      cur = nxt;
     }
     sv_wait_vmcnt<0>();
     return;
@@ -294,197 +306,179 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(uint8_t* __restrict__ 
   const sv_u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const sv_f32x4 fz = {0.f, 0.f, 0.f, 0.f};
 
-  // ---- weight cursor: unit (round, window, tile slot) whose loads go out next
-  int w_r = 0, w_w = 0, w_i = 0, w_T = 0, w_W = 1, w_KB = 1, w_ntile = 1, w_t0 = 0;
-  __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, 0x00020000);
-  __amdgpu_buffer_rsrc_t srs = crs;
-  auto w_load_round = [&]() {
-    while (w_r < nrounds) {
-      const ChainRound& rd = rounds[w_r];
-      w_T = tiles_of(rd);
-      if (w_T > 0) {
-        w_KB = rd.K / 128;
-        w_W = (w_KB + kSW - 1) / kSW;
-        w_ntile = rd.N / 16;
-        w_t0 = rd.tile0 + wg;
-        crs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(rd.codes), 0,
-                                                rd.N * (rd.K / 2), 0x00020000);
-        srs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(rd.sz), 0,
-                                                rd.N * (rd.K / 64) * 4, 0x00020000);
-        return;
-      }
-      ++w_r;                                      // (never: every round gives each workgroup a tile)
-    }
-  };
-  w_load_round();
-  sv_u32x4 wb[kR];
-  sv_u32x2 szr[kR];
-  auto issue = [&](sv_u32x4& wv, sv_u32x2& sv) {
-    const bool live = w_r < nrounds;
-    const int b = w_w * kSW + wave;
-    const bool ok = live && b < w_KB;
-    const int blk = ok ? sv_pk_block(w_t0 + w_i * grid, b, w_KB, w_ntile) : 0;
-    wv = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? lane * 16 : kSvOutOfRange, blk * 1024,
-                                               kStreamC);
-    sv = __builtin_amdgcn_raw_buffer_load_b64(srs, ok ? col * 8 : kSvOutOfRange, blk * 128,
-                                              kStreamC);
-    if (live && ++w_i == w_T) {
-      w_i = 0;
-      if (++w_w == w_W) {
-        w_w = 0;
-        ++w_r;
-        w_load_round();
-      }
-    }
-  };
-#pragma unroll
-  for (int k = 0; k < kR; ++k) issue(wb[k], szr[k]);
-
   sv_f32x4 yacc[TM][MT];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int a = 0; a < MT; ++a) yacc[i][a] = fz;
 
-  int slot = 0;                                   // ring slot of the next unit computed
-  int ws = 0;
+  int ws = 0;                                     // window steps so far (slot = ws % S)
   float* const tpose = reinterpret_cast<float*>(lds + G::TPOSE) + wave * 256;
-  for (int ri = 0; ri < nrounds; ++ri) {
-    const ChainRound& rd = rounds[ri];
-    const int T = tiles_of(rd);
-    const int KB = rd.K / 128;
+
+  // One round of T tiles, its weights in a ring of P windows x T units held
+  // in registers (wb[p][i]: 1 KiB of codes, szr[p][i]: the lane's 8 bytes of
+  // the scale/zero record).  Every index is static and every unit computed
+  // issues the loads of the unit P T places later (out of range past the
+  // round's last window), so the wait before a unit is exact: the P T - 1
+  // units issued after it may still be in flight.  The ring starts when the round does, before its
+  // barrier is passed: the weights do not depend on earlier links, and P T
+  // units (4 to 6 KiB per wave) are what the stream needs in flight without
+  // queueing the round's activation loads behind them.
+  // The fields of a round in scalar registers, read one round ahead.
+  struct Info {
+    const uint8_t* codes;
+    const void* sz;
+    float* y;
+    void* xo;
+    float alpha;
+    int K, N, xo_cols, tile0, ntiles;
+  };
+  auto fetch = [&](int ri) {
+    const ChainRound& rd = rounds[ri < nrounds ? ri : nrounds - 1];
+    return Info{uni(rd.codes), uni(rd.sz), uni(rd.y), uni(rd.xo),
+                __int_as_float(uni(__float_as_int(rd.alpha))), uni(rd.K), uni(rd.N),
+                uni(rd.xo_cols), uni(rd.tile0), uni(rd.ntiles)};
+  };
+
+  auto run_round = [&](auto tc, auto pc, const Info& rd) {
+    constexpr int T = decltype(tc)::value;
+    constexpr int P = decltype(pc)::value;
+    const int K = rd.K, N = rd.N;
+    const int KB = K / 128;
     const int W = (KB + kSW - 1) / kSW;
-    if (T > 0) {
-      for (int w = 0; w < W; ++w) {
-        sv_barrier_no_fence();                    // A: window w landed (or abort)
-        if (*abort_flag) {
-          sv_wait_vmcnt<0>();
-          return;
-        }
+    const int ntile = N / 16;
+    const int t0 = rd.tile0 + wg;
+    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(rd.codes), 0, N * (K / 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(rd.sz), 0, N * (K / 64) * 4, 0x00020000);
+    sv_u32x4 wb[P][T];
+    sv_u32x2 szr[P][T];
+    // unit (w, i) -> ring slot [w % P][i]
+    auto issue = [&](const int p, const int i, const int w) {
+      const int b = w * kSW + wave;
+      const bool ok = w < W && b < KB;
+      const int blk = ok ? sv_pk_block(t0 + i * grid, b, KB, ntile) : 0;
+      wb[p][i] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? lane * 16 : kSvOutOfRange,
+                                                       blk * 1024, kStreamC);
+      szr[p][i] = __builtin_amdgcn_raw_buffer_load_b64(srs, ok ? col * 8 : kSvOutOfRange,
+                                                       blk * 128, kStreamC);
+    };
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int i = 0; i < T; ++i) issue(p, i, p);
+    for (int w0 = 0; w0 < W; w0 += P) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        // Every step issues its P T loads, also past the round's last window
+        // (out of range), so that every path through the loop keeps the same
+        // loads in flight and the compiler's own waits stay as exact as ours.
+        const int w = w0 + p;
+        const bool live = w < W;                  // wave-uniform
         const int b = w * kSW + wave;
-        const bool valid = b < KB;                // wave-uniform
-        const uint8_t* const win = lds + ((ws + w) % G::S) * G::WINB;
-        // activation operands of block b: row tile a, group h, two 32-k slices
-        sv_u32x4 a0[2][MT], a1[2][MT];
-        float xsA[MT];
-        if (valid) {
-#pragma unroll
-          for (int a = 0; a < MT; ++a) {
-            const uint8_t* rp = win + (16 * a + col) * G::ROWB;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const int c0 = 16 * wave + 8 * h + 2 * q;   // 16-byte column in the window row
-              a0[h][a] = *reinterpret_cast<const sv_u32x4*>(rp + ((c0 ^ col) << 4));
-              a1[h][a] = *reinterpret_cast<const sv_u32x4*>(rp + (((c0 + 1) ^ col) << 4));
-            }
-            // group row sums: an all-ones A operand puts the sum of row col on
-            // lane (col, q); the correction wants group q on lane (col, q)
-            sv_f32x4 g0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(ones),
-                                                                  sv_as_bf16x8(a0[0][a]), fz,
-                                                                  0, 0, 0);
-            g0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(ones),
-                                                         sv_as_bf16x8(a1[0][a]), g0, 0, 0, 0);
-            sv_f32x4 g1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(ones),
-                                                                  sv_as_bf16x8(a0[1][a]), fz,
-                                                                  0, 0, 0);
-            g1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(ones),
-                                                         sv_as_bf16x8(a1[1][a]), g1, 0, 0, 0);
-            xsA[a] = q == 0 ? g0[0] : (q == 1 ? g1[0] : 0.0f);
+        const bool valid = live && b < KB;        // wave-uniform
+        {
+          if (live) {
+            sv_barrier_no_fence();                // A: window w landed (or abort)
+            if (abort_flag) return false;
           }
-        }
-        // T units of this window, ring slots slot .. slot + T - 1 (mod kR):
-        // a switch into the unrolled ring keeps every register index static.
-        int rem = T, ti = 0;
-        auto unit = [&](auto kc) {
-          constexpr int k = decltype(kc)::value;
-          sv_wait_vmcnt<2 * (kR - 1)>();          // unit k's two loads have landed
+          const uint8_t* const win = lds + ((ws + w) % G::S) * G::WINB;
+          // activation operands of block b: row tile a, group h, two 32-k slices
+          sv_u32x4 a0[2][MT], a1[2][MT];
+          float xsA[MT];
           if (valid) {
-            const sv_u32x4 wv = wb[k];
-            const sv_u32x2 sv = szr[k];
-            sv_f32x4 t[MT];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const sv_u32x4 b0 = sv_w4_dequant8(h ? wv.z : wv.x, magic);
-              const sv_u32x4 b1 = sv_w4_dequant8(h ? wv.w : wv.y, magic);
-              const float sc = sv_materialize(sv_half_lo(h ? sv.y : sv.x));
+            for (int a = 0; a < MT; ++a) {
+              const uint8_t* rp = win + (16 * a + col) * G::ROWB;
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const int c0 = 16 * wave + 8 * h + 2 * q;   // 16-byte column in the window row
+                a0[h][a] = *reinterpret_cast<const sv_u32x4*>(rp + ((c0 ^ col) << 4));
+                a1[h][a] = *reinterpret_cast<const sv_u32x4*>(rp + (((c0 + 1) ^ col) << 4));
+              }
+              // group row sums: an all-ones A operand puts the sum of row col
+              // on lane (col, q); the correction wants group q on lane (col, q)
+              sv_f32x4 g0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  sv_as_bf16x8(ones), sv_as_bf16x8(a0[0][a]), fz, 0, 0, 0);
+              g0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(ones),
+                                                           sv_as_bf16x8(a1[0][a]), g0, 0, 0, 0);
+              sv_f32x4 g1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  sv_as_bf16x8(ones), sv_as_bf16x8(a0[1][a]), fz, 0, 0, 0);
+              g1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(ones),
+                                                           sv_as_bf16x8(a1[1][a]), g1, 0, 0, 0);
+              xsA[a] = q == 0 ? g0[0] : (q == 1 ? g1[0] : 0.0f);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < T; ++i) {
+            // unit (w, i) has landed: the P T - 1 units issued after it may not
+            sv_wait_vmcnt<2 * (P * T - 1)>();
+            if (valid) {
+              const sv_u32x4 wv = wb[p][i];
+              const sv_u32x2 sv = szr[p][i];
+              sv_f32x4 t[MT];
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const sv_u32x4 b0 = sv_w4_dequant8(h ? wv.z : wv.x, magic);
+                const sv_u32x4 b1 = sv_w4_dequant8(h ? wv.w : wv.y, magic);
+                const float sc = sv_materialize(sv_half_lo(h ? sv.y : sv.x));
+#pragma unroll
+                for (int a = 0; a < MT; ++a) {
+                  sv_f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                      sv_as_bf16x8(a0[h][a]), sv_as_bf16x8(b0), fz, 0, 0, 0);
+                  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a1[h][a]),
+                                                                sv_as_bf16x8(b1), acc, 0, 0, 0);
+#pragma unroll
+                  for (int j = 0; j < 4; ++j) t[a][j] = h ? fmaf(sc, acc[j], t[a][j]) : sc * acc[j];
+                }
+              }
+              // bias and zero point of the block's two groups (lanes q >= 2 add 0)
+              const unsigned int szq = q == 0 ? sv.x : sv.y;
+              const float v = -(sv_half_lo(szq) * (128.0f + sv_half_hi(szq)));
+              const float nsz = q < 2 ? v : 0.0f;
 #pragma unroll
               for (int a = 0; a < MT; ++a) {
-                sv_f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    sv_as_bf16x8(a0[h][a]), sv_as_bf16x8(b0), fz, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a1[h][a]),
-                                                              sv_as_bf16x8(b1), acc, 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) t[a][i] = h ? fmaf(sc, acc[i], t[a][i]) : sc * acc[i];
+                t[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsA[a], nsz, t[a], 0, 0, 0);
+                yacc[i][a] += t[a];
               }
             }
-            // bias and zero point of the block's two groups (lanes q >= 2 add 0)
-            const unsigned int szq = q == 0 ? sv.x : sv.y;
-            const float v = -(sv_half_lo(szq) * (128.0f + sv_half_hi(szq)));
-            const float nsz = q < 2 ? v : 0.0f;
-#pragma unroll
-            for (int a = 0; a < MT; ++a)
-              t[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsA[a], nsz, t[a], 0, 0, 0);
-            switch (ti) {
-#define SV_ACC_CASE(I)                                                     \
-  case I:                                                                  \
-    if constexpr (I < TM) {                                                \
-      _Pragma("unroll") for (int a = 0; a < MT; ++a) yacc[I][a] += t[a];   \
-    }                                                                      \
-    break;
-              SV_ACC_CASE(0)
-              SV_ACC_CASE(1)
-              SV_ACC_CASE(2)
-              SV_ACC_CASE(3)
-              SV_ACC_CASE(4)
-              SV_ACC_CASE(5)
-#undef SV_ACC_CASE
-              default:
-                break;
-            }
-          }
-          sv_compiler_fence();
-          issue(wb[k], szr[k]);                   // the unit kR ahead into the freed slot
-          sv_compiler_fence();
-          ++ti;
-          --rem;
-        };
-        for (;;) {
-          switch (slot) {
-#define SV_UNIT_CASE(K)                              \
-  case K:                                            \
-    if (rem == 0) goto window_done;                  \
-    unit(std::integral_constant<int, K>{});          \
-    slot = (K + 1) % kR;                             \
-    [[fallthrough]];
-            SV_UNIT_CASE(0)
-            SV_UNIT_CASE(1)
-            SV_UNIT_CASE(2)
-            SV_UNIT_CASE(3)
-            SV_UNIT_CASE(4)
-            SV_UNIT_CASE(5)
-#undef SV_UNIT_CASE
-#define SV_UNIT_CASE(K)                              \
-  case K:                                            \
-    if constexpr (K < kR) {                          \
-      if (rem == 0) goto window_done;                \
-      unit(std::integral_constant<int, K>{});        \
-      slot = (K + 1) % kR;                           \
-    }                                                \
-    [[fallthrough]];
-            SV_UNIT_CASE(6)
-            SV_UNIT_CASE(7)
-            SV_UNIT_CASE(8)
-            SV_UNIT_CASE(9)
-            SV_UNIT_CASE(10)
-            SV_UNIT_CASE(11)
-#undef SV_UNIT_CASE
-            default:
-              break;
+            sv_compiler_fence();
+            issue(p, i, w + P);                   // unit (w + P, i) into the freed slot
+            sv_compiler_fence();
           }
         }
-      window_done:;
       }
-      ws += W;
+    }
+    ws += W;
+    return true;
+  };
+
+  Info rd = fetch(0);
+  for (int ri = 0; ri < nrounds; ++ri) {
+    const Info nxt = fetch(ri + 1);
+    const int tt = (rd.ntiles - wg + grid - 1) / grid;
+    const int T = tt < TM ? tt : TM;
+    // ring depth P T: 4 to 6 units of 1 KiB per wave
+    bool go = true;
+    // (m > 16: two row tiles double the activation operands and accumulators;
+    // the ring keeps to 2 to 4 units so the registers hold)
+    constexpr int P1 = MT == 1 ? 4 : 2, P2 = MT == 1 ? 2 : 1, P3 = MT == 1 ? 2 : 1;
+    switch (T) {
+      case 1: go = run_round(std::integral_constant<int, 1>{}, std::integral_constant<int, P1>{}, rd); break;
+      case 2: go = run_round(std::integral_constant<int, 2>{}, std::integral_constant<int, P2>{}, rd); break;
+      case 3: go = run_round(std::integral_constant<int, 3>{}, std::integral_constant<int, P3>{}, rd); break;
+      case 4: go = run_round(std::integral_constant<int, 4>{}, std::integral_constant<int, 1>{}, rd); break;
+      default:
+        if constexpr (TM >= 6) {
+          if (T == 5) go = run_round(std::integral_constant<int, 5>{}, std::integral_constant<int, 1>{}, rd);
+          else if (T == 6) go = run_round(std::integral_constant<int, 6>{}, std::integral_constant<int, 1>{}, rd);
+        }
+        break;
+    }
+    if (!go) {
+      sv_wait_vmcnt<0>();
+      return;
     }
     // ---- end of the round: fixed-order sum of the 8 waves' partial sums ----
     sv_barrier_no_fence();                        // E1: every wave done with the windows
@@ -501,8 +495,13 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(uint8_t* __restrict__ 
     }
     sv_barrier_no_fence();                        // E2: partial sums in LDS
     if (T > 0) {
-      __amdgpu_buffer_rsrc_t yrs =
-          __builtin_amdgcn_make_buffer_rsrc(rd.y, 0, m * rd.N * 4, 0x00020000);
+      const int N = rd.N, xo_cols = rd.xo_cols, tile0 = rd.tile0;
+      const bool has_xo = rd.xo != nullptr;
+      const float alpha = rd.alpha;
+      const __amdgpu_buffer_rsrc_t yrs =
+          __builtin_amdgcn_make_buffer_rsrc(rd.y, 0, m * N * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t ors =
+          __builtin_amdgcn_make_buffer_rsrc(rd.xo, 0, has_xo ? m * xo_cols * 2 : 0, 0x00020000);
       for (int v = wave; v < T * MT; v += kSW) {
         sv_f32x4 s = *reinterpret_cast<const sv_f32x4*>(lds + (v * kSW) * 1024 + lane * 16);
 #pragma unroll
@@ -520,36 +519,46 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(uint8_t* __restrict__ 
         const sv_f32x4 o = *reinterpret_cast<const sv_f32x4*>(tpose + (lane >> 2) * 16 +
                                                                4 * (lane & 3));
         sv_compiler_fence();
-        const int tile = rd.tile0 + wg + (v / MT) * grid;
+        const int tile = tile0 + wg + (v / MT) * grid;
         const int n0 = 16 * tile;
         const int row = 16 * (v % MT) + (lane >> 2);
         const unsigned int off =
-            row < m ? static_cast<unsigned int>((row * rd.N + n0 + 4 * (lane & 3)) * 4)
+            row < m ? static_cast<unsigned int>((row * N + n0 + 4 * (lane & 3)) * 4)
                     : kSvOutOfRange;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(sv_u32x4, o), yrs, off, 0,
                                                kStreamC);
-        if (rd.xo != nullptr && n0 < rd.xo_cols) {
+        if (has_xo && n0 < xo_cols) {
           sv_u32x2 pk;
-          pk.x = bf16_rne(rd.alpha * o[0]) | (bf16_rne(rd.alpha * o[1]) << 16);
-          pk.y = bf16_rne(rd.alpha * o[2]) | (bf16_rne(rd.alpha * o[3]) << 16);
-          *reinterpret_cast<sv_u32x2*>(lds + G::STAGE + v * 512 + lane * 8) = pk;
+          pk.x = bf16_rne(alpha * o[0]) | (bf16_rne(alpha * o[1]) << 16);
+          pk.y = bf16_rne(alpha * o[2]) | (bf16_rne(alpha * o[3]) << 16);
+          const unsigned int xoff =
+              row < m ? static_cast<unsigned int>((row * xo_cols + n0 + 4 * (lane & 3)) * 2)
+                      : kSvOutOfRange;
+          __builtin_amdgcn_raw_buffer_store_b64(pk, ors, xoff, 0, kSc1);
         }
       }
     }
-    sv_barrier_no_fence();                        // E3: xo staged for the IO wave
+    // The hand-off is complete at agent scope before the IO wave arrives.
+    // No weight load of this wave is in flight here (the round's ring is
+    // consumed; the next round's starts after E3), so this waits only for the
+    // stores and the round's out-of-range tail loads.
+    sv_wait_vmcnt<0>();
+    sv_barrier_no_fence();                        // E3
+    rd = nxt;
   }
   sv_wait_vmcnt<0>();
 }
 
 template <int MT>
-sv_status launch_chain(void* plan, int m, int grid, hipStream_t st) {
+sv_status launch_chain(void* plan, int nrounds, int m, int grid, hipStream_t st) {
   auto kern = chain_kernel<MT>;
   constexpr int kLds = ChainGeo<MT>::LDS;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess)
     return SV_ERR_HIP;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreadsC), kLds, st, static_cast<uint8_t*>(plan),
-                     m);
+  uint8_t* const p = static_cast<uint8_t*>(plan);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreadsC), kLds, st, p, p + sync_off(nrounds), m,
+                     nrounds);
   SV_LAUNCH_CHECK();
   return SV_OK;
 }
@@ -709,7 +718,6 @@ sv_status build_chain_image(int format, const sv_pass_link* links, int count, in
   hdr->nlinks = count;
   hdr->nsignals = nsig;
   hdr->spin_limit = kSpinLimit;
-  hdr->status = 0;
   for (int g = 0; g < kNG; ++g) hdr->group_size[g] = grid / kNG + (g < grid % kNG ? 1 : 0);
   *grid_out = grid;
   *nr_out = nr;
@@ -777,6 +785,10 @@ sv_status sv_chain_run(const sv_pass* pass, hipStream_t stream) {
   if ((reinterpret_cast<uintptr_t>(pass->plan) & 255u) != 0) return SV_ERR_ALIGN;
   if (pass->grid < 1 || pass->grid > kMaxGridC || pass->grid > device_cus())
     return SV_ERR_INVALID_ARG;
-  return pass->m > 16 ? launch_chain<2>(pass->plan, pass->m, pass->grid, stream)
-                      : launch_chain<1>(pass->plan, pass->m, pass->grid, stream);
+  if (pass->items < 1) return SV_ERR_INVALID_ARG;
+  return pass->m > 16 ? launch_chain<2>(pass->plan, pass->items, pass->m, pass->grid, stream)
+                      : launch_chain<1>(pass->plan, pass->items, pass->m, pass->grid, stream);
 }
+
+// Byte offset of a chain plan's status word (sv_pass_status).
+size_t sv_chain_status_offset(const sv_pass* pass) { return sync_off(pass->items) + kStatusOff; }
