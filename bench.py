@@ -3,20 +3,24 @@
 
 One step = one verify pass of a synthetic 9B-class decoder weight stack
 (32 layers, hidden 4096, FFN 12288; q/k/v/o 4096x4096, gate/up 4096x12288,
-down 12288x4096; W4 asymmetric, group 64) at k = 16 bf16 draft rows -- the
-128 GEMMs (per layer: fused qkv, o, fused gate|up, down) planned once and run
-by the pass executor in one launch -- followed by the accept/correct call for
-those k drafts over a 152000-entry vocabulary.  The step is captured in a HIP
-graph and replayed; inputs are resident in HBM before timing starts.
+down 12288x4096; W4 asymmetric, group 64) at k = 16 bf16 draft rows, run in
+MODEL ORDER -- per layer fused qkv -> o -> fused gate|up -> down, each GEMM
+reading the bf16 hand-off of the one before (sv_pass_chain_plan; one launch,
+a device-wide barrier between dependent GEMMs) -- followed by the
+accept/correct call for those k drafts over a 152000-entry vocabulary.  The
+step is captured in a HIP graph and replayed; inputs are resident in HBM
+before timing starts.
 
 Printed: one JSON line.  `value` is drafted tokens per second (k / step
-time).  Extra fields report the weight stream (GB/s of the W4 pass), the
-roofline of the pass kernel, the accept latency, the k sweep (W4 and W8), the
-per-GEMM-launch variant, the int8 path, accept statistics over 4096 trials
-per noise level, the measured HBM read peak, and the CPU oracle baseline.
+time).  Extra fields report the weight stream of the ordered pass, the
+roofline of its kernel, the same 128 GEMMs without ordering (the unordered
+executor: an upper bound, not a model pass), the accept latency, the k sweeps
+(W4 ordered and unordered, W8 unordered), the per-GEMM-launch variant, the
+int8 path, accept statistics over 4096 trials per noise level, the measured
+HBM read peak, a warm-up curve, and the CPU oracle baseline.
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 200] [--quick]
-       python bench.py --profile-pass [--format w4|w8|w4_i8] [--k K]
+       python bench.py --profile-pass [--format w4|w4_unordered|w8|w4_i8] [--k K]
                         (copy kernel, read probe and two executor passes, for
                          rocprofv3 counters)
        python bench.py --profile-accept [--k K] [--trials B]
@@ -34,6 +38,17 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = ("verify-pass weight GB/s and drafted tokens/s at k=16, 9B-shape W4; accept µs")
+WARMUP_CURVE_STEPS = 20
+
+
+def handoff_alpha(K):
+    """Scale of the bf16 hand-off between chained GEMMs that keeps the
+    activations near unit size for the synthetic weights (codes and zero
+    points uniform on 0..15, scales uniform on [0.01, 0.05]):
+    1 / sqrt(K E[w^2]), E[w^2] = E[(c - z)^2] E[s^2]."""
+    import numpy as np
+    ew2 = (2 * 255 / 12.0) * ((0.05 ** 3 - 0.01 ** 3) / (3 * 0.04))
+    return float(np.float32(1.0 / np.sqrt(K * ew2)))
 HBM_PEAK_GBPS = 8000.0
 BF16_DENSE_PEAK_TFLOPS = 2500.0
 LAYERS, HIDDEN, FFN, GROUP = 32, 4096, 12288, 64
@@ -107,7 +122,7 @@ def time_graph(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps, g
 
 
-def recorded_traffic(name, k):
+def recorded_traffic(name, k, kernel="pass_kernel"):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel reading), or None
     when it was taken at another k or on other kernel sources."""
@@ -118,7 +133,7 @@ def recorded_traffic(name, k):
     except (OSError, ValueError):
         return None
     if f"_k{k}" not in name or rec.get("sources_sha256") != rocprof_summary.sources_sha256(
-            "pass_kernel"):
+            kernel):
         return None
     return rec.get("traffic_bytes")
 
@@ -179,24 +194,39 @@ def int8_quant_error(torch, sv, synth, layer, k, dev):
 
 
 # --------------------------------------------------------------- cpu oracle --
-def cpu_baseline(k=16, min_seconds=10.0):
-    """The binary64 oracle on the host: whole layers of the W4 stack at k rows
-    (7 matrices, dequantize + matmul, rows in chunks), as many as fill about
-    min_seconds of oracle time, plus one accept trial at V = 152000; the step
-    time is extrapolated to 32 layers + accept.  Only the oracle calls are
-    timed (each layer's synthetic matrices are made before its clock starts)."""
+def cpu_baseline(k=16, min_seconds=6.0, accept_trials=8, dev=None):
+    """The binary64 oracle on the host, timed on bounded samples of each
+    workload (only the oracle calls are timed; synthetic inputs are made
+    before each clock starts):
+
+    * the headline: whole layers of the W4 stack at k rows (7 matrices,
+      dequantize + matmul, rows in chunks), as many as fill about
+      min_seconds, extrapolated to 32 layers, plus one accept trial at
+      V = 152000 -> drafted tokens/s of one step;
+    * the one-layer problem in full (K = 512, N = 1024, k = 4, accept over
+      V = 1000);
+    * one W8 layer and one int8-path layer (rotation + quantization + int8
+      GEMM) at k rows, extrapolated to 32 layers;
+    * accept at scale (V = 152000, k = 32): accept_trials trials per sigma in
+      {0.1, 1, 3}, reported per trial (inputs drawn on `dev` when given).
+    """
     import numpy as np
     import torch
     import oracle
     from verify_pass_sv_amd import synth
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        threads = 1
+        blas_threads = 1
     shapes = [(N, K) for _, N, K in oracle.decoder_stack_shapes(HIDDEN, FFN)]
-    xs = {K: synth.activations(k, K, seed=7).view(torch.int16).numpy().view(np.uint16)
-          for K in (HIDDEN, FFN)}
+    as_bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    xs = {K: as_bits(synth.activations(k, K, seed=7)) for K in (HIDDEN, FFN)}
+
+    def chunks(n, step=2048):
+        return [(r0, min(n, r0 + step)) for r0 in range(0, n, step)]
+
+    # W4 layers
     t_layers, n_layers = 0.0, 0
     while n_layers < LAYERS and (n_layers == 0 or t_layers < min_seconds):
         mats = []
@@ -205,8 +235,8 @@ def cpu_baseline(k=16, min_seconds=10.0):
             mats.append((K, c.numpy(), s.numpy(), z.numpy()))
         t0 = time.perf_counter()
         for K, c, s, z in mats:
-            for r0 in range(0, c.shape[0], 2048):
-                oracle.qgemm_w4(xs[K], c[r0:r0 + 2048], s[r0:r0 + 2048], z[r0:r0 + 2048])
+            for r0, r1 in chunks(c.shape[0]):
+                oracle.qgemm_w4(xs[K], c[r0:r1], s[r0:r1], z[r0:r1])
         t_layers += time.perf_counter() - t0
         n_layers += 1
         del mats
@@ -216,11 +246,66 @@ def cpu_baseline(k=16, min_seconds=10.0):
     oracle.verify_accept(tgt.numpy(), dft.numpy(), tok.numpy(), seed=0)
     t_acc = time.perf_counter() - t1
     t_step = LAYERS * t_layer + t_acc
-    return {"value": k / t_step, "unit": "drafted tokens/s", "cores": threads, "kind": "oracle",
+    del tgt, dft, tok
+
+    # the one-layer problem, in full
+    c, s, z = synth.w4_matrix(1024, 512, seed=1)
+    x = as_bits(synth.activations(4, 512, seed=2))
+    tt, td, tk = synth.accept_inputs(1, 4, 1000, seed=3, sigma=1.0)
+    t0 = time.perf_counter()
+    oracle.qgemm_w4(x, c.numpy(), s.numpy(), z.numpy())
+    oracle.verify_accept(tt.numpy(), td.numpy(), tk.numpy(), seed=0)
+    t_tiny = time.perf_counter() - t0
+
+    # one W8 layer, one int8-path layer
+    t_w8 = 0.0
+    for i, (N, K) in enumerate(shapes):
+        c, s = synth.w8_matrix(N, K, seed=5000 + i)
+        c, s = c.numpy(), s.numpy()
+        t0 = time.perf_counter()
+        for r0, r1 in chunks(N):
+            oracle.qgemm_w8(xs[K], c[r0:r1], s[r0:r1])
+        t_w8 += time.perf_counter() - t0
+    signs = {K: np.where(np.random.default_rng(K).random(K) < 0.5, -1, 1).astype(np.int8)
+             for K in (HIDDEN, FFN)}
+    t_i8 = 0.0
+    for i, (N, K) in enumerate(shapes):
+        c, s, z = synth.w4_matrix(N, K, seed=900 + i)
+        c, s, z = c.numpy(), s.numpy(), z.numpy()
+        t0 = time.perf_counter()
+        xq, xsc, _ = oracle.hadamard_i8(xs[K], signs[K], 4096)
+        for r0, r1 in chunks(N):
+            oracle.qgemm_w4_i8(xq, xsc, c[r0:r1], s[r0:r1], z[r0:r1])
+        t_i8 += time.perf_counter() - t0
+
+    # accept at scale: V = 152000, k = 32, per sigma
+    per_sigma = {}
+    for sigma in (0.1, 1.0, 3.0):
+        tt, td, tk = synth.accept_inputs(accept_trials, 32, VOCAB, seed=71, sigma=sigma,
+                                         device=dev if dev is not None else "cpu")
+        tt, td, tk = tt.cpu().numpy(), td.cpu().numpy(), tk.cpu().numpy()
+        t0 = time.perf_counter()
+        r = oracle.verify_accept(tt, td, tk, seed=0)
+        per_sigma[str(sigma)] = {
+            "us_per_trial": round((time.perf_counter() - t0) / accept_trials * 1e6, 1),
+            "mean_accepted": round(float(np.mean([t.n_acc for t in r])), 3)}
+        del tt, td, tk
+
+    ext = lambda t: round(LAYERS * t, 2)
+    return {"value": k / t_step, "unit": "drafted tokens/s", "cores": blas_threads,
+            "kind": "oracle",
             "sample": (f"{n_layers} of 32 layers (7 W4 matrices each, k={k}, binary64 "
                        f"dequantize+matmul) timed {t_layers:.1f} s, {t_layer:.2f} s per layer "
                        f"extrapolated x32, plus 1 accept trial (V={VOCAB}, k={k}) "
-                       f"{t_acc:.2f} s; {t_step:.1f} s per step")}
+                       f"{t_acc:.2f} s; {t_step:.1f} s per step"),
+            "os_cpu_count": os.cpu_count(), "blas_threads": blas_threads,
+            "tiny_full_s": round(t_tiny, 4),
+            "tiny_full": "W4 K=512 N=1024 k=4 GEMM + accept over V=1000, timed in full",
+            "w8_layer_s": round(t_w8, 3), "w8_pass_s_extrapolated_x32": ext(t_w8),
+            "int8_layer_s": round(t_i8, 3), "int8_pass_s_extrapolated_x32": ext(t_i8),
+            "accept_v152000_k32": per_sigma,
+            "accept_sample": (f"{accept_trials} trials per sigma (a bounded sample; "
+                              f"the 4096-trial statistics run in the test suite)")}
 
 
 # --------------------------------------------------------------------- main --
@@ -234,8 +319,9 @@ def main():
     ap.add_argument("--k", type=int, default=16)
     ap.add_argument("--quick", action="store_true", help="skip sweeps, stats and cpu baseline")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--format", default="w4", choices=("w4", "w8", "w4_i8"),
-                    help="weight path of --profile-pass")
+    ap.add_argument("--format", default="w4", choices=("w4", "w4_unordered", "w8", "w4_i8"),
+                    help="weight path of --profile-pass (w4: the pass in model order; the "
+                         "others: every GEMM on a fixed input, no ordering)")
     ap.add_argument("--profile-pass", action="store_true",
                     help="copy kernel + read probe + 2 eager W4 passes, then exit")
     ap.add_argument("--profile-accept", action="store_true",
@@ -326,6 +412,22 @@ def main():
     def w4_pass(kk):
         return sv.sv_pass_plan("w4", w4_gemms(kk))
 
+    # the same stack in model order: each GEMM reads the bf16 hand-off of the
+    # one before it (the q part of qkv, the gate part of gate|up)
+    h0 = synth.activations(32, HIDDEN, seed=11, device=dev)
+    handed = {"qkv": HIDDEN, "o": HIDDEN, "gateup": FFN, "down": HIDDEN}
+    chain_xo = [[torch.empty((32, handed[name]), dtype=torch.bfloat16, device=dev)
+                 for (name, *_r) in layer] for layer in w4]
+
+    def w4_chain(kk):
+        h, links = h0[:kk], []
+        for li, layer in enumerate(w4):
+            for gi, (name, N, K, c, s, z, pc, ps) in enumerate(layer):
+                xo = chain_xo[li][gi][:kk]
+                links.append((h, pc, ps, N, y_own[li][gi][:kk], xo, handoff_alpha(K)))
+                h = xo
+        return sv.sv_pass_chain_plan(links)
+
     def w4_launches(kk, packed=True):
         xh, xf = x_h[:kk].contiguous(), x_f[:kk].contiguous()
         out = {N: y[:kk] for N, y in ys.items()}
@@ -352,6 +454,8 @@ def main():
         sink = torch.empty(sv.sv_read_probe_sink_words(), dtype=torch.int32, device=dev)
         sv.sv_read_bandwidth_probe(src, sink)
         if args.format == "w4":
+            p = w4_chain(k)
+        elif args.format == "w4_unordered":
             p = w4_pass(k)
         elif args.format == "w4_i8":
             xi = {K: synth.int8_activations(k, K, seed=13 + K, device=dev) for K in (HIDDEN, FFN)}
@@ -370,27 +474,40 @@ def main():
         for _ in range(2):
             sv.sv_pass_run(p)
         torch.cuda.synchronize()
+        assert sv.sv_pass_status(p) == 0
         log("profile pass done")
         return
 
-    # ---- the step: W4 pass at k rows + accept over V = 152000 ----
+    # ---- the step: the W4 pass in model order at k rows + accept over
+    # V = 152000 (three launches: the chain, the accept statistics, decide) ----
     tgt, dft, tok = synth.accept_inputs(1, k, VOCAB, seed=21, sigma=1.0, device=dev)
     acc_out = {"tokens": torch.empty((1, k + 1), dtype=torch.int32, device=dev),
                "n_acc": torch.empty((1,), dtype=torch.int32, device=dev),
                "status": torch.empty((1,), dtype=torch.int32, device=dev)}
     acc_ws = torch.empty(sv.sv_verify_accept_workspace_bytes(1, k, VOCAB), dtype=torch.uint8,
                          device=dev)
-    plan = w4_pass(k)
+    plan = w4_chain(k)
 
     def step():
         sv.sv_pass_run(plan)
         sv.sv_verify_accept(tgt, dft, tok, seed=0, out=acc_out, workspace=acc_ws)
 
-    log(f"timing the step (graph replay); pass plan: {plan.items} items on {plan.grid} "
+    # warm-up curve: the first steps of the process, each timed on its own
+    # (events around one eager step), before any other timing
+    curve = []
+    for _ in range(WARMUP_CURVE_STEPS):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        curve.append(round(e0.elapsed_time(e1), 4))
+    log(f"timing the step (graph replay); chain plan: {plan.items} rounds on {plan.grid} "
         f"workgroups")
     ms_step, _ = time_graph(torch, step, args.steps, args.warmup)
+    assert sv.sv_pass_status(plan) == 0, "chain plan reported a barrier timeout"
 
-    # ---- roofline of the pass kernel: one launch per pass.  Its average
+    # ---- roofline of the chain kernel: one launch per pass.  Its average
     # launch duration is event-timed on the stream the kernel runs on, over
     # graph replays of REPS back-to-back launches (amortizing the replay's
     # own launch latency) ----
@@ -401,9 +518,23 @@ def main():
     weight_gbps = pass_bytes / (ms_pass * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(weight_gbps, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(weight_gbps / HBM_PEAK_GBPS, 4),
-                "traffic": recorded_traffic("w4_pass_9b_k16", k),
-                "kernel": "pass_kernel<W4> (all 128 GEMMs of the pass in one launch)",
+                "traffic": recorded_traffic("w4_chain_9b_k16", k, "chain_kernel"),
+                "kernel": "chain_kernel<1> (the 128 GEMMs of the pass in model order, "
+                          "one launch, device-wide barriers between dependent GEMMs)",
                 "bytes_per_launch": pass_bytes, "launch_us": round(ms_pass * 1e3, 2)}
+    # the same GEMMs without ordering (each reads a fixed input; the executor
+    # runs them in any order): an upper bound of the weight stream, not a pass
+    plan_u = w4_pass(k)
+    ms_rep_u, _ = time_graph(torch, lambda: [sv.sv_pass_run(plan_u) for _ in range(REPS)],
+                             max(2, args.steps // REPS), max(1, args.warmup // REPS))
+    ms_u = ms_rep_u / REPS
+    gbps_u = pass_bytes / (ms_u * 1e-3) / 1e9
+    unordered = {"pass_ms": round(ms_u, 4), "GBps": round(gbps_u, 1),
+                 "frac_of_8TBps": round(gbps_u / HBM_PEAK_GBPS, 4),
+                 "kernel": "pass_kernel<W4>",
+                 "traffic": recorded_traffic("w4_pass_9b_k16", k, "pass_kernel"),
+                 "note": "128 GEMMs on fixed inputs in one launch, no ordering: "
+                         "an upper bound of the weight stream, not a model pass"}
 
     # ---- accept latency at k = 32 (B = 1) and throughput at B = 64 ----
     def accept_bench(B, kk):
@@ -433,6 +564,9 @@ def main():
     extra = {"weight_GBps": round(weight_gbps, 1),
              "weight_frac_of_8TBps": round(weight_gbps / HBM_PEAK_GBPS, 4),
              "pass_ms": round(ms_pass, 4), "pass_weight_bytes": pass_bytes,
+             "pass_order": "model order (chain)",
+             "unordered_upper_bound": unordered,
+             "warmup_curve_ms": curve,
              "accept_us_k32_B1": round(accept_us_b1, 2),
              "accept_host_wall_us_k32_B1": round(accept_host_us_b1, 1),
              "accept_us_per_trial_k32_B64": round(accept_us_b64 / 64, 3),
@@ -453,15 +587,21 @@ def main():
             ms_l, _ = time_graph(torch, lambda Ls=Ls: [fn() for _, fn in Ls], 20, 20)
             extra[key] = {"pass_ms": round(ms_l, 4),
                           "GBps": round(pass_bytes / (ms_l * 1e-3) / 1e9, 1)}
-        # W4 k sweep: memory-bound to MFMA crossover, latency ratio
-        sweep = {}
+        # W4 k sweeps (model order and unordered): latency ratio t(32)/t(1)
+        sweep, sweep_u = {}, {}
         for kk in (1, 4, 8, 16, 32):
-            pk = w4_pass(kk)
-            ms, _ = time_graph(torch, lambda pk=pk: sv.sv_pass_run(pk), 60, 60)
-            sweep[kk] = {"pass_ms": round(ms, 4), "GBps": round(pass_bytes / (ms * 1e-3) / 1e9, 1),
-                         "drafted_tok_s": round(kk / (ms * 1e-3), 1)}
+            for table, mk in ((sweep, w4_chain), (sweep_u, w4_pass)):
+                pk = mk(kk)
+                ms, _ = time_graph(torch, lambda pk=pk: sv.sv_pass_run(pk), 40, 40)
+                table[kk] = {"pass_ms": round(ms, 4),
+                             "GBps": round(pass_bytes / (ms * 1e-3) / 1e9, 1),
+                             "drafted_tok_s": round(kk / (ms * 1e-3), 1)}
+                del pk
         extra["w4_k_sweep"] = sweep
         extra["w4_latency_ratio_k32_over_k1"] = round(sweep[32]["pass_ms"] / sweep[1]["pass_ms"], 3)
+        extra["w4_k_sweep_unordered"] = sweep_u
+        extra["w4_latency_ratio_k32_over_k1_unordered"] = round(
+            sweep_u[32]["pass_ms"] / sweep_u[1]["pass_ms"], 3)
         # MFMA utilisation of the W4 pass at k = 16 and 32: the useful flops
         # (2 k per weight) over the measured pass time against the dense bf16
         # peak, and from the recorded counters the fraction of cycles the
@@ -688,7 +828,7 @@ def main():
     cpu = None
     if not (args.quick or args.no_cpu):
         log("timing the CPU oracle baseline")
-        cpu = cpu_baseline(k)
+        cpu = cpu_baseline(k, dev=dev)
 
     line = {
         "metric": METRIC, "value": round(k / (ms_step * 1e-3), 1), "unit": "drafted tokens/s",
@@ -699,7 +839,7 @@ def main():
                                "32 layers (hidden 4096, ffn 12288), k=16 bf16 draft rows, "
                                "then accept/correct over V=152000",
                    "k": k, "layers": LAYERS, "hidden": HIDDEN, "ffn": FFN, "group": GROUP,
-                   "vocab": VOCAB, "launches_per_step": 1 + 3,
+                   "vocab": VOCAB, "launches_per_step": 3, "pass_order": "model order",
                    "graph": "hipGraph replay"},
         "roofline": roofline, "cpu_baseline": cpu, **extra,
     }

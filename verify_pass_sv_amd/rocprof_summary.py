@@ -26,6 +26,7 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 # Sources whose change makes recorded counters stale, per kernel family.
 KERNEL_SOURCES = {
     "pass_kernel": ["csrc/pass.hip", "csrc/w4_packed_dev.h", "csrc/sv_common.h"],
+    "chain_kernel": ["csrc/pass_chain.hip", "csrc/w4_packed_dev.h", "csrc/sv_common.h"],
     "stats_kernel": ["csrc/verify_accept.hip", "csrc/sv_common.h", "csrc/sv_philox.h"],
     "decide_kernel": ["csrc/verify_accept.hip", "csrc/sv_common.h", "csrc/sv_philox.h"],
     "sampled_rows_kernel": ["csrc/verify_sampled.hip", "csrc/sv_common.h", "csrc/sv_philox.h"],
@@ -55,12 +56,16 @@ def read_stats(trace_dir):
     return rows
 
 
-def read_counters(pmc_dir):
+def read_counters(pmc_dir, largest=()):
+    """Per kernel name, each counter averaged over its dispatches; for the
+    kernels named in `largest`, the largest reading instead (the copy kernel
+    of known size shares its name with the runtime's small copies)."""
     agg = collections.defaultdict(lambda: collections.defaultdict(list))
     for f in glob.glob(os.path.join(pmc_dir, "**", "*_counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
             agg[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
-    return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in agg.items()}
+    return {k: {c: (max(v) if any(n in k for n in largest) else sum(v) / len(v))
+                for c, v in d.items()} for k, d in agg.items()}
 
 
 def pick(d, key):
@@ -90,7 +95,7 @@ def main():
         if a.kernel in r[0]:
             kname, kstat = r[0], r
             break
-    cnt = read_counters(a.pmc)
+    cnt = read_counters(a.pmc, largest=(COPY_KERNEL,))
     kc_name, kc = pick(cnt, a.kernel)
     _, cc = pick(cnt, COPY_KERNEL)
     copy_kib = a.copy_bytes / 1024.0
