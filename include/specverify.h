@@ -441,6 +441,34 @@ sv_status sv_verify_accept(const float* target_logits, const float* draft_logits
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * sv_verify_accept_noalloc -- sv_verify_accept for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument and no allocation
+ * of any kind.  Its workspace is a fixed array of SV_ACCEPT_SCRATCH_BYTES
+ * (2 MiB) per device, held by the library until the process ends; the
+ * device's address of it is looked up once per device, on the first call
+ * made with that device current.
+ *
+ * Arguments, outputs, results and errors as sv_verify_accept, except:
+ *   SV_ERR_WORKSPACE  sv_verify_accept_workspace_bytes(B, k, V) exceeds
+ *                     SV_ACCEPT_SCRATCH_BYTES (e.g. B = 64, k = 32 and
+ *                     V = 262144 fit; B = 256, k = 32, V = 152000 does not);
+ *                     nothing is enqueued
+ *   SV_ERR_HIP        the array's device address could not be looked up
+ * Every call on one device shares that device's array: calls that overlap on
+ * one device (other streams, other host threads) race and must be ordered by
+ * the caller.  The array keeps the last call's contents; nothing in it needs
+ * to start at zero.
+ */
+#define SV_ACCEPT_SCRATCH_BYTES (2u << 20)
+size_t sv_verify_accept_noalloc_max_bytes(void);
+sv_status sv_verify_accept_noalloc(const float* target_logits, const float* draft_logits,
+                                   const int32_t* draft_tokens, int B, int k, int V,
+                                   uint64_t seed, uint32_t offset,
+                                   int32_t* out_tokens, int32_t* out_n_acc, int32_t* out_status,
+                                   float* p_at, float* q_at, float* lse, hipStream_t stream);
+
+/*
  * sv_verify_accept_stats -- sv_verify_accept whose target softmax statistics
  * come from the vocabulary projection's epilogue (the sv_pass_gemm `stats`
  * output) instead of a read of the target logits: the fused LM-head verify.

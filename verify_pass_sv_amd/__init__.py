@@ -17,7 +17,7 @@ _BINDING_NAMES = (
     "sv_verify_coupled", "sv_verify_coupled_workspace_bytes", "sv_verify_tree",
     "sv_verify_tree_workspace_bytes", "sv_verify_accept_stats", "sv_pass_status",
     "sv_pass_chain_plan", "sv_pass_chain_image", "SvPassLink", "PASS_STATUS_STALE",
-    "PASS_STATUS_TIMEOUT",
+    "PASS_STATUS_TIMEOUT", "sv_verify_accept_noalloc", "sv_verify_accept_noalloc_max_bytes",
 )
 
 __all__ = list(_BINDING_NAMES)

@@ -18,6 +18,7 @@ SV_MAX_ROWS = 32
 EXPORTED_SYMBOLS = (
     "sv_status_str", "sv_version", "sv_qgemm_w4", "sv_qgemm_w8", "sv_hadamard_i8",
     "sv_qgemm_w4_i8", "sv_verify_accept_workspace_bytes", "sv_verify_accept",
+    "sv_verify_accept_noalloc_max_bytes", "sv_verify_accept_noalloc",
     "sv_philox4x32_10", "sv_read_probe_sink_words", "sv_read_bandwidth_probe",
     "sv_w4_packed_codes_bytes", "sv_w4_packed_sz_bytes", "sv_w4_pack", "sv_qgemm_w4_packed",
     "sv_w8_pack", "sv_pass_plan_bytes", "sv_pass_plan", "sv_pass_run",
@@ -92,6 +93,9 @@ def _load():
                                    vp, vp, sz, vp]),
         "sv_verify_accept_stats": (i32, [vp, vp, vp, vp, i32, i32, i32, u64, u32, vp, vp, vp,
                                          vp, vp, vp, vp, sz, vp]),
+        "sv_verify_accept_noalloc_max_bytes": (sz, []),
+        "sv_verify_accept_noalloc": (i32, [vp, vp, vp, i32, i32, i32, u64, u32, vp, vp, vp, vp,
+                                           vp, vp, vp]),
         "sv_philox4x32_10": (i32, [vp, vp, vp, i32, vp]),
         "sv_read_probe_sink_words": (i32, []),
         "sv_read_bandwidth_probe": (i32, [vp, sz, vp, vp]),
@@ -475,6 +479,31 @@ def sv_verify_accept(target_logits, draft_logits, draft_tokens, seed, offset=0, 
         _ptr(out["tokens"]), _ptr(out["n_acc"]), _ptr(out["status"]), _ptr(out.get("p_at")),
         _ptr(out.get("q_at")), _ptr(out.get("lse")), _ptr(workspace),
         ctypes.c_size_t(workspace.numel()), _stream(stream)))
+    return out
+
+
+def sv_verify_accept_noalloc_max_bytes():
+    return int(lib.sv_verify_accept_noalloc_max_bytes())
+
+
+def sv_verify_accept_noalloc(target_logits, draft_logits, draft_tokens, seed, out, offset=0,
+                             stream=None):
+    """sv_verify_accept on the library's fixed per-device workspace: no
+    device allocation in the library (the caller passes every output in
+    `out`: tokens, n_acc, status, and optionally p_at, q_at, lse)."""
+    B, k1, V = target_logits.shape
+    k = k1 - 1
+    _need(target_logits, "target_logits", torch.float32, (B, k + 1, V))
+    _need(draft_logits, "draft_logits", torch.float32, (B, k, V))
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, k))
+    _need(out["tokens"], "tokens", torch.int32, (B, k + 1))
+    _need(out["n_acc"], "n_acc", torch.int32, (B,))
+    _need(out["status"], "status", torch.int32, (B,))
+    _check("sv_verify_accept_noalloc", lib.sv_verify_accept_noalloc(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), B, k, V,
+        ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), ctypes.c_uint32(int(offset) & 0xFFFFFFFF),
+        _ptr(out["tokens"]), _ptr(out["n_acc"]), _ptr(out["status"]), _ptr(out.get("p_at")),
+        _ptr(out.get("q_at")), _ptr(out.get("lse")), _stream(stream)))
     return out
 
 

@@ -37,6 +37,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -827,4 +829,52 @@ extern "C" sv_status sv_philox4x32_10(const uint32_t* ctr, const uint32_t* key, 
                      n);
   SV_LAUNCH_CHECK();
   return SV_OK;
+}
+
+// ---- no-allocation variant -----------------------------------------------
+// The workspace of sv_verify_accept_noalloc: one fixed array per device,
+// held until the process ends.  Host code never passes `scratch` itself (in
+// host code the name is a stand-in, not a device address): it looks up each
+// device's address once, with that device current, and passes that.
+namespace {
+__device__ __align__(256) unsigned char scratch[SV_ACCEPT_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];               // per device, set on first use
+
+// Device address of this device's scratch array (nullptr on a HIP error).
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" size_t sv_verify_accept_noalloc_max_bytes(void) { return SV_ACCEPT_SCRATCH_BYTES; }
+
+extern "C" sv_status sv_verify_accept_noalloc(const float* target_logits,
+                                              const float* draft_logits,
+                                              const int32_t* draft_tokens, int B, int k, int V,
+                                              uint64_t seed, uint32_t offset,
+                                              int32_t* out_tokens, int32_t* out_n_acc,
+                                              int32_t* out_status, float* p_at, float* q_at,
+                                              float* lse, hipStream_t stream) {
+  if (B < 1 || k < 1 || k > SV_MAX_ROWS || V < 1) return SV_ERR_INVALID_ARG;
+  if (static_cast<long long>(k + 1) * V >= (1LL << 31)) return SV_ERR_INVALID_ARG;
+  const size_t need = ws_layout(B, k, V).bytes;
+  if (need > SV_ACCEPT_SCRATCH_BYTES) return SV_ERR_WORKSPACE;   // beyond the fixed array
+  if (!target_logits || !draft_logits || !draft_tokens || !out_tokens || !out_n_acc ||
+      !out_status)
+    return SV_ERR_NULL;
+  void* ws = scratch_address();
+  if (!ws) return SV_ERR_HIP;
+  return verify_accept(target_logits, nullptr, draft_logits, draft_tokens, B, k, V, seed, offset,
+                       out_tokens, out_n_acc, out_status, p_at, q_at, lse, ws, need, stream);
 }
