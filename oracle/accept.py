@@ -88,7 +88,7 @@ class AcceptResult:
         return self.n_acc + 1 if self.status == 0 else 0
 
 
-def accept_trial(target_logits, draft_logits, draft_tokens, u, u2, ties=None):
+def accept_trial(target_logits, draft_logits, draft_tokens, u, u2, ties=None, force=None):
     """One trial of the accept/correct step with explicit uniforms.
 
     target_logits [k + 1, V], draft_logits [k, V], draft_tokens [k];
@@ -112,13 +112,13 @@ def accept_trial(target_logits, draft_logits, draft_tokens, u, u2, ties=None):
 
     P = probs(t, lse_t[:, None])
     Q = probs(d, lse_d[:, None])
-    res = accept_on_probs(P, Q, toks, u, u2, ties)
+    res = accept_on_probs(P, Q, toks, u, u2, ties, force)
     res.lse_target = lse_t
     res.lse_draft = lse_d
     return res
 
 
-def accept_on_probs(P, Q, draft_tokens, u, u2, ties=None):
+def accept_on_probs(P, Q, draft_tokens, u, u2, ties=None, force=None):
     """The accept scan and the replacement/bonus draw on explicit rows.
 
     P [k + 1, V]: the target's distributions (row k for the bonus), Q [k, V]:
@@ -127,6 +127,12 @@ def accept_on_probs(P, Q, draft_tokens, u, u2, ties=None):
     residual[, accept relative to p]) replaces the near-tie widths of
     reading 6: an accept decision is flagged when |u q - p| is below
     max(accept, relative * p) (flags only; the decisions do not depend on it).
+
+    force = {position: accepted} takes the given decision at a position whose
+    decision is flagged (a near tie of reading 6, which a binary32 evaluation
+    may take either way) and continues the trial from it; forcing a position
+    that is not flagged raises ValueError.  It lets a comparison follow the
+    device's choice at an undecidable position and check everything after it.
     """
     tie_a, tie_r, tie_p = ((NEAR_TIE_ACCEPT, NEAR_TIE_RESIDUAL, 0.0) if ties is None
                            else (tuple(ties) + (0.0,))[:3])
@@ -146,7 +152,12 @@ def accept_on_probs(P, Q, draft_tokens, u, u2, ties=None):
         lhs = u[i] * q_at[i]
         flags[i] = (abs(lhs - p_at[i]) < max(tie_a, tie_p * p_at[i]) and p_at[i] > 0.0
                     and q_at[i] > 0.0)
-        if not (lhs < p_at[i]):
+        accepted = lhs < p_at[i]
+        if force is not None and i in force:
+            if not flags[i]:
+                raise ValueError(f"position {i} is not a near tie; its decision is fixed")
+            accepted = bool(force[i])
+        if not accepted:
             n_acc = i
             break
 

@@ -1,8 +1,11 @@
 """GPU parity of sv_verify_accept (and its Philox) against the oracle.
 
-Token decisions must be bit-exact except where the oracle flags a near tie
-(|u q - p| < 1e-6 for an accept decision, or a residual threshold within
-1e-6 * S of a bin edge); softmax diagnostics within 2e-3 relative.
+Token decisions must be bit-exact.  Where the oracle flags a near tie
+(|u q - p| < 1e-6 for an accept decision) it continues from the device's
+decision and the rest of the trial must match; a flagged replacement draw
+(threshold within 1e-6 S of a bin edge) must be a token whose bin lies
+within that width of the threshold.  Softmax diagnostics within 2e-3
+relative.
 """
 import os
 
@@ -23,41 +26,64 @@ def _sv():
     return sv
 
 
-def _compare(out, res, k, check_diag=True):
-    """Compare device outputs with oracle results trial by trial."""
+def _oracle_following(tgt, dft, tok, seed, offset, b, n_acc_dev):
+    """The oracle's trial b, continued from the device's decision at every
+    flagged (near-tie) accept position it reaches: accepted there iff the
+    device accepted more drafts than that position.  Returns the result and
+    the positions that were forced."""
+    k = tok.shape[-1]
+    u, u2 = oracle.accept_uniforms(seed, b, k, offset=offset)
+    force = {}
+    while True:
+        r = oracle.accept_trial(tgt, dft, tok, u, u2, force=force)
+        if r.status != 0:
+            return r, force
+        pending = [int(i) for i in np.flatnonzero(r.accept_flags) if int(i) not in force]
+        if not pending:
+            return r, force
+        force[pending[0]] = bool(n_acc_dev > pending[0])
+
+
+def _compare_full(out, tgt, dft, tok, seed, offset=0, trials=None, check_diag=True):
+    """Every trial compared with the oracle.  At a flagged accept decision
+    the oracle follows the device's choice and everything after it must
+    match; a flagged replacement draw must be a token whose cumulative-sum
+    bin lies within the oracle's residual width of the threshold.  Returns
+    (trials with a forced decision, trials with a flagged draw)."""
     n_acc = out["n_acc"].cpu().numpy()
     status = out["status"].cpu().numpy()
     toks = out["tokens"].cpu().numpy()
-    flagged = 0
-    for b, r in enumerate(res):
-        assert status[b] == r.status, (b, status[b], r.status)
+    tol = oracle.accept.NEAR_TIE_RESIDUAL
+    n_forced = n_draw = 0
+    trials = range(tok.shape[0]) if trials is None else trials
+    for j, b in enumerate(trials):
+        r, force = _oracle_following(tgt[j], dft[j], tok[j], seed, offset, b, n_acc[j])
+        assert status[j] == r.status, (b, status[j], r.status)
         if r.status != 0:
-            assert n_acc[b] == -1 and np.all(toks[b] == -1)
+            assert n_acc[j] == -1 and np.all(toks[j] == -1)
             continue
-        acc_flag = r.accept_flags is not None and r.accept_flags.any()
-        if acc_flag:
-            flagged += 1
-            first = int(np.argmax(r.accept_flags))
-            assert toks[b, :first].tolist() == r.tokens[:first]
-            continue
-        assert n_acc[b] == r.n_acc, (b, n_acc[b], r.n_acc)
-        assert toks[b, :r.n_acc].tolist() == r.tokens[:r.n_acc]
-        assert np.all(toks[b, r.n_out:] == -1)
-        if r.residual_flag:
-            flagged += 1
-            continue
-        assert toks[b, r.n_acc] == r.tokens[r.n_acc], (b, toks[b], r.tokens)
-    if check_diag and "p_at" in out:
-        p = out["p_at"].cpu().numpy(); q = out["q_at"].cpu().numpy()
-        lse = out["lse"].cpu().numpy()
-        for b, r in enumerate(res):
-            if r.status != 0:
-                continue
-            np.testing.assert_allclose(p[b], r.p_at, rtol=2e-3, atol=1e-12)
-            np.testing.assert_allclose(q[b], r.q_at, rtol=2e-3, atol=1e-12)
+        n_forced += bool(force)
+        assert n_acc[j] == r.n_acc, (b, n_acc[j], r.n_acc, force)
+        assert toks[j, :r.n_acc].tolist() == r.tokens[:r.n_acc], b
+        assert np.all(toks[j, r.n_out:] == -1)
+        v = int(toks[j, r.n_acc])
+        if not r.residual_flag:
+            assert v == r.tokens[-1], (b, v, r.tokens[-1])
+        else:
+            n_draw += 1
+            csum, thr = r.extra["residual_csum"], r.extra["residual_thr"]
+            S = csum[-1]
+            lo = csum[v - 1] if v > 0 else 0.0
+            assert lo - tol * S <= thr <= csum[v] + tol * S, (b, v, r.tokens[-1])
+        if check_diag and "p_at" in out:
+            np.testing.assert_allclose(out["p_at"][j].cpu().numpy()[:len(r.p_at)], r.p_at,
+                                       rtol=2e-3, atol=1e-12)
+            np.testing.assert_allclose(out["q_at"][j].cpu().numpy()[:len(r.q_at)], r.q_at,
+                                       rtol=2e-3, atol=1e-12)
             ref_lse = np.concatenate([r.lse_target, r.lse_draft])
-            np.testing.assert_allclose(lse[b], ref_lse, rtol=2e-3, atol=2e-5)
-    return flagged
+            np.testing.assert_allclose(out["lse"][j].cpu().numpy(), ref_lse, rtol=2e-3,
+                                       atol=2e-5)
+    return n_forced, n_draw
 
 
 def test_philox_known_answer_vectors():
@@ -103,9 +129,8 @@ def test_matches_oracle(B, k, V, sigma):
     tgt, dft, tok = synth.accept_inputs(B, k, V, seed=B + k + V, sigma=sigma)
     out = sv.sv_verify_accept(*to_dev(tgt, dft, tok), seed=0, diagnostics=True)
     torch.cuda.synchronize()
-    res = oracle.verify_accept(tgt.numpy(), dft.numpy(), tok.numpy(), seed=0)
-    flagged = _compare(out, res, k)
-    assert flagged <= max(2, B // 4)
+    n_forced, n_draw = _compare_full(out, tgt.numpy(), dft.numpy(), tok.numpy(), seed=0)
+    assert n_forced + n_draw <= max(2, B // 4)
 
 
 @pytest.mark.parametrize("V", [200000, 200003])
@@ -118,29 +143,64 @@ def test_matches_oracle_multi_batch_spans(V):
     tgt, dft, tok = synth.accept_inputs(B, k, V, seed=V % 97, sigma=0.3)
     out = sv.sv_verify_accept(*to_dev(tgt, dft, tok), seed=5, diagnostics=True)
     torch.cuda.synchronize()
-    res = oracle.verify_accept(tgt.numpy(), dft.numpy(), tok.numpy(), seed=5)
     # p_at / q_at (from the recorded token logits) are checked against the
-    # oracle inside _compare; a draw near a bin edge is flagged, as usual
-    _compare(out, res, k)
+    # oracle inside _compare_full
+    _compare_full(out, tgt.numpy(), dft.numpy(), tok.numpy(), seed=5)
 
 
 @pytest.mark.parametrize("sigma", [0.1, 1.0, 3.0])
-def test_full_vocab_k32_sampled_trials(sigma):
-    # V = 152000, k = 32 at the launch configuration of the bench (B = 64);
-    # the oracle checks 8 of the trials
+def test_full_vocab_k32_all_trials(sigma):
+    # V = 152000, k = 32 at the launch configuration of the bench (B = 64):
+    # every trial against the oracle, flagged decisions followed
     sv = _sv()
     B, k, V = 64, 32, 152000
+    print(f"accept V={V} k={k} B={B} sigma={sigma}", flush=True)
     tgt, dft, tok = synth.accept_inputs(B, k, V, seed=int(sigma * 10), sigma=sigma, device=DEV)
     out = sv.sv_verify_accept(tgt, dft, tok, seed=0, diagnostics=True)
     torch.cuda.synchronize()
-    pick = [0, 1, 7, 20, 33, 41, 50, 63]
-    res = []
-    for b in pick:
-        r = oracle.verify_accept(tgt[b:b + 1].cpu().numpy(), dft[b:b + 1].cpu().numpy(),
-                                 tok[b:b + 1].cpu().numpy(), seed=0, trial_base=b)[0]
-        res.append(r)
-    sub = {key: val[pick] for key, val in out.items()}
-    _compare(sub, res, k)
+    t, d, kk = tgt.cpu().numpy(), dft.cpu().numpy(), tok.cpu().numpy()
+    del tgt, dft
+    # at V = 152000 most probabilities lie far below 1e-6, so the absolute
+    # near-tie width flags many decisions; each is followed, not skipped
+    n_forced, n_draw = _compare_full(out, t, d, kk, seed=0)
+    print(f"sigma={sigma}: {n_forced} trials followed the device through a near tie, "
+          f"{n_draw} flagged draws checked for validity")
+    assert n_draw <= 8
+
+
+@pytest.mark.parametrize("sigma", [0.1, 1.0])
+def test_acceptance_length_z_test_4096_trials(sigma):
+    # 4096 trials on one pair of logit blocks (V = 152000, k = 32), drafts
+    # drawn from q in binary64: the accepted length has the law
+    # P(n_acc >= j) = prod_{i < j} beta_i, beta_i = sum_v min(p_i(v), q_i(v))
+    # (the chance that position i accepts a draft from q_i; Speculative
+    # Decoding Clearly Explained, "Accept from left to right").  The mean of
+    # the device's n_acc must lie within 4 standard errors of that law's.
+    sv = _sv()
+    k, V, B, calls = 32, 152000, 64, 64
+    t1, d1, _ = synth.accept_inputs(1, k, V, seed=400 + int(sigma * 10), sigma=sigma)
+    t, d = t1[0].numpy().astype(np.float64), d1[0].numpy().astype(np.float64)
+    P = np.exp(t - oracle.row_lse(t)[0][:, None])
+    Q = np.exp(d - oracle.row_lse(d)[0][:, None])
+    beta = np.minimum(P[:k], Q).sum(axis=1)
+    reach = np.cumprod(beta)                   # P(n_acc >= j), j = 1..k
+    mean = reach.sum()
+    var = sum((2 * j + 1) * reach[j] for j in range(k)) - mean ** 2
+    rng = np.random.default_rng(17)
+    drafts = np.stack([rng.choice(V, size=B * calls, p=Q[i] / Q[i].sum()) for i in range(k)],
+                      axis=1).astype(np.int32)
+    tgt = t1.to(DEV).expand(B, k + 1, V).contiguous()
+    dft = d1.to(DEV).expand(B, k, V).contiguous()
+    n = []
+    for c in range(calls):
+        tok = torch.from_numpy(drafts[c * B:(c + 1) * B]).to(DEV)
+        out = sv.sv_verify_accept(tgt, dft, tok, seed=11, offset=c)
+        n.append(out["n_acc"].cpu().numpy())
+    n = np.concatenate(n)
+    assert (n >= 0).all()
+    z = (n.mean() - mean) / np.sqrt(var / n.size)
+    print(f"sigma={sigma}: mean n_acc {n.mean():.4f} vs law {mean:.4f}, z = {z:.2f}")
+    assert abs(z) < 4, z
 
 
 def test_invalid_inputs_report_status():
@@ -157,8 +217,7 @@ def test_invalid_inputs_report_status():
     torch.cuda.synchronize()
     assert out["status"].cpu().tolist() == [1, 1, 2, 2, 2, 0]
     assert out["n_acc"].cpu().tolist()[:5] == [-1] * 5
-    res = oracle.verify_accept(tgt.numpy(), dft.numpy(), tok.numpy(), seed=3)
-    _compare(out, res, k)
+    _compare_full(out, tgt.numpy(), dft.numpy(), tok.numpy(), seed=3)
 
 
 def test_identical_distributions_accept_all_and_bonus():
@@ -168,8 +227,7 @@ def test_identical_distributions_accept_all_and_bonus():
     out = sv.sv_verify_accept(*to_dev(tgt, dft, tok), seed=1)
     torch.cuda.synchronize()
     assert np.all(out["n_acc"].cpu().numpy() == k)
-    res = oracle.verify_accept(tgt.numpy(), dft.numpy(), tok.numpy(), seed=1)
-    _compare(out, res, k)
+    _compare_full(out, tgt.numpy(), dft.numpy(), tok.numpy(), seed=1)
 
 
 def test_argument_errors():

@@ -222,3 +222,30 @@ def test_k1_reduces_to_single_position():
         assert res.n_acc in (0, 1) and res.n_out == res.n_acc + 1
         seen.add(res.n_acc)
     assert seen == {0, 1}
+
+
+def test_forced_decision_at_a_near_tie_continues_the_trial():
+    # position 0 is an exact tie: u q(d) = 1/2 * 1/2 = 1/4 = p(d), so the
+    # strict test rejects; forcing "accept" there must continue exactly as a
+    # trial whose u lies just below the tie (accepting naturally), and
+    # forcing "reject" must reproduce the unforced trial
+    from oracle import accept_on_probs
+    P = np.array([[0.25, 0.25, 0.25, 0.25], [0.375, 0.25, 0.25, 0.125],
+                  [0.125, 0.25, 0.25, 0.375], [0.25, 0.25, 0.25, 0.25]])
+    Q = np.array([[0.5, 0.125, 0.125, 0.25], [0.125, 0.25, 0.25, 0.375],
+                  [0.375, 0.25, 0.25, 0.125]])
+    toks = [0, 0, 3]
+    u = np.array([0.5, 0.3, 0.9, 0.0])
+    u2 = np.array([0.6, 0.2, 0.7, 0.4])
+    plain = accept_on_probs(P, Q, toks, u, u2)
+    assert plain.n_acc == 0 and plain.accept_flags[0]
+    forced_rej = accept_on_probs(P, Q, toks, u, u2, force={0: False})
+    assert (forced_rej.n_acc, forced_rej.tokens) == (plain.n_acc, plain.tokens)
+    forced_acc = accept_on_probs(P, Q, toks, u, u2, force={0: True})
+    below = accept_on_probs(P, Q, toks, np.array([0.5 - 1e-9, 0.3, 0.9, 0.0]), u2)
+    assert forced_acc.n_acc >= 1
+    assert (forced_acc.n_acc, forced_acc.tokens) == (below.n_acc, below.tokens)
+    assert forced_acc.tokens != plain.tokens
+    # a position whose decision is not a near tie cannot be forced
+    with pytest.raises(ValueError):
+        accept_on_probs(P, Q, toks, np.array([0.2, 0.3, 0.9, 0.0]), u2, force={0: False})
