@@ -165,10 +165,35 @@ constexpr float kBinsPerUnit = 32.f;
 constexpr int kCap = 2048;                      // tokens of one bin resolved in LDS
 constexpr int kPer = kBins / kThreads;          // bins (and candidate slots) per thread
 static_assert(kCap / kThreads == kPer, "one range size for bins and candidates");
+static_assert(kCap >= kBins, "the candidate arrays hold the fixed-point bins first");
 
 __device__ __forceinline__ int bin_of(float x, float mx) {
   const float d = (mx - x) * kBinsPerUnit;      // >= 0; +inf for x = -inf
   return d < static_cast<float>(kBins - 1) ? static_cast<int>(d) : kBins - 1;
+}
+
+// Masses in [0, 1] summed by many threads at once (histogram bins, radix
+// digits) go through 66-bit fixed point: m = (hi 2^33 + lo) 2^-66, both
+// chunks below 2^33 (hi = 2^33 only for m = 1), bits below 2^-66 dropped.
+// Chunk sums are integer additions, exact for up to 2^31 terms whatever
+// their order, so every run (and every interleaving of the atomics) yields
+// the same bin; one rounding turns a bin back into binary64.
+typedef unsigned long long u64;
+__device__ __forceinline__ void fx_split(double m, u64& hi, u64& lo) {
+  const double t = m * 0x1p33;                  // exact
+  const double h = floor(t);
+  hi = static_cast<u64>(h);
+  lo = static_cast<u64>((t - h) * 0x1p33);     // t - h and the scaling are exact
+}
+__device__ __forceinline__ double fx_value(u64 hi, u64 lo) {
+  // chunk sums stay below 2^53 for V < 2^20 (exact); beyond, one rounding each
+  return static_cast<double>(hi) * 0x1p-33 + static_cast<double>(lo) * 0x1p-66;
+}
+__device__ __forceinline__ void fx_add(u64* hi, u64* lo, double m) {
+  u64 h, l;
+  fx_split(m, h, l);
+  if (h) atomicAdd(hi, h);
+  if (l) atomicAdd(lo, l);
 }
 
 // f(x, v) for the n tokens at p (v counted from p); each thread visits its
@@ -405,14 +430,20 @@ __device__ void radix_select(const float* row, int V, float mx, float T, int top
     const double need = static_cast<double>(top_p) * s1;
     unsigned int prefix = 0u, pmask = 0u;
     double above = 0.0;
+    // digit masses in fixed point (dsh as 256 high then 256 low chunk sums)
+    u64* const dhi = reinterpret_cast<u64*>(dsh);
+    u64* const dlo = dhi + 256;
+    static_assert(kThreads == 512, "dsh holds the 2 x 256 digit chunk sums");
     for (int shift = 24; shift >= 0; shift -= 8) {
-      dsh[tid] = 0.0;
+      dhi[tid] = 0ull;                          // (dhi and dlo: 512 words)
       __syncthreads();
       for (int v = tid; v < V; v += kThreads) {
         const float x = row[v];
         const unsigned int key = order_key(x);
-        if ((key & pmask) == prefix && kept_by(key, v, tau, tie))
-          atomicAdd(&dsh[(key >> shift) & 255u], mass(x, mx, T));
+        if ((key & pmask) == prefix && kept_by(key, v, tau, tie)) {
+          const unsigned int d = (key >> shift) & 255u;
+          fx_add(dhi + d, dlo + d, mass(x, mx, T));
+        }
       }
       __syncthreads();
       if (tid == 0) {
@@ -421,7 +452,7 @@ __device__ void radix_select(const float* row, int V, float mx, float T, int top
         int pick = -1, last = -1;
         double run = above;
         for (int d = 255; d >= 0; --d) {
-          const double md = dsh[d];
+          const double md = fx_value(dhi[d], dlo[d]);
           if (md > 0.0) last = d;
           if (md > 0.0 && run + md >= need) {
             pick = d;
@@ -432,7 +463,7 @@ __device__ void radix_select(const float* row, int V, float mx, float T, int top
         if (pick < 0) {
           pick = last < 0 ? 0 : last;
           run = above;
-          for (int d = 255; d > pick; --d) run += dsh[d];
+          for (int d = 255; d > pick; --d) run += fx_value(dhi[d], dlo[d]);
         }
         ish[0] = pick;
         above_sh = run;                         // mass above the chosen digit
@@ -464,9 +495,8 @@ __device__ void radix_select(const float* row, int V, float mx, float T, int top
 // a full pass -- maximum, argmax, validity, then the bins (or the whole mass
 // when nothing truncates) -- are taken per slice by W workgroups per row.
 // Maxima and whole masses merge in slice order; each slice adds its nonzero
-// bins into the row's histogram with device atomics (counts exactly; the
-// binary64 masses in arrival order, which moves a bin's mass only in its last
-// bits, as the LDS atomics inside a workgroup already do).
+// bins into the row's histogram with device atomics on integers (counts and
+// the fixed-point mass chunks), exact in any order.
 struct SlicePart {
   float m;                          // slice maximum (-inf when empty)
   int am;                           // smallest index of it (V when empty)
@@ -476,7 +506,8 @@ struct SlicePart {
 static_assert(sizeof(SlicePart) == 16, "slice record layout");
 constexpr int kMaxSlices = 16;
 static_assert(kMaxSlices <= 64, "one slice record per lane");
-constexpr size_t kRowHistBytes = kBins * (sizeof(int) + sizeof(double));
+// per row: counts (int), then the high and the low mass chunk sums (u64)
+constexpr size_t kRowHistBytes = kBins * (sizeof(int) + 2 * sizeof(u64));
 
 __host__ __device__ inline int slice_len(int V, int W) { return ((V + W - 1) / W + 3) & ~3; }
 
@@ -528,7 +559,8 @@ __global__ __launch_bounds__(kThreads) void sampled_slice_max_kernel(
     char* h = hist + (static_cast<size_t>(b) * gridDim.y + rho) * kRowHistBytes;
     for (int j = w * kThreads + tid; j < kBins; j += W * kThreads) {
       reinterpret_cast<int*>(h)[j] = 0;
-      reinterpret_cast<double*>(h + kBins * sizeof(int))[j] = 0.0;
+      reinterpret_cast<u64*>(h + kBins * sizeof(int))[j] = 0ull;
+      reinterpret_cast<u64*>(h + kBins * sizeof(int))[kBins + j] = 0ull;
     }
   }
   float mx = -INFINITY;
@@ -575,7 +607,7 @@ __global__ __launch_bounds__(kThreads) void sampled_slice_bins_kernel(
     int trunc, const SlicePart* __restrict__ parts, double* __restrict__ slice_s,
     char* __restrict__ hist) {
   __shared__ int hcnt[kBins];
-  __shared__ double hmass[kBins];
+  __shared__ u64 hhi[kBins], hlo[kBins];
   __shared__ double dsh[kThreads];
   const int tid = threadIdx.x;
   const int w = blockIdx.x, rho = blockIdx.y, b = blockIdx.z;
@@ -598,23 +630,26 @@ __global__ __launch_bounds__(kThreads) void sampled_slice_bins_kernel(
   }
   for (int j = tid; j < kBins; j += kThreads) {
     hcnt[j] = 0;
-    hmass[j] = 0.0;
+    hhi[j] = 0ull;
+    hlo[j] = 0ull;
   }
   __syncthreads();
   scan_span(row, n, vec, [&](float x, int) {
     const int bn = bin_of(x, mx);
     atomicAdd(&hcnt[bn], 1);
-    atomicAdd(&hmass[bn], mass(x, mx, T));
+    fx_add(hhi + bn, hlo + bn, mass(x, mx, T));
   });
   __syncthreads();
   char* h = hist + rid * kRowHistBytes;
   int* gc = reinterpret_cast<int*>(h);
-  double* gm = reinterpret_cast<double*>(h + kBins * sizeof(int));
+  u64* ghi = reinterpret_cast<u64*>(h + kBins * sizeof(int));
+  u64* glo = ghi + kBins;
   for (int j = tid; j < kBins; j += kThreads) {
     const int c = hcnt[j];
     if (c != 0) {
       atomicAdd(&gc[j], c);
-      atomicAdd(&gm[j], hmass[j]);
+      if (hhi[j]) atomicAdd(&ghi[j], hhi[j]);
+      if (hlo[j]) atomicAdd(&glo[j], hlo[j]);
     }
   }
 }
@@ -709,21 +744,29 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
     // resolved exactly from its tokens, sorted in LDS.
     if (W > 1) {
       const char* h = hist + rid * kRowHistBytes;
+      const u64* ghi = reinterpret_cast<const u64*>(h + kBins * sizeof(int));
       for (int j = tid; j < kBins; j += kThreads) {
         hcnt[j] = reinterpret_cast<const int*>(h)[j];
-        hmass[j] = reinterpret_cast<const double*>(h + kBins * sizeof(int))[j];
+        hmass[j] = fx_value(ghi[j], ghi[kBins + j]);
       }
     } else {
+      // fixed-point chunk sums in the candidate arrays (free until the
+      // boundary bins are gathered), then one binary64 value per bin
+      u64* const hhi = reinterpret_cast<u64*>(cand);
+      u64* const hlo = reinterpret_cast<u64*>(cmass);
       for (int j = tid; j < kBins; j += kThreads) {
         hcnt[j] = 0;
-        hmass[j] = 0.0;
+        hhi[j] = 0ull;
+        hlo[j] = 0ull;
       }
       __syncthreads();
       scan_row(row, V, [&](float x, int) {
         const int bn = bin_of(x, mx);
         atomicAdd(&hcnt[bn], 1);
-        atomicAdd(&hmass[bn], mass(x, mx, T));
+        fx_add(hhi + bn, hlo + bn, mass(x, mx, T));
       });
+      __syncthreads();
+      for (int j = tid; j < kBins; j += kThreads) hmass[j] = fx_value(hhi[j], hlo[j]);
     }
     __syncthreads();
     bool exact = true;
