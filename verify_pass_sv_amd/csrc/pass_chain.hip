@@ -21,23 +21,25 @@
 // Work split (every link spans the whole grid, one workgroup per compute
 // unit): tile i (16 output channels) of a link belongs to workgroup i mod G.
 // A link with more than 6 G tiles runs as several rounds of at most 6 tiles
-// per workgroup.  Inside a workgroup the 8 stream waves split K: in each
-// window of 8 blocks of 128 k, wave j takes block j for every tile of the
-// round, so one activation operand (read once from LDS) feeds up to 6 tiles.
+// per workgroup.  Inside a workgroup the 8 stream waves split K: of the
+// blocks of 128 k, wave j takes blocks j, j + 8, j + 16, .. for every tile of
+// the round, so one activation operand (read once from LDS) feeds up to 6
+// tiles.
 // Partial sums of the 8 waves meet in LDS at the end of the round and are
 // added in a fixed order (deterministic results).
 //
 // Wave roles:
-//   * 8 stream waves: weight + scale/zero loads (a ring of 4 to 6 units of
-//     1 KiB per wave, its first units issued before the round's barrier is
-//     passed), dequantization, bf16 MFMAs, the per-group fold and zero-point
-//     correction, the reduction, and the y and xo stores.  A round's ring is
-//     consumed when it ends, so waiting for the xo stores there waits for
-//     nothing else.
-//   * 1 IO wave: activation windows into LDS (buffer -> LDS loads, all 128 KiB
-//     of window slots at once, then one window per freed slot) and the phase
-//     barrier (arrive, bounded poll).  Its vector-memory queue holds no weight
-//     loads.
+//   * 8 stream waves: each streams its own operands -- the weight units of
+//     its k-blocks (a register ring of 4 to 6 units of 1 KiB, its first units
+//     issued before the round's barrier is passed) and the activation blocks
+//     of the same k-blocks (buffer -> LDS loads into the wave's own ring of 4
+//     blocks of 4 KiB, 2 of 8 KiB at m > 16), then dequantization, bf16
+//     MFMAs, the per-group fold and zero-point correction, the reduction, and
+//     the y and xo stores.  A wave reads no other wave's blocks, so nothing
+//     synchronizes the waves inside a round, and each keeps its loads in
+//     flight up to the exact count the next step needs.
+//   * 1 IO wave: the phase barrier (arrive, bounded poll); its vector-memory
+//     queue holds only the poll loads.
 //
 // Phase barrier: 16 counters (64-bit, 4 KiB apart); workgroup w adds 1 to
 // counter w mod 16 after its part of a link that a waiting link follows, and
@@ -123,13 +125,13 @@ __host__ __device__ inline size_t chain_bytes(int nrounds) {
 
 template <int MT>
 struct ChainGeo {
-  static constexpr int S = MT == 1 ? 4 : 2;              // activation window slots (128 KiB)
-  static constexpr int ROWB = 2048;                      // 1024 k of bf16 per row
-  static constexpr int WINB = 16 * MT * ROWB;            // bytes per window
-  static constexpr int WLOADS = WINB / 1024;             // 1 KiB loads per window
-  static constexpr int TPOSE = S * WINB;                 // per-wave transposes
+  static constexpr int A = MT == 1 ? 4 : 2;              // activation blocks per wave ring
+  static constexpr int BLKB = 16 * MT * 256;             // bytes per block: 16 MT rows x 128 k
+  static constexpr int BLOADS = BLKB / 1024;             // 1 KiB loads per block
+  static constexpr int WAVEB = A * BLKB;                 // one wave's ring
+  static constexpr int TPOSE = kSW * WAVEB;              // per-wave transposes (128 KiB on)
   static constexpr int LDS = TPOSE + kSW * 1024;
-  static_assert(kSW * kTmax * MT * 1024 <= S * WINB, "reduction area fits the windows");
+  static_assert(kSW * kTmax * MT * 1024 <= kSW * WAVEB, "reduction area fits the rings");
   static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 workgroup");
 };
 
@@ -145,19 +147,18 @@ __device__ __forceinline__ T* uni(T* p) {
   return reinterpret_cast<T*>(lo | (hi << 32));
 }
 
+// 16 bytes per lane from a buffer into LDS (lane l -> lds + 16 l).  A plain
+// device function: the builtin called from a lambda inside a generic lambda
+// makes the host-side compile drop the kernel's launch stub.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, uint8_t* lds_dst,
+                                           unsigned int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (sv_lds_void*)lds_dst, 16, off, 0, 0, 0);
+}
+
 __device__ __forceinline__ unsigned int bf16_rne(float f) {
   const unsigned int u = __float_as_uint(f);
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;   // NaN stays NaN
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-// s_waitcnt vmcnt(n) with n clamped to the 6-bit field (a clamped wait is
-// only stricter).
-__device__ __forceinline__ void wait_vm_upto(int n) {
-  if (n >= 63) sv_wait_vmcnt<63>();
-  else if (n >= 32) sv_wait_vmcnt<32>();
-  else if (n >= 16) sv_wait_vmcnt<16>();
-  else sv_wait_vmcnt<0>();
 }
 
 template <int MT>
@@ -208,26 +209,19 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
                                            __HIP_MEMORY_SCOPE_AGENT);
       epoch = c / (static_cast<uint64_t>(nsig) * hdr->group_size[g]);
     }
-    int ws = 0;                                   // window steps so far (slot = ws % S)
     // The fields of the round, read one round ahead so their scalar loads
     // are not waited for when the round starts.
     struct Cur {
-      const void* x;
-      int K, ntiles, tile0, sig;
+      int sig;
       uint32_t flags;
     };
     auto fetch = [&](int ri) {
       const ChainRound& rd = rounds[ri < nrounds ? ri : nrounds - 1];
-      return Cur{uni(rd.x), uni(rd.K), uni(rd.ntiles), uni(rd.tile0), uni(rd.signal_index),
-                 static_cast<uint32_t>(uni(static_cast<int>(rd.flags)))};
+      return Cur{uni(rd.signal_index), static_cast<uint32_t>(uni(static_cast<int>(rd.flags)))};
     };
     Cur cur = fetch(0);
     for (int ri = 0; ri < nrounds; ++ri) {
       const Cur nxt = fetch(ri + 1);
-      const int tt = (cur.ntiles - wg + grid - 1) / grid;
-      const int T = tt < TM ? tt : TM;
-      const int K = cur.K;
-      const int W = (K / 128 + kSW - 1) / kSW;
       if (cur.flags & kFlagWait) {
         // every earlier link complete on every workgroup
         const int gi = lane < kNG ? lane : 0;
@@ -249,45 +243,13 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
         if (!ok) {
           if (lane == 0) atomicOr(status, SV_PASS_STATUS_TIMEOUT);
           abort_flag = 1;
-          sv_barrier_no_fence();                  // the stream waves wait at window 0
+          sv_barrier_no_fence();                  // B0: the stream waves see the abort
           sv_wait_vmcnt<0>();
           return;
         }
       }
-      const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<void*>(cur.x), 0, m * K * 2, 0x00020000);
-      // Window w: rows 0 .. 16 MT - 1, k in [1024 w, 1024 w + 1024).  Load L
-      // covers half a row (64 columns of 16 bytes); LDS position c of row r
-      // holds global column c ^ (r % 16), so the 16 rows of an MFMA operand
-      // read 16 different bank groups.
-      auto issue_window = [&](int w) {
-        uint8_t* const base = lds + ((ws + w) % G::S) * G::WINB;
-#pragma unroll 4
-        for (int L = 0; L < G::WLOADS; ++L) {
-          const int r = L >> 1;
-          const int c = ((L & 1) << 6) + lane;
-          const int k = w * 1024 + 8 * (c ^ (r & 15));
-          const unsigned int off =
-              r < m && k < K ? static_cast<unsigned int>((r * K + k) * 2) : kSvOutOfRange;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              xrs, (sv_lds_void*)(base + r * G::ROWB + (L & 1) * 1024), 16, off, 0, 0, 0);
-        }
-      };
-      if (T > 0) {
-        // LA windows in flight: window w + LA goes out once barrier A(w) has
-        // freed the slot of window w - 1 (S >= LA + 2 slots hold w - 1 .. w + LA)
-        constexpr int LA = G::S >= 4 ? 2 : 1;
-        for (int w = 0; w < LA && w < W; ++w) issue_window(w);
-        for (int w = 0; w < W; ++w) {
-          // windows issued after w: w + 1 .. min(w + LA - 1, W - 1)
-          const int after = (w + LA - 1 < W - 1 ? w + LA - 1 : W - 1) - w;
-          wait_vm_upto(after * G::WLOADS);
-          sv_barrier_no_fence();                  // A: window w is in its slot
-          if (w + LA < W) issue_window(w + LA);
-        }
-        ws += W;
-      }
-      sv_barrier_no_fence();                      // E1: partial sums may overwrite the windows
+      sv_barrier_no_fence();                      // B0: the round's inputs are complete
+      sv_barrier_no_fence();                      // E1: partial sums may overwrite the blocks
       sv_barrier_no_fence();                      // E2: partial sums written
       sv_barrier_no_fence();                      // E3: every stream wave's xo stores complete
       if (cur.flags & kFlagSignal) {
@@ -312,22 +274,28 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
 #pragma unroll
     for (int a = 0; a < MT; ++a) yacc[i][a] = fz;
 
-  int ws = 0;                                     // window steps so far (slot = ws % S)
   float* const tpose = reinterpret_cast<float*>(lds + G::TPOSE) + wave * 256;
+  uint8_t* const act = lds + wave * G::WAVEB;     // this wave's activation block ring
 
-  // One round of T tiles, its weights in a ring of P windows x T units held
-  // in registers (wb[p][i]: 1 KiB of codes, szr[p][i]: the lane's 8 bytes of
-  // the scale/zero record).  Every index is static and every unit computed
-  // issues the loads of the unit P T places later (out of range past the
-  // round's last window), so the wait before a unit is exact: the P T - 1
-  // units issued after it may still be in flight.  The ring starts when the round does, before its
-  // barrier is passed: the weights do not depend on earlier links, and P T
-  // units (4 to 6 KiB per wave) are what the stream needs in flight without
-  // queueing the round's activation loads behind them.
+  // One round of T tiles.  Step w of a wave covers its k-block b = 8 w +
+  // wave for every tile of the round: the activation block (16 MT rows x 128
+  // k, bf16) comes into the wave's own LDS ring of A blocks, the weight units
+  // (tile i, block b) into a register ring of P steps x T units (wb[p][i]:
+  // 1 KiB of codes, szr[p][i]: the lane's 8 bytes of the scale/zero record).
+  // Issue order: the weights of steps 0 .. P-1 when the round starts (they do
+  // not depend on earlier links, so they stream while the barrier is polled),
+  // the activation blocks of steps 0 .. A-1 once the barrier is passed, then
+  // per step w: after unit (w, i) the unit (w + P, i), after the last unit
+  // the activation block of step w + A (out of range past the round's last
+  // step).  The number of loads issued after those a step needs is then the
+  // same at every step (one value for the first max(A, P) steps, one after),
+  // so the wait before a step is exact.  No step synchronizes the waves: each
+  // reads only its own blocks.
   // The fields of a round in scalar registers, read one round ahead.
   struct Info {
     const uint8_t* codes;
     const void* sz;
+    const void* x;
     float* y;
     void* xo;
     float alpha;
@@ -335,7 +303,7 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
   };
   auto fetch = [&](int ri) {
     const ChainRound& rd = rounds[ri < nrounds ? ri : nrounds - 1];
-    return Info{uni(rd.codes), uni(rd.sz), uni(rd.y), uni(rd.xo),
+    return Info{uni(rd.codes), uni(rd.sz), uni(rd.x), uni(rd.y), uni(rd.xo),
                 __int_as_float(uni(__float_as_int(rd.alpha))), uni(rd.K), uni(rd.N),
                 uni(rd.xo_cols), uni(rd.tile0), uni(rd.ntiles)};
   };
@@ -343,6 +311,15 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
   auto run_round = [&](auto tc, auto pc, const Info& rd) {
     constexpr int T = decltype(tc)::value;
     constexpr int P = decltype(pc)::value;
+    constexpr int A = G::A;
+    constexpr int AL = G::BLOADS;                 // loads per activation block
+    // loads a step may leave in flight: see the issue order above
+    constexpr int kAfterW = AL + (P - 1) * (2 * T + AL);
+    constexpr int kAfterA = (A - 1) * (2 * T + AL);
+    constexpr int kWaitSteady = kAfterW < kAfterA ? kAfterW : kAfterA;
+    constexpr int kWaitEarly = kAfterW < AL * (A - 1) ? kAfterW : AL * (A - 1);
+    constexpr int kEarly = A > P ? A : P;
+    static_assert(kWaitSteady <= 63 && kWaitEarly <= kWaitSteady, "vmcnt field");
     const int K = rd.K, N = rd.N;
     const int KB = K / 128;
     const int W = (KB + kSW - 1) / kSW;
@@ -352,6 +329,8 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
         const_cast<uint8_t*>(rd.codes), 0, N * (K / 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(rd.sz), 0, N * (K / 64) * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(rd.x), 0, m * K * 2, 0x00020000);
     sv_u32x4 wb[P][T];
     sv_u32x2 szr[P][T];
     // unit (w, i) -> ring slot [w % P][i]
@@ -364,36 +343,67 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
       szr[p][i] = __builtin_amdgcn_raw_buffer_load_b64(srs, ok ? col * 8 : kSvOutOfRange,
                                                        blk * 128, kStreamC);
     };
+    // activation block of step w -> ring slot w % A.  Load L brings rows
+    // 4 L .. 4 L + 3 (lane l: row 4 L + l / 16, LDS column l % 16, which
+    // holds global column (l % 16) ^ (row % 16), so the 16 rows of an MFMA
+    // operand read 16 different bank groups)
+    // (row 4 L + l / 16 has row % 16 = 4 (L % 4) + l / 16, whose XOR with the
+    // LDS column is xl ^ 4 (L % 4) for xl = (l % 16) ^ (l / 16))
+    const int lrow = lane >> 4;
+    const int lx16 = 16 * ((lane & 15) ^ lrow);
+    const int lbase = lrow * K * 2;
+    // (the loads are issued on every path, the offsets chosen by per-lane
+    // selects: a load under a branch would leave the compiler's own count of
+    // the loads in flight short, and its waits stricter than these)
+    auto issue_act = [&](const int w) {
+      const int b = w * kSW + wave;
+      const int lim = uni(w < W && b < KB ? m : 0);   // rows to load (0: none)
+      uint8_t* const dst = act + (w % A) * G::BLKB;
+      const int ub = uni(256 * b);
+      unsigned int o[AL];
+#pragma unroll
+      for (int L = 0; L < AL; ++L) {
+        const int off = lbase + (lx16 ^ (64 * (L & 3))) + (ub + L * 8 * K);
+        o[L] = lrow + 4 * L < lim ? static_cast<unsigned int>(off) : kSvOutOfRange;
+      }
+      sv_compiler_fence();
+#pragma unroll
+      for (int L = 0; L < AL; ++L)
+        lds_load16(xrs, dst + L * 1024, o[L]);
+    };
 #pragma unroll
     for (int p = 0; p < P; ++p)
 #pragma unroll
       for (int i = 0; i < T; ++i) issue(p, i, p);
+    sv_barrier_no_fence();                        // B0: the round's inputs are complete
+    if (abort_flag) return false;
+    sv_compiler_fence();
+#pragma unroll
+    for (int a = 0; a < A; ++a) issue_act(a);
+    sv_compiler_fence();
     for (int w0 = 0; w0 < W; w0 += P) {
 #pragma unroll
       for (int p = 0; p < P; ++p) {
-        // Every step issues its P T loads, also past the round's last window
-        // (out of range), so that every path through the loop keeps the same
+        // Every step issues its loads, also past the round's last step (out
+        // of range), so that every path through the loop keeps the same
         // loads in flight and the compiler's own waits stay as exact as ours.
         const int w = w0 + p;
-        const bool live = w < W;                  // wave-uniform
         const int b = w * kSW + wave;
-        const bool valid = live && b < KB;        // wave-uniform
+        const bool valid = w < W && b < KB;       // wave-uniform
+        if (w < kEarly) sv_wait_vmcnt<kWaitEarly>();
+        else sv_wait_vmcnt<kWaitSteady>();
         {
-          if (live) {
-            sv_barrier_no_fence();                // A: window w landed (or abort)
-            if (abort_flag) return false;
-          }
-          const uint8_t* const win = lds + ((ws + w) % G::S) * G::WINB;
+          const uint8_t* const blk = act + (w % A) * G::BLKB;
           // activation operands of block b: row tile a, group h, two 32-k slices
           sv_u32x4 a0[2][MT], a1[2][MT];
           float xsA[MT];
           if (valid) {
 #pragma unroll
             for (int a = 0; a < MT; ++a) {
-              const uint8_t* rp = win + (16 * a + col) * G::ROWB;
+              const uint8_t* rp = blk + (16 * a + col) * 256;
 #pragma unroll
               for (int h = 0; h < 2; ++h) {
-                const int c0 = 16 * wave + 8 * h + 2 * q;   // 16-byte column in the window row
+                const int c0 = 8 * h + 2 * q;     // 16-byte column in the block row
                 a0[h][a] = *reinterpret_cast<const sv_u32x4*>(rp + ((c0 ^ col) << 4));
                 a1[h][a] = *reinterpret_cast<const sv_u32x4*>(rp + (((c0 + 1) ^ col) << 4));
               }
@@ -412,8 +422,6 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
           }
 #pragma unroll
           for (int i = 0; i < T; ++i) {
-            // unit (w, i) has landed: the P T - 1 units issued after it may not
-            sv_wait_vmcnt<2 * (P * T - 1)>();
             if (valid) {
               const sv_u32x4 wv = wb[p][i];
               const sv_u32x2 sv = szr[p][i];
@@ -448,9 +456,13 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
             sv_compiler_fence();
           }
         }
+        // the block's operands are in registers (the MFMAs above used them):
+        // its slot takes the block of step w + A
+        sv_compiler_fence();
+        issue_act(w + A);
+        sv_compiler_fence();
       }
     }
-    ws += W;
     return true;
   };
 
@@ -469,19 +481,28 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
       case 2: go = run_round(std::integral_constant<int, 2>{}, std::integral_constant<int, P2>{}, rd); break;
       case 3: go = run_round(std::integral_constant<int, 3>{}, std::integral_constant<int, P3>{}, rd); break;
       case 4: go = run_round(std::integral_constant<int, 4>{}, std::integral_constant<int, 1>{}, rd); break;
-      default:
+      case 5:
+      case 6:
         if constexpr (TM >= 6) {
           if (T == 5) go = run_round(std::integral_constant<int, 5>{}, std::integral_constant<int, 1>{}, rd);
-          else if (T == 6) go = run_round(std::integral_constant<int, 6>{}, std::integral_constant<int, 1>{}, rd);
+          else go = run_round(std::integral_constant<int, 6>{}, std::integral_constant<int, 1>{}, rd);
         }
+        break;
+      default:                                    // no tile of this round here
+        sv_barrier_no_fence();                    // B0
+        go = !abort_flag;
         break;
     }
     if (!go) {
       sv_wait_vmcnt<0>();
       return;
     }
+    // every activation load of the round has landed (the tail's out-of-range
+    // ones included) before the partial sums overwrite the blocks
+    sv_wait_vmcnt<0>();
+
     // ---- end of the round: fixed-order sum of the 8 waves' partial sums ----
-    sv_barrier_no_fence();                        // E1: every wave done with the windows
+    sv_barrier_no_fence();                        // E1: every wave done with its blocks
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if (i < T) {
@@ -539,9 +560,9 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
       }
     }
     // The hand-off is complete at agent scope before the IO wave arrives.
-    // No weight load of this wave is in flight here (the round's ring is
-    // consumed; the next round's starts after E3), so this waits only for the
-    // stores and the round's out-of-range tail loads.
+    // No load of this wave is in flight here (the round's rings are consumed
+    // and drained before E1; the next round's start after E3), so this waits
+    // only for the stores.
     sv_wait_vmcnt<0>();
     sv_barrier_no_fence();                        // E3
     rd = nxt;
