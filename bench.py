@@ -21,7 +21,7 @@ HBM read peak, a warm-up curve, and the CPU oracle baseline.
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 200] [--quick]
        python bench.py --profile-pass [--format w4|w4_unordered|w8|w4_i8] [--k K]
-                        (copy kernel, read probe and two executor passes, for
+                        (copy kernel, read probe and eight executor passes, for
                          rocprofv3 counters)
        python bench.py --profile-accept [--k K] [--trials B]
                         (copy kernel and accept calls at V = 152000, for
@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 
 METRIC = ("verify-pass weight GB/s and drafted tokens/s at k=16, 9B-shape W4; accept µs")
 WARMUP_CURVE_STEPS = 20
+PROFILE_PASSES = 8
 
 
 def handoff_alpha(K):
@@ -323,7 +324,7 @@ def main():
                     help="weight path of --profile-pass (w4: the pass in model order; the "
                          "others: every GEMM on a fixed input, no ordering)")
     ap.add_argument("--profile-pass", action="store_true",
-                    help="copy kernel + read probe + 2 eager W4 passes, then exit")
+                    help="copy kernel + read probe + 8 eager passes, then exit")
     ap.add_argument("--profile-accept", action="store_true",
                     help="copy kernel + eager sv_verify_accept calls (V=152000), then exit")
     ap.add_argument("--trials", type=int, default=1,
@@ -471,7 +472,8 @@ def main():
                                y_own[li][gi][:k]))
                     del c
             p = sv.sv_pass_plan("w8", g8)
-        for _ in range(2):
+        # several passes, so the trace's average is dominated by warm launches
+        for _ in range(PROFILE_PASSES):
             sv.sv_pass_run(p)
         torch.cuda.synchronize()
         assert sv.sv_pass_status(p) == 0
