@@ -21,7 +21,7 @@ HBM read peak, a warm-up curve, and the CPU oracle baseline.
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 200] [--quick]
        python bench.py --profile-pass [--format w4|w4_unordered|w8|w4_i8] [--k K]
-                        (copy kernel, read probe and eight executor passes, for
+                        (copy kernel, read probe and 40 executor passes, for
                          rocprofv3 counters)
        python bench.py --profile-accept [--k K] [--trials B]
                         (copy kernel and accept calls at V = 152000, for
@@ -39,7 +39,7 @@ if ROOT not in sys.path:
 
 METRIC = ("verify-pass weight GB/s and drafted tokens/s at k=16, 9B-shape W4; accept µs")
 WARMUP_CURVE_STEPS = 20
-PROFILE_PASSES = 8
+PROFILE_PASSES = 40
 
 
 def handoff_alpha(K):
@@ -324,7 +324,7 @@ def main():
                     help="weight path of --profile-pass (w4: the pass in model order; the "
                          "others: every GEMM on a fixed input, no ordering)")
     ap.add_argument("--profile-pass", action="store_true",
-                    help="copy kernel + read probe + 8 eager passes, then exit")
+                    help="copy kernel + read probe + 40 eager passes, then exit")
     ap.add_argument("--profile-accept", action="store_true",
                     help="copy kernel + eager sv_verify_accept calls (V=152000), then exit")
     ap.add_argument("--trials", type=int, default=1,
@@ -604,18 +604,22 @@ def main():
         extra["w4_k_sweep_unordered"] = sweep_u
         extra["w4_latency_ratio_k32_over_k1_unordered"] = round(
             sweep_u[32]["pass_ms"] / sweep_u[1]["pass_ms"], 3)
-        # MFMA utilisation of the W4 pass at k = 16 and 32: the useful flops
-        # (2 k per weight) over the measured pass time against the dense bf16
-        # peak, and from the recorded counters the fraction of cycles the
-        # MFMA pipe was busy (SQ_VALU_MFMA_BUSY_CYCLES per SIMD over the
-        # active cycles GRBM_GUI_ACTIVE per XCD) with the clock they imply
+        # MFMA utilisation of the unordered W4 executor at k = 1, 16 and 32
+        # (the kernel whose counters are recorded): the useful flops (2 k per
+        # weight) over its measured pass time against the dense bf16 peak,
+        # and from the recorded counters the fraction of cycles the MFMA pipe
+        # was busy (SQ_VALU_MFMA_BUSY_CYCLES per SIMD over the active cycles
+        # GRBM_GUI_ACTIVE per XCD) with the clock they imply.  At k = 1 the
+        # pass streams at the read probe's rate, so the MFMA form costs the
+        # small-k case nothing a vector form could win back.
         n_weights = sum(N * K for layer in w4 for (_, N, K, *_r) in layer)
         n_simd = 4 * torch.cuda.get_device_properties(0).multi_processor_count
-        mfma = {}
-        for kk in (16, 32):
-            tf = 2.0 * kk * n_weights / (sweep[kk]["pass_ms"] * 1e-3) / 1e12
+        mfma = {"kernel": "pass_kernel<W4> (unordered)"}
+        for kk in (1, 16, 32):
+            tf = 2.0 * kk * n_weights / (sweep_u[kk]["pass_ms"] * 1e-3) / 1e12
             row = {"useful_TFLOPs": round(tf, 1),
-                   "frac_of_bf16_dense_peak": round(tf / BF16_DENSE_PEAK_TFLOPS, 4)}
+                   "frac_of_bf16_dense_peak": round(tf / BF16_DENSE_PEAK_TFLOPS, 4),
+                   "GBps": sweep_u[kk]["GBps"]}
             rec = recorded_counters(f"w4_pass_9b_k{kk}")
             if rec:
                 c = rec["counters"]
