@@ -32,8 +32,8 @@
 //   * 8 stream waves: each streams its own operands -- the weight units of
 //     its k-blocks (a register ring of 4 to 6 units of 1 KiB, its first units
 //     issued before the round's barrier is passed) and the activation blocks
-//     of the same k-blocks (buffer -> LDS loads into the wave's own ring of 4
-//     blocks of 4 KiB, 2 of 8 KiB at m > 16), then dequantization, bf16
+//     of the same k-blocks (buffer -> LDS loads into the wave's own ring of 2
+//     blocks of 4 KiB, 8 KiB at m > 16), then dequantization, bf16
 //     MFMAs, the per-group fold and zero-point correction, the reduction, and
 //     the y and xo stores.  A wave reads no other wave's blocks, so nothing
 //     synchronizes the waves inside a round, and each keeps its loads in
@@ -125,11 +125,11 @@ __host__ __device__ inline size_t chain_bytes(int nrounds) {
 
 template <int MT>
 struct ChainGeo {
-  static constexpr int A = MT == 1 ? 4 : 2;              // activation blocks per wave ring
+  static constexpr int A = 2;                            // activation blocks per wave ring
   static constexpr int BLKB = 16 * MT * 256;             // bytes per block: 16 MT rows x 128 k
   static constexpr int BLOADS = BLKB / 1024;             // 1 KiB loads per block
   static constexpr int WAVEB = A * BLKB;                 // one wave's ring
-  static constexpr int TPOSE = kSW * WAVEB;              // per-wave transposes (128 KiB on)
+  static constexpr int TPOSE = kSW * WAVEB;              // per-wave transposes (after the rings)
   static constexpr int LDS = TPOSE + kSW * 1024;
   static_assert(kSW * kTmax * MT * 1024 <= kSW * WAVEB, "reduction area fits the rings");
   static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 workgroup");
@@ -471,11 +471,11 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
     const Info nxt = fetch(ri + 1);
     const int tt = (rd.ntiles - wg + grid - 1) / grid;
     const int T = tt < TM ? tt : TM;
-    // ring depth P T: 4 to 6 units of 1 KiB per wave
+    // ring depth P T: 4 to 6 units of 1 KiB per wave (measured: deeper
+    // rings queue the activation loads behind more weight loads and run
+    // slower; at m > 16 the same depths fit the registers)
     bool go = true;
-    // (m > 16: two row tiles double the activation operands and accumulators;
-    // the ring keeps to 2 to 4 units so the registers hold)
-    constexpr int P1 = MT == 1 ? 4 : 2, P2 = MT == 1 ? 2 : 1, P3 = MT == 1 ? 2 : 1;
+    constexpr int P1 = 4, P2 = 2, P3 = 2;
     switch (T) {
       case 1: go = run_round(std::integral_constant<int, 1>{}, std::integral_constant<int, P1>{}, rd); break;
       case 2: go = run_round(std::integral_constant<int, 2>{}, std::integral_constant<int, P2>{}, rd); break;
