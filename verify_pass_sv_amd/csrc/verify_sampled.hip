@@ -163,6 +163,7 @@ __device__ int ordered_tie(const float* row, int V, unsigned int tau, int want,
 constexpr int kBins = 2048;
 constexpr float kBinsPerUnit = 32.f;
 constexpr int kCap = 2048;                      // tokens of one bin resolved in LDS
+constexpr int kPeek = 4096;                     // entries that set a row's provisional maximum
 constexpr int kPer = kBins / kThreads;          // bins (and candidate slots) per thread
 static_assert(kCap / kThreads == kPer, "one range size for bins and candidates");
 static_assert(kCap >= kBins, "the candidate arrays hold the fixed-point bins first");
@@ -679,42 +680,97 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
 
   // maximum, argmax (smallest index among equal maxima), validity
   const size_t rid = static_cast<size_t>(b) * R + rho;
+  const float T = temperature;
+  const bool trunc_k = top_k > 0 && top_k < V;
+  const bool trunc_p = top_p < 1.f;
+  const bool trunc = trunc_k || trunc_p;
   float mx = -INFINITY;
   int am = V;
   int bad = 0;
+  // Masses exp((l - mref) / T) are taken against a reference mref >= every
+  // logit of the row; the kept probabilities, ratios of such masses, do not
+  // depend on which.  With one workgroup per row, mref is the maximum of the
+  // row's first kPeek entries raised by min(4, 8 T), and the maximum, the
+  // validity, and the bins (or the whole mass) come out of one pass; should
+  // a logit exceed mref after all, mref becomes the row maximum and the bins
+  // (or the mass) take a second pass.  (The fixed-point bin masses resolve
+  // 2^-66 of mref's scale, at most e^8 of the maximum's.)
+  float mref = -INFINITY;
+  bool fused = false;
+  double s_fused = 0.0;
+  u64* const hhi = reinterpret_cast<u64*>(cand);  // fixed-point bins (one pass)
+  u64* const hlo = reinterpret_cast<u64*>(cmass);
   if (W > 1) {
     merge_slices(parts + rid * W, W, mx, am, bad);
+    mref = mx;
   } else {
+    float m0 = -INFINITY;
+    for (int v = tid; v < min(V, kPeek); v += kThreads) m0 = fmaxf(m0, row[v]);
+    dsh[tid] = m0;
+    __syncthreads();
+    for (int w = kThreads / 2; w > 0; w >>= 1) {
+      if (tid < w) dsh[tid] = fmax(dsh[tid], dsh[tid + w]);
+      __syncthreads();
+    }
+    m0 = static_cast<float>(dsh[0]);
+    __syncthreads();
+    fused = m0 > -INFINITY && m0 < INFINITY;
+    const float ref = fused ? m0 + fminf(4.f, 8.f * T) : INFINITY;
+    if (fused && trunc) {
+      for (int j = tid; j < kBins; j += kThreads) {
+        hcnt[j] = 0;
+        hhi[j] = 0ull;
+        hlo[j] = 0ull;
+      }
+      __syncthreads();
+    }
+    int over = 0;
+    double sl = 0.0;
     scan_row(row, V, [&](float x, int v) {
       bad |= (x != x) | (x == INFINITY);
       if (x > mx || (x == mx && v < am)) {
         mx = x;
         am = v;
       }
+      if (fused) {
+        if (x > ref) {
+          over = 1;
+        } else if (trunc) {
+          const int bn = bin_of(x, ref);
+          atomicAdd(&hcnt[bn], 1);
+          fx_add(hhi + bn, hlo + bn, mass(x, ref, T));
+        } else {
+          sl += mass(x, ref, T);
+        }
+      }
     });
-    // (the maxima go through dsh, the indices through hcnt, both free here)
+    // (the maxima go through dsh, the indices through hmass, free here)
+    int* const ash = reinterpret_cast<int*>(hmass);
     dsh[tid] = mx;
-    hcnt[tid] = am;
-    ish[tid] = bad;
+    ash[tid] = am;
+    ish[tid] = bad | (over << 1);
     __syncthreads();
     for (int w = kThreads / 2; w > 0; w >>= 1) {
       if (tid < w) {
         const double o = dsh[tid + w];
-        const int oa = hcnt[tid + w];
-        if (o > dsh[tid] || (o == dsh[tid] && oa < hcnt[tid])) {
+        const int oa = ash[tid + w];
+        if (o > dsh[tid] || (o == dsh[tid] && oa < ash[tid])) {
           dsh[tid] = o;
-          hcnt[tid] = oa;
+          ash[tid] = oa;
         }
         ish[tid] |= ish[tid + w];
       }
       __syncthreads();
     }
     mx = static_cast<float>(dsh[0]);
-    am = hcnt[0];
-    bad = ish[0] | (mx == -INFINITY);
+    am = ash[0];
+    bad = (ish[0] & 1) | (mx == -INFINITY);
+    fused = fused && !(ish[0] & 2);
     __syncthreads();
+    if (fused && !trunc) s_fused = block_sum(sl, dsh);
+    mref = fused ? ref : mx;
   }
-  out.m = mx;
+  out.m = mref;
   out.argmax = am;
   out.status = bad ? 2 : 0;
   out.tau = 0u;                                 // every non-NaN key exceeds 0
@@ -724,24 +780,23 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
     if (tid == 0) rows[static_cast<size_t>(b) * R + rho] = out;
     return;
   }
-  const float T = temperature;
   unsigned int tau = 0u;
   int tie = -1;
 
-  const bool trunc_k = top_k > 0 && top_k < V;
-  const bool trunc_p = top_p < 1.f;
   double s = 0.0;                               // kept mass
-  if (!trunc_k && !trunc_p) {
+  if (!trunc) {
     if (W > 1) {
       for (int w = 0; w < W; ++w) s += slice_s[rid * W + w];
+    } else if (fused) {
+      s = s_fused;
     } else {
-      scan_row(row, V, [&](float x, int) { s += mass(x, mx, T); });
+      scan_row(row, V, [&](float x, int) { s += mass(x, mref, T); });
       s = block_sum(s, dsh);
     }
   } else {
-    // Bins of 1/32 logit below the maximum (monotone in the logit): counts
-    // and binary64 masses.  The boundary bin of each truncation is then
-    // resolved exactly from its tokens, sorted in LDS.
+    // Bins of 1/32 logit below mref (monotone in the logit): counts and
+    // binary64 masses.  The boundary bin of each truncation is then resolved
+    // exactly from its tokens, sorted in LDS.
     if (W > 1) {
       const char* h = hist + rid * kRowHistBytes;
       const u64* ghi = reinterpret_cast<const u64*>(h + kBins * sizeof(int));
@@ -752,20 +807,20 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
     } else {
       // fixed-point chunk sums in the candidate arrays (free until the
       // boundary bins are gathered), then one binary64 value per bin
-      u64* const hhi = reinterpret_cast<u64*>(cand);
-      u64* const hlo = reinterpret_cast<u64*>(cmass);
-      for (int j = tid; j < kBins; j += kThreads) {
-        hcnt[j] = 0;
-        hhi[j] = 0ull;
-        hlo[j] = 0ull;
+      if (!fused) {
+        for (int j = tid; j < kBins; j += kThreads) {
+          hcnt[j] = 0;
+          hhi[j] = 0ull;
+          hlo[j] = 0ull;
+        }
+        __syncthreads();
+        scan_row(row, V, [&](float x, int) {
+          const int bn = bin_of(x, mref);
+          atomicAdd(&hcnt[bn], 1);
+          fx_add(hhi + bn, hlo + bn, mass(x, mref, T));
+        });
+        __syncthreads();
       }
-      __syncthreads();
-      scan_row(row, V, [&](float x, int) {
-        const int bn = bin_of(x, mx);
-        atomicAdd(&hcnt[bn], 1);
-        fx_add(hhi + bn, hlo + bn, mass(x, mx, T));
-      });
-      __syncthreads();
       for (int j = tid; j < kBins; j += kThreads) hmass[j] = fx_value(hhi[j], hlo[j]);
     }
     __syncthreads();
@@ -776,7 +831,7 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
       int above = 0;
       bk = bins_cross_count(hcnt, top_k, above, ish);
       rk = top_k - above;
-      exact = bk < kBins && gather_bin(row, V, mx, T, bk, cand, cmass, ish) >= rk;
+      exact = bk < kBins && gather_bin(row, V, mref, T, bk, cand, cmass, ish) >= rk;
       if (exact) {
         tau = static_cast<unsigned int>(cand[rk - 1] >> 32);
         tie = static_cast<int>(~static_cast<unsigned int>(cand[rk - 1]));
@@ -792,7 +847,7 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
       const int bp = cross_mass(hmass, bk, need, above, dsh, ish);
       int n = 0;
       if (bp < bk) {
-        n = gather_bin(row, V, mx, T, bp, cand, cmass, ish);
+        n = gather_bin(row, V, mref, T, bp, cand, cmass, ish);
       } else if (trunc_k) {
         n = rk;                                 // inside the top-k boundary bin, still sorted
       }
@@ -809,10 +864,10 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
     if (!exact) {
       tau = 0u;
       tie = -1;
-      radix_select(row, V, mx, T, top_k, top_p, tau, tie, dsh, above_sh, ish);
+      radix_select(row, V, mref, T, top_k, top_p, tau, tie, dsh, above_sh, ish);
       s = 0.0;
       scan_row(row, V, [&](float x, int v) {
-        if (kept_by(order_key(x), v, tau, tie)) s += mass(x, mx, T);
+        if (kept_by(order_key(x), v, tau, tie)) s += mass(x, mref, T);
       });
       s = block_sum(s, dsh);
     }
@@ -826,7 +881,7 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
     double pd = 0.0;
     if (tok >= 0 && tok < V) {
       const float x = row[tok];
-      pd = kept_by(order_key(x), tok, tau, tie) ? mass(x, mx, T) / s : 0.0;
+      pd = kept_by(order_key(x), tok, tau, tie) ? mass(x, mref, T) / s : 0.0;
     }
     out.pd = pd;
     rows[static_cast<size_t>(b) * R + rho] = out;
