@@ -21,12 +21,17 @@
 //             It describes the kept set by a key threshold and a
 //             tie cut: token v is kept iff key(l_v) > tau, or key(l_v) == tau
 //             and v <= tie, where key() maps binary32 order to unsigned order.
-//             One pass bins the row below its maximum (1/32 logit, counts and
-//             binary64 masses); the boundary bin of top-k (count) and of top-p
-//             (mass, on the renormalised top-k row) is resolved exactly from
-//             its tokens, gathered and sorted in LDS (logit down, index up).
-//             A boundary bin larger than the LDS list falls back to radix
-//             passes over the whole row.  Then the kept mass S and the kept
+//             One pass reads the row once against a provisional reference
+//             (the maximum of its first entries, raised) and bins it (1/32
+//             logit): counts for top-k, counts and binary64 masses for top-p
+//             alone, the whole mass without truncation.  The top_k largest
+//             tokens are sorted in LDS -- from a list the pass keeps of the
+//             tokens above a bin predicted from the row's first entries, else
+//             gathered by a second read -- and top-p on the renormalised
+//             top-k row is resolved on their masses; top-p alone resolves its
+//             boundary bin from its tokens, gathered and sorted in LDS.  A
+//             boundary larger than the LDS list falls back to radix passes
+//             over the whole row.  Then the kept mass S and the kept
 //             probability of the row's draft token.  Masses are
 //             exp((l - m) / T) in binary64 throughout.
 //  2. decide  one workgroup per trial: the accept scan on the kept
@@ -79,14 +84,49 @@ __device__ __forceinline__ float key_value(unsigned int key) {
 __device__ __forceinline__ bool kept_by(unsigned int key, int v, unsigned int tau, int tie) {
   return key > tau || (key == tau && v <= tie);
 }
-// Unnormalised probability exp((x - m) / T) in binary64: the difference of two
-// binary32 values is exact there, so the masses that place the top-p
-// boundary and the probabilities of the accept test carry binary64 accuracy
-// (the product with the binary64 reciprocal of T adds one rounding).
-__device__ __forceinline__ double mass(float x, float m, float T) {
-  return exp((static_cast<double>(x) - static_cast<double>(m)) *
-             (1.0 / static_cast<double>(T)));
+// Unnormalised probability exp((x - m) / T), x <= m, in binary64, as
+// 2^(y / 64) with y = 64 log2(e) (x - m) / T.  With n = rint(y), f = y - n
+// (|f| <= 1/2, exact) and n = 64 i + j (0 <= j < 64):
+//   2^(y / 64) = 2^i * 2^(j / 64) * e^(f ln2 / 64),
+// the middle factor from a 64-entry table in LDS, the last one from its
+// Taylor polynomial of degree 5 (|f ln2 / 64| <= 0.0055, remainder below
+// 4e-17).  The difference of two binary32 values is exact in binary64; the
+// product with the binary64 constant adds one rounding (an error of |y| 2^-53
+// in y: relative 1e-14 in the mass at |x - m| / T = 50), the table entry, the
+// polynomial and the product two ulps at most.  So the masses that place the
+// top-p boundary and the probabilities of the accept test carry binary64
+// accuracy, at about 17 vector operations and one LDS read per token.
+constexpr int kExpTab = 64;
+constexpr double kLog2e64 = 64.0 * 1.4426950408889634;     // 64 log2(e)
+constexpr double kE1 = 0.6931471805599453 / 64.0;           // ln(2) / 64
+constexpr double kE2 = kE1 * kE1 / 2.0;
+constexpr double kE3 = kE2 * kE1 / 3.0;
+constexpr double kE4 = kE3 * kE1 / 4.0;
+constexpr double kE5 = kE4 * kE1 / 5.0;
+// 2^(j / 64), j = 0..63, by threads 0..63 (a barrier before the first use).
+__device__ __forceinline__ void exp_table_init(double* tab) {
+  if (threadIdx.x < kExpTab) tab[threadIdx.x] = exp2(threadIdx.x * (1.0 / kExpTab));
 }
+struct Mass {
+  const double* tab;                // 2^(j / 64) in LDS
+  double m;                         // reference logit
+  double c;                         // 64 log2(e) / T
+  __device__ Mass(const double* t, float ref, float T)
+      : tab(t), m(static_cast<double>(ref)), c(kLog2e64 / static_cast<double>(T)) {}
+  __device__ __forceinline__ double operator()(float x) const {
+    // clamped where the mass is below the smallest subnormal (and at x = -inf)
+    const double y = fmax((static_cast<double>(x) - m) * c, -70000.0);
+    const double n = rint(y);
+    const double f = y - n;
+    double p = fma(f, kE5, kE4);
+    p = fma(f, p, kE3);
+    p = fma(f, p, kE2);
+    p = fma(f, p, kE1);
+    p = fma(f, p, 1.0);
+    const int ni = static_cast<int>(n);
+    return ldexp(tab[ni & (kExpTab - 1)] * p, ni >> 6);
+  }
+};
 
 // Fixed-order workgroup reductions (every thread gets the result).
 __device__ double block_sum(double x, double* sh) {
@@ -168,33 +208,38 @@ constexpr int kPer = kBins / kThreads;          // bins (and candidate slots) pe
 static_assert(kCap / kThreads == kPer, "one range size for bins and candidates");
 static_assert(kCap >= kBins, "the candidate arrays hold the fixed-point bins first");
 
-__device__ __forceinline__ int bin_of(float x, float mx) {
-  const float d = (mx - x) * kBinsPerUnit;      // >= 0; +inf for x = -inf
-  return d < static_cast<float>(kBins - 1) ? static_cast<int>(d) : kBins - 1;
+// 0 for x >= mref (and for NaN), kBins - 1 from 64 logits below mref on
+__device__ __forceinline__ int bin_of(float x, float mref) {
+  const float d = (mref - x) * kBinsPerUnit;
+  return static_cast<int>(fminf(fmaxf(d, 0.f), static_cast<float>(kBins - 1)));
+}
+// Candidate order: decreasing logit, then increasing index.
+__device__ __forceinline__ unsigned long long cand_key(float x, int v) {
+  return (static_cast<unsigned long long>(order_key(x)) << 32) | static_cast<unsigned int>(~v);
 }
 
 // Masses in [0, 1] summed by many threads at once (histogram bins, radix
-// digits) go through 66-bit fixed point: m = (hi 2^33 + lo) 2^-66, both
-// chunks below 2^33 (hi = 2^33 only for m = 1), bits below 2^-66 dropped.
-// Chunk sums are integer additions, exact for up to 2^31 terms whatever
-// their order, so every run (and every interleaving of the atomics) yields
-// the same bin; one rounding turns a bin back into binary64.
+// digits) go through 63-bit fixed point: m = (hi 2^32 + lo) 2^-63 with
+// hi = floor(m 2^31) <= 2^31 and lo < 2^32, bits below 2^-63 dropped.  Chunk
+// sums are integer additions, exact for up to 2^32 terms whatever their
+// order, so every run (and every interleaving of the atomics) yields the same
+// bin; one rounding turns a bin back into binary64.
 typedef unsigned long long u64;
 __device__ __forceinline__ void fx_split(double m, u64& hi, u64& lo) {
-  const double t = m * 0x1p33;                  // exact
+  const double t = fmin(m, 1.0) * 0x1p31;       // exact
   const double h = floor(t);
-  hi = static_cast<u64>(h);
-  lo = static_cast<u64>((t - h) * 0x1p33);     // t - h and the scaling are exact
+  hi = static_cast<unsigned int>(h);
+  lo = static_cast<unsigned int>((t - h) * 0x1p32);   // t - h and the scaling are exact
 }
 __device__ __forceinline__ double fx_value(u64 hi, u64 lo) {
-  // chunk sums stay below 2^53 for V < 2^20 (exact); beyond, one rounding each
-  return static_cast<double>(hi) * 0x1p-33 + static_cast<double>(lo) * 0x1p-66;
+  // chunk sums stay below 2^53 for V < 2^21 (exact); beyond, one rounding each
+  return static_cast<double>(hi) * 0x1p-31 + static_cast<double>(lo) * 0x1p-63;
 }
 __device__ __forceinline__ void fx_add(u64* hi, u64* lo, double m) {
   u64 h, l;
   fx_split(m, h, l);
-  if (h) atomicAdd(hi, h);
-  if (l) atomicAdd(lo, l);
+  atomicAdd(hi, h);
+  atomicAdd(lo, l);
 }
 
 // f(x, v) for the n tokens at p (v counted from p); each thread visits its
@@ -333,28 +378,13 @@ __device__ int cross_mass(const double* m, int n, double need, double& above, do
   return r;
 }
 
-// The tokens of bin bn, sorted by decreasing logit then increasing index (as
-// key << 32 | ~index), with their masses; their number, or -1 past kCap.
-__device__ int gather_bin(const float* row, int V, float mx, float T, int bn,
-                          unsigned long long* cand, double* cmass, int* ish) {
+// Sorts cand[0 .. n) (n <= kCap) into decreasing order by a bitonic network
+// over the next power of two (padding sorts last).
+__device__ void sort_cand(unsigned long long* cand, int n) {
   const int tid = threadIdx.x;
-  if (tid == 0) ish[kThreads] = 0;
-  __syncthreads();
-  scan_row(row, V, [&](float x, int v) {
-    if (bin_of(x, mx) == bn) {
-      const int slot = atomicAdd(&ish[kThreads], 1);
-      if (slot < kCap)
-        cand[slot] = (static_cast<unsigned long long>(order_key(x)) << 32) |
-                     static_cast<unsigned int>(~v);
-    }
-  });
-  __syncthreads();
-  const int n = ish[kThreads];
-  __syncthreads();
-  if (n > kCap) return -1;
   int npow = 1;
   while (npow < n) npow <<= 1;
-  for (int j = n + tid; j < npow; j += kThreads) cand[j] = 0ull;   // sorts last
+  for (int j = n + tid; j < npow; j += kThreads) cand[j] = 0ull;
   __syncthreads();
   for (int size = 2; size <= npow; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -372,9 +402,34 @@ __device__ int gather_bin(const float* row, int V, float mx, float T, int bn,
       __syncthreads();
     }
   }
-  for (int j = tid; j < n; j += kThreads)
-    cmass[j] = mass(key_value(static_cast<unsigned int>(cand[j] >> 32)), mx, T);
+}
+
+// Masses of the first n sorted candidates.
+__device__ void cand_masses(const unsigned long long* cand, int n, const Mass& ms, double* cmass) {
+  for (int j = threadIdx.x; j < n; j += kThreads)
+    cmass[j] = ms(key_value(static_cast<unsigned int>(cand[j] >> 32)));
   __syncthreads();
+}
+
+// The tokens of bins lo..hi, sorted (decreasing logit, increasing index);
+// their number, or -1 past kCap.
+__device__ int gather_bins(const float* row, int V, float mref, int lo, int hi,
+                           unsigned long long* cand, int* ish) {
+  const int tid = threadIdx.x;
+  if (tid == 0) ish[kThreads] = 0;
+  __syncthreads();
+  scan_row(row, V, [&](float x, int v) {
+    const int bn = bin_of(x, mref);
+    if (bn >= lo && bn <= hi) {
+      const int slot = atomicAdd(&ish[kThreads], 1);
+      if (slot < kCap) cand[slot] = cand_key(x, v);
+    }
+  });
+  __syncthreads();
+  const int n = ish[kThreads];
+  __syncthreads();
+  if (n > kCap) return -1;
+  sort_cand(cand, n);
   return n;
 }
 
@@ -382,7 +437,7 @@ __device__ int gather_bin(const float* row, int V, float mx, float T, int bn,
 // holds more tokens than the LDS candidate list: top-k by 8-bit digits of the
 // key with integer histograms, top-p by 8-bit digits on binary64 masses.
 // Updates (tau, tie).
-__device__ void radix_select(const float* row, int V, float mx, float T, int top_k, float top_p,
+__device__ void radix_select(const float* row, int V, const Mass& ms, int top_k, float top_p,
                              unsigned int& tau, int& tie, double* dsh, double& above_sh,
                              int* ish) {
   const int tid = threadIdx.x;
@@ -425,7 +480,7 @@ __device__ void radix_select(const float* row, int V, float mx, float T, int top
     double s1 = 0.0;
     for (int v = tid; v < V; v += kThreads) {
       const float x = row[v];
-      if (kept_by(order_key(x), v, tau, tie)) s1 += mass(x, mx, T);
+      if (kept_by(order_key(x), v, tau, tie)) s1 += ms(x);
     }
     s1 = block_sum(s1, dsh);
     const double need = static_cast<double>(top_p) * s1;
@@ -443,7 +498,7 @@ __device__ void radix_select(const float* row, int V, float mx, float T, int top
         const unsigned int key = order_key(x);
         if ((key & pmask) == prefix && kept_by(key, v, tau, tie)) {
           const unsigned int d = (key >> shift) & 255u;
-          fx_add(dhi + d, dlo + d, mass(x, mx, T));
+          fx_add(dhi + d, dlo + d, ms(x));
         }
       }
       __syncthreads();
@@ -477,7 +532,7 @@ __device__ void radix_select(const float* row, int V, float mx, float T, int top
       pmask |= 255u << shift;
     }
     // tokens with key == prefix (all of equal mass): how many reach `need`
-    const double e_tau = mass(key_value(prefix), mx, T);
+    const double e_tau = ms(key_value(prefix));
     int n_tied = 0;
     for (int v = tid; v < V; v += kThreads) {
       const unsigned int key = order_key(row[v]);
@@ -610,6 +665,7 @@ __global__ __launch_bounds__(kThreads) void sampled_slice_bins_kernel(
   __shared__ int hcnt[kBins];
   __shared__ u64 hhi[kBins], hlo[kBins];
   __shared__ double dsh[kThreads];
+  __shared__ double etab[kExpTab];
   const int tid = threadIdx.x;
   const int w = blockIdx.x, rho = blockIdx.y, b = blockIdx.z;
   const size_t rid = static_cast<size_t>(b) * gridDim.y + rho;
@@ -617,6 +673,9 @@ __global__ __launch_bounds__(kThreads) void sampled_slice_bins_kernel(
   int am, bad;
   merge_slices(parts + rid * W, W, mx, am, bad);
   if (bad) return;
+  exp_table_init(etab);
+  __syncthreads();
+  const Mass ms(etab, mx, T);
   const int L = slice_len(V, W);
   const int v0 = w * L;
   const int n = v0 < V ? min(L, V - v0) : 0;
@@ -624,7 +683,7 @@ __global__ __launch_bounds__(kThreads) void sampled_slice_bins_kernel(
   const bool vec = (V & 3) == 0;
   if (!trunc) {
     double s = 0.0;
-    scan_span(row, n, vec, [&](float x, int) { s += mass(x, mx, T); });
+    scan_span(row, n, vec, [&](float x, int) { s += ms(x); });
     s = block_sum(s, dsh);
     if (tid == 0) slice_s[rid * W + w] = s;
     return;
@@ -638,7 +697,7 @@ __global__ __launch_bounds__(kThreads) void sampled_slice_bins_kernel(
   scan_span(row, n, vec, [&](float x, int) {
     const int bn = bin_of(x, mx);
     atomicAdd(&hcnt[bn], 1);
-    fx_add(hhi + bn, hlo + bn, mass(x, mx, T));
+    fx_add(hhi + bn, hlo + bn, ms(x));
   });
   __syncthreads();
   char* h = hist + rid * kRowHistBytes;
@@ -655,6 +714,190 @@ __global__ __launch_bounds__(kThreads) void sampled_slice_bins_kernel(
   }
 }
 
+// The rows kernel's pass over a row (one workgroup per row) accumulates, per
+// setting: the whole mass (no truncation); bin counts (top-k, with or
+// without top-p: every mass that it needs comes from the gathered top
+// tokens); bin counts and masses (top-p alone); or nothing (the maximum,
+// argmax and validity alone, before a second pass).
+enum RowMode { kSum, kCount, kCountMass, kTrack };
+
+struct RowScan {                    // one thread's share of the pass
+  float mx;                         // maximum seen, first at index am
+  int am;
+  int bad;                          // NaN or +inf seen
+  int over;                         // a logit above the reference
+  double sl;                        // mass (kSum)
+};
+
+struct RowLds {                     // the pass's LDS arrays
+  int* hcnt;                        // bin counts
+  u64* hhi;                         // bin masses, high and low fixed-point chunks
+  u64* hlo;
+  unsigned long long* cand;         // kCount: tokens of bins <= bhat
+  int* ncand;                       //   and their number (also past kCap)
+};
+
+template <int Mode, bool Track>
+__device__ __forceinline__ void row_step(float x, int v, float ref, const Mass& ms, int bhat,
+                                         const RowLds& lds, RowScan& st) {
+  if (Track) {
+    st.bad |= !(x < INFINITY);
+    st.over |= x > ref;
+    if (x > st.mx) {                // each thread visits ascending indices
+      st.mx = x;
+      st.am = v;
+    }
+  }
+  if (Mode == kSum) st.sl += ms(x);
+  if (Mode == kCount || Mode == kCountMass) {
+    const int bn = bin_of(x, ref);
+    atomicAdd(&lds.hcnt[bn], 1);
+    if (Mode == kCountMass) fx_add(lds.hhi + bn, lds.hlo + bn, ms(x));
+    if (Mode == kCount && bn <= bhat) {
+      const int slot = atomicAdd(lds.ncand, 1);
+      if (slot < kCap) lds.cand[slot] = cand_key(x, v);
+    }
+  }
+}
+
+__device__ __forceinline__ void clear_bins(int Mode, const RowLds& lds) {
+  for (int j = threadIdx.x; j < kBins; j += kThreads) {
+    lds.hcnt[j] = 0;
+    if (Mode == kCountMass) {
+      lds.hhi[j] = 0ull;
+      lds.hlo[j] = 0ull;
+    }
+  }
+  if (threadIdx.x == 0) *lds.ncand = 0;
+  __syncthreads();
+}
+
+// The row's first n0 = min(V, kPeek) entries, kFirst per thread in ascending
+// index order (index -1 for an empty slot).
+constexpr int kFirst = kPeek / kThreads;
+static_assert(kFirst % 4 == 0, "whole 16-byte loads");
+__device__ __forceinline__ void load_first(const float* row, int n0, bool vec, float* xs, int* vs) {
+  const int tid = threadIdx.x;
+  if (vec) {
+    const float4* r4 = reinterpret_cast<const float4*>(row);
+#pragma unroll
+    for (int u = 0; u < kFirst / 4; ++u) {
+      const int j = tid + u * kThreads;
+      const bool in = 4 * j < n0;
+      const float4 a = r4[in ? j : 0];
+      xs[4 * u] = a.x;
+      xs[4 * u + 1] = a.y;
+      xs[4 * u + 2] = a.z;
+      xs[4 * u + 3] = a.w;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) vs[4 * u + c] = in ? 4 * j + c : -1;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kFirst; ++u) {
+      const int j = tid + u * kThreads;
+      const bool in = j < n0;
+      xs[u] = row[in ? j : 0];
+      vs[u] = in ? j : -1;
+    }
+  }
+}
+
+// Maximum over the workgroup (binary32 maxima: exact in any order).
+__device__ float block_max(float x, float* fsh) {
+  const int tid = threadIdx.x;
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  if ((tid & 63) == 0) fsh[tid >> 6] = x;
+  __syncthreads();
+  float r = fsh[0];
+  for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, fsh[w]);
+  __syncthreads();
+  return r;
+}
+
+// The workgroup's maximum with its smallest index, and the OR of the flags.
+__device__ void block_argmax(RowScan& st, float* fsh, int* ish) {
+  const int tid = threadIdx.x;
+  int flags = st.bad | (st.over << 1);
+  float mx = st.mx;
+  int am = st.am;
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(mx, o, 64);
+    const int oa = __shfl_xor(am, o, 64);
+    if (om > mx || (om == mx && oa < am)) {
+      mx = om;
+      am = oa;
+    }
+    flags |= __shfl_xor(flags, o, 64);
+  }
+  if ((tid & 63) == 0) {
+    fsh[tid >> 6] = mx;
+    ish[tid >> 6] = am;
+    ish[kThreads / 64 + (tid >> 6)] = flags;
+  }
+  __syncthreads();
+  mx = fsh[0];
+  am = ish[0];
+  flags = ish[kThreads / 64];
+  for (int w = 1; w < kThreads / 64; ++w) {
+    const float om = fsh[w];
+    const int oa = ish[w];
+    if (om > mx || (om == mx && oa < am)) {
+      mx = om;
+      am = oa;
+    }
+    flags |= ish[kThreads / 64 + w];
+  }
+  __syncthreads();
+  st.mx = mx;
+  st.am = am;
+  st.bad = flags & 1;
+  st.over = flags >> 1;
+}
+
+// The pass against the provisional reference ref, starting from the first
+// entries held in registers.  With spec > 0 (top-k), once those entries are
+// counted, bhat becomes the first bin where their count reaches spec, and
+// the pass lists every token of bins <= bhat as it goes; returns bhat (-1
+// when nothing is listed).
+template <int Mode>
+__device__ __forceinline__ int row_pass(const float* row, int V, int n0, bool vec, const float* xs, const int* vs,
+                        float ref, const Mass& ms, int spec, const RowLds& lds, RowScan& st,
+                        int* ish) {
+  if (Mode != kSum && Mode != kTrack) clear_bins(Mode, lds);
+#pragma unroll
+  for (int u = 0; u < kFirst; ++u)
+    if (vs[u] >= 0) row_step<Mode, true>(xs[u], vs[u], ref, ms, -1, lds, st);
+  int bhat = -1;
+  if (Mode == kCount && spec > 0) {
+    __syncthreads();
+    int above;
+    const int bh = bins_cross_count(lds.hcnt, spec, above, ish);
+    if (bh < kBins) {
+      bhat = bh;
+#pragma unroll
+      for (int u = 0; u < kFirst; ++u) {
+        if (vs[u] >= 0 && bin_of(xs[u], ref) <= bhat) {
+          const int slot = atomicAdd(lds.ncand, 1);
+          if (slot < kCap) lds.cand[slot] = cand_key(xs[u], vs[u]);
+        }
+      }
+    }
+  }
+  scan_span(row + n0, V - n0, vec, [&](float x, int v) {
+    row_step<Mode, true>(x, v + n0, ref, ms, bhat, lds, st);
+  });
+  return bhat;
+}
+
+// A second pass over the whole row against its maximum.
+template <int Mode>
+__device__ __forceinline__ void row_repass(const float* row, int V, float mx, const Mass& ms, const RowLds& lds,
+                           RowScan& st) {
+  if (Mode != kSum) clear_bins(Mode, lds);
+  scan_row(row, V, [&](float x, int v) { row_step<Mode, false>(x, v, mx, ms, -1, lds, st); });
+}
+
 __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
     const float* __restrict__ tgt, const float* __restrict__ dft, const int32_t* __restrict__ toks,
     int k, int V, float temperature, int top_k, float top_p, int W,
@@ -667,6 +910,9 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
   __shared__ double hmass[kBins];
   __shared__ unsigned long long cand[kCap];
   __shared__ double cmass[kCap];
+  __shared__ double etab[kExpTab];
+  __shared__ float fsh[kThreads / 64];
+  __shared__ int ncand;
   const int tid = threadIdx.x;
   const int rho = blockIdx.x;                   // 0..k target rows, k+1..2k draft rows
   const int b = blockIdx.y;
@@ -677,13 +923,17 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
                           : dft + (static_cast<size_t>(b) * k + i) * V;
   const int tok = i < k ? toks[static_cast<size_t>(b) * k + i] : -1;
   SampledRow out = {};
+  exp_table_init(etab);
 
-  // maximum, argmax (smallest index among equal maxima), validity
   const size_t rid = static_cast<size_t>(b) * R + rho;
   const float T = temperature;
   const bool trunc_k = top_k > 0 && top_k < V;
   const bool trunc_p = top_p < 1.f;
   const bool trunc = trunc_k || trunc_p;
+  const int mode = !trunc ? kSum : trunc_k ? kCount : kCountMass;
+  // (during the pass the fixed-point bins live in the candidate arrays)
+  const RowLds lds = {hcnt, reinterpret_cast<u64*>(cand), reinterpret_cast<u64*>(cmass), cand,
+                      &ncand};
   float mx = -INFINITY;
   int am = V;
   int bad = 0;
@@ -691,84 +941,69 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
   // logit of the row; the kept probabilities, ratios of such masses, do not
   // depend on which.  With one workgroup per row, mref is the maximum of the
   // row's first kPeek entries raised by min(4, 8 T), and the maximum, the
-  // validity, and the bins (or the whole mass) come out of one pass; should
-  // a logit exceed mref after all, mref becomes the row maximum and the bins
-  // (or the mass) take a second pass.  (The fixed-point bin masses resolve
-  // 2^-66 of mref's scale, at most e^8 of the maximum's.)
+  // validity, and the counts (and masses) come out of one pass; should a
+  // logit exceed mref after all, mref becomes the row maximum and the
+  // accumulation takes a second pass.  (The fixed-point bin masses resolve
+  // 2^-63 of mref's scale, at most e^8 of the maximum's.)  For top-k, the
+  // counts of those first entries also predict a bin bhat that holds about
+  // 3 top_k tokens of the row, and the pass lists the tokens down to it, so
+  // that the boundary needs no second read when the prediction holds.
   float mref = -INFINITY;
-  bool fused = false;
-  double s_fused = 0.0;
-  u64* const hhi = reinterpret_cast<u64*>(cand);  // fixed-point bins (one pass)
-  u64* const hlo = reinterpret_cast<u64*>(cmass);
+  double sl = 0.0;
+  int bhat = -1;
   if (W > 1) {
     merge_slices(parts + rid * W, W, mx, am, bad);
     mref = mx;
+    __syncthreads();                            // (the table)
   } else {
+    const bool vec = (V & 3) == 0;
+    const int n0 = min(V, kPeek);
+    float xs[kFirst];
+    int vs[kFirst];
+    load_first(row, n0, vec, xs, vs);
     float m0 = -INFINITY;
-    for (int v = tid; v < min(V, kPeek); v += kThreads) m0 = fmaxf(m0, row[v]);
-    dsh[tid] = m0;
-    __syncthreads();
-    for (int w = kThreads / 2; w > 0; w >>= 1) {
-      if (tid < w) dsh[tid] = fmax(dsh[tid], dsh[tid + w]);
-      __syncthreads();
-    }
-    m0 = static_cast<float>(dsh[0]);
-    __syncthreads();
-    fused = m0 > -INFINITY && m0 < INFINITY;
+#pragma unroll
+    for (int u = 0; u < kFirst; ++u)
+      if (vs[u] >= 0) m0 = fmaxf(m0, xs[u]);
+    m0 = block_max(m0, fsh);                    // (its barrier also orders the table)
+    const bool fused = m0 > -INFINITY && m0 < INFINITY;
     const float ref = fused ? m0 + fminf(4.f, 8.f * T) : INFINITY;
-    if (fused && trunc) {
-      for (int j = tid; j < kBins; j += kThreads) {
-        hcnt[j] = 0;
-        hhi[j] = 0ull;
-        hlo[j] = 0ull;
-      }
-      __syncthreads();
+    const Mass ms(etab, ref, T);
+    // top-k: the first entries' count that predicts about 3 top_k tokens
+    int spec = 0;
+    if (trunc_k && V > n0 && 6 * top_k <= kCap)
+      spec = static_cast<int>((3ll * top_k * n0 + V - 1) / V) + 1;
+    RowScan st = {-INFINITY, V, 0, 0, 0.0};
+    if (!fused)
+      row_pass<kTrack>(row, V, n0, vec, xs, vs, ref, ms, 0, lds, st, ish);
+    else if (mode == kSum)
+      row_pass<kSum>(row, V, n0, vec, xs, vs, ref, ms, 0, lds, st, ish);
+    else if (mode == kCount)
+      bhat = row_pass<kCount>(row, V, n0, vec, xs, vs, ref, ms, spec, lds, st, ish);
+    else
+      row_pass<kCountMass>(row, V, n0, vec, xs, vs, ref, ms, 0, lds, st, ish);
+    const double sl1 = st.sl;
+    block_argmax(st, fsh, ish);
+    mx = st.mx;
+    am = st.am;
+    bad = st.bad | (mx == -INFINITY);
+    if (!bad && (!fused || st.over)) {
+      mref = mx;
+      bhat = -1;
+      const Mass ms2(etab, mx, T);
+      RowScan s2 = {-INFINITY, V, 0, 0, 0.0};
+      if (mode == kSum)
+        row_repass<kSum>(row, V, mx, ms2, lds, s2);
+      else if (mode == kCount)
+        row_repass<kCount>(row, V, mx, ms2, lds, s2);
+      else
+        row_repass<kCountMass>(row, V, mx, ms2, lds, s2);
+      sl = s2.sl;
+    } else {
+      mref = ref;
+      sl = sl1;
     }
-    int over = 0;
-    double sl = 0.0;
-    scan_row(row, V, [&](float x, int v) {
-      bad |= (x != x) | (x == INFINITY);
-      if (x > mx || (x == mx && v < am)) {
-        mx = x;
-        am = v;
-      }
-      if (fused) {
-        if (x > ref) {
-          over = 1;
-        } else if (trunc) {
-          const int bn = bin_of(x, ref);
-          atomicAdd(&hcnt[bn], 1);
-          fx_add(hhi + bn, hlo + bn, mass(x, ref, T));
-        } else {
-          sl += mass(x, ref, T);
-        }
-      }
-    });
-    // (the maxima go through dsh, the indices through hmass, free here)
-    int* const ash = reinterpret_cast<int*>(hmass);
-    dsh[tid] = mx;
-    ash[tid] = am;
-    ish[tid] = bad | (over << 1);
     __syncthreads();
-    for (int w = kThreads / 2; w > 0; w >>= 1) {
-      if (tid < w) {
-        const double o = dsh[tid + w];
-        const int oa = ash[tid + w];
-        if (o > dsh[tid] || (o == dsh[tid] && oa < ash[tid])) {
-          dsh[tid] = o;
-          ash[tid] = oa;
-        }
-        ish[tid] |= ish[tid + w];
-      }
-      __syncthreads();
-    }
-    mx = static_cast<float>(dsh[0]);
-    am = ash[0];
-    bad = (ish[0] & 1) | (mx == -INFINITY);
-    fused = fused && !(ish[0] & 2);
-    __syncthreads();
-    if (fused && !trunc) s_fused = block_sum(sl, dsh);
-    mref = fused ? ref : mx;
   }
   out.m = mref;
   out.argmax = am;
@@ -780,6 +1015,7 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
     if (tid == 0) rows[static_cast<size_t>(b) * R + rho] = out;
     return;
   }
+  const Mass ms(etab, mref, T);
   unsigned int tau = 0u;
   int tie = -1;
 
@@ -787,87 +1023,76 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
   if (!trunc) {
     if (W > 1) {
       for (int w = 0; w < W; ++w) s += slice_s[rid * W + w];
-    } else if (fused) {
-      s = s_fused;
     } else {
-      scan_row(row, V, [&](float x, int) { s += mass(x, mref, T); });
-      s = block_sum(s, dsh);
+      s = block_sum(sl, dsh);
     }
   } else {
-    // Bins of 1/32 logit below mref (monotone in the logit): counts and
-    // binary64 masses.  The boundary bin of each truncation is then resolved
-    // exactly from its tokens, sorted in LDS.
+    // bins of 1/32 logit below mref (monotone in the logit): counts, and for
+    // top-p alone binary64 masses
     if (W > 1) {
       const char* h = hist + rid * kRowHistBytes;
-      const u64* ghi = reinterpret_cast<const u64*>(h + kBins * sizeof(int));
-      for (int j = tid; j < kBins; j += kThreads) {
-        hcnt[j] = reinterpret_cast<const int*>(h)[j];
-        hmass[j] = fx_value(ghi[j], ghi[kBins + j]);
+      for (int j = tid; j < kBins; j += kThreads) hcnt[j] = reinterpret_cast<const int*>(h)[j];
+      if (!trunc_k) {
+        const u64* ghi = reinterpret_cast<const u64*>(h + kBins * sizeof(int));
+        for (int j = tid; j < kBins; j += kThreads)
+          hmass[j] = fx_value(ghi[j], ghi[kBins + j]);
       }
-    } else {
-      // fixed-point chunk sums in the candidate arrays (free until the
-      // boundary bins are gathered), then one binary64 value per bin
-      if (!fused) {
-        for (int j = tid; j < kBins; j += kThreads) {
-          hcnt[j] = 0;
-          hhi[j] = 0ull;
-          hlo[j] = 0ull;
-        }
-        __syncthreads();
-        scan_row(row, V, [&](float x, int) {
-          const int bn = bin_of(x, mref);
-          atomicAdd(&hcnt[bn], 1);
-          fx_add(hhi + bn, hlo + bn, mass(x, mref, T));
-        });
-        __syncthreads();
-      }
-      for (int j = tid; j < kBins; j += kThreads) hmass[j] = fx_value(hhi[j], hlo[j]);
+    } else if (!trunc_k) {
+      for (int j = tid; j < kBins; j += kThreads)
+        hmass[j] = fx_value(lds.hhi[j], lds.hlo[j]);
     }
     __syncthreads();
-    bool exact = true;
-    int bk = kBins, rk = 0;                     // top-k: boundary bin, kept tokens in it
-    double mass_k = 0.0;                        // kept mass after top-k
+    bool exact = false;
     if (trunc_k) {
+      // the top_k tokens, sorted: from the list the pass made when it reaches
+      // the boundary bin, else gathered by a second read of the bins down to it
       int above = 0;
-      bk = bins_cross_count(hcnt, top_k, above, ish);
-      rk = top_k - above;
-      exact = bk < kBins && gather_bin(row, V, mref, T, bk, cand, cmass, ish) >= rk;
+      const int bk = bins_cross_count(hcnt, top_k, above, ish);
+      int n = -1;
+      if (bhat >= 0 && bk <= bhat && ncand <= kCap) {
+        n = ncand;
+        sort_cand(cand, n);
+      } else if (bk < kBins && above + hcnt[bk] <= kCap) {
+        n = gather_bins(row, V, mref, 0, bk, cand, ish);
+      }
+      exact = n >= top_k;
       if (exact) {
-        tau = static_cast<unsigned int>(cand[rk - 1] >> 32);
-        tie = static_cast<int>(~static_cast<unsigned int>(cand[rk - 1]));
-        mass_k = sum_before(hmass, bk, dsh) + sum_before(cmass, rk, dsh);
-        s = mass_k;
+        cand_masses(cand, top_k, ms, cmass);
+        int r = top_k;                          // tokens kept
+        if (trunc_p) {
+          // top-p on the renormalised top-k row
+          const double need = static_cast<double>(top_p) * sum_before(cmass, top_k, dsh);
+          double before = 0.0;
+          const int j = cross_mass(cmass, top_k, need, before, dsh, ish);
+          r = j < top_k ? j + 1 : top_k;
+        }
+        tau = static_cast<unsigned int>(cand[r - 1] >> 32);
+        tie = static_cast<int>(~static_cast<unsigned int>(cand[r - 1]));
+        s = sum_before(cmass, r, dsh);
       }
-    }
-    if (exact && trunc_p) {
-      const double s1 = trunc_k ? mass_k : sum_before(hmass, kBins, dsh);
-      const double need = static_cast<double>(top_p) * s1;
-      // the boundary among the bins wholly kept by top-k (those before bk)
+    } else {
+      const double need = static_cast<double>(top_p) * sum_before(hmass, kBins, dsh);
       double above = 0.0;
-      const int bp = cross_mass(hmass, bk, need, above, dsh, ish);
-      int n = 0;
-      if (bp < bk) {
-        n = gather_bin(row, V, mref, T, bp, cand, cmass, ish);
-      } else if (trunc_k) {
-        n = rk;                                 // inside the top-k boundary bin, still sorted
-      }
+      const int bp = cross_mass(hmass, kBins, need, above, dsh, ish);
+      const int n = bp < kBins ? gather_bins(row, V, mref, bp, bp, cand, ish) : -1;
       exact = n > 0;
       if (exact) {
+        cand_masses(cand, n, ms, cmass);
         double before = 0.0;
         const int j = cross_mass(cmass, n, need - above, before, dsh, ish);
         const int r = j < n ? j + 1 : n;        // tokens kept from the boundary bin
         tau = static_cast<unsigned int>(cand[r - 1] >> 32);
         tie = static_cast<int>(~static_cast<unsigned int>(cand[r - 1]));
-        s = sum_before(hmass, bp < bk ? bp : bk, dsh) + sum_before(cmass, r, dsh);
+        s = sum_before(hmass, bp, dsh) + sum_before(cmass, r, dsh);
       }
     }
     if (!exact) {
       tau = 0u;
       tie = -1;
-      radix_select(row, V, mref, T, top_k, top_p, tau, tie, dsh, above_sh, ish);
+      radix_select(row, V, ms, top_k, top_p, tau, tie, dsh, above_sh, ish);
       s = 0.0;
       scan_row(row, V, [&](float x, int v) {
-        if (kept_by(order_key(x), v, tau, tie)) s += mass(x, mref, T);
+        if (kept_by(order_key(x), v, tau, tie)) s += ms(x);
       });
       s = block_sum(s, dsh);
     }
@@ -881,7 +1106,7 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
     double pd = 0.0;
     if (tok >= 0 && tok < V) {
       const float x = row[tok];
-      pd = kept_by(order_key(x), tok, tau, tie) ? mass(x, mref, T) / s : 0.0;
+      pd = kept_by(order_key(x), tok, tau, tie) ? ms(x) / s : 0.0;
     }
     out.pd = pd;
     rows[static_cast<size_t>(b) * R + rho] = out;
@@ -971,7 +1196,7 @@ __global__ __launch_bounds__(kThreads) void sampled_decide_kernel(
 struct ResidualRows {
   const float* trow;
   const float* drow;
-  float tm, dm, temp;
+  Mass tmass, dmass;                // exp((l - m) / T) against each row's reference
   unsigned int ttau, dtau;
   int ttie, dtie;
   double ts, ds;
@@ -979,11 +1204,9 @@ struct ResidualRows {
 // The weight of entry v from its target logit x and draft logit y.
 __device__ __forceinline__ double res_weight(const ResidualRows& q, float x, float y, int v,
                                              bool plain) {
-  const double pv =
-      kept_by(order_key(x), v, q.ttau, q.ttie) ? mass(x, q.tm, q.temp) / q.ts : 0.0;
+  const double pv = kept_by(order_key(x), v, q.ttau, q.ttie) ? q.tmass(x) / q.ts : 0.0;
   if (plain) return pv;
-  const double qv =
-      kept_by(order_key(y), v, q.dtau, q.dtie) ? mass(y, q.dm, q.temp) / q.ds : 0.0;
+  const double qv = kept_by(order_key(y), v, q.dtau, q.dtie) ? q.dmass(y) / q.ds : 0.0;
   return fmax(0.0, pv - qv);
 }
 
@@ -1001,22 +1224,16 @@ __device__ __forceinline__ void res_load(const ResidualRows& q, int V, int blk, 
 }
 __device__ __forceinline__ ResidualRows residual_rows(const float* tgt, const float* dft,
                                                       const SampledRow* rows, int b, int k,
-                                                      int V, int r) {
-  ResidualRows q;
+                                                      int V, int r, const double* etab) {
   const SampledRow* rr = rows + static_cast<size_t>(b) * (2 * k + 1);
   const SampledRow* rt = rr + r;
   const SampledRow* rd = r < k ? rr + k + 1 + r : rt;
-  q.trow = tgt + (static_cast<size_t>(b) * (k + 1) + r) * V;
-  q.drow = r < k ? dft + (static_cast<size_t>(b) * k + r) * V : q.trow;
-  q.tm = rt->m;
-  q.dm = rd->m;
-  q.temp = rt->temp;
-  q.ttau = rt->tau;
-  q.dtau = rd->tau;
-  q.ttie = rt->tie;
-  q.dtie = rd->tie;
-  q.ts = rt->s;
-  q.ds = rd->s;
+  ResidualRows q = {tgt + (static_cast<size_t>(b) * (k + 1) + r) * V,
+                    r < k ? dft + (static_cast<size_t>(b) * k + r) * V
+                          : tgt + (static_cast<size_t>(b) * (k + 1) + r) * V,
+                    Mass(etab, rt->m, rt->temp),
+                    Mass(etab, rd->m, rt->temp),
+                    rt->tau, rd->tau, rt->tie, rd->tie, rt->s, rd->s};
   return q;
 }
 __device__ __forceinline__ double thread_res_sum(const ResidualRows& q, int V, int blk, bool plain) {
@@ -1051,13 +1268,16 @@ __global__ __launch_bounds__(kThreads) void sampled_resid_kernel(
     const SampledRow* __restrict__ rows, const SampledDecision* __restrict__ decs,
     double* __restrict__ totals) {
   __shared__ double wsh[2][kThreads];
+  __shared__ double etab[kExpTab];
   const int tid = threadIdx.x;
   const int blk = blockIdx.x;
   const int b = blockIdx.y;
   const int G = gridDim.x;
   const SampledDecision dec = decs[b];
   if (dec.status != 0) return;
-  const ResidualRows q = residual_rows(tgt, dft, rows, b, k, V, dec.n_acc);
+  exp_table_init(etab);
+  __syncthreads();
+  const ResidualRows q = residual_rows(tgt, dft, rows, b, k, V, dec.n_acc, etab);
   wsh[0][tid] = thread_res_sum(q, V, blk, dec.plain != 0);
   wsh[1][tid] = dec.plain ? 0.0 : thread_res_sum(q, V, blk, true);
   __syncthreads();
@@ -1076,10 +1296,12 @@ __global__ __launch_bounds__(kThreads) void sampled_select_kernel(
   __shared__ double wsh[kThreads];
   __shared__ double run_sh, thr_sh;
   __shared__ int ish[3];
+  __shared__ double etab[kExpTab];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const SampledDecision dec = decs[b];
   if (dec.status != 0) return;
+  exp_table_init(etab);
   // the trial's block totals, staged in LDS by every thread when they fit
   const double* tot = totals + static_cast<size_t>(b) * 2 * G;
   if (2 * G <= kThreads) {
@@ -1124,7 +1346,7 @@ __global__ __launch_bounds__(kThreads) void sampled_select_kernel(
   __syncthreads();
   const int blk = ish[0];
   const bool plain = dec.plain != 0 || ish[1] == 1;
-  const ResidualRows q = residual_rows(tgt, dft, rows, b, k, V, dec.n_acc);
+  const ResidualRows q = residual_rows(tgt, dft, rows, b, k, V, dec.n_acc, etab);
   const double mine = thread_res_sum(q, V, blk, plain);
   wsh[tid] = mine;
   __syncthreads();
