@@ -380,7 +380,7 @@ __device__ int cross_mass(const double* m, int n, double need, double& above, do
 
 // Sorts cand[0 .. n) (n <= kCap) into decreasing order by a bitonic network
 // over the next power of two (padding sorts last).
-__device__ void sort_cand(unsigned long long* cand, int n) {
+__device__ __noinline__ void sort_cand(unsigned long long* cand, int n) {
   const int tid = threadIdx.x;
   int npow = 1;
   while (npow < n) npow <<= 1;
@@ -413,7 +413,7 @@ __device__ void cand_masses(const unsigned long long* cand, int n, const Mass& m
 
 // The tokens of bins lo..hi, sorted (decreasing logit, increasing index);
 // their number, or -1 past kCap.
-__device__ int gather_bins(const float* row, int V, float mref, int lo, int hi,
+__device__ __noinline__ int gather_bins(const float* row, int V, float mref, int lo, int hi,
                            unsigned long long* cand, int* ish) {
   const int tid = threadIdx.x;
   if (tid == 0) ish[kThreads] = 0;
@@ -547,16 +547,20 @@ __device__ void radix_select(const float* row, int V, const Mass& ms, int top_k,
 
 }
 
-// Rows split into W slices (few rows per call): the row statistics that need
-// a full pass -- maximum, argmax, validity, then the bins (or the whole mass
-// when nothing truncates) -- are taken per slice by W workgroups per row.
+// Rows split into W slices (few rows per call): the pass over a row --
+// maximum, argmax, validity, then the bins (or the whole mass when nothing
+// truncates) against the row's provisional reference -- is taken per slice
+// by W workgroups per row, and so is the gather of the boundary bins' tokens.
 // Maxima and whole masses merge in slice order; each slice adds its nonzero
-// bins into the row's histogram with device atomics on integers (counts and
-// the fixed-point mass chunks), exact in any order.
+// bins into the row's histogram, and its gathered tokens into the row's
+// candidate list, with device atomics on integers (counts, the fixed-point
+// mass chunks, list slots): the histogram is exact in any order and the list
+// is sorted before use.
 struct SlicePart {
   float m;                          // slice maximum (-inf when empty)
   int am;                           // smallest index of it (V when empty)
-  int bad;                          // NaN or +inf seen
+  int flags;                        // 1: NaN or +inf seen, 2: a logit above the
+                                    // reference, 4: no usable reference
   int pad;
 };
 static_assert(sizeof(SlicePart) == 16, "slice record layout");
@@ -564,6 +568,18 @@ constexpr int kMaxSlices = 16;
 static_assert(kMaxSlices <= 64, "one slice record per lane");
 // per row: counts (int), then the high and the low mass chunk sums (u64)
 constexpr size_t kRowHistBytes = kBins * (sizeof(int) + 2 * sizeof(u64));
+struct RowPlan {                    // per row, for the slices' gather and the rows launch
+  float ref;                        // the row's provisional reference
+  int lo, hi;                       // bins the slices gather (none when lo > hi)
+  int ncand;                        // tokens gathered (past kCap: overflow)
+  int ticket;                       // slices done with the pass
+  float mx;                         // the merged slice records: maximum,
+  int am;                           //   its smallest index,
+  int flags;                        //   flags (SlicePart)
+  double need;                      // top-p alone: top_p times the row's mass,
+  double above;                     //   and the mass of the bins before bin lo
+};
+static_assert(sizeof(RowPlan) == 48, "row plan layout");
 
 __host__ __device__ inline int slice_len(int V, int W) { return ((V + W - 1) / W + 3) & ~3; }
 
@@ -573,145 +589,36 @@ __device__ __forceinline__ const float* row_ptr(const float* tgt, const float* d
                   : dft + (static_cast<size_t>(b) * k + (rho - k - 1)) * V;
 }
 
-// The row's maximum, argmax and validity from its W slice records, merged in
-// slice order (the same in every thread and launch).  Called by whole waves.
+// The row's maximum, argmax and flags from its W slice records, merged in
+// slice order (the same in every thread and launch).  Called by whole waves;
+// the records are read at device scope (written by other workgroups of the
+// same launch, when the last slice merges them).
 __device__ __forceinline__ void merge_slices(const SlicePart* part, int W, float& mx, int& am,
-                                             int& bad) {
+                                             int& flags) {
   // lane w loads slice w's record (all W loads in flight at once); every
   // lane then merges the W records in order
   const int lane = threadIdx.x & 63;
-  SlicePart mine = {-INFINITY, 0x7FFFFFFF, 0, 0};
-  if (lane < W) mine = part[lane];
+  float pm = -INFINITY;
+  int pa = 0x7FFFFFFF, pf = 0;
+  if (lane < W) {
+    const int* q = reinterpret_cast<const int*>(part + lane);
+    pm = __int_as_float(__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    pa = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    pf = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   mx = -INFINITY;
   am = 0x7FFFFFFF;
-  bad = 0;
+  flags = 0;
   for (int w = 0; w < W; ++w) {
-    const float m = __shfl(mine.m, w, 64);
-    const int a = __shfl(mine.am, w, 64);
+    const float m = __shfl(pm, w, 64);
+    const int a = __shfl(pa, w, 64);
     if (m > mx || (m == mx && a < am)) {
       mx = m;
       am = a;
     }
-    bad |= __shfl(mine.bad, w, 64);
+    flags |= __shfl(pf, w, 64);
   }
-  bad |= mx == -INFINITY;
-}
-
-// grid (W, 2k+1, B): slice maximum, argmax, validity; clears the row's
-// histogram.
-__global__ __launch_bounds__(kThreads) void sampled_slice_max_kernel(
-    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V, int W,
-    SlicePart* __restrict__ parts, char* __restrict__ hist) {
-  __shared__ float msh[kThreads];
-  __shared__ int ash[kThreads];
-  __shared__ int bsh[kThreads];
-  const int tid = threadIdx.x;
-  const int w = blockIdx.x, rho = blockIdx.y, b = blockIdx.z;
-  const int L = slice_len(V, W);
-  const int v0 = w * L;
-  const int n = v0 < V ? min(L, V - v0) : 0;
-  const float* row = row_ptr(tgt, dft, b, rho, k, V);
-  {
-    char* h = hist + (static_cast<size_t>(b) * gridDim.y + rho) * kRowHistBytes;
-    for (int j = w * kThreads + tid; j < kBins; j += W * kThreads) {
-      reinterpret_cast<int*>(h)[j] = 0;
-      reinterpret_cast<u64*>(h + kBins * sizeof(int))[j] = 0ull;
-      reinterpret_cast<u64*>(h + kBins * sizeof(int))[kBins + j] = 0ull;
-    }
-  }
-  float mx = -INFINITY;
-  int am = V;
-  int bad = 0;
-  scan_span(row + v0, n, (V & 3) == 0, [&](float x, int v) {
-    bad |= (x != x) | (x == INFINITY);
-    if (x > mx || (x == mx && v0 + v < am)) {
-      mx = x;
-      am = v0 + v;
-    }
-  });
-  msh[tid] = mx;
-  ash[tid] = am;
-  bsh[tid] = bad;
-  __syncthreads();
-  for (int h = kThreads / 2; h > 0; h >>= 1) {
-    if (tid < h) {
-      const float o = msh[tid + h];
-      const int oa = ash[tid + h];
-      if (o > msh[tid] || (o == msh[tid] && oa < ash[tid])) {
-        msh[tid] = o;
-        ash[tid] = oa;
-      }
-      bsh[tid] |= bsh[tid + h];
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    SlicePart q;
-    q.m = msh[0];
-    q.am = ash[0];
-    q.bad = bsh[0];
-    q.pad = 0;
-    parts[(static_cast<size_t>(b) * gridDim.y + rho) * W + w] = q;
-  }
-}
-
-// grid (W, 2k+1, B): with truncation, the slice's bin counts and binary64
-// masses below the row maximum, added into the row's histogram; without, the
-// slice's whole mass.  Nothing for a row that fails its check.
-__global__ __launch_bounds__(kThreads) void sampled_slice_bins_kernel(
-    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V, int W, float T,
-    int trunc, const SlicePart* __restrict__ parts, double* __restrict__ slice_s,
-    char* __restrict__ hist) {
-  __shared__ int hcnt[kBins];
-  __shared__ u64 hhi[kBins], hlo[kBins];
-  __shared__ double dsh[kThreads];
-  __shared__ double etab[kExpTab];
-  const int tid = threadIdx.x;
-  const int w = blockIdx.x, rho = blockIdx.y, b = blockIdx.z;
-  const size_t rid = static_cast<size_t>(b) * gridDim.y + rho;
-  float mx;
-  int am, bad;
-  merge_slices(parts + rid * W, W, mx, am, bad);
-  if (bad) return;
-  exp_table_init(etab);
-  __syncthreads();
-  const Mass ms(etab, mx, T);
-  const int L = slice_len(V, W);
-  const int v0 = w * L;
-  const int n = v0 < V ? min(L, V - v0) : 0;
-  const float* row = row_ptr(tgt, dft, b, rho, k, V) + v0;
-  const bool vec = (V & 3) == 0;
-  if (!trunc) {
-    double s = 0.0;
-    scan_span(row, n, vec, [&](float x, int) { s += ms(x); });
-    s = block_sum(s, dsh);
-    if (tid == 0) slice_s[rid * W + w] = s;
-    return;
-  }
-  for (int j = tid; j < kBins; j += kThreads) {
-    hcnt[j] = 0;
-    hhi[j] = 0ull;
-    hlo[j] = 0ull;
-  }
-  __syncthreads();
-  scan_span(row, n, vec, [&](float x, int) {
-    const int bn = bin_of(x, mx);
-    atomicAdd(&hcnt[bn], 1);
-    fx_add(hhi + bn, hlo + bn, ms(x));
-  });
-  __syncthreads();
-  char* h = hist + rid * kRowHistBytes;
-  int* gc = reinterpret_cast<int*>(h);
-  u64* ghi = reinterpret_cast<u64*>(h + kBins * sizeof(int));
-  u64* glo = ghi + kBins;
-  for (int j = tid; j < kBins; j += kThreads) {
-    const int c = hcnt[j];
-    if (c != 0) {
-      atomicAdd(&gc[j], c);
-      if (hhi[j]) atomicAdd(&ghi[j], hhi[j]);
-      if (hlo[j]) atomicAdd(&glo[j], hlo[j]);
-    }
-  }
+  flags |= mx == -INFINITY;
 }
 
 // The rows kernel's pass over a row (one workgroup per row) accumulates, per
@@ -898,11 +805,229 @@ __device__ __forceinline__ void row_repass(const float* row, int V, float mx, co
   scan_row(row, V, [&](float x, int v) { row_step<Mode, false>(x, v, mx, ms, -1, lds, st); });
 }
 
+// grid (rows): clears what the slices add into -- the row's counts (and
+// mass chunks for top-p alone), its candidate count and its ticket.
+__global__ __launch_bounds__(kThreads) void sampled_clear_kernel(char* __restrict__ hist,
+                                                                 RowPlan* __restrict__ plans,
+                                                                 int chunks) {
+  const size_t rid = blockIdx.x;
+  uint4* h = reinterpret_cast<uint4*>(hist + rid * kRowHistBytes);
+  const int n16 = static_cast<int>((chunks ? kRowHistBytes : kBins * sizeof(int)) / 16);
+  for (int j = threadIdx.x; j < n16; j += kThreads) h[j] = make_uint4(0u, 0u, 0u, 0u);
+  if (threadIdx.x == 0) {
+    plans[rid].ncand = 0;
+    plans[rid].ticket = 0;
+  }
+}
+
+// A slice's first kChunk entries are loaded (16-byte rows) together with the
+// row's first entries, before the reference is known; the rest of a longer
+// slice is scanned after them.
+constexpr int kChunk4 = 8 * kThreads;           // float4 loads per chunk (16384 entries)
+template <int Mode>
+__device__ __forceinline__ void slice_scan(const float* row, int v0, int n, bool vec,
+                                           const float4* pre, int c4, float ref, const Mass& ms,
+                                           const RowLds& lds, RowScan& st) {
+  if (Mode == kCount || Mode == kCountMass) clear_bins(Mode, lds);
+  int done = 0;
+  if (vec) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = threadIdx.x + u * kThreads;
+      if (j < c4) {
+        const int v = v0 + 4 * j;
+        row_step<Mode, true>(pre[u].x, v, ref, ms, -1, lds, st);
+        row_step<Mode, true>(pre[u].y, v + 1, ref, ms, -1, lds, st);
+        row_step<Mode, true>(pre[u].z, v + 2, ref, ms, -1, lds, st);
+        row_step<Mode, true>(pre[u].w, v + 3, ref, ms, -1, lds, st);
+      }
+    }
+    done = 4 * c4;
+  }
+  scan_span(row + v0 + done, n - done, vec, [&](float x, int v) {
+    row_step<Mode, true>(x, v0 + done + v, ref, ms, -1, lds, st);
+  });
+}
+
+// grid (W, 2k+1, B): one slice's pass against the row's provisional
+// reference (every slice derives the same one from the row's first
+// entries); the last slice of a row to finish merges the slice records and
+// plans the gather of the boundary bins.
+__global__ __launch_bounds__(kThreads) void sampled_slice_pass_kernel(
+    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V, int W, float T,
+    int top_k, float top_p, SlicePart* __restrict__ parts, double* __restrict__ slice_s,
+    char* __restrict__ hist, RowPlan* __restrict__ plans) {
+  __shared__ int hcnt[kBins];
+  __shared__ u64 hhi[kBins], hlo[kBins];
+  __shared__ double dsh[kThreads];
+  __shared__ double etab[kExpTab];
+  __shared__ float fsh[kThreads / 64];
+  __shared__ int ish[kThreads + 1];
+  __shared__ int nc;
+  const int tid = threadIdx.x;
+  const int w = blockIdx.x, rho = blockIdx.y, b = blockIdx.z;
+  const size_t rid = static_cast<size_t>(b) * gridDim.y + rho;
+  const float* row = row_ptr(tgt, dft, b, rho, k, V);
+  exp_table_init(etab);
+  const bool vec = (V & 3) == 0;
+  const int L = slice_len(V, W);
+  const int v0 = w * L;
+  const int n = v0 < V ? min(L, V - v0) : 0;
+  float4 pre[8];
+  const int c4 = vec ? min(n >> 2, kChunk4) : 0;
+  if (c4 > 0) {
+    const float4* r4 = reinterpret_cast<const float4*>(row + v0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) pre[u] = r4[min(static_cast<int>(threadIdx.x) + u * kThreads, c4 - 1)];
+  }
+  const int n0 = min(V, kPeek);
+  float xs[kFirst];
+  int vs[kFirst];
+  load_first(row, n0, vec, xs, vs);
+  float m0 = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kFirst; ++u)
+    if (vs[u] >= 0) m0 = fmaxf(m0, xs[u]);
+  m0 = block_max(m0, fsh);                      // (its barrier also orders the table)
+  const bool fused = m0 > -INFINITY && m0 < INFINITY;
+  const float ref = fused ? m0 + fminf(4.f, 8.f * T) : INFINITY;
+  const bool trunc_k = top_k > 0 && top_k < V;
+  const bool trunc = trunc_k || top_p < 1.f;
+  const int mode = !fused ? kTrack : !trunc ? kSum : trunc_k ? kCount : kCountMass;
+  const Mass ms(etab, ref, T);
+  const RowLds lds = {hcnt, hhi, hlo, nullptr, &nc};
+  RowScan st = {-INFINITY, V, 0, 0, 0.0};
+  if (mode == kTrack)
+    slice_scan<kTrack>(row, v0, n, vec, pre, c4, ref, ms, lds, st);
+  else if (mode == kSum)
+    slice_scan<kSum>(row, v0, n, vec, pre, c4, ref, ms, lds, st);
+  else if (mode == kCount)
+    slice_scan<kCount>(row, v0, n, vec, pre, c4, ref, ms, lds, st);
+  else
+    slice_scan<kCountMass>(row, v0, n, vec, pre, c4, ref, ms, lds, st);
+  const double sl = st.sl;
+  block_argmax(st, fsh, ish);                   // (its barriers also close the bins)
+  if (mode == kSum) {
+    const double s = block_sum(sl, dsh);
+    if (tid == 0) slice_s[rid * W + w] = s;
+  }
+  char* h = hist + rid * kRowHistBytes;
+  int* gc = reinterpret_cast<int*>(h);
+  u64* ghi = reinterpret_cast<u64*>(h + kBins * sizeof(int));
+  u64* glo = ghi + kBins;
+  if (mode == kCount || mode == kCountMass) {
+    for (int j = tid; j < kBins; j += kThreads) {
+      const int c = hcnt[j];
+      if (c != 0) {
+        atomicAdd(&gc[j], c);
+        if (mode == kCountMass) {
+          atomicAdd(&ghi[j], hhi[j]);
+          atomicAdd(&glo[j], hlo[j]);
+        }
+      }
+    }
+  }
+  if (tid == 0) {
+    int* q = reinterpret_cast<int*>(parts + rid * W + w);
+    __hip_atomic_store(q, __float_as_int(st.mx), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, st.am, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 2, st.bad | (st.over << 1) | (fused ? 0 : 4), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // The last slice of the row to finish (device-scope ticket).  Everything
+  // the other slices read -- the records and the bins -- goes through
+  // device-scope stores, atomics and loads, which bypass the compute units'
+  // non-coherent caches; every wave waits for its own to complete, then the
+  // barrier, then the ticket is counted.  (No cache-wide fence: written back
+  // and invalidated by every workgroup, it costs more than the pass.)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) ish[0] = atomicAdd(&plans[rid].ticket, 1);
+  __syncthreads();
+  if (ish[0] != W - 1) return;
+  float mx;
+  int am, rf;
+  merge_slices(parts + rid * W, W, mx, am, rf);
+  int lo = 1, hi = 0;
+  double need = 0.0, above = 0.0;
+  if (rf == 0 && (mode == kCount || mode == kCountMass)) {
+    double* hmass = reinterpret_cast<double*>(hhi);
+    for (int j = tid; j < kBins; j += kThreads) {
+      hcnt[j] = __hip_atomic_load(gc + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (mode == kCountMass)
+        hmass[j] = fx_value(__hip_atomic_load(ghi + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                            __hip_atomic_load(glo + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    }
+    __syncthreads();
+    if (mode == kCount) {
+      int above = 0;
+      const int bk = bins_cross_count(hcnt, top_k, above, ish);
+      if (bk < kBins && above + hcnt[bk] <= kCap) {
+        lo = 0;
+        hi = bk;
+      }
+    } else {
+      need = static_cast<double>(top_p) * sum_before(hmass, kBins, dsh);
+      const int bp = cross_mass(hmass, kBins, need, above, dsh, ish);
+      if (bp < kBins && hcnt[bp] <= kCap) {
+        lo = bp;
+        hi = bp;
+      }
+    }
+  }
+  if (tid == 0) {
+    RowPlan* pl = plans + rid;
+    pl->ref = ref;
+    pl->lo = lo;
+    pl->hi = hi;
+    pl->mx = mx;
+    pl->am = am;
+    pl->flags = rf;
+    pl->need = need;
+    pl->above = above;
+  }
+}
+
+// grid (W, 2k+1, B): the tokens of the planned bins in one slice, added to
+// the row's candidate list (one reservation of list slots per slice).
+__global__ __launch_bounds__(kThreads) void sampled_slice_gather_kernel(
+    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V, int W,
+    RowPlan* __restrict__ plans, unsigned long long* __restrict__ gcand) {
+  __shared__ unsigned long long lc[kCap];
+  __shared__ int ln, base;
+  const int tid = threadIdx.x;
+  const int w = blockIdx.x, rho = blockIdx.y, b = blockIdx.z;
+  const size_t rid = static_cast<size_t>(b) * gridDim.y + rho;
+  const int lo = plans[rid].lo, hi = plans[rid].hi;
+  if (lo > hi) return;
+  const float ref = plans[rid].ref;
+  const float* row = row_ptr(tgt, dft, b, rho, k, V);
+  const int L = slice_len(V, W);
+  const int v0 = w * L;
+  const int n = v0 < V ? min(L, V - v0) : 0;
+  if (tid == 0) ln = 0;
+  __syncthreads();
+  scan_span(row + v0, n, (V & 3) == 0, [&](float x, int v) {
+    const int bn = bin_of(x, ref);
+    if (bn >= lo && bn <= hi) {
+      const int slot = atomicAdd(&ln, 1);
+      if (slot < kCap) lc[slot] = cand_key(x, v0 + v);
+    }
+  });
+  __syncthreads();
+  const int m = ln;
+  if (tid == 0) base = m > 0 ? atomicAdd(&plans[rid].ncand, m) : 0;
+  __syncthreads();
+  const int b0 = base;
+  if (m <= kCap)
+    for (int j = tid; j < m && b0 + j < kCap; j += kThreads) gcand[rid * kCap + b0 + j] = lc[j];
+}
+
 __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
     const float* __restrict__ tgt, const float* __restrict__ dft, const int32_t* __restrict__ toks,
     int k, int V, float temperature, int top_k, float top_p, int W,
-    const SlicePart* __restrict__ parts, const double* __restrict__ slice_s,
-    const char* __restrict__ hist, SampledRow* __restrict__ rows) {
+    const double* __restrict__ slice_s, const RowPlan* __restrict__ plans,
+    const unsigned long long* __restrict__ gcand, SampledRow* __restrict__ rows) {
   __shared__ double dsh[kThreads];
   __shared__ double above_sh;
   __shared__ int ish[kThreads + 1];
@@ -951,9 +1076,20 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
   float mref = -INFINITY;
   double sl = 0.0;
   int bhat = -1;
+  bool local = true;                            // the bins (or mass) are this workgroup's
+  bool redo = false;                            // a pass against the row maximum
   if (W > 1) {
-    merge_slices(parts + rid * W, W, mx, am, bad);
-    mref = mx;
+    const int rf = plans[rid].flags;
+    mx = plans[rid].mx;
+    am = plans[rid].am;
+    bad = rf & 1;
+    // a logit above the slices' reference (or none usable): this
+    // workgroup's own pass
+    redo = !bad && (rf & 6);
+    if (!redo) {
+      mref = plans[rid].ref;
+      local = false;
+    }
     __syncthreads();                            // (the table)
   } else {
     const bool vec = (V & 3) == 0;
@@ -987,24 +1123,26 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
     mx = st.mx;
     am = st.am;
     bad = st.bad | (mx == -INFINITY);
-    if (!bad && (!fused || st.over)) {
-      mref = mx;
-      bhat = -1;
-      const Mass ms2(etab, mx, T);
-      RowScan s2 = {-INFINITY, V, 0, 0, 0.0};
-      if (mode == kSum)
-        row_repass<kSum>(row, V, mx, ms2, lds, s2);
-      else if (mode == kCount)
-        row_repass<kCount>(row, V, mx, ms2, lds, s2);
-      else
-        row_repass<kCountMass>(row, V, mx, ms2, lds, s2);
-      sl = s2.sl;
-    } else {
+    redo = !bad && (!fused || st.over);
+    if (!redo) {
       mref = ref;
       sl = sl1;
     }
-    __syncthreads();
   }
+  if (redo) {
+    mref = mx;
+    bhat = -1;
+    const Mass ms2(etab, mx, T);
+    RowScan s2 = {-INFINITY, V, 0, 0, 0.0};
+    if (mode == kSum)
+      row_repass<kSum>(row, V, mx, ms2, lds, s2);
+    else if (mode == kCount)
+      row_repass<kCount>(row, V, mx, ms2, lds, s2);
+    else
+      row_repass<kCountMass>(row, V, mx, ms2, lds, s2);
+    sl = s2.sl;
+  }
+  __syncthreads();
   out.m = mref;
   out.argmax = am;
   out.status = bad ? 2 : 0;
@@ -1021,49 +1159,59 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
 
   double s = 0.0;                               // kept mass
   if (!trunc) {
-    if (W > 1) {
+    if (!local) {
       for (int w = 0; w < W; ++w) s += slice_s[rid * W + w];
     } else {
       s = block_sum(sl, dsh);
     }
   } else {
-    // bins of 1/32 logit below mref (monotone in the logit): counts, and for
-    // top-p alone binary64 masses
-    if (W > 1) {
-      const char* h = hist + rid * kRowHistBytes;
-      for (int j = tid; j < kBins; j += kThreads) hcnt[j] = reinterpret_cast<const int*>(h)[j];
-      if (!trunc_k) {
-        const u64* ghi = reinterpret_cast<const u64*>(h + kBins * sizeof(int));
-        for (int j = tid; j < kBins; j += kThreads)
-          hmass[j] = fx_value(ghi[j], ghi[kBins + j]);
+    // the top tokens, sorted (decreasing logit, increasing index): for top-k
+    // every token of the bins down to the one where the count reaches top_k
+    // (bin bk); for top-p alone the tokens of the bin where the mass reaches
+    // need = top_p S (bin bp), after `above` in the bins before it
+    int n = -1, bk = kBins, bp = kBins;
+    double need = 0.0, above = 0.0;
+    if (!local) {
+      // W > 1: the slices' plan and gathered list
+      const RowPlan& pl = plans[rid];
+      if (pl.lo <= pl.hi && pl.ncand <= kCap) {
+        n = pl.ncand;
+        for (int j = tid; j < n; j += kThreads) cand[j] = gcand[rid * kCap + j];
+        sort_cand(cand, n);
+        bk = pl.hi;
+        bp = pl.lo;
+        need = pl.need;
+        above = pl.above;
       }
-    } else if (!trunc_k) {
-      for (int j = tid; j < kBins; j += kThreads)
-        hmass[j] = fx_value(lds.hhi[j], lds.hlo[j]);
-    }
-    __syncthreads();
-    bool exact = false;
-    if (trunc_k) {
-      // the top_k tokens, sorted: from the list the pass made when it reaches
-      // the boundary bin, else gathered by a second read of the bins down to it
-      int above = 0;
-      const int bk = bins_cross_count(hcnt, top_k, above, ish);
-      int n = -1;
+    } else if (trunc_k) {
+      // from the list the pass made when it reaches bin bk, else by a second
+      // read of the bins down to it
+      int cnt_above = 0;
+      bk = bins_cross_count(hcnt, top_k, cnt_above, ish);
       if (bhat >= 0 && bk <= bhat && ncand <= kCap) {
         n = ncand;
         sort_cand(cand, n);
-      } else if (bk < kBins && above + hcnt[bk] <= kCap) {
+      } else if (bk < kBins && cnt_above + hcnt[bk] <= kCap) {
         n = gather_bins(row, V, mref, 0, bk, cand, ish);
       }
+    } else {
+      for (int j = tid; j < kBins; j += kThreads) hmass[j] = fx_value(lds.hhi[j], lds.hlo[j]);
+      __syncthreads();
+      need = static_cast<double>(top_p) * sum_before(hmass, kBins, dsh);
+      bp = cross_mass(hmass, kBins, need, above, dsh, ish);
+      if (bp < kBins) n = gather_bins(row, V, mref, bp, bp, cand, ish);
+    }
+    bool exact = false;
+    if (trunc_k) {
       exact = n >= top_k;
       if (exact) {
         cand_masses(cand, top_k, ms, cmass);
         int r = top_k;                          // tokens kept
         if (trunc_p) {
           // top-p on the renormalised top-k row
-          const double need = static_cast<double>(top_p) * sum_before(cmass, top_k, dsh);
+          const double need_k = static_cast<double>(top_p) * sum_before(cmass, top_k, dsh);
           double before = 0.0;
-          const int j = cross_mass(cmass, top_k, need, before, dsh, ish);
+          const int j = cross_mass(cmass, top_k, need_k, before, dsh, ish);
           r = j < top_k ? j + 1 : top_k;
         }
         tau = static_cast<unsigned int>(cand[r - 1] >> 32);
@@ -1071,10 +1219,6 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
         s = sum_before(cmass, r, dsh);
       }
     } else {
-      const double need = static_cast<double>(top_p) * sum_before(hmass, kBins, dsh);
-      double above = 0.0;
-      const int bp = cross_mass(hmass, kBins, need, above, dsh, ish);
-      const int n = bp < kBins ? gather_bins(row, V, mref, bp, bp, cand, ish) : -1;
       exact = n > 0;
       if (exact) {
         cand_masses(cand, n, ms, cmass);
@@ -1083,7 +1227,7 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
         const int r = j < n ? j + 1 : n;        // tokens kept from the boundary bin
         tau = static_cast<unsigned int>(cand[r - 1] >> 32);
         tie = static_cast<int>(~static_cast<unsigned int>(cand[r - 1]));
-        s = sum_before(hmass, bp, dsh) + sum_before(cmass, r, dsh);
+        s = above + sum_before(cmass, r, dsh);
       }
     }
     if (!exact) {
@@ -1398,19 +1542,19 @@ __global__ __launch_bounds__(kThreads) void sampled_select_kernel(
 namespace {
 // Slices per row: enough workgroups to cover the chip when a call has fewer
 // rows than compute units and rows are long; else one workgroup per row.
-// (up to four 512-thread workgroups per compute unit, which one round of the
-// chip holds; slices of 2048 tokens at least).
+// (Three slice workgroups fit a compute unit (their LDS), so 768 fill one
+// round of the chip; slices of 2048 tokens at least.)
 int row_slices(int B, int k, int V) {
   const long long rows = static_cast<long long>(B) * (2 * k + 1);
   if (rows >= 256 || V < 16384) return 1;
-  long long w = 1024 / rows;
+  long long w = 768 / rows;
   if (w > kMaxSlices) w = kMaxSlices;
   if (w > V / 2048) w = V / 2048;
   return static_cast<int>(w);
 }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 struct SampledWs {
-  size_t rows_off, dec_off, tot_off, part_off, ss_off, hist_off, bytes;
+  size_t rows_off, dec_off, tot_off, part_off, ss_off, hist_off, plan_off, cand_off, bytes;
   int W;
 };
 SampledWs sampled_ws(int B, int k, int V) {
@@ -1421,12 +1565,14 @@ SampledWs sampled_ws(int B, int k, int V) {
   w.dec_off = align256(nrow * sizeof(SampledRow));
   w.tot_off = align256(w.dec_off + static_cast<size_t>(B) * sizeof(SampledDecision));
   w.bytes = w.tot_off + static_cast<size_t>(B) * 2 * res_blocks(V) * sizeof(double);
-  w.part_off = w.ss_off = w.hist_off = 0;
+  w.part_off = w.ss_off = w.hist_off = w.plan_off = w.cand_off = 0;
   if (w.W > 1) {
     w.part_off = align256(w.bytes);
     w.ss_off = align256(w.part_off + nrow * w.W * sizeof(SlicePart));
     w.hist_off = align256(w.ss_off + nrow * w.W * sizeof(double));
-    w.bytes = w.hist_off + nrow * kRowHistBytes;
+    w.plan_off = align256(w.hist_off + nrow * kRowHistBytes);
+    w.cand_off = align256(w.plan_off + nrow * sizeof(RowPlan));
+    w.bytes = w.cand_off + nrow * kCap * sizeof(unsigned long long);
   }
   // temperature 0 runs as a chain tree, whose span partials share the space
   const size_t chain = sv_greedy_chain_workspace_bytes(B, k, V);
@@ -1478,19 +1624,27 @@ extern "C" sv_status sv_verify_sampled(const float* target_logits, const float* 
   SlicePart* parts = reinterpret_cast<SlicePart*>(ws + L.part_off);
   double* slice_s = reinterpret_cast<double*>(ws + L.ss_off);
   char* hist = ws + L.hist_off;
+  RowPlan* plans = reinterpret_cast<RowPlan*>(ws + L.plan_off);
+  unsigned long long* gcand = reinterpret_cast<unsigned long long*>(ws + L.cand_off);
   if (L.W > 1) {
-    const int trunc = (sampling->top_k > 0 && sampling->top_k < V) || sampling->top_p < 1.f;
-    hipLaunchKernelGGL(sampled_slice_max_kernel, dim3(L.W, 2 * k + 1, B), dim3(kThreads), 0,
-                       stream, target_logits, draft_logits, k, V, L.W, parts, hist);
+    // mass chunks only for top-p alone
+    const int chunks = !(sampling->top_k > 0 && sampling->top_k < V) && sampling->top_p < 1.f;
+    hipLaunchKernelGGL(sampled_clear_kernel, dim3(B * (2 * k + 1)), dim3(kThreads), 0, stream,
+                       hist, plans, chunks);
     SV_LAUNCH_CHECK();
-    hipLaunchKernelGGL(sampled_slice_bins_kernel, dim3(L.W, 2 * k + 1, B), dim3(kThreads), 0,
-                       stream, target_logits, draft_logits, k, V, L.W, T, trunc, parts, slice_s,
-                       hist);
+    hipLaunchKernelGGL(sampled_slice_pass_kernel, dim3(L.W, 2 * k + 1, B), dim3(kThreads), 0,
+                       stream, target_logits, draft_logits, k, V, L.W, T, sampling->top_k,
+                       sampling->top_p, parts, slice_s, hist, plans);
     SV_LAUNCH_CHECK();
+    if (chunks || (sampling->top_k > 0 && sampling->top_k < V)) {
+      hipLaunchKernelGGL(sampled_slice_gather_kernel, dim3(L.W, 2 * k + 1, B), dim3(kThreads),
+                         0, stream, target_logits, draft_logits, k, V, L.W, plans, gcand);
+      SV_LAUNCH_CHECK();
+    }
   }
   hipLaunchKernelGGL(sampled_rows_kernel, dim3(2 * k + 1, B), dim3(kThreads), 0, stream,
                      target_logits, draft_logits, draft_tokens, k, V, T, sampling->top_k,
-                     sampling->top_p, L.W, parts, slice_s, hist, rows);
+                     sampling->top_p, L.W, slice_s, plans, gcand, rows);
   SV_LAUNCH_CHECK();
   hipLaunchKernelGGL(sampled_decide_kernel, dim3(B), dim3(kThreads), 0, stream, draft_tokens, k,
                      V, rows, static_cast<unsigned int>(seed & 0xFFFFFFFFu),
