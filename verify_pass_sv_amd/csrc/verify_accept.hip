@@ -38,6 +38,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 namespace {
 
@@ -85,6 +86,14 @@ __device__ __forceinline__ int quad_or(int v) {
   v |= dpp_quad<kDppXor1>(v);
   return v | dpp_quad<kDppXor2>(v);
 }
+// The same over the 2 lanes of a pair (the permute [1,0,3,2] alone).
+__device__ __forceinline__ float pair_max(float v) {
+  return fmaxf(v, __int_as_float(dpp_quad<kDppXor1>(__float_as_int(v))));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  return v + __int_as_float(dpp_quad<kDppXor1>(__float_as_int(v)));
+}
+__device__ __forceinline__ int pair_or(int v) { return v | dpp_quad<kDppXor1>(v); }
 
 // Online softmax statistics: running max m and sum s of exp(v - m).
 __device__ __forceinline__ void stat_add4(float& m, float& s, int& bad, float4 v) {
@@ -309,33 +318,55 @@ __device__ __forceinline__ float resid_weight(float tl, float lt, float dl, floa
   return fmaxf(0.f, p - q);
 }
 
-// Stages block `blk` of the residual rows (target row pt, draft row pd) into
-// LDS: every thread issues its 2 x 8 coalesced loads before storing any.
-__device__ __forceinline__ void stage_block(const float* pt, const float* pd, int V, int blk,
-                                            float* st, float* sd) {
-  const int lo = blk * kBlk;
-  float a[kPerThread], d[kPerThread];
+// One thread's kPerThread consecutive entries a .. a+7 of the residual rows
+// (target row pt, draft row pd): two 16-byte loads per row when the entries
+// are whole and aligned, else one guarded load each; entries past V read as
+// -inf (weight 0) and are never counted.
+__device__ __forceinline__ void load_entries(const float* pt, const float* pd, int V, int a,
+                                             float* t, float* d) {
+  if ((V & 3) == 0 && a + kPerThread <= V) {
+    const float4* t4 = reinterpret_cast<const float4*>(pt + a);
+    const float4 t0 = t4[0], t1 = t4[1];
+    t[0] = t0.x; t[1] = t0.y; t[2] = t0.z; t[3] = t0.w;
+    t[4] = t1.x; t[5] = t1.y; t[6] = t1.z; t[7] = t1.w;
+    if (pd != nullptr) {
+      const float4* d4 = reinterpret_cast<const float4*>(pd + a);
+      const float4 d0 = d4[0], d1 = d4[1];
+      d[0] = d0.x; d[1] = d0.y; d[2] = d0.z; d[3] = d0.w;
+      d[4] = d1.x; d[5] = d1.y; d[6] = d1.z; d[7] = d1.w;
+    } else {
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const int e = lo + i * kThreads + threadIdx.x;
-    a[i] = e < V ? pt[e] : -INFINITY;
-    d[i] = (pd != nullptr && e < V) ? pd[e] : -INFINITY;
-  }
+      for (int i = 0; i < kPerThread; ++i) d[i] = -INFINITY;
+    }
+  } else {
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    st[i * kThreads + threadIdx.x] = a[i];
-    sd[i * kThreads + threadIdx.x] = d[i];
+    for (int i = 0; i < kPerThread; ++i) {
+      const int e = a + i;
+      t[i] = e < V ? pt[e] : -INFINITY;
+      d[i] = (pd != nullptr && e < V) ? pd[e] : -INFINITY;
+    }
   }
 }
 
-// Sum of this thread's 8 consecutive weights of the staged block, in order.
-__device__ __forceinline__ double thread_sum(const float* st, const float* sd, int n_valid,
-                                             float lt, float ld, bool bonus) {
+// Sum of this thread's 8 consecutive weights w of block blk, in order
+// (entries past V not counted).
+__device__ __forceinline__ double thread_sum(const float* pt, const float* pd, int V, int blk,
+                                             float lt, float ld, bool bonus, float* w) {
+  const int a = blk * kBlk + threadIdx.x * kPerThread;
+  float t[kPerThread], d[kPerThread];
+  load_entries(pt, pd, V, a, t, d);
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) w[i] = resid_weight(t[i], lt, d[i], ld, bonus);
   double acc = 0.0;
-  const int a = threadIdx.x * kPerThread;
-  for (int v = a; v < a + kPerThread && v < n_valid; ++v)
-    acc += static_cast<double>(resid_weight(st[v], lt, sd[v], ld, bonus));
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i)
+    if (a + i < V) acc += static_cast<double>(w[i]);
   return acc;
+}
+__device__ __forceinline__ double thread_sum(const float* pt, const float* pd, int V, int blk,
+                                             float lt, float ld, bool bonus) {
+  float w[kPerThread];
+  return thread_sum(pt, pd, V, blk, lt, ld, bonus, w);
 }
 
 // Group sums (16 consecutive threads, in order) and the block total (groups
@@ -358,8 +389,8 @@ __device__ __forceinline__ void block_sums(const double* tsum, double* gsum, dou
 __device__ void select_trial(const float* __restrict__ tgt, const float* __restrict__ dft, int k,
                              int V, int b, const Decision dec,
                              const double* __restrict__ totals,
-                             int32_t* __restrict__ out_tokens, float* st, float* sd,
-                             double* tsum, double* gsum, double* btot_p, double* dyn_tot);
+                             int32_t* __restrict__ out_tokens, double* tsum, double* gsum,
+                             double* btot_p, double* dyn_tot);
 
 // ---- kernel 2: decide + residual block totals + select-----------------------------
 // Every workgroup of a trial merges the trial's statistics and takes the same
@@ -380,7 +411,6 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
   __shared__ float lse_sh[2 * SV_MAX_ROWS + 1];
   __shared__ int bad_sh[2 * SV_MAX_ROWS + 1];
   __shared__ Decision dec;
-  __shared__ float st[kBlk], sd[kBlk];
   __shared__ double tsum[kThreads];
   __shared__ double gsum[kGroups];
   __shared__ double btot;
@@ -423,36 +453,43 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
   //    round of the workgroup, lane sub taking partials sub, sub + 4, ..; the
   //    row maximum first, then the sum rescaled to it, each combined over the
   //    quad in a fixed order
-  {
-    const int sub = tid & 3;
-    for (int j0 = 0; j0 < R; j0 += kThreads / 4) {
-      const int j = j0 + (tid >> 2);
+  // (2 lanes per row when there are more rows than quads, so that every row
+  // is merged in one round)
+  auto merge_rows = [&](auto lanes_c) {
+    constexpr int kL = decltype(lanes_c)::value;
+    const int sub = tid & (kL - 1);
+    for (int j0 = 0; j0 < R; j0 += kThreads / kL) {
+      const int j = j0 + tid / kL;
       const bool own = j < R;
       float m = -INFINITY;
       int bad = 0;
       if (own) {
 #pragma unroll 5
-        for (int i = sub; i < CG; i += 4) {
+        for (int i = sub; i < CG; i += kL) {
           m = fmaxf(m, pm[j * CG + i]);
           bad |= pb[j * CG + i];
         }
       }
-      m = quad_max(m);
-      bad = quad_or(bad);
+      m = kL == 4 ? quad_max(m) : pair_max(m);
+      bad = kL == 4 ? quad_or(bad) : pair_or(bad);
       float sum = 0.f;
       if (own && m != -INFINITY) {
 #pragma unroll 5
-        for (int i = sub; i < CG; i += 4)
+        for (int i = sub; i < CG; i += kL)
           sum += ps[j * CG + i] * exp2_fast((pm[j * CG + i] - m) * kLog2e);
       }
-      sum = quad_sum(sum);
+      sum = kL == 4 ? quad_sum(sum) : pair_sum(sum);
       if (own && sub == 0) {
         const int bd = bad | (m == -INFINITY) | !(sum > 0.f);
         lse_sh[j] = bd ? NAN : m + logf(sum);
         bad_sh[j] = bd;
       }
     }
-  }
+  };
+  if (R <= kThreads / 4)
+    merge_rows(std::integral_constant<int, 4>{});
+  else
+    merge_rows(std::integral_constant<int, 2>{});
   __syncthreads();
 
   // 3. decisions (wave 0): accept iff u_i q_i(d_i) < p_i(d_i), first rejection
@@ -495,8 +532,10 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
         if (p_at) p_at[static_cast<size_t>(b) * k + i] = status == 0 ? p : NAN;
         if (q_at) q_at[static_cast<size_t>(b) * k + i] = status == 0 ? q : NAN;
       }
-      if (i <= k) {
-        // accepted drafts; position n_acc is written by the selection
+      if (i <= k && !(status == 0 && i == n_acc)) {
+        // accepted drafts, -1 after them; position n_acc is left to the
+        // selection (two workgroups writing one word would race: their
+        // caches are written back in either order)
         const bool keep = status == 0 && i < n_acc;
         out_tokens[static_cast<size_t>(b) * (k + 1) + i] = keep ? tok : -1;
       }
@@ -517,37 +556,34 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
   const int b0 = static_cast<int>(static_cast<long long>(nb) * c / C2);
   const int b1 = static_cast<int>(static_cast<long long>(nb) * (c + 1) / C2);
   double* tot = totals + static_cast<size_t>(b) * nb;
-  if (dec.status != 0) {
-    for (int blk = b0 + tid; blk < b1; blk += kThreads) tot[blk] = 0.0;
-    return;
-  }
+  if (dec.status != 0) return;
   const int r = dec.n_acc;
   const bool bonus = r == k;
   const float* pt = tgt + (static_cast<size_t>(b) * (k + 1) + r) * V;
   const float* pd = bonus ? nullptr : dft + (static_cast<size_t>(b) * k + r) * V;
   for (int blk = b0; blk < b1; ++blk) {
-    stage_block(pt, pd, V, blk, st, sd);
-    __syncthreads();
-    tsum[tid] = thread_sum(st, sd, min(kBlk, V - blk * kBlk), dec.lse_t, dec.lse_d, bonus);
+    tsum[tid] = thread_sum(pt, pd, V, blk, dec.lse_t, dec.lse_d, bonus);
     __syncthreads();
     block_sums(tsum, gsum, &btot);
-    if (tid == 0) tot[blk] = btot;
+    if (tid == 0)
+      __hip_atomic_store(reinterpret_cast<unsigned long long*>(tot + blk),
+                         static_cast<unsigned long long>(__double_as_longlong(btot)),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // The last workgroup of the trial to finish (device-scope counter, zeroed
-  // by kernel 1 of this call) selects the token: release the block totals
-  // before counting, acquire them after seeing the final count.
+  // by kernel 1 of this call) selects the token.  The block totals go
+  // through device-scope stores and loads, which bypass the compute units'
+  // non-coherent caches: each wave waits for its own to complete, then the
+  // barrier, then the count.
   __shared__ int is_last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    is_last = atomicAdd(&done[b], 1) == C2 - 1;
-    if (is_last) __threadfence();
-  }
+  if (tid == 0) is_last = atomicAdd(&done[b], 1) == C2 - 1;
   __syncthreads();
   if (!is_last) return;
   extern __shared__ double dyn_tot[];   // resid_blocks(V) doubles
-  select_trial(tgt, dft, k, V, b, dec, totals, out_tokens, st, sd, tsum, gsum, &btot, dyn_tot);
+  select_trial(tgt, dft, k, V, b, dec, totals, out_tokens, tsum, gsum, &btot, dyn_tot);
 }
 
 // ---- select the replacement / bonus token ------------------------------------
@@ -558,10 +594,10 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
 __device__ void select_trial(const float* __restrict__ tgt, const float* __restrict__ dft, int k,
                              int V, int b, const Decision dec,
                              const double* __restrict__ totals,
-                             int32_t* __restrict__ out_tokens, float* st, float* sd,
-                             double* tsum, double* gsum, double* btot_p, double* dyn_tot) {
-  __shared__ double sh_S, sh_pc, sh_thr;
-  __shared__ int sh_blk;
+                             int32_t* __restrict__ out_tokens, double* tsum, double* gsum,
+                             double* btot_p, double* dyn_tot) {
+  __shared__ double sh_S, sh_pc, sh_thr, sh_q[2];
+  __shared__ int sh_blk, sh_ts;
   double& btot = *btot_p;
   const int tid = threadIdx.x;
   const int r = dec.n_acc;
@@ -569,34 +605,38 @@ __device__ void select_trial(const float* __restrict__ tgt, const float* __restr
   const float* pd = r < k ? dft + (static_cast<size_t>(b) * k + r) * V : nullptr;
   bool bonus = r == k;
   const int nb = resid_blocks(V);
-  const double* T = totals + static_cast<size_t>(b) * nb;
+  const unsigned long long* T =
+      reinterpret_cast<const unsigned long long*>(totals + static_cast<size_t>(b) * nb);
 
   // Block totals -> LDS (dyn_tot), then replaced in place by their running
-  // sums in vocabulary order.  Thread 0 adds them one after another, exactly
-  // the additions of a sequential walk, with its LDS loads batched 8 at a time.
+  // sums in vocabulary order: wave 0, lane l adding a contiguous range of
+  // blocks after the exclusive running sum of the ranges before it (one
+  // fixed association).
   auto running_sums = [&]() {
-    if (tid == 0) {
-      double P = 0.0;
-      int i = 0;
-      for (; i + 8 <= nb; i += 8) {
-        double t8[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) t8[u] = dyn_tot[i + u];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          P += t8[u];
-          dyn_tot[i + u] = P;
-        }
+    if (tid < 64) {
+      const int per = (nb + 63) / 64;
+      const int i0 = min(nb, tid * per), i1 = min(nb, i0 + per);
+      double c = 0.0;
+      for (int i = i0; i < i1; ++i) c += dyn_tot[i];
+      double incl = c;
+      for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(incl, o, 64);
+        if (tid >= o) incl += y;
       }
-      for (; i < nb; ++i) {
-        P += dyn_tot[i];
-        dyn_tot[i] = P;
+      double run = __shfl_up(incl, 1, 64);
+      if (tid == 0) run = 0.0;
+      for (int i = i0; i < i1; ++i) {
+        run += dyn_tot[i];
+        dyn_tot[i] = run;
       }
-      sh_S = P;
+      const double S = __shfl(incl, 63, 64);
+      if (tid == 0) sh_S = S;
     }
     __syncthreads();
   };
-  for (int i = tid; i < nb; i += kThreads) dyn_tot[i] = T[i];
+  for (int i = tid; i < nb; i += kThreads)
+    dyn_tot[i] = __longlong_as_double(static_cast<long long>(
+        __hip_atomic_load(T + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
   __syncthreads();
   running_sums();
   // Rounding left no residual mass: sample from p_r instead, with block
@@ -606,9 +646,7 @@ __device__ void select_trial(const float* __restrict__ tgt, const float* __restr
     bonus = true;
     pd = nullptr;
     for (int blk = 0; blk < nb; ++blk) {
-      stage_block(pt, pd, V, blk, st, sd);
-      __syncthreads();
-      tsum[tid] = thread_sum(st, sd, min(kBlk, V - blk * kBlk), dec.lse_t, dec.lse_d, true);
+      tsum[tid] = thread_sum(pt, pd, V, blk, dec.lse_t, dec.lse_d, true);
       __syncthreads();
       block_sums(tsum, gsum, &btot);
       if (tid == 0) dyn_tot[blk] = btot;
@@ -640,20 +678,16 @@ __device__ void select_trial(const float* __restrict__ tgt, const float* __restr
   __syncthreads();
   const double thr = sh_thr, pc = sh_pc;
   const int blk = sh_blk;
-  const int n_valid = min(kBlk, V - blk * kBlk);
-  stage_block(pt, pd, V, blk, st, sd);
-  __syncthreads();
-  tsum[tid] = thread_sum(st, sd, n_valid, dec.lse_t, dec.lse_d, bonus);
+  float w[kPerThread];                          // kept for the replay below
+  tsum[tid] = thread_sum(pt, pd, V, blk, dec.lse_t, dec.lse_d, bonus, w);
   __syncthreads();
   block_sums(tsum, gsum, &btot);
+  // groups, then threads inside the group (thread 0, on sums held in
+  // registers); every comparison is pc + (group prefix + (thread prefix +
+  // run)), the association under which the block total was formed
+  double qg = 0.0, qt = 0.0;
   if (tid == 0) {
-    // groups, then threads inside the group, then the thread's 8 entries;
-    // every comparison is pc + (group prefix + (thread prefix + run)), the
-    // association under which the block total was formed.  The sums of a
-    // level are read into registers first; the walk stops updating at the
-    // first crossing.
     int gs = kGroups - 1;
-    double qg = 0.0;
     {
       double gv[kGroups];
 #pragma unroll
@@ -675,7 +709,6 @@ __device__ void select_trial(const float* __restrict__ tgt, const float* __restr
       }
     }
     int ts = gs * kGroupThreads + kGroupThreads - 1;
-    double qt = 0.0;
     {
       double tv[kGroupThreads];
 #pragma unroll
@@ -696,20 +729,29 @@ __device__ void select_trial(const float* __restrict__ tgt, const float* __restr
         }
       }
     }
-    const int a = ts * kPerThread;
+    sh_ts = ts;
+    sh_q[0] = qg;
+    sh_q[1] = qt;
+  }
+  __syncthreads();
+  // the chosen thread runs through its own 8 weights in order (the values
+  // its sum was formed from)
+  if (tid == sh_ts) {
+    const int a = blk * kBlk + tid * kPerThread;
+    const double qg2 = sh_q[0], qt2 = sh_q[1];
     int tok = -1, last_pos = -1;
     double run = 0.0;
-    for (int v = a; v < a + kPerThread && v < n_valid; ++v) {
-      const float w = resid_weight(st[v], dec.lse_t, sd[v], dec.lse_d, bonus);
-      run += static_cast<double>(w);
-      if (w > 0.f) last_pos = v;
-      if (pc + (qg + (qt + run)) > thr) {
-        tok = v;
+    for (int i = 0; i < kPerThread && a + i < V; ++i) {
+      const double wi = static_cast<double>(w[i]);
+      run += wi;
+      if (wi > 0.0) last_pos = a + i;
+      if (pc + (qg2 + (qt2 + run)) > thr) {
+        tok = a + i;
         break;
       }
     }
-    if (tok < 0) tok = last_pos >= 0 ? last_pos : min(a, n_valid - 1);
-    out_tokens[static_cast<size_t>(b) * (k + 1) + r] = blk * kBlk + tok;
+    if (tok < 0) tok = last_pos >= 0 ? last_pos : min(a, V - 1);
+    out_tokens[static_cast<size_t>(b) * (k + 1) + r] = tok;
   }
 }
 
