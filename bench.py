@@ -331,8 +331,10 @@ def main():
                     help="B of --profile-accept and --profile-verify")
     ap.add_argument("--profile-verify", choices=("sampled", "coupled", "tree"),
                     help="copy kernel + eager calls of one verification rule "
-                         "(V=152000; sampled at T=0.7, top-p 0.9; tree with --k nodes), "
+                         "(V=152000; sampled at --sampling; tree with --k nodes), "
                          "then exit")
+    ap.add_argument("--sampling", default="0.7,0,0.9",
+                    help="temperature,top_k,top_p of --profile-verify sampled")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
@@ -382,7 +384,9 @@ def main():
             if rule == "sampled":
                 ws = torch.empty(max(16, sv.sv_verify_sampled_workspace_bytes(B, k, VOCAB)),
                                  dtype=torch.uint8, device=dev)
-                call = lambda i: sv.sv_verify_sampled(t, d, tk, i, 0, 0.7, 0, 0.9, out=out,
+                temp, top_k, top_p = args.sampling.split(",")
+                setting = (float(temp), int(top_k), float(top_p))
+                call = lambda i: sv.sv_verify_sampled(t, d, tk, i, 0, *setting, out=out,
                                                       workspace=ws)
             else:
                 ws = torch.empty(max(16, sv.sv_verify_coupled_workspace_bytes(B, k, VOCAB)),
