@@ -625,8 +625,9 @@ __device__ __forceinline__ void merge_slices(const SlicePart* part, int W, float
 // setting: the whole mass (no truncation); bin counts (top-k, with or
 // without top-p: every mass that it needs comes from the gathered top
 // tokens); bin counts and masses (top-p alone); or nothing (the maximum,
-// argmax and validity alone, before a second pass).
-enum RowMode { kSum, kCount, kCountMass, kTrack };
+// argmax and validity alone, before a second pass).  kList (top-k, once a
+// bin bhat is predicted) only lists the tokens of bins <= bhat.
+enum RowMode { kSum, kCount, kCountMass, kTrack, kList };
 
 struct RowScan {                    // one thread's share of the pass
   float mx;                         // maximum seen, first at index am
@@ -664,6 +665,10 @@ __device__ __forceinline__ void row_step(float x, int v, float ref, const Mass& 
       const int slot = atomicAdd(lds.ncand, 1);
       if (slot < kCap) lds.cand[slot] = cand_key(x, v);
     }
+  }
+  if (Mode == kList && bin_of(x, ref) <= bhat) {
+    const int slot = atomicAdd(lds.ncand, 1);
+    if (slot < kCap) lds.cand[slot] = cand_key(x, v);
   }
 }
 
@@ -765,8 +770,9 @@ __device__ void block_argmax(RowScan& st, float* fsh, int* ish) {
 // The pass against the provisional reference ref, starting from the first
 // entries held in registers.  With spec > 0 (top-k), once those entries are
 // counted, bhat becomes the first bin where their count reaches spec, and
-// the pass lists every token of bins <= bhat as it goes; returns bhat (-1
-// when nothing is listed).
+// the rest of the pass only lists every token of bins <= bhat (the counts
+// then hold the first entries alone); returns bhat (-1 when nothing is
+// listed, and the counts are whole).
 template <int Mode>
 __device__ __forceinline__ int row_pass(const float* row, int V, int n0, bool vec, const float* xs, const int* vs,
                         float ref, const Mass& ms, int spec, const RowLds& lds, RowScan& st,
@@ -791,18 +797,27 @@ __device__ __forceinline__ int row_pass(const float* row, int V, int n0, bool ve
       }
     }
   }
-  scan_span(row + n0, V - n0, vec, [&](float x, int v) {
-    row_step<Mode, true>(x, v + n0, ref, ms, bhat, lds, st);
-  });
+  if (Mode == kCount && bhat >= 0)
+    scan_span(row + n0, V - n0, vec, [&](float x, int v) {
+      row_step<kList, true>(x, v + n0, ref, ms, bhat, lds, st);
+    });
+  else
+    scan_span(row + n0, V - n0, vec, [&](float x, int v) {
+      row_step<Mode, true>(x, v + n0, ref, ms, bhat, lds, st);
+    });
   return bhat;
 }
 
-// A second pass over the whole row against its maximum.
+// A further pass over the whole row against the reference mx (a rare path:
+// out of line, its arguments by value so that the callers' copies stay in
+// registers); returns the pass's mass (kSum).
 template <int Mode>
-__device__ __forceinline__ void row_repass(const float* row, int V, float mx, const Mass& ms, const RowLds& lds,
-                           RowScan& st) {
+__device__ __noinline__ double row_repass(const float* row, int V, float mx, Mass ms,
+                                          RowLds lds) {
   if (Mode != kSum) clear_bins(Mode, lds);
+  RowScan st = {-INFINITY, V, 0, 0, 0.0};
   scan_row(row, V, [&](float x, int v) { row_step<Mode, false>(x, v, mx, ms, -1, lds, st); });
+  return st.sl;
 }
 
 // grid (rows): clears what the slices add into -- the row's counts (and
@@ -1023,18 +1038,24 @@ __global__ __launch_bounds__(kThreads) void sampled_slice_gather_kernel(
     for (int j = tid; j < m && b0 + j < kCap; j += kThreads) gcand[rid * kCap + b0 + j] = lc[j];
 }
 
-__global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
+// One instantiation per pass mode (the setting decides it): kSum without
+// truncation, kCount for top-k (with or without top-p), kCountMass for top-p
+// alone; each holds only its own code, registers and LDS.
+template <int Mode>
+__global__ __launch_bounds__(kThreads, Mode == kCountMass ? 4 : 6) void sampled_rows_kernel(
     const float* __restrict__ tgt, const float* __restrict__ dft, const int32_t* __restrict__ toks,
     int k, int V, float temperature, int top_k, float top_p, int W,
     const double* __restrict__ slice_s, const RowPlan* __restrict__ plans,
     const unsigned long long* __restrict__ gcand, SampledRow* __restrict__ rows) {
+  static_assert(Mode == kSum || Mode == kCount || Mode == kCountMass, "pass mode");
+  constexpr int kB = Mode == kSum ? 1 : kBins;
+  constexpr int kC = Mode == kSum ? 1 : kCap;
   __shared__ double dsh[kThreads];
   __shared__ double above_sh;
   __shared__ int ish[kThreads + 1];
-  __shared__ int hcnt[kBins];
-  __shared__ double hmass[kBins];
-  __shared__ unsigned long long cand[kCap];
-  __shared__ double cmass[kCap];
+  __shared__ int hcnt[kB];
+  __shared__ unsigned long long cand[kC];
+  __shared__ double cmass[kC];
   __shared__ double etab[kExpTab];
   __shared__ float fsh[kThreads / 64];
   __shared__ int ncand;
@@ -1052,10 +1073,10 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
 
   const size_t rid = static_cast<size_t>(b) * R + rho;
   const float T = temperature;
-  const bool trunc_k = top_k > 0 && top_k < V;
+  constexpr int mode = Mode;
+  constexpr bool trunc_k = Mode == kCount;      // top_k in (0, V)
+  constexpr bool trunc = Mode != kSum;
   const bool trunc_p = top_p < 1.f;
-  const bool trunc = trunc_k || trunc_p;
-  const int mode = !trunc ? kSum : trunc_k ? kCount : kCountMass;
   // (during the pass the fixed-point bins live in the candidate arrays)
   const RowLds lds = {hcnt, reinterpret_cast<u64*>(cand), reinterpret_cast<u64*>(cmass), cand,
                       &ncand};
@@ -1133,14 +1154,12 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
     mref = mx;
     bhat = -1;
     const Mass ms2(etab, mx, T);
-    RowScan s2 = {-INFINITY, V, 0, 0, 0.0};
     if (mode == kSum)
-      row_repass<kSum>(row, V, mx, ms2, lds, s2);
+      sl = row_repass<kSum>(row, V, mx, ms2, lds);
     else if (mode == kCount)
-      row_repass<kCount>(row, V, mx, ms2, lds, s2);
+      row_repass<kCount>(row, V, mx, ms2, lds);
     else
-      row_repass<kCountMass>(row, V, mx, ms2, lds, s2);
-    sl = s2.sl;
+      row_repass<kCountMass>(row, V, mx, ms2, lds);
   }
   __syncthreads();
   out.m = mref;
@@ -1184,17 +1203,26 @@ __global__ __launch_bounds__(kThreads) void sampled_rows_kernel(
         above = pl.above;
       }
     } else if (trunc_k) {
-      // from the list the pass made when it reaches bin bk, else by a second
-      // read of the bins down to it
-      int cnt_above = 0;
-      bk = bins_cross_count(hcnt, top_k, cnt_above, ish);
-      if (bhat >= 0 && bk <= bhat && ncand <= kCap) {
+      // from the list the pass made when it holds top_k tokens or more (all
+      // of those in bins <= bhat, so the top_k largest of the row), else
+      // counted by a second read and gathered by a third (bins down to bk)
+      if (bhat >= 0 && ncand >= top_k && ncand <= kCap) {
         n = ncand;
         sort_cand(cand, n);
-      } else if (bk < kBins && cnt_above + hcnt[bk] <= kCap) {
-        n = gather_bins(row, V, mref, 0, bk, cand, ish);
+      } else {
+        if (bhat >= 0) {
+          row_repass<kCount>(row, V, mref, ms, lds);
+          __syncthreads();
+        }
+        int cnt_above = 0;
+        bk = bins_cross_count(hcnt, top_k, cnt_above, ish);
+        if (bk < kBins && cnt_above + hcnt[bk] <= kCap)
+          n = gather_bins(row, V, mref, 0, bk, cand, ish);
       }
     } else {
+      // binary64 bin masses in place of the high chunks (each thread its own
+      // bins; the candidates overwrite them once the boundary bin is known)
+      double* const hmass = reinterpret_cast<double*>(lds.hhi);
       for (int j = tid; j < kBins; j += kThreads) hmass[j] = fx_value(lds.hhi[j], lds.hlo[j]);
       __syncthreads();
       need = static_cast<double>(top_p) * sum_before(hmass, kBins, dsh);
@@ -1642,9 +1670,15 @@ extern "C" sv_status sv_verify_sampled(const float* target_logits, const float* 
       SV_LAUNCH_CHECK();
     }
   }
-  hipLaunchKernelGGL(sampled_rows_kernel, dim3(2 * k + 1, B), dim3(kThreads), 0, stream,
-                     target_logits, draft_logits, draft_tokens, k, V, T, sampling->top_k,
-                     sampling->top_p, L.W, slice_s, plans, gcand, rows);
+  {
+    const bool tk = sampling->top_k > 0 && sampling->top_k < V;
+    const bool tp = sampling->top_p < 1.f;
+    auto rows_kernel = tk ? sampled_rows_kernel<kCount>
+                          : tp ? sampled_rows_kernel<kCountMass> : sampled_rows_kernel<kSum>;
+    hipLaunchKernelGGL(rows_kernel, dim3(2 * k + 1, B), dim3(kThreads), 0, stream,
+                       target_logits, draft_logits, draft_tokens, k, V, T, sampling->top_k,
+                       sampling->top_p, L.W, slice_s, plans, gcand, rows);
+  }
   SV_LAUNCH_CHECK();
   hipLaunchKernelGGL(sampled_decide_kernel, dim3(B), dim3(kThreads), 0, stream, draft_tokens, k,
                      V, rows, static_cast<unsigned int>(seed & 0xFFFFFFFFu),
