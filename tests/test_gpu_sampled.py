@@ -262,3 +262,31 @@ def test_large_tied_boundary_bins(n_tied, settings):
     tok = torch.from_numpy(oracle.sample_drafts(dft.numpy(), 5, *settings))
     out, res = _run(tgt, dft, tok, seed=8, settings=settings)
     assert _compare(out, res) <= 1
+
+
+@pytest.mark.parametrize("settings", [(1.0, 0, 1.0), (1.0, 50, 1.0), (0.7, 0, 0.9),
+                                      (0.8, 100, 0.95)],
+                         ids=["plain", "k50", "T0.7_p0.9", "T0.8_k100_p0.95"])
+@pytest.mark.parametrize("B", [6, 40], ids=["sliced_rows", "one_workgroup_per_row"])
+def test_rows_whose_first_entries_mislead_the_pass(B, settings):
+    # The pass bins a row against a reference taken from its first 4096
+    # entries (their maximum raised by min(4, 8 T)), and for top-k lists the
+    # tokens above a bin predicted from their counts.  Rows where that
+    # misleads: a later logit above the reference (the pass is taken again
+    # against the row maximum), first entries shifted up (the list falls
+    # short of top_k) or down (the list overflows), and a lone huge logit
+    # far into one row.  The outputs must still match the oracle.
+    k, V = 3, 20000
+    tgt, dft, tok = synth.accept_inputs(B, k, V, seed=31, sigma=1.0)
+    for t in (tgt, dft):
+        for i in range(t.shape[1]):
+            t[0, i, 10000] = t[0, i, :4096].max() + 4.5
+        t[1, :, :4096] += 3.0
+        t[2, :, :4096] -= 3.0
+        t[3, 1, 15000] = 50.0
+    out, res = _run(tgt, dft, tok, seed=4, settings=settings)
+    flagged = _compare(out, res)
+    assert (out["status"] == 0).all()
+    # (at V = 20000 a draft's p is about 5e-5, so the 1e-6 band of the
+    # accept test flags a few percent of the decisions)
+    assert flagged <= max(2, B // 5)
