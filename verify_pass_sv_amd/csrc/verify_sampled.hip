@@ -659,7 +659,9 @@ __device__ __forceinline__ void row_step(float x, int v, float ref, const Mass& 
   if (Mode == kSum) st.sl += ms(x);
   if (Mode == kCount || Mode == kCountMass) {
     const int bn = bin_of(x, ref);
-    atomicAdd(&lds.hcnt[bn], 1);
+    // (top-p alone needs no counts: its boundary bin's gather reports an
+    // overflow of the candidate list by itself)
+    if (Mode == kCount) atomicAdd(&lds.hcnt[bn], 1);
     if (Mode == kCountMass) fx_add(lds.hhi + bn, lds.hlo + bn, ms(x));
     if (Mode == kCount && bn <= bhat) {
       const int slot = atomicAdd(lds.ncand, 1);
@@ -932,13 +934,13 @@ __global__ __launch_bounds__(kThreads) void sampled_slice_pass_kernel(
   u64* glo = ghi + kBins;
   if (mode == kCount || mode == kCountMass) {
     for (int j = tid; j < kBins; j += kThreads) {
-      const int c = hcnt[j];
-      if (c != 0) {
-        atomicAdd(&gc[j], c);
-        if (mode == kCountMass) {
-          atomicAdd(&ghi[j], hhi[j]);
-          atomicAdd(&glo[j], hlo[j]);
-        }
+      if (mode == kCount) {
+        const int c = hcnt[j];
+        if (c != 0) atomicAdd(&gc[j], c);
+      } else {
+        const u64 hj = hhi[j], lj = hlo[j];
+        if (hj != 0ull) atomicAdd(&ghi[j], hj);
+        if (lj != 0ull) atomicAdd(&glo[j], lj);
       }
     }
   }
@@ -984,7 +986,7 @@ __global__ __launch_bounds__(kThreads) void sampled_slice_pass_kernel(
     } else {
       need = static_cast<double>(top_p) * sum_before(hmass, kBins, dsh);
       const int bp = cross_mass(hmass, kBins, need, above, dsh, ish);
-      if (bp < kBins && hcnt[bp] <= kCap) {
+      if (bp < kBins) {                         // (an overflowing gather shows in ncand)
         lo = bp;
         hi = bp;
       }
