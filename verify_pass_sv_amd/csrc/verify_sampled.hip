@@ -1572,12 +1572,13 @@ __global__ __launch_bounds__(kThreads) void sampled_select_kernel(
 namespace {
 // Slices per row: enough workgroups to cover the chip when a call has fewer
 // rows than compute units and rows are long; else one workgroup per row.
-// (Three slice workgroups fit a compute unit (their LDS), so 768 fill one
-// round of the chip; slices of 2048 tokens at least.)
+// (Two slice workgroups fit a compute unit -- their registers -- so 512 fill
+// one round of the chip; measured: 768, two rounds, took 4-7 us more at
+// B = 1; slices of 2048 tokens at least.)
 int row_slices(int B, int k, int V) {
   const long long rows = static_cast<long long>(B) * (2 * k + 1);
   if (rows >= 256 || V < 16384) return 1;
-  long long w = 768 / rows;
+  long long w = 512 / rows;
   if (w > kMaxSlices) w = kMaxSlices;
   if (w > V / 2048) w = V / 2048;
   return static_cast<int>(w);
