@@ -10,11 +10,13 @@
 //
 // Temperature 0 (greedy verification) runs as the chain tree d_0 <- d_1 <- ..
 // through the draft-tree kernels (sv_verify_tree's row maxima over many
-// workgroups per row, then one wave per trial).  Other settings take four
-// launches on the caller's stream (six when a call has fewer rows than
-// compute units: two slice launches then take each row's full passes --
-// maximum, argmax and validity, then the bins or the whole mass -- over W
-// workgroups per row, merged by the rows launch in slice order):
+// workgroups per row, then one wave per trial).  Other settings take three
+// launches on the caller's stream (four in a large call, whose selection is
+// a launch of its own).  A call with fewer rows than compute units
+// first takes three more: a clear, a pass of W workgroups per row (each
+// row's maximum, argmax, validity and bins or whole mass, merged in slice
+// order, the boundary planned by the row's last slice) and a gather of the
+// boundary tokens by the same slices:
 //  1. rows    one workgroup per (trial, row), target rows 0..k then draft rows
 //             0..k-1.  It checks the row and takes its maximum (and the
 //             argmax, smallest index among equal maxima, into the record).
@@ -40,10 +42,11 @@
 //  3. resid   one workgroup per (2048-entry vocabulary block, trial): block
 //             totals of the residual weights max(0, p'_r - q'_r) (or p'_k for
 //             the bonus), per-thread ranges of 4 entries added in order and
-//             their running sums formed in one fixed association.
-//  4. select  one workgroup per trial: S, the block whose running sum
-//             exceeds u' S, then the thread range and the entry inside it,
-//             replaying the same sums in the same order.
+//             their running sums formed in one fixed association.  The last
+//             workgroup of a trial to finish (a device-scope counter) selects:
+//             S, the block whose running sum exceeds u' S, then the thread
+//             range and the entry inside it, replaying the same sums in the
+//             same order.
 #include "sv_common.h"
 #include "sv_philox.h"
 
@@ -1303,10 +1306,11 @@ __global__ __launch_bounds__(kThreads) void sampled_decide_kernel(
     const int32_t* __restrict__ toks, int k, int V, const SampledRow* __restrict__ rows, unsigned int key0, unsigned int key1,
     unsigned int offset, SampledDecision* __restrict__ decs, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ out_n_acc, int32_t* __restrict__ out_status, float* __restrict__ p_at,
-    float* __restrict__ q_at) {
+    float* __restrict__ q_at, int* __restrict__ done) {
   __shared__ int ish[2];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
+  if (tid == 0) done[b] = 0;                    // launch 3's completion counter
   const int R = 2 * k + 1;
   const SampledRow* rr = rows + static_cast<size_t>(b) * R;
   const int32_t* tk = toks + static_cast<size_t>(b) * k;
@@ -1435,87 +1439,93 @@ __device__ void scan_inclusive(double* a) {
   }
 }
 
-// Launch 3: block totals of the residual weights (and of p_r alone, for the
-// S = 0 fallback): the last of the per-thread sums' running sums.
-__global__ __launch_bounds__(kThreads) void sampled_resid_kernel(
-    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V,
-    const SampledRow* __restrict__ rows, const SampledDecision* __restrict__ decs,
-    double* __restrict__ totals) {
-  __shared__ double wsh[2][kThreads];
-  __shared__ double etab[kExpTab];
-  const int tid = threadIdx.x;
-  const int blk = blockIdx.x;
-  const int b = blockIdx.y;
-  const int G = gridDim.x;
-  const SampledDecision dec = decs[b];
-  if (dec.status != 0) return;
-  exp_table_init(etab);
-  __syncthreads();
-  const ResidualRows q = residual_rows(tgt, dft, rows, b, k, V, dec.n_acc, etab);
-  wsh[0][tid] = thread_res_sum(q, V, blk, dec.plain != 0);
-  wsh[1][tid] = dec.plain ? 0.0 : thread_res_sum(q, V, blk, true);
-  __syncthreads();
-  scan_inclusive(wsh[0]);
-  scan_inclusive(wsh[1]);
-  if (tid < 2) totals[(static_cast<size_t>(b) * 2 + tid) * G + blk] = wsh[tid][kThreads - 1];
-}
-
-// Launch 4: S = sum of the block totals; the block whose running sum first
-// exceeds u' S; inside it, the thread whose running sum does; that thread
-// replays its entries with the same association.
-__global__ __launch_bounds__(kThreads) void sampled_select_kernel(
-    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V,
-    const SampledRow* __restrict__ rows, const SampledDecision* __restrict__ decs,
-    const double* __restrict__ totals, int G, int32_t* __restrict__ out_tokens) {
-  __shared__ double wsh[kThreads];
+// The selection of trial b, run by the last workgroup of launch 3 to finish
+// it: S = sum of the block totals; the block whose running sum first exceeds
+// u' S; inside it, the thread whose running sum does; that thread replays
+// its entries with the same association.  The running sums of the block
+// totals are formed by wave 0, lane l adding a contiguous range after the
+// exclusive sum of the ranges before it (one fixed association); the totals
+// are read with device-scope loads (written by other workgroups).
+__device__ void select_token(const float* __restrict__ tgt, const float* __restrict__ dft, int k,
+                             int V, const SampledRow* __restrict__ rows,
+                             const SampledDecision& dec, double* __restrict__ totals,
+                             int G, int b, const double* etab, double* wsh, double* lsh,
+                             int32_t* __restrict__ out_tokens) {
   __shared__ double run_sh, thr_sh;
   __shared__ int ish[3];
-  __shared__ double etab[kExpTab];
   const int tid = threadIdx.x;
-  const int b = blockIdx.x;
-  const SampledDecision dec = decs[b];
-  if (dec.status != 0) return;
-  exp_table_init(etab);
-  // the trial's block totals, staged in LDS by every thread when they fit
-  const double* tot = totals + static_cast<size_t>(b) * 2 * G;
+  double* const tot = totals + static_cast<size_t>(b) * 2 * G;
+  // both rows of totals (residual, then p_r alone), 2 G doubles: into LDS
+  // when they fit (lsh holds kThreads), else worked on in place after an
+  // agent-scope acquire (a vocabulary past 2^19 entries)
+  double* tsh = lsh;
   if (2 * G <= kThreads) {
-    for (int i = tid; i < 2 * G; i += kThreads) wsh[i] = tot[i];
-    tot = wsh;
+    const unsigned long long* t64 = reinterpret_cast<const unsigned long long*>(tot);
+    for (int i = tid; i < 2 * G; i += kThreads)
+      tsh[i] = __longlong_as_double(static_cast<long long>(
+          __hip_atomic_load(t64 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+  } else {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    tsh = tot;
   }
   __syncthreads();
-  if (tid == 0) {
+  if (tid < 64) {
+    // running sums of row `which`, in place; S the last one
+    auto run_sums = [&](int which) {
+      double* t = tsh + which * G;
+      const int per = (G + 63) / 64;
+      const int i0 = min(G, tid * per), i1 = min(G, i0 + per);
+      double c = 0.0;
+      for (int i = i0; i < i1; ++i) c += t[i];
+      double incl = c;
+      for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(incl, o, 64);
+        if (tid >= o) incl += y;
+      }
+      double run = __shfl_up(incl, 1, 64);
+      if (tid == 0) run = 0.0;
+      for (int i = i0; i < i1; ++i) {
+        run += t[i];
+        t[i] = run;
+      }
+      return __shfl(incl, 63, 64);
+    };
     int which = 0;
-    double S = 0.0;
-    for (int g = 0; g < G; ++g) S += tot[g];
+    double S = run_sums(0);
     if (!(S > 0.0)) {                           // only through rounding: w = p_r
       which = 1;
-      S = 0.0;
-      for (int g = 0; g < G; ++g) S += tot[G + g];
+      S = run_sums(1);
     }
     const double thr = dec.u2 * S;
-    double run = 0.0;
-    int blk = -1, lastnz = -1;
-    double lastnz_run = 0.0;
-    for (int g = 0; g < G; ++g) {
-      const double w = tot[which * G + g];
-      if (w > 0.0) {
-        lastnz = g;
-        lastnz_run = run;
-      }
-      if (run + w > thr) {
-        blk = g;
+    // the first block whose running sum exceeds thr (wave ballots over 64
+    // blocks at a time); none (rounding left thr at the end): the last block
+    // with weight
+    const double* t = tsh + which * G;
+    int blk = -1;
+    for (int c0 = 0; c0 < G; c0 += 64) {
+      const int i = c0 + tid;
+      const unsigned long long hit = __ballot(i < G && t[i] > thr);
+      if (hit) {
+        blk = c0 + __ffsll(static_cast<long long>(hit)) - 1;
         break;
       }
-      run += w;
     }
-    if (blk < 0) {                              // rounding left the threshold past the end
-      blk = lastnz;
-      run = lastnz_run;
+    if (blk < 0) {
+      int lastnz = -1;
+      for (int c0 = 0; c0 < G; c0 += 64) {
+        const int i = c0 + tid;
+        const bool nz = i < G && (i == 0 ? t[0] > 0.0 : t[i] > t[i - 1]);
+        const unsigned long long m = __ballot(nz);
+        if (m) lastnz = c0 + 63 - __clzll(static_cast<long long>(m));
+      }
+      blk = lastnz < 0 ? 0 : lastnz;
     }
-    ish[0] = blk;
-    ish[1] = which;
-    run_sh = run;
-    thr_sh = thr;
+    if (tid == 0) {
+      ish[0] = blk;
+      ish[1] = which;
+      run_sh = blk > 0 ? t[blk - 1] : 0.0;
+      thr_sh = thr;
+    }
   }
   __syncthreads();
   const int blk = ish[0];
@@ -1524,9 +1534,9 @@ __global__ __launch_bounds__(kThreads) void sampled_select_kernel(
   const double mine = thread_res_sum(q, V, blk, plain);
   wsh[tid] = mine;
   __syncthreads();
-  // the running sums of the thread sums as launch 3 formed them; the owner
-  // is the first thread whose running sum crosses the threshold (they never
-  // decrease); rounding that leaves none: the last thread with weight
+  // the running sums of the thread sums as the block total was formed; the
+  // owner is the first thread whose running sum crosses the threshold (they
+  // never decrease); rounding that leaves none: the last thread with weight
   scan_inclusive(wsh);
   if (tid == 0) {
     ish[2] = kThreads;
@@ -1567,6 +1577,66 @@ __global__ __launch_bounds__(kThreads) void sampled_select_kernel(
   }
 }
 
+// Launch 3: block totals of the residual weights (and of p_r alone, for the
+// S = 0 fallback): the last of the per-thread sums' running sums, stored at
+// device scope.  In a small call (fold) the last workgroup of the trial to
+// finish (a device-scope counter, zeroed by launch 2) selects the token:
+// every wave waits for its own stores to complete before the barrier and the
+// count.  In a large one a fourth launch selects (the waits would hold every
+// workgroup's slot).
+__global__ __launch_bounds__(kThreads) void sampled_resid_kernel(
+    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V,
+    const SampledRow* __restrict__ rows, const SampledDecision* __restrict__ decs,
+    double* __restrict__ totals, int fold, int* __restrict__ done,
+    int32_t* __restrict__ out_tokens) {
+  __shared__ double wsh[2][kThreads];
+  __shared__ double etab[kExpTab];
+  __shared__ int last;
+  const int tid = threadIdx.x;
+  const int blk = blockIdx.x;
+  const int b = blockIdx.y;
+  const int G = gridDim.x;
+  const SampledDecision dec = decs[b];
+  if (dec.status != 0) return;
+  exp_table_init(etab);
+  __syncthreads();
+  const ResidualRows q = residual_rows(tgt, dft, rows, b, k, V, dec.n_acc, etab);
+  wsh[0][tid] = thread_res_sum(q, V, blk, dec.plain != 0);
+  wsh[1][tid] = dec.plain ? 0.0 : thread_res_sum(q, V, blk, true);
+  __syncthreads();
+  scan_inclusive(wsh[0]);
+  scan_inclusive(wsh[1]);
+  if (tid < 2)
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(
+                           totals + (static_cast<size_t>(b) * 2 + tid) * G + blk),
+                       static_cast<unsigned long long>(__double_as_longlong(wsh[tid][kThreads - 1])),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!fold) return;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) last = atomicAdd(&done[b], 1) == G - 1;
+  __syncthreads();
+  if (!last) return;
+  // (the totals of the trial go to wsh[1] when they fit; the thread sums of
+  // the chosen block to wsh[0])
+  select_token(tgt, dft, k, V, rows, dec, totals, G, b, etab, wsh[0], wsh[1], out_tokens);
+}
+
+// Launch 4 of a large call: one workgroup per trial selects the token.
+__global__ __launch_bounds__(kThreads) void sampled_select_kernel(
+    const float* __restrict__ tgt, const float* __restrict__ dft, int k, int V,
+    const SampledRow* __restrict__ rows, const SampledDecision* __restrict__ decs,
+    double* __restrict__ totals, int G, int32_t* __restrict__ out_tokens) {
+  __shared__ double wsh[2][kThreads];
+  __shared__ double etab[kExpTab];
+  const int b = blockIdx.x;
+  const SampledDecision dec = decs[b];
+  if (dec.status != 0) return;
+  exp_table_init(etab);
+  __syncthreads();
+  select_token(tgt, dft, k, V, rows, dec, totals, G, b, etab, wsh[0], wsh[1], out_tokens);
+}
+
 }  // namespace
 
 namespace {
@@ -1585,7 +1655,8 @@ int row_slices(int B, int k, int V) {
 }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 struct SampledWs {
-  size_t rows_off, dec_off, tot_off, part_off, ss_off, hist_off, plan_off, cand_off, bytes;
+  size_t rows_off, dec_off, tot_off, done_off, part_off, ss_off, hist_off, plan_off, cand_off,
+      bytes;
   int W;
 };
 SampledWs sampled_ws(int B, int k, int V) {
@@ -1595,7 +1666,8 @@ SampledWs sampled_ws(int B, int k, int V) {
   w.rows_off = 0;
   w.dec_off = align256(nrow * sizeof(SampledRow));
   w.tot_off = align256(w.dec_off + static_cast<size_t>(B) * sizeof(SampledDecision));
-  w.bytes = w.tot_off + static_cast<size_t>(B) * 2 * res_blocks(V) * sizeof(double);
+  w.done_off = align256(w.tot_off + static_cast<size_t>(B) * 2 * res_blocks(V) * sizeof(double));
+  w.bytes = w.done_off + static_cast<size_t>(B) * sizeof(int);
   w.part_off = w.ss_off = w.hist_off = w.plan_off = w.cand_off = 0;
   if (w.W > 1) {
     w.part_off = align256(w.bytes);
@@ -1645,6 +1717,7 @@ extern "C" sv_status sv_verify_sampled(const float* target_logits, const float* 
   SampledRow* rows = reinterpret_cast<SampledRow*>(ws + L.rows_off);
   SampledDecision* decs = reinterpret_cast<SampledDecision*>(ws + L.dec_off);
   double* totals = reinterpret_cast<double*>(ws + L.tot_off);
+  int* done = reinterpret_cast<int*>(ws + L.done_off);
   const int G = res_blocks(V);
   // Greedy verification (T = 0) is the chain tree d_0 <- d_1 <- .. of the
   // draft-tree kernels: row maxima over many workgroups per row, then one
@@ -1686,13 +1759,18 @@ extern "C" sv_status sv_verify_sampled(const float* target_logits, const float* 
   hipLaunchKernelGGL(sampled_decide_kernel, dim3(B), dim3(kThreads), 0, stream, draft_tokens, k,
                      V, rows, static_cast<unsigned int>(seed & 0xFFFFFFFFu),
                      static_cast<unsigned int>(seed >> 32), offset, decs, out_tokens, out_n_acc,
-                     out_status, p_at, q_at);
+                     out_status, p_at, q_at, done);
   SV_LAUNCH_CHECK();
+  // (small calls select in launch 3's last workgroup per trial; measured:
+  // B = 1 3 us faster, B = 64 0.25 us per trial slower than a fourth launch)
+  const int fold = static_cast<long long>(B) * G <= 2048;
   hipLaunchKernelGGL(sampled_resid_kernel, dim3(G, B), dim3(kThreads), 0, stream, target_logits,
-                     draft_logits, k, V, rows, decs, totals);
+                     draft_logits, k, V, rows, decs, totals, fold, done, out_tokens);
   SV_LAUNCH_CHECK();
-  hipLaunchKernelGGL(sampled_select_kernel, dim3(B), dim3(kThreads), 0, stream, target_logits,
-                     draft_logits, k, V, rows, decs, totals, G, out_tokens);
-  SV_LAUNCH_CHECK();
+  if (!fold) {
+    hipLaunchKernelGGL(sampled_select_kernel, dim3(B), dim3(kThreads), 0, stream, target_logits,
+                       draft_logits, k, V, rows, decs, totals, G, out_tokens);
+    SV_LAUNCH_CHECK();
+  }
   return SV_OK;
 }
