@@ -19,19 +19,21 @@
 //             epilogue wrote, instead of reading the logits.
 //  2. decide  one workgroup per (trial, residual share): merges the trial's
 //             partials into log-sum-exp values (all loads in flight at once,
-//             staged in LDS, 4 lanes per row, fixed order), evaluates
-//             p_i(d_i), q_i(d_i) from the recorded token logits, draws the
-//             Philox uniforms and takes the accept decisions with one wave
-//             ballot (first rejection = first zero bit), then sums the
-//             residual weights max(0, p_r - q_r) (or p_k for the bonus) of its
-//             2048-float blocks in binary64: blocks staged in LDS, 16 groups of
-//             16 threads of 8 entries each, always in the same order.  Every
-//             workgroup of a trial reaches the same decision; workgroup 0
-//             writes the per-trial outputs.  The last workgroup of the trial
-//             to finish (a device-scope counter) runs the inverse-CDF
-//             selection over the running sums of the block totals (formed in
-//             order, searched by a wave ballot) and replays the same sums
-//             inside the chosen block, so the chosen bin always exists.
+//             staged in LDS, 4 lanes per row -- 2 past 64 rows -- in a fixed
+//             order), evaluates p_i(d_i), q_i(d_i) from the recorded token
+//             logits, draws the Philox uniforms and takes the accept
+//             decisions with one wave ballot (first rejection = first zero
+//             bit), then sums the residual weights max(0, p_r - q_r) (or p_k
+//             for the bonus) of its 2048-float blocks in binary64: 16 groups
+//             of 16 threads of 8 consecutive entries each (loaded straight
+//             from memory), always in the same order.  Every workgroup of a
+//             trial reaches the same decision; workgroup 0 writes the
+//             per-trial outputs but the drawn token.  The last workgroup of
+//             the trial to finish (a device-scope counter) runs the
+//             inverse-CDF selection over the running sums of the block
+//             totals (formed by a wave in one fixed association, searched by
+//             a wave ballot) and replays the same sums inside the chosen
+//             block, so the chosen bin always exists.
 #include "sv_common.h"
 #include "sv_philox.h"
 

@@ -25,8 +25,8 @@
 //             and v <= tie, where key() maps binary32 order to unsigned order.
 //             One pass reads the row once against a provisional reference
 //             (the maximum of its first entries, raised) and bins it (1/32
-//             logit): counts for top-k, counts and binary64 masses for top-p
-//             alone, the whole mass without truncation.  The top_k largest
+//             logit): counts for top-k, binary64 masses for top-p alone,
+//             the whole mass without truncation.  The top_k largest
 //             tokens are sorted in LDS -- from a list the pass keeps of the
 //             tokens above a bin predicted from the row's first entries, else
 //             gathered by a second read -- and top-p on the renormalised
@@ -627,7 +627,7 @@ __device__ __forceinline__ void merge_slices(const SlicePart* part, int W, float
 // The rows kernel's pass over a row (one workgroup per row) accumulates, per
 // setting: the whole mass (no truncation); bin counts (top-k, with or
 // without top-p: every mass that it needs comes from the gathered top
-// tokens); bin counts and masses (top-p alone); or nothing (the maximum,
+// tokens); bin masses (top-p alone); or nothing (the maximum,
 // argmax and validity alone, before a second pass).  kList (top-k, once a
 // bin bhat is predicted) only lists the tokens of bins <= bhat.
 enum RowMode { kSum, kCount, kCountMass, kTrack, kList };
@@ -825,8 +825,8 @@ __device__ __noinline__ double row_repass(const float* row, int V, float mx, Mas
   return st.sl;
 }
 
-// grid (rows): clears what the slices add into -- the row's counts (and
-// mass chunks for top-p alone), its candidate count and its ticket.
+// grid (rows): clears what the slices add into -- the row's counts (and for
+// top-p alone its mass chunks), its candidate count and its ticket.
 __global__ __launch_bounds__(kThreads) void sampled_clear_kernel(char* __restrict__ hist,
                                                                  RowPlan* __restrict__ plans,
                                                                  int chunks) {
@@ -1092,7 +1092,7 @@ __global__ __launch_bounds__(kThreads, Mode == kCountMass ? 4 : 6) void sampled_
   // logit of the row; the kept probabilities, ratios of such masses, do not
   // depend on which.  With one workgroup per row, mref is the maximum of the
   // row's first kPeek entries raised by min(4, 8 T), and the maximum, the
-  // validity, and the counts (and masses) come out of one pass; should a
+  // validity, and the counts (or masses) come out of one pass; should a
   // logit exceed mref after all, mref becomes the row maximum and the
   // accumulation takes a second pass.  (The fixed-point bin masses resolve
   // 2^-63 of mref's scale, at most e^8 of the maximum's.)  For top-k, the
