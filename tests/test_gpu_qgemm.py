@@ -41,7 +41,34 @@ def test_w4_matches_oracle(m, K, N):
                       what=f"w4 m={m} K={K} N={N}")
 
 
-@pytest.mark.parametrize("K", [512, 4096, 320])
+# sv_qgemm_w4 with K % 512 == 0 runs the streaming kernel of
+# sv_qgemm_w4_packed in its row-major mode: T = ceil(N / 4096) tiles of 16
+# channels per workgroup (T in 1, 2, 3, 4, 6), 1024-wide chunks of k through
+# a ring of LDS slots, scales and zeros copied per pair of tiles.  These
+# cases take every T, both row tiles (MT 1 and 2), waves whose block lies past
+# K, one, several and ragged chunks, an odd T (a half-used scale copy) and a
+# last workgroup with fewer tiles.
+@pytest.mark.parametrize("m,K,N", [(16, 4608, 512),      # T 1, ragged last chunk
+                                   (32, 2560, 256),      # MT 2, ragged last chunk
+                                   (5, 8704, 4112),      # T 2, 9 chunks
+                                   (20, 4096, 8192),     # MT 2, T 2
+                                   (16, 16384, 32),      # 16 chunks, 2 tiles in total
+                                   (16, 4096, 4112),     # T 2, full K
+                                   (5, 512, 4112),       # waves past K
+                                   (1, 1024, 11200),     # T 3
+                                   (32, 2048, 8208),     # MT 2, T 3
+                                   (24, 512, 16000),     # MT 2, T 4
+                                   (9, 1536, 25616)])    # T 6, last workgroup 5 tiles
+def test_w4_row_major_kernels(m, K, N):
+    sv = _sv()
+    x, codes, scales, zeros = _w4_case(m, K, N, seed=40 + m)
+    y = sv.sv_qgemm_w4(*to_dev(x, codes, scales, zeros))
+    torch.cuda.synchronize()
+    assert_rows_close(y.cpu().numpy(), _w4_oracle(x, codes, scales, zeros),
+                      what=f"w4 m={m} K={K} N={N}")
+
+
+@pytest.mark.parametrize("K", [512, 4096, 4608, 320])
 def test_w4_one_hot_rows_expose_exact_dequant(K):
     # an activation row e_j makes Y[r, n] the single dequantized weight
     # (c - z) * s, which is exact in binary32 for integer zero points

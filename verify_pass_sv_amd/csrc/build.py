@@ -42,7 +42,7 @@ def _hipcc():
 # Kernels that wait on exact counts of their own outstanding vector memory
 # operations: a register spill would add scratch loads and stores to that
 # count, so their build fails if any kernel of the file uses scratch.
-NO_SCRATCH = {"pass.hip", "pass_chain.hip", "qgemm_w4_packed.hip"}
+NO_SCRATCH = {"pass.hip", "pass_chain.hip", "qgemm_w4_packed.hip", "qgemm_w4.hip"}
 RESOURCE_REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
 
 
@@ -87,7 +87,10 @@ def build(verbose=False, jobs=None):
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda c: _run(c[0], verbose, c[1]), cmds))
     tmp = LIB + ".tmp"
-    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
+    # -z defs: a symbol left undefined (such as a kernel launch stub the host
+    # compile dropped) fails the link instead of the first load.
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Wl,-z,defs", "-o", tmp, *objs],
+         verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -1,5 +1,6 @@
 // sv_qgemm_w4: dequant-fused skinny GEMM over 4-bit asymmetric group-quantized
-// weights, Y[r, n] = sum_k X[r, k] (C[n, k] - Z[n, g]) S[n, g], g = k / 64.
+// weights, Y[r, n] = sum_k X[r, k] (C[n, k] - Z[n, g]) S[n, g], g = k / 64,
+// on the row-major codes / scales / zeros of the contract.
 //
 // Source: Karpathy's Trick for Faster Local LLMs, "How Uzu optimizes bytes and
 // tokens per pass" (Medium tier = 4-bit asymmetric integer quantization, one
@@ -7,7 +8,15 @@
 // is streamed once per pass); Speculative Decoding Clearly Explained, "Check
 // the guesses together" (all draft positions scored in one pass).
 //
-// Design (gfx950, wave64):
+// K % 512 == 0 (the common case): the streaming kernel of
+// sv_qgemm_w4_packed in its row-major mode (qgemm_w4_packed.hip): activations
+// staged once per workgroup in LDS for T consecutive 16-channel tiles, weight
+// chunks in flight through a ring of LDS / register slots, one 16-byte load
+// per lane and k block straight from the row-major codes, made into MFMA
+// operands by one lane swap.
+// Other K (a multiple of 64) take the plain kernel below.
+//
+// Plain kernel:
 //  * One workgroup owns 16 output channels; its waves split K.  Every code
 //    byte is loaded exactly once (8 bytes per lane = one 64-wide group of one
 //    row across 4 lanes) and dequantized once for all m rows.
@@ -20,37 +29,13 @@
 //    removes the bias and applies zero point and scale in binary32.  For
 //    integer z and a one-hot activation row the result is exactly
 //    (c - z) * s.
-//  * Per-group scales and zero points of the lane's channel are loaded 8
-//    groups at a time (16 bytes per lane).
 //  * Split-K partials of the waves are reduced through LDS in a fixed order,
 //    so results are deterministic.
-#include "sv_common.h"
+#include "w4_packed_dev.h"
 
 namespace {
 
 constexpr int kGroup = 64;
-
-// A bf16 exponent pattern held in a VGPR the compiler cannot fold: with it,
-// "keep the nibbles, insert the exponent" is a single v_and_or_b32.
-__device__ __forceinline__ unsigned int opaque_u32(unsigned int v) {
-  unsigned int r;
-  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
-  return r;
-}
-
-// 8 nibbles (one dword, natural order) -> 4 dwords of bf16 pairs (128 + c).
-// byte0 <- w.byte j (low nibble = even k), byte2 <- u.byte j (low nibble =
-// odd k), bytes 1 and 3 <- 0; the and-or keeps the nibbles and inserts the
-// bf16 exponent 0x43 (value 128).
-__device__ __forceinline__ sv_u32x4 dequant8_bias128(unsigned int w, unsigned int magic) {
-  const unsigned int u = w >> 4;
-  sv_u32x4 out;
-  out.x = (__builtin_amdgcn_perm(u, w, 0x0C040C00u) & 0x000F000Fu) | magic;
-  out.y = (__builtin_amdgcn_perm(u, w, 0x0C050C01u) & 0x000F000Fu) | magic;
-  out.z = (__builtin_amdgcn_perm(u, w, 0x0C060C02u) & 0x000F000Fu) | magic;
-  out.w = (__builtin_amdgcn_perm(u, w, 0x0C070C03u) & 0x000F000Fu) | magic;
-  return out;
-}
 
 template <int MT, int W, bool VEC_SZ>
 __global__ __launch_bounds__(64 * W) void qgemm_w4_kernel(
@@ -82,7 +67,7 @@ __global__ __launch_bounds__(64 * W) void qgemm_w4_kernel(
     const int r = col + 16 * t;
     xrow[t] = x + (size_t)(r < m ? r : 0) * K + q * 16;
   }
-  const unsigned int magic = opaque_u32(0x43004300u);
+  const unsigned int magic = sv_opaque_u32(0x43004300u);
 
   const sv_u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const sv_f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
@@ -93,8 +78,8 @@ __global__ __launch_bounds__(64 * W) void qgemm_w4_kernel(
   // One group: dequantize the lane's 16 nibbles, two MFMAs against the
   // weights, two against all-ones, then fold bias, zero point and scale.
   auto do_group = [&](sv_u32x2 wv, float s, float zb, const sv_u32x4 (&xa)[MT][2]) {
-    const sv_u32x4 b0 = dequant8_bias128(wv.x, magic);
-    const sv_u32x4 b1 = dequant8_bias128(wv.y, magic);
+    const sv_u32x4 b0 = sv_w4_dequant8_natural(wv.x, magic);
+    const sv_u32x4 b1 = sv_w4_dequant8_natural(wv.y, magic);
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       sv_f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -180,6 +165,9 @@ void launch_w4(bool vec, dim3 grid, hipStream_t st, const uint16_t* x, int m, in
                        codes, s, z, N, y);
 }
 
+
+
+
 }  // namespace
 
 extern "C" sv_status sv_qgemm_w4(const void* x, int m, int K, const uint8_t* codes,
@@ -193,11 +181,16 @@ extern "C" sv_status sv_qgemm_w4(const void* x, int m, int K, const uint8_t* cod
       !sv_aligned16(zeros) || !sv_aligned16(y))
     return SV_ERR_ALIGN;
   const int G = K / kGroup;
-  const bool vec = (G % 8) == 0;
-  const dim3 grid(N / 16);
   const uint16_t* xs = static_cast<const uint16_t*>(x);
   const uint16_t* ss = static_cast<const uint16_t*>(scales);
   const uint16_t* zs = static_cast<const uint16_t*>(zeros);
+  // Buffer-resource offsets are 32-bit: the streaming kernel takes matrices
+  // of less than 2 GiB of codes (and activations of less than 2 GiB).
+  if (K % 512 == 0 && static_cast<long long>(N) * K / 2 < (1LL << 31) &&
+      static_cast<long long>(SV_MAX_ROWS) * K * 2 < (1LL << 31))
+    return sv_w4_rowmajor_gemm(xs, m, K, codes, ss, zs, N, y, stream);
+  const bool vec = (G % 8) == 0;
+  const dim3 grid(N / 16);
   if (m <= 16)
     launch_w4<1, 8>(vec, grid, stream, xs, m, K, codes, ss, zs, N, y);
   else

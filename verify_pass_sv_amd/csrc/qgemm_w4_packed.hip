@@ -41,6 +41,11 @@
 //    zero point and scale in binary32 (exact (c - z) * s for a one-hot row
 //    and integer z).
 //  * Split-K partials of the 8 waves are summed through LDS in a fixed order.
+//
+// The same kernel serves sv_qgemm_w4 on the row-major codes (K % 512 == 0,
+// sv_w4_rowmajor_gemm): each lane loads its 16 bytes of a row's k block
+// directly and one lane swap turns them into MFMA operands (see the kernel's
+// RM notes); scales and zeros are copied from their row-major arrays.
 #include "w4_packed_dev.h"
 
 namespace {
@@ -105,19 +110,35 @@ __global__ void pack_sz_kernel(const uint16_t* __restrict__ scales,
 // MT: 16-row activation tiles (m <= 16 * MT); T: row tiles per workgroup;
 // PPW: 128-wide k blocks per wave per chunk (chunk = 8 * PPW * 128 k);
 // P: pipeline slots (P - 1 chunks in flight while one computes).
-template <int MT, int T, int PPW, int P>
+// RM: the weights are the row-major codes / scales / zeros of sv_qgemm_w4
+// (sz0 = scales, sz1 = zeros) instead of the packed layout (sz0 = records).
+//  * Codes: lane l loads the 16 bytes 16q .. 16q + 15 (q = l >> 4) of row
+//    16t + (l & 15)'s 64-byte block; lane q then holds codes k = 32q +
+//    [0, 32) of the block, half a group.  One v_permlane32_swap per dword
+//    pair trades the upper 8 bytes of lanes q = 0, 1 for the lower 8 bytes of
+//    lanes q = 2, 3: every lane then holds 16 codes of each of the block's two
+//    groups, at group offset oq = 32 (q & 1) + 16 (q >> 1) (16 q in the packed
+//    layout), and reads its activation operand at the same offset.
+//  * Scales and zeros of a chunk (16 groups x 16 rows = 512 bytes per tile
+//    and array) come in by buffer -> LDS copies of 1 KiB that each take the
+//    scales (or zeros) of two tiles.
+template <int MT, int T, int PPW, int P, bool RM>
 __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
     const uint16_t* __restrict__ x, int m, int K, const uint8_t* __restrict__ pcodes,
-    const uint16_t* __restrict__ psz, int N, float* __restrict__ y) {
+    const uint16_t* __restrict__ sz0, const uint16_t* __restrict__ sz1, int N,
+    float* __restrict__ y) {
   constexpr int KC = PPW * 128 * kWaves;          // k per chunk
   constexpr int PITCH = KC + 8;                   // bf16 per LDS row (16-byte pad)
   constexpr int BUF = 16 * MT * PITCH;            // bf16 per LDS slot
   constexpr int SEGS = KC / 512;                  // 1 KiB DMA pieces per row
   constexpr int D = 16 * MT * SEGS / kWaves;      // activation DMA pieces per wave per chunk
-  constexpr int DS = (T + kWaves - 1) / kWaves;   // scale/zero DMA pieces per wave per chunk
+  // scale/zero copies of 1 KiB per chunk: one per tile (packed), one per
+  // tile pair and array (row-major)
+  constexpr int NSZ = RM ? 2 * ((T + 1) / 2) : T;
+  constexpr int DS = (NSZ + kWaves - 1) / kWaves; // scale/zero DMA pieces per wave per chunk
   constexpr int L = T * PPW + D + DS;             // loads per wave per chunk
-  constexpr int SZB = (T + 1) * 512;              // u16 per LDS slot of scales/zeros: 1 KiB per
-                                                  // tile plus 1 KiB that absorbs dummy loads
+  constexpr int SZB = (NSZ + 1) * 512;            // u16 per LDS slot of scales/zeros: the
+                                                  // copies plus 1 KiB that absorbs dummy loads
   static_assert(PPW == 1, "one 128-wide k block per wave per chunk");
   static_assert((16 * MT * SEGS) % kWaves == 0, "uneven DMA split");
   static_assert(P * (BUF + SZB) * 2 <= kLdsBytes, "pipeline slots do not fit LDS");
@@ -134,14 +155,21 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
   const int ntile = N / 16;
   const int t0 = blockIdx.x * T;
   const int KB = K / 128;
+  const int G = K / kGroup;
   const int nchunk = (K + KC - 1) / KC;
-  const unsigned int magic = sv_opaque_u32(0x43434343u);
+  const int oq = RM ? 32 * (q & 1) + 16 * (q >> 1) : 16 * q;  // group offset of the lane's codes
+  const unsigned int magic = sv_opaque_u32(RM ? 0x43004300u : 0x43434343u);
   const sv_u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const sv_f32x4 fz = {0.f, 0.f, 0.f, 0.f};
+  // ntile * KB * 1024 = N * K / 2 bytes of codes in either layout
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(pcodes), 0, static_cast<int>(ntile * KB * 1024u), 0x00020000);
+  // packed records (N * K / 16 bytes), or the row-major scales (N * G * 2)
+  const int szbytes = RM ? N * G * 2 : static_cast<int>(ntile * KB * 128u);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(psz), 0, static_cast<int>(ntile * KB * 128u), 0x00020000);
+      const_cast<uint16_t*>(sz0), 0, szbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(RM ? sz1 : sz0), 0, szbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(x), 0, m * K * 2, 0x00020000);
 
@@ -170,20 +198,45 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
 #pragma unroll
       for (int p = 0; p < PPW; ++p) {
         const bool ok = live && (t0 + t < ntile) && (jb + p < KB);
-        const int blk = ok ? sv_pk_block(t0 + t, jb + p, KB, ntile) : 0;
-        wb[slot][t][p] = __builtin_amdgcn_raw_buffer_load_b128(
-            wrs, ok ? lane * 16 : kSvOutOfRange, blk * 1024, 0);
+        if constexpr (RM) {
+          // row 16 (t0 + t) + col, bytes 16q .. 16q + 15 of its k block
+          const unsigned int off =
+              ok ? static_cast<unsigned>(16 * (t0 + t) + col) * static_cast<unsigned>(K / 2) +
+                       64u * (jb + p) + 16u * q
+                 : kSvOutOfRange;
+          wb[slot][t][p] = __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0);
+        } else {
+          const int blk = ok ? sv_pk_block(t0 + t, jb + p, KB, ntile) : 0;
+          wb[slot][t][p] = __builtin_amdgcn_raw_buffer_load_b128(
+              wrs, ok ? lane * 16 : kSvOutOfRange, blk * 1024, 0);
+        }
       }
 #pragma unroll
     for (int i = 0; i < DS; ++i) {
-      const int t = wave + kWaves * i;            // this piece's tile (>= T: dummy)
-      // lane -> k block c * 8 + lane / 8 of the tile, 16-byte piece lane % 8
-      const int jj = c * (KC / 128) + (lane >> 3);
-      const bool ok = live && t < T && (t0 + t < ntile) && jj < KB;
-      const unsigned int off =
-          ok ? sv_pk_block(t0 + t, jj, KB, ntile) * 128 + (lane & 7) * 16 : kSvOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          srs, (sv_lds_void*)(szl + slot * SZB + (t < T ? t : T) * 512), 16, off, 0, 0, 0);
+      const int piece = wave + kWaves * i;        // this wave's copy (>= NSZ: dummy)
+      if constexpr (RM) {
+        // copy (tile pair piece / 2, scales if piece is even else zeros):
+        // lane -> tile 2 (piece / 2) + lane / 32, row (lane / 2) % 16, groups
+        // 16 c + 8 (lane % 2) .. + 7 of the chunk
+        const int t = 2 * (piece >> 1) + (lane >> 5);
+        const int gg = c * (KC / kGroup) + 8 * (lane & 1);
+        const bool ok = live && piece < NSZ && t < T && (t0 + t < ntile) && gg < G;
+        const unsigned int off =
+            ok ? static_cast<unsigned>(((16 * (t0 + t) + ((lane >> 1) & 15)) * G + gg) * 2)
+               : kSvOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            (piece & 1) ? zrs : srs,
+            (sv_lds_void*)(szl + slot * SZB + (piece < NSZ ? piece : NSZ) * 512), 16, off, 0, 0, 0);
+      } else {
+        const int t = piece;                      // this piece's tile
+        // lane -> k block c * 8 + lane / 8 of the tile, 16-byte piece lane % 8
+        const int jj = c * (KC / 128) + (lane >> 3);
+        const bool ok = live && t < T && (t0 + t < ntile) && jj < KB;
+        const unsigned int off =
+            ok ? sv_pk_block(t0 + t, jj, KB, ntile) * 128 + (lane & 7) * 16 : kSvOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            srs, (sv_lds_void*)(szl + slot * SZB + (t < T ? t : T) * 512), 16, off, 0, 0, 0);
+      }
     }
     const int k0 = c * KC;
     uint16_t* dst = lds + slot * BUF;
@@ -205,18 +258,34 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
     const int jb = c * (KC / 128) + wave * PPW;
     const uint16_t* buf = lds + slot * BUF;
     // this wave's k block inside the chunk is block `wave` of each tile's KiB
-    const uint16_t* szp = szl + slot * SZB + (wave * 16 + col) * 4;
+    // (packed); row-major: groups 2 wave, 2 wave + 1 of the lane's row in the
+    // tile's scale and zero copies
+    const uint16_t* szp = RM ? szl + slot * SZB + col * 16 + 2 * wave
+                             : szl + slot * SZB + (wave * 16 + col) * 4;
 #pragma unroll
     for (int p = 0; p < PPW; ++p) {
       if (jb + p >= KB) break;
       const int kl = (wave * PPW + p) * 128;       // k offset inside the chunk
+      if constexpr (RM) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          sv_u32x4 v = wb[slot][t][p];
+          const auto s0 = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+          v.x = s0[0];
+          v.z = s0[1];
+          v.y = s1[0];
+          v.w = s1[1];
+          wb[slot][t][p] = v;
+        }
+      }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {                // the two groups of the block
         sv_u32x4 a0[MT], a1[MT];
         sv_f32x4 xs[MT];
 #pragma unroll
         for (int a = 0; a < MT; ++a) {
-          const uint16_t* ap = buf + (col + 16 * a) * PITCH + kl + 64 * h + 16 * q;
+          const uint16_t* ap = buf + (col + 16 * a) * PITCH + kl + 64 * h + oq;
           a0[a] = *reinterpret_cast<const sv_u32x4*>(ap);
           a1[a] = *reinterpret_cast<const sv_u32x4*>(ap + 8);
           xs[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a0[a]),
@@ -228,8 +297,10 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
 #pragma unroll
         for (int t = 0; t < T; ++t) {
           const sv_u32x4 w = wb[slot][t][p];
-          const sv_u32x4 b0 = sv_w4_dequant8(h ? w.z : w.x, magic);
-          const sv_u32x4 b1 = sv_w4_dequant8(h ? w.w : w.y, magic);
+          const sv_u32x4 b0 = RM ? sv_w4_dequant8_natural(h ? w.z : w.x, magic)
+                                 : sv_w4_dequant8(h ? w.z : w.x, magic);
+          const sv_u32x4 b1 = RM ? sv_w4_dequant8_natural(h ? w.w : w.y, magic)
+                                 : sv_w4_dequant8(h ? w.w : w.y, magic);
 #pragma unroll
           for (int a = 0; a < MT; ++a) {
             acc[t][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -240,10 +311,19 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
         }
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-          const sv_u32x2 sbt = *reinterpret_cast<const sv_u32x2*>(szp + t * 512);
-          const unsigned int sz = h ? sbt.y : sbt.x;
-          const float s = sv_half_lo(sz);
-          const float zb = 128.0f + sv_half_hi(sz);
+          float s, zb;
+          if constexpr (RM) {
+            const uint16_t* sp = szp + (t >> 1) * 1024 + (t & 1) * 256;
+            const unsigned int sw = *reinterpret_cast<const unsigned int*>(sp);
+            const unsigned int zw = *reinterpret_cast<const unsigned int*>(sp + 512);
+            s = h ? sv_half_hi(sw) : sv_half_lo(sw);
+            zb = 128.0f + (h ? sv_half_hi(zw) : sv_half_lo(zw));
+          } else {
+            const sv_u32x2 sbt = *reinterpret_cast<const sv_u32x2*>(szp + t * 512);
+            const unsigned int sz = h ? sbt.y : sbt.x;
+            s = sv_half_lo(sz);
+            zb = 128.0f + sv_half_hi(sz);
+          }
 #pragma unroll
           for (int a = 0; a < MT; ++a)
 #pragma unroll
@@ -296,37 +376,47 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
   }
 }
 
-template <int MT, int T>
-sv_status launch_packed(const uint16_t* x, int m, int K, const uint8_t* pc, const uint16_t* ps,
-                        int N, float* y, hipStream_t st) {
+template <int MT, int T, bool RM>
+sv_status launch_packed(const uint16_t* x, int m, int K, const uint8_t* pc, const uint16_t* sz0,
+                        const uint16_t* sz1, int N, float* y, hipStream_t st) {
   // Chunks of 1024 k; three LDS slots for m <= 16 (two chunks in flight),
   // two for m <= 32 (32 activation rows per slot).
   constexpr int PPW = 1;
   constexpr int P = MT == 1 ? 3 : 2;
-  auto kern = qgemm_w4p_kernel<MT, T, PPW, P>;
+  constexpr int NSZ = RM ? 2 * ((T + 1) / 2) : T;
+  auto kern = qgemm_w4p_kernel<MT, T, PPW, P, RM>;
   // LDS: P slots of activations + scales/zeros, reused for the final reduction.
-  constexpr int kBuf = 16 * MT * (PPW * 128 * kWaves + 8) + (T + 1) * 512;
+  constexpr int kBuf = 16 * MT * (PPW * 128 * kWaves + 8) + (NSZ + 1) * 512;
   constexpr int kLds = (P * kBuf * 2 > T * MT * 256 * kWaves * 4) ? P * kBuf * 2
                                                                   : T * MT * 256 * kWaves * 4;
   const dim3 grid((N / 16 + T - 1) / T);
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess)
     return SV_ERR_HIP;
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), kLds, st, x, m, K, pc, ps, N, y);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), kLds, st, x, m, K, pc, sz0, sz1, N, y);
   SV_LAUNCH_CHECK();
   return SV_OK;
 }
 
-template <int MT>
-sv_status dispatch_T(int T, const uint16_t* x, int m, int K, const uint8_t* pc,
-                     const uint16_t* ps, int N, float* y, hipStream_t st) {
-  switch (T) {
-    case 1: return launch_packed<MT, 1>(x, m, K, pc, ps, N, y, st);
-    case 2: return launch_packed<MT, 2>(x, m, K, pc, ps, N, y, st);
-    case 3: return launch_packed<MT, 3>(x, m, K, pc, ps, N, y, st);
-    case 4: return launch_packed<MT, 4>(x, m, K, pc, ps, N, y, st);
-    default: return launch_packed<MT, 6>(x, m, K, pc, ps, N, y, st);
+// Row tiles per workgroup: spread the N/16 tiles over at most 256
+// workgroups (one per compute unit) so each reuses its staged activations
+// across as many tiles as possible.
+template <bool RM>
+sv_status dispatch(const uint16_t* x, int m, int K, const uint8_t* pc, const uint16_t* sz0,
+                   const uint16_t* sz1, int N, float* y, hipStream_t st) {
+  const int T = (N / 16 + 255) / 256;
+  if (m <= 16) {
+    if (T <= 1) return launch_packed<1, 1, RM>(x, m, K, pc, sz0, sz1, N, y, st);
+    if (T <= 2) return launch_packed<1, 2, RM>(x, m, K, pc, sz0, sz1, N, y, st);
+    if (T <= 3) return launch_packed<1, 3, RM>(x, m, K, pc, sz0, sz1, N, y, st);
+    if (T <= 4) return launch_packed<1, 4, RM>(x, m, K, pc, sz0, sz1, N, y, st);
+    return launch_packed<1, 6, RM>(x, m, K, pc, sz0, sz1, N, y, st);
   }
+  if (T <= 1) return launch_packed<2, 1, RM>(x, m, K, pc, sz0, sz1, N, y, st);
+  if (T <= 2) return launch_packed<2, 2, RM>(x, m, K, pc, sz0, sz1, N, y, st);
+  if (T <= 3) return launch_packed<2, 3, RM>(x, m, K, pc, sz0, sz1, N, y, st);
+  if (T <= 4) return launch_packed<2, 4, RM>(x, m, K, pc, sz0, sz1, N, y, st);
+  return launch_packed<2, 6, RM>(x, m, K, pc, sz0, sz1, N, y, st);
 }
 
 }  // namespace
@@ -372,14 +462,13 @@ extern "C" sv_status sv_qgemm_w4_packed(const void* x, int m, int K, const uint8
   if (!sv_aligned16(x) || !sv_aligned16(packed_codes) || !sv_aligned16(packed_sz) ||
       !sv_aligned16(y))
     return SV_ERR_ALIGN;
-  // Row tiles per workgroup: spread the N/16 tiles over at most 256
-  // workgroups (one per compute unit) so each reuses its staged activations
-  // across as many tiles as possible.
-  const int tiles = N / 16;
-  int T = (tiles + 255) / 256;
-  T = T <= 1 ? 1 : T <= 2 ? 2 : T <= 3 ? 3 : T <= 4 ? 4 : 6;
-  const uint16_t* xs = static_cast<const uint16_t*>(x);
   const uint16_t* ps = static_cast<const uint16_t*>(packed_sz);
-  if (m <= 16) return dispatch_T<1>(T, xs, m, K, packed_codes, ps, N, y, stream);
-  return dispatch_T<2>(T, xs, m, K, packed_codes, ps, N, y, stream);
+  return dispatch<false>(static_cast<const uint16_t*>(x), m, K, packed_codes, ps, ps, N, y,
+                         stream);
+}
+
+sv_status sv_w4_rowmajor_gemm(const uint16_t* x, int m, int K, const uint8_t* codes,
+                              const uint16_t* scales, const uint16_t* zeros, int N, float* y,
+                              hipStream_t stream) {
+  return dispatch<true>(x, m, K, codes, scales, zeros, N, y, stream);
 }
