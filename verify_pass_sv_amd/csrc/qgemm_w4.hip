@@ -31,7 +31,7 @@
 //    (c - z) * s.
 //  * Split-K partials of the waves are reduced through LDS in a fixed order,
 //    so results are deterministic.
-#include "w4_packed_dev.h"
+#include "w4_rowmajor.h"
 
 namespace {
 

@@ -46,7 +46,7 @@
 // sv_w4_rowmajor_gemm): each lane loads its 16 bytes of a row's k block
 // directly and one lane swap turns them into MFMA operands (see the kernel's
 // RM notes); scales and zeros are copied from their row-major arrays.
-#include "w4_packed_dev.h"
+#include "w4_rowmajor.h"
 
 namespace {
 

@@ -50,21 +50,6 @@ __device__ __forceinline__ sv_u32x4 sv_w4_dequant8(unsigned int w, unsigned int 
   return o;
 }
 
-// Row-major word (byte i = code 2i in the low nibble, code 2i + 1 in the
-// high nibble) -> four bf16 pairs holding 128 + c in natural k order: one
-// byte permute places the low and the high nibble of byte i in the two
-// halves, one and-or keeps the nibbles and inserts the bf16 exponent pattern
-// `magic` = 0x43004300 (value 128).
-__device__ __forceinline__ sv_u32x4 sv_w4_dequant8_natural(unsigned int w, unsigned int magic) {
-  const unsigned int u = w >> 4;
-  sv_u32x4 o;
-  o.x = (__builtin_amdgcn_perm(u, w, 0x0C040C00u) & 0x000F000Fu) | magic;
-  o.y = (__builtin_amdgcn_perm(u, w, 0x0C050C01u) & 0x000F000Fu) | magic;
-  o.z = (__builtin_amdgcn_perm(u, w, 0x0C060C02u) & 0x000F000Fu) | magic;
-  o.w = (__builtin_amdgcn_perm(u, w, 0x0C070C03u) & 0x000F000Fu) | magic;
-  return o;
-}
-
 // Workgroup barrier without the memory fence of __syncthreads (which would
 // wait for every outstanding global load); the "memory" clobber keeps the
 // compiler from moving memory accesses across it.  LDS data written by
@@ -88,11 +73,3 @@ __device__ __forceinline__ void sv_wait_vmcnt() {
 // writes nothing.  The check covers the per-lane (VGPR) offset, which is
 // where this marker goes.
 constexpr unsigned int kSvOutOfRange = 0x80000000u;
-
-// Host side, shared by the two W4 GEMM sources: the streaming kernel of
-// sv_qgemm_w4_packed run on the row-major codes, scales and zeros of
-// sv_qgemm_w4 (m in 1..32, N % 16 == 0, K % 512 == 0, N * K / 2 < 2^31, all
-// pointers 16-byte aligned; the caller checks).
-__attribute__((visibility("hidden"))) sv_status sv_w4_rowmajor_gemm(
-    const uint16_t* x, int m, int K, const uint8_t* codes, const uint16_t* scales,
-    const uint16_t* zeros, int N, float* y, hipStream_t stream);
