@@ -523,7 +523,10 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
           __builtin_amdgcn_make_buffer_rsrc(rd.y, 0, m * N * 4, 0x00020000);
       const __amdgpu_buffer_rsrc_t ors =
           __builtin_amdgcn_make_buffer_rsrc(rd.xo, 0, has_xo ? m * xo_cols * 2 : 0, 0x00020000);
-      for (int v = wave; v < T * MT; v += kSW) {
+      // one (tile, row tile) pair per wave at most: T * MT <= 6 < kSW
+      static_assert(TM * MT <= kSW, "one output pair per stream wave");
+      const int v = wave;
+      if (v < T * MT) {
         sv_f32x4 s = *reinterpret_cast<const sv_f32x4*>(lds + (v * kSW) * 1024 + lane * 16);
 #pragma unroll
         for (int j = 1; j < kSW; ++j) {
@@ -543,11 +546,7 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
         const int tile = tile0 + wg + (v / MT) * grid;
         const int n0 = 16 * tile;
         const int row = 16 * (v % MT) + (lane >> 2);
-        const unsigned int off =
-            row < m ? static_cast<unsigned int>((row * N + n0 + 4 * (lane & 3)) * 4)
-                    : kSvOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(sv_u32x4, o), yrs, off, 0,
-                                               kStreamC);
+        // the hand-off first (the next link reads it), then y
         if (has_xo && n0 < xo_cols) {
           sv_u32x2 pk;
           pk.x = bf16_rne(alpha * o[0]) | (bf16_rne(alpha * o[1]) << 16);
@@ -557,13 +556,25 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
                       : kSvOutOfRange;
           __builtin_amdgcn_raw_buffer_store_b64(pk, ors, xoff, 0, kSc1);
         }
+        sv_compiler_fence();
+        const unsigned int off =
+            row < m ? static_cast<unsigned int>((row * N + n0 + 4 * (lane & 3)) * 4)
+                    : kSvOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(sv_u32x4, o), yrs, off, 0,
+                                               kStreamC);
       }
     }
     // The hand-off is complete at agent scope before the IO wave arrives.
     // No load of this wave is in flight here (the round's rings are consumed
-    // and drained before E1; the next round's start after E3), so this waits
-    // only for the stores.
-    sv_wait_vmcnt<0>();
+    // and drained before E1; the next round's start after E3), and stores
+    // complete in issue order, so allowing the one y store to stay in flight
+    // waits exactly for the xo store before it (and for the y store of the
+    // previous round).  That y store completes before any load of the next
+    // round does (in-order counting), and so before this wave writes y again.
+    if (T > 0 && wave < T * MT)
+      sv_wait_vmcnt<1>();
+    else
+      sv_wait_vmcnt<0>();
     sv_barrier_no_fence();                        // E3
     rd = nxt;
   }
