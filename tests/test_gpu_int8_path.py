@@ -80,9 +80,33 @@ def test_w4_i8_matches_oracle(m, K, N):
     assert_rows_close(y.cpu().numpy(), ref, what=f"w4_i8 m={m} K={K} N={N}")
 
 
-def test_w4_i8_one_hot_exact():
+# sv_qgemm_w4_i8 with K % 512 == 0 runs the streaming kernel in its
+# row-major int8 mode (T = ceil(N / 4096) tiles of 16 channels per
+# workgroup, 1024-wide chunks, MT = 1 or 2 row tiles); other K the plain
+# kernel.  Every T, both MT, waves past K, ragged chunks and a short last
+# workgroup.
+@pytest.mark.parametrize("m,K,N", [(16, 4608, 512),      # T 1, ragged last chunk
+                                   (32, 2560, 256),      # MT 2
+                                   (5, 8704, 4112),      # T 2, 9 chunks
+                                   (5, 512, 4112),       # waves past K
+                                   (1, 1024, 11200),     # T 3
+                                   (24, 512, 16000),     # MT 2, T 4
+                                   (9, 1536, 25616)])    # T 6, last workgroup 5 tiles
+def test_w4_i8_streaming_kernel(m, K, N):
     sv = _sv()
-    N, K, m = 64, 1024, 32
+    codes, scales, zeros = synth.w4_matrix(N, K, seed=80 + m)
+    xq, xscale = synth.int8_activations(m, K, seed=81 + m)
+    y = sv.sv_qgemm_w4_i8(*to_dev(xq, xscale, codes, scales, zeros))
+    torch.cuda.synchronize()
+    ref = oracle.qgemm_w4_i8(xq.numpy(), xscale.numpy(), codes.numpy(), scales.numpy(),
+                             zeros.numpy())
+    assert_rows_close(y.cpu().numpy(), ref, what=f"w4_i8 m={m} K={K} N={N}")
+
+
+@pytest.mark.parametrize("K", [1024, 4608, 320])
+def test_w4_i8_one_hot_exact(K):
+    sv = _sv()
+    N, m = 64, 32
     codes, scales, zeros = synth.w4_matrix(N, K, seed=70)
     cols = np.random.default_rng(7).choice(K, size=m, replace=False)
     xq = torch.zeros((m, K), dtype=torch.int8)
@@ -94,9 +118,11 @@ def test_w4_i8_one_hot_exact():
     assert np.array_equal(y.cpu().numpy(), W[:, cols].T.astype(np.float32))
 
 
-def test_w4_i8_full_size_sampled():
+@pytest.mark.parametrize("N,K", [(4096, 4096), (12288, 4096), (24576, 4096), (4096, 12288)])
+def test_w4_i8_full_size_sampled(N, K):
+    # the 9B-class layer shapes at k = 16, sampled output channels
     sv = _sv()
-    N, K, m = 4096, 12288, 16
+    m = 16
     codes, scales, zeros = synth.w4_matrix(N, K, seed=71, device=DEV)
     xq, xscale = synth.int8_activations(m, K, seed=72, device=DEV)
     y = sv.sv_qgemm_w4_i8(xq, xscale, codes, scales, zeros)
@@ -105,7 +131,7 @@ def test_w4_i8_full_size_sampled():
     idx = torch.as_tensor(rows, device=DEV)
     ref = oracle.qgemm_w4_i8(xq.cpu().numpy(), xscale.cpu().numpy(), codes[idx].cpu().numpy(),
                              scales[idx].cpu().numpy(), zeros[idx].cpu().numpy())
-    assert_rows_close(y[:, idx].cpu().numpy(), ref, what="w4_i8 full")
+    assert_rows_close(y[:, idx].cpu().numpy(), ref, what=f"w4_i8 full {N}x{K}")
 
 
 def test_rotate_quantize_gemm_chain():

@@ -13,20 +13,18 @@
 // of one channel expanded to bytes 0..15 (one byte permute pair per dword).
 // A second MFMA against all-ones bytes gives Xg in the accumulator layout.
 // I and Xg are exact; the zero point and scale fold is binary32.
-#include "sv_common.h"
+//
+// With K % 512 == 0 the call runs the streaming kernel of
+// sv_qgemm_w4_packed in its row-major int8 mode (qgemm_w4_packed.hip):
+// activations staged once per workgroup in LDS for T consecutive 16-channel
+// tiles, 1024-wide chunks through a ring of slots, the same per-group
+// arithmetic.  Other K take the plain kernel below: one workgroup per 16
+// channels, waves split K.
+#include "w4_rowmajor.h"
 
 namespace {
 
 constexpr int kGroup = 64;
-
-// 8 nibbles (one dword, natural order) -> 2 dwords of bytes c0..c7.
-__device__ __forceinline__ sv_u32x2 expand8(unsigned int w) {
-  const unsigned int u = w >> 4;
-  sv_u32x2 r;
-  r.x = __builtin_amdgcn_perm(u, w, 0x05010400u) & 0x0F0F0F0Fu;
-  r.y = __builtin_amdgcn_perm(u, w, 0x07030602u) & 0x0F0F0F0Fu;
-  return r;
-}
 
 template <int MT, int W, bool VEC_SZ>
 __global__ __launch_bounds__(64 * W) void qgemm_w4_i8_kernel(
@@ -63,7 +61,7 @@ __global__ __launch_bounds__(64 * W) void qgemm_w4_i8_kernel(
   for (int t = 0; t < MT; ++t) yacc[t] = sv_f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto do_group = [&](sv_u32x2 wv, float s, float z, int g) {
-    const sv_u32x2 lo = expand8(wv.x), hi = expand8(wv.y);
+    const sv_u32x2 lo = sv_w4_expand8_natural(wv.x), hi = sv_w4_expand8_natural(wv.y);
     const sv_u32x4 bw = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -146,6 +144,11 @@ extern "C" sv_status sv_qgemm_w4_i8(const int8_t* xq, const float* xscale, int m
   const dim3 grid(N / 16);
   const uint16_t* ss = static_cast<const uint16_t*>(scales);
   const uint16_t* zs = static_cast<const uint16_t*>(zeros);
+  // Buffer-resource offsets are 32-bit: the streaming kernel takes matrices
+  // of less than 2 GiB of codes (and activations of less than 2 GiB).
+  if (K % 512 == 0 && static_cast<long long>(N) * K / 2 < (1LL << 31) &&
+      static_cast<long long>(SV_MAX_ROWS) * K < (1LL << 31))
+    return sv_w4_i8_rowmajor_gemm(xq, xscale, m, K, codes, ss, zs, N, y, stream);
   if (m <= 16)
     launch_i8<1, 8>(vec, grid, stream, xq, xscale, m, K, codes, ss, zs, N, y);
   else

@@ -112,6 +112,11 @@ __global__ void pack_sz_kernel(const uint16_t* __restrict__ scales,
 // P: pipeline slots (P - 1 chunks in flight while one computes).
 // RM: the weights are the row-major codes / scales / zeros of sv_qgemm_w4
 // (sz0 = scales, sz1 = zeros) instead of the packed layout (sz0 = records).
+// I8 (with RM, for sv_qgemm_w4_i8): x is int8 [m, K] with a per-row scale
+// xsc [m]; each group is one v_mfma_i32_16x16x64_i8 per tile (A = the lane's
+// 16 activations, B = its 16 codes expanded to bytes), exact in int32, with
+// the group sums Xg from an all-ones MFMA; the fold is
+//     y += s * (I - z * Xg)   (binary32),  y *= xsc[r] at the end.
 //  * Codes: lane l loads the 16 bytes 16q .. 16q + 15 (q = l >> 4) of row
 //    16t + (l & 15)'s 64-byte block; lane q then holds codes k = 32q +
 //    [0, 32) of the block, half a group.  One v_permlane32_swap per dword
@@ -122,15 +127,18 @@ __global__ void pack_sz_kernel(const uint16_t* __restrict__ scales,
 //  * Scales and zeros of a chunk (16 groups x 16 rows = 512 bytes per tile
 //    and array) come in by buffer -> LDS copies of 1 KiB that each take the
 //    scales (or zeros) of two tiles.
-template <int MT, int T, int PPW, int P, bool RM>
+template <int MT, int T, int PPW, int P, bool RM, bool I8>
 __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
-    const uint16_t* __restrict__ x, int m, int K, const uint8_t* __restrict__ pcodes,
-    const uint16_t* __restrict__ sz0, const uint16_t* __restrict__ sz1, int N,
-    float* __restrict__ y) {
+    const void* __restrict__ x, const float* __restrict__ xsc, int m, int K,
+    const uint8_t* __restrict__ pcodes, const uint16_t* __restrict__ sz0,
+    const uint16_t* __restrict__ sz1, int N, float* __restrict__ y) {
+  static_assert(RM || !I8, "int8 activations come with row-major weights");
+  constexpr int XB = I8 ? 1 : 2;                  // bytes per activation
   constexpr int KC = PPW * 128 * kWaves;          // k per chunk
-  constexpr int PITCH = KC + 8;                   // bf16 per LDS row (16-byte pad)
-  constexpr int BUF = 16 * MT * PITCH;            // bf16 per LDS slot
-  constexpr int SEGS = KC / 512;                  // 1 KiB DMA pieces per row
+  constexpr int PITCHB = KC * XB + 16;            // bytes per LDS row (16-byte pad)
+  constexpr int PITCH = PITCHB / 2;               // the same in 16-bit units
+  constexpr int BUF = 16 * MT * PITCH;            // 16-bit units per LDS slot
+  constexpr int SEGS = KC * XB / 1024;            // 1 KiB DMA pieces per row
   constexpr int D = 16 * MT * SEGS / kWaves;      // activation DMA pieces per wave per chunk
   // scale/zero copies of 1 KiB per chunk: one per tile (packed), one per
   // tile pair and array (row-major)
@@ -160,6 +168,8 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
   const int oq = RM ? 32 * (q & 1) + 16 * (q >> 1) : 16 * q;  // group offset of the lane's codes
   const unsigned int magic = sv_opaque_u32(RM ? 0x43004300u : 0x43434343u);
   const sv_u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const sv_u32x4 ones8 = {0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
+  const sv_i32x4 izero = {0, 0, 0, 0};
   const sv_f32x4 fz = {0.f, 0.f, 0.f, 0.f};
   // ntile * KB * 1024 = N * K / 2 bytes of codes in either layout
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -171,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
   const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(RM ? sz1 : sz0), 0, szbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(x), 0, m * K * 2, 0x00020000);
+      const_cast<void*>(x), 0, m * K * XB, 0x00020000);
 
   sv_f32x4 yacc[T][MT];
 #pragma unroll
@@ -248,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
       // rows); lanes past K land in the next row (ignored) or fail the range
       // check past the end of x
       const unsigned int off =
-          live && r < m ? (r * K + k0) * 2 + seg * 1024 + lane * 16 : kSvOutOfRange;
+          live && r < m ? (r * K + k0) * XB + seg * 1024 + lane * 16 : kSvOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (sv_lds_void*)(dst + r * PITCH + seg * 512), 16,
                                                off, 0, 0, 0);
     }
@@ -279,56 +289,101 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
           wb[slot][t][p] = v;
         }
       }
+      if constexpr (I8) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {                // the two groups of the block
-        sv_u32x4 a0[MT], a1[MT];
-        sv_f32x4 xs[MT];
-#pragma unroll
-        for (int a = 0; a < MT; ++a) {
-          const uint16_t* ap = buf + (col + 16 * a) * PITCH + kl + 64 * h + oq;
-          a0[a] = *reinterpret_cast<const sv_u32x4*>(ap);
-          a1[a] = *reinterpret_cast<const sv_u32x4*>(ap + 8);
-          xs[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a0[a]),
-                                                          sv_as_bf16x8(ones), fz, 0, 0, 0);
-          xs[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a1[a]),
-                                                          sv_as_bf16x8(ones), xs[a], 0, 0, 0);
-        }
-        sv_f32x4 acc[T][MT];
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const sv_u32x4 w = wb[slot][t][p];
-          const sv_u32x4 b0 = RM ? sv_w4_dequant8_natural(h ? w.z : w.x, magic)
-                                 : sv_w4_dequant8(h ? w.z : w.x, magic);
-          const sv_u32x4 b1 = RM ? sv_w4_dequant8_natural(h ? w.w : w.y, magic)
-                                 : sv_w4_dequant8(h ? w.w : w.y, magic);
+        for (int h = 0; h < 2; ++h) {              // the two groups of the block
+          const uint8_t* const xb = reinterpret_cast<const uint8_t*>(buf);
+          sv_u32x4 a8[MT];
+          sv_f32x4 xg[MT];
 #pragma unroll
           for (int a = 0; a < MT; ++a) {
-            acc[t][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                sv_as_bf16x8(a0[a]), sv_as_bf16x8(b0), fz, 0, 0, 0);
-            acc[t][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                sv_as_bf16x8(a1[a]), sv_as_bf16x8(b1), acc[t][a], 0, 0, 0);
-          }
-        }
+            a8[a] = *reinterpret_cast<const sv_u32x4*>(xb + (col + 16 * a) * PITCHB + kl +
+                                                       64 * h + oq);
+            // exact group sums Xg (all-ones B): lane (col, q) gets rows 4q .. 4q + 3
+            const sv_i32x4 g = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                sv_as_i32x4(a8[a]), sv_as_i32x4(ones8), izero, 0, 0, 0);
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-          float s, zb;
-          if constexpr (RM) {
+            for (int i = 0; i < 4; ++i) xg[a][i] = static_cast<float>(g[i]);
+          }
+          sv_i32x4 acc[T][MT];
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            const sv_u32x4 w = wb[slot][t][p];
+            const sv_u32x2 lo = sv_w4_expand8_natural(h ? w.z : w.x);
+            const sv_u32x2 hi = sv_w4_expand8_natural(h ? w.w : w.y);
+            const sv_u32x4 bw = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+            for (int a = 0; a < MT; ++a)
+              acc[t][a] = __builtin_amdgcn_mfma_i32_16x16x64_i8(sv_as_i32x4(a8[a]),
+                                                                sv_as_i32x4(bw), izero, 0, 0, 0);
+          }
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
             const uint16_t* sp = szp + (t >> 1) * 1024 + (t & 1) * 256;
             const unsigned int sw = *reinterpret_cast<const unsigned int*>(sp);
             const unsigned int zw = *reinterpret_cast<const unsigned int*>(sp + 512);
-            s = h ? sv_half_hi(sw) : sv_half_lo(sw);
-            zb = 128.0f + (h ? sv_half_hi(zw) : sv_half_lo(zw));
-          } else {
-            const sv_u32x2 sbt = *reinterpret_cast<const sv_u32x2*>(szp + t * 512);
-            const unsigned int sz = h ? sbt.y : sbt.x;
-            s = sv_half_lo(sz);
-            zb = 128.0f + sv_half_hi(sz);
+            const float sg = h ? sv_half_hi(sw) : sv_half_lo(sw);
+            const float zg = h ? sv_half_hi(zw) : sv_half_lo(zw);
+#pragma unroll
+            for (int a = 0; a < MT; ++a)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                yacc[t][a][i] = fmaf(sg, fmaf(-zg, xg[a][i], static_cast<float>(acc[t][a][i])),
+                                     yacc[t][a][i]);
           }
-#pragma unroll
-          for (int a = 0; a < MT; ++a)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              yacc[t][a][i] = fmaf(s, fmaf(-zb, xs[a][i], acc[t][a][i]), yacc[t][a][i]);
+        }
+      } else {
+  #pragma unroll
+        for (int h = 0; h < 2; ++h) {                // the two groups of the block
+          sv_u32x4 a0[MT], a1[MT];
+          sv_f32x4 xs[MT];
+  #pragma unroll
+          for (int a = 0; a < MT; ++a) {
+            const uint16_t* ap = buf + (col + 16 * a) * PITCH + kl + 64 * h + oq;
+            a0[a] = *reinterpret_cast<const sv_u32x4*>(ap);
+            a1[a] = *reinterpret_cast<const sv_u32x4*>(ap + 8);
+            xs[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a0[a]),
+                                                            sv_as_bf16x8(ones), fz, 0, 0, 0);
+            xs[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a1[a]),
+                                                            sv_as_bf16x8(ones), xs[a], 0, 0, 0);
+          }
+          sv_f32x4 acc[T][MT];
+  #pragma unroll
+          for (int t = 0; t < T; ++t) {
+            const sv_u32x4 w = wb[slot][t][p];
+            const sv_u32x4 b0 = RM ? sv_w4_dequant8_natural(h ? w.z : w.x, magic)
+                                   : sv_w4_dequant8(h ? w.z : w.x, magic);
+            const sv_u32x4 b1 = RM ? sv_w4_dequant8_natural(h ? w.w : w.y, magic)
+                                   : sv_w4_dequant8(h ? w.w : w.y, magic);
+  #pragma unroll
+            for (int a = 0; a < MT; ++a) {
+              acc[t][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  sv_as_bf16x8(a0[a]), sv_as_bf16x8(b0), fz, 0, 0, 0);
+              acc[t][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  sv_as_bf16x8(a1[a]), sv_as_bf16x8(b1), acc[t][a], 0, 0, 0);
+            }
+          }
+  #pragma unroll
+          for (int t = 0; t < T; ++t) {
+            float s, zb;
+            if constexpr (RM) {
+              const uint16_t* sp = szp + (t >> 1) * 1024 + (t & 1) * 256;
+              const unsigned int sw = *reinterpret_cast<const unsigned int*>(sp);
+              const unsigned int zw = *reinterpret_cast<const unsigned int*>(sp + 512);
+              s = h ? sv_half_hi(sw) : sv_half_lo(sw);
+              zb = 128.0f + (h ? sv_half_hi(zw) : sv_half_lo(zw));
+            } else {
+              const sv_u32x2 sbt = *reinterpret_cast<const sv_u32x2*>(szp + t * 512);
+              const unsigned int sz = h ? sbt.y : sbt.x;
+              s = sv_half_lo(sz);
+              zb = 128.0f + sv_half_hi(sz);
+            }
+  #pragma unroll
+            for (int a = 0; a < MT; ++a)
+  #pragma unroll
+              for (int i = 0; i < 4; ++i)
+                yacc[t][a][i] = fmaf(s, fmaf(-zb, xs[a][i], acc[t][a][i]), yacc[t][a][i]);
+          }
         }
       }
     }
@@ -372,28 +427,29 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
     for (int w = 0; w < kWaves; ++w) acc += red[(((w * T + t) * MT + a) * 4 + i) * 64 + l];
     const int r = 16 * a + 4 * (l >> 4) + i;
     const int n = 16 * (t0 + t) + (l & 15);
-    if (r < m && t0 + t < ntile) y[static_cast<size_t>(r) * N + n] = acc;
+    if (r < m && t0 + t < ntile) y[static_cast<size_t>(r) * N + n] = I8 ? acc * xsc[r] : acc;
   }
 }
 
-template <int MT, int T, bool RM>
-sv_status launch_packed(const uint16_t* x, int m, int K, const uint8_t* pc, const uint16_t* sz0,
-                        const uint16_t* sz1, int N, float* y, hipStream_t st) {
+template <int MT, int T, bool RM, bool I8>
+sv_status launch_packed(const void* x, const float* xsc, int m, int K, const uint8_t* pc,
+                        const uint16_t* sz0, const uint16_t* sz1, int N, float* y,
+                        hipStream_t st) {
   // Chunks of 1024 k; three LDS slots for m <= 16 (two chunks in flight),
   // two for m <= 32 (32 activation rows per slot).
   constexpr int PPW = 1;
   constexpr int P = MT == 1 ? 3 : 2;
   constexpr int NSZ = RM ? 2 * ((T + 1) / 2) : T;
-  auto kern = qgemm_w4p_kernel<MT, T, PPW, P, RM>;
+  auto kern = qgemm_w4p_kernel<MT, T, PPW, P, RM, I8>;
   // LDS: P slots of activations + scales/zeros, reused for the final reduction.
-  constexpr int kBuf = 16 * MT * (PPW * 128 * kWaves + 8) + (NSZ + 1) * 512;
+  constexpr int kBuf = 16 * MT * ((PPW * 128 * kWaves * (I8 ? 1 : 2) + 16) / 2) + (NSZ + 1) * 512;
   constexpr int kLds = (P * kBuf * 2 > T * MT * 256 * kWaves * 4) ? P * kBuf * 2
                                                                   : T * MT * 256 * kWaves * 4;
   const dim3 grid((N / 16 + T - 1) / T);
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess)
     return SV_ERR_HIP;
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), kLds, st, x, m, K, pc, sz0, sz1, N, y);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), kLds, st, x, xsc, m, K, pc, sz0, sz1, N, y);
   SV_LAUNCH_CHECK();
   return SV_OK;
 }
@@ -401,22 +457,24 @@ sv_status launch_packed(const uint16_t* x, int m, int K, const uint8_t* pc, cons
 // Row tiles per workgroup: spread the N/16 tiles over at most 256
 // workgroups (one per compute unit) so each reuses its staged activations
 // across as many tiles as possible.
-template <bool RM>
-sv_status dispatch(const uint16_t* x, int m, int K, const uint8_t* pc, const uint16_t* sz0,
-                   const uint16_t* sz1, int N, float* y, hipStream_t st) {
+template <bool RM, bool I8>
+sv_status dispatch(const void* x, const float* xsc, int m, int K, const uint8_t* pc,
+                   const uint16_t* sz0, const uint16_t* sz1, int N, float* y, hipStream_t st) {
   const int T = (N / 16 + 255) / 256;
+#define SV_LAUNCH_T(mt, t) launch_packed<mt, t, RM, I8>(x, xsc, m, K, pc, sz0, sz1, N, y, st)
   if (m <= 16) {
-    if (T <= 1) return launch_packed<1, 1, RM>(x, m, K, pc, sz0, sz1, N, y, st);
-    if (T <= 2) return launch_packed<1, 2, RM>(x, m, K, pc, sz0, sz1, N, y, st);
-    if (T <= 3) return launch_packed<1, 3, RM>(x, m, K, pc, sz0, sz1, N, y, st);
-    if (T <= 4) return launch_packed<1, 4, RM>(x, m, K, pc, sz0, sz1, N, y, st);
-    return launch_packed<1, 6, RM>(x, m, K, pc, sz0, sz1, N, y, st);
+    if (T <= 1) return SV_LAUNCH_T(1, 1);
+    if (T <= 2) return SV_LAUNCH_T(1, 2);
+    if (T <= 3) return SV_LAUNCH_T(1, 3);
+    if (T <= 4) return SV_LAUNCH_T(1, 4);
+    return SV_LAUNCH_T(1, 6);
   }
-  if (T <= 1) return launch_packed<2, 1, RM>(x, m, K, pc, sz0, sz1, N, y, st);
-  if (T <= 2) return launch_packed<2, 2, RM>(x, m, K, pc, sz0, sz1, N, y, st);
-  if (T <= 3) return launch_packed<2, 3, RM>(x, m, K, pc, sz0, sz1, N, y, st);
-  if (T <= 4) return launch_packed<2, 4, RM>(x, m, K, pc, sz0, sz1, N, y, st);
-  return launch_packed<2, 6, RM>(x, m, K, pc, sz0, sz1, N, y, st);
+  if (T <= 1) return SV_LAUNCH_T(2, 1);
+  if (T <= 2) return SV_LAUNCH_T(2, 2);
+  if (T <= 3) return SV_LAUNCH_T(2, 3);
+  if (T <= 4) return SV_LAUNCH_T(2, 4);
+  return SV_LAUNCH_T(2, 6);
+#undef SV_LAUNCH_T
 }
 
 }  // namespace
@@ -463,12 +521,17 @@ extern "C" sv_status sv_qgemm_w4_packed(const void* x, int m, int K, const uint8
       !sv_aligned16(y))
     return SV_ERR_ALIGN;
   const uint16_t* ps = static_cast<const uint16_t*>(packed_sz);
-  return dispatch<false>(static_cast<const uint16_t*>(x), m, K, packed_codes, ps, ps, N, y,
-                         stream);
+  return dispatch<false, false>(x, nullptr, m, K, packed_codes, ps, ps, N, y, stream);
 }
 
 sv_status sv_w4_rowmajor_gemm(const uint16_t* x, int m, int K, const uint8_t* codes,
                               const uint16_t* scales, const uint16_t* zeros, int N, float* y,
                               hipStream_t stream) {
-  return dispatch<true>(x, m, K, codes, scales, zeros, N, y, stream);
+  return dispatch<true, false>(x, nullptr, m, K, codes, scales, zeros, N, y, stream);
+}
+
+sv_status sv_w4_i8_rowmajor_gemm(const int8_t* xq, const float* xscale, int m, int K,
+                                 const uint8_t* codes, const uint16_t* scales,
+                                 const uint16_t* zeros, int N, float* y, hipStream_t stream) {
+  return dispatch<true, true>(xq, xscale, m, K, codes, scales, zeros, N, y, stream);
 }

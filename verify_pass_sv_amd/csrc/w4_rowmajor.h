@@ -19,6 +19,15 @@ __device__ __forceinline__ sv_u32x4 sv_w4_dequant8_natural(unsigned int w, unsig
   return o;
 }
 
+// Row-major word (8 codes) -> 2 dwords of bytes c0 .. c7 (values 0..15).
+__device__ __forceinline__ sv_u32x2 sv_w4_expand8_natural(unsigned int w) {
+  const unsigned int u = w >> 4;
+  sv_u32x2 r;
+  r.x = __builtin_amdgcn_perm(u, w, 0x05010400u) & 0x0F0F0F0Fu;
+  r.y = __builtin_amdgcn_perm(u, w, 0x07030602u) & 0x0F0F0F0Fu;
+  return r;
+}
+
 // Host side: the streaming kernel of sv_qgemm_w4_packed run on the row-major
 // codes, scales and zeros of sv_qgemm_w4 (m in 1..32, N % 16 == 0,
 // K % 512 == 0, N * K / 2 < 2^31, all pointers 16-byte aligned; the caller
@@ -26,3 +35,9 @@ __device__ __forceinline__ sv_u32x4 sv_w4_dequant8_natural(unsigned int w, unsig
 __attribute__((visibility("hidden"))) sv_status sv_w4_rowmajor_gemm(
     const uint16_t* x, int m, int K, const uint8_t* codes, const uint16_t* scales,
     const uint16_t* zeros, int N, float* y, hipStream_t stream);
+
+// The same kernel for sv_qgemm_w4_i8: int8 activations xq [m, K] with the
+// per-row scale xscale [m] (same conditions).
+__attribute__((visibility("hidden"))) sv_status sv_w4_i8_rowmajor_gemm(
+    const int8_t* xq, const float* xscale, int m, int K, const uint8_t* codes,
+    const uint16_t* scales, const uint16_t* zeros, int N, float* y, hipStream_t stream);
