@@ -155,6 +155,27 @@ def test_w8_matches_oracle(m, K, N):
     assert_rows_close(y.cpu().numpy(), ref, what=f"w8 m={m} K={K} N={N}")
 
 
+# sv_qgemm_w8 runs the streaming kernel in its 8-bit mode: T = ceil(N / 4096)
+# tiles of 16 channels per workgroup, 512-wide chunks of 64-wide blocks,
+# MT = 1 or 2 row tiles.  Every T, both MT, a ragged last chunk (K % 512 !=
+# 0), waves past K and a short last workgroup.
+@pytest.mark.parametrize("m,K,N", [(16, 4672, 512),      # T 1, ragged last chunk
+                                   (32, 2560, 256),      # MT 2
+                                   (5, 8704, 4112),      # T 2, 17 chunks
+                                   (3, 192, 4112),       # waves past K, one chunk
+                                   (1, 1024, 11200),     # T 3
+                                   (24, 512, 16000),     # MT 2, T 4
+                                   (9, 1536, 25616)])    # T 6, last workgroup 5 tiles
+def test_w8_streaming_kernel(m, K, N):
+    sv = _sv()
+    codes, scales = synth.w8_matrix(N, K, seed=50 + m)
+    x = synth.activations(m, K, seed=51 + m)
+    y = sv.sv_qgemm_w8(*to_dev(x, codes, scales))
+    torch.cuda.synchronize()
+    ref = oracle.qgemm_w8(bf16_bits(x), codes.numpy(), scales.numpy())
+    assert_rows_close(y.cpu().numpy(), ref, what=f"w8 m={m} K={K} N={N}")
+
+
 def test_w8_one_hot_rows_exact():
     sv = _sv()
     N, K, m = 64, 1024, 32
@@ -171,7 +192,7 @@ def test_w8_one_hot_rows_exact():
     assert np.array_equal(y.cpu().numpy(), expect)
 
 
-@pytest.mark.parametrize("N,K", [(4096, 4096), (4096, 12288)])
+@pytest.mark.parametrize("N,K", [(4096, 4096), (12288, 4096), (24576, 4096), (4096, 12288)])
 def test_w8_full_size_sampled(N, K):
     sv = _sv()
     for m in (1, 16, 32):

@@ -117,6 +117,11 @@ __global__ void pack_sz_kernel(const uint16_t* __restrict__ scales,
 // 16 activations, B = its 16 codes expanded to bytes), exact in int32, with
 // the group sums Xg from an all-ones MFMA; the fold is
 //     y += s * (I - z * Xg)   (binary32),  y *= xsc[r] at the end.
+// W8 (with RM, for sv_qgemm_w8): row-major int8 codes [N, K] with one fp16
+// scale per channel (sz0).  A k block is 64 wide (a lane's 16 codes, one
+// 16-byte load), a chunk 512; a code c becomes bf16 128 + c through
+// v_cvt_f32_ubyte; the MFMAs accumulate over the whole of K (no groups), an
+// all-ones MFMA the row sums, and y = s * (acc - 128 xsum) at the end.
 //  * Codes: lane l loads the 16 bytes 16q .. 16q + 15 (q = l >> 4) of row
 //    16t + (l & 15)'s 64-byte block; lane q then holds codes k = 32q +
 //    [0, 32) of the block, half a group.  One v_permlane32_swap per dword
@@ -127,14 +132,17 @@ __global__ void pack_sz_kernel(const uint16_t* __restrict__ scales,
 //  * Scales and zeros of a chunk (16 groups x 16 rows = 512 bytes per tile
 //    and array) come in by buffer -> LDS copies of 1 KiB that each take the
 //    scales (or zeros) of two tiles.
-template <int MT, int T, int PPW, int P, bool RM, bool I8>
+template <int MT, int T, int PPW, int P, bool RM, bool I8, bool W8>
 __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
     const void* __restrict__ x, const float* __restrict__ xsc, int m, int K,
     const uint8_t* __restrict__ pcodes, const uint16_t* __restrict__ sz0,
     const uint16_t* __restrict__ sz1, int N, float* __restrict__ y) {
   static_assert(RM || !I8, "int8 activations come with row-major weights");
+  static_assert(RM || !W8, "8-bit weights are row-major");
+  static_assert(!(I8 && W8), "one mode at a time");
   constexpr int XB = I8 ? 1 : 2;                  // bytes per activation
-  constexpr int KC = PPW * 128 * kWaves;          // k per chunk
+  constexpr int KBK = W8 ? 64 : 128;              // k per block (one 16-byte load per lane)
+  constexpr int KC = PPW * KBK * kWaves;          // k per chunk
   constexpr int PITCHB = KC * XB + 16;            // bytes per LDS row (16-byte pad)
   constexpr int PITCH = PITCHB / 2;               // the same in 16-bit units
   constexpr int BUF = 16 * MT * PITCH;            // 16-bit units per LDS slot
@@ -142,10 +150,10 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
   constexpr int D = 16 * MT * SEGS / kWaves;      // activation DMA pieces per wave per chunk
   // scale/zero copies of 1 KiB per chunk: one per tile (packed), one per
   // tile pair and array (row-major)
-  constexpr int NSZ = RM ? 2 * ((T + 1) / 2) : T;
+  constexpr int NSZ = W8 ? 0 : RM ? 2 * ((T + 1) / 2) : T;
   constexpr int DS = (NSZ + kWaves - 1) / kWaves; // scale/zero DMA pieces per wave per chunk
   constexpr int L = T * PPW + D + DS;             // loads per wave per chunk
-  constexpr int SZB = (NSZ + 1) * 512;            // u16 per LDS slot of scales/zeros: the
+  constexpr int SZB = W8 ? 0 : (NSZ + 1) * 512;   // u16 per LDS slot of scales/zeros: the
                                                   // copies plus 1 KiB that absorbs dummy loads
   static_assert(PPW == 1, "one 128-wide k block per wave per chunk");
   static_assert((16 * MT * SEGS) % kWaves == 0, "uneven DMA split");
@@ -162,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
   const int q = lane >> 4;
   const int ntile = N / 16;
   const int t0 = blockIdx.x * T;
-  const int KB = K / 128;
+  const int KB = K / KBK;
   const int G = K / kGroup;
   const int nchunk = (K + KC - 1) / KC;
   const int oq = RM ? 32 * (q & 1) + 16 * (q >> 1) : 16 * q;  // group offset of the lane's codes
@@ -171,9 +179,9 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
   const sv_u32x4 ones8 = {0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
   const sv_i32x4 izero = {0, 0, 0, 0};
   const sv_f32x4 fz = {0.f, 0.f, 0.f, 0.f};
-  // ntile * KB * 1024 = N * K / 2 bytes of codes in either layout
+  // N * K / 2 bytes of 4-bit codes in either layout, N * K of 8-bit ones
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(pcodes), 0, static_cast<int>(ntile * KB * 1024u), 0x00020000);
+      const_cast<uint8_t*>(pcodes), 0, W8 ? N * K : N * (K / 2), 0x00020000);
   // packed records (N * K / 16 bytes), or the row-major scales (N * G * 2)
   const int szbytes = RM ? N * G * 2 : static_cast<int>(ntile * KB * 128u);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
@@ -190,6 +198,10 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
     for (int a = 0; a < MT; ++a) yacc[t][a] = fz;
 
   sv_u32x4 wb[P][T][PPW];
+  // W8: row sums of the activations over all of K, per row tile
+  sv_f32x4 xsacc[MT];
+#pragma unroll
+  for (int a = 0; a < MT; ++a) xsacc[a] = fz;
   uint16_t* const szl = lds + P * BUF;            // P slots of T KiB: scales/zeros
 
   // Issue all L loads of chunk c into slot `slot`: this wave's weight blocks
@@ -202,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
   // destinations are never consumed).  That keeps the vmcnt waits exact.
   auto issue = [&](const int slot, int c) {
     const bool live = c < nchunk;
-    const int jb = c * (KC / 128) + wave * PPW;
+    const int jb = c * (KC / KBK) + wave * PPW;
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
@@ -210,8 +222,10 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
         const bool ok = live && (t0 + t < ntile) && (jb + p < KB);
         if constexpr (RM) {
           // row 16 (t0 + t) + col, bytes 16q .. 16q + 15 of its k block
+          // (64 bytes per block and row in either width)
           const unsigned int off =
-              ok ? static_cast<unsigned>(16 * (t0 + t) + col) * static_cast<unsigned>(K / 2) +
+              ok ? static_cast<unsigned>(16 * (t0 + t) + col) *
+                           static_cast<unsigned>(W8 ? K : K / 2) +
                        64u * (jb + p) + 16u * q
                  : kSvOutOfRange;
           wb[slot][t][p] = __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0);
@@ -265,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
   };
 
   auto compute = [&](const int slot, int c) {
-    const int jb = c * (KC / 128) + wave * PPW;
+    const int jb = c * (KC / KBK) + wave * PPW;
     const uint16_t* buf = lds + slot * BUF;
     // this wave's k block inside the chunk is block `wave` of each tile's KiB
     // (packed); row-major: groups 2 wave, 2 wave + 1 of the lane's row in the
@@ -275,8 +289,8 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
 #pragma unroll
     for (int p = 0; p < PPW; ++p) {
       if (jb + p >= KB) break;
-      const int kl = (wave * PPW + p) * 128;       // k offset inside the chunk
-      if constexpr (RM) {
+      const int kl = (wave * PPW + p) * KBK;       // k offset inside the chunk
+      if constexpr (RM && !W8) {
 #pragma unroll
         for (int t = 0; t < T; ++t) {
           sv_u32x4 v = wb[slot][t][p];
@@ -332,12 +346,41 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
                                      yacc[t][a][i]);
           }
         }
+      } else if constexpr (W8) {
+        // one 64-wide block: the lane's codes 16q .. 16q + 15 against
+        // activations 16q .. 16q + 15 (two MFMA k slices of 8)
+        sv_u32x4 a0[MT], a1[MT];
+#pragma unroll
+        for (int a = 0; a < MT; ++a) {
+          const uint16_t* ap = buf + (col + 16 * a) * PITCH + kl + 16 * q;
+          a0[a] = *reinterpret_cast<const sv_u32x4*>(ap);
+          a1[a] = *reinterpret_cast<const sv_u32x4*>(ap + 8);
+          xsacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a0[a]),
+                                                             sv_as_bf16x8(ones), xsacc[a], 0, 0, 0);
+          xsacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(a1[a]),
+                                                             sv_as_bf16x8(ones), xsacc[a], 0, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const sv_u32x4 w = wb[slot][t][p];
+          const sv_u32x2 c0 = sv_w8_cvt4_bias128(w.x), c1 = sv_w8_cvt4_bias128(w.y);
+          const sv_u32x2 c2 = sv_w8_cvt4_bias128(w.z), c3 = sv_w8_cvt4_bias128(w.w);
+          const sv_u32x4 b0 = {c0.x, c0.y, c1.x, c1.y};
+          const sv_u32x4 b1 = {c2.x, c2.y, c3.x, c3.y};
+#pragma unroll
+          for (int a = 0; a < MT; ++a) {
+            yacc[t][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                sv_as_bf16x8(a0[a]), sv_as_bf16x8(b0), yacc[t][a], 0, 0, 0);
+            yacc[t][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                sv_as_bf16x8(a1[a]), sv_as_bf16x8(b1), yacc[t][a], 0, 0, 0);
+          }
+        }
       } else {
-  #pragma unroll
+#pragma unroll
         for (int h = 0; h < 2; ++h) {                // the two groups of the block
           sv_u32x4 a0[MT], a1[MT];
           sv_f32x4 xs[MT];
-  #pragma unroll
+#pragma unroll
           for (int a = 0; a < MT; ++a) {
             const uint16_t* ap = buf + (col + 16 * a) * PITCH + kl + 64 * h + oq;
             a0[a] = *reinterpret_cast<const sv_u32x4*>(ap);
@@ -348,14 +391,14 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
                                                             sv_as_bf16x8(ones), xs[a], 0, 0, 0);
           }
           sv_f32x4 acc[T][MT];
-  #pragma unroll
+#pragma unroll
           for (int t = 0; t < T; ++t) {
             const sv_u32x4 w = wb[slot][t][p];
             const sv_u32x4 b0 = RM ? sv_w4_dequant8_natural(h ? w.z : w.x, magic)
                                    : sv_w4_dequant8(h ? w.z : w.x, magic);
             const sv_u32x4 b1 = RM ? sv_w4_dequant8_natural(h ? w.w : w.y, magic)
                                    : sv_w4_dequant8(h ? w.w : w.y, magic);
-  #pragma unroll
+#pragma unroll
             for (int a = 0; a < MT; ++a) {
               acc[t][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                   sv_as_bf16x8(a0[a]), sv_as_bf16x8(b0), fz, 0, 0, 0);
@@ -363,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
                   sv_as_bf16x8(a1[a]), sv_as_bf16x8(b1), acc[t][a], 0, 0, 0);
             }
           }
-  #pragma unroll
+#pragma unroll
           for (int t = 0; t < T; ++t) {
             float s, zb;
             if constexpr (RM) {
@@ -378,9 +421,9 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
               s = sv_half_lo(sz);
               zb = 128.0f + sv_half_hi(sz);
             }
-  #pragma unroll
+#pragma unroll
             for (int a = 0; a < MT; ++a)
-  #pragma unroll
+#pragma unroll
               for (int i = 0; i < 4; ++i)
                 yacc[t][a][i] = fmaf(s, fmaf(-zb, xs[a][i], acc[t][a][i]), yacc[t][a][i]);
           }
@@ -409,6 +452,17 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
   }
   __syncthreads();
 
+  // W8: the 128 bias of the codes leaves once, y = acc - 128 * xsum (the
+  // channel scale is applied at the store)
+  if constexpr (W8) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int a = 0; a < MT; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) yacc[t][a][i] = fmaf(-128.0f, xsacc[a][i], yacc[t][a][i]);
+  }
+
   // Fixed-order reduction of the 8 waves' partials through LDS.
   float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
@@ -427,11 +481,13 @@ __global__ __launch_bounds__(kThreads) void qgemm_w4p_kernel(
     for (int w = 0; w < kWaves; ++w) acc += red[(((w * T + t) * MT + a) * 4 + i) * 64 + l];
     const int r = 16 * a + 4 * (l >> 4) + i;
     const int n = 16 * (t0 + t) + (l & 15);
-    if (r < m && t0 + t < ntile) y[static_cast<size_t>(r) * N + n] = I8 ? acc * xsc[r] : acc;
+    if (r < m && t0 + t < ntile)
+      y[static_cast<size_t>(r) * N + n] =
+          W8 ? acc * sv_half_lo(sz0[n]) : I8 ? acc * xsc[r] : acc;
   }
 }
 
-template <int MT, int T, bool RM, bool I8>
+template <int MT, int T, bool RM, bool I8, bool W8>
 sv_status launch_packed(const void* x, const float* xsc, int m, int K, const uint8_t* pc,
                         const uint16_t* sz0, const uint16_t* sz1, int N, float* y,
                         hipStream_t st) {
@@ -439,10 +495,11 @@ sv_status launch_packed(const void* x, const float* xsc, int m, int K, const uin
   // two for m <= 32 (32 activation rows per slot).
   constexpr int PPW = 1;
   constexpr int P = MT == 1 ? 3 : 2;
-  constexpr int NSZ = RM ? 2 * ((T + 1) / 2) : T;
-  auto kern = qgemm_w4p_kernel<MT, T, PPW, P, RM, I8>;
+  constexpr int NSZ = W8 ? 0 : RM ? 2 * ((T + 1) / 2) : T;
+  auto kern = qgemm_w4p_kernel<MT, T, PPW, P, RM, I8, W8>;
   // LDS: P slots of activations + scales/zeros, reused for the final reduction.
-  constexpr int kBuf = 16 * MT * ((PPW * 128 * kWaves * (I8 ? 1 : 2) + 16) / 2) + (NSZ + 1) * 512;
+  constexpr int kBuf = 16 * MT * ((PPW * (W8 ? 64 : 128) * kWaves * (I8 ? 1 : 2) + 16) / 2) +
+                       (W8 ? 0 : (NSZ + 1) * 512);
   constexpr int kLds = (P * kBuf * 2 > T * MT * 256 * kWaves * 4) ? P * kBuf * 2
                                                                   : T * MT * 256 * kWaves * 4;
   const dim3 grid((N / 16 + T - 1) / T);
@@ -457,11 +514,12 @@ sv_status launch_packed(const void* x, const float* xsc, int m, int K, const uin
 // Row tiles per workgroup: spread the N/16 tiles over at most 256
 // workgroups (one per compute unit) so each reuses its staged activations
 // across as many tiles as possible.
-template <bool RM, bool I8>
+template <bool RM, bool I8, bool W8 = false>
 sv_status dispatch(const void* x, const float* xsc, int m, int K, const uint8_t* pc,
                    const uint16_t* sz0, const uint16_t* sz1, int N, float* y, hipStream_t st) {
   const int T = (N / 16 + 255) / 256;
-#define SV_LAUNCH_T(mt, t) launch_packed<mt, t, RM, I8>(x, xsc, m, K, pc, sz0, sz1, N, y, st)
+#define SV_LAUNCH_T(mt, t) \
+  launch_packed<mt, t, RM, I8, W8>(x, xsc, m, K, pc, sz0, sz1, N, y, st)
   if (m <= 16) {
     if (T <= 1) return SV_LAUNCH_T(1, 1);
     if (T <= 2) return SV_LAUNCH_T(1, 2);
@@ -528,6 +586,12 @@ sv_status sv_w4_rowmajor_gemm(const uint16_t* x, int m, int K, const uint8_t* co
                               const uint16_t* scales, const uint16_t* zeros, int N, float* y,
                               hipStream_t stream) {
   return dispatch<true, false>(x, nullptr, m, K, codes, scales, zeros, N, y, stream);
+}
+
+sv_status sv_w8_rowmajor_gemm(const uint16_t* x, int m, int K, const int8_t* codes,
+                              const uint16_t* scales, int N, float* y, hipStream_t stream) {
+  return dispatch<true, false, true>(x, nullptr, m, K, reinterpret_cast<const uint8_t*>(codes),
+                                     scales, scales, N, y, stream);
 }
 
 sv_status sv_w4_i8_rowmajor_gemm(const int8_t* xq, const float* xscale, int m, int K,

@@ -10,22 +10,9 @@
 // unsigned byte, v_cvt_f32_ubyteN, upper half of the binary32 pattern); a
 // second MFMA against an all-ones operand accumulates sum_k X[r, k], and the
 // epilogue forms S[n] * (acc - 128 * xsum) once per channel.
-#include "sv_common.h"
+#include "w4_rowmajor.h"
 
 namespace {
-
-// 4 int8 codes (one dword) -> 2 dwords of bf16 pairs holding 128 + c.
-__device__ __forceinline__ sv_u32x2 cvt4_bias128(unsigned int d) {
-  const unsigned int u = d ^ 0x80808080u;
-  const unsigned int f0 = __float_as_uint(static_cast<float>(u & 0xFFu));
-  const unsigned int f1 = __float_as_uint(static_cast<float>((u >> 8) & 0xFFu));
-  const unsigned int f2 = __float_as_uint(static_cast<float>((u >> 16) & 0xFFu));
-  const unsigned int f3 = __float_as_uint(static_cast<float>(u >> 24));
-  sv_u32x2 r;
-  r.x = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
-  r.y = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
-  return r;
-}
 
 template <int MT, int W>
 __global__ __launch_bounds__(64 * W) void qgemm_w8_kernel(
@@ -66,8 +53,8 @@ __global__ __launch_bounds__(64 * W) void qgemm_w8_kernel(
 #pragma unroll
     for (int j = 0; j < UNR; ++j) {
       if (b0 + j >= be) break;
-      const sv_u32x2 p0 = cvt4_bias128(wv[j].x), p1 = cvt4_bias128(wv[j].y);
-      const sv_u32x2 p2 = cvt4_bias128(wv[j].z), p3 = cvt4_bias128(wv[j].w);
+      const sv_u32x2 p0 = sv_w8_cvt4_bias128(wv[j].x), p1 = sv_w8_cvt4_bias128(wv[j].y);
+      const sv_u32x2 p2 = sv_w8_cvt4_bias128(wv[j].z), p3 = sv_w8_cvt4_bias128(wv[j].w);
       const sv_u32x4 bl = {p0.x, p0.y, p1.x, p1.y};
       const sv_u32x4 bh = {p2.x, p2.y, p3.x, p3.y};
 #pragma unroll
@@ -116,6 +103,11 @@ extern "C" sv_status sv_qgemm_w8(const void* x, int m, int K, const int8_t* code
   const dim3 grid(N / 16);
   const uint16_t* xs = static_cast<const uint16_t*>(x);
   const uint16_t* ss = static_cast<const uint16_t*>(scales);
+  // Buffer-resource offsets are 32-bit: the streaming kernel takes matrices
+  // of less than 2 GiB of codes (and activations of less than 2 GiB).
+  if (static_cast<long long>(N) * K < (1LL << 31) &&
+      static_cast<long long>(SV_MAX_ROWS) * K * 2 < (1LL << 31))
+    return sv_w8_rowmajor_gemm(xs, m, K, codes, ss, N, y, stream);
   if (m <= 16)
     hipLaunchKernelGGL((qgemm_w8_kernel<1, 8>), grid, dim3(512), 0, stream, xs, m, K, codes,
                        ss, N, y);
