@@ -335,6 +335,10 @@ def main():
                          "then exit")
     ap.add_argument("--sampling", default="0.7,0,0.9",
                     help="temperature,top_k,top_p of --profile-verify sampled")
+    ap.add_argument("--profile-single", action="store_true",
+                    help="single-GEMM entry points (row-major and packed W4, int8 x W4, "
+                         "W8) on 8 layers of the 9B shapes at --k rows, 13 rounds each, "
+                         "then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
@@ -365,6 +369,38 @@ def main():
             sv.sv_verify_accept(t, d, tk, seed=i, out=out, workspace=ws)
         torch.cuda.synchronize()
         log(f"profile-accept: {calls} calls at B={B}, k={k}, V={VOCAB}")
+        return
+    if args.profile_single:
+        # 8 layers x (qkv, o, gate|up, down), so that the weights of one round
+        # (0.9-1.7 GB) come from HBM, not from the 256 MB memory-side cache
+        shapes = [(3 * HIDDEN, HIDDEN), (HIDDEN, HIDDEN), (2 * FFN, HIDDEN), (HIDDEN, FFN)]
+        xs = {K: synth.activations(k, K, seed=6 + K, device=dev) for K in (HIDDEN, FFN)}
+        xq = {K: synth.int8_activations(k, K, seed=7 + K, device=dev) for K in (HIDDEN, FFN)}
+        ys = {N: torch.empty((k, N), dtype=torch.float32, device=dev) for N, _ in shapes}
+        w4, w8 = [], []
+        for layer in range(8):
+            for N, K in shapes:
+                c, s_, z = synth.w4_matrix(N, K, seed=100 * layer + N + K, device=dev)
+                pc, ps = sv.sv_w4_pack(c, s_, z)
+                w4.append((N, K, c, s_, z, pc, ps))
+                w8.append((N, K) + tuple(synth.w8_matrix(N, K, seed=100 * layer + N + K,
+                                                         device=dev)))
+        calls = {
+            "sv_qgemm_w4": lambda: [sv.sv_qgemm_w4(xs[K], c, s_, z, y=ys[N])
+                                    for (N, K, c, s_, z, pc, ps) in w4],
+            "sv_qgemm_w4_packed": lambda: [sv.sv_qgemm_w4_packed(xs[K], pc, ps, N, y=ys[N])
+                                           for (N, K, c, s_, z, pc, ps) in w4],
+            "sv_qgemm_w4_i8": lambda: [sv.sv_qgemm_w4_i8(xq[K][0], xq[K][1], c, s_, z, y=ys[N])
+                                       for (N, K, c, s_, z, pc, ps) in w4],
+            "sv_qgemm_w8": lambda: [sv.sv_qgemm_w8(xs[K], c, s_, y=ys[N])
+                                    for (N, K, c, s_) in w8],
+        }
+        torch.cuda.synchronize()
+        for name, fn in calls.items():
+            for _ in range(13):
+                fn()
+            torch.cuda.synchronize()
+            log(f"profile-single: {name}, 13 rounds of 32 GEMMs at k={k}")
         return
     if args.profile_verify:
         src = torch.empty(1 << 28, dtype=torch.uint8, device=dev).random_(0, 255)

@@ -75,7 +75,67 @@ def pick(d, key):
     raise KeyError(f"no kernel matching {key!r}")
 
 
+# Single-GEMM launches (bench.py --profile-single): each entry point runs 13
+# rounds of 32 GEMMs, 8 layers of (qkv, o, gate|up, down) in that order.
+SINGLE_SHAPES = [("qkv", 12288, 4096), ("o", 4096, 4096), ("gate/up", 24576, 4096),
+                 ("down", 4096, 12288)]
+SINGLE_MODES = {  # template flags (row-major, int8 activations, 8-bit weights)
+    ("true", "false", "false"): ("sv_qgemm_w4", "w4"),
+    ("false", "false", "false"): ("sv_qgemm_w4_packed", "w4"),
+    ("true", "true", "false"): ("sv_qgemm_w4_i8", "w4"),
+    ("true", "false", "true"): ("sv_qgemm_w8", "w8"),
+}
+
+
+def single_gemm_summary(trace_dir, title, command, out):
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*_kernel_trace.csv"), recursive=True):
+        rows += [r for r in csv.DictReader(open(f)) if "qgemm_w4p_kernel<" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    fam = collections.defaultdict(list)
+    for r in rows:
+        flags = tuple(x.strip() for x in r["Kernel_Name"].split(">")[0].split(",")[-3:])
+        fam[SINGLE_MODES[flags]].append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [f"# {title}", "", "Commands (run from the repository root with TMPDIR=/tmp):", "",
+             "```", command, "```", "",
+             "Per-dispatch durations from the kernel trace; each entry point's first 3 rounds "
+             "(96 dispatches) are dropped, the other 10 averaged per matrix shape. Algorithmic "
+             "bytes: codes plus scales and zero points (W4: N K / 2 + N K / 16), codes plus "
+             "channel scales (W8: N K + 2 N).", "",
+             "| entry point | matrix (N x K) | avg us | TB/s |", "|---|---|---:|---:|"]
+    summary = {}
+    for (name, fmt), d in fam.items():
+        per = collections.defaultdict(list)
+        for i, us in enumerate(d[96:]):
+            per[i % 4].append(us)
+        tot_us, tot_b = 0.0, 0
+        for j, (sn, N, K) in enumerate(SINGLE_SHAPES):
+            avg = sum(per[j]) / len(per[j])
+            b = N * K // 2 + N * (K // 64) * 4 if fmt == "w4" else N * K + 2 * N
+            tot_us += avg
+            tot_b += b
+            lines.append(f"| `{name}` | {sn} {N} x {K} | {avg:.2f} | {b / (avg * 1e-6) / 1e12:.2f} |")
+        summary[name] = {"pass_of_128_ms": round(32 * tot_us / 1e3, 4),
+                         "TBps": round(tot_b / (tot_us * 1e-6) / 1e12, 3)}
+        lines.append(f"| `{name}` | 128 GEMMs of a pass, sum | {32 * tot_us:.1f} | "
+                     f"{tot_b / (tot_us * 1e-6) / 1e12:.2f} |")
+    open(out + ".md", "w").write("\n".join(lines) + "\n")
+    json.dump(summary, open(out + ".json", "w"), indent=1)
+    print(json.dumps(summary))
+
+
 def main():
+    import sys
+    if "--single-gemm" in sys.argv:
+        sp = argparse.ArgumentParser()
+        sp.add_argument("--single-gemm", required=True, help="rocprofv3 --kernel-trace directory")
+        sp.add_argument("--title", required=True)
+        sp.add_argument("--command", required=True)
+        sp.add_argument("--out", required=True)
+        a = sp.parse_args()
+        single_gemm_summary(a.single_gemm, a.title, a.command, a.out)
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--trace", required=True)
     ap.add_argument("--pmc", required=True)
