@@ -708,18 +708,37 @@ def main():
         ms_i8, _ = time_graph(torch, int8_pass, 60, 60)
         ms_i8g, _ = time_graph(torch, lambda: sv.sv_pass_run(p8), 60, 60)
         ms_rot, _ = time_graph(torch, rotate, 20, 5)
+        # the same int8 x W4 GEMMs as 128 single launches on the row-major codes
+        L8 = [(lambda xq=xq, xs=xs, c=c, s=s, z=z, yy=yy:
+               sv.sv_qgemm_w4_i8(xq, xs, c, s, z, y=yy))
+              for (xq, xs, pc, ps, N, yy), (name, N2, K, c, s, z, pc2, ps2)
+              in zip(gi8, [g for layer in w4 for g in layer])]
+        ms_i8l, _ = time_graph(torch, lambda: [fn() for fn in L8], 20, 20)
+        del L8
         extra["int8_path"] = {"pass_ms": round(ms_i8, 4),
                               "GBps": round(pass_bytes / (ms_i8 * 1e-3) / 1e9, 1),
                               "gemm_launch_ms": round(ms_i8g, 4),
                               "gemm_GBps": round(pass_bytes / (ms_i8g * 1e-3) / 1e9, 1),
                               "hadamard_ms_all_rows": round(ms_rot, 4),
-                              "hadamard_rows": int((n_h + n_f) * k)}
+                              "hadamard_rows": int((n_h + n_f) * k),
+                              "row_major_launches_ms": round(ms_i8l, 4),
+                              "row_major_launches_GBps": round(
+                                  pass_bytes / (ms_i8l * 1e-3) / 1e9, 1)}
         extra["int8_path"]["quant_error"] = int8_quant_error(torch, sv, synth, w4[0], k, dev)
         del xo_h, xo_f
         log("W8 k sweep")
         # W8 k sweep on the executor (8-bit stack packed once)
         w8 = make_w8_stack(torch, synth, dev)
         b8 = w8_bytes(w8)
+        # the pass's W8 GEMMs as 128 single launches on the row-major codes
+        xh, xf = x_h[:k].contiguous(), x_f[:k].contiguous()
+        L8 = [(lambda xx=(xh if K == HIDDEN else xf), c=c, s=s, yy=y_own[li][gi][:k]:
+               sv.sv_qgemm_w8(xx, c, s, y=yy))
+              for li, layer in enumerate(w8) for gi, (name, N, K, c, s) in enumerate(layer)]
+        ms_l8, _ = time_graph(torch, lambda: [fn() for fn in L8], 20, 20)
+        extra["w8_row_major_launches"] = {"pass_ms": round(ms_l8, 4),
+                                          "GBps": round(b8 / (ms_l8 * 1e-3) / 1e9, 1)}
+        del L8
         w8p = [[(N, K, sv.sv_w8_pack(c), s) for (name, N, K, c, s) in layer] for layer in w8]
         del w8
         sweep8 = {}
