@@ -1,5 +1,6 @@
 // sv_w4_pack + sv_qgemm_w4_packed: the verify GEMM over 4-bit asymmetric
-// group-quantized weights stored in a tile-major layout made for gfx950.
+// group-quantized weights stored in a tile-major layout made for gfx950 (and
+// the streaming kernel of the single-GEMM entry points on row-major weights).
 //
 // Source: Karpathy's Trick for Faster Local LLMs, "How Uzu optimizes bytes and
 // tokens per pass" (4-bit asymmetric integer quantization, one scale per
@@ -42,10 +43,15 @@
 //    and integer z).
 //  * Split-K partials of the 8 waves are summed through LDS in a fixed order.
 //
-// The same kernel serves sv_qgemm_w4 on the row-major codes (K % 512 == 0,
-// sv_w4_rowmajor_gemm): each lane loads its 16 bytes of a row's k block
-// directly and one lane swap turns them into MFMA operands (see the kernel's
-// RM notes); scales and zeros are copied from their row-major arrays.
+// The same kernel serves the single-GEMM entry points on the row-major
+// formats (see the kernel's RM, I8 and W8 notes):
+//  * sv_qgemm_w4 (K % 512 == 0, sv_w4_rowmajor_gemm): each lane loads its 16
+//    bytes of a row's k block directly and one lane swap turns them into
+//    MFMA operands; scales and zeros are copied from their row-major arrays;
+//  * sv_qgemm_w4_i8 (K % 512 == 0, sv_w4_i8_rowmajor_gemm): the same weights
+//    against int8 activations, one v_mfma_i32_16x16x64_i8 per group;
+//  * sv_qgemm_w8 (sv_w8_rowmajor_gemm): 8-bit codes in 64-wide blocks,
+//    accumulated over the whole of K, one scale per channel.
 #include "w4_rowmajor.h"
 
 namespace {
