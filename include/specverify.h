@@ -334,12 +334,15 @@ sv_status sv_pass_chain_plan(int format, const sv_pass_link* links, int count, i
  *
  *   Y[r, n] = S[n] * sum_k X[r, k] * C[n, k]
  *
- *   x       bf16 [m, K], m in 1 .. 2^20 (rows are independent tokens; a
- *           verify pass may batch all its activation rows in one call), K % 64 == 0
+ *   x       bf16 [m, K], m in 1 .. SV_MAX_ROWS, K % 64 == 0
  *   codes   int8 [N, K], values in [-127, 127] (-128 is rejected by nothing
  *           but is outside the format; it dequantizes as -128 * S)
  *   scales  f16 [N]
  *   N % 16 == 0;  y f32 [m, N], fully overwritten.
+ *
+ * Every weight byte is read from HBM once for all m rows; binary32
+ * accumulation; deterministic.  SV_ERR_INVALID_ARG for m or K out of range
+ * or N % 16 != 0; SV_ERR_ALIGN for pointers not 16-byte aligned.
  */
 sv_status sv_qgemm_w8(const void* x, int m, int K, const int8_t* codes,
                       const void* scales, int N, float* y, hipStream_t stream);
