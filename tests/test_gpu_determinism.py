@@ -191,3 +191,27 @@ def test_passes_repeat_bitwise(m):
     for r in runs[1:]:
         for i, (a, b) in enumerate(zip(runs[0], r)):
             assert torch.equal(a, b), f"output {i} differs between runs"
+
+
+@pytest.mark.parametrize("m", [1, 16, 32])
+def test_single_gemms_repeat_bitwise(m):
+    # the single-GEMM entry points on their streaming kernels: row-major and
+    # packed W4, int8 x W4 and W8, on a 4096-channel and a 24576-channel matrix
+    sv = _sv()
+    print(f"single GEMMs m={m}", flush=True)
+    for N, K in ((4096, 12288), (24576, 4096)):
+        c, s, z = synth.w4_matrix(N, K, seed=N + K, device=DEV)
+        pc, ps = sv.sv_w4_pack(c, s, z)
+        c8, s8 = synth.w8_matrix(N, K, seed=N + K + 1, device=DEV)
+        x = synth.activations(m, K, seed=K, device=DEV)
+        xq, xs = synth.int8_activations(m, K, seed=K + 1, device=DEV)
+        calls = {
+            "w4": lambda y: sv.sv_qgemm_w4(x, c, s, z, y=y),
+            "w4_packed": lambda y: sv.sv_qgemm_w4_packed(x, pc, ps, N, y=y),
+            "w4_i8": lambda y: sv.sv_qgemm_w4_i8(xq, xs, c, s, z, y=y),
+            "w8": lambda y: sv.sv_qgemm_w8(x, c8, s8, y=y),
+        }
+        for name, call in calls.items():
+            y = torch.empty((m, N), dtype=torch.float32, device=DEV)
+            runs = _repeat(lambda: call(y), {"y": y}, None)
+            _assert_same(runs, f"{name} {N}x{K} m={m}")
