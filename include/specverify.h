@@ -342,7 +342,8 @@ sv_status sv_pass_chain_plan(int format, const sv_pass_link* links, int count, i
  *
  * Every weight byte is read from HBM once for all m rows; binary32
  * accumulation; deterministic.  SV_ERR_INVALID_ARG for m or K out of range
- * or N % 16 != 0; SV_ERR_ALIGN for pointers not 16-byte aligned.
+ * or N % 16 != 0; SV_ERR_ALIGN for pointers not 16-byte aligned;
+ * SV_ERR_UNSUPPORTED for N * K >= 2^31 (a matrix of 2 GiB or more).
  */
 sv_status sv_qgemm_w8(const void* x, int m, int K, const int8_t* codes,
                       const void* scales, int N, float* y, hipStream_t stream);

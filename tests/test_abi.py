@@ -55,6 +55,8 @@ def test_argument_validation_before_launch():
     assert L.sv_qgemm_w4(fake, 33, 512, fake, fake, fake, 64, 64, fake, None) == 2
     assert L.sv_qgemm_w4(fake, 4, 512, fake, fake, fake, 40, 64, fake, None) == 2
     assert L.sv_qgemm_w8(fake, 4, 100, fake, fake, 64, fake, None) == 2
+    # a W8 matrix of 2 GiB or more (32-bit buffer offsets)
+    assert L.sv_qgemm_w8(fake, 4, 65536, fake, fake, 32768, fake, None) == 4
     # misaligned pointer
     assert L.sv_qgemm_w4(odd, 4, 512, fake, fake, fake, 64, 64, fake, None) == 3
     # Hadamard block must be a power of two dividing K, at most 4096
