@@ -115,6 +115,42 @@ def test_chain_links_match_oracle(m):
             _check_xo(xo.cpu(), y64, got, a, cols, f"m={m} K={K} N={N}")
 
 
+# Rounds longer than the weight ring: ragged k-block counts (35 and 19
+# blocks: the last step of some waves is empty), 1, 2 and 6 tiles per
+# workgroup, and a 96-block link (12 steps per wave).  The grid is 40
+# workgroups.
+LONG_LINKS = [(256, 640, 640), (4480, 640, 640), (2432, 1280, 1280), (12288, 640, 640),
+              (4096, 3840, 0), (640, 640, 0)]
+
+
+@pytest.mark.parametrize("m", [1, 16, 17])
+def test_chain_long_rounds_match_oracle(m):
+    sv = _sv()
+    links, refs = [], []
+    for i, (K, N, cols) in enumerate(LONG_LINKS):
+        host, pc, ps = _weights(N, K, seed=900 + 17 * i + m)
+        x = synth.activations(m, K, seed=950 + i + m)
+        y = _nan((m, N), torch.float32)
+        xo = _nan((m, cols), torch.bfloat16) if cols else None
+        a = alpha_for(K)
+        links.append((x.to(DEV), pc, ps, N, y, xo, a))
+        refs.append((x, host, a, cols))
+    p = sv.sv_pass_chain_plan(links)
+    assert p.grid == 40 and p.info.chain == 1
+    for _ in range(2):                                  # the same plan twice
+        sv.sv_pass_run(p)
+        torch.cuda.synchronize()
+        assert sv.sv_pass_status(p) == 0
+        for (K, N, cols), (x, pc, ps, _, y, xo, a), (xh, host, _a, _c) in zip(LONG_LINKS, links, refs):
+            y64 = oracle.qgemm_w4(bf16_bits(xh), *host)
+            got = y.cpu().numpy()
+            assert np.isfinite(got).all()
+            assert_rows_close(got, y64, what=f"chain link m={m} K={K} N={N}")
+            if cols:
+                _check_xo(xo.cpu(), y64, got, a, cols, f"m={m} K={K} N={N}")
+            y.fill_(float("nan"))
+
+
 def _decoder_chain(layers, m, H, F, seed, h0=None):
     """qkv -> o -> gate|up -> down per layer; each link's x is the previous
     link's xo (q, gate and down part as the hand-off)."""
