@@ -247,14 +247,16 @@ def test_chain_graph_replays():
     assert sv.sv_pass_status(p) == 0
 
 
-def test_chain_9b_stack_k16_sampled():
-    """The 32-layer, 3.93 GB stack chained in model order at k = 16, in the
-    launch configuration of the benchmark: 16 sampled channels of every y
+@pytest.mark.parametrize("m", [16, 1, 32])
+def test_chain_9b_stack_sampled(m):
+    """The 32-layer, 3.93 GB stack chained in model order at k = m, in the
+    launch configuration of the benchmark (k = 16) and of its k sweep (k = 1;
+    k = 32, where gate/up runs as two rounds): 16 sampled channels of every y
     against the product of the link's actual input with the oracle's
     dequantized weights (the first link against the oracle outright), every
     xo bit-exactly the hand-off of its y."""
     sv = _sv()
-    H, F, m = 4096, 12288, 16
+    H, F = 4096, 12288
     h = synth.activations(m, H, seed=11, device=DEV)
     links, hosts, samples = [], [], []
     rng = np.random.default_rng(2025)
