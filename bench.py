@@ -672,8 +672,9 @@ def main():
         log("int8 path")
         # int8 path: every activation row of the pass (4 inputs per layer, 41 or
         # 123 outlier channels x50) rotated by the block-4096 Hadamard and
-        # quantized per token -- batched into one call per input width -- then
-        # all 128 int8 x W4 GEMMs in one executor launch
+        # quantized per token -- batched into one call per input width, and
+        # timed again as one call per link as a model runs it -- then all 128
+        # int8 x W4 GEMMs in one executor launch
         n_h, n_f = 3 * LAYERS, LAYERS               # qkv, o, gate|up inputs; down inputs
         signs_h = synth.hadamard_signs(HIDDEN, seed=3, device=dev)
         signs_f = synth.hadamard_signs(FFN, seed=4, device=dev)
@@ -708,6 +709,21 @@ def main():
         ms_i8, _ = time_graph(torch, int8_pass, 60, 60)
         ms_i8g, _ = time_graph(torch, lambda: sv.sv_pass_run(p8), 60, 60)
         ms_rot, _ = time_graph(torch, rotate, 20, 5)
+        # In a model each rotation waits for the link before it, so it runs as
+        # one call per GEMM input (k rows each), 128 calls in layer order.
+        rot_calls, ih, jf = [], 0, 0
+        for layer in w4:
+            for (name, N, K, *_rest) in layer:
+                if K == HIDDEN:
+                    xin, sg, ih = xo_h[ih * k:(ih + 1) * k], signs_h, ih + 1
+                else:
+                    xin, sg, jf = xo_f[jf * k:(jf + 1) * k], signs_f, jf + 1
+                outq = torch.empty((k, K), dtype=torch.int8, device=dev)
+                outs = torch.empty((k,), dtype=torch.float32, device=dev)
+                rot_calls.append(lambda xin=xin, sg=sg, outq=outq, outs=outs:
+                                 sv.sv_hadamard_i8(xin, sg, 4096, outq, outs))
+        ms_rot_link, _ = time_graph(torch, lambda: [fn() for fn in rot_calls], 20, 5)
+        del rot_calls
         # the same int8 x W4 GEMMs as 128 single launches on the row-major codes
         L8 = [(lambda xq=xq, xs=xs, c=c, s=s, z=z, yy=yy:
                sv.sv_qgemm_w4_i8(xq, xs, c, s, z, y=yy))
@@ -721,6 +737,8 @@ def main():
                               "gemm_GBps": round(pass_bytes / (ms_i8g * 1e-3) / 1e9, 1),
                               "hadamard_ms_all_rows": round(ms_rot, 4),
                               "hadamard_rows": int((n_h + n_f) * k),
+                              "hadamard_ms_per_link_calls": round(ms_rot_link, 4),
+                              "hadamard_calls_per_link": len(w4) * len(w4[0]),
                               "row_major_launches_ms": round(ms_i8l, 4),
                               "row_major_launches_GBps": round(
                                   pass_bytes / (ms_i8l * 1e-3) / 1e9, 1)}

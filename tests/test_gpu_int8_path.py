@@ -47,6 +47,22 @@ def test_hadamard_codes_and_scales(m, K, block, outliers):
     assert not np.any(diff & ~ties), f"{int((diff & ~ties).sum())} code mismatches off ties"
 
 
+@pytest.mark.parametrize("K", [4096, 12288, 16384])
+def test_hadamard_few_row_form_matches_many_row_form(K):
+    """Calls of fewer than 256 rows run four waves per 4096-block, larger calls
+    one wave per block: the same rows give the same codes and scales bit for
+    bit (the butterflies meet the same pairs in the same order)."""
+    sv = _sv()
+    x, _ = synth.outlier_activations(300, K, seed=77 + K)
+    xd, sd = to_dev(x, synth.hadamard_signs(K, seed=9))
+    q_all, s_all = sv.sv_hadamard_i8(xd, sd, 4096)          # 300 rows: one wave per block
+    for lo, hi in ((0, 1), (5, 21), (40, 295)):            # 1, 16 and 255 rows
+        q, s = sv.sv_hadamard_i8(xd[lo:hi], sd, 4096)
+        torch.cuda.synchronize()
+        assert torch.equal(q, q_all[lo:hi]), (K, lo, hi)
+        assert torch.equal(s.view(torch.int32), s_all[lo:hi].view(torch.int32)), (K, lo, hi)
+
+
 def test_hadamard_zero_row():
     sv = _sv()
     K = 4096

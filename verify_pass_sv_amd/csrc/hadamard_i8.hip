@@ -13,11 +13,15 @@
 // the sign flip; each value is rounded once to binary32 after the b^-1/2
 // scale.  The row maximum, the scale amax/127 and the round-half-to-even
 // decision are binary32.  Negligible bytes: latency-bound.
-//   * block 4096 (the verify pass's block): one wave per 4096-wide block.
-//     Each lane holds 64 contiguous values in registers; the six stages with
-//     partners inside a lane run in registers, a padded LDS transpose then
-//     gives each lane the values 64 apart, and the last six stages run in
-//     registers again.  No workgroup barrier until the row maximum.
+//   * block 4096 (the verify pass's block), calls of 256 rows or more: one
+//     wave per 4096-wide block.  Each lane holds 64 contiguous values in
+//     registers; the six stages with partners inside a lane run in
+//     registers, a padded LDS transpose then gives each lane the values 64
+//     apart, and the last six stages run in registers again.  No workgroup
+//     barrier until the row maximum.
+//   * block 4096, fewer rows (one link's k rows): four waves per block, 16
+//     values per lane, two LDS transposes; a quarter of the serial
+//     instruction stream per wave.
 //   * other blocks: the row is staged in LDS and all blocks of the row are
 //     transformed in place, stage by stage.
 // Both orders of butterflies are the same, so both give identical binary64
@@ -198,6 +202,104 @@ __global__ __launch_bounds__(256) void hadamard4096_i8_kernel(
   }
 }
 
+// ---- block 4096, few rows: four waves per block ------------------------------
+// The latency form, for calls with few rows (a verify pass rotating one
+// link's k rows at a time): four waves per 4096-block, 16 values per lane.
+// Stages h = 1..8 run in registers on the lane's 16 contiguous values; a
+// padded LDS transpose gives each lane the 16 values of index bits 4-7
+// (stages h = 16..128), a second one those of bits 8-11 (h = 256..2048).
+// The stages run in the same ascending order on the same pairs as in the
+// one-wave kernel, so every binary64 value and code is the same.
+constexpr int kPadB = kB4 + kB4 / 16;             // doubles per block: one pad per 16
+constexpr int kFewRows = 256;                     // calls below this many rows
+
+__device__ __forceinline__ int padx(int e) { return e + (e >> 4); }
+
+__global__ __launch_bounds__(1024) void hadamard4096x4_i8_kernel(
+    const uint16_t* __restrict__ x, int K, const int8_t* __restrict__ signs,
+    int8_t* __restrict__ xq, float* __restrict__ xscale) {
+  extern __shared__ double tb4[];                // kPadB doubles per block
+  __shared__ float wmax[16];
+  const int r = blockIdx.x;
+  const int t = threadIdx.x & 255;               // thread of the block
+  const int base = (threadIdx.x >> 8) * kB4;     // the block's first element
+  double* const tb = tb4 + (threadIdx.x >> 8) * kPadB;
+  // element 16 t + i of the block
+  double v[16];
+  {
+    const uint16_t* xr = x + static_cast<size_t>(r) * K + base + 16 * t;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const sv_u32x4 w = sv_ld16(xr + 8 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * h + 2 * e] = static_cast<double>(__uint_as_float(w[e] << 16));
+        v[8 * h + 2 * e + 1] = static_cast<double>(__uint_as_float(w[e] & 0xFFFF0000u));
+      }
+    }
+    const sv_u32x4 sw = sv_ld16(signs + base + 16 * t);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int sgn = static_cast<int8_t>((sw[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+      v[e] *= static_cast<double>(sgn);
+    }
+  }
+  // index bits 0-3
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if ((i & h) == 0) bfly(v[i], v[i + h]);
+  // transpose 1: thread t takes the elements ((t >> 4) << 8) | (j << 4) | (t & 15)
+  const int e1 = ((t >> 4) << 8) | (t & 15);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) tb[padx(16 * t + i)] = v[i];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = tb[padx(e1 | (j << 4))];
+  // index bits 4-7
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if ((j & h) == 0) bfly(v[j], v[j + h]);
+  __syncthreads();                               // transpose 1 read everywhere
+  // transpose 2: thread t takes the elements (j << 8) | t
+#pragma unroll
+  for (int j = 0; j < 16; ++j) tb[padx(e1 | (j << 4))] = v[j];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = tb[padx((j << 8) | t)];
+  // index bits 8-11
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if ((j & h) == 0) bfly(v[j], v[j + h]);
+
+  float f[16];
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    f[j] = static_cast<float>(v[j] / 64.0);      // 4096^-1/2, exact
+    amax = fmaxf(amax, fabsf(f[j]));
+  }
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  float rmax = 0.f;
+  const int nw = blockDim.x >> 6;
+  for (int w = 0; w < nw; ++w) rmax = fmaxf(rmax, wmax[w]);
+  const float scale = rmax > 0.f ? rmax / 127.0f : 1.0f;
+  if (threadIdx.x == 0) xscale[r] = scale;
+  int8_t* out = xq + static_cast<size_t>(r) * K + base + t;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float q = rintf(f[j] / scale);
+    out[256 * j] = static_cast<int8_t>(fminf(127.f, fmaxf(-127.f, q)));
+  }
+}
+
 }  // namespace
 
 extern "C" sv_status sv_hadamard_i8(const void* x, int m, int K, const int8_t* signs,
@@ -209,6 +311,19 @@ extern "C" sv_status sv_hadamard_i8(const void* x, int m, int K, const int8_t* s
     return SV_ERR_INVALID_ARG;
   if (!sv_aligned16(x) || !sv_aligned16(signs) || !sv_aligned16(xq) || !sv_aligned16(xscale))
     return SV_ERR_ALIGN;
+  if (block == kB4 && K % kB4 == 0 && m < kFewRows) {
+    const int nb = K / kB4;                        // 1 to 4 blocks: 256 to 1024 threads
+    const size_t lds = static_cast<size_t>(nb) * kPadB * sizeof(double);
+    if (lds > 65536 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(hadamard4096x4_i8_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(4 * kPadB * sizeof(double))) != hipSuccess)
+      return SV_ERR_HIP;
+    hipLaunchKernelGGL(hadamard4096x4_i8_kernel, dim3(m), dim3(256 * nb), lds, stream,
+                       static_cast<const uint16_t*>(x), K, signs, xq, xscale);
+    SV_LAUNCH_CHECK();
+    return SV_OK;
+  }
   if (block == kB4 && K % kB4 == 0) {
     const int nw = K / kB4;
     const size_t lds4 = static_cast<size_t>(nw) * kPadRow * sizeof(double);
