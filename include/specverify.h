@@ -269,7 +269,7 @@ sv_status sv_pass_status(const sv_pass* pass, uint32_t* status, hipStream_t stre
  * Trick ..., "How Uzu optimizes bytes and tokens per pass": the activations
  * are the intermediate values passed between layers; "Why batch-one decoding
  * is memory-bound": the pass reads every layer's weight blocks once).  A
- * chain is an ordered array of links, each one W4 GEMM
+ * chain is an ordered array of links, each one W4 or W8 GEMM
  *   y = x W^T                         (y f32 [m, N], fully overwritten)
  * that may also write the bf16 input of a later link
  *   xo = bf16_rne(alpha * y[:, :xo_cols])     (xo bf16 [m, xo_cols]).
@@ -292,7 +292,9 @@ sv_status sv_pass_status(const sv_pass* pass, uint32_t* status, hipStream_t stre
  * link's xo is exactly that xo; no xo overlaps the x of its own or an
  * earlier link, or another xo; no y overlaps any x, xo or other y.  Later
  * links may read only xo, never y, of earlier links.
- * Formats: SV_PASS_W4 (W8 and W4_I8 return SV_ERR_UNSUPPORTED); group 64.
+ * Formats: SV_PASS_W4 (codes and scale/zero records from sv_w4_pack; group
+ * 64) and SV_PASS_W8 (codes from sv_w8_pack, `scales` the f16 [N] channel
+ * scales); SV_PASS_W4_I8 returns SV_ERR_UNSUPPORTED.
  * sv_pass_chain_bytes: plan buffer bytes (0 if an argument is invalid); the
  * plan buffer must be 256-byte aligned.  sv_pass_chain_plan validates,
  * writes the plan (its barrier counters included) with `stream`,

@@ -141,7 +141,8 @@ def test_chain_buffer_rules():
     bad[0]["xo"] += 64                          # xo not 128-byte aligned
     bad[1]["x"] += 64
     assert status(bad) == 3
-    assert status(base, fmt="w8") == 4          # W8 chains are not built
+    assert status(base, fmt="w8") == 0          # W8 chains are built
+    assert status(base, fmt="w4_i8") == 4       # int8 chains are not
     assert status(base, m=33) == 2
     bad = [dict(d) for d in base]
     bad[0]["xo"] = 0                            # xo_cols without an xo

@@ -344,3 +344,81 @@ def test_barrier_timeout_is_reported_and_the_launch_ends():
     torch.cuda.synchronize()
     assert sv.sv_pass_status(p) == 0
     _check_chain(links, hosts)
+
+
+def alpha_for_w8(K):
+    """The same for the synthetic W8 weights: E[w^2] = E[c^2] E[s^2] with c
+    uniform on -127..127 (E[c^2] = 127 * 128 / 3) and s ~ U(0.01, 0.05)."""
+    ew2 = (127 * 128 / 3.0) * ((0.05 ** 3 - 0.01 ** 3) / (3 * 0.04))
+    return float(np.float32(1.0 / np.sqrt(K * ew2)))
+
+
+def _weights8(N, K, seed):
+    codes, scales = synth.w8_matrix(N, K, seed=seed)
+    sv = _sv()
+    return (codes.numpy(), scales.numpy()), sv.sv_w8_pack(codes.to(DEV)), scales.to(DEV)
+
+
+@pytest.mark.parametrize("m", [1, 16, 17, 32])
+def test_w8_chain_links_match_oracle(m):
+    """The W8 chain on independent links (one to six tiles per workgroup, two
+    rounds at m > 16, ragged k-block counts): every y against the oracle's W8
+    GEMM, every xo bit-exactly the hand-off of its y."""
+    sv = _sv()
+    links, refs = [], []
+    for i, (K, N, cols) in enumerate(LINKS + LONG_LINKS[1:3]):
+        host, pc, sc = _weights8(N, K, seed=1300 + 7 * i + m)
+        x = synth.activations(m, K, seed=1400 + i + m)
+        y = _nan((m, N), torch.float32)
+        xo = _nan((m, cols), torch.bfloat16) if cols else None
+        a = alpha_for_w8(K)
+        links.append((x.to(DEV), pc, sc, N, y, xo, a))
+        refs.append((x, host, a, cols))
+    p = sv.sv_pass_chain_plan(links, fmt="w8")
+    assert p.grid == 40 and p.info.chain == 1
+    sv.sv_pass_run(p)
+    torch.cuda.synchronize()
+    assert sv.sv_pass_status(p) == 0
+    for (x, pc, sc, N, y, xo, a), (xh, host, _a, cols) in zip(links, refs):
+        y64 = oracle.qgemm_w8(bf16_bits(xh), *host)
+        got = y.cpu().numpy()
+        assert np.isfinite(got).all()
+        assert_rows_close(got, y64, what=f"W8 chain link m={m} K={xh.shape[1]} N={N}")
+        if cols:
+            assert np.array_equal(bf16_bits(xo), _rne_handoff(got, a, cols)), (m, N)
+
+
+def test_w8_chain_9b_stack_sampled():
+    """The 32-layer W8 stack (6.98 GB) in model order at k = 16: 16 sampled
+    channels of every y against the link's actual input times the oracle's
+    dequantized weights, the first link against the oracle outright, every xo
+    the hand-off of its y."""
+    sv = _sv()
+    H, F, m = 4096, 12288, 16
+    h = synth.activations(m, H, seed=21, device=DEV)
+    links, samples = [], []
+    rng = np.random.default_rng(2026)
+    for layer in range(32):
+        for i, (N, K, cols) in enumerate(((3 * H, H, H), (H, H, H), (2 * F, H, F), (H, F, H))):
+            c, s = synth.w8_matrix(N, K, seed=3000 + 10 * layer + i, device=DEV)
+            pc = sv.sv_w8_pack(c)
+            rows = np.sort(rng.choice(N, size=16, replace=False))
+            ri = torch.as_tensor(rows, device=DEV)
+            samples.append((rows, c[ri].cpu().numpy(), s[ri].cpu().numpy()))
+            del c
+            xo = _nan((m, cols), torch.bfloat16)
+            links.append((h, pc, s, N, _nan((m, N), torch.float32), xo, alpha_for_w8(K)))
+            h = xo
+    p = sv.sv_pass_chain_plan(links, fmt="w8")
+    sv.sv_pass_run(p)
+    torch.cuda.synchronize()
+    assert sv.sv_pass_status(p) == 0
+    for j, ((x, pc, s, N, y, xo, a), (rows, c, sc)) in enumerate(zip(links, samples)):
+        got = y.cpu().numpy()
+        assert np.isfinite(got).all(), f"link {j}"
+        ref = _as_f64(x) @ oracle.dequant_w8(c, sc).T
+        assert_rows_close(got[:, rows], ref, what=f"W8 9B chain link {j} N={N}")
+        assert np.array_equal(bf16_bits(xo), _rne_handoff(got, a, xo.shape[1])), j
+        if j == 0:
+            assert_rows_close(got[:, rows], oracle.qgemm_w8(bf16_bits(x), c, sc),
+                              what="W8 9B chain first link (oracle)")

@@ -326,9 +326,10 @@ def sv_pass_status(p, stream=None):
     return int(v.value)
 
 
-def _chain_links(links, group):
+def _chain_links(links, group, fmt="w4"):
     """links: sequence of (x bf16 [m, K], packed_codes, packed_sz, N, y f32 [m, N],
-    xo bf16 [m, xo_cols] or None, alpha)."""
+    xo bf16 [m, xo_cols] or None, alpha); for "w8" the codes are sv_w8_pack's
+    and packed_sz is the f16 [N] channel scales."""
     arr = (SvPassLink * len(links))()
     m, keep = None, []
     for i, (x, codes, sc, N, y, xo, alpha) in enumerate(links):
@@ -337,8 +338,12 @@ def _chain_links(links, group):
         if mm != m:
             raise ValueError("every link of a chain has the same number of rows m")
         _need(x, "x", torch.bfloat16)
-        _need(codes, "packed_codes", torch.uint8, (N * K // 2,))
-        _need(sc, "packed_sz", torch.float16, (N * (K // group) * 2,))
+        if fmt == "w8":
+            _need(codes, "packed_codes", torch.uint8, (N * K,))
+            _need(sc, "scales", torch.float16, (N,))
+        else:
+            _need(codes, "packed_codes", torch.uint8, (N * K // 2,))
+            _need(sc, "packed_sz", torch.float16, (N * (K // group) * 2,))
         _need(y, "y", torch.float32, (m, N))
         xo_cols = 0
         if xo is not None:
@@ -352,8 +357,8 @@ def _chain_links(links, group):
     return arr, m, keep
 
 
-def sv_pass_chain_plan(links, group=64, stream=None, plan=None):
-    """Plan a verify pass in model order (W4).  links: sequence of
+def sv_pass_chain_plan(links, group=64, stream=None, plan=None, fmt="w4"):
+    """Plan a verify pass in model order (fmt "w4" or "w8").  links: sequence of
     (x, packed_codes, packed_sz, N, y, xo, alpha) -- see _chain_links; a link
     whose x is an earlier link's xo waits for every earlier link.  `plan`: an
     optional uint8 device buffer to plan into (256-byte aligned), e.g. one
@@ -361,8 +366,10 @@ def sv_pass_chain_plan(links, group=64, stream=None, plan=None):
     Synchronizes `stream`."""
     if len(links) == 0:
         raise ValueError("a chain needs at least one link")
-    arr, m, keep = _chain_links(links, group)
-    nbytes = int(lib.sv_pass_chain_bytes(PASS_FORMATS["w4"], arr, len(links), m))
+    if fmt not in ("w4", "w8"):
+        raise ValueError("a chain runs the w4 or w8 format")
+    arr, m, keep = _chain_links(links, group, fmt)
+    nbytes = int(lib.sv_pass_chain_bytes(PASS_FORMATS[fmt], arr, len(links), m))
     if nbytes == 0:
         raise SvError("sv_pass_chain_bytes", 2)
     if plan is None:
@@ -376,7 +383,7 @@ def sv_pass_chain_plan(links, group=64, stream=None, plan=None):
         nbytes = plan.numel()
     info = SvPass()
     _check("sv_pass_chain_plan", lib.sv_pass_chain_plan(
-        PASS_FORMATS["w4"], arr, len(links), m, group, _ptr(plan), nbytes, ctypes.byref(info),
+        PASS_FORMATS[fmt], arr, len(links), m, group, _ptr(plan), nbytes, ctypes.byref(info),
         _stream(stream)))
     return Pass(raw, info, keep)
 

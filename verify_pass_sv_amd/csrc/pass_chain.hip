@@ -9,7 +9,8 @@
 // draft positions are scored in that one pass).
 //
 // A chain is an ordered list of links.  Link i computes
-//   y_i = x_i W_i^T                      (f32 [m, N_i], 4-bit group-64 weights)
+//   y_i = x_i W_i^T     (f32 [m, N_i]; W4: 4-bit group-64 weights, W8: 8-bit
+//                        codes with one scale per output channel)
 // and, optionally, the input of a later link
 //   xo_i = bf16_rne(alpha_i * y_i[:, :xo_cols_i])   (bf16 [m, xo_cols_i]).
 // A link whose x is an earlier link's xo waits, at a device-wide phase
@@ -61,12 +62,19 @@
 // rank-2 v_mfma_f32_16x16x4_f32 update t -= sum_g xsum[r, g] s[n, g]
 // (128 + z[n, g]) whose row sums come from all-ones MFMAs on the same
 // activation operand.  For a one-hot row and integer z every step is exact.
+//
+// W8 (two 1 KiB units of 64 k per block, the layout of sv_w8_pack): bf16
+// 128 + c by a sign flip and byte conversions, the MFMAs accumulate
+// sum x (128 + c) over the whole round, all-ones MFMAs the row sums; each
+// wave subtracts 128 times its row sums before the reduction, and the
+// channel scale (loaded first in the round) multiplies the sum.
 #include <algorithm>
 #include <cstddef>
 #include <type_traits>
 #include <vector>
 
 #include "w4_packed_dev.h"
+#include "w4_rowmajor.h"
 
 namespace {
 
@@ -161,7 +169,7 @@ __device__ __forceinline__ unsigned int bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int MT>
+template <int MT, int F>
 // `plan` (header and rounds) is only read; `sync` (counters and status, at
 // plan + sync_off(nrounds)) is written.  Kept as two restrict pointers so the
 // plan's uniform fields load through the scalar cache.
@@ -173,7 +181,7 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
   const ChainHeader* hdr = reinterpret_cast<const ChainHeader*>(plan);
   unsigned int* const status = reinterpret_cast<unsigned int*>(sync + kStatusOff);
   if (hdr->magic != kChainMagic) return;                 // not a chain plan: touch nothing
-  if (hdr->version != kChainVersion || hdr->format != SV_PASS_W4 || hdr->m != m ||
+  if (hdr->version != kChainVersion || hdr->format != F || hdr->m != m ||
       hdr->grid != static_cast<int>(gridDim.x) || hdr->nrounds != nrounds) {
     if (threadIdx.x == 0) atomicOr(status, SV_PASS_STATUS_STALE);
     return;
@@ -268,11 +276,17 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
   const sv_u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const sv_f32x4 fz = {0.f, 0.f, 0.f, 0.f};
 
+  constexpr bool W8 = F == SV_PASS_W8;
   sv_f32x4 yacc[TM][MT];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int a = 0; a < MT; ++a) yacc[i][a] = fz;
+  // W8: the wave's activation row sums (lane (col, q): rows 4q .. 4q + 3)
+  sv_f32x4 xacc[MT];
+#pragma unroll
+  for (int a = 0; a < MT; ++a) xacc[a] = fz;
+  float csc = 0.f;                                // W8: channel scale of the wave's output pair
 
   float* const tpose = reinterpret_cast<float*>(lds + G::TPOSE) + wave * 256;
   uint8_t* const act = lds + wave * G::WAVEB;     // this wave's activation block ring
@@ -325,23 +339,45 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
     const int W = (KB + kSW - 1) / kSW;
     const int ntile = N / 16;
     const int t0 = rd.tile0 + wg;
+    // W4: 1 KiB units of 128 k and their scale/zero records; W8: two 1 KiB
+    // units of 64 k per 128-k block and the f16 channel scales
     const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(rd.codes), 0, N * (K / 2), 0x00020000);
+        const_cast<uint8_t*>(rd.codes), 0, W8 ? N * K : N * (K / 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(rd.sz), 0, N * (K / 64) * 4, 0x00020000);
+        const_cast<void*>(rd.sz), 0, W8 ? N * 2 : N * (K / 64) * 4, 0x00020000);
+    if constexpr (W8) {
+      // the channel scale of this wave's output pair, issued before every
+      // other load of the round (so it is not counted in any wait below)
+      const int tile = t0 + (wave / MT) * grid;
+      const unsigned int off = wave < T * MT ? static_cast<unsigned int>((16 * tile + col) * 2)
+                                             : kSvOutOfRange;
+      csc = __half2float(__builtin_bit_cast(
+          __half, static_cast<unsigned short>(__builtin_amdgcn_raw_buffer_load_b16(
+                      srs, off, 0, kStreamC))));
+    }
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(rd.x), 0, m * K * 2, 0x00020000);
     sv_u32x4 wb[P][T];
-    sv_u32x2 szr[P][T];
-    // unit (w, i) -> ring slot [w % P][i]
+    // W4: the lane's 8 bytes of the record; W8: the second 64-k unit
+    std::conditional_t<W8, sv_u32x4, sv_u32x2> szr[P][T];
+    // unit (w, i) -> ring slot [w % P][i]; two loads per unit in both formats
     auto issue = [&](const int p, const int i, const int w) {
       const int b = w * kSW + wave;
       const bool ok = w < W && b < KB;
-      const int blk = ok ? sv_pk_block(t0 + i * grid, b, KB, ntile) : 0;
-      wb[p][i] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? lane * 16 : kSvOutOfRange,
-                                                       blk * 1024, kStreamC);
-      szr[p][i] = __builtin_amdgcn_raw_buffer_load_b64(srs, ok ? col * 8 : kSvOutOfRange,
-                                                       blk * 128, kStreamC);
+      if constexpr (W8) {
+        const int blk = ok ? sv_pk_block(t0 + i * grid, 2 * b, 2 * KB, ntile) : 0;
+        const int blk1 = ok ? sv_pk_block(t0 + i * grid, 2 * b + 1, 2 * KB, ntile) : 0;
+        wb[p][i] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? lane * 16 : kSvOutOfRange,
+                                                         blk * 1024, kStreamC);
+        szr[p][i] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? lane * 16 : kSvOutOfRange,
+                                                          blk1 * 1024, kStreamC);
+      } else {
+        const int blk = ok ? sv_pk_block(t0 + i * grid, b, KB, ntile) : 0;
+        wb[p][i] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? lane * 16 : kSvOutOfRange,
+                                                         blk * 1024, kStreamC);
+        szr[p][i] = __builtin_amdgcn_raw_buffer_load_b64(srs, ok ? col * 8 : kSvOutOfRange,
+                                                         blk * 128, kStreamC);
+      }
     };
     // activation block of step w -> ring slot w % A.  Load L brings rows
     // 4 L .. 4 L + 3 (lane l: row 4 L + l / 16, LDS column l % 16, which
@@ -407,6 +443,16 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
                 a0[h][a] = *reinterpret_cast<const sv_u32x4*>(rp + ((c0 ^ col) << 4));
                 a1[h][a] = *reinterpret_cast<const sv_u32x4*>(rp + (((c0 + 1) ^ col) << 4));
               }
+              if constexpr (W8) {
+                // row sums in the output layout: activations times all-ones
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                  xacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                      sv_as_bf16x8(a0[h][a]), sv_as_bf16x8(ones), xacc[a], 0, 0, 0);
+                  xacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                      sv_as_bf16x8(a1[h][a]), sv_as_bf16x8(ones), xacc[a], 0, 0, 0);
+                }
+              } else {
               // group row sums: an all-ones A operand puts the sum of row col
               // on lane (col, q); the correction wants group q on lane (col, q)
               sv_f32x4 g0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -418,11 +464,32 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
               g1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sv_as_bf16x8(ones),
                                                            sv_as_bf16x8(a1[1][a]), g1, 0, 0, 0);
               xsA[a] = q == 0 ? g0[0] : (q == 1 ? g1[0] : 0.0f);
+              }
             }
           }
 #pragma unroll
           for (int i = 0; i < T; ++i) {
-            if (valid) {
+            if constexpr (W8) {
+             if (valid) {
+              // unit 2b + h holds k = 64 h + 16 q + [0, 16) of the block for
+              // channel col: the k of a0[h] then a1[h]
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const sv_u32x4 wv = h ? szr[p][i] : wb[p][i];
+                const sv_u32x2 l0 = sv_w8_cvt4_bias128(wv.x), l1 = sv_w8_cvt4_bias128(wv.y);
+                const sv_u32x2 h0 = sv_w8_cvt4_bias128(wv.z), h1 = sv_w8_cvt4_bias128(wv.w);
+                const sv_u32x4 b0 = {l0.x, l0.y, l1.x, l1.y};
+                const sv_u32x4 b1 = {h0.x, h0.y, h1.x, h1.y};
+#pragma unroll
+                for (int a = 0; a < MT; ++a) {
+                  yacc[i][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                      sv_as_bf16x8(a0[h][a]), sv_as_bf16x8(b0), yacc[i][a], 0, 0, 0);
+                  yacc[i][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                      sv_as_bf16x8(a1[h][a]), sv_as_bf16x8(b1), yacc[i][a], 0, 0, 0);
+                }
+              }
+             }
+            } else if (valid) {
               const sv_u32x4 wv = wb[p][i];
               const sv_u32x2 sv = szr[p][i];
               sv_f32x4 t[MT];
@@ -503,6 +570,17 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
 
     // ---- end of the round: fixed-order sum of the 8 waves' partial sums ----
     sv_barrier_no_fence();                        // E1: every wave done with its blocks
+    if constexpr (W8) {
+      // W8: y = s (sum x (128 + c) - 128 sum x), the bias folded per wave
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int a = 0; a < MT; ++a)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) yacc[i][a][j] = fmaf(-128.0f, xacc[a][j], yacc[i][a][j]);
+#pragma unroll
+      for (int a = 0; a < MT; ++a) xacc[a] = fz;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if (i < T) {
@@ -534,6 +612,10 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
               *reinterpret_cast<const sv_f32x4*>(lds + (v * kSW + j) * 1024 + lane * 16);
 #pragma unroll
           for (int i = 0; i < 4; ++i) s[i] += p[i];
+        }
+        if constexpr (W8) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[i] *= csc;    // lane (col, q): channel col
         }
         // MFMA layout (lane (col, q): rows 4q .. 4q + 3 of channel col) ->
         // lane l: row l / 4, channels 4 (l % 4) .. + 3
@@ -581,9 +663,9 @@ __global__ __launch_bounds__(kThreadsC) void chain_kernel(const uint8_t* __restr
   sv_wait_vmcnt<0>();
 }
 
-template <int MT>
+template <int MT, int F>
 sv_status launch_chain(void* plan, int nrounds, int m, int grid, hipStream_t st) {
-  auto kern = chain_kernel<MT>;
+  auto kern = chain_kernel<MT, F>;
   constexpr int kLds = ChainGeo<MT>::LDS;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess)
@@ -605,9 +687,8 @@ int chain_rounds(int format, const sv_pass_link* links, int count, int m, int gr
                  sv_status* st) {
   const int tm = round_tiles(m > 16 ? 2 : 1);
   *st = SV_OK;
-  if (format != SV_PASS_W4) {
-    *st = format == SV_PASS_W8 || format == SV_PASS_W4_I8 ? SV_ERR_UNSUPPORTED
-                                                          : SV_ERR_INVALID_ARG;
+  if (format != SV_PASS_W4 && format != SV_PASS_W8) {
+    *st = format == SV_PASS_W4_I8 ? SV_ERR_UNSUPPORTED : SV_ERR_INVALID_ARG;
     return 0;
   }
   if (!links) {
@@ -630,7 +711,7 @@ int chain_rounds(int format, const sv_pass_link* links, int count, int m, int gr
       *st = SV_ERR_INVALID_ARG;
       return 0;
     }
-    if (static_cast<long long>(e.N) * e.K / 2 >= (1LL << 31) ||
+    if (static_cast<long long>(e.N) * e.K / (format == SV_PASS_W8 ? 1 : 2) >= (1LL << 31) ||
         static_cast<long long>(m) * e.N * 4 >= (1LL << 31) ||
         static_cast<long long>(m) * e.K * 2 >= (1LL << 31)) {
       *st = SV_ERR_UNSUPPORTED;
@@ -813,13 +894,17 @@ extern "C" sv_status sv_pass_chain_plan(int format, const sv_pass_link* links, i
 
 // Called by sv_pass_run for chain plans.
 sv_status sv_chain_run(const sv_pass* pass, hipStream_t stream) {
-  if (pass->format != SV_PASS_W4) return SV_ERR_INVALID_ARG;
+  if (pass->format != SV_PASS_W4 && pass->format != SV_PASS_W8) return SV_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(pass->plan) & 255u) != 0) return SV_ERR_ALIGN;
   if (pass->grid < 1 || pass->grid > kMaxGridC || pass->grid > device_cus())
     return SV_ERR_INVALID_ARG;
   if (pass->items < 1) return SV_ERR_INVALID_ARG;
-  return pass->m > 16 ? launch_chain<2>(pass->plan, pass->items, pass->m, pass->grid, stream)
-                      : launch_chain<1>(pass->plan, pass->items, pass->m, pass->grid, stream);
+  void* const pl = pass->plan;
+  if (pass->format == SV_PASS_W8)
+    return pass->m > 16 ? launch_chain<2, SV_PASS_W8>(pl, pass->items, pass->m, pass->grid, stream)
+                        : launch_chain<1, SV_PASS_W8>(pl, pass->items, pass->m, pass->grid, stream);
+  return pass->m > 16 ? launch_chain<2, SV_PASS_W4>(pl, pass->items, pass->m, pass->grid, stream)
+                      : launch_chain<1, SV_PASS_W4>(pl, pass->items, pass->m, pass->grid, stream);
 }
 
 // Byte offset of a chain plan's status word (sv_pass_status).
