@@ -42,6 +42,14 @@ WARMUP_CURVE_STEPS = 20
 PROFILE_PASSES = 40
 
 
+def handoff_alpha_w8(K):
+    """The same for the synthetic W8 weights (codes uniform on -127..127,
+    scales uniform on [0.01, 0.05]): E[w^2] = E[c^2] E[s^2]."""
+    import numpy as np
+    ew2 = (127 * 128 / 3.0) * ((0.05 ** 3 - 0.01 ** 3) / (3 * 0.04))
+    return float(np.float32(1.0 / np.sqrt(K * ew2)))
+
+
 def handoff_alpha(K):
     """Scale of the bf16 hand-off between chained GEMMs that keeps the
     activations near unit size for the synthetic weights (codes and zero
@@ -770,6 +778,21 @@ def main():
         extra["w8_k_sweep"] = sweep8
         extra["w8_latency_ratio_k32_over_k1"] = round(sweep8[32]["pass_ms"] /
                                                       sweep8[1]["pass_ms"], 3)
+        # the W8 stack in model order (the same hand-offs as the W4 chain)
+        chain8 = {}
+        for kk in (1, 16, 32):
+            h, links = h0[:kk], []
+            for li, layer in enumerate(w8p):
+                for gi, (N, K, pc, s) in enumerate(layer):
+                    xo = chain_xo[li][gi][:kk]
+                    links.append((h, pc, s, N, y_own[li][gi][:kk], xo, handoff_alpha_w8(K)))
+                    h = xo
+            pk = sv.sv_pass_chain_plan(links, fmt="w8")
+            ms, _ = time_graph(torch, lambda pk=pk: sv.sv_pass_run(pk), 40, 40)
+            if sv.sv_pass_status(pk) != 0:
+                raise RuntimeError(f"W8 chain status {sv.sv_pass_status(pk)}")
+            chain8[kk] = {"pass_ms": round(ms, 4), "GBps": round(b8 / (ms * 1e-3) / 1e9, 1)}
+        extra["w8_k_sweep_model_order"] = chain8
         del w8p
         log("accept statistics")
         # accept statistics: 4096 trials per noise level, k = 32
